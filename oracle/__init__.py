@@ -1,0 +1,279 @@
+"""CPU oracle for the MoE expert path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never imports, links or calls anything here, and this
+package imports nothing from the product path.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, double precision, per-token
+loops); this module only builds that file with gcc, loads it with ctypes and
+marshals numpy arrays.  bf16 tensors are passed as ``uint16`` bit patterns.
+
+Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
+  logits               -- pinned: E=1 / dense reduction and per-element brute force
+  selection_scores     -- pinned: monotonicity / bias closed forms
+  topk                 -- pinned: brute-force subset enumeration, all-equal closed form
+  weights              -- pinned: sum identities, E=1 closed form
+  permute              -- pinned: `even` routing closed form (MegaMoE page,
+                          force-load-balancing table), golden fixture
+  aux                  -- pinned: uniform-probability closed form (aux == coeff),
+                          E=1 closed form.  The formula itself is a reading (the
+                          pages name a "standard aux_loss" without a formula).
+  forward              -- pinned: E=1/k=1 dense SwiGLU MLP, token-permutation
+                          invariance, linearity in w2
+  backward_tokens, weight_grads, weight_grad_elements, router_weight_grad
+                       -- pinned: central finite differences of the forward and
+                          an independent torch fp64 autograd formulation
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+SOFTMAX = 0
+SIGMOID = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into libmoe_oracle.so (gcc, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64, i32, f64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    sig = {
+        "oracle_logits": [i64, i32, i32, P, P, P],
+        "oracle_selection_scores": [i64, i32, i32, P, P, P],
+        "oracle_topk": [i64, i32, i32, i32, i32, P, P],
+        "oracle_weights": [i64, i32, i32, i32, i32, f64, P, P, P],
+        "oracle_permute": [i64, i32, i32, P, P, P, P, P],
+        "oracle_aux": [i64, i32, i32, i32, f64, P, P],
+        "oracle_forward": [i64, i32, i32, i32, i32, P, P, P, P, P, i64, P, P],
+        "oracle_backward_tokens": [i64, i32, i32, i32, i32, i32, i32, f64, f64, f64,
+                                   P, P, P, P, P, P, P, P, i64, P, P, P],
+        "oracle_weight_grads": [i64, i32, i32, i32, i32, P, P, P, P, P, P, i32, P,
+                                i64, P, P, P],
+        "oracle_weight_grad_elements": [i64, i32, i32, i32, P, P, P, P, P, P, i64,
+                                        P, P, P, P, P],
+        "oracle_router_weight_grad": [i64, i32, i32, P, P, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = None
+    lib.oracle_aux.restype = f64
+    _lib = lib
+    return lib
+
+
+def _c(a: Optional[np.ndarray], dtype) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def logits(x: np.ndarray, Wr: np.ndarray) -> np.ndarray:
+    """l = x . Wr^T in double.  x [T,H] bf16 bits (uint16), Wr [E,H] fp32."""
+    x = _c(x, np.uint16)
+    Wr = _c(Wr, np.float32)
+    T, H = x.shape
+    E = Wr.shape[0]
+    out = np.empty((T, E), np.float64)
+    _load().oracle_logits(T, H, E, _p(x), _p(Wr), _p(out))
+    return out
+
+
+def selection_scores(logits32: np.ndarray, score: int, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp32 selection scores from fp32 logits (S = l, or fp32(sigmoid(l)) + b)."""
+    l32 = _c(logits32, np.float32)
+    T, E = l32.shape
+    b = _c(bias, np.float32)
+    out = np.empty((T, E), np.float32)
+    _load().oracle_selection_scores(T, E, score, _p(l32), _p(b), _p(out))
+    return out
+
+
+def topk(S: np.ndarray, k: int, n_groups: int = 1, topk_groups: int = 1) -> np.ndarray:
+    """Group-limited top-k on fp32 scores -> int32 [T,k], best first."""
+    S = _c(S, np.float32)
+    T, E = S.shape
+    out = np.empty((T, k), np.int32)
+    _load().oracle_topk(T, E, k, n_groups, topk_groups, _p(S), _p(out))
+    return out
+
+
+def weights(logits64: np.ndarray, idx: np.ndarray, score: int, renorm: bool, scale: float) -> np.ndarray:
+    """Routing weights [T,k] in double from double logits and chosen indices."""
+    l = _c(logits64, np.float64)
+    idx = _c(idx, np.int32)
+    T, E = l.shape
+    k = idx.shape[1]
+    out = np.empty((T, k), np.float64)
+    _load().oracle_weights(T, E, k, score, int(bool(renorm)), float(scale), _p(l), _p(idx), _p(out))
+    return out
+
+
+def permute(idx: np.ndarray, E: int):
+    """-> counts [E], offsets [E+1], row_map [T*k], pos [T*k] (all int32)."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    row_map = np.empty(T * k, np.int32)
+    pos = np.empty(T * k, np.int32)
+    _load().oracle_permute(T, k, E, _p(idx), _p(counts), _p(offsets), _p(row_map), _p(pos))
+    return counts, offsets, row_map, pos
+
+
+def aux(logits64: np.ndarray, counts: np.ndarray, k: int, score: int, coeff: float) -> float:
+    l = _c(logits64, np.float64)
+    counts = _c(counts, np.int32)
+    T, E = l.shape
+    return float(_load().oracle_aux(T, E, k, score, float(coeff), _p(l), _p(counts)))
+
+
+def _toks(toks, T):
+    if toks is None:
+        return None, T
+    t = _c(np.asarray(toks), np.int64)
+    return t, t.shape[0]
+
+
+def forward(x, w1, w2, idx, w, toks=None) -> np.ndarray:
+    """y [ntok,H] double for the listed tokens (all when toks is None)."""
+    x = _c(x, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    k = idx.shape[1]
+    tk, n = _toks(toks, T)
+    y = np.empty((n, H), np.float64)
+    _load().oracle_forward(T, H, I, E, k, _p(x), _p(w1), _p(w2), _p(idx), _p(w), n, _p(tk), _p(y))
+    return y
+
+
+def backward_tokens(x, Wr, logits64, w1, w2, idx, counts, dy, *, score, renorm, scale,
+                    coeff, d_aux=1.0, toks=None):
+    """-> dx [ntok,H], dlogits [ntok,E] (double).  Wr may be None (logits supplied)."""
+    x = _c(x, np.uint16)
+    Wr = _c(Wr, np.float32)
+    l = _c(logits64, np.float64)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    idx = _c(idx, np.int32)
+    counts = _c(counts, np.int32)
+    dy = _c(dy, np.uint16)
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    k = idx.shape[1]
+    tk, n = _toks(toks, T)
+    dx = np.empty((n, H), np.float64)
+    dl = np.empty((n, E), np.float64)
+    _load().oracle_backward_tokens(T, H, I, E, k, score, int(bool(renorm)), float(scale),
+                                   float(coeff), float(d_aux), _p(x), _p(Wr), _p(l), _p(w1),
+                                   _p(w2), _p(idx), _p(counts), _p(dy), n, _p(tk), _p(dx), _p(dl))
+    return dx, dl
+
+
+def weight_grads(x, w1, w2, idx, w, dy, experts=None, toks=None):
+    """-> dW1 [ne,2I,H], dW2 [ne,H,I] (double) for the listed experts."""
+    x = _c(x, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    dy = _c(dy, np.uint16)
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    k = idx.shape[1]
+    ex = None if experts is None else _c(np.asarray(experts), np.int32)
+    ne = E if ex is None else ex.shape[0]
+    tk, n = _toks(toks, T)
+    dW1 = np.empty((ne, twoI, H), np.float64)
+    dW2 = np.empty((ne, H, I), np.float64)
+    _load().oracle_weight_grads(T, H, I, E, k, _p(x), _p(w1), _p(w2), _p(idx), _p(w), _p(dy),
+                                ne, _p(ex), n, _p(tk), _p(dW1), _p(dW2))
+    return dW1, dW2
+
+
+def weight_grad_elements(x, w1, w2, idx, w, dy, which, ee, rr, cc) -> np.ndarray:
+    """Single elements of dW1 (which=1, [e,n,h]) or dW2 (which=2, [e,h,i])."""
+    x = _c(x, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    dy = _c(dy, np.uint16)
+    which = _c(which, np.int32)
+    ee = _c(ee, np.int32)
+    rr = _c(rr, np.int32)
+    cc = _c(cc, np.int32)
+    T, H = x.shape
+    I = w2.shape[2]
+    k = idx.shape[1]
+    out = np.empty(which.shape[0], np.float64)
+    _load().oracle_weight_grad_elements(T, H, I, k, _p(x), _p(w1), _p(w2), _p(idx), _p(w), _p(dy),
+                                        which.shape[0], _p(which), _p(ee), _p(rr), _p(cc), _p(out))
+    return out
+
+
+def router_weight_grad(x, dlogits64) -> np.ndarray:
+    x = _c(x, np.uint16)
+    dl = _c(dlogits64, np.float64)
+    T, H = x.shape
+    E = dl.shape[1]
+    out = np.empty((E, H), np.float64)
+    _load().oracle_router_weight_grad(T, H, E, _p(x), _p(dl), _p(out))
+    return out
+
+
+def route(logits64: np.ndarray, *, score: int, k: int, n_groups: int = 1, topk_groups: int = 1,
+          bias=None, renorm: bool = False, scale: float = 1.0, coeff: float = 0.0,
+          logits32: Optional[np.ndarray] = None):
+    """Full router of the oracle: fp32 selection, top-k, weights, permutation, aux.
+
+    ``logits32`` is the fp32 logits tensor the decision is taken on; by default
+    the double logits rounded to fp32.
+    """
+    l32 = np.asarray(logits64, np.float32) if logits32 is None else np.asarray(logits32, np.float32)
+    S = selection_scores(l32, score, bias)
+    idx = topk(S, k, n_groups, topk_groups)
+    E = l32.shape[1]
+    w = weights(logits64, idx, score, renorm, scale)
+    counts, offsets, row_map, pos = permute(idx, E)
+    a = aux(logits64, counts, k, score, coeff)
+    return dict(S=S, idx=idx, w=w, counts=counts, offsets=offsets, row_map=row_map,
+                pos=pos, aux=a)

@@ -1,0 +1,591 @@
+/*
+ * moe_oracle.c -- CPU oracle for the MoE expert path (router -> dispatch ->
+ * grouped GEMM1 -> SwiGLU -> grouped GEMM2 -> weighted combine, and the
+ * backward of all of it).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * What it follows (page "MegaMoE", Primus technical guide):
+ *   - intro: fused router = score function + group-limited top-k + aux score;
+ *     expert path = dispatch -> GEMM1 -> SwiGLU -> GEMM2 -> combine with a
+ *     weighted reduce; the load-balancing aux loss is returned.
+ *   - "Design: two stages + weight modules": w1 is [g, 2I, H] holding gate
+ *     rows then up rows, w2 is [g, H, I]; backward yields dW2, then dW1.
+ *   - "Required" settings: gated SwiGLU with SiLU, no bias in the linears.
+ *   - "Router force load balancing": the `even` routing formula (a test pin).
+ * SwiGLU itself is silu(x_glu) * x_linear (page "GDN <-> FLA Parity in
+ * Primus", "What changed and why", table B, the fused-SwiGLU patch row), with
+ * x_glu the gate half.
+ *
+ * Precision: every value on the expert path is computed in double from the
+ * exact (bf16 / fp32) inputs; nothing is rounded to bf16 in between.  The one
+ * place floating point decides an integer -- the top-k -- takes its decision
+ * on an fp32 score tensor, as the GPU path does.  Readings where the pages are
+ * silent (tie rules, group score, aux formula, sigmoid weight scaling, bias
+ * use) are stated at each function.
+ *
+ * Everything is written as the plain definition: per-token loops over the
+ * selected experts, no blocking, no fusion.  OpenMP splits only independent
+ * outer iterations (tokens, or experts for the weight gradients).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_SOFTMAX 0
+#define OR_SIGMOID 1
+
+/* bf16 bit pattern -> exact double (bf16 is the top half of an fp32). */
+static double bf(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+static double silu(double z) { return z * sigmoid(z); }
+
+/* ------------------------------------------------------------------------ */
+/* Router projection: l[t,e] = sum_h x[t,h] * Wr[e,h]  (Wr is [E,H], fp32).   */
+/* Output in double; callers round to fp32 when they need the fp32 logits.   */
+/* ------------------------------------------------------------------------ */
+void oracle_logits(int64_t T, int32_t H, int32_t E, const uint16_t *x,
+                   const float *Wr, double *logits)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int32_t h = 0; h < H; ++h)
+                acc += bf(x[t * H + h]) * (double)Wr[(int64_t)e * H + h];
+            logits[t * E + e] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Selection scores S (fp32), the tensor the top-k decides on.               */
+/*   softmax router: S = l  (softmax is strictly increasing, so the top-k of  */
+/*                   the probabilities is the top-k of the logits; deciding  */
+/*                   on l avoids ties created by rounding exp).               */
+/*   sigmoid router: S = fp32(sigmoid(l)) + b, an fp32 add; b (nullable) is  */
+/*                   a per-expert bias that takes part in selection only.    */
+/* logits are the fp32 logits.                                               */
+/* ------------------------------------------------------------------------ */
+void oracle_selection_scores(int64_t T, int32_t E, int32_t score,
+                             const float *logits, const float *bias, float *S)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t e = 0; e < E; ++e) {
+            float l = logits[t * E + e];
+            if (score == OR_SOFTMAX) {
+                S[t * E + e] = l;
+            } else {
+                float s = (float)sigmoid((double)l);
+                float b = bias ? bias[e] : 0.0f;
+                S[t * E + e] = s + b;
+            }
+        }
+}
+
+/* a ranks before b: larger value first, equal values -> lower index first. */
+static int ranks_before(float va, int32_t ia, float vb, int32_t ib)
+{
+    return va > vb || (va == vb && ia < ib);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Group-limited top-k on fp32 scores S [T,E] -> idx [T,k].                   */
+/*   G groups of E/G contiguous experts (reading: contiguous blocks).        */
+/*   If G > 1: group score = sum (fp32 add) of the two largest S in the      */
+/*   group (just the largest when a group has one expert); the kg best       */
+/*   groups are kept (ties -> lower group index); only their experts are     */
+/*   eligible.  Then the k best eligible experts, best first (ties -> lower  */
+/*   expert index).  Selection is by repeated arg-max.                       */
+/* ------------------------------------------------------------------------ */
+void oracle_topk(int64_t T, int32_t E, int32_t k, int32_t G, int32_t kg,
+                 const float *S, int32_t *idx)
+{
+#pragma omp parallel
+    {
+        unsigned char *eligible = (unsigned char *)malloc((size_t)E);
+        unsigned char *taken = (unsigned char *)malloc((size_t)E);
+        float *gs = (float *)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
+        unsigned char *gtaken = (unsigned char *)malloc((size_t)(G > 0 ? G : 1));
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const float *s = S + t * E;
+            if (G > 1) {
+                int32_t gsz = E / G;
+                for (int32_t g = 0; g < G; ++g) {
+                    int32_t best = -1, second = -1;
+                    for (int32_t e = g * gsz; e < (g + 1) * gsz; ++e)
+                        if (best < 0 || ranks_before(s[e], e, s[best], best))
+                            best = e;
+                    for (int32_t e = g * gsz; e < (g + 1) * gsz; ++e)
+                        if (e != best &&
+                            (second < 0 || ranks_before(s[e], e, s[second], second)))
+                            second = e;
+                    gs[g] = (second >= 0) ? s[best] + s[second] : s[best];
+                    gtaken[g] = 0;
+                }
+                for (int32_t e = 0; e < E; ++e) eligible[e] = 0;
+                for (int32_t r = 0; r < kg; ++r) {
+                    int32_t bg = -1;
+                    for (int32_t g = 0; g < G; ++g)
+                        if (!gtaken[g] && (bg < 0 || ranks_before(gs[g], g, gs[bg], bg)))
+                            bg = g;
+                    gtaken[bg] = 1;
+                    for (int32_t e = bg * gsz; e < (bg + 1) * gsz; ++e) eligible[e] = 1;
+                }
+            } else {
+                for (int32_t e = 0; e < E; ++e) eligible[e] = 1;
+            }
+            for (int32_t e = 0; e < E; ++e) taken[e] = 0;
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t be = -1;
+                for (int32_t e = 0; e < E; ++e)
+                    if (eligible[e] && !taken[e] &&
+                        (be < 0 || ranks_before(s[e], e, s[be], be)))
+                        be = e;
+                taken[be] = 1;
+                idx[t * k + j] = be;
+            }
+        }
+        free(eligible);
+        free(taken);
+        free(gs);
+        free(gtaken);
+    }
+}
+
+/* Router probabilities of one token over all E experts (double):            */
+/*   softmax router: p = softmax(l);  sigmoid router: s = sigmoid(l).        */
+static void token_scores(int32_t E, int32_t score, const double *l, double *out)
+{
+    if (score == OR_SOFTMAX) {
+        double m = l[0];
+        for (int32_t e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+        double z = 0.0;
+        for (int32_t e = 0; e < E; ++e) { out[e] = exp(l[e] - m); z += out[e]; }
+        for (int32_t e = 0; e < E; ++e) out[e] /= z;
+    } else {
+        for (int32_t e = 0; e < E; ++e) out[e] = sigmoid(l[e]);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Routing weights w [T,k] (double) for given indices.                       */
+/*   softmax: w_j = p[idx_j], divided by sum_j p[idx_j] when renorm != 0.    */
+/*   sigmoid: w_j = scale * s[idx_j] / sum_j s[idx_j]  (normalised, then     */
+/*            scaled); the selection bias never enters the weights.          */
+/* ------------------------------------------------------------------------ */
+void oracle_weights(int64_t T, int32_t E, int32_t k, int32_t score,
+                    int32_t renorm, double scale, const double *logits,
+                    const int32_t *idx, double *w)
+{
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            token_scores(E, score, logits + t * E, p);
+            double z = 0.0;
+            for (int32_t j = 0; j < k; ++j) z += p[idx[t * k + j]];
+            for (int32_t j = 0; j < k; ++j) {
+                double v = p[idx[t * k + j]];
+                if (score == OR_SOFTMAX)
+                    w[t * k + j] = renorm ? v / z : v;
+                else
+                    w[t * k + j] = scale * v / z;
+            }
+        }
+        free(p);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch bookkeeping.  Flat slot f = t*k + j.                             */
+/*   counts[e]  = number of slots routed to e                                */
+/*   offsets    = exclusive prefix sum of counts, offsets[E] = T*k           */
+/*   row_map[r] = the flat slot placed at sorted row r: experts in ascending */
+/*                order, and inside one expert ascending flat slot (stable)  */
+/*   pos[f]     = the sorted row of flat slot f (inverse of row_map)         */
+/* ------------------------------------------------------------------------ */
+void oracle_permute(int64_t T, int32_t k, int32_t E, const int32_t *idx,
+                    int32_t *counts, int32_t *offsets, int32_t *row_map,
+                    int32_t *pos)
+{
+    int64_t M = T * k;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t f = 0; f < M; ++f) counts[idx[f]] += 1;
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int64_t r = 0;
+    for (int32_t e = 0; e < E; ++e)
+        for (int64_t f = 0; f < M; ++f)
+            if (idx[f] == e) {
+                row_map[r] = (int32_t)f;
+                pos[f] = (int32_t)r;
+                ++r;
+            }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Load-balancing aux loss (reading; the pages give no formula):             */
+/*   aux = coeff * E / (k * T^2) * sum_e counts[e] * sum_t p[t,e]            */
+/* = coeff * E * sum_e f_e * P_e with f_e = counts[e]/(k T), P_e = mean_t p. */
+/* p = softmax(l) for the softmax router, s / sum_e s for the sigmoid one.  */
+/* ------------------------------------------------------------------------ */
+double oracle_aux(int64_t T, int32_t E, int32_t k, int32_t score, double coeff,
+                  const double *logits, const int32_t *counts)
+{
+    if (T == 0) return 0.0;
+    double *P = (double *)calloc((size_t)E, sizeof(double));
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        token_scores(E, score, logits + t * E, p);
+        if (score == OR_SIGMOID) {
+            double z = 0.0;
+            for (int32_t e = 0; e < E; ++e) z += p[e];
+            for (int32_t e = 0; e < E; ++e) p[e] /= z;
+        }
+        for (int32_t e = 0; e < E; ++e) P[e] += p[e];
+    }
+    double acc = 0.0;
+    for (int32_t e = 0; e < E; ++e) acc += (double)counts[e] * P[e];
+    free(P);
+    free(p);
+    return coeff * (double)E / ((double)k * (double)T * (double)T) * acc;
+}
+
+/* One (token, expert) pair of the expert MLP, forward:                     */
+/*   g[i] = sum_h x[h] w1[e,i,h],  u[i] = sum_h x[h] w1[e,I+i,h]             */
+/*   a[i] = silu(g[i]) * u[i],     o[h] = sum_i w2[e,h,i] a[i]               */
+static void expert_mlp(int32_t H, int32_t I, const uint16_t *xt,
+                       const uint16_t *w1e, const uint16_t *w2e, double *g,
+                       double *u, double *a, double *o)
+{
+    for (int32_t i = 0; i < I; ++i) {
+        double sg = 0.0, su = 0.0;
+        for (int32_t h = 0; h < H; ++h) {
+            double xv = bf(xt[h]);
+            sg += xv * bf(w1e[(int64_t)i * H + h]);
+            su += xv * bf(w1e[(int64_t)(I + i) * H + h]);
+        }
+        g[i] = sg;
+        u[i] = su;
+        a[i] = silu(sg) * su;
+    }
+    if (o)
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < I; ++i) acc += bf(w2e[(int64_t)h * I + i]) * a[i];
+            o[h] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert forward for a list of tokens (toks == NULL: tokens 0..ntok-1).     */
+/*   y[t] = sum_{j=0..k-1} w[t,j] * o(t, idx[t,j])   (j ascending)           */
+/* x [T,H] bf16, w1 [E,2I,H] bf16, w2 [E,H,I] bf16, y [ntok,H] double.       */
+/* ------------------------------------------------------------------------ */
+void oracle_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                    const uint16_t *x, const uint16_t *w1, const uint16_t *w2,
+                    const int32_t *idx, const double *w, int64_t ntok,
+                    const int64_t *toks, double *y)
+{
+    (void)T;
+    (void)E;
+#pragma omp parallel
+    {
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < ntok; ++n) {
+            int64_t t = toks ? toks[n] : n;
+            double *yt = y + n * H;
+            for (int32_t h = 0; h < H; ++h) yt[h] = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = idx[t * k + j];
+                expert_mlp(H, I, x + t * H, w1 + (int64_t)e * 2 * I * H,
+                           w2 + (int64_t)e * H * I, g, u, a, o);
+                for (int32_t h = 0; h < H; ++h) yt[h] += w[t * k + j] * o[h];
+            }
+        }
+        free(g);
+        free(u);
+        free(a);
+        free(o);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward for a list of tokens: dx [ntok,H] and dlogits [ntok,E] (double). */
+/* Loss = sum_t <dy[t], y[t]> + d_aux * aux.                                 */
+/* Per slot (t,j), e = idx[t,j]:                                             */
+/*   dw_j  = <dy_t, o>                                                       */
+/*   dA_i  = w_j * sum_h w2[e,h,i] dy_t[h]                                   */
+/*   dg_i  = dA_i * u_i * sig(g_i) * (1 + g_i (1 - sig(g_i)))                */
+/*   du_i  = dA_i * silu(g_i)                                                */
+/*   dx_t += sum_i (w1[e,i,:] dg_i + w1[e,I+i,:] du_i)                       */
+/* Router (counts are constants, the selection carries no gradient):        */
+/*   softmax: dp at selected e_j = renorm ? (dw_j - sum dw w)/sum p_sel      */
+/*                                        : dw_j                             */
+/*            plus aux: d_aux*coeff*E/(k T^2)*counts[e] at every e;         */
+/*            dl = p * (dp - <dp, p>)                                        */
+/*   sigmoid: ds at selected e_j = scale/sum s_sel * (dw_j - sum dw w/scale) */
+/*            plus aux through p = s/sum s: (a_e - sum a p)/sum s;           */
+/*            dl = ds * s * (1 - s)                                          */
+/*   dx_t += sum_e dl[e] Wr[e,:]   (when Wr != NULL)                         */
+/* logits are the router logits in double, counts the routed counts.        */
+/* ------------------------------------------------------------------------ */
+void oracle_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E,
+                            int32_t k, int32_t score, int32_t renorm,
+                            double scale, double coeff, double d_aux,
+                            const uint16_t *x, const float *Wr,
+                            const double *logits, const uint16_t *w1,
+                            const uint16_t *w2, const int32_t *idx,
+                            const int32_t *counts, const uint16_t *dy,
+                            int64_t ntok, const int64_t *toks, double *dx,
+                            double *dlogits)
+{
+#pragma omp parallel
+    {
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+        double *p = (double *)malloc(sizeof(double) * (size_t)E);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)E);
+        double *wt = (double *)malloc(sizeof(double) * (size_t)k);
+        double *dw = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < ntok; ++n) {
+            int64_t t = toks ? toks[n] : n;
+            const uint16_t *xt = x + t * H;
+            const uint16_t *dyt = dy + t * H;
+            double *dxt = dx + n * H;
+            for (int32_t h = 0; h < H; ++h) dxt[h] = 0.0;
+
+            /* routing weights of this token */
+            token_scores(E, score, logits + t * E, p);
+            double zsel = 0.0;
+            for (int32_t j = 0; j < k; ++j) zsel += p[idx[t * k + j]];
+            for (int32_t j = 0; j < k; ++j) {
+                double v = p[idx[t * k + j]];
+                if (score == OR_SOFTMAX) wt[j] = renorm ? v / zsel : v;
+                else wt[j] = scale * v / zsel;
+            }
+
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = idx[t * k + j];
+                const uint16_t *w1e = w1 + (int64_t)e * 2 * I * H;
+                const uint16_t *w2e = w2 + (int64_t)e * H * I;
+                expert_mlp(H, I, xt, w1e, w2e, g, u, a, o);
+                double acc = 0.0;
+                for (int32_t h = 0; h < H; ++h) acc += bf(dyt[h]) * o[h];
+                dw[j] = acc;
+                for (int32_t i = 0; i < I; ++i) {
+                    double dA = 0.0;
+                    for (int32_t h = 0; h < H; ++h)
+                        dA += bf(w2e[(int64_t)h * I + i]) * bf(dyt[h]);
+                    dA *= wt[j];
+                    double sg = sigmoid(g[i]);
+                    double dg = dA * u[i] * sg * (1.0 + g[i] * (1.0 - sg));
+                    double du = dA * silu(g[i]);
+                    for (int32_t h = 0; h < H; ++h)
+                        dxt[h] += bf(w1e[(int64_t)i * H + h]) * dg +
+                                  bf(w1e[(int64_t)(I + i) * H + h]) * du;
+                }
+            }
+
+            /* router */
+            double sdw = 0.0;
+            for (int32_t j = 0; j < k; ++j) sdw += dw[j] * wt[j];
+            for (int32_t e = 0; e < E; ++e) dp[e] = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = idx[t * k + j];
+                if (score == OR_SOFTMAX)
+                    dp[e] += renorm ? (dw[j] - sdw) / zsel : dw[j];
+                else
+                    dp[e] += scale / zsel * (dw[j] - sdw / scale);
+            }
+            double *dl = dlogits + n * E;
+            double aux_scale = (T > 0) ? d_aux * coeff * (double)E /
+                                             ((double)k * (double)T * (double)T)
+                                       : 0.0;
+            if (score == OR_SOFTMAX) {
+                for (int32_t e = 0; e < E; ++e) dp[e] += aux_scale * (double)counts[e];
+                double dot = 0.0;
+                for (int32_t e = 0; e < E; ++e) dot += dp[e] * p[e];
+                for (int32_t e = 0; e < E; ++e) dl[e] = p[e] * (dp[e] - dot);
+            } else {
+                double q = 0.0;
+                for (int32_t e = 0; e < E; ++e) q += p[e];
+                double ap = 0.0;
+                for (int32_t e = 0; e < E; ++e) ap += aux_scale * (double)counts[e] * (p[e] / q);
+                for (int32_t e = 0; e < E; ++e)
+                    dp[e] += (aux_scale * (double)counts[e] - ap) / q;
+                for (int32_t e = 0; e < E; ++e) dl[e] = dp[e] * p[e] * (1.0 - p[e]);
+            }
+            if (Wr)
+                for (int32_t e = 0; e < E; ++e)
+                    for (int32_t h = 0; h < H; ++h)
+                        dxt[h] += dl[e] * (double)Wr[(int64_t)e * H + h];
+        }
+        free(g);
+        free(u);
+        free(a);
+        free(o);
+        free(p);
+        free(dp);
+        free(wt);
+        free(dw);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert weight gradients for a list of experts (experts == NULL: 0..ne-1), */
+/* summed over the listed tokens (toks == NULL: all T tokens):               */
+/*   dW2[e,h,i]   = sum_{(t,j): idx=e} w_tj dy_t[h] a_i                      */
+/*   dW1[e,i,h]   = sum dg_i x_t[h],   dW1[e,I+i,h] = sum du_i x_t[h]        */
+/* dW1 [ne,2I,H], dW2 [ne,H,I] in double, overwritten.  w [T,k] double.     */
+/* ------------------------------------------------------------------------ */
+void oracle_weight_grads(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                         const uint16_t *x, const uint16_t *w1,
+                         const uint16_t *w2, const int32_t *idx,
+                         const double *w, const uint16_t *dy, int32_t ne,
+                         const int32_t *experts, int64_t ntok,
+                         const int64_t *toks, double *dW1, double *dW2)
+{
+    (void)E;
+#pragma omp parallel
+    {
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t q = 0; q < ne; ++q) {
+            int32_t e = experts ? experts[q] : q;
+            const uint16_t *w1e = w1 + (int64_t)e * 2 * I * H;
+            const uint16_t *w2e = w2 + (int64_t)e * H * I;
+            double *d1 = dW1 + (int64_t)q * 2 * I * H;
+            double *d2 = dW2 + (int64_t)q * H * I;
+            memset(d1, 0, sizeof(double) * (size_t)2 * I * H);
+            memset(d2, 0, sizeof(double) * (size_t)H * I);
+            int64_t nt = toks ? ntok : T;
+            for (int64_t n = 0; n < nt; ++n) {
+                int64_t t = toks ? toks[n] : n;
+                for (int32_t j = 0; j < k; ++j) {
+                    if (idx[t * k + j] != e) continue;
+                    const uint16_t *xt = x + t * H;
+                    const uint16_t *dyt = dy + t * H;
+                    double wj = w[t * k + j];
+                    expert_mlp(H, I, xt, w1e, w2e, g, u, a, NULL);
+                    for (int32_t h = 0; h < H; ++h) {
+                        double c = wj * bf(dyt[h]);
+                        for (int32_t i = 0; i < I; ++i) d2[(int64_t)h * I + i] += c * a[i];
+                    }
+                    for (int32_t i = 0; i < I; ++i) {
+                        double dA = 0.0;
+                        for (int32_t h = 0; h < H; ++h)
+                            dA += bf(w2e[(int64_t)h * I + i]) * bf(dyt[h]);
+                        dA *= wj;
+                        double sg = sigmoid(g[i]);
+                        double dg = dA * u[i] * sg * (1.0 + g[i] * (1.0 - sg));
+                        double du = dA * silu(g[i]);
+                        for (int32_t h = 0; h < H; ++h) {
+                            double xv = bf(xt[h]);
+                            d1[(int64_t)i * H + h] += dg * xv;
+                            d1[(int64_t)(I + i) * H + h] += du * xv;
+                        }
+                    }
+                }
+            }
+        }
+        free(g);
+        free(u);
+        free(a);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Single elements of dW1 / dW2 (for full-size shapes, where whole weight    */
+/* gradients are out of reach on the CPU).  Element q is                     */
+/*   which[q] == 1: dW1[ee[q], rr[q], cc[q]]   (row n < 2I, column h)        */
+/*   which[q] == 2: dW2[ee[q], rr[q], cc[q]]   (row h, column i)             */
+/* summed over all T tokens; same definitions as oracle_weight_grads.        */
+/* ------------------------------------------------------------------------ */
+void oracle_weight_grad_elements(int64_t T, int32_t H, int32_t I, int32_t k,
+                                 const uint16_t *x, const uint16_t *w1,
+                                 const uint16_t *w2, const int32_t *idx,
+                                 const double *w, const uint16_t *dy,
+                                 int64_t nel, const int32_t *which,
+                                 const int32_t *ee, const int32_t *rr,
+                                 const int32_t *cc, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nel; ++q) {
+        int32_t e = ee[q];
+        const uint16_t *w1e = w1 + (int64_t)e * 2 * I * H;
+        const uint16_t *w2e = w2 + (int64_t)e * H * I;
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t j = 0; j < k; ++j) {
+                if (idx[t * k + j] != e) continue;
+                const uint16_t *xt = x + t * H;
+                const uint16_t *dyt = dy + t * H;
+                double wj = w[t * k + j];
+                int32_t i = (which[q] == 2) ? cc[q] : (rr[q] % I);
+                double sg_, su_;
+                {
+                    double s1 = 0.0, s2 = 0.0;
+                    for (int32_t h = 0; h < H; ++h) {
+                        double xv = bf(xt[h]);
+                        s1 += xv * bf(w1e[(int64_t)i * H + h]);
+                        s2 += xv * bf(w1e[(int64_t)(I + i) * H + h]);
+                    }
+                    sg_ = s1;
+                    su_ = s2;
+                }
+                if (which[q] == 2) {
+                    double ai = silu(sg_) * su_;
+                    acc += wj * bf(dyt[rr[q]]) * ai;
+                } else {
+                    double dA = 0.0;
+                    for (int32_t h = 0; h < H; ++h)
+                        dA += bf(w2e[(int64_t)h * I + i]) * bf(dyt[h]);
+                    dA *= wj;
+                    double sg = sigmoid(sg_);
+                    double d = (rr[q] < I) ? dA * su_ * sg * (1.0 + sg_ * (1.0 - sg))
+                                           : dA * silu(sg_);
+                    acc += d * bf(xt[cc[q]]);
+                }
+            }
+        out[q] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router weight gradient: dWr[e,h] = sum_t dlogits[t,e] x[t,h]  (double).   */
+/* ------------------------------------------------------------------------ */
+void oracle_router_weight_grad(int64_t T, int32_t H, int32_t E,
+                               const uint16_t *x, const double *dlogits,
+                               double *dWr)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t e = 0; e < E; ++e)
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < T; ++t) acc += dlogits[t * E + e] * bf(x[t * H + h]);
+            dWr[(int64_t)e * H + h] = acc;
+        }
+}
