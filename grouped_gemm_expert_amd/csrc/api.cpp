@@ -1,0 +1,435 @@
+// Host layer of libmoe: argument validation, workspace carving and the launch
+// sequence of every C entry point declared in include/moe.h.  Nothing here
+// allocates, frees or synchronises; every call only enqueues on the stream.
+#include <string.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+    char *base;
+    size_t used = 0;
+    explicit Carver(void *b) : base((char *)b) {}
+    template <class T>
+    T *take(int64_t n)
+    {
+        T *p = base ? (T *)(base + used) : nullptr;
+        used += align_up(sizeof(T) * (size_t)(n > 0 ? n : 0));
+        return p;
+    }
+};
+
+struct FwdWs {
+    float *prob_part;
+    int32_t *chunk_hist;
+    Sched sched;
+    float *o;
+};
+
+struct BwdWs {
+    Sched sched;
+    uint16_t *dh;
+    float *dw_part;
+    float *dxp;
+};
+
+FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
+{
+    Carver cv(ws);
+    const int64_t M = c.T * c.k;
+    FwdWs w;
+    w.prob_part = cv.take<float>(router_blocks(c.T) * c.E);
+    w.chunk_hist = cv.take<int32_t>(permute_chunks(M) * c.E);
+    w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
+    w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
+    w.sched.order = cv.take<int32_t>(c.E);
+    w.o = cv.take<float>(M * c.H);
+    if (bytes) *bytes = cv.used;
+    return w;
+}
+
+BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
+{
+    Carver cv(ws);
+    const int64_t M = c.T * c.k;
+    BwdWs w;
+    w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
+    w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
+    w.sched.order = cv.take<int32_t>(c.E);
+    w.dh = cv.take<uint16_t>(M * 2 * c.I);
+    w.dw_part = cv.take<float>(M * dgrad2_cols(c.I));
+    w.dxp = cv.take<float>(M * c.H);
+    if (bytes) *bytes = cv.used;
+    return w;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)                                  \
+    do {                                               \
+        hipError_t e_ = (expr);                        \
+        if (e_ != hipSuccess) return MOE_EHIP;         \
+    } while (0)
+
+#define MOE_CHECK(expr)                                \
+    do {                                               \
+        moe_status s_ = (expr);                        \
+        if (s_ != MOE_OK) return s_;                   \
+    } while (0)
+
+moe_status check_ptrs(std::initializer_list<const void *> ps)
+{
+    for (const void *p : ps)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+moe_status check_opt_ptr(const void *p) { return (!p || aligned16(p)) ? MOE_OK : MOE_EINVAL; }
+
+GemmArgs gemm_args(const moe_config &c, const moe_gemm_args &a, const Sched &sc)
+{
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.T = c.T;
+    g.M = c.T * c.k;
+    g.E = c.E;
+    g.k = c.k;
+    g.H = c.H;
+    g.I = c.I;
+    g.counts = a.counts;
+    g.offsets = a.offsets;
+    g.row_map = a.row_map;
+    g.topk_w = a.topk_w;
+    g.x = a.x;
+    g.dy = a.dy;
+    g.w1 = a.w1;
+    g.w2 = a.w2;
+    g.h = a.h;
+    g.a = a.a;
+    g.o = a.o;
+    g.dh = a.dh;
+    g.dw_part = a.dw_part;
+    g.dxp = a.dxp;
+    g.dW1 = a.dW1;
+    g.dW2 = a.dW2;
+    g.dw_bf16 = a.dw_dtype == MOE_BF16;
+    g.dw_acc = a.dw_accumulate != 0;
+    g.sched = sc;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null or misaligned pointer, bad enum or size)";
+    case MOE_EUNSUPPORTED: return "unsupported shape or option";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char *moe_version(void) { return "libmoe 0.1 gfx950"; }
+
+moe_status moe_check_config(const moe_config *cfg)
+{
+    if (!cfg) return MOE_EINVAL;
+    const moe_config &c = *cfg;
+    if (c.T < 0 || c.H <= 0 || c.I <= 0 || c.E <= 0 || c.k <= 0) return MOE_EINVAL;
+    if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID) return MOE_EINVAL;
+    if (c.k > c.E || c.k > 32 || c.E > 1024) return MOE_EUNSUPPORTED;
+    if (c.n_groups < 1 || c.n_groups > 64 || c.E % c.n_groups != 0) return MOE_EUNSUPPORTED;
+    if (c.topk_groups < 1 || c.topk_groups > c.n_groups) return MOE_EUNSUPPORTED;
+    if (c.n_groups > 1 && (int64_t)c.k > (int64_t)c.topk_groups * (c.E / c.n_groups))
+        return MOE_EUNSUPPORTED;
+    if (c.H % 64 != 0 || c.I % 64 != 0) return MOE_EUNSUPPORTED;
+    const int64_t M = c.T * (int64_t)c.k;
+    const int64_t widest = c.H > 2 * c.I ? c.H : 2 * (int64_t)c.I;
+    if (M >= (1ll << 31) || M * widest >= (1ll << 31)) return MOE_EUNSUPPORTED;
+    if ((int64_t)2 * c.I * c.H >= (1ll << 31)) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_config *cfg, size_t *fwd_bytes, size_t *bwd_bytes)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    size_t f = 0, b = 0;
+    carve_fwd(*cfg, nullptr, &f);
+    carve_bwd(*cfg, nullptr, &b);
+    if (fwd_bytes) *fwd_bytes = f;
+    if (bwd_bytes) *bwd_bytes = b;
+    return MOE_OK;
+}
+
+int32_t moe_dw_part_cols(const moe_config *cfg) { return cfg ? dgrad2_cols(cfg->I) : 0; }
+
+moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                      const float *bias, float *logits, float *sel_scores,
+                      int32_t *topk_idx, float *topk_w, int32_t *counts, float *aux,
+                      void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    MOE_CHECK(check_ptrs({logits, topk_idx, topk_w, counts, aux}));
+    MOE_CHECK(check_opt_ptr(bias));
+    MOE_CHECK(check_opt_ptr(sel_scores));
+    if (Wr) MOE_CHECK(check_ptrs({x, Wr}));
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    if (c.T == 0) {
+        MOE_TRY(launch_fill_i32(counts, c.E, 0, stream));
+        MOE_TRY(launch_fill_f32(aux, 1, 0.f, stream));
+        return MOE_OK;
+    }
+    if (Wr)
+        MOE_TRY(launch_simt_gemm(c.T, c.E, c.H, x, true, c.H, 1, Wr, false, c.H, 1, logits, c.E,
+                                 false, stream));
+    RouterArgs ra;
+    ra.T = c.T;
+    ra.E = c.E;
+    ra.k = c.k;
+    ra.G = c.n_groups;
+    ra.kg = c.topk_groups;
+    ra.score = c.score;
+    ra.renorm = c.renorm;
+    ra.scale = c.scale;
+    ra.aux_coeff = c.aux_coeff;
+    ra.logits = logits;
+    ra.bias = bias;
+    ra.sel = sel_scores;
+    ra.topk_w = topk_w;
+    ra.topk_idx = topk_idx;
+    ra.counts = counts;
+    ra.aux = aux;
+    ra.prob_part = w.prob_part;
+    MOE_TRY(launch_router(ra, stream));
+    return MOE_OK;
+}
+
+moe_status moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *counts,
+                       int32_t *offsets, int32_t *row_map, int32_t *pos, void *ws,
+                       size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    MOE_CHECK(check_ptrs({counts, offsets}));
+    if (c.T > 0) MOE_CHECK(check_ptrs({topk_idx, row_map, pos}));
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    MOE_TRY(launch_permute(c.T * c.k, c.E, topk_idx, counts, offsets, row_map, pos, w.chunk_hist,
+                           stream));
+    return MOE_OK;
+}
+
+moe_status moe_grouped_gemm(int32_t op, const moe_config *cfg, const moe_gemm_args *args,
+                            void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    if (!args) return MOE_EINVAL;
+    const moe_config &c = *cfg;
+    const moe_gemm_args &a = *args;
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    MOE_CHECK(check_ptrs({a.counts, a.offsets}));
+    switch (op) {
+    case MOE_GEMM_UP_SWIGLU:
+        MOE_CHECK(check_ptrs({a.x, a.w1, a.row_map, a.a}));
+        MOE_CHECK(check_opt_ptr(a.h));
+        break;
+    case MOE_GEMM_DOWN:
+        MOE_CHECK(check_ptrs({a.a, a.w2, a.o}));
+        break;
+    case MOE_GEMM_DOWN_DGRAD:
+        MOE_CHECK(check_ptrs({a.dy, a.w2, a.row_map, a.topk_w, a.h, a.a, a.dh, a.dw_part}));
+        break;
+    case MOE_GEMM_UP_DGRAD:
+        MOE_CHECK(check_ptrs({a.dh, a.w1, a.dxp}));
+        break;
+    case MOE_GEMM_DOWN_WGRAD:
+        MOE_CHECK(check_ptrs({a.dy, a.a, a.row_map, a.topk_w, a.dW2}));
+        break;
+    case MOE_GEMM_UP_WGRAD:
+        MOE_CHECK(check_ptrs({a.dh, a.x, a.row_map, a.dW1}));
+        break;
+    default:
+        return MOE_EINVAL;
+    }
+    if (a.dw_dtype != MOE_F32 && a.dw_dtype != MOE_BF16) return MOE_EINVAL;
+    const bool wgrad = op == MOE_GEMM_DOWN_WGRAD || op == MOE_GEMM_UP_WGRAD;
+    if (c.T == 0 && !wgrad) return MOE_OK;
+    MOE_TRY(launch_schedule(c.E, a.counts, w.sched, stream));
+    MOE_TRY(launch_grouped_gemm(op, gemm_args(c, a, w.sched), stream));
+    return MOE_OK;
+}
+
+moe_status moe_swiglu(int32_t backward, int64_t M, int32_t I, const uint16_t *h, const float *da,
+                      uint16_t *out, hipStream_t stream)
+{
+    if (M < 0 || I <= 0) return MOE_EINVAL;
+    if (M == 0) return MOE_OK;
+    MOE_CHECK(check_ptrs({h, out}));
+    if (backward) MOE_CHECK(check_ptrs({da}));
+    MOE_TRY(launch_swiglu(backward, M, I, h, da, out, stream));
+    return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config *cfg, const float *o, const float *topk_w,
+                       const int32_t *pos, float *y, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    if (c.T == 0) return MOE_OK;
+    MOE_CHECK(check_ptrs({o, pos, y}));
+    MOE_CHECK(check_opt_ptr(topk_w));
+    MOE_TRY(launch_combine(c.T, c.k, c.H, o, topk_w, pos, y, stream));
+    return MOE_OK;
+}
+
+static moe_status check_saved(const moe_saved *s)
+{
+    if (!s) return MOE_EINVAL;
+    return check_ptrs({s->logits, s->topk_idx, s->topk_w, s->counts, s->offsets, s->row_map,
+                       s->pos, s->h, s->a});
+}
+
+moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                       const float *bias, const uint16_t *w1, const uint16_t *w2, float *y,
+                       float *aux, const moe_saved *saved, void *ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    if (!saved || !aux) return MOE_EINVAL;
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    if (c.T == 0) {
+        MOE_CHECK(check_ptrs({saved->counts, saved->offsets, aux}));
+        MOE_TRY(launch_fill_i32(saved->counts, c.E, 0, stream));
+        MOE_TRY(launch_fill_i32(saved->offsets, c.E + 1, 0, stream));
+        MOE_TRY(launch_fill_f32(aux, 1, 0.f, stream));
+        return MOE_OK;
+    }
+    MOE_CHECK(check_saved(saved));
+    MOE_CHECK(check_ptrs({x, w1, w2, y}));
+    MOE_CHECK(moe_router(cfg, x, Wr, bias, saved->logits, nullptr, saved->topk_idx,
+                         saved->topk_w, saved->counts, aux, ws, ws_bytes, stream));
+    MOE_TRY(launch_permute(c.T * c.k, c.E, saved->topk_idx, saved->counts, saved->offsets,
+                           saved->row_map, saved->pos, w.chunk_hist, stream));
+    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    moe_gemm_args a;
+    memset(&a, 0, sizeof a);
+    a.x = x;
+    a.w1 = w1;
+    a.w2 = w2;
+    a.counts = saved->counts;
+    a.offsets = saved->offsets;
+    a.row_map = saved->row_map;
+    a.topk_w = saved->topk_w;
+    a.h = saved->h;
+    a.a = saved->a;
+    a.o = w.o;
+    GemmArgs g = gemm_args(c, a, w.sched);
+    MOE_TRY(launch_grouped_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
+    MOE_TRY(launch_grouped_gemm(MOE_GEMM_DOWN, g, stream));
+    MOE_TRY(launch_combine(c.T, c.k, c.H, w.o, saved->topk_w, saved->pos, y, stream));
+    return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                        const float *Wr, const uint16_t *w1, const uint16_t *w2,
+                        const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
+                        float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
+                        int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
+    MOE_CHECK(check_saved(saved));
+    MOE_CHECK(check_ptrs({x, w1, w2, dy, dx, dlogits, dW1, dW2}));
+    MOE_CHECK(check_opt_ptr(Wr));
+    MOE_CHECK(check_opt_ptr(dWr));
+    MOE_CHECK(check_opt_ptr(d_aux));
+    size_t need = 0;
+    BwdWs w = carve_bwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    moe_gemm_args a;
+    memset(&a, 0, sizeof a);
+    a.x = x;
+    a.dy = dy;
+    a.w1 = w1;
+    a.w2 = w2;
+    a.counts = saved->counts;
+    a.offsets = saved->offsets;
+    a.row_map = saved->row_map;
+    a.topk_w = saved->topk_w;
+    a.h = saved->h;
+    a.a = saved->a;
+    a.dh = w.dh;
+    a.dw_part = w.dw_part;
+    a.dxp = w.dxp;
+    a.dW1 = dW1;
+    a.dW2 = dW2;
+    a.dw_dtype = dw_dtype;
+    a.dw_accumulate = dw_accumulate;
+    GemmArgs g = gemm_args(c, a, w.sched);
+    // GEMM2 stage: dgrad (+ SwiGLU backward, routing-weight row-dots), dW2
+    if (c.T > 0) MOE_TRY(launch_grouped_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
+    MOE_TRY(launch_grouped_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
+    // GEMM1 stage: dgrad, dW1
+    if (c.T > 0) MOE_TRY(launch_grouped_gemm(MOE_GEMM_UP_DGRAD, g, stream));
+    MOE_TRY(launch_grouped_gemm(MOE_GEMM_UP_WGRAD, g, stream));
+    if (c.T == 0) {
+        if (dWr && Wr) MOE_TRY(launch_fill_f32(dWr, (int64_t)c.E * c.H, 0.f, stream));
+        return MOE_OK;
+    }
+    // router: d logits, then dx = un-permute(dxp) + dlogits . Wr, dWr = dlogits^T . x
+    RouterBwdArgs rb;
+    rb.T = c.T;
+    rb.E = c.E;
+    rb.k = c.k;
+    rb.score = c.score;
+    rb.renorm = c.renorm;
+    rb.ncols = dgrad2_cols(c.I);
+    rb.scale = c.scale;
+    rb.aux_coeff = c.aux_coeff;
+    rb.logits = saved->logits;
+    rb.topk_w = saved->topk_w;
+    rb.dw_part = w.dw_part;
+    rb.d_aux = d_aux;
+    rb.topk_idx = saved->topk_idx;
+    rb.counts = saved->counts;
+    rb.pos = saved->pos;
+    rb.dlogits = dlogits;
+    MOE_TRY(launch_router_bwd(rb, stream));
+    MOE_TRY(launch_combine(c.T, c.k, c.H, w.dxp, nullptr, saved->pos, dx, stream));
+    if (Wr) {
+        MOE_TRY(launch_simt_gemm(c.T, c.H, c.E, dlogits, false, c.E, 1, Wr, false, 1, c.H, dx, c.H,
+                                 true, stream));
+        if (dWr)
+            MOE_TRY(launch_simt_gemm(c.E, c.H, c.T, dlogits, false, 1, c.E, x, true, 1, c.H, dWr,
+                                     c.H, false, stream));
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

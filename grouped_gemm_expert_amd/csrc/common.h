@@ -1,0 +1,141 @@
+// Internal header of libmoe: device helpers and the launch functions each
+// translation unit exports to the host layer (api.cpp).  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+MOE_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+MOE_DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+MOE_DEV uint32_t pack_bf2(float lo, float hi)
+{
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+MOE_DEV float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Ranking used everywhere in the router: larger value first, equal values
+// -> lower index first.  idx < 0 marks an empty candidate that never wins.
+MOE_DEV bool ranks_before(float va, int ia, float vb, int ib)
+{
+    if (ib < 0) return ia >= 0;
+    if (ia < 0) return false;
+    return va > vb || (va == vb && ia < ib);
+}
+
+// Wave-wide arg-max under ranks_before (butterfly; every lane gets the winner).
+MOE_DEV void wave_argmax(float &v, int &i)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float ov = __shfl_xor(v, off, 64);
+        int oi = __shfl_xor(i, off, 64);
+        if (ranks_before(ov, oi, v, i)) { v = ov; i = oi; }
+    }
+}
+
+MOE_DEV float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+MOE_DEV float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Launch functions (host side, one per kernel family).  All enqueue on
+// `stream` and return hipGetLastError() of the launch.
+// ---------------------------------------------------------------------------
+
+// fill int32 / fp32 buffers with a value (small kernels instead of memset,
+// so that captured graphs hold only kernel nodes)
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
+
+// fp32-accumulating SIMT GEMM: C[m,n] (=|+=) sum_k A(m,k) * B(n,k), with
+// A(m,k) = A[m*sam + k*sak], B(n,k) = B[n*sbn + k*sbk]; A/B bf16 or fp32.
+hipError_t launch_simt_gemm(int64_t Mr, int64_t Nc, int64_t K, const void *A, bool a_bf16,
+                            int64_t sam, int64_t sak, const void *B, bool b_bf16, int64_t sbn,
+                            int64_t sbk, float *C, int64_t ldc, bool accumulate, hipStream_t s);
+
+// router: selection + weights + counts + aux partial sums; then aux finalize
+struct RouterArgs {
+    int64_t T;
+    int32_t E, k, G, kg, score, renorm;
+    float scale, aux_coeff;
+    const float *logits, *bias;
+    float *sel, *topk_w;
+    int32_t *topk_idx, *counts;
+    float *aux, *prob_part;  // prob_part [nblk, E]
+};
+int64_t router_blocks(int64_t T);
+hipError_t launch_router(const RouterArgs &a, hipStream_t s);
+
+// permute: histogram / scan / stable scatter
+int64_t permute_chunks(int64_t M);
+hipError_t launch_permute(int64_t M, int32_t E, const int32_t *idx, int32_t *counts,
+                          int32_t *offsets, int32_t *row_map, int32_t *pos,
+                          int32_t *chunk_hist, hipStream_t s);
+
+// schedule: m-tile prefix sums for the grouped GEMMs and experts sorted by
+// count (descending, ties -> lower index) for the weight-gradient GEMMs
+struct Sched {
+    int32_t *mt_off256;  // [E+1]
+    int32_t *mt_off128;  // [E+1]
+    int32_t *order;      // [E]
+};
+hipError_t launch_schedule(int32_t E, const int32_t *counts, const Sched &sc, hipStream_t s);
+
+struct GemmArgs {
+    int64_t T, M;
+    int32_t E, k, H, I;
+    const int32_t *counts, *offsets, *row_map;
+    const float *topk_w;
+    const uint16_t *x, *dy, *w1, *w2;
+    uint16_t *h, *a, *dh;
+    float *o, *dw_part, *dxp;
+    void *dW1, *dW2;
+    int32_t dw_bf16, dw_acc;
+    Sched sched;
+};
+int32_t dgrad2_cols(int32_t I);
+hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
+
+// elementwise / reductions
+hipError_t launch_combine(int64_t T, int32_t k, int32_t H, const float *o, const float *w,
+                          const int32_t *pos, float *y, hipStream_t s);
+hipError_t launch_swiglu(int32_t backward, int64_t M, int32_t I, const uint16_t *h,
+                         const float *da, uint16_t *out, hipStream_t s);
+struct RouterBwdArgs {
+    int64_t T;
+    int32_t E, k, score, renorm, ncols;
+    float scale, aux_coeff;
+    const float *logits, *topk_w, *dw_part, *d_aux;
+    const int32_t *topk_idx, *counts, *pos;
+    float *dlogits;
+};
+hipError_t launch_router_bwd(const RouterBwdArgs &a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,321 @@
+// Router kernels: fp32 SIMT GEMM (router projection and its gradients),
+// selection + routing weights + counts + aux partials, aux finalize.
+//
+// Follows the MegaMoE page (Primus technical guide), intro: the fused router
+// is a score function, a group-limited top-k and an aux score.
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- fills ----
+__global__ void k_fill_i32(int32_t *p, int64_t n, int32_t v)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+__global__ void k_fill_f32(float *p, int64_t n, float v)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = ceil_div(n, 256);
+    if (blocks > 4096) blocks = 4096;
+    k_fill_i32<<<(unsigned)blocks, 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = ceil_div(n, 256);
+    if (blocks > 4096) blocks = 4096;
+    k_fill_f32<<<(unsigned)blocks, 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------- SIMT GEMM ----
+// 64x64 output tile, 16-deep k slices through LDS, 256 threads x 4x4 outputs.
+// Plain fp32 FMA accumulation in ascending k order per output.
+template <bool ABF, bool BBF>
+__global__ __launch_bounds__(256) void k_simt_gemm(int64_t Mr, int64_t Nc, int64_t K,
+                                                   const void *Av, int64_t sam, int64_t sak,
+                                                   const void *Bv, int64_t sbn, int64_t sbk,
+                                                   float *C, int64_t ldc, int accumulate)
+{
+    __shared__ float As[16][64 + 4];
+    __shared__ float Bs[16][64 + 4];
+    const int tid = threadIdx.x;
+    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    const int tm = tid / 16, tn = tid % 16;  // 16x16 threads, 4x4 each
+    float acc[4][4] = {};
+    for (int64_t k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int q = tid + i * 256;      // 0..1023 = 16 k x 64 rows
+            int kk = q / 64, r = q % 64;
+            int64_t m = m0 + r, n = n0 + r, kx = k0 + kk;
+            float av = 0.f, bv = 0.f;
+            if (m < Mr && kx < K) {
+                int64_t off = m * sam + kx * sak;
+                av = ABF ? bf2f(((const uint16_t *)Av)[off]) : ((const float *)Av)[off];
+            }
+            if (n < Nc && kx < K) {
+                int64_t off = n * sbn + kx * sbk;
+                bv = BBF ? bf2f(((const uint16_t *)Bv)[off]) : ((const float *)Bv)[off];
+            }
+            As[kk][r] = av;
+            Bs[kk][r] = bv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][tm * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tn * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int64_t m = m0 + tm * 4 + i;
+        if (m >= Mr) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int64_t n = n0 + tn * 4 + j;
+            if (n >= Nc) continue;
+            float v = acc[i][j];
+            if (accumulate) v += C[m * ldc + n];
+            C[m * ldc + n] = v;
+        }
+    }
+}
+
+hipError_t launch_simt_gemm(int64_t Mr, int64_t Nc, int64_t K, const void *A, bool a_bf16,
+                            int64_t sam, int64_t sak, const void *B, bool b_bf16, int64_t sbn,
+                            int64_t sbk, float *C, int64_t ldc, bool accumulate, hipStream_t s)
+{
+    if (Mr <= 0 || Nc <= 0) return hipSuccess;
+    dim3 grid((unsigned)ceil_div(Nc, 64), (unsigned)ceil_div(Mr, 64));
+    int acc = accumulate ? 1 : 0;
+    if (a_bf16 && !b_bf16)
+        k_simt_gemm<true, false><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
+    else if (!a_bf16 && b_bf16)
+        k_simt_gemm<false, true><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
+    else if (!a_bf16 && !b_bf16)
+        k_simt_gemm<false, false><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
+    else
+        k_simt_gemm<true, true><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
+    return hipGetLastError();
+}
+
+// -------------------------------------------------------------- router ----
+// One wavefront per token; a block holds 4 waves and walks TOK_PER_BLOCK
+// tokens, accumulating the aux column sums of its tokens in registers.
+// Expert e lives in lane e % 64, register slot e / 64.
+constexpr int RT_WAVES = 4;
+constexpr int RT_TOK_PER_WAVE = 8;
+constexpr int RT_TOK_PER_BLOCK = RT_WAVES * RT_TOK_PER_WAVE;
+
+int64_t router_blocks(int64_t T) { return ceil_div(T, RT_TOK_PER_BLOCK); }
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
+{
+    __shared__ float sS[RT_WAVES][64 * EPL];
+    __shared__ float red[RT_WAVES][64 * EPL];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = p.E, k = p.k;
+    float colsum[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) colsum[q] = 0.f;
+
+    for (int it = 0; it < RT_TOK_PER_WAVE; ++it) {
+        const int64_t t = (int64_t)blockIdx.x * RT_TOK_PER_BLOCK + wave * RT_TOK_PER_WAVE + it;
+        if (t >= p.T) break;  // wave-uniform
+        float l[EPL], S[EPL], sc[EPL];
+        bool ok[EPL];
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+            int e = lane + 64 * q;
+            ok[q] = e < E;
+            l[q] = ok[q] ? p.logits[t * E + e] : 0.f;
+            if (p.score == MOE_SOFTMAX) {
+                S[q] = l[q];
+            } else {
+                // fp32(sigmoid(l)) evaluated in double, then rounded once
+                float s = (float)(1.0 / (1.0 + exp(-(double)l[q])));
+                sc[q] = s;
+                S[q] = s + ((p.bias && ok[q]) ? p.bias[e] : 0.f);
+            }
+            if (p.sel && ok[q]) p.sel[t * E + e] = S[q];
+        }
+        // softmax probabilities (fp32) of all experts
+        if (p.score == MOE_SOFTMAX) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (ok[q]) m = fmaxf(m, l[q]);
+            m = wave_max(m);
+            float z = 0.f;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) {
+                sc[q] = ok[q] ? expf(l[q] - m) : 0.f;
+                z += sc[q];
+            }
+            z = wave_sum(z);
+            float rz = 1.0f / z;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) sc[q] *= rz;
+        }
+        // eligibility under the group limit
+        bool elig[EPL];
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) elig[q] = ok[q];
+        if (p.G > 1) {
+            const int gsz = E / p.G;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q)
+                if (ok[q]) sS[wave][lane + 64 * q] = S[q];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float gsv = 0.f;
+            int gid = -1;
+            if (lane < p.G) {
+                float b1 = 0.f, b2 = 0.f;
+                int i1 = -1, i2 = -1;
+                for (int e = lane * gsz; e < (lane + 1) * gsz; ++e) {
+                    float v = sS[wave][e];
+                    if (ranks_before(v, e, b1, i1)) {
+                        b2 = b1; i2 = i1; b1 = v; i1 = e;
+                    } else if (ranks_before(v, e, b2, i2)) {
+                        b2 = v; i2 = e;
+                    }
+                }
+                gsv = (i2 >= 0) ? b1 + b2 : b1;
+                gid = lane;
+            }
+            uint64_t kept = 0;
+            for (int r = 0; r < p.kg; ++r) {
+                float v = gsv;
+                int i = gid;
+                wave_argmax(v, i);
+                kept |= 1ull << i;
+                if (lane == i) gid = -1;
+            }
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) {
+                int e = lane + 64 * q;
+                elig[q] = ok[q] && ((kept >> (e / gsz)) & 1ull);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        // top-k by repeated wave arg-max
+        int my_idx = -1;
+        float my_val = 0.f;
+        float zsel = 0.f;
+        for (int j = 0; j < k; ++j) {
+            float bv = 0.f;
+            int bi = -1;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) {
+                int e = lane + 64 * q;
+                if (elig[q] && ranks_before(S[q], e, bv, bi)) { bv = S[q]; bi = e; }
+            }
+            wave_argmax(bv, bi);
+            // owner lane removes the winner and publishes its prob / sigmoid
+            float pv = 0.f;
+            if ((bi & 63) == lane) {
+#pragma unroll
+                for (int q = 0; q < EPL; ++q)
+                    if (lane + 64 * q == bi) { elig[q] = false; pv = sc[q]; }
+            }
+            pv = __shfl(pv, bi & 63, 64);
+            zsel += pv;
+            if (lane == j) { my_idx = bi; my_val = pv; }
+        }
+        if (lane < k) {
+            float w;
+            if (p.score == MOE_SOFTMAX) w = p.renorm ? my_val / zsel : my_val;
+            else w = p.scale * my_val / zsel;
+            p.topk_idx[t * k + lane] = my_idx;
+            p.topk_w[t * k + lane] = w;
+            if (my_idx >= 0) atomicAdd(&p.counts[my_idx], 1);
+        }
+        // aux probabilities: softmax p, or s / sum_e s for the sigmoid router
+        if (p.score == MOE_SOFTMAX) {
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) colsum[q] += sc[q];
+        } else {
+            float z = 0.f;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) z += ok[q] ? sc[q] : 0.f;
+            z = wave_sum(z);
+            float rz = 1.0f / z;
+#pragma unroll
+            for (int q = 0; q < EPL; ++q) colsum[q] += ok[q] ? sc[q] * rz : 0.f;
+        }
+    }
+    // block partial of the column sums: fixed order over the waves
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) red[wave][lane + 64 * q] = colsum[q];
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < RT_WAVES; ++w) v += red[w][e];
+        p.prob_part[(int64_t)blockIdx.x * E + e] = v;
+    }
+}
+
+// aux = coeff * E / (k T^2) * sum_e counts[e] * P[e],  P[e] = sum of the
+// block partials in block order.  One block of 1024 threads.
+__global__ __launch_bounds__(1024) void k_aux_finalize(RouterArgs p, int64_t nblk)
+{
+    __shared__ double red[1024];
+    double v = 0.0;
+    for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+        float P = 0.f;
+        for (int64_t b = 0; b < nblk; ++b) P += p.prob_part[b * p.E + e];
+        v += (double)p.counts[e] * (double)P;
+    }
+    red[threadIdx.x] = v;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        double T = (double)p.T;
+        p.aux[0] = (float)((double)p.aux_coeff * (double)p.E / ((double)p.k * T * T) * red[0]);
+    }
+}
+
+hipError_t launch_router(const RouterArgs &a, hipStream_t s)
+{
+    hipError_t err = launch_fill_i32(a.counts, a.E, 0, s);
+    if (err != hipSuccess) return err;
+    int64_t nblk = router_blocks(a.T);
+    int epl = (int)ceil_div(a.E, 64);
+    if (epl <= 1) k_router_select<1><<<(unsigned)nblk, 256, 0, s>>>(a);
+    else if (epl <= 2) k_router_select<2><<<(unsigned)nblk, 256, 0, s>>>(a);
+    else if (epl <= 4) k_router_select<4><<<(unsigned)nblk, 256, 0, s>>>(a);
+    else if (epl <= 8) k_router_select<8><<<(unsigned)nblk, 256, 0, s>>>(a);
+    else k_router_select<16><<<(unsigned)nblk, 256, 0, s>>>(a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k_aux_finalize<<<1, 1024, 0, s>>>(a, nblk);
+    return hipGetLastError();
+}
+
+}  // namespace moe

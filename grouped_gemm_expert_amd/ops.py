@@ -1,0 +1,230 @@
+"""Python binding of libmoe (include/moe.h): argument marshalling only.
+
+Every function here has the name of a C entry point, takes torch tensors that
+already live on the GPU, passes their device pointers and the current HIP
+stream to the library, and raises if the library reports an error.  No step of
+the expert path runs in Python or in PyTorch: torch only owns the memory and
+the stream.  If libmoe.so is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_F32, MOE_BF16 = 0, 1
+(MOE_GEMM_UP_SWIGLU, MOE_GEMM_DOWN, MOE_GEMM_DOWN_DGRAD, MOE_GEMM_UP_DGRAD,
+ MOE_GEMM_DOWN_WGRAD, MOE_GEMM_UP_WGRAD) = range(6)
+
+_P = ctypes.c_void_p
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("renorm", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("aux_coeff", ctypes.c_float)]
+
+
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("logits", "topk_idx", "topk_w", "counts", "offsets",
+                                  "row_map", "pos", "h", "a")]
+
+
+class MoeGemmArgs(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "dy", "w1", "w2", "counts", "offsets", "row_map",
+                                  "topk_w", "h", "a", "o", "dh", "dw_part", "dxp", "dW1",
+                                  "dW2")] + [("dw_dtype", ctypes.c_int32),
+                                             ("dw_accumulate", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise MoeError(f"{_LIB_PATH} is missing: build it with "
+                       "`python -m grouped_gemm_expert_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    S = ctypes.c_int  # moe_status
+    CFG = ctypes.POINTER(MoeConfig)
+    sz = ctypes.c_size_t
+    lib.moe_status_string.argtypes = [S]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_char_p
+    lib.moe_check_config.argtypes = [CFG]
+    lib.moe_check_config.restype = S
+    lib.moe_workspace_size.argtypes = [CFG, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.moe_workspace_size.restype = S
+    lib.moe_dw_part_cols.argtypes = [CFG]
+    lib.moe_dw_part_cols.restype = ctypes.c_int32
+    lib.moe_router.argtypes = [CFG] + [_P] * 9 + [_P, sz, _P]
+    lib.moe_router.restype = S
+    lib.moe_permute.argtypes = [CFG] + [_P] * 5 + [_P, sz, _P]
+    lib.moe_permute.restype = S
+    lib.moe_grouped_gemm.argtypes = [ctypes.c_int32, CFG, ctypes.POINTER(MoeGemmArgs), _P, sz, _P]
+    lib.moe_grouped_gemm.restype = S
+    lib.moe_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
+    lib.moe_swiglu.restype = S
+    lib.moe_combine.argtypes = [CFG, _P, _P, _P, _P, _P]
+    lib.moe_combine.restype = S
+    lib.moe_forward.argtypes = [CFG] + [_P] * 7 + [ctypes.POINTER(MoeSaved), _P, sz, _P]
+    lib.moe_forward.restype = S
+    lib.moe_backward.argtypes = ([CFG, ctypes.POINTER(MoeSaved)] + [_P] * 11
+                                 + [ctypes.c_int32, ctypes.c_int32, _P, sz, _P])
+    lib.moe_backward.restype = S
+    return lib
+
+
+_lib = _load()
+
+SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspace_size",
+           "moe_dw_part_cols", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_swiglu",
+           "moe_combine", "moe_forward", "moe_backward")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise MoeError("tensor arguments must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MoeError(f"{what}: {_lib.moe_status_string(status).decode()} (status {status})")
+
+
+def config(T, H, I, E, k, n_groups=1, topk_groups=1, score="softmax", renorm=False,
+           scale=1.0, aux_coeff=0.01) -> MoeConfig:
+    sc = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}.get(score, score)
+    return MoeConfig(int(T), int(H), int(I), int(E), int(k), int(n_groups), int(topk_groups),
+                     int(sc), int(bool(renorm)), float(scale), float(aux_coeff))
+
+
+def config_from_workload(w, T=None) -> MoeConfig:
+    return config(w.T if T is None else T, w.H, w.I, w.E, w.k, w.n_groups, w.topk_groups,
+                  w.score, w.renorm, w.scale, w.aux_coeff)
+
+
+def moe_version() -> str:
+    return _lib.moe_version().decode()
+
+
+def moe_check_config(cfg: MoeConfig) -> int:
+    return int(_lib.moe_check_config(ctypes.byref(cfg)))
+
+
+def moe_workspace_size(cfg: MoeConfig):
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(f), ctypes.byref(b)),
+           "moe_workspace_size")
+    return int(f.value), int(b.value)
+
+
+def moe_dw_part_cols(cfg: MoeConfig) -> int:
+    return int(_lib.moe_dw_part_cols(ctypes.byref(cfg)))
+
+
+def workspace(cfg: MoeConfig, which: str = "fwd", device="cuda") -> torch.Tensor:
+    f, b = moe_workspace_size(cfg)
+    n = f if which == "fwd" else b
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_router(cfg, x, Wr, bias, logits, sel_scores, topk_idx, topk_w, counts, aux, ws,
+               stream=None):
+    _check(_lib.moe_router(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias), _ptr(logits),
+                           _ptr(sel_scores), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                           _ptr(aux), _ptr(ws), ws.numel(), _stream(stream)), "moe_router")
+
+
+def moe_permute(cfg, topk_idx, counts, offsets, row_map, pos, ws, stream=None):
+    _check(_lib.moe_permute(ctypes.byref(cfg), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                            _ptr(row_map), _ptr(pos), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_permute")
+
+
+def moe_grouped_gemm(op, cfg, ws, stream=None, dw_dtype=MOE_F32, dw_accumulate=False, **tensors):
+    args = MoeGemmArgs()
+    for name, t in tensors.items():
+        if name not in dict(MoeGemmArgs._fields_):
+            raise MoeError(f"unknown grouped-GEMM argument {name}")
+        setattr(args, name, None if t is None else t.data_ptr())
+    args.dw_dtype = dw_dtype
+    args.dw_accumulate = int(bool(dw_accumulate))
+    _check(_lib.moe_grouped_gemm(int(op), ctypes.byref(cfg), ctypes.byref(args), _ptr(ws),
+                                 ws.numel(), _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_swiglu(backward, h, out, da=None, stream=None):
+    M = h.shape[0]
+    I = h.shape[1] // 2
+    _check(_lib.moe_swiglu(int(bool(backward)), M, I, _ptr(h), _ptr(da), _ptr(out),
+                           _stream(stream)), "moe_swiglu")
+
+
+def moe_combine(cfg, o, topk_w, pos, y, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(cfg), _ptr(o), _ptr(topk_w), _ptr(pos), _ptr(y),
+                            _stream(stream)), "moe_combine")
+
+
+def _saved_struct(saved: dict) -> MoeSaved:
+    s = MoeSaved()
+    for name, _ in MoeSaved._fields_:
+        setattr(s, name, saved[name].data_ptr())
+    return s
+
+
+def alloc_saved(cfg: MoeConfig, device="cuda") -> dict:
+    """The forward's saved tensors (caller-owned; see moe_saved in moe.h)."""
+    T, E, k, I = cfg.T, cfg.E, cfg.k, cfg.I
+    M = T * k
+    i32 = dict(dtype=torch.int32, device=device)
+    return {
+        "logits": torch.empty((T, E), dtype=torch.float32, device=device),
+        "topk_idx": torch.empty((T, k), **i32),
+        "topk_w": torch.empty((T, k), dtype=torch.float32, device=device),
+        "counts": torch.empty((E,), **i32),
+        "offsets": torch.empty((E + 1,), **i32),
+        "row_map": torch.empty((max(M, 1),), **i32),
+        "pos": torch.empty((max(M, 1),), **i32),
+        "h": torch.empty((max(M, 1), 2 * I), dtype=torch.bfloat16, device=device),
+        "a": torch.empty((max(M, 1), I), dtype=torch.bfloat16, device=device),
+    }
+
+
+def moe_forward(cfg, x, Wr, bias, w1, w2, y, aux, saved: dict, ws, stream=None):
+    s = _saved_struct(saved)
+    _check(_lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias), _ptr(w1),
+                            _ptr(w2), _ptr(y), _ptr(aux), ctypes.byref(s), _ptr(ws), ws.numel(),
+                            _stream(stream)), "moe_forward")
+
+
+def moe_backward(cfg, saved: dict, x, Wr, w1, w2, dy, d_aux, dx, dlogits, dWr, dW1, dW2, ws,
+                 dw_accumulate=False, stream=None):
+    s = _saved_struct(saved)
+    dw_dtype = MOE_BF16 if dW1.dtype == torch.bfloat16 else MOE_F32
+    _check(_lib.moe_backward(ctypes.byref(cfg), ctypes.byref(s), _ptr(x), _ptr(Wr), _ptr(w1),
+                             _ptr(w2), _ptr(dy), _ptr(d_aux), _ptr(dx), _ptr(dlogits), _ptr(dWr),
+                             _ptr(dW1), _ptr(dW2), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
+                             ws.numel(), _stream(stream)), "moe_backward")

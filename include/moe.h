@@ -1,0 +1,274 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert-path library (libmoe.so).
+ *
+ * The path (page "MegaMoE", Primus technical guide, intro): a fused router
+ * (score function, group-limited top-k, load-balancing aux score), token
+ * dispatch, grouped GEMM1 over w1 [E, 2I, H] (gate rows then up rows), SwiGLU,
+ * grouped GEMM2 over w2 [E, H, I], and a top-k-weighted combine; plus the
+ * backward, which produces dW2 before dW1 (section "Design: two stages +
+ * weight modules").  On one GPU, dispatch and combine are local permutations.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers, row-major, densely packed, and
+ *    16-byte aligned.  bf16 tensors are passed as uint16_t bit patterns.
+ *  - The caller owns every buffer, including the workspace `ws` (size from
+ *    moe_workspace_size).  The library never allocates, frees, or
+ *    synchronises: each call only enqueues kernels on `stream` and returns.
+ *    No device-to-host copy or host wait happens inside any call, so the
+ *    calls can be captured into a HIP graph (the MegaMoE page, "Example 2",
+ *    describes the expert path as sync-free for that reason).
+ *  - Errors are reported as moe_status; nothing throws across the ABI.
+ *    Arguments are validated on the host from the config and the pointers
+ *    only (device data is never read back): unsupported shapes return
+ *    MOE_EUNSUPPORTED (the page's "Required" section: the layer asserts on
+ *    anything it does not support), bad arguments MOE_EINVAL, a too-small
+ *    workspace MOE_EWORKSPACE, and a failed kernel launch MOE_EHIP.
+ *    T == 0 is a valid no-op that returns MOE_OK.
+ *  - Indices produced or consumed (topk_idx, offsets, row_map, pos) are int32.
+ *    A caller-supplied topk_idx with entries outside [0, E) is undefined
+ *    behaviour.
+ *  - Notation: T tokens, H hidden, I expert intermediate size, E experts,
+ *    k experts per token, M = T*k routed rows.  Flat slot f = t*k + j.
+ *    Sorted row r: rows grouped by expert in ascending expert order, and
+ *    inside one expert by ascending flat slot (a stable order).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,        /* null / misaligned pointer, bad enum, negative size */
+    MOE_EUNSUPPORTED = 2,  /* shape or option outside what the kernels implement */
+    MOE_EWORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_size() */
+    MOE_EHIP = 4           /* a kernel launch failed */
+} moe_status;
+
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };      /* router score function */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };             /* dtype of weight gradients */
+
+/*
+ * Layer configuration (host struct, read during the call only).
+ *   score        MOE_SOFTMAX: p = softmax(logits); weights are p of the
+ *                selected experts, divided by their sum when renorm != 0.
+ *                MOE_SIGMOID: s = sigmoid(logits); weights are
+ *                scale * s_sel / sum(s_sel).  An optional per-expert bias
+ *                enters the selection score only (s + bias), never a weight.
+ *   n_groups     experts form n_groups contiguous groups of E/n_groups; when
+ *                n_groups > 1, each group is scored by the sum of its two
+ *                best selection scores, the topk_groups best groups are kept
+ *                and only their experts can be chosen (group-limited top-k).
+ *   aux_coeff    load-balancing aux loss
+ *                aux = aux_coeff * E / (k*T^2) * sum_e counts[e] * sum_t p[t,e]
+ *                with p the softmax probabilities, or s / sum_e s for sigmoid.
+ * Ties in any ranking go to the lower index (expert or group).
+ * Supported: 1 <= k <= E <= 1024, k <= 32, n_groups divides E,
+ * 1 <= topk_groups <= n_groups, k <= topk_groups * E / n_groups,
+ * H % 64 == 0, I % 64 == 0, T * k < 2^31.
+ */
+typedef struct {
+    int64_t T;
+    int32_t H, I, E, k;
+    int32_t n_groups, topk_groups;
+    int32_t score;
+    int32_t renorm;
+    float scale;
+    float aux_coeff;
+} moe_config;
+
+/*
+ * Tensors the forward writes and the backward reads (all device pointers,
+ * caller-allocated with the sizes below).
+ *   logits   [T,E]  fp32  router logits (input when the router weight is NULL)
+ *   topk_idx [T,k]  int32 chosen experts, best first
+ *   topk_w   [T,k]  fp32  routing weights
+ *   counts   [E]    int32 rows per expert
+ *   offsets  [E+1]  int32 exclusive prefix sum of counts
+ *   row_map  [M]    int32 sorted row -> flat slot
+ *   pos      [M]    int32 flat slot -> sorted row
+ *   h        [M,2I] bf16  GEMM1 output per sorted row: gate | up
+ *   a        [M,I]  bf16  SwiGLU output per sorted row
+ */
+typedef struct {
+    float *logits;
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *row_map;
+    int32_t *pos;
+    uint16_t *h;
+    uint16_t *a;
+} moe_saved;
+
+const char *moe_status_string(moe_status s);
+
+/* Library version string and the gfx target it was built for. */
+const char *moe_version(void);
+
+/* Validate cfg (returns the status moe_forward would return for it). */
+moe_status moe_check_config(const moe_config *cfg);
+
+/*
+ * Workspace bytes needed by moe_forward (fwd_bytes) and moe_backward
+ * (bwd_bytes); either output pointer may be NULL.  The router, permute,
+ * grouped-GEMM and combine entry points need at most fwd_bytes.
+ */
+moe_status moe_workspace_size(const moe_config *cfg, size_t *fwd_bytes, size_t *bwd_bytes);
+
+/*
+ * Fused router (MegaMoE page, intro: score function + group-limited top-k +
+ * aux score).
+ *   x          [T,H] bf16 tokens (read only when Wr != NULL)
+ *   Wr         [E,H] fp32 router weight, or NULL: then `logits` is an input
+ *   bias       [E]   fp32 selection-only bias, or NULL
+ *   logits     [T,E] fp32: output (x . Wr^T) when Wr != NULL, else input
+ *   sel_scores [T,E] fp32 selection scores, or NULL: S = logits (softmax) or
+ *              fp32(sigmoid(logits)) + bias (sigmoid).  The top-k is decided
+ *              on exactly these fp32 values.
+ *   topk_idx   [T,k] int32 out;  topk_w [T,k] fp32 out
+ *   counts     [E] int32 out (rows routed to each expert)
+ *   aux        [1] fp32 out (load-balancing aux loss)
+ */
+moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                      const float *bias, float *logits, float *sel_scores,
+                      int32_t *topk_idx, float *topk_w, int32_t *counts, float *aux,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dispatch bookkeeping (the one-GPU form of the MegaMoE token dispatch):
+ * histogram, exclusive scan and a stable scatter of the flat slots.
+ *   topk_idx [T,k] int32 in
+ *   counts [E], offsets [E+1], row_map [M], pos [M] int32 out
+ * Bit-exact and deterministic.
+ */
+moe_status moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *counts,
+                       int32_t *offsets, int32_t *row_map, int32_t *pos,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped GEMMs over the sorted rows of each expert (bf16 MFMA, fp32
+ * accumulation).  Expert e owns sorted rows [offsets[e], offsets[e+1]);
+ * empty experts are allowed.  Rows that come from token tensors are read
+ * through row_map (token = row_map[r] / k): dispatch is fused into the load.
+ *
+ *   MOE_GEMM_UP_SWIGLU   h[r,:] = x[tok(r)] . w1[e]^T  (2I columns, fp32
+ *                        accumulate); a[r,i] = silu(g)*u computed from the
+ *                        fp32 accumulators g = col i, u = col I+i.
+ *                        Writes h (bf16, may be NULL) and a (bf16).
+ *   MOE_GEMM_DOWN        o[r,:] = a[r] . w2[e]^T       -> o [M,H] fp32
+ *   MOE_GEMM_DOWN_DGRAD  dA'[r,i] = dy[tok(r)] . w2[e][:,i]; then
+ *                        dw_part[r, n] = partial row-dot <dA'[r], a[r]> over
+ *                        column tile n, and with dA = topk_w[slot(r)] * dA':
+ *                        dh[r,i] = dA*u*sig(g)*(1+g*(1-sig(g))),
+ *                        dh[r,I+i] = dA*silu(g)   (g,u from h)  -> dh bf16
+ *   MOE_GEMM_UP_DGRAD    dxp[r,:] = dh[r] . w1[e]       -> dxp [M,H] fp32
+ *   MOE_GEMM_DOWN_WGRAD  dW2[e] (+)= sum_r (topk_w * dy[tok(r)])^T a[r]
+ *   MOE_GEMM_UP_WGRAD    dW1[e] (+)= sum_r dh[r]^T x[tok(r)]
+ * Weight gradients are fp32 or bf16 (dw_dtype) and overwritten
+ * (dw_accumulate = 0; empty experts get exact zeros) or accumulated into
+ * (dw_accumulate = 1; empty experts untouched).
+ * dw_part has moe_dw_part_cols(cfg) columns per row.
+ */
+enum {
+    MOE_GEMM_UP_SWIGLU = 0,
+    MOE_GEMM_DOWN = 1,
+    MOE_GEMM_DOWN_DGRAD = 2,
+    MOE_GEMM_UP_DGRAD = 3,
+    MOE_GEMM_DOWN_WGRAD = 4,
+    MOE_GEMM_UP_WGRAD = 5
+};
+
+typedef struct {
+    const uint16_t *x;        /* [T,H]  bf16 tokens */
+    const uint16_t *dy;       /* [T,H]  bf16 upstream gradient */
+    const uint16_t *w1;       /* [E,2I,H] bf16 */
+    const uint16_t *w2;       /* [E,H,I]  bf16 */
+    const int32_t *counts;    /* [E] */
+    const int32_t *offsets;   /* [E+1] */
+    const int32_t *row_map;   /* [M] */
+    const float *topk_w;      /* [T,k] */
+    uint16_t *h;              /* [M,2I] bf16 */
+    uint16_t *a;              /* [M,I]  bf16 */
+    float *o;                 /* [M,H]  fp32 */
+    uint16_t *dh;             /* [M,2I] bf16 */
+    float *dw_part;           /* [M, moe_dw_part_cols] fp32 */
+    float *dxp;               /* [M,H]  fp32 */
+    void *dW1;                /* [E,2I,H] fp32 or bf16 */
+    void *dW2;                /* [E,H,I]  fp32 or bf16 */
+    int32_t dw_dtype;         /* MOE_F32 | MOE_BF16 */
+    int32_t dw_accumulate;    /* 0 overwrite, 1 accumulate */
+} moe_gemm_args;
+
+int32_t moe_dw_part_cols(const moe_config *cfg);
+
+moe_status moe_grouped_gemm(int32_t op, const moe_config *cfg, const moe_gemm_args *args,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Stand-alone SwiGLU (silu(gate) * up, MegaMoE page "Required": gated SwiGLU
+ * with SiLU) on bf16 h [M,2I] (gate | up):
+ *   backward == 0:  out[r,i] = silu(g)*u                       (out [M,I] bf16)
+ *   backward == 1:  da [M,I] fp32 in;  out [M,2I] bf16 =
+ *                   (da*u*sig(g)*(1+g*(1-sig(g))) | da*silu(g))
+ * The fused path computes the forward from fp32 accumulators inside
+ * MOE_GEMM_UP_SWIGLU; this entry exists for unfused use and testing.
+ */
+moe_status moe_swiglu(int32_t backward, int64_t M, int32_t I, const uint16_t *h,
+                      const float *da, uint16_t *out, hipStream_t stream);
+
+/*
+ * Weighted combine (MegaMoE page, intro: the combine is a weighted reduce):
+ *   y[t,:] = sum_{j=0..k-1} topk_w[t,j] * o[pos[t*k+j], :]   (j ascending,
+ *   fp32, deterministic).  topk_w may be NULL (all weights 1: the
+ *   un-permute reduce of the backward).  o [M,H] fp32, y [T,H] fp32.
+ */
+moe_status moe_combine(const moe_config *cfg, const float *o, const float *topk_w,
+                       const int32_t *pos, float *y, hipStream_t stream);
+
+/*
+ * Whole forward: router (unless Wr == NULL, then saved->logits is the input),
+ * permute, GEMM1 + SwiGLU, GEMM2, combine.
+ *   x [T,H] bf16, Wr [E,H] fp32 or NULL, bias [E] fp32 or NULL,
+ *   w1 [E,2I,H] bf16, w2 [E,H,I] bf16  in
+ *   y [T,H] fp32, aux [1] fp32, and every tensor of `saved`  out
+ */
+moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                       const float *bias, const uint16_t *w1, const uint16_t *w2,
+                       float *y, float *aux, const moe_saved *saved,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Whole backward of loss = <dy, y> + d_aux * aux, in the order of the MegaMoE
+ * page's design section: the GEMM2 stage first (dW2), then the GEMM1 stage
+ * (dW1), then the router.
+ *   saved      the forward's saved tensors
+ *   dy [T,H] bf16, d_aux [1] fp32 device scalar or NULL (= 0)
+ *   dx [T,H] fp32 out: expert path plus router path (dlogits . Wr) when
+ *              Wr != NULL
+ *   dlogits [T,E] fp32 out
+ *   dWr [E,H] fp32 out, or NULL (skipped; also skipped when Wr == NULL)
+ *   dW1 [E,2I,H], dW2 [E,H,I] fp32 or bf16 (dw_dtype), overwritten or
+ *              accumulated (dw_accumulate) as in moe_grouped_gemm
+ * The selection itself and the bias carry no gradient; counts are constants
+ * of the aux loss.
+ */
+moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                        const float *Wr, const uint16_t *w1, const uint16_t *w2,
+                        const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
+                        float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
+                        int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

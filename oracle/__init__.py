@@ -21,6 +21,7 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
                           pages name a "standard aux_loss" without a formula).
   forward              -- pinned: E=1/k=1 dense SwiGLU MLP, token-permutation
                           invariance, linearity in w2
+  expert_rows          -- pinned: y = sum_j w_j o_j against forward
   backward_tokens, weight_grads, weight_grad_elements, router_weight_grad
                        -- pinned: central finite differences of the forward and
                           an independent torch fp64 autograd formulation
@@ -79,6 +80,7 @@ def _load():
         "oracle_weight_grad_elements": [i64, i32, i32, i32, P, P, P, P, P, P, i64,
                                         P, P, P, P, P],
         "oracle_router_weight_grad": [i64, i32, i32, P, P, P],
+        "oracle_expert_rows": [i32, i32, i32, P, P, P, P, i64, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -248,6 +250,23 @@ def weight_grad_elements(x, w1, w2, idx, w, dy, which, ee, rr, cc) -> np.ndarray
     _load().oracle_weight_grad_elements(T, H, I, k, _p(x), _p(w1), _p(w2), _p(idx), _p(w), _p(dy),
                                         which.shape[0], _p(which), _p(ee), _p(rr), _p(cc), _p(out))
     return out
+
+
+def expert_rows(x, w1, w2, idx, slots):
+    """Per flat slot f = t*k + j: (g, u, a, o) in double, see moe_oracle.c."""
+    x = _c(x, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    idx = _c(idx, np.int32)
+    sl = _c(np.asarray(slots), np.int64)
+    H = x.shape[1]
+    I = w2.shape[2]
+    k = idx.shape[1]
+    n = sl.shape[0]
+    g = np.empty((n, I)); u = np.empty((n, I)); a = np.empty((n, I)); o = np.empty((n, H))
+    _load().oracle_expert_rows(H, I, k, _p(x), _p(w1), _p(w2), _p(idx), n, _p(sl), _p(g), _p(u),
+                               _p(a), _p(o))
+    return g, u, a, o
 
 
 def router_weight_grad(x, dlogits64) -> np.ndarray:

@@ -589,3 +589,25 @@ void oracle_router_weight_grad(int64_t T, int32_t H, int32_t E,
             dWr[(int64_t)e * H + h] = acc;
         }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Per-slot intermediates of the expert MLP for listed flat slots f = t*k+j  */
+/* (e = idx[f]): g [n,I], u [n,I], a [n,I], o [n,H] in double, where         */
+/* g, u are the gate / up halves of x_t . w1[e]^T, a = silu(g) * u and       */
+/* o = a . w2[e]^T (the expert output before the routing weight).           */
+/* ------------------------------------------------------------------------ */
+void oracle_expert_rows(int32_t H, int32_t I, int32_t k, const uint16_t *x,
+                        const uint16_t *w1, const uint16_t *w2,
+                        const int32_t *idx, int64_t n, const int64_t *slots,
+                        double *g, double *u, double *a, double *o)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n; ++q) {
+        int64_t f = slots[q];
+        int64_t t = f / k;
+        int32_t e = idx[f];
+        expert_mlp(H, I, x + t * H, w1 + (int64_t)e * 2 * I * H,
+                   w2 + (int64_t)e * H * I, g + q * I, u + q * I, a + q * I,
+                   o + q * H);
+    }
+}

@@ -1,0 +1,189 @@
+"""End-to-end GPU parity of moe_forward / moe_backward against the oracle on
+seeded inputs: forward output, aux loss, dx (expert and router paths),
+dlogits, dW1, dW2, dWr, plus the edge cases of the method."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from grouped_gemm_expert_amd import inputs
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+E2E = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed"]
+
+
+def _oracle_logits32(w, dc):
+    if dc["Wr"] is None:
+        return dc["logits"].numpy(), dc["logits"].double().numpy()
+    l64 = oracle.logits(hz.bits(dc["x"]), dc["Wr"].numpy())
+    return l64.astype(np.float32), l64
+
+
+def _compare_all(w, dc, got, tol_f=hz.FWD_TOL, tol_g=hz.GRAD_TOL, backward=True, d_aux=1.0):
+    """Oracle on the fp32 logits the GPU routed on (generated or the oracle's own)."""
+    l32, l64 = _oracle_logits32(w, dc)
+    bias = None if dc["bias"] is None else dc["bias"].numpy()
+    r = oracle.route(l64, score=hz.SCORE[w.score], k=w.k, n_groups=w.n_groups,
+                     topk_groups=w.topk_groups, bias=bias, renorm=w.renorm, scale=w.scale,
+                     coeff=w.aux_coeff, logits32=l32)
+    sv = got["saved"]
+    assert np.array_equal(sv["topk_idx"].cpu().numpy(), r["idx"])
+    assert np.array_equal(sv["counts"].cpu().numpy(), r["counts"])
+    assert np.array_equal(sv["offsets"].cpu().numpy(), r["offsets"])
+    if w.T:
+        assert np.array_equal(sv["row_map"].cpu().numpy()[:w.M], r["row_map"])
+        assert np.array_equal(sv["pos"].cpu().numpy()[:w.M], r["pos"])
+    ref = hz.oracle_forward_backward(w, dc, r, l64, backward=backward, d_aux=d_aux)
+    hz.assert_close(f"{w.name} y", got["y"].cpu().numpy(), ref["y"], tol_f)
+    aux_g = float(got["aux"].cpu())
+    assert abs(aux_g - r["aux"]) <= 1e-4 * abs(r["aux"]) + 1e-9, (aux_g, r["aux"])
+    if not backward:
+        return r, ref
+    hz.assert_close(f"{w.name} dx", got["dx"].cpu().numpy(), ref["dx"], tol_g)
+    hz.assert_close(f"{w.name} dlogits", got["dlogits"].cpu().numpy(), ref["dlogits"], tol_g)
+    hz.assert_close(f"{w.name} dW1", got["dW1"].float().cpu().numpy(), ref["dW1"], tol_g)
+    hz.assert_close(f"{w.name} dW2", got["dW2"].float().cpu().numpy(), ref["dW2"], tol_g)
+    if got.get("dWr") is not None:
+        hz.assert_close(f"{w.name} dWr", got["dWr"].cpu().numpy(), ref["dWr"], tol_g)
+    return r, ref
+
+
+@pytest.mark.parametrize("name", E2E)
+def test_forward_backward_matches_oracle(name):
+    w = inputs.WORKLOADS[name]
+    hz.say(f"e2e {inputs.describe(w)}")
+    dc = inputs.make_inputs(w)
+    d = hz.to_device(dc)
+    l32, _ = _oracle_logits32(w, dc)
+    got = hz.run_hip(w, d, logits_in=torch.from_numpy(l32).cuda() if dc["Wr"] is not None else None)
+    torch.cuda.synchronize()
+    _compare_all(w, dc, got)
+
+
+@pytest.mark.parametrize("name", ["mid_softmax", "mid_sigmoid"])
+def test_forward_with_router_weight_path(name):
+    """Full forward from the router weight (the GPU forms its own logits);
+    values are compared on tokens routed identically."""
+    w = inputs.WORKLOADS[name]
+    hz.say(f"e2e-Wr {inputs.describe(w)}")
+    dc = inputs.make_inputs(w)
+    d = hz.to_device(dc)
+    got = hz.run_hip(w, d)
+    torch.cuda.synchronize()
+    l64, r = hz.oracle_route(w, dc)
+    ig = got["saved"]["topk_idx"].cpu().numpy()
+    same = (ig == r["idx"]).all(1)
+    hz.say(f"identically routed tokens: {int(same.sum())} of {w.T}")
+    assert same.mean() >= 0.99
+    toks = np.nonzero(same)[0]
+    ref = hz.oracle_forward_backward(w, dc, r, l64, toks=toks)
+    hz.assert_close(f"{name} y(Wr path)", got["y"].cpu().numpy()[toks], ref["y"], hz.FWD_TOL)
+    hz.assert_close(f"{name} dx(Wr path)", got["dx"].cpu().numpy()[toks], ref["dx"], hz.GRAD_TOL)
+
+
+def _wl(base, **kw):
+    return dataclasses.replace(inputs.WORKLOADS[base], **kw)
+
+
+EDGE = {
+    "single_token": _wl("mid_softmax", T=1),
+    "one_expert_top1": _wl("mid_softmax", E=1, k=1, T=300),
+    "k_equals_E": _wl("mid_softmax", E=8, k=8, T=200),
+    "sigmoid_no_groups": _wl("mid_sigmoid", n_groups=1, topk_groups=1, T=300),
+    "wide_tile_tail": _wl("mid_softmax", H=320, I=448, T=333, E=4, k=2),
+    "small_dims": _wl("mid_softmax", H=64, I=64, T=130, E=4, k=2),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_edge_cases(case):
+    w = EDGE[case]
+    hz.say(f"edge {case}: {inputs.describe(w)}")
+    dc = inputs.make_inputs(w, seed=1)
+    d = hz.to_device(dc)
+    l32, _ = _oracle_logits32(w, dc)
+    got = hz.run_hip(w, d, logits_in=torch.from_numpy(l32).cuda() if dc["Wr"] is not None else None)
+    torch.cuda.synchronize()
+    _compare_all(w, dc, got)
+
+
+def test_all_tokens_to_one_expert_and_empty_experts():
+    """Logits that send every token's first choice to expert 3: most experts
+    are empty; their dW must be exact zeros (overwrite mode)."""
+    w = _wl("mid_skewed", E=16, k=2, n_groups=1, topk_groups=1, T=400)
+    hz.say(f"edge hot-expert: {inputs.describe(w)}")
+    dc = inputs.make_inputs(w, seed=2)
+    lg = torch.full((w.T, w.E), -20.0)
+    lg[:, 3] = 5.0
+    lg[:, 7] = 1.0 + 0.01 * torch.arange(w.T) / w.T
+    dc["logits"] = lg
+    d = hz.to_device(dc)
+    got = hz.run_hip(w, d)
+    torch.cuda.synchronize()
+    r, _ = _compare_all(w, dc, got)
+    empty = np.nonzero(r["counts"] == 0)[0]
+    assert len(empty) == w.E - 2
+    assert not got["dW1"][empty].any() and not got["dW2"][empty].any()
+
+
+def test_zero_tokens_is_a_noop():
+    from grouped_gemm_expert_amd import ops
+    w = _wl("mid_softmax", T=0)
+    hz.say("edge T=0")
+    cfg = ops.config_from_workload(w)
+    saved = ops.alloc_saved(cfg)
+    y = torch.empty((0, w.H), device="cuda")
+    aux = torch.full((1,), 7.0, device="cuda")
+    x = torch.empty((0, w.H), dtype=torch.bfloat16, device="cuda")
+    w1 = torch.zeros((w.E, 2 * w.I, w.H), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros((w.E, w.H, w.I), dtype=torch.bfloat16, device="cuda")
+    Wr = torch.zeros((w.E, w.H), device="cuda")
+    ws = ops.workspace(cfg, "fwd")
+    ops.moe_forward(cfg, x, Wr, None, w1, w2, y, aux, saved, ws)
+    torch.cuda.synchronize()
+    assert float(aux.cpu()) == 0.0
+    assert int(saved["counts"].sum()) == 0
+
+
+def test_accumulate_mode_and_bf16_weight_grads():
+    w = inputs.WORKLOADS["mid_skewed"]
+    hz.say(f"dW modes {inputs.describe(w)}")
+    dc = inputs.make_inputs(w, seed=3)
+    d = hz.to_device(dc)
+    base = hz.run_hip(w, d)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    init1 = torch.randn((w.E, 2 * w.I, w.H), generator=g).cuda()
+    init2 = torch.randn((w.E, w.H, w.I), generator=g).cuda()
+    acc = hz.run_hip(w, d, dw_accumulate=True, dW_init=(init1, init2))
+    torch.cuda.synchronize()
+    counts = base["saved"]["counts"].cpu().numpy()
+    empty = np.nonzero(counts == 0)[0]
+    assert len(empty) > 0
+    # empty experts untouched (bit-identical), the rest = init + gradient
+    assert torch.equal(acc["dW1"][empty], init1[empty])
+    assert torch.equal(acc["dW2"][empty], init2[empty])
+    hz.assert_close("dW1 accumulate", (acc["dW1"] - init1).cpu().numpy(),
+                    base["dW1"].cpu().numpy(), (1e-5, 1e-5))
+    # bf16 stores: same values to bf16 rounding
+    b16 = hz.run_hip(w, d, dw_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = base["dW2"].cpu().numpy()
+    got = b16["dW2"].float().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-12)
+
+
+def test_run_to_run_determinism():
+    w = inputs.WORKLOADS["mid_sigmoid"]
+    hz.say(f"determinism {inputs.describe(w)}")
+    d = hz.to_device(inputs.make_inputs(w, seed=4))
+    a = hz.run_hip(w, d)
+    b = hz.run_hip(w, d)
+    torch.cuda.synchronize()
+    for key in ("y", "aux", "dx", "dlogits", "dW1", "dW2", "dWr"):
+        assert torch.equal(a[key], b[key]), key
+    for key in ("topk_idx", "row_map", "pos", "h", "a"):
+        assert torch.equal(a["saved"][key], b["saved"][key]), key

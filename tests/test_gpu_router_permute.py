@@ -1,0 +1,150 @@
+"""GPU parity of the router and the dispatch bookkeeping: bit-exact integer
+results given the same fp32 logits, routing weights and aux within fp32
+rounding, and the router projection within its fp32 error bound."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from grouped_gemm_expert_amd import inputs
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+ROUTER_CASES = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "deepseek_v3", "skewed",
+                "uniform", "fine_grained"]
+
+
+def _logits_for(w, seed=0):
+    """fp32 logits the test hands to both sides: generated ones, or the
+    oracle's projection of the generated x and router weight."""
+    if w.logits is not None:
+        dc = inputs.make_inputs(w, seed=seed, with_dy=False)
+        return dc, dc["logits"].numpy()
+    dc = inputs.make_inputs(w, seed=seed, with_dy=False)
+    l64 = oracle.logits(hz.bits(dc["x"]), dc["Wr"].numpy())
+    return dc, l64.astype(np.float32)
+
+
+@pytest.mark.parametrize("name", ROUTER_CASES)
+def test_router_bit_exact_given_logits(name):
+    from grouped_gemm_expert_amd import ops
+    w = inputs.WORKLOADS[name]
+    hz.say(f"router {inputs.describe(w)}")
+    dc, l32 = _logits_for(w)
+    bias = None if dc["bias"] is None else dc["bias"].numpy()
+    cfg = ops.config_from_workload(w)
+    dev = "cuda"
+    logits = torch.from_numpy(l32).to(dev)
+    bias_d = None if dc["bias"] is None else dc["bias"].to(dev)
+    sel = torch.empty_like(logits)
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = ops.workspace(cfg, "fwd", dev)
+    ops.moe_router(cfg, None, None, bias_d, logits, sel, idx, wts, counts, aux, ws)
+    torch.cuda.synchronize()
+
+    S_ref = oracle.selection_scores(l32, hz.SCORE[w.score], bias)
+    idx_ref = oracle.topk(S_ref, w.k, w.n_groups, w.topk_groups)
+    l64 = l32.astype(np.float64)
+    w_ref = oracle.weights(l64, idx_ref, hz.SCORE[w.score], w.renorm, w.scale)
+    counts_ref, *_ = oracle.permute(idx_ref, w.E)
+    aux_ref = oracle.aux(l64, counts_ref, w.k, hz.SCORE[w.score], w.aux_coeff)
+
+    sel_g = sel.cpu().numpy()
+    assert np.array_equal(sel_g.view(np.uint32), S_ref.view(np.uint32)), \
+        int((sel_g != S_ref).sum())
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.array_equal(counts.cpu().numpy(), counts_ref)
+    wg = wts.cpu().numpy().astype(np.float64)
+    assert np.abs(wg - w_ref).max() <= 4e-6 * max(1.0, w.scale)
+    assert abs(float(aux.cpu()) - aux_ref) <= 1e-4 * abs(aux_ref) + 1e-9
+    hz.say(f"router ok: counts min={counts_ref.min()} max={counts_ref.max()} "
+           f"empty={(counts_ref == 0).sum()} aux={aux_ref:.6g}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_softmax", "mid_sigmoid", "fine_grained"])
+def test_router_projection_and_routing_with_router_weight(name):
+    """The GPU computes its own fp32 logits; they must sit within the fp32
+    accumulation bound of the oracle's, and every routing difference must be
+    explained by a perturbation within that bound."""
+    from grouped_gemm_expert_amd import ops
+    w = inputs.WORKLOADS[name]
+    if name == "fine_grained":
+        w = dataclasses.replace(w, T=2048)
+    hz.say(f"router+projection {inputs.describe(w)}")
+    dc = inputs.make_inputs(w, with_dy=False)
+    d = hz.to_device(dc)
+    cfg = ops.config_from_workload(w)
+    logits = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((w.E,), dtype=torch.int32, device="cuda")
+    aux = torch.empty((1,), dtype=torch.float32, device="cuda")
+    ws = ops.workspace(cfg, "fwd")
+    ops.moe_router(cfg, d["x"], d["Wr"], d["bias"], logits, None, idx, wts, counts, aux, ws)
+    torch.cuda.synchronize()
+    l64 = oracle.logits(hz.bits(dc["x"]), dc["Wr"].numpy())
+    eps = hz.projection_error_bound(dc["x"], dc["Wr"])
+    lg = logits.cpu().numpy().astype(np.float64)
+    assert (np.abs(lg - l64) <= eps + np.spacing(np.abs(l64).astype(np.float32))).all()
+    bias = None if dc["bias"] is None else dc["bias"].numpy()
+    S = oracle.selection_scores(l64.astype(np.float32), hz.SCORE[w.score], bias)
+    idx_ref = oracle.topk(S, w.k, w.n_groups, w.topk_groups)
+    ig = idx.cpu().numpy()
+    diff = (ig != idx_ref).any(1)
+    hz.say(f"tokens routed differently: {int(diff.sum())} of {w.T}")
+    ok = hz.routing_valid_under_perturbation(w, l64, bias, ig, eps)
+    assert ok[diff].all()
+    assert diff.sum() <= max(1, w.T // 200)
+
+
+PERMUTE_CASES = [
+    ("uniform", 1000, 8, 2), ("uniform", 4097, 64, 6), ("uniform", 8192, 256, 8),
+    ("one_expert", 3000, 16, 1), ("one_hot_expert", 2500, 32, 4), ("even", 512, 8, 2),
+    ("zipf", 16384, 128, 8), ("single_token", 1, 8, 8), ("empty_most", 777, 1024, 2),
+]
+
+
+@pytest.mark.parametrize("pattern,T,E,k", PERMUTE_CASES)
+def test_permute_bit_exact(pattern, T, E, k):
+    from grouped_gemm_expert_amd import ops
+    hz.say(f"permute {pattern} T={T} E={E} k={k}")
+    rng = np.random.default_rng(T + E + k)
+    if pattern == "uniform":
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    elif pattern == "one_expert":
+        idx = np.full((T, k), 3 % E)
+    elif pattern == "one_hot_expert":
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        idx[:, 0] = 5
+        idx[:, 1:] = np.where(idx[:, 1:] == 5, 6, idx[:, 1:])
+    elif pattern == "even":
+        idx = (np.arange(T * k) % E).reshape(T, k)
+    elif pattern == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        idx = rng.choice(E, size=(T, k), p=p / p.sum())
+    elif pattern == "single_token":
+        idx = rng.permutation(E)[:k][None, :]
+    else:
+        idx = rng.choice([1, 1000], size=(T, k))
+    idx = idx.astype(np.int32)
+    cfg = ops.config(T=T, H=64, I=64, E=E, k=k)
+    dev = "cuda"
+    M = T * k
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    row_map = torch.empty((M,), dtype=torch.int32, device=dev)
+    pos = torch.empty((M,), dtype=torch.int32, device=dev)
+    ws = ops.workspace(cfg, "fwd", dev)
+    ops.moe_permute(cfg, torch.from_numpy(idx).to(dev), counts, offsets, row_map, pos, ws)
+    torch.cuda.synchronize()
+    c, o, rm, ps = oracle.permute(idx, E)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(row_map.cpu().numpy(), rm)
+    assert np.array_equal(pos.cpu().numpy(), ps)

@@ -229,3 +229,21 @@ def test_empty_expert_gets_zero_weight_grad(oracle_lib):
     for e in (0, 2, 3, 5, 6, 7):
         assert not dW1[e].any() and not dW2[e].any()
     assert dW1[1].any() and dW2[4].any()
+
+
+def test_expert_rows_recombine_to_forward(oracle_lib):
+    d, w = _small("softmax", True)
+    l64, r = _route(oracle_lib, d, w)
+    X, W1, W2 = _bits(d["x"]), _bits(d["w1"]), _bits(d["w2"])
+    y = oracle_lib.forward(X, W1, W2, r["idx"], r["w"])
+    slots = np.arange(w.T * w.k)
+    g, u, a, o = oracle_lib.expert_rows(X, W1, W2, r["idx"], slots)
+    yy = (o.reshape(w.T, w.k, w.H) * r["w"][:, :, None]).sum(1)
+    assert np.allclose(yy, y, rtol=1e-13, atol=1e-15)
+    # gate / up halves: single expert reduces to the dense products
+    x = d["x"].double().numpy()
+    for f in (0, 7, 100):
+        t, e = f // w.k, r["idx"].ravel()[f]
+        w1e = d["w1"][e].double().numpy()
+        assert np.allclose(g[f], x[t] @ w1e[:w.I].T, rtol=1e-13, atol=1e-15)
+        assert np.allclose(u[f], x[t] @ w1e[w.I:].T, rtol=1e-13, atol=1e-15)

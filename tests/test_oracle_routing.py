@@ -242,3 +242,14 @@ def test_aux_token_permutation_invariant(oracle_lib):
     assert np.array_equal(r["offsets"], r2["offsets"])
     assert np.array_equal(r2["idx"], r["idx"][perm])
     assert math.isclose(r["aux"], r2["aux"], rel_tol=1e-12)
+
+
+def test_logits_match_library_matmul(oracle_lib):
+    import torch
+    rng = np.random.default_rng(8)
+    x = torch.from_numpy(rng.standard_normal((37, 96)).astype(np.float32)).to(torch.bfloat16)
+    Wr = rng.standard_normal((11, 96)).astype(np.float32) * 0.02
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    l = oracle_lib.logits(bits, Wr)
+    ref = x.double().numpy() @ Wr.astype(np.float64).T
+    assert np.allclose(l, ref, rtol=1e-13, atol=1e-15)
