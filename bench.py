@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""MoE expert-path benchmark on one MI355X.
+
+One step = moe_forward + moe_backward of the DeepSeek-V3-style group-limited
+MoE layer (T=8192 tokens, H=7168, I=2048, 256 experts in 8 groups, top-4
+groups, top-8 experts, sigmoid scores + selection bias, scale 2.5) on seeded
+synthetic inputs that are resident in HBM before the timed region.  Weight
+gradients are accumulated into fp32 main-gradient buffers (the training
+setting where several micro-batches add into the same gradient).
+
+Prints ONE JSON line on stdout.  Per-stage device times come from HIP events
+that the library records on its own stream around each stage
+(moe_set_stage_events); the roofline entry is for the slowest grouped GEMM.
+The CPU baseline is the oracle, timed on a bounded token sample of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_wgrad"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_flops(w, stage):
+    """Algorithmic flops of one grouped-GEMM op (actual routed rows, no padding)."""
+    M = w.T * w.k
+    two_i = 2 * w.I
+    return {"up_swiglu": 2 * M * two_i * w.H, "down": 2 * M * w.H * w.I,
+            "down_dgrad": 2 * M * w.H * w.I, "up_dgrad": 2 * M * two_i * w.H,
+            "down_wgrad": 2 * M * w.H * w.I, "up_wgrad": 2 * M * two_i * w.H}[stage]
+
+
+def stage_bytes(w, stage, with_router_weight):
+    """Algorithmic HBM bytes of the memory-bound stages (each operand once)."""
+    T, E, k, H = w.T, w.E, w.k, w.H
+    M = T * k
+    return {
+        "router_proj": T * H * 2 + E * H * 4 + T * E * 4,
+        "router": T * E * 4 + E * 4 + T * k * 8 + E * 4,
+        "permute": 2 * M * 4 + 2 * M * 4 + 2 * (E + 1) * 4,
+        "combine": M * H * 4 + T * H * 4 + M * 8,
+        "router_bwd": T * E * 4 * 2 + M * 12,
+        "unpermute": M * H * 4 + T * H * 4 + M * 4,
+    }.get(stage)
+
+
+def run_gpu(args, w):
+    import torch
+    from grouped_gemm_expert_amd import inputs, ops
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating inputs on {dev}: {inputs.describe(w)}")
+    d = inputs.make_inputs(w, device=dev, seed=0)
+    cfg = ops.config_from_workload(w)
+    saved = ops.alloc_saved(cfg, dev)
+    if d["logits"] is not None:
+        saved["logits"].copy_(d["logits"])
+    y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    wsf = ops.workspace(cfg, "fwd", dev)
+    wsb = ops.workspace(cfg, "bwd", dev)
+    dx = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    dl = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+    dWr = torch.empty((w.E, w.H), dtype=torch.float32, device=dev) if d["Wr"] is not None else None
+    dW1 = torch.zeros((w.E, 2 * w.I, w.H), dtype=torch.float32, device=dev)
+    dW2 = torch.zeros((w.E, w.H, w.I), dtype=torch.float32, device=dev)
+    d_aux = torch.ones((1,), dtype=torch.float32, device=dev)
+    acc = args.dw_mode == "accumulate"
+
+    def step():
+        ops.moe_forward(cfg, d["x"], d["Wr"], d["bias"], d["w1"], d["w2"], y, aux, saved, wsf)
+        ops.moe_backward(cfg, saved, d["x"], d["Wr"], d["w1"], d["w2"], d["dy"], d_aux, dx, dl,
+                         dWr, dW1, dW2, wsb, dw_accumulate=acc)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)] for s in ops.STAGES}
+    for pairs in ev.values():          # torch creates its HIP events on first record
+        for a, b in pairs:
+            a.record()
+            b.record()
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for s, sid in ops.STAGES.items():
+            ops.moe_set_stage_events(sid, *ev[s][i])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for sid in ops.STAGES.values():
+        ops.moe_set_stage_events(sid, None, None)
+    elapsed = t1 - t0
+
+    stage_ms = {}
+    for s in ops.STAGES:
+        if s == "router_proj" and d["Wr"] is None:
+            continue
+        if s == "router_grads" and d["Wr"] is None:
+            continue
+        times = [a.elapsed_time(b) for a, b in ev[s]]
+        stage_ms[s] = sum(times) / len(times)
+    counts = saved["counts"].cpu()
+    log(f"[bench] step {elapsed / K * 1e3:.3f} ms; active experts {(counts > 0).sum().item()}, "
+        f"max rows {counts.max().item()}")
+    return dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved)
+
+
+def cpu_baseline(w, d, target_s=12.0):
+    """The oracle (as it stands) on a bounded sample of the same workload: the
+    first S tokens as a batch -- router projection, routing, expert forward,
+    backward (dx, dlogits), expert and router weight gradients."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from grouped_gemm_expert_amd import inputs
+
+    score = 0 if w.score == "softmax" else 1
+    bias = None if d["bias"] is None else d["bias"].cpu().numpy()
+    Wr = None if d["Wr"] is None else d["Wr"].cpu().numpy()
+
+    def prepare(S):
+        """Host copies for the first S tokens.  The weight arrays have the full
+        [E, ...] shape but are zero-allocated lazily; only the experts these
+        tokens route to are filled (and ever touched by the oracle)."""
+        x = inputs.bf16_bits(d["x"][:S])
+        dy = inputs.bf16_bits(d["dy"][:S])
+        if Wr is not None:
+            l64 = oracle.logits(x, Wr)
+        else:
+            l64 = d["logits"][:S].double().cpu().numpy()
+        S_sel = oracle.selection_scores(l64.astype(np.float32), score, bias)
+        used = np.unique(oracle.topk(S_sel, w.k, w.n_groups, w.topk_groups))
+        w1 = np.zeros((w.E, 2 * w.I, w.H), np.uint16)
+        w2 = np.zeros((w.E, w.H, w.I), np.uint16)
+        for e in used.tolist():
+            w1[e] = inputs.bf16_bits(d["w1"][e])
+            w2[e] = inputs.bf16_bits(d["w2"][e])
+        return x, dy, w1, w2, used
+
+    def run(S, x, dy, w1, w2, used):
+        t0 = time.perf_counter()
+        if Wr is not None:
+            l64 = oracle.logits(x, Wr)
+        else:
+            l64 = d["logits"][:S].double().cpu().numpy()
+        r = oracle.route(l64, score=score, k=w.k, n_groups=w.n_groups, topk_groups=w.topk_groups,
+                         bias=bias, renorm=w.renorm, scale=w.scale, coeff=w.aux_coeff)
+        oracle.forward(x, w1, w2, r["idx"], r["w"])
+        _, dlog = oracle.backward_tokens(x, Wr, l64, w1, w2, r["idx"], r["counts"], dy,
+                                         score=score, renorm=w.renorm, scale=w.scale,
+                                         coeff=w.aux_coeff)
+        oracle.weight_grads(x, w1, w2, r["idx"], r["w"], dy, experts=used)
+        if Wr is not None:
+            oracle.router_weight_grad(x, dlog)
+        return time.perf_counter() - t0
+
+    S0 = 4
+    data = prepare(S0)
+    t_cal = run(S0, *data)
+    S = int(max(S0, min(512, S0 * target_s / max(t_cal, 1e-3))))
+    log(f"[bench] cpu baseline: calibration {S0} tokens in {t_cal:.2f} s -> sample {S} tokens")
+    data = prepare(S)
+    t = run(S, *data)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} tokens of the workload as one batch, fwd+bwd incl. weight "
+                      f"gradients of the {len(data[4])} experts they route to; {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="deepseek_v3")
+    ap.add_argument("--dw-mode", choices=["accumulate", "overwrite"], default="accumulate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    from grouped_gemm_expert_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"workload {w.name} is forward-only; the metric is fwd+bwd")
+    g = run_gpu(args, w)
+    K = args.steps
+    elapsed = g["elapsed"]
+    stage_ms = g["stage_ms"]
+
+    gemm_ms = {s: stage_ms[s] for s in GEMM_STAGES}
+    total_gemm_flops = sum(gemm_flops(w, s) for s in GEMM_STAGES)
+    gemm_tflops = total_gemm_flops / (sum(gemm_ms.values()) * 1e-3) / 1e12
+    dom = max(gemm_ms, key=gemm_ms.get)
+    dom_tflops = gemm_flops(w, dom) / (gemm_ms[dom] * 1e-3) / 1e12
+
+    stages = {}
+    for s, ms in stage_ms.items():
+        e = {"ms": round(ms, 4)}
+        if s in GEMM_STAGES:
+            e["TFLOP/s"] = round(gemm_flops(w, s) / (ms * 1e-3) / 1e12, 1)
+        else:
+            b = stage_bytes(w, s, g["d"]["Wr"] is not None)
+            if b:
+                e["GB/s"] = round(b / (ms * 1e-3) / 1e9, 1)
+        stages[s] = e
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.T * K / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
+                   "n_groups": w.n_groups, "topk_groups": w.topk_groups, "score": w.score,
+                   "dw": f"fp32 {args.dw_mode}", "outputs": "fp32 y/dx, bf16 operands"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "grouped_gemm": {"TFLOP/s": round(gemm_tflops, 1),
+                         "pct_of_bf16_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
+                         "flops_per_step": total_gemm_flops,
+                         "ms_per_step": round(sum(gemm_ms.values()), 4)},
+        "stages": stages,
+        "active_experts": sum(1 for c in g["counts"] if c > 0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, g["d"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

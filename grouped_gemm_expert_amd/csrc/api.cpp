@@ -33,7 +33,8 @@ struct FwdWs {
     float *prob_part;
     int32_t *chunk_hist;
     Sched sched;
-    float *o;
+    float *wrow;
+    float *o;   // [M,H] fp32; the single-op grouped GEMMs reuse it for xg / dyw
 };
 
 struct BwdWs {
@@ -41,6 +42,9 @@ struct BwdWs {
     uint16_t *dh;
     float *dw_part;
     float *dxp;
+    float *wrow;
+    uint16_t *xg;
+    uint16_t *dyw;
 };
 
 FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
@@ -52,7 +56,8 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     w.chunk_hist = cv.take<int32_t>(permute_chunks(M) * c.E);
     w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
-    w.sched.order = cv.take<int32_t>(c.E);
+    w.sched.order = cv.take<int32_t>(c.E + 1);
+    w.wrow = cv.take<float>(M);
     w.o = cv.take<float>(M * c.H);
     if (bytes) *bytes = cv.used;
     return w;
@@ -65,15 +70,47 @@ BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
     BwdWs w;
     w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
-    w.sched.order = cv.take<int32_t>(c.E);
+    w.sched.order = cv.take<int32_t>(c.E + 1);
     w.dh = cv.take<uint16_t>(M * 2 * c.I);
     w.dw_part = cv.take<float>(M * dgrad2_cols(c.I));
     w.dxp = cv.take<float>(M * c.H);
+    w.wrow = cv.take<float>(M);
+    w.xg = cv.take<uint16_t>(M * c.H);
+    w.dyw = cv.take<uint16_t>(M * c.H);
     if (bytes) *bytes = cv.used;
     return w;
 }
 
-moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+// Stage event registry (see moe_set_stage_events).
+hipEvent_t g_stage_start[MOE_STAGE_COUNT];
+hipEvent_t g_stage_stop[MOE_STAGE_COUNT];
+
+// Records the stage's registered events around a scope of launches.
+struct StageMark {
+    int id;
+    hipStream_t s;
+    StageMark(int stage, hipStream_t stream) : id(stage), s(stream)
+    {
+        if (g_stage_start[id]) (void)hipEventRecord(g_stage_start[id], s);
+    }
+    ~StageMark()
+    {
+        if (g_stage_stop[id]) (void)hipEventRecord(g_stage_stop[id], s);
+    }
+};
+
+hipError_t run_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
+{
+    StageMark mark(op, s);
+    if (!g.dw_acc && (op == MOE_GEMM_DOWN_WGRAD || op == MOE_GEMM_UP_WGRAD)) {
+        // experts without rows get exact zeros; the GEMM only visits the others
+        const bool up = op == MOE_GEMM_UP_WGRAD;
+        hipError_t e = launch_zero_empty(g.E, (int64_t)2 * g.I * g.H / (up ? 1 : 2), g.counts,
+                                         up ? g.dW1 : g.dW2, g.dw_bf16, s);
+        if (e != hipSuccess) return e;
+    }
+    return launch_grouped_gemm(op, g, s);
+}
 
 #define MOE_TRY(expr)                                  \
     do {                                               \
@@ -146,6 +183,15 @@ const char *moe_status_string(moe_status s)
 
 const char *moe_version(void) { return "libmoe 0.1 gfx950"; }
 
+moe_status moe_set_stage_events(int32_t stage, hipEvent_t start, hipEvent_t stop)
+{
+    if (stage < 0 || stage >= MOE_STAGE_COUNT) return MOE_EINVAL;
+    if ((start == nullptr) != (stop == nullptr)) return MOE_EINVAL;
+    g_stage_start[stage] = start;
+    g_stage_stop[stage] = stop;
+    return MOE_OK;
+}
+
 moe_status moe_check_config(const moe_config *cfg)
 {
     if (!cfg) return MOE_EINVAL;
@@ -197,9 +243,11 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
         MOE_TRY(launch_fill_f32(aux, 1, 0.f, stream));
         return MOE_OK;
     }
-    if (Wr)
+    if (Wr) {
+        StageMark mark(MOE_STAGE_ROUTER_PROJ, stream);
         MOE_TRY(launch_simt_gemm(c.T, c.E, c.H, x, true, c.H, 1, Wr, false, c.H, 1, logits, c.E,
                                  false, stream));
+    }
     RouterArgs ra;
     ra.T = c.T;
     ra.E = c.E;
@@ -218,6 +266,7 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
     ra.counts = counts;
     ra.aux = aux;
     ra.prob_part = w.prob_part;
+    StageMark mark(MOE_STAGE_ROUTER, stream);
     MOE_TRY(launch_router(ra, stream));
     return MOE_OK;
 }
@@ -276,7 +325,23 @@ moe_status moe_grouped_gemm(int32_t op, const moe_config *cfg, const moe_gemm_ar
     const bool wgrad = op == MOE_GEMM_DOWN_WGRAD || op == MOE_GEMM_UP_WGRAD;
     if (c.T == 0 && !wgrad) return MOE_OK;
     MOE_TRY(launch_schedule(c.E, a.counts, w.sched, stream));
-    MOE_TRY(launch_grouped_gemm(op, gemm_args(c, a, w.sched), stream));
+    GemmArgs g = gemm_args(c, a, w.sched);
+    // per-sorted-row operands the op reads (see launch_gather_rows)
+    const int64_t M = c.T * c.k;
+    uint16_t *xg = (uint16_t *)w.o, *dyw = (uint16_t *)w.o + M * c.H;
+    if (op == MOE_GEMM_DOWN_DGRAD)
+        MOE_TRY(launch_gather_rows(M, c.k, c.H, a.row_map, a.topk_w, nullptr, nullptr, nullptr,
+                                   nullptr, w.wrow, stream));
+    if (op == MOE_GEMM_DOWN_WGRAD)
+        MOE_TRY(launch_gather_rows(M, c.k, c.H, a.row_map, a.topk_w, nullptr, a.dy, nullptr, dyw,
+                                   w.wrow, stream));
+    if (op == MOE_GEMM_UP_WGRAD)
+        MOE_TRY(launch_gather_rows(M, c.k, c.H, a.row_map, a.topk_w, a.x,
+                                   nullptr, xg, nullptr, nullptr, stream));
+    g.wrow = w.wrow;
+    g.xg = xg;
+    g.dyw = dyw;
+    MOE_TRY(run_gemm(op, g, stream));
     return MOE_OK;
 }
 
@@ -299,6 +364,7 @@ moe_status moe_combine(const moe_config *cfg, const float *o, const float *topk_
     if (c.T == 0) return MOE_OK;
     MOE_CHECK(check_ptrs({o, pos, y}));
     MOE_CHECK(check_opt_ptr(topk_w));
+    StageMark mark(MOE_STAGE_COMBINE, stream);
     MOE_TRY(launch_combine(c.T, c.k, c.H, o, topk_w, pos, y, stream));
     return MOE_OK;
 }
@@ -332,9 +398,12 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
     MOE_CHECK(check_ptrs({x, w1, w2, y}));
     MOE_CHECK(moe_router(cfg, x, Wr, bias, saved->logits, nullptr, saved->topk_idx,
                          saved->topk_w, saved->counts, aux, ws, ws_bytes, stream));
-    MOE_TRY(launch_permute(c.T * c.k, c.E, saved->topk_idx, saved->counts, saved->offsets,
-                           saved->row_map, saved->pos, w.chunk_hist, stream));
-    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    {
+        StageMark mark(MOE_STAGE_PERMUTE, stream);
+        MOE_TRY(launch_permute(c.T * c.k, c.E, saved->topk_idx, saved->counts, saved->offsets,
+                               saved->row_map, saved->pos, w.chunk_hist, stream));
+        MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    }
     moe_gemm_args a;
     memset(&a, 0, sizeof a);
     a.x = x;
@@ -348,8 +417,9 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
     a.a = saved->a;
     a.o = w.o;
     GemmArgs g = gemm_args(c, a, w.sched);
-    MOE_TRY(launch_grouped_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
-    MOE_TRY(launch_grouped_gemm(MOE_GEMM_DOWN, g, stream));
+    MOE_TRY(run_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
+    MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));
+    StageMark mark(MOE_STAGE_COMBINE, stream);
     MOE_TRY(launch_combine(c.T, c.k, c.H, w.o, saved->topk_w, saved->pos, y, stream));
     return MOE_OK;
 }
@@ -392,12 +462,17 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
     a.dw_dtype = dw_dtype;
     a.dw_accumulate = dw_accumulate;
     GemmArgs g = gemm_args(c, a, w.sched);
+    g.wrow = w.wrow;
+    g.xg = w.xg;
+    g.dyw = w.dyw;
+    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, x, dy, w.xg,
+                               w.dyw, w.wrow, stream));
     // GEMM2 stage: dgrad (+ SwiGLU backward, routing-weight row-dots), dW2
-    if (c.T > 0) MOE_TRY(launch_grouped_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
-    MOE_TRY(launch_grouped_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
+    if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
+    MOE_TRY(run_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
     // GEMM1 stage: dgrad, dW1
-    if (c.T > 0) MOE_TRY(launch_grouped_gemm(MOE_GEMM_UP_DGRAD, g, stream));
-    MOE_TRY(launch_grouped_gemm(MOE_GEMM_UP_WGRAD, g, stream));
+    if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_UP_DGRAD, g, stream));
+    MOE_TRY(run_gemm(MOE_GEMM_UP_WGRAD, g, stream));
     if (c.T == 0) {
         if (dWr && Wr) MOE_TRY(launch_fill_f32(dWr, (int64_t)c.E * c.H, 0.f, stream));
         return MOE_OK;
@@ -420,9 +495,16 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
     rb.counts = saved->counts;
     rb.pos = saved->pos;
     rb.dlogits = dlogits;
-    MOE_TRY(launch_router_bwd(rb, stream));
-    MOE_TRY(launch_combine(c.T, c.k, c.H, w.dxp, nullptr, saved->pos, dx, stream));
+    {
+        StageMark mark(MOE_STAGE_ROUTER_BWD, stream);
+        MOE_TRY(launch_router_bwd(rb, stream));
+    }
+    {
+        StageMark mark(MOE_STAGE_UNPERMUTE, stream);
+        MOE_TRY(launch_combine(c.T, c.k, c.H, w.dxp, nullptr, saved->pos, dx, stream));
+    }
     if (Wr) {
+        StageMark mark(MOE_STAGE_ROUTER_GRADS, stream);
         MOE_TRY(launch_simt_gemm(c.T, c.H, c.E, dlogits, false, c.E, 1, Wr, false, 1, c.H, dx, c.H,
                                  true, stream));
         if (dWr)

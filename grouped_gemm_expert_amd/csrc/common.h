@@ -104,7 +104,7 @@ hipError_t launch_permute(int64_t M, int32_t E, const int32_t *idx, int32_t *cou
 struct Sched {
     int32_t *mt_off256;  // [E+1]
     int32_t *mt_off128;  // [E+1]
-    int32_t *order;      // [E]
+    int32_t *order;      // [E+1]; order[E] = number of non-empty experts
 };
 hipError_t launch_schedule(int32_t E, const int32_t *counts, const Sched &sc, hipStream_t s);
 
@@ -114,6 +114,8 @@ struct GemmArgs {
     const int32_t *counts, *offsets, *row_map;
     const float *topk_w;
     const uint16_t *x, *dy, *w1, *w2;
+    const uint16_t *xg, *dyw;  // per sorted row: x[tok], bf16(topk_w * dy[tok])
+    const float *wrow;         // per sorted row: topk_w of its slot
     uint16_t *h, *a, *dh;
     float *o, *dw_part, *dxp;
     void *dW1, *dW2;
@@ -122,6 +124,16 @@ struct GemmArgs {
 };
 int32_t dgrad2_cols(int32_t I);
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
+// zero the weight gradient of every expert without rows (overwrite mode)
+hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *counts, void *dW,
+                             int32_t bf16, hipStream_t s);
+
+// backward pre-pass: per sorted row r (slot f = row_map[r], token f / k):
+// wrow[r] = topk_w[f] (1 when topk_w is null; stored if wrow); xg[r] = x[token]
+// (if xg); dyw[r] = bf16(wrow * dy[token]) (if dyw)
+hipError_t launch_gather_rows(int64_t M, int32_t k, int32_t H, const int32_t *row_map,
+                              const float *topk_w, const uint16_t *x, const uint16_t *dy,
+                              uint16_t *xg, uint16_t *dyw, float *wrow, hipStream_t s);
 
 // elementwise / reductions
 hipError_t launch_combine(int64_t T, int32_t k, int32_t H, const float *o, const float *w,

@@ -15,9 +15,10 @@
 // Scheduling: forward and dgrad GEMMs tile the sorted rows of each expert
 // (M-grouped); the per-expert m-tile prefix sums live on the device, the
 // grid is sized from a host-side upper bound and surplus blocks exit.  The
-// weight-gradient GEMMs tile each expert's [rows x cols] output and loop over
-// its routed rows (K-grouped), longest experts first; an expert with no rows
-// gets exact zeros (overwrite) or is left untouched (accumulate).  Block
+// weight-gradient GEMMs tile the [rows x cols] output of each expert that has
+// rows and loop over those rows (K-grouped), longest experts first; experts
+// without rows are zeroed by a separate fill (overwrite) or left untouched
+// (accumulate).  Block
 // indices are remapped so that each of the 8 XCDs works on a contiguous run
 // of tiles (neighbouring tiles share operand panels in that XCD's L2).
 #include "common.h"
@@ -25,6 +26,13 @@
 namespace moe {
 
 constexpr int BK = 64;  // k elements per LDS stage
+
+// LDS is addressed through explicit local-address-space pointers so that the
+// compiler emits ds_read / ds_write (a generic pointer would become FLAT).
+typedef __attribute__((address_space(3))) char lds_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 MOE_DEV int swz(int r) { return (r ^ (r >> 3)) & 7; }
 MOE_DEV int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
@@ -37,6 +45,7 @@ struct TileCfg {
     static constexpr int FM = WM / 32, FN = WN / 32;
     static constexpr int LDS_BYTES = 2 * (BM + BN) * 128;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
+    static_assert(BM == 256 || BM == 128, "m-tile prefix sums exist for 256 and 128 rows");
 };
 
 // ------------------------------------------------------------- loaders ----
@@ -59,58 +68,65 @@ struct RowLoader {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) reg[i] = *(const u32x4_t *)(p + off[i]);
     }
-    MOE_DEV void store(char *lds) const
+    MOE_DEV void store(lds_t *lds) const
     {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) *(u32x4_t *)(lds + lds_off(row(i), c)) = reg[i];
+        for (int i = 0; i < CPT; ++i) *(lds_u32x4 *)(lds + lds_off(row(i), c)) = reg[i];
     }
 };
 
-// ROWS x 64 tile whose source has rows along k: element (n, k) sits at
-// kptr(k)[n].  Each thread loads 8 k-rows x 8 n (8 x 16 bytes), transposes in
-// registers and stores 8 tile rows' chunk.  A null kptr row and columns at or
-// beyond `nlim` read as zeros (nlim is a multiple of 8); an optional per-k-row
-// scale multiplies the row (in fp32, rounded to bf16).
+// ROWS x 64 tile whose source rows run along k: element (n, k) of the stage
+// starting at k0 is base[(k0 + k) * ld + n], zero where k0 + k >= klim or
+// n >= nlim (nlim a multiple of 8).  Each thread loads 8 k-rows x 8 n
+// (8 x 16 bytes), transposes the 8x8 block in registers and stores 8 tile
+// rows' chunk.  Out-of-range reads are clamped to a valid address and zeroed
+// with selects, so the loop has no branches.
 template <int ROWS, int NT>
 struct TransLoader {
     static constexpr int NB = ROWS / 8;
     static constexpr int BLOCKS = NB * 8;
     static constexpr int BPT = (BLOCKS + NT - 1) / NT;
     u32x4_t reg[BPT][8];
+    const uint16_t *base;
+    int64_t ld, klim;
+    int64_t ncol[BPT];  // clamped first column of each owned block
+    bool nok[BPT];
     int tid;
-    MOE_DEV void init(int t) { tid = t; }
+    MOE_DEV void init(int t, const uint16_t *b, int64_t ld_, int64_t n0, int64_t nlim,
+                      int64_t klim_)
+    {
+        tid = t;
+        base = b;
+        ld = ld_;
+        klim = klim_;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            int64_t n = n0 + nb(i) * 8;
+            nok[i] = n < nlim;
+            ncol[i] = nok[i] ? n : 0;
+        }
+    }
     MOE_DEV bool has(int i) const { return BLOCKS % NT == 0 || tid + i * NT < BLOCKS; }
     MOE_DEV int nb(int i) const { return (tid + i * NT) % NB; }
     MOE_DEV int kb(int i) const { return (tid + i * NT) / NB; }
-    // rowptr(kk) -> pointer to element n=0 of k-row k0+kk (or nullptr), scale(kk)
-    template <class RowPtr, class Scale>
-    MOE_DEV void load(int64_t n0, int64_t nlim, RowPtr rowptr, Scale scale)
+    MOE_DEV void load(int64_t k0)
     {
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             if (!has(i)) continue;
-            const int64_t n = n0 + nb(i) * 8;
-            const bool nok = n < nlim;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                int kk = kb(i) * 8 + r;
-                const uint16_t *p = nok ? rowptr(kk) : nullptr;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (p) v = *(const u32x4_t *)(p + n);
-                float s = scale(kk);
-                if (s != 1.0f) {
+                const int64_t k = k0 + kb(i) * 8 + r;
+                const bool ok = nok[i] && k < klim;
+                const int64_t kc = k < klim ? k : klim - 1;
+                u32x4_t v = *(const u32x4_t *)(base + kc * ld + ncol[i]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint32_t d = v[q];
-                        v[q] = pack_bf2(bf2f((uint16_t)(d & 0xffffu)) * s,
-                                        bf2f((uint16_t)(d >> 16)) * s);
-                    }
-                }
+                for (int q = 0; q < 4; ++q) v[q] = ok ? v[q] : 0u;
                 reg[i][r] = v;
             }
         }
     }
-    MOE_DEV void store(char *lds) const
+    MOE_DEV void store(lds_t *lds) const
     {
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
@@ -124,7 +140,7 @@ struct TransLoader {
                     o[kp] = (n & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
                                     : ((lo & 0xffffu) | (hi << 16));
                 }
-                *(u32x4_t *)(lds + lds_off(nb(i) * 8 + n, kb(i))) = o;
+                *(lds_u32x4 *)(lds + lds_off(nb(i) * 8 + n, kb(i))) = o;
             }
         }
     }
@@ -147,7 +163,7 @@ struct Acc {
 
 // One 64-deep LDS stage: 4 MFMA k-steps of 16.
 template <class C>
-MOE_DEV void mma_stage(const char *As, const char *Bs, Acc<C> &acc, int wm, int wn, int lane)
+MOE_DEV void mma_stage(const lds_t *As, const lds_t *Bs, Acc<C> &acc, int wm, int wn, int lane)
 {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -156,30 +172,30 @@ MOE_DEV void mma_stage(const char *As, const char *Bs, Acc<C> &acc, int wm, int 
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
             int r = wm * C::WM + i * 32 + (lane & 31);
-            a[i] = *(const bf16x8_t *)(As + lds_off(r, ch));
+            a[i] = *(const lds_bf16x8 *)(As + lds_off(r, ch));
         }
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) {
             int r = wn * C::WN + j * 32 + (lane & 31);
-            b[j] = *(const bf16x8_t *)(Bs + lds_off(r, ch));
+            b[j] = *(const lds_bf16x8 *)(Bs + lds_off(r, ch));
         }
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
-                acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+                acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc.v[i][j], 0, 0, 0);
     }
 }
 
 // Software-pipelined main loop over nk stages: global loads for stage s+1 are
 // issued before the MFMAs of stage s and land in the other LDS buffer after.
 template <class C, class LoadA, class LoadB>
-MOE_DEV void mainloop(char *lds, int nk, LoadA &&loadA, LoadB &&loadB, Acc<C> &acc)
+MOE_DEV void mainloop(lds_t *lds, int nk, LoadA &&loadA, LoadB &&loadB, Acc<C> &acc)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    char *As[2] = {lds, lds + C::BM * 128};
-    char *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
+    lds_t *As[2] = {lds, lds + C::BM * 128};
+    lds_t *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
     acc.zero();
     if (nk <= 0) return;
     loadA(0, As[0], true, false);
@@ -203,27 +219,48 @@ MOE_DEV void mainloop(char *lds, int nk, LoadA &&loadA, LoadB &&loadB, Acc<C> &a
     }
 }
 
-// Element (i, j, r) of the accumulators <-> tile coordinates:
-//   row = wm*WM + i*32 + (r/4)*8 + (lane/32)*4 + r%4,  col = wn*WN + j*32 + lane%32
+// The MFMA takes the B fragment as its first operand, so each 32x32 block
+// holds the transposed product: element r of acc.v[i][j] is
+//   tile row (from A) = wm*WM + i*32 + lane%32
+//   tile col (from B) = wn*WN + j*32 + (r/4)*8 + (lane/32)*4 + r%4
+// i.e. every lane owns one row and four runs of four consecutive columns,
+// which the epilogues store as 8- or 16-byte vectors.
 template <class C>
-MOE_DEV int acc_row(int wm, int i, int r, int lane)
+MOE_DEV int acc_row(int wm, int i, int lane) { return wm * C::WM + i * 32 + (lane & 31); }
+template <class C>
+MOE_DEV int acc_col(int wn, int j, int rg, int lane)
 {
-    return wm * C::WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    return wn * C::WN + j * 32 + rg * 8 + (lane >> 5) * 4;
 }
-template <class C>
-MOE_DEV int acc_col(int wn, int j, int lane) { return wn * C::WN + j * 32 + (lane & 31); }
+
+MOE_DEV uint64_t pack_bf4(float a, float b, float c, float d)
+{
+    return (uint64_t)pack_bf2(a, b) | ((uint64_t)pack_bf2(c, d) << 32);
+}
+MOE_DEV void unpack_bf4(uint64_t v, float (&o)[4])
+{
+    o[0] = bf2f((uint16_t)(v & 0xffffu));
+    o[1] = bf2f((uint16_t)((v >> 16) & 0xffffu));
+    o[2] = bf2f((uint16_t)((v >> 32) & 0xffffu));
+    o[3] = bf2f((uint16_t)(v >> 48));
+}
 
 // ------------------------------------------------------- tile schedules ----
-// XCD-aware remap of block b over `total` tiles (grid >= total rounded up to
-// 8): XCD x (= b % 8) gets tiles [x*q, (x+1)*q) with q = ceil(total/8).
+// XCD-aware remap of block b over `total` tiles.  Blocks are dispatched to
+// the 8 XCDs round-robin (block b runs on XCD b % 8); consecutive tiles are
+// dealt to the XCDs in chunks of XCD_CHUNK (the CUs of one XCD), so the tiles
+// an XCD runs together are neighbours (they share operand panels in its L2)
+// while tiles of unequal cost spread evenly over all XCDs.  The grid is a
+// multiple of 8 * XCD_CHUNK and at least `total` rounded up to that.
+constexpr int64_t XCD_CHUNK = 32;
 MOE_DEV int64_t xcd_remap(int64_t b, int64_t total)
 {
-    int64_t q = (total + 7) >> 3;
-    int64_t t8 = q << 3;
-    if (b >= t8) return -1;
-    int64_t L = (b & 7) * q + (b >> 3);
+    const int64_t x = b & 7, j = b >> 3;
+    const int64_t L = ((j / XCD_CHUNK) * 8 + x) * XCD_CHUNK + (j % XCD_CHUNK);
     return L < total ? L : -1;
 }
+
+int64_t grid_for(int64_t total) { return ceil_div(total, 8 * XCD_CHUNK) * 8 * XCD_CHUNK; }
 
 struct MTile {
     int e;
@@ -261,8 +298,30 @@ MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offse
 int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
 {
     int64_t mt = M / BM + (M < E ? M : E) + 1;
-    int64_t total = mt * nN;
-    return ceil_div(total, 8) * 8;
+    return grid_for(mt * nN);
+}
+
+// fp32 tile store: rows [m0, seg_end), columns [n0, n0 + BN) below ncols,
+// row stride ncols; 16-byte stores.
+template <class C>
+MOE_DEV void store_rows_f32(const Acc<C> &acc, float *out, int64_t m0, int64_t seg_end, int64_t n0,
+                            int64_t ncols, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t m = m0 + acc_row<C>(wm, i, lane);
+        if (m >= seg_end) continue;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int64_t col = n0 + acc_col<C>(wn, j, rg, lane);
+                if (col >= ncols) continue;
+                f32x4_t v = {acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
+                             acc.v[i][j][rg * 4 + 3]};
+                *(f32x4_t *)(out + m * ncols + col) = v;
+            }
+    }
 }
 
 // =========================================================================
@@ -273,11 +332,12 @@ int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
     const int nN = (int)ceil_div(I, C::BN / 2);
     MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x;
     RowLoader<C::BM, C::NT> la;
     RowLoader<C::BN, C::NT> lb;
@@ -304,32 +364,38 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
     Acc<C> acc;
     mainloop<C>(
         lds, H / BK,
-        [&](int s, char *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, char *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
         acc);
 
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     constexpr int HF = C::FN / 2;
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t m = t.m0 + acc_row<C>(wm, i, lane);
+        if (m >= t.seg_end) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = t.m0 + acc_row<C>(wm, i, r, lane);
-            if (m >= t.seg_end) continue;
+        for (int j = 0; j < HF; ++j)
 #pragma unroll
-            for (int j = 0; j < HF; ++j) {
-                const int64_t col = i0 + wn * (C::WN / 2) + j * 32 + (lane & 31);
+            for (int rg = 0; rg < 4; ++rg) {
+                // gate columns of wave column wn start at i0 + wn*WN/2
+                const int64_t col = i0 + wn * (C::WN / 2) + j * 32 + rg * 8 + (lane >> 5) * 4;
                 if (col >= I) continue;
-                const float gv = acc.v[i][j][r], uv = acc.v[i][j + HF][r];
-                const float av = gv * sigmoidf_(gv) * uv;
-                if (g.h) {
-                    g.h[m * 2 * I + col] = f2bf(gv);
-                    g.h[m * 2 * I + I + col] = f2bf(uv);
+                float gv[4], uv[4], av[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    gv[q] = acc.v[i][j][rg * 4 + q];
+                    uv[q] = acc.v[i][j + HF][rg * 4 + q];
+                    av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
                 }
-                g.a[m * I + col] = f2bf(av);
+                if (g.h) {
+                    *(uint64_t *)(g.h + m * 2 * I + col) = pack_bf4(gv[0], gv[1], gv[2], gv[3]);
+                    *(uint64_t *)(g.h + m * 2 * I + I + col) = pack_bf4(uv[0], uv[1], uv[2], uv[3]);
+                }
+                *(uint64_t *)(g.a + m * I + col) = pack_bf4(av[0], av[1], av[2], av[3]);
             }
-        }
+    }
 }
 
 // =========================================================================
@@ -338,11 +404,12 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
     const int nN = (int)ceil_div(H, C::BN);
     MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x;
     RowLoader<C::BM, C::NT> la;
     RowLoader<C::BN, C::NT> lb;
@@ -365,23 +432,12 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
     Acc<C> acc;
     mainloop<C>(
         lds, I / BK,
-        [&](int s, char *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, char *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
         acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = t.m0 + acc_row<C>(wm, i, r, lane);
-            if (m >= t.seg_end) continue;
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int64_t col = n0 + acc_col<C>(wn, j, lane);
-                if (col < H) g.o[m * H + col] = acc.v[i][j][r];
-            }
-        }
+    store_rows_f32<C>(acc, g.o, t.m0, t.seg_end, n0, H, wm, wn, lane);
 }
 
 // =========================================================================
@@ -392,16 +448,16 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
     const int nN = (int)ceil_div(I, C::BN);
     MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x;
     RowLoader<C::BM, C::NT> la;
     TransLoader<C::BN, C::NT> lb;
     la.init(tid, g.dy);
-    lb.init(tid);
 #pragma unroll
     for (int q = 0; q < la.CPT; ++q) {
         int64_t m = t.m0 + la.row(q);
@@ -411,48 +467,49 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     const uint16_t *w2e = g.w2 + (int64_t)t.e * H * I;
     const int64_t n0 = (int64_t)t.nt * C::BN;
     // B(n = i, k = hh) = w2[e, hh, i]: k-row hh starts at w2e + hh*I
+    lb.init(tid, w2e, I, n0, I, H);
     Acc<C> acc;
     mainloop<C>(
         lds, H / BK,
-        [&](int s, char *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, char *dst, bool ld, bool st) {
-            if (ld)
-                lb.load(n0, I,
-                        [&](int kk) -> const uint16_t * { return w2e + ((int64_t)s * BK + kk) * I; },
-                        [](int) { return 1.0f; });
-            if (st) lb.store(dst);
-        },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
         acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    float *red = (float *)lds;  // [WAVES_N][BM]; the LDS tiles are free now
+    lds_f32 *red = (lds_f32 *)lds;  // [WAVES_N][BM]; the LDS tiles are free now
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+        const int rl = acc_row<C>(wm, i, lane);
+        const int64_t m = t.m0 + rl;
+        const bool mok = m < t.seg_end;
+        const float wgt = mok ? g.wrow[m] : 0.f;
+        float part = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rl = acc_row<C>(wm, i, r, lane);
-            const int64_t m = t.m0 + rl;
-            const bool mok = m < t.seg_end;
-            const float wgt = mok ? g.topk_w[g.row_map[m]] : 0.f;
-            float part = 0.f;
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int64_t col = n0 + acc_col<C>(wn, j, lane);
+            for (int rg = 0; rg < 4; ++rg) {
+                const int64_t col = n0 + acc_col<C>(wn, j, rg, lane);
                 if (!mok || col >= I) continue;
-                const float dap = acc.v[i][j][r];
-                const float gv = bf2f(g.h[m * 2 * I + col]);
-                const float uv = bf2f(g.h[m * 2 * I + I + col]);
-                const float av = bf2f(g.a[m * I + col]);
-                part += dap * av;
-                const float da = wgt * dap;
-                const float sg = sigmoidf_(gv);
-                g.dh[m * 2 * I + col] = f2bf(da * uv * sg * (1.0f + gv * (1.0f - sg)));
-                g.dh[m * 2 * I + I + col] = f2bf(da * gv * sg);
-            }
+                float gv[4], uv[4], av[4], dg[4], du[4];
+                unpack_bf4(*(const uint64_t *)(g.h + m * 2 * I + col), gv);
+                unpack_bf4(*(const uint64_t *)(g.h + m * 2 * I + I + col), uv);
+                unpack_bf4(*(const uint64_t *)(g.a + m * I + col), av);
 #pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-            if ((lane & 31) == 0) red[wn * C::BM + rl] = part;
-        }
+                for (int q = 0; q < 4; ++q) {
+                    const float dap = acc.v[i][j][rg * 4 + q];
+                    part += dap * av[q];
+                    const float da = wgt * dap;
+                    const float sg = sigmoidf_(gv[q]);
+                    dg[q] = da * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                    du[q] = da * gv[q] * sg;
+                }
+                *(uint64_t *)(g.dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
+                *(uint64_t *)(g.dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
+            }
+        // lanes l and l+32 hold the same row
+        part += __shfl_xor(part, 32, 64);
+        if (lane < 32) red[wn * C::BM + rl] = part;
+    }
     __syncthreads();
     for (int rl = tid; rl < C::BM; rl += C::NT) {
         const int64_t m = t.m0 + rl;
@@ -470,16 +527,16 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
     const int nN = (int)ceil_div(H, C::BN);
     MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x;
     RowLoader<C::BM, C::NT> la;
     TransLoader<C::BN, C::NT> lb;
     la.init(tid, g.dh);
-    lb.init(tid);
 #pragma unroll
     for (int q = 0; q < la.CPT; ++q) {
         int64_t m = t.m0 + la.row(q);
@@ -489,32 +546,16 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     const uint16_t *w1e = g.w1 + (int64_t)t.e * 2 * I * H;
     const int64_t n0 = (int64_t)t.nt * C::BN;
     // B(n = hh, k = nn) = w1[e, nn, hh]: k-row nn starts at w1e + nn*H
+    lb.init(tid, w1e, H, n0, H, 2 * I);
     Acc<C> acc;
     mainloop<C>(
         lds, 2 * I / BK,
-        [&](int s, char *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, char *dst, bool ld, bool st) {
-            if (ld)
-                lb.load(n0, H,
-                        [&](int kk) -> const uint16_t * { return w1e + ((int64_t)s * BK + kk) * H; },
-                        [](int) { return 1.0f; });
-            if (st) lb.store(dst);
-        },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
         acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = t.m0 + acc_row<C>(wm, i, r, lane);
-            if (m >= t.seg_end) continue;
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int64_t col = n0 + acc_col<C>(wn, j, lane);
-                if (col < H) g.dxp[m * H + col] = acc.v[i][j][r];
-            }
-        }
+    store_rows_f32<C>(acc, g.dxp, t.m0, t.seg_end, n0, H, wm, wn, lane);
 }
 
 // =========================================================================
@@ -522,23 +563,33 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
 //   DOWN:  dW2[e, hh, i] (+)= sum_r topk_w(r) dy[tok(r), hh] a[r, i]
 //   UP:    dW1[e, n, hh] (+)= sum_r dh[r, n] x[tok(r), hh]
 // Output tile rows come from operand A, columns from operand B; both are
-// transposed loads over k = routed row.
+// transposed loads over k = routed row.  The token rows are read from
+// per-sorted-row copies (dyw = topk_w * dy[tok], xg = x[tok]) written by the
+// gather pre-pass, so the k loop has no index loads.
 // =========================================================================
 template <class C, bool UP>
 __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
 {
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
     const int R = UP ? 2 * I : H;   // output rows
     const int Cc = UP ? H : I;      // output cols
     const int nR = (int)ceil_div(R, C::BM), nC = (int)ceil_div(Cc, C::BN);
     const int64_t tpe = (int64_t)nR * nC;
-    const int64_t total = (int64_t)g.E * tpe;
+    const int64_t total = (int64_t)g.sched.order[g.E] * tpe;  // non-empty experts only
     const int64_t L = xcd_remap(blockIdx.x, total);
     if (L < 0) return;
     const int e = g.sched.order[L / tpe];
+    // inside one expert: groups of GR row tiles sweep all column tiles, so
+    // the tiles running together share A and B panels in L2
+    constexpr int GR = 4;
     const int64_t rest = L % tpe;
-    const int rt = (int)(rest / nC), ct = (int)(rest % nC);
+    const int64_t grp = rest / ((int64_t)GR * nC);
+    const int64_t first = grp * GR;
+    const int64_t gr = nR - first < GR ? nR - first : GR;
+    const int64_t in = rest - grp * (int64_t)GR * nC;
+    const int rt = (int)(first + in % gr), ct = (int)(in / gr);
     const int64_t seg0 = g.offsets[e], seg1 = g.offsets[e + 1];
     const int64_t cnt = seg1 - seg0;
     const int64_t r0 = (int64_t)rt * C::BM, c0 = (int64_t)ct * C::BN;
@@ -547,82 +598,85 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t dW_off = (int64_t)e * R * Cc;
     void *dWv = UP ? g.dW1 : g.dW2;
-    if (cnt == 0) {
-        if (g.dw_acc) return;
-        // exact zeros for an expert without rows
-        for (int q = tid; q < C::BM * C::BN; q += C::NT) {
-            const int64_t rr = r0 + q / C::BN, cc = c0 + q % C::BN;
-            if (rr >= R || cc >= Cc) continue;
-            const int64_t o = dW_off + rr * Cc + cc;
-            if (g.dw_bf16) ((uint16_t *)dWv)[o] = 0;
-            else ((float *)dWv)[o] = 0.f;
-        }
-        return;
-    }
+    // Operands are row-major per sorted row: A rows of length R, B rows of
+    // length Cc (DOWN: w*dy gathered, a;  UP: dh, x gathered); k = sorted row
+    // of this expert, so the loaders start at row seg0 and stop at seg1.
+    const uint16_t *Ab = (UP ? g.dh : g.dyw) + seg0 * R;
+    const uint16_t *Bb = (UP ? g.xg : g.a) + seg0 * Cc;
     TransLoader<C::BM, C::NT> la;
     TransLoader<C::BN, C::NT> lb;
-    la.init(tid);
-    lb.init(tid);
+    la.init(tid, Ab, R, r0, R, cnt);
+    lb.init(tid, Bb, Cc, c0, Cc, cnt);
     const int nk = (int)ceil_div(cnt, BK);
     Acc<C> acc;
     mainloop<C>(
         lds, nk,
-        [&](int s, char *dst, bool ld, bool st) {
-            if (ld)
-                la.load(r0, R,
-                        [&](int kk) -> const uint16_t * {
-                            const int64_t m = seg0 + (int64_t)s * BK + kk;
-                            if (m >= seg1) return nullptr;
-                            if (UP) return g.dh + m * 2 * I;
-                            return g.dy + (int64_t)(g.row_map[m] / g.k) * H;
-                        },
-                        [&](int kk) -> float {
-                            if (UP) return 1.0f;
-                            const int64_t m = seg0 + (int64_t)s * BK + kk;
-                            return m < seg1 ? g.topk_w[g.row_map[m]] : 1.0f;
-                        });
-            if (st) la.store(dst);
-        },
-        [&](int s, char *dst, bool ld, bool st) {
-            if (ld)
-                lb.load(c0, Cc,
-                        [&](int kk) -> const uint16_t * {
-                            const int64_t m = seg0 + (int64_t)s * BK + kk;
-                            if (m >= seg1) return nullptr;
-                            if (UP) return g.x + (int64_t)(g.row_map[m] / g.k) * H;
-                            return g.a + m * I;
-                        },
-                        [](int) { return 1.0f; });
-            if (st) lb.store(dst);
-        },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
+        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
         acc);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+        const int64_t rr = r0 + acc_row<C>(wm, i, lane);
+        if (rr >= R) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t rr = r0 + acc_row<C>(wm, i, r, lane);
-            if (rr >= R) continue;
+        for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int64_t cc = c0 + acc_col<C>(wn, j, lane);
+            for (int rg = 0; rg < 4; ++rg) {
+                const int64_t cc = c0 + acc_col<C>(wn, j, rg, lane);
                 if (cc >= Cc) continue;
                 const int64_t o = dW_off + rr * Cc + cc;
-                float v = acc.v[i][j][r];
+                f32x4_t v = {acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
+                             acc.v[i][j][rg * 4 + 3]};
                 if (g.dw_bf16) {
-                    uint16_t *p = (uint16_t *)dWv;
-                    if (g.dw_acc) v += bf2f(p[o]);
-                    p[o] = f2bf(v);
+                    uint64_t *p = (uint64_t *)((uint16_t *)dWv + o);
+                    if (g.dw_acc) {
+                        float old[4];
+                        unpack_bf4(*p, old);
+                        v[0] += old[0]; v[1] += old[1]; v[2] += old[2]; v[3] += old[3];
+                    }
+                    *p = pack_bf4(v[0], v[1], v[2], v[3]);
                 } else {
-                    float *p = (float *)dWv;
-                    if (g.dw_acc) v += p[o];
-                    p[o] = v;
+                    f32x4_t *p = (f32x4_t *)((float *)dWv + o);
+                    if (g.dw_acc) v += *p;
+                    *p = v;
                 }
             }
-        }
+    }
+}
+
+// ---------------------------------------------------------- empty experts ----
+// dW[e] = 0 for every expert e without rows; grid (chunks, E), 16-byte stores.
+__global__ __launch_bounds__(256) void k_zero_empty(int64_t per_expert, const int32_t *counts,
+                                                    void *dW, int32_t bf16)
+{
+    const int e = blockIdx.y;
+    if (counts[e] != 0) return;
+    const int64_t bytes = per_expert * (bf16 ? 2 : 4);
+    u32x4_t *p = (u32x4_t *)((char *)dW + (int64_t)e * bytes);
+    const int64_t n = bytes / 16;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n;
+         q += (int64_t)gridDim.x * blockDim.x)
+        p[q] = z;
+}
+
+hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *counts, void *dW,
+                             int32_t bf16, hipStream_t s)
+{
+    dim3 grid(64, (unsigned)E);
+    k_zero_empty<<<grid, 256, 0, s>>>(per_expert, counts, dW, bf16);
+    return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- launch ----
-using Big = TileCfg<256, 256, 128, 128>;  // 4 waves, 128x128 per wave
+#ifndef MOE_TILE_BM
+#define MOE_TILE_BM 256
+#define MOE_TILE_BN 256
+#define MOE_TILE_WM 64
+#define MOE_TILE_WN 128
+#endif
+// 256x256 output tiles, 8 waves of 64x128 by default (two waves per SIMD)
+using Big = TileCfg<MOE_TILE_BM, MOE_TILE_BN, MOE_TILE_WM, MOE_TILE_WN>;
 
 int32_t dgrad2_cols(int32_t I) { return (int32_t)ceil_div(I, Big::BN); }
 
@@ -649,12 +703,14 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
     case MOE_GEMM_UP_DGRAD:
         return launch_k(k_up_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
     case MOE_GEMM_DOWN_WGRAD: {
-        int64_t total = (int64_t)g.E * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN);
-        return launch_k(k_wgrad<C, false>, ceil_div(total, 8) * 8, g, s, C::NT);
+        const int64_t act = g.M < g.E ? g.M : g.E;  // non-empty experts, at most
+        int64_t total = act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN);
+        return launch_k(k_wgrad<C, false>, grid_for(total), g, s, C::NT);
     }
     case MOE_GEMM_UP_WGRAD: {
-        int64_t total = (int64_t)g.E * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN);
-        return launch_k(k_wgrad<C, true>, ceil_div(total, 8) * 8, g, s, C::NT);
+        const int64_t act = g.M < g.E ? g.M : g.E;
+        int64_t total = act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN);
+        return launch_k(k_wgrad<C, true>, grid_for(total), g, s, C::NT);
     }
     default:
         return hipErrorInvalidValue;

@@ -159,9 +159,10 @@ hipError_t launch_permute(int64_t M, int32_t E, const int32_t *idx, int32_t *cou
 }
 
 // ------------------------------------------------------------- schedule ----
-// mt_off*[e] = sum_{e' < e} ceil(counts[e'] / BM) for BM = 256 and 128, and
+// mt_off*[e] = sum_{e' < e} ceil(counts[e'] / BM) for BM = 256 and 128,
 // order[] = experts by count descending (ties -> lower expert index), so the
-// weight-gradient GEMMs start the longest K loops first.
+// weight-gradient GEMMs start the longest K loops first, and order[E] = the
+// number of experts with at least one row (they come first in order[]).
 __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *counts,
                                                    int32_t *mt256, int32_t *mt128,
                                                    int32_t *order)
@@ -187,6 +188,9 @@ __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *cou
         }
         order[rank] = e;
     }
+    int32_t nact;
+    block_excl_scan_1024((e < E && c > 0) ? 1 : 0, tmp, nact);
+    if (e == 0) order[E] = nact;
 }
 
 hipError_t launch_schedule(int32_t E, const int32_t *counts, const Sched &sc, hipStream_t s)

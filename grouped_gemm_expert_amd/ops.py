@@ -14,7 +14,9 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIBRARY may name another build of the same library (a tuning variant).
+_LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
@@ -81,6 +83,8 @@ def _load():
     lib.moe_backward.argtypes = ([CFG, ctypes.POINTER(MoeSaved)] + [_P] * 11
                                  + [ctypes.c_int32, ctypes.c_int32, _P, sz, _P])
     lib.moe_backward.restype = S
+    lib.moe_set_stage_events.argtypes = [ctypes.c_int32, _P, _P]
+    lib.moe_set_stage_events.restype = S
     return lib
 
 
@@ -88,7 +92,18 @@ _lib = _load()
 
 SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspace_size",
            "moe_dw_part_cols", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_swiglu",
-           "moe_combine", "moe_forward", "moe_backward")
+           "moe_combine", "moe_forward", "moe_backward", "moe_set_stage_events")
+
+STAGES = {"up_swiglu": 0, "down": 1, "down_dgrad": 2, "up_dgrad": 3, "down_wgrad": 4,
+          "up_wgrad": 5, "router_proj": 6, "router": 7, "permute": 8, "combine": 9,
+          "router_bwd": 10, "unpermute": 11, "router_grads": 12}
+
+
+def moe_set_stage_events(stage: int, start, stop):
+    """Register torch.cuda.Event objects (or None) for a stage of the path."""
+    sp = None if start is None else ctypes.c_void_p(start.cuda_event)
+    ep = None if stop is None else ctypes.c_void_p(stop.cuda_event)
+    _check(_lib.moe_set_stage_events(int(stage), sp, ep), "moe_set_stage_events")
 
 
 def lib_path() -> str:

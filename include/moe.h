@@ -267,6 +267,29 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
                         float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
                         int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Profiling hook.  Stages of the path that moe_forward / moe_backward (and the
+ * single-stage entry points) launch; the six grouped-GEMM ops use their
+ * MOE_GEMM_* values.  When an event pair is registered for a stage, the
+ * library records `start` on the call's stream right before the stage's
+ * kernels and `stop` right after them, every time the stage runs, so the
+ * caller can read the stage's device time with hipEventElapsedTime.
+ * Passing NULL events unregisters.  The registry is process-wide host state:
+ * set it from one thread while no other thread calls the library.
+ */
+enum {
+    MOE_STAGE_ROUTER_PROJ = 6,   /* logits = x . Wr^T */
+    MOE_STAGE_ROUTER = 7,        /* selection, weights, counts, aux */
+    MOE_STAGE_PERMUTE = 8,       /* histogram, scan, scatter, tile schedule */
+    MOE_STAGE_COMBINE = 9,       /* weighted combine */
+    MOE_STAGE_ROUTER_BWD = 10,   /* d logits */
+    MOE_STAGE_UNPERMUTE = 11,    /* dx from the expert path */
+    MOE_STAGE_ROUTER_GRADS = 12, /* dx += dlogits . Wr, dWr */
+    MOE_STAGE_COUNT = 13
+};
+
+moe_status moe_set_stage_events(int32_t stage, hipEvent_t start, hipEvent_t stop);
+
 #ifdef __cplusplus
 }
 #endif
