@@ -1,14 +1,14 @@
 // Grouped bf16 GEMMs of the MoE expert path on gfx950 MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
-// Every GEMM is written as C[r, c] = sum_k A(r, k) * B(c, k): both operands
-// are staged through LDS as [rows][64] bf16 tiles (k contiguous, 128 bytes a
-// row, 16-byte chunks XOR-swizzled so that MFMA fragment reads and transposed
-// stores are free of bank conflicts).  Operands whose k index is contiguous
-// in memory are copied row by row (RowLoader); operands whose rows are
-// contiguous along the output dimension instead (the weights in dgrad, both
-// operands in wgrad) are loaded as 8x8 blocks and transposed in registers
-// (TransLoader).  Token rows are gathered through row_map while loading:
+// Every GEMM is written as C[r, c] = sum_k A(r, k) * B(c, k), staged
+// through double-buffered LDS tiles 64 deep in k.  Operands whose k index is
+// contiguous in memory are copied row by row into [rows][64] tiles
+// (RowLoader) and read with 16-byte LDS reads; operands that are contiguous
+// along the output dimension instead (the weights in dgrad, both operands in
+// wgrad) are copied in their own layout into [64][rows] tiles (ColLoader) and
+// read with gfx950's transposing LDS reads.  16-byte chunks are XOR-swizzled
+// so stores and fragment reads are free of bank conflicts.  Token rows are gathered through row_map while loading:
 // dispatch is fused into the load, as the MegaMoE page (intro) fuses it into
 // the first grouped GEMM.
 //
@@ -48,101 +48,99 @@ struct TileCfg {
     static_assert(BM == 256 || BM == 128, "m-tile prefix sums exist for 256 and 128 rows");
 };
 
+#ifndef MOE_PREFETCH
+#define MOE_PREFETCH 1
+#endif
+
 // ------------------------------------------------------------- loaders ----
-// ROWS x 64 tile from rows with contiguous k.  Thread tid owns chunk tid % 8
-// of rows tid/8 + i*(NT/8).
+// Both loaders keep two register sets, so the global loads of stage s+2 are
+// issued while stage s is computed and stored to LDS at the end of stage s+1
+// (two stages of latency cover).
+
+// K-major tile: ROWS x 64 with k contiguous (128 bytes a row).  Thread tid
+// owns chunk tid % 8 of rows tid/8 + i*(NT/8); each owned row has its own
+// element offset from `base` (rows may be gathered).
 template <int ROWS, int NT>
 struct RowLoader {
     static constexpr int RSTEP = NT / 8;
     static constexpr int CPT = ROWS / RSTEP;
     static_assert(ROWS % RSTEP == 0, "rows split evenly");
     const uint16_t *base;
-    uint32_t off[CPT];  // element offset of each owned row from base
-    u32x4_t reg[CPT];
+    uint32_t off[CPT];
+    u32x4_t reg[MOE_PREFETCH][CPT];
     int c, r0;
     MOE_DEV void init(int tid, const uint16_t *b) { c = tid & 7; r0 = tid >> 3; base = b; }
     MOE_DEV int row(int i) const { return r0 + i * RSTEP; }
+    template <int S>
     MOE_DEV void load(int64_t k0)
     {
         const uint16_t *p = base + k0 + c * 8;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) reg[i] = *(const u32x4_t *)(p + off[i]);
+        for (int i = 0; i < CPT; ++i) reg[S][i] = *(const u32x4_t *)(p + off[i]);
     }
+    template <int S>
     MOE_DEV void store(lds_t *lds) const
     {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) *(lds_u32x4 *)(lds + lds_off(row(i), c)) = reg[i];
+        for (int i = 0; i < CPT; ++i) *(lds_u32x4 *)(lds + lds_off(row(i), c)) = reg[S][i];
     }
 };
 
-// ROWS x 64 tile whose source rows run along k: element (n, k) of the stage
-// starting at k0 is base[(k0 + k) * ld + n], zero where k0 + k >= klim or
-// n >= nlim (nlim a multiple of 8).  Each thread loads 8 k-rows x 8 n
-// (8 x 16 bytes), transposes the 8x8 block in registers and stores 8 tile
-// rows' chunk.  Out-of-range reads are clamped to a valid address and zeroed
-// with selects, so the loop has no branches.
+// N-major tile: 64 k-rows x ROWS, the other index contiguous (ROWS*2 bytes a
+// k-row), in the source's own layout; the MFMA fragments are read from it
+// with transposing LDS reads.  16-byte chunk c of k-row k sits at
+// nmaj_off(k, c): the chunk index is XORed with 4*(k % 4), which keeps both
+// the row stores and the transposing reads free of bank conflicts.
+template <int ROWS>
+MOE_DEV int nmaj_off(int k, int c) { return k * (ROWS * 2) + ((c ^ ((k & 3) << 2)) << 4); }
+
+// Element (n, k) of the stage starting at k0 is base[(k0 + k) * ld + n], zero
+// where k0 + k >= klim or n >= nlim (nlim a multiple of 8).  Thread tid owns
+// chunk tid % (ROWS/8) of k-rows tid/(ROWS/8) + i*(NT*8/ROWS).  Out-of-range
+// reads are clamped to a valid address and zeroed with selects (no branches).
 template <int ROWS, int NT>
-struct TransLoader {
-    static constexpr int NB = ROWS / 8;
-    static constexpr int BLOCKS = NB * 8;
-    static constexpr int BPT = (BLOCKS + NT - 1) / NT;
-    u32x4_t reg[BPT][8];
+struct ColLoader {
+    static constexpr int CPR = ROWS / 8;
+    static constexpr int KSTEP = NT / CPR;
+    static constexpr int CPT = 64 / KSTEP;
+    static_assert(NT % CPR == 0 && 64 % KSTEP == 0, "chunks split evenly");
     const uint16_t *base;
-    int64_t ld, klim;
-    int64_t ncol[BPT];  // clamped first column of each owned block
-    bool nok[BPT];
-    int tid;
-    MOE_DEV void init(int t, const uint16_t *b, int64_t ld_, int64_t n0, int64_t nlim,
+    int64_t ld, klim, ncol;
+    bool nok;
+    int c, k0r;
+    u32x4_t reg[MOE_PREFETCH][CPT];
+    MOE_DEV void init(int tid, const uint16_t *b, int64_t ld_, int64_t n0, int64_t nlim,
                       int64_t klim_)
     {
-        tid = t;
         base = b;
         ld = ld_;
         klim = klim_;
-#pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            int64_t n = n0 + nb(i) * 8;
-            nok[i] = n < nlim;
-            ncol[i] = nok[i] ? n : 0;
-        }
+        c = tid % CPR;
+        k0r = tid / CPR;
+        const int64_t n = n0 + c * 8;
+        nok = n < nlim;
+        ncol = nok ? n : 0;
     }
-    MOE_DEV bool has(int i) const { return BLOCKS % NT == 0 || tid + i * NT < BLOCKS; }
-    MOE_DEV int nb(int i) const { return (tid + i * NT) % NB; }
-    MOE_DEV int kb(int i) const { return (tid + i * NT) / NB; }
+    MOE_DEV int krow(int i) const { return k0r + i * KSTEP; }
+    template <int S>
     MOE_DEV void load(int64_t k0)
     {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            if (!has(i)) continue;
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t k = k0 + krow(i);
+            const bool ok = nok && k < klim;
+            const int64_t kc = k < klim ? k : klim - 1;
+            u32x4_t v = *(const u32x4_t *)(base + kc * ld + ncol);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int64_t k = k0 + kb(i) * 8 + r;
-                const bool ok = nok[i] && k < klim;
-                const int64_t kc = k < klim ? k : klim - 1;
-                u32x4_t v = *(const u32x4_t *)(base + kc * ld + ncol[i]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = ok ? v[q] : 0u;
-                reg[i][r] = v;
-            }
+            for (int q = 0; q < 4; ++q) v[q] = ok ? v[q] : 0u;
+            reg[S][i] = v;
         }
     }
+    template <int S>
     MOE_DEV void store(lds_t *lds) const
     {
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            if (!has(i)) continue;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                u32x4_t o;
-#pragma unroll
-                for (int kp = 0; kp < 4; ++kp) {
-                    uint32_t lo = reg[i][2 * kp][n >> 1], hi = reg[i][2 * kp + 1][n >> 1];
-                    o[kp] = (n & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                    : ((lo & 0xffffu) | (hi << 16));
-                }
-                *(lds_u32x4 *)(lds + lds_off(nb(i) * 8 + n, kb(i))) = o;
-            }
-        }
+        for (int i = 0; i < CPT; ++i) *(lds_u32x4 *)(lds + nmaj_off<ROWS>(krow(i), c)) = reg[S][i];
     }
 };
 
@@ -161,24 +159,50 @@ struct Acc {
     }
 };
 
+// MFMA operand fragment for rows rbase + lane%32 and k = kk*16 + (lane/32)*8
+// + [0, 8).  K-major tile: one 16-byte read.  N-major tile: two transposing
+// reads; in each group of 16 lanes, lane 4r+q addresses k-row kb + r at
+// columns 4q..4q+3 of its 16-column slice, and lane j receives the four
+// k-values of column j.
+MOE_DEV bf16x8_t frag_kmaj(const lds_t *T, int rbase, int kk, int lane)
+{
+    return *(const lds_bf16x8 *)(T + lds_off(rbase + (lane & 31), kk * 2 + (lane >> 5)));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <int ROWS>
+MOE_DEV bf16x8_t frag_nmaj(const lds_t *T, int rbase, int kk, int lane)
+{
+    const int g = lane >> 4, j = lane & 15, r = j >> 2, q = j & 3;
+    const int n = rbase + (g & 1) * 16 + 4 * q;
+    const int k = kk * 16 + (g >> 1) * 8 + r;
+    const int within = (q & 1) * 8;
+    v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(T + nmaj_off<ROWS>(k, n >> 3) + within));
+    v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(T + nmaj_off<ROWS>(k + 4, n >> 3) + within));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // One 64-deep LDS stage: 4 MFMA k-steps of 16.
-template <class C>
+template <class C, bool A_NMAJ, bool B_NMAJ>
 MOE_DEV void mma_stage(const lds_t *As, const lds_t *Bs, Acc<C> &acc, int wm, int wn, int lane)
 {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
         bf16x8_t a[C::FM], b[C::FN];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            int r = wm * C::WM + i * 32 + (lane & 31);
-            a[i] = *(const lds_bf16x8 *)(As + lds_off(r, ch));
-        }
+        for (int i = 0; i < C::FM; ++i)
+            a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
+                          : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            int r = wn * C::WN + j * 32 + (lane & 31);
-            b[j] = *(const lds_bf16x8 *)(Bs + lds_off(r, ch));
-        }
+        for (int j = 0; j < C::FN; ++j)
+            b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
+                          : frag_kmaj(Bs, wn * C::WN + j * 32, kk, lane);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -187,10 +211,23 @@ MOE_DEV void mma_stage(const lds_t *As, const lds_t *Bs, Acc<C> &acc, int wm, in
     }
 }
 
-// Software-pipelined main loop over nk stages: global loads for stage s+1 are
-// issued before the MFMAs of stage s and land in the other LDS buffer after.
-template <class C, class LoadA, class LoadB>
-MOE_DEV void mainloop(lds_t *lds, int nk, LoadA &&loadA, LoadB &&loadB, Acc<C> &acc)
+template <int S>
+struct SetTag {
+    static constexpr int value = S;
+};
+
+#ifndef MOE_PREFETCH
+#define MOE_PREFETCH 1
+#endif
+
+// Main loop over nk stages of 64 k.  Stage s computes from LDS buffer s%2.
+// Prefetch distance 1: the loads of stage s+1 are issued before the MFMAs of
+// stage s and stored to the other LDS buffer after them.  Prefetch distance 2
+// (two register sets): the loads of stage s+2 fill register set s%2 while
+// set (s+1)%2, loaded during stage s-1, is stored; unrolled by two so each
+// register set index is static.
+template <class C, bool A_NMAJ, bool B_NMAJ, class LA, class LB>
+MOE_DEV void mainloop(lds_t *lds, int nk, LA &la, LB &lb, Acc<C> &acc)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -198,25 +235,53 @@ MOE_DEV void mainloop(lds_t *lds, int nk, LoadA &&loadA, LoadB &&loadB, Acc<C> &
     lds_t *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
     acc.zero();
     if (nk <= 0) return;
-    loadA(0, As[0], true, false);
-    loadB(0, Bs[0], true, false);
-    loadA(0, As[0], false, true);
-    loadB(0, Bs[0], false, true);
+    la.template load<0>(0);
+    lb.template load<0>(0);
+#if MOE_PREFETCH == 2
+    if (nk > 1) {
+        la.template load<1>(BK);
+        lb.template load<1>(BK);
+    }
+#endif
+    la.template store<0>(As[0]);
+    lb.template store<0>(Bs[0]);
     __syncthreads();
+#if MOE_PREFETCH == 2
+    auto step = [&](auto tag, int s) {
+        constexpr int S = decltype(tag)::value;
+        if (s + 2 < nk) {
+            la.template load<S>((int64_t)(s + 2) * BK);
+            lb.template load<S>((int64_t)(s + 2) * BK);
+        }
+        mma_stage<C, A_NMAJ, B_NMAJ>(As[S], Bs[S], acc, wm, wn, lane);
+        if (s + 1 < nk) {
+            la.template store<1 - S>(As[1 - S]);
+            lb.template store<1 - S>(Bs[1 - S]);
+        }
+        __syncthreads();
+    };
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
+        step(SetTag<0>(), s);
+        step(SetTag<1>(), s + 1);
+    }
+    if (s < nk) step(SetTag<0>(), s);
+#else
     for (int s = 0; s < nk; ++s) {
         const int cur = s & 1;
         const bool more = s + 1 < nk;
         if (more) {
-            loadA(s + 1, As[cur ^ 1], true, false);
-            loadB(s + 1, Bs[cur ^ 1], true, false);
+            la.template load<0>((int64_t)(s + 1) * BK);
+            lb.template load<0>((int64_t)(s + 1) * BK);
         }
-        mma_stage<C>(As[cur], Bs[cur], acc, wm, wn, lane);
+        mma_stage<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], acc, wm, wn, lane);
         if (more) {
-            loadA(s + 1, As[cur ^ 1], false, true);
-            loadB(s + 1, Bs[cur ^ 1], false, true);
+            la.template store<0>(As[cur ^ 1]);
+            lb.template store<0>(Bs[cur ^ 1]);
         }
         __syncthreads();
     }
+#endif
 }
 
 // The MFMA takes the B fragment as its first operand, so each 32x32 block
@@ -362,11 +427,7 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
         lb.off[q] = (uint32_t)(n * H);
     }
     Acc<C> acc;
-    mainloop<C>(
-        lds, H / BK,
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
-        acc);
+    mainloop<C, false, false>(lds, H / BK, la, lb, acc);
 
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -430,11 +491,7 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
         lb.off[q] = (uint32_t)(n * I);
     }
     Acc<C> acc;
-    mainloop<C>(
-        lds, I / BK,
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
-        acc);
+    mainloop<C, false, false>(lds, I / BK, la, lb, acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     store_rows_f32<C>(acc, g.o, t.m0, t.seg_end, n0, H, wm, wn, lane);
@@ -456,7 +513,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x;
     RowLoader<C::BM, C::NT> la;
-    TransLoader<C::BN, C::NT> lb;
+    ColLoader<C::BN, C::NT> lb;
     la.init(tid, g.dy);
 #pragma unroll
     for (int q = 0; q < la.CPT; ++q) {
@@ -469,11 +526,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     // B(n = i, k = hh) = w2[e, hh, i]: k-row hh starts at w2e + hh*I
     lb.init(tid, w2e, I, n0, I, H);
     Acc<C> acc;
-    mainloop<C>(
-        lds, H / BK,
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
-        acc);
+    mainloop<C, false, true>(lds, H / BK, la, lb, acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     lds_f32 *red = (lds_f32 *)lds;  // [WAVES_N][BM]; the LDS tiles are free now
@@ -535,7 +588,7 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x;
     RowLoader<C::BM, C::NT> la;
-    TransLoader<C::BN, C::NT> lb;
+    ColLoader<C::BN, C::NT> lb;
     la.init(tid, g.dh);
 #pragma unroll
     for (int q = 0; q < la.CPT; ++q) {
@@ -548,11 +601,7 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     // B(n = hh, k = nn) = w1[e, nn, hh]: k-row nn starts at w1e + nn*H
     lb.init(tid, w1e, H, n0, H, 2 * I);
     Acc<C> acc;
-    mainloop<C>(
-        lds, 2 * I / BK,
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
-        acc);
+    mainloop<C, false, true>(lds, 2 * I / BK, la, lb, acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     store_rows_f32<C>(acc, g.dxp, t.m0, t.seg_end, n0, H, wm, wn, lane);
@@ -603,17 +652,13 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     // of this expert, so the loaders start at row seg0 and stop at seg1.
     const uint16_t *Ab = (UP ? g.dh : g.dyw) + seg0 * R;
     const uint16_t *Bb = (UP ? g.xg : g.a) + seg0 * Cc;
-    TransLoader<C::BM, C::NT> la;
-    TransLoader<C::BN, C::NT> lb;
+    ColLoader<C::BM, C::NT> la;
+    ColLoader<C::BN, C::NT> lb;
     la.init(tid, Ab, R, r0, R, cnt);
     lb.init(tid, Bb, Cc, c0, Cc, cnt);
     const int nk = (int)ceil_div(cnt, BK);
     Acc<C> acc;
-    mainloop<C>(
-        lds, nk,
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) la.load((int64_t)s * BK); if (st) la.store(dst); },
-        [&](int s, lds_t *dst, bool ld, bool st) { if (ld) lb.load((int64_t)s * BK); if (st) lb.store(dst); },
-        acc);
+    mainloop<C, true, true>(lds, nk, la, lb, acc);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         const int64_t rr = r0 + acc_row<C>(wm, i, lane);
