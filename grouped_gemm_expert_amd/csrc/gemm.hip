@@ -2,13 +2,14 @@
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
 // Every GEMM is written as C[r, c] = sum_k A(r, k) * B(c, k), staged
-// through double-buffered LDS tiles 64 deep in k.  Operands whose k index is
-// contiguous in memory are copied row by row into [rows][64] tiles
-// (RowLoader) and read with 16-byte LDS reads; operands that are contiguous
-// along the output dimension instead (the weights in dgrad, both operands in
-// wgrad) are copied in their own layout into [64][rows] tiles (ColLoader) and
-// read with gfx950's transposing LDS reads.  16-byte chunks are XOR-swizzled
-// so stores and fragment reads are free of bank conflicts.  Token rows are gathered through row_map while loading:
+// through double-buffered LDS tiles 64 deep in k that are filled by direct
+// global->LDS copies.  Operands whose k index is contiguous in memory are
+// copied row by row into [rows][64] tiles (KLoad) and read with 16-byte LDS
+// reads; operands that are contiguous along the output dimension instead
+// (the weights in dgrad, both operands in wgrad) are copied in their own
+// layout into [64][rows] tiles (NLoad) and read with gfx950's transposing
+// LDS reads.  16-byte chunks are XOR-swizzled so that fragment reads are free
+// of bank conflicts.  Token rows are gathered through row_map while loading:
 // dispatch is fused into the load, as the MegaMoE page (intro) fuses it into
 // the first grouped GEMM.
 //
@@ -48,99 +49,112 @@ struct TileCfg {
     static_assert(BM == 256 || BM == 128, "m-tile prefix sums exist for 256 and 128 rows");
 };
 
-#ifndef MOE_PREFETCH
-#define MOE_PREFETCH 1
-#endif
-
 // ------------------------------------------------------------- loaders ----
-// Both loaders keep two register sets, so the global loads of stage s+2 are
-// issued while stage s is computed and stored to LDS at the end of stage s+1
-// (two stages of latency cover).
+// Operand tiles go from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane l of a wave writes bytes [16 l, 16 l + 16)
+// of a 1 KB LDS block whose address is uniform over the wave (it travels in
+// M0), so each loader picks, per lane, the 16 global bytes that belong at
+// that LDS position under the tile's swizzle.  The copies run asynchronously
+// while the MFMAs of the previous stage execute; there are no staging
+// registers and no ds_write in the main loop.
 
-// K-major tile: ROWS x 64 with k contiguous (128 bytes a row).  Thread tid
-// owns chunk tid % 8 of rows tid/8 + i*(NT/8); each owned row has its own
-// element offset from `base` (rows may be gathered).
+typedef __attribute__((address_space(3))) void lds_void;
+
+MOE_DEV int wave_uniform_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+MOE_DEV void copy16_to_lds(const char *src, lds_t *dst_block)
+{
+    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst_block, 16, 0, 0);
+}
+
+// Wait until every global->LDS copy this wave issued has landed: s_waitcnt
+// vmcnt(0) (expcnt and lgkmcnt fields left at their maxima).
+MOE_DEV void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// K-major tile: ROWS x 64 with k contiguous (128 bytes a row; chunk c of row r
+// at lds_off(r, c)).  1 KB block q holds rows 8q .. 8q+7; wave w fills blocks
+// w*NI .. w*NI+NI-1, and its lane l takes row 8q + l/8 at physical chunk l%8,
+// i.e. logical chunk (l%8) ^ swz(row).  off[i] is the byte offset of that
+// lane's 16 bytes from `base` at k = 0 (rows may be gathered).
 template <int ROWS, int NT>
-struct RowLoader {
-    static constexpr int RSTEP = NT / 8;
-    static constexpr int CPT = ROWS / RSTEP;
-    static_assert(ROWS % RSTEP == 0, "rows split evenly");
-    const uint16_t *base;
-    uint32_t off[CPT];
-    u32x4_t reg[MOE_PREFETCH][CPT];
-    int c, r0;
-    MOE_DEV void init(int tid, const uint16_t *b) { c = tid & 7; r0 = tid >> 3; base = b; }
-    MOE_DEV int row(int i) const { return r0 + i * RSTEP; }
-    template <int S>
-    MOE_DEV void load(int64_t k0)
+struct KLoad {
+    static constexpr int NI = ROWS / 8 / (NT / 64);
+    static_assert(NI * 8 * (NT / 64) == ROWS, "1 KB blocks split evenly over the waves");
+    const char *base;
+    uint32_t off[NI];
+    int q0;
+    MOE_DEV void init(const void *b, int wave) { base = (const char *)b; q0 = wave * NI; }
+    MOE_DEV int row(int i, int lane) const { return (q0 + i) * 8 + (lane >> 3); }
+    MOE_DEV void set(int i, int lane, uint32_t row_bytes)
     {
-        const uint16_t *p = base + k0 + c * 8;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) reg[S][i] = *(const u32x4_t *)(p + off[i]);
+        off[i] = row_bytes + ((uint32_t)((lane & 7) ^ swz(row(i, lane))) << 4);
     }
-    template <int S>
-    MOE_DEV void store(lds_t *lds) const
+    MOE_DEV void issue(lds_t *tile, int64_t k0, int) const
     {
+        const char *p = base + k0 * 2;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) *(lds_u32x4 *)(lds + lds_off(row(i), c)) = reg[S][i];
+        for (int i = 0; i < NI; ++i) copy16_to_lds(p + off[i], tile + (q0 + i) * 1024);
     }
+    MOE_DEV void zero_tail(lds_t *, int) const {}
 };
 
 // N-major tile: 64 k-rows x ROWS, the other index contiguous (ROWS*2 bytes a
 // k-row), in the source's own layout; the MFMA fragments are read from it
 // with transposing LDS reads.  16-byte chunk c of k-row k sits at
-// nmaj_off(k, c): the chunk index is XORed with 4*(k % 4), which keeps both
-// the row stores and the transposing reads free of bank conflicts.
+// nmaj_off(k, c): the chunk index is XORed with 4*(k % 4), which keeps the
+// transposing reads free of bank conflicts.
 template <int ROWS>
 MOE_DEV int nmaj_off(int k, int c) { return k * (ROWS * 2) + ((c ^ ((k & 3) << 2)) << 4); }
 
-// Element (n, k) of the stage starting at k0 is base[(k0 + k) * ld + n], zero
-// where k0 + k >= klim or n >= nlim (nlim a multiple of 8).  Thread tid owns
-// chunk tid % (ROWS/8) of k-rows tid/(ROWS/8) + i*(NT*8/ROWS).  Out-of-range
-// reads are clamped to a valid address and zeroed with selects (no branches).
+// 1 KB block q holds k-rows q*KPB .. q*KPB+KPB-1; lane l takes k-row
+// q*KPB + l/CPR at physical chunk l%CPR, logical chunk (l%CPR) ^ 4*(k%4).
+// Element (n, k) of the stage at k0 is at byte ((k0 + k) * ld + n) * 2 from
+// base.  k-rows at or past the stage's valid count are read from its last
+// valid row and zeroed in LDS once landed (zero_tail), so a partial last
+// stage adds nothing; columns at or past nlim are read from column 0: they
+// feed only output rows/columns that are never stored.
 template <int ROWS, int NT>
-struct ColLoader {
+struct NLoad {
     static constexpr int CPR = ROWS / 8;
-    static constexpr int KSTEP = NT / CPR;
-    static constexpr int CPT = 64 / KSTEP;
-    static_assert(NT % CPR == 0 && 64 % KSTEP == 0, "chunks split evenly");
-    const uint16_t *base;
-    int64_t ld, klim, ncol;
-    bool nok;
-    int c, k0r;
-    u32x4_t reg[MOE_PREFETCH][CPT];
-    MOE_DEV void init(int tid, const uint16_t *b, int64_t ld_, int64_t n0, int64_t nlim,
-                      int64_t klim_)
+    static constexpr int KPB = 64 / CPR;
+    static constexpr int NI = 64 / KPB / (NT / 64);
+    static_assert(NI * KPB * (NT / 64) == 64, "1 KB blocks split evenly over the waves");
+    const char *base;
+    uint32_t ldb;       // bytes per k-row
+    uint32_t ncol[NI];  // byte offset of the lane's 8 columns in block i
+    int q0, lane;
+    MOE_DEV int krow(int i) const { return (q0 + i) * KPB + lane / CPR; }
+    MOE_DEV void init(const void *b, int64_t ld, int64_t n0, int64_t nlim, int wave, int ln)
     {
-        base = b;
-        ld = ld_;
-        klim = klim_;
-        c = tid % CPR;
-        k0r = tid / CPR;
-        const int64_t n = n0 + c * 8;
-        nok = n < nlim;
-        ncol = nok ? n : 0;
-    }
-    MOE_DEV int krow(int i) const { return k0r + i * KSTEP; }
-    template <int S>
-    MOE_DEV void load(int64_t k0)
-    {
+        base = (const char *)b;
+        ldb = (uint32_t)(ld * 2);
+        q0 = wave * NI;
+        lane = ln;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int64_t k = k0 + krow(i);
-            const bool ok = nok && k < klim;
-            const int64_t kc = k < klim ? k : klim - 1;
-            u32x4_t v = *(const u32x4_t *)(base + kc * ld + ncol);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = ok ? v[q] : 0u;
-            reg[S][i] = v;
+        for (int i = 0; i < NI; ++i) {
+            const int k = krow(i);
+            const int c = (lane % CPR) ^ ((k & 3) << 2);
+            int64_t n = n0 + c * 8;
+            if (n >= nlim) n = 0;
+            ncol[i] = (uint32_t)(n * 2);
         }
     }
-    template <int S>
-    MOE_DEV void store(lds_t *lds) const
+    MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid) const
     {
+        const char *p = base + k0 * (int64_t)ldb;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) *(lds_u32x4 *)(lds + nmaj_off<ROWS>(krow(i), c)) = reg[S][i];
+        for (int i = 0; i < NI; ++i) {
+            int k = krow(i);
+            if (k >= kvalid) k = kvalid - 1;
+            copy16_to_lds(p + (uint32_t)k * ldb + ncol[i], tile + (q0 + i) * 1024);
+        }
+    }
+    MOE_DEV void zero_tail(lds_t *tile, int kvalid) const
+    {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (krow(i) >= kvalid) *(lds_u32x4 *)(tile + (q0 + i) * 1024 + lane * 16) = z;
     }
 };
 
@@ -211,77 +225,49 @@ MOE_DEV void mma_stage(const lds_t *As, const lds_t *Bs, Acc<C> &acc, int wm, in
     }
 }
 
-template <int S>
-struct SetTag {
-    static constexpr int value = S;
-};
-
-#ifndef MOE_PREFETCH
-#define MOE_PREFETCH 1
-#endif
-
-// Main loop over nk stages of 64 k.  Stage s computes from LDS buffer s%2.
-// Prefetch distance 1: the loads of stage s+1 are issued before the MFMAs of
-// stage s and stored to the other LDS buffer after them.  Prefetch distance 2
-// (two register sets): the loads of stage s+2 fill register set s%2 while
-// set (s+1)%2, loaded during stage s-1, is stored; unrolled by two so each
-// register set index is static.
-template <class C, bool A_NMAJ, bool B_NMAJ, class LA, class LB>
-MOE_DEV void mainloop(lds_t *lds, int nk, LA &la, LB &lb, Acc<C> &acc)
+// Main loop over the K/64 stages, two LDS buffers.  Stage s: issue the
+// copies of stage s+1 into the other buffer (free: every wave passed the
+// barrier that ended stage s-1), run the MFMAs of stage s, wait for this
+// wave's copies, zero a partial last stage's tail rows (KTAIL), barrier.
+// One barrier a stage covers both hazards: the next stage's data has landed
+// for every wave, and no wave still reads the buffer the stage after will
+// overwrite.
+template <class C, bool A_NMAJ, bool B_NMAJ, bool KTAIL, class LA, class LB>
+MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> &acc)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     lds_t *As[2] = {lds, lds + C::BM * 128};
     lds_t *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
     acc.zero();
+    const int nk = (int)ceil_div(K, BK);
     if (nk <= 0) return;
-    la.template load<0>(0);
-    lb.template load<0>(0);
-#if MOE_PREFETCH == 2
-    if (nk > 1) {
-        la.template load<1>(BK);
-        lb.template load<1>(BK);
-    }
-#endif
-    la.template store<0>(As[0]);
-    lb.template store<0>(Bs[0]);
-    __syncthreads();
-#if MOE_PREFETCH == 2
-    auto step = [&](auto tag, int s) {
-        constexpr int S = decltype(tag)::value;
-        if (s + 2 < nk) {
-            la.template load<S>((int64_t)(s + 2) * BK);
-            lb.template load<S>((int64_t)(s + 2) * BK);
-        }
-        mma_stage<C, A_NMAJ, B_NMAJ>(As[S], Bs[S], acc, wm, wn, lane);
-        if (s + 1 < nk) {
-            la.template store<1 - S>(As[1 - S]);
-            lb.template store<1 - S>(Bs[1 - S]);
-        }
-        __syncthreads();
+    auto kvalid = [&](int s) -> int {
+        const int64_t rem = K - (int64_t)s * BK;
+        return KTAIL ? (rem < BK ? (int)rem : BK) : BK;
     };
-    int s = 0;
-    for (; s + 1 < nk; s += 2) {
-        step(SetTag<0>(), s);
-        step(SetTag<1>(), s + 1);
-    }
-    if (s < nk) step(SetTag<0>(), s);
-#else
+    auto fill = [&](int s, int buf) {
+        la.issue(As[buf], (int64_t)s * BK, kvalid(s));
+        lb.issue(Bs[buf], (int64_t)s * BK, kvalid(s));
+    };
+    auto land = [&](int s, int buf) {
+        wait_copies();
+        if (KTAIL && kvalid(s) < BK) {
+            la.zero_tail(As[buf], kvalid(s));
+            lb.zero_tail(Bs[buf], kvalid(s));
+        }
+    };
+    fill(0, 0);
+    land(0, 0);
+    __syncthreads();
     for (int s = 0; s < nk; ++s) {
         const int cur = s & 1;
         const bool more = s + 1 < nk;
-        if (more) {
-            la.template load<0>((int64_t)(s + 1) * BK);
-            lb.template load<0>((int64_t)(s + 1) * BK);
-        }
+        if (more) fill(s + 1, cur ^ 1);
         mma_stage<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], acc, wm, wn, lane);
-        if (more) {
-            la.template store<0>(As[cur ^ 1]);
-            lb.template store<0>(Bs[cur ^ 1]);
-        }
+        if (more) land(s + 1, cur ^ 1);
         __syncthreads();
     }
-#endif
 }
 
 // The MFMA takes the B fragment as its first operand, so each 32x32 block
@@ -403,31 +389,31 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
     const int nN = (int)ceil_div(I, C::BN / 2);
     MTile t;
     if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
-    const int tid = threadIdx.x;
-    RowLoader<C::BM, C::NT> la;
-    RowLoader<C::BN, C::NT> lb;
-    la.init(tid, g.x);
+    const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(g.x, wave0);
     const uint16_t *w1e = g.w1 + (int64_t)t.e * 2 * I * H;
-    lb.init(tid, w1e);
+    lb.init(w1e, wave0);
     const int64_t i0 = (int64_t)t.nt * (C::BN / 2);
 #pragma unroll
-    for (int q = 0; q < la.CPT; ++q) {
-        int64_t m = t.m0 + la.row(q);
+    for (int q = 0; q < la.NI; ++q) {
+        int64_t m = t.m0 + la.row(q, lane0);
         if (m >= t.seg_end) m = t.seg_end - 1;
-        la.off[q] = (uint32_t)((g.row_map[m] / g.k) * (int64_t)H);
+        la.set(q, lane0, (uint32_t)((g.row_map[m] / g.k) * (int64_t)H * 2));
     }
 #pragma unroll
-    for (int q = 0; q < lb.CPT; ++q) {
-        int r = lb.row(q);
+    for (int q = 0; q < lb.NI; ++q) {
+        int r = lb.row(q, lane0);
         int wn = r / C::WN, qq = r % C::WN;
         int half = C::WN / 2;
         int64_t i = i0 + wn * half + (qq < half ? qq : qq - half);
         if (i >= I) i = I - 1;
         int64_t n = qq < half ? i : I + i;
-        lb.off[q] = (uint32_t)(n * H);
+        lb.set(q, lane0, (uint32_t)(n * H * 2));
     }
     Acc<C> acc;
-    mainloop<C, false, false>(lds, H / BK, la, lb, acc);
+    mainloop<C, false, false, false>(lds, H, la, lb, acc);
 
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -471,27 +457,27 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
     const int nN = (int)ceil_div(H, C::BN);
     MTile t;
     if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
-    const int tid = threadIdx.x;
-    RowLoader<C::BM, C::NT> la;
-    RowLoader<C::BN, C::NT> lb;
-    la.init(tid, g.a);
+    const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(g.a, wave0);
     const uint16_t *w2e = g.w2 + (int64_t)t.e * H * I;
-    lb.init(tid, w2e);
+    lb.init(w2e, wave0);
 #pragma unroll
-    for (int q = 0; q < la.CPT; ++q) {
-        int64_t m = t.m0 + la.row(q);
+    for (int q = 0; q < la.NI; ++q) {
+        int64_t m = t.m0 + la.row(q, lane0);
         if (m >= t.seg_end) m = t.seg_end - 1;
-        la.off[q] = (uint32_t)(m * I);
+        la.set(q, lane0, (uint32_t)(m * I * 2));
     }
     const int64_t n0 = (int64_t)t.nt * C::BN;
 #pragma unroll
-    for (int q = 0; q < lb.CPT; ++q) {
-        int64_t n = n0 + lb.row(q);
+    for (int q = 0; q < lb.NI; ++q) {
+        int64_t n = n0 + lb.row(q, lane0);
         if (n >= H) n = H - 1;
-        lb.off[q] = (uint32_t)(n * I);
+        lb.set(q, lane0, (uint32_t)(n * I * 2));
     }
     Acc<C> acc;
-    mainloop<C, false, false>(lds, I / BK, la, lb, acc);
+    mainloop<C, false, false, false>(lds, I, la, lb, acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     store_rows_f32<C>(acc, g.o, t.m0, t.seg_end, n0, H, wm, wn, lane);
@@ -511,22 +497,22 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     const int nN = (int)ceil_div(I, C::BN);
     MTile t;
     if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
-    const int tid = threadIdx.x;
-    RowLoader<C::BM, C::NT> la;
-    ColLoader<C::BN, C::NT> lb;
-    la.init(tid, g.dy);
+    const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    NLoad<C::BN, C::NT> lb;
+    la.init(g.dy, wave0);
 #pragma unroll
-    for (int q = 0; q < la.CPT; ++q) {
-        int64_t m = t.m0 + la.row(q);
+    for (int q = 0; q < la.NI; ++q) {
+        int64_t m = t.m0 + la.row(q, lane0);
         if (m >= t.seg_end) m = t.seg_end - 1;
-        la.off[q] = (uint32_t)((g.row_map[m] / g.k) * (int64_t)H);
+        la.set(q, lane0, (uint32_t)((g.row_map[m] / g.k) * (int64_t)H * 2));
     }
     const uint16_t *w2e = g.w2 + (int64_t)t.e * H * I;
     const int64_t n0 = (int64_t)t.nt * C::BN;
     // B(n = i, k = hh) = w2[e, hh, i]: k-row hh starts at w2e + hh*I
-    lb.init(tid, w2e, I, n0, I, H);
+    lb.init(w2e, I, n0, I, wave0, lane0);
     Acc<C> acc;
-    mainloop<C, false, true>(lds, H / BK, la, lb, acc);
+    mainloop<C, false, true, false>(lds, H, la, lb, acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     lds_f32 *red = (lds_f32 *)lds;  // [WAVES_N][BM]; the LDS tiles are free now
@@ -586,22 +572,22 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     const int nN = (int)ceil_div(H, C::BN);
     MTile t;
     if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
-    const int tid = threadIdx.x;
-    RowLoader<C::BM, C::NT> la;
-    ColLoader<C::BN, C::NT> lb;
-    la.init(tid, g.dh);
+    const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    NLoad<C::BN, C::NT> lb;
+    la.init(g.dh, wave0);
 #pragma unroll
-    for (int q = 0; q < la.CPT; ++q) {
-        int64_t m = t.m0 + la.row(q);
+    for (int q = 0; q < la.NI; ++q) {
+        int64_t m = t.m0 + la.row(q, lane0);
         if (m >= t.seg_end) m = t.seg_end - 1;
-        la.off[q] = (uint32_t)(m * 2 * I);
+        la.set(q, lane0, (uint32_t)(m * 2 * I * 2));
     }
     const uint16_t *w1e = g.w1 + (int64_t)t.e * 2 * I * H;
     const int64_t n0 = (int64_t)t.nt * C::BN;
     // B(n = hh, k = nn) = w1[e, nn, hh]: k-row nn starts at w1e + nn*H
-    lb.init(tid, w1e, H, n0, H, 2 * I);
+    lb.init(w1e, H, n0, H, wave0, lane0);
     Acc<C> acc;
-    mainloop<C, false, true>(lds, 2 * I / BK, la, lb, acc);
+    mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     store_rows_f32<C>(acc, g.dxp, t.m0, t.seg_end, n0, H, wm, wn, lane);
@@ -652,13 +638,12 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     // of this expert, so the loaders start at row seg0 and stop at seg1.
     const uint16_t *Ab = (UP ? g.dh : g.dyw) + seg0 * R;
     const uint16_t *Bb = (UP ? g.xg : g.a) + seg0 * Cc;
-    ColLoader<C::BM, C::NT> la;
-    ColLoader<C::BN, C::NT> lb;
-    la.init(tid, Ab, R, r0, R, cnt);
-    lb.init(tid, Bb, Cc, c0, Cc, cnt);
-    const int nk = (int)ceil_div(cnt, BK);
+    NLoad<C::BM, C::NT> la;
+    NLoad<C::BN, C::NT> lb;
+    la.init(Ab, R, r0, R, wave_uniform_id(), lane);
+    lb.init(Bb, Cc, c0, Cc, wave_uniform_id(), lane);
     Acc<C> acc;
-    mainloop<C, true, true>(lds, nk, la, lb, acc);
+    mainloop<C, true, true, true>(lds, cnt, la, lb, acc);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         const int64_t rr = r0 + acc_row<C>(wm, i, lane);
