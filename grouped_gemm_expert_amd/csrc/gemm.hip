@@ -58,13 +58,20 @@ struct TileCfg {
 // while the MFMAs of the previous stage execute; there are no staging
 // registers and no ds_write in the main loop.
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 MOE_DEV int wave_uniform_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// The copy is issued from inline assembly: the compiler then does not track
+// it, so it inserts no vmcnt wait in front of the LDS reads of the other
+// buffer (it cannot prove that those do not alias the copy's destination);
+// the main loop waits for its copies itself (wait_copies) before the barrier
+// that publishes them.  M0 carries the LDS block address.
 MOE_DEV void copy16_to_lds(const char *src, lds_t *dst_block)
 {
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst_block, 16, 0, 0);
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_block);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0v)
+                 : "memory", "m0");
 }
 
 // Wait until every global->LDS copy this wave issued has landed: s_waitcnt
