@@ -31,6 +31,15 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_wgrad"]
+# kernel-name fragment of each grouped-GEMM op in a rocprofv3 trace
+GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k_down_dgrad<",
+                "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<"}
+# The measured HBM traffic of the grouped GEMMs lives in this file, next to a
+# hash of the kernel sources it was taken with; a changed kernel reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
+                  for f in ("gemm.hip", "common.h")]
+COPY_BYTES = 1 << 30        # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
 def log(*a):
@@ -127,6 +136,99 @@ def run_gpu(args, w):
     return dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved)
 
 
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from the committed PMC record, or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = [l for l in fh if l.startswith("traffic-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("traffic-record: "):])
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    e = rec["kernels"].get(stage)
+    return None if e is None else e["hbm_bytes"]
+
+
+def copy_calibration():
+    """A plain 1 GiB device copy, three times, as an elementwise kernel (b = a * 1,
+    so that it is a kernel and not a DMA transfer): the reference whose
+    FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {COPY_BYTES} bytes 3 times")
+
+
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
+    """Turn four rocprofv3 --pmc runs (bench FETCH_SIZE, bench WRITE_SIZE, copy
+    FETCH_SIZE, copy WRITE_SIZE) into the traffic record bench.py reads."""
+    import csv
+    import glob
+
+    def rows(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        out.sort()
+        return out
+
+    def copy_kib(d, counter):
+        v = [x for _, n, x in rows(d, counter) if "MulFunctor" in n]
+        return sorted(v)[len(v) // 2]
+
+    kib = COPY_BYTES / 1024.0
+    sf = kib / copy_kib(cfetch_dir, "FETCH_SIZE")
+    sw = kib / copy_kib(cwrite_dir, "WRITE_SIZE")
+    fetch, write = rows(fetch_dir, "FETCH_SIZE"), rows(write_dir, "WRITE_SIZE")
+    kern = {}
+    for stage, frag in GEMM_KERNELS.items():
+        want_up = stage == "up_wgrad"
+        def pick(rs):
+            v = [x for _, n, x in rs if frag in n and
+                 (stage not in ("down_wgrad", "up_wgrad") or n.split(">")[-2].strip().endswith("true") == want_up)]
+            return sum(v) / len(v) if v else None
+        f, wr = pick(fetch), pick(write)
+        if f is None or wr is None:
+            continue
+        kern[stage] = {"fetch_kib": round(f, 1), "write_kib": round(wr, 1),
+                       "hbm_bytes": int(round((f * sf + wr * sw) * 1024))}
+    rec = {"source_hash": kernel_source_hash(), "copy_scale_fetch": round(sf, 4),
+           "copy_scale_write": round(sw, 4), "kernels": kern}
+    L = ["# HBM traffic of the grouped GEMMs: DeepSeek-V3-style MoE layer (T=8192 H=7168 I=2048 "
+         "E=256 G=8 kg=4 k=8), MI355X", "",
+         "Commands (from the repository root on the GPU box):", "", "```"] + cmds + ["```", "",
+         f"Calibration: a plain {COPY_BYTES} byte device copy reads FETCH_SIZE x {sf:.4f} and "
+         f"WRITE_SIZE x {sw:.4f} of its true size; the per-launch figures below are scaled by "
+         "those factors.", "",
+         "| op | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | HBM bytes/launch (scaled) |",
+         "|---|---:|---:|---:|"]
+    for k, v in kern.items():
+        L.append(f"| {k} | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | {v['hbm_bytes']:,} |")
+    L += ["", "traffic-record: " + json.dumps(rec)]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def cpu_baseline(w, d, target_s=12.0):
     """The oracle (as it stands) on a bounded sample of the same workload: the
     first S tokens as a batch -- router projection, routing, expert forward,
@@ -198,7 +300,18 @@ def main():
     ap.add_argument("--workload", default="deepseek_v3")
     ap.add_argument("--dw-mode", choices=["accumulate", "overwrite"], default="accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB copy that calibrates the PMC byte counters")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the traffic record from four rocprofv3 --pmc output folders")
+    ap.add_argument("--pmc-commands", default="", help="commands recorded with --pmc-summary (;-separated)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, TRAFFIC_FILE, [c.strip() for c in args.pmc_commands.split(";") if c.strip()])
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -250,7 +363,8 @@ def main():
                    "dw": f"fp32 {args.dw_mode}", "outputs": "fp32 y/dx, bf16 operands"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom)},
         "grouped_gemm": {"TFLOP/s": round(gemm_tflops, 1),
                          "pct_of_bf16_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
                          "flops_per_step": total_gemm_flops,

@@ -706,16 +706,14 @@ hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *count
 }
 
 // ----------------------------------------------------------------- launch ----
-#ifndef MOE_TILE_BM
-#define MOE_TILE_BM 256
-#define MOE_TILE_BN 256
-#define MOE_TILE_WM 64
-#define MOE_TILE_WN 128
-#endif
-// 256x256 output tiles, 8 waves of 64x128 by default (two waves per SIMD)
-using Big = TileCfg<MOE_TILE_BM, MOE_TILE_BN, MOE_TILE_WM, MOE_TILE_WN>;
+// 256x256 output tiles computed by 8 waves (two a SIMD).  Wave tiles are
+// 128 rows x 64 columns where the column operand is read with transposing LDS
+// reads (down_dgrad, up_dgrad: the transposed operand then supplies the
+// smaller fragment count) and for up_swiglu; 64 x 128 elsewhere.
+using Tall = TileCfg<256, 256, 128, 64>;
+using Wide = TileCfg<256, 256, 64, 128>;
 
-int32_t dgrad2_cols(int32_t I) { return (int32_t)ceil_div(I, Big::BN); }
+int32_t dgrad2_cols(int32_t I) { return (int32_t)ceil_div(I, Tall::BN); }
 
 template <class K>
 static hipError_t launch_k(K kern, int64_t blocks, const GemmArgs &g, hipStream_t s, int nt)
@@ -727,24 +725,33 @@ static hipError_t launch_k(K kern, int64_t blocks, const GemmArgs &g, hipStream_
 
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
 {
-    using C = Big;
     switch (op) {
-    case MOE_GEMM_UP_SWIGLU:
+    case MOE_GEMM_UP_SWIGLU: {
+        using C = Tall;
         return launch_k(k_up_swiglu<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2)),
                         g, s, C::NT);
-    case MOE_GEMM_DOWN:
+    }
+    case MOE_GEMM_DOWN: {
+        using C = Wide;
         return launch_k(k_down<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
-    case MOE_GEMM_DOWN_DGRAD:
+    }
+    case MOE_GEMM_DOWN_DGRAD: {
+        using C = Tall;
         return launch_k(k_down_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN)),
                         g, s, C::NT);
-    case MOE_GEMM_UP_DGRAD:
+    }
+    case MOE_GEMM_UP_DGRAD: {
+        using C = Tall;
         return launch_k(k_up_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
+    }
     case MOE_GEMM_DOWN_WGRAD: {
+        using C = Wide;
         const int64_t act = g.M < g.E ? g.M : g.E;  // non-empty experts, at most
         int64_t total = act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN);
         return launch_k(k_wgrad<C, false>, grid_for(total), g, s, C::NT);
     }
     case MOE_GEMM_UP_WGRAD: {
+        using C = Wide;
         const int64_t act = g.M < g.E ? g.M : g.E;
         int64_t total = act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN);
         return launch_k(k_wgrad<C, true>, grid_for(total), g, s, C::NT);
