@@ -38,7 +38,7 @@ GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k
 # hash of the kernel sources it was taken with; a changed kernel reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
-                  for f in ("gemm.hip", "common.h")]
+                  for f in ("gemm.hip", "tile.h", "common.h")]
 COPY_BYTES = 1 << 30        # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 

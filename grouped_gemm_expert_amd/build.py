@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "router.hip", "permute.hip", "gemm.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "router.hip", "permute.hip", "gemm.hip", "dense.hip", "elementwise.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # No packed fp32 instructions: keep every fp32 op scalar on this target.

@@ -35,6 +35,7 @@ struct FwdWs {
     Sched sched;
     float *wrow;
     float *o;   // [M,H] fp32; the single-op grouped GEMMs reuse it for xg / dyw
+    void *router;  // router GEMM scratch (router_ws_bytes_fwd)
 };
 
 struct BwdWs {
@@ -45,6 +46,7 @@ struct BwdWs {
     float *wrow;
     uint16_t *xg;
     uint16_t *dyw;
+    void *router;  // router GEMM scratch (router_ws_bytes_bwd)
 };
 
 FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
@@ -59,6 +61,7 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     w.sched.order = cv.take<int32_t>(c.E + 1);
     w.wrow = cv.take<float>(M);
     w.o = cv.take<float>(M * c.H);
+    w.router = cv.take<char>((int64_t)router_ws_bytes_fwd(c.T, c.E, c.H));
     if (bytes) *bytes = cv.used;
     return w;
 }
@@ -77,6 +80,7 @@ BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
     w.wrow = cv.take<float>(M);
     w.xg = cv.take<uint16_t>(M * c.H);
     w.dyw = cv.take<uint16_t>(M * c.H);
+    w.router = cv.take<char>((int64_t)router_ws_bytes_bwd(c.T, c.E, c.H));
     if (bytes) *bytes = cv.used;
     return w;
 }
@@ -245,8 +249,7 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
     }
     if (Wr) {
         StageMark mark(MOE_STAGE_ROUTER_PROJ, stream);
-        MOE_TRY(launch_simt_gemm(c.T, c.E, c.H, x, true, c.H, 1, Wr, false, c.H, 1, logits, c.E,
-                                 false, stream));
+        MOE_TRY(launch_router_logits(c.T, c.E, c.H, x, Wr, logits, w.router, stream));
     }
     RouterArgs ra;
     ra.T = c.T;
@@ -505,11 +508,7 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
     }
     if (Wr) {
         StageMark mark(MOE_STAGE_ROUTER_GRADS, stream);
-        MOE_TRY(launch_simt_gemm(c.T, c.H, c.E, dlogits, false, c.E, 1, Wr, false, 1, c.H, dx, c.H,
-                                 true, stream));
-        if (dWr)
-            MOE_TRY(launch_simt_gemm(c.E, c.H, c.T, dlogits, false, 1, c.E, x, true, 1, c.H, dWr,
-                                     c.H, false, stream));
+        MOE_TRY(launch_router_grads(c.T, c.E, c.H, dlogits, x, Wr, dx, dWr, w.router, stream));
     }
     return MOE_OK;
 }

@@ -74,11 +74,17 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s);
 
-// fp32-accumulating SIMT GEMM: C[m,n] (=|+=) sum_k A(m,k) * B(n,k), with
-// A(m,k) = A[m*sam + k*sak], B(n,k) = B[n*sbn + k*sbk]; A/B bf16 or fp32.
-hipError_t launch_simt_gemm(int64_t Mr, int64_t Nc, int64_t K, const void *A, bool a_bf16,
-                            int64_t sam, int64_t sak, const void *B, bool b_bf16, int64_t sbn,
-                            int64_t sbk, float *C, int64_t ldc, bool accumulate, hipStream_t s);
+// Router GEMMs on bf16 MFMA with exact three-way bf16 splits of the fp32
+// operands (fp32-accurate products, fp32 accumulation).  The workspace sizes
+// are what the two calls need (device memory, 256-byte aligned).
+size_t router_ws_bytes_fwd(int64_t T, int32_t E, int32_t H);
+size_t router_ws_bytes_bwd(int64_t T, int32_t E, int32_t H);
+// logits[T, E] = x[T, H] . Wr[E, H]^T
+hipError_t launch_router_logits(int64_t T, int32_t E, int32_t H, const uint16_t *x, const float *Wr,
+                                float *logits, void *ws, hipStream_t s);
+// dx[T, H] += dl[T, E] . Wr[E, H];  dWr[E, H] = dl^T . x  (if dWr)
+hipError_t launch_router_grads(int64_t T, int32_t E, int32_t H, const float *dl, const uint16_t *x,
+                               const float *Wr, float *dx, float *dWr, void *ws, hipStream_t s);
 
 // router: selection + weights + counts + aux partial sums; then aux finalize
 struct RouterArgs {

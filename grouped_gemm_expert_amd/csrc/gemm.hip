@@ -22,303 +22,10 @@
 // (accumulate).  Block
 // indices are remapped so that each of the 8 XCDs works on a contiguous run
 // of tiles (neighbouring tiles share operand panels in that XCD's L2).
-#include "common.h"
+#include "tile.h"
 
 namespace moe {
 
-constexpr int BK = 64;  // k elements per LDS stage
-
-// LDS is addressed through explicit local-address-space pointers so that the
-// compiler emits ds_read / ds_write (a generic pointer would become FLAT).
-typedef __attribute__((address_space(3))) char lds_t;
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
-typedef __attribute__((address_space(3))) float lds_f32;
-
-MOE_DEV int swz(int r) { return (r ^ (r >> 3)) & 7; }
-MOE_DEV int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
-
-template <int BM_, int BN_, int WM_, int WN_>
-struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-    static constexpr int NT = WAVES_M * WAVES_N * 64;
-    static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int LDS_BYTES = 2 * (BM + BN) * 128;
-    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
-    static_assert(BM == 256 || BM == 128, "m-tile prefix sums exist for 256 and 128 rows");
-};
-
-// ------------------------------------------------------------- loaders ----
-// Operand tiles go from global memory straight into LDS (gfx950
-// global_load_lds_dwordx4): lane l of a wave writes bytes [16 l, 16 l + 16)
-// of a 1 KB LDS block whose address is uniform over the wave (it travels in
-// M0), so each loader picks, per lane, the 16 global bytes that belong at
-// that LDS position under the tile's swizzle.  The copies run asynchronously
-// while the MFMAs of the previous stage execute; there are no staging
-// registers and no ds_write in the main loop.
-
-MOE_DEV int wave_uniform_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
-
-// The copy is issued from inline assembly: the compiler then does not track
-// it, so it inserts no vmcnt wait in front of the LDS reads of the other
-// buffer (it cannot prove that those do not alias the copy's destination);
-// the main loop waits for its copies itself (wait_copies) before the barrier
-// that publishes them.  M0 carries the LDS block address.
-MOE_DEV void copy16_to_lds(const char *src, lds_t *dst_block)
-{
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_block);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(m0v)
-                 : "memory", "m0");
-}
-
-// Wait until every global->LDS copy this wave issued has landed: s_waitcnt
-// vmcnt(0) (expcnt and lgkmcnt fields left at their maxima).
-MOE_DEV void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// K-major tile: ROWS x 64 with k contiguous (128 bytes a row; chunk c of row r
-// at lds_off(r, c)).  1 KB block q holds rows 8q .. 8q+7; wave w fills blocks
-// w*NI .. w*NI+NI-1, and its lane l takes row 8q + l/8 at physical chunk l%8,
-// i.e. logical chunk (l%8) ^ swz(row).  off[i] is the byte offset of that
-// lane's 16 bytes from `base` at k = 0 (rows may be gathered).
-template <int ROWS, int NT>
-struct KLoad {
-    static constexpr int NI = ROWS / 8 / (NT / 64);
-    static_assert(NI * 8 * (NT / 64) == ROWS, "1 KB blocks split evenly over the waves");
-    const char *base;
-    uint32_t off[NI];
-    int q0;
-    MOE_DEV void init(const void *b, int wave) { base = (const char *)b; q0 = wave * NI; }
-    MOE_DEV int row(int i, int lane) const { return (q0 + i) * 8 + (lane >> 3); }
-    MOE_DEV void set(int i, int lane, uint32_t row_bytes)
-    {
-        off[i] = row_bytes + ((uint32_t)((lane & 7) ^ swz(row(i, lane))) << 4);
-    }
-    MOE_DEV void issue(lds_t *tile, int64_t k0, int) const
-    {
-        const char *p = base + k0 * 2;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) copy16_to_lds(p + off[i], tile + (q0 + i) * 1024);
-    }
-    MOE_DEV void zero_tail(lds_t *, int) const {}
-};
-
-// N-major tile: 64 k-rows x ROWS, the other index contiguous (ROWS*2 bytes a
-// k-row), in the source's own layout; the MFMA fragments are read from it
-// with transposing LDS reads.  16-byte chunk c of k-row k sits at
-// nmaj_off(k, c): the chunk index is XORed with 4*(k % 4), which keeps the
-// transposing reads free of bank conflicts.
-template <int ROWS>
-MOE_DEV int nmaj_off(int k, int c) { return k * (ROWS * 2) + ((c ^ ((k & 3) << 2)) << 4); }
-
-// 1 KB block q holds k-rows q*KPB .. q*KPB+KPB-1; lane l takes k-row
-// q*KPB + l/CPR at physical chunk l%CPR, logical chunk (l%CPR) ^ 4*(k%4).
-// Element (n, k) of the stage at k0 is at byte ((k0 + k) * ld + n) * 2 from
-// base.  k-rows at or past the stage's valid count are read from its last
-// valid row and zeroed in LDS once landed (zero_tail), so a partial last
-// stage adds nothing; columns at or past nlim are read from column 0: they
-// feed only output rows/columns that are never stored.
-template <int ROWS, int NT>
-struct NLoad {
-    static constexpr int CPR = ROWS / 8;
-    static constexpr int KPB = 64 / CPR;
-    static constexpr int NI = 64 / KPB / (NT / 64);
-    static_assert(NI * KPB * (NT / 64) == 64, "1 KB blocks split evenly over the waves");
-    const char *base;
-    uint32_t ldb;       // bytes per k-row
-    uint32_t ncol[NI];  // byte offset of the lane's 8 columns in block i
-    int q0, lane;
-    MOE_DEV int krow(int i) const { return (q0 + i) * KPB + lane / CPR; }
-    MOE_DEV void init(const void *b, int64_t ld, int64_t n0, int64_t nlim, int wave, int ln)
-    {
-        base = (const char *)b;
-        ldb = (uint32_t)(ld * 2);
-        q0 = wave * NI;
-        lane = ln;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int k = krow(i);
-            const int c = (lane % CPR) ^ ((k & 3) << 2);
-            int64_t n = n0 + c * 8;
-            if (n >= nlim) n = 0;
-            ncol[i] = (uint32_t)(n * 2);
-        }
-    }
-    MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid) const
-    {
-        const char *p = base + k0 * (int64_t)ldb;
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            int k = krow(i);
-            if (k >= kvalid) k = kvalid - 1;
-            copy16_to_lds(p + (uint32_t)k * ldb + ncol[i], tile + (q0 + i) * 1024);
-        }
-    }
-    MOE_DEV void zero_tail(lds_t *tile, int kvalid) const
-    {
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-            if (krow(i) >= kvalid) *(lds_u32x4 *)(tile + (q0 + i) * 1024 + lane * 16) = z;
-    }
-};
-
-// ------------------------------------------------------------ MFMA core ----
-template <class C>
-struct Acc {
-    f32x16_t v[C::FM][C::FN];
-    MOE_DEV void zero()
-    {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
-    }
-};
-
-// MFMA operand fragment for rows rbase + lane%32 and k = kk*16 + (lane/32)*8
-// + [0, 8).  K-major tile: one 16-byte read.  N-major tile: two transposing
-// reads; in each group of 16 lanes, lane 4r+q addresses k-row kb + r at
-// columns 4q..4q+3 of its 16-column slice, and lane j receives the four
-// k-values of column j.
-MOE_DEV bf16x8_t frag_kmaj(const lds_t *T, int rbase, int kk, int lane)
-{
-    return *(const lds_bf16x8 *)(T + lds_off(rbase + (lane & 31), kk * 2 + (lane >> 5)));
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-template <int ROWS>
-MOE_DEV bf16x8_t frag_nmaj(const lds_t *T, int rbase, int kk, int lane)
-{
-    const int g = lane >> 4, j = lane & 15, r = j >> 2, q = j & 3;
-    const int n = rbase + (g & 1) * 16 + 4 * q;
-    const int k = kk * 16 + (g >> 1) * 8 + r;
-    const int within = (q & 1) * 8;
-    v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(T + nmaj_off<ROWS>(k, n >> 3) + within));
-    v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_v4i16 *)(T + nmaj_off<ROWS>(k + 4, n >> 3) + within));
-    typedef short v8i16 __attribute__((ext_vector_type(8)));
-    v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// One 64-deep LDS stage: 4 MFMA k-steps of 16.
-template <class C, bool A_NMAJ, bool B_NMAJ>
-MOE_DEV void mma_stage(const lds_t *As, const lds_t *Bs, Acc<C> &acc, int wm, int wn, int lane)
-{
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        bf16x8_t a[C::FM], b[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
-                          : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
-                          : frag_kmaj(Bs, wn * C::WN + j * 32, kk, lane);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc.v[i][j], 0, 0, 0);
-    }
-}
-
-// Main loop over the K/64 stages, two LDS buffers.  Stage s: issue the
-// copies of stage s+1 into the other buffer (free: every wave passed the
-// barrier that ended stage s-1), run the MFMAs of stage s, wait for this
-// wave's copies, zero a partial last stage's tail rows (KTAIL), barrier.
-// One barrier a stage covers both hazards: the next stage's data has landed
-// for every wave, and no wave still reads the buffer the stage after will
-// overwrite.
-template <class C, bool A_NMAJ, bool B_NMAJ, bool KTAIL, class LA, class LB>
-MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> &acc)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    lds_t *As[2] = {lds, lds + C::BM * 128};
-    lds_t *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
-    acc.zero();
-    const int nk = (int)ceil_div(K, BK);
-    if (nk <= 0) return;
-    auto kvalid = [&](int s) -> int {
-        const int64_t rem = K - (int64_t)s * BK;
-        return KTAIL ? (rem < BK ? (int)rem : BK) : BK;
-    };
-    auto fill = [&](int s, int buf) {
-        la.issue(As[buf], (int64_t)s * BK, kvalid(s));
-        lb.issue(Bs[buf], (int64_t)s * BK, kvalid(s));
-    };
-    auto land = [&](int s, int buf) {
-        wait_copies();
-        if (KTAIL && kvalid(s) < BK) {
-            la.zero_tail(As[buf], kvalid(s));
-            lb.zero_tail(Bs[buf], kvalid(s));
-        }
-    };
-    fill(0, 0);
-    land(0, 0);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        const int cur = s & 1;
-        const bool more = s + 1 < nk;
-        if (more) fill(s + 1, cur ^ 1);
-        mma_stage<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], acc, wm, wn, lane);
-        if (more) land(s + 1, cur ^ 1);
-        __syncthreads();
-    }
-}
-
-// The MFMA takes the B fragment as its first operand, so each 32x32 block
-// holds the transposed product: element r of acc.v[i][j] is
-//   tile row (from A) = wm*WM + i*32 + lane%32
-//   tile col (from B) = wn*WN + j*32 + (r/4)*8 + (lane/32)*4 + r%4
-// i.e. every lane owns one row and four runs of four consecutive columns,
-// which the epilogues store as 8- or 16-byte vectors.
-template <class C>
-MOE_DEV int acc_row(int wm, int i, int lane) { return wm * C::WM + i * 32 + (lane & 31); }
-template <class C>
-MOE_DEV int acc_col(int wn, int j, int rg, int lane)
-{
-    return wn * C::WN + j * 32 + rg * 8 + (lane >> 5) * 4;
-}
-
-MOE_DEV uint64_t pack_bf4(float a, float b, float c, float d)
-{
-    return (uint64_t)pack_bf2(a, b) | ((uint64_t)pack_bf2(c, d) << 32);
-}
-MOE_DEV void unpack_bf4(uint64_t v, float (&o)[4])
-{
-    o[0] = bf2f((uint16_t)(v & 0xffffu));
-    o[1] = bf2f((uint16_t)((v >> 16) & 0xffffu));
-    o[2] = bf2f((uint16_t)((v >> 32) & 0xffffu));
-    o[3] = bf2f((uint16_t)(v >> 48));
-}
-
-// ------------------------------------------------------- tile schedules ----
-// XCD-aware remap of block b over `total` tiles.  Blocks are dispatched to
-// the 8 XCDs round-robin (block b runs on XCD b % 8); consecutive tiles are
-// dealt to the XCDs in chunks of XCD_CHUNK (the CUs of one XCD), so the tiles
-// an XCD runs together are neighbours (they share operand panels in its L2)
-// while tiles of unequal cost spread evenly over all XCDs.  The grid is a
-// multiple of 8 * XCD_CHUNK and at least `total` rounded up to that.
-constexpr int64_t XCD_CHUNK = 32;
-MOE_DEV int64_t xcd_remap(int64_t b, int64_t total)
-{
-    const int64_t x = b & 7, j = b >> 3;
-    const int64_t L = ((j / XCD_CHUNK) * 8 + x) * XCD_CHUNK + (j % XCD_CHUNK);
-    return L < total ? L : -1;
-}
-
-int64_t grid_for(int64_t total) { return ceil_div(total, 8 * XCD_CHUNK) * 8 * XCD_CHUNK; }
 
 struct MTile {
     int e;

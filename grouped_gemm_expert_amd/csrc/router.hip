@@ -1,5 +1,5 @@
-// Router kernels: fp32 SIMT GEMM (router projection and its gradients),
-// selection + routing weights + counts + aux partials, aux finalize.
+// Router kernels: selection + routing weights + counts + aux partials, aux
+// finalize.  (The router projection and its gradients are in dense.hip.)
 //
 // Follows the MegaMoE page (Primus technical guide), intro: the fused router
 // is a score function, a group-limited top-k and an aux score.
@@ -34,87 +34,6 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s)
     int64_t blocks = ceil_div(n, 256);
     if (blocks > 4096) blocks = 4096;
     k_fill_f32<<<(unsigned)blocks, 256, 0, s>>>(p, n, v);
-    return hipGetLastError();
-}
-
-// ----------------------------------------------------------- SIMT GEMM ----
-// 64x64 output tile, 16-deep k slices through LDS, 256 threads x 4x4 outputs.
-// Plain fp32 FMA accumulation in ascending k order per output.
-template <bool ABF, bool BBF>
-__global__ __launch_bounds__(256) void k_simt_gemm(int64_t Mr, int64_t Nc, int64_t K,
-                                                   const void *Av, int64_t sam, int64_t sak,
-                                                   const void *Bv, int64_t sbn, int64_t sbk,
-                                                   float *C, int64_t ldc, int accumulate)
-{
-    __shared__ float As[16][64 + 4];
-    __shared__ float Bs[16][64 + 4];
-    const int tid = threadIdx.x;
-    const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
-    const int tm = tid / 16, tn = tid % 16;  // 16x16 threads, 4x4 each
-    float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < K; k0 += 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int q = tid + i * 256;      // 0..1023 = 16 k x 64 rows
-            int kk = q / 64, r = q % 64;
-            int64_t m = m0 + r, n = n0 + r, kx = k0 + kk;
-            float av = 0.f, bv = 0.f;
-            if (m < Mr && kx < K) {
-                int64_t off = m * sam + kx * sak;
-                av = ABF ? bf2f(((const uint16_t *)Av)[off]) : ((const float *)Av)[off];
-            }
-            if (n < Nc && kx < K) {
-                int64_t off = n * sbn + kx * sbk;
-                bv = BBF ? bf2f(((const uint16_t *)Bv)[off]) : ((const float *)Bv)[off];
-            }
-            As[kk][r] = av;
-            Bs[kk][r] = bv;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[kk][tm * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tn * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t m = m0 + tm * 4 + i;
-        if (m >= Mr) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int64_t n = n0 + tn * 4 + j;
-            if (n >= Nc) continue;
-            float v = acc[i][j];
-            if (accumulate) v += C[m * ldc + n];
-            C[m * ldc + n] = v;
-        }
-    }
-}
-
-hipError_t launch_simt_gemm(int64_t Mr, int64_t Nc, int64_t K, const void *A, bool a_bf16,
-                            int64_t sam, int64_t sak, const void *B, bool b_bf16, int64_t sbn,
-                            int64_t sbk, float *C, int64_t ldc, bool accumulate, hipStream_t s)
-{
-    if (Mr <= 0 || Nc <= 0) return hipSuccess;
-    dim3 grid((unsigned)ceil_div(Nc, 64), (unsigned)ceil_div(Mr, 64));
-    int acc = accumulate ? 1 : 0;
-    if (a_bf16 && !b_bf16)
-        k_simt_gemm<true, false><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
-    else if (!a_bf16 && b_bf16)
-        k_simt_gemm<false, true><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
-    else if (!a_bf16 && !b_bf16)
-        k_simt_gemm<false, false><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
-    else
-        k_simt_gemm<true, true><<<grid, 256, 0, s>>>(Mr, Nc, K, A, sam, sak, B, sbn, sbk, C, ldc, acc);
     return hipGetLastError();
 }
 
