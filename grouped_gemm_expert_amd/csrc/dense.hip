@@ -80,7 +80,7 @@ __global__ __launch_bounds__(C::NT) void k_dense(DenseArgs d)
         return rem < BK ? (int)rem : BK;
     };
     Acc<C> acc;
-    pipeline<C, A_NMAJ, B_NMAJ>(
+    pipeline<C, A_NMAJ, B_NMAJ, decltype(la)::NI + decltype(lb)::NI>(
         lds, v0, v1,
         [&](int v, lds_t *As, lds_t *Bs) {
             const int t = (int)(v / d.spt);

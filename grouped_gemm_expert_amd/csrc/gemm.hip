@@ -66,29 +66,6 @@ int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
     return grid_for(mt * nN);
 }
 
-// fp32 tile store: rows [m0, seg_end), columns [n0, n0 + BN) below ncols,
-// row stride ncols; 16-byte stores.
-template <class C>
-MOE_DEV void store_rows_f32(const Acc<C> &acc, float *out, int64_t m0, int64_t seg_end, int64_t n0,
-                            int64_t ncols, int wm, int wn, int lane)
-{
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int64_t m = m0 + acc_row<C>(wm, i, lane);
-        if (m >= seg_end) continue;
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int64_t col = n0 + acc_col<C>(wn, j, rg, lane);
-                if (col >= ncols) continue;
-                f32x4_t v = {acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
-                             acc.v[i][j][rg * 4 + 3]};
-                *(f32x4_t *)(out + m * ncols + col) = v;
-            }
-    }
-}
-
 // =========================================================================
 // GEMM1 + SwiGLU:  h[r, n] = x[tok(r)] . w1[e, n, :],  a = silu(g) * u
 // B tile rows: wave column wn covers gate columns i0 + wn*WN/2 + [0, WN/2)
@@ -129,33 +106,56 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
     Acc<C> acc;
     mainloop<C, false, false, false>(lds, H, la, lb, acc);
 
+    // SwiGLU on the fp32 accumulators, then out through LDS: staging row r
+    // holds the tile's 128 gate | 128 up | 128 a values of that row as bf16
+    // (48 chunks of 16 bytes, XOR-swizzled by row), and lane l < 48 writes
+    // chunk l of a row to h (gate, up) or a with one 16-byte store.
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     constexpr int HF = C::FN / 2;
+    constexpr int GCOLS = C::BN / 2;  // gate columns of the tile
+    static_assert(3 * GCOLS == 48 * 8, "staging row = 48 chunks");
+    auto soff = [](int r, int chunk) { return r * (3 * GCOLS * 2) + ((chunk ^ (r & 15)) << 4); };
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int64_t m = t.m0 + acc_row<C>(wm, i, lane);
-        if (m >= t.seg_end) continue;
+    for (int half = 0; half < 2; ++half) {
+        if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
 #pragma unroll
-        for (int j = 0; j < HF; ++j)
+        for (int i = 0; i < C::FM; ++i) {
+            if ((wm * C::WM + i * 32) / EPI_ROWS != half) continue;
+            const int r = acc_row<C>(wm, i, lane) - half * EPI_ROWS;
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                // gate columns of wave column wn start at i0 + wn*WN/2
-                const int64_t col = i0 + wn * (C::WN / 2) + j * 32 + rg * 8 + (lane >> 5) * 4;
-                if (col >= I) continue;
-                float gv[4], uv[4], av[4];
+            for (int j = 0; j < HF; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    gv[q] = acc.v[i][j][rg * 4 + q];
-                    uv[q] = acc.v[i][j + HF][rg * 4 + q];
-                    av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+                for (int rg = 0; rg < 4; ++rg) {
+                    // gate column (tile-local) of wave column wn starts at wn*WN/2
+                    const int gc = wn * (C::WN / 2) + j * 32 + rg * 8 + (lane >> 5) * 4;
+                    float gv[4], uv[4], av[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        gv[q] = acc.v[i][j][rg * 4 + q];
+                        uv[q] = acc.v[i][j + HF][rg * 4 + q];
+                        av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+                    }
+                    const int sub = (lane >> 5) << 3;  // byte offset inside the 16-byte chunk
+                    *(lds_u64 *)(lds + soff(r, gc >> 3) + sub) = pack_bf4(gv[0], gv[1], gv[2], gv[3]);
+                    *(lds_u64 *)(lds + soff(r, 16 + (gc >> 3)) + sub) = pack_bf4(uv[0], uv[1], uv[2], uv[3]);
+                    *(lds_u64 *)(lds + soff(r, 32 + (gc >> 3)) + sub) = pack_bf4(av[0], av[1], av[2], av[3]);
                 }
-                if (g.h) {
-                    *(uint64_t *)(g.h + m * 2 * I + col) = pack_bf4(gv[0], gv[1], gv[2], gv[3]);
-                    *(uint64_t *)(g.h + m * 2 * I + I + col) = pack_bf4(uv[0], uv[1], uv[2], uv[3]);
-                }
-                *(uint64_t *)(g.a + m * I + col) = pack_bf4(av[0], av[1], av[2], av[3]);
+        }
+        __syncthreads();
+        const int seg = lane >> 4;                     // 0 gate, 1 up, 2 a
+        const int64_t col = i0 + 8 * (lane & 15);      // column within I
+        const bool live = lane < 48 && col < I && (seg == 2 || g.h != nullptr);
+        for (int r = wave; r < EPI_ROWS; r += C::NT / 64) {
+            const int64_t m = t.m0 + half * EPI_ROWS + r;
+            if (m >= t.seg_end) break;
+            if (live) {
+                const u32x4_t v = *(const lds_u32x4 *)(lds + soff(r, lane));
+                uint16_t *dst = seg == 2 ? g.a + m * I + col : g.h + m * 2 * I + (seg ? I : 0) + col;
+                *(u32x4_t *)dst = v;
             }
+        }
+        __syncthreads();
     }
 }
 
@@ -192,9 +192,7 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
     }
     Acc<C> acc;
     mainloop<C, false, false, false>(lds, I, la, lb, acc);
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    store_rows_f32<C>(acc, g.o, t.m0, t.seg_end, n0, H, wm, wn, lane);
+    store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
 }
 
 // =========================================================================
@@ -227,50 +225,65 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     lb.init(w2e, I, n0, I, wave0, lane0);
     Acc<C> acc;
     mainloop<C, false, true, false>(lds, H, la, lb, acc);
+    // dA' leaves through the LDS staging tile; lane l then owns columns
+    // n0 + 4l .. n0 + 4l + 3 of a row: it loads h (gate, up) and a there,
+    // applies the routing weight and the SwiGLU backward, stores dh, and the
+    // wave sums dA'.a over the tile's columns of the row (dw_part[m, nt]).
+    // The loads of RB rows are issued together (addresses clamped to valid
+    // rows) so that their latencies overlap.
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    lds_f32 *red = (lds_f32 *)lds;  // [WAVES_N][BM]; the LDS tiles are free now
+    const int64_t col = n0 + 4 * lane;
+    const bool cok = col < I;
+    const int64_t colc = cok ? col : 0;
+    constexpr int NW = C::NT / 64, RB = 4;
+    static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int rl = acc_row<C>(wm, i, lane);
-        const int64_t m = t.m0 + rl;
-        const bool mok = m < t.seg_end;
-        const float wgt = mok ? g.wrow[m] : 0.f;
-        float part = 0.f;
+    for (int half = 0; half < 2; ++half) {
+        if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
+        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
+        __syncthreads();
+        for (int r0 = wave; r0 < EPI_ROWS; r0 += RB * NW) {
+            uint64_t hg[RB], hu[RB], hv[RB];
+            float wgt[RB];
+            f32x4_t dap[RB];
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+            for (int b = 0; b < RB; ++b) {
+                const int r = r0 + b * NW;
+                int64_t m = t.m0 + half * EPI_ROWS + r;
+                if (m >= t.seg_end) m = t.seg_end - 1;
+                hg[b] = *(const uint64_t *)(g.h + m * 2 * I + colc);
+                hu[b] = *(const uint64_t *)(g.h + m * 2 * I + I + colc);
+                hv[b] = *(const uint64_t *)(g.a + m * I + colc);
+                wgt[b] = g.wrow[m];
+                dap[b] = epi_read_f32(lds, r, lane);
+            }
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int64_t col = n0 + acc_col<C>(wn, j, rg, lane);
-                if (!mok || col >= I) continue;
+            for (int b = 0; b < RB; ++b) {
+                const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
+                if (m >= t.seg_end) break;
                 float gv[4], uv[4], av[4], dg[4], du[4];
-                unpack_bf4(*(const uint64_t *)(g.h + m * 2 * I + col), gv);
-                unpack_bf4(*(const uint64_t *)(g.h + m * 2 * I + I + col), uv);
-                unpack_bf4(*(const uint64_t *)(g.a + m * I + col), av);
+                unpack_bf4(hg[b], gv);
+                unpack_bf4(hu[b], uv);
+                unpack_bf4(hv[b], av);
+                float part = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float dap = acc.v[i][j][rg * 4 + q];
-                    part += dap * av[q];
-                    const float da = wgt * dap;
+                    part += dap[b][q] * av[q];
+                    const float da = wgt[b] * dap[b][q];
                     const float sg = sigmoidf_(gv[q]);
                     dg[q] = da * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
                     du[q] = da * gv[q] * sg;
                 }
-                *(uint64_t *)(g.dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
-                *(uint64_t *)(g.dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
+                if (cok) {
+                    *(uint64_t *)(g.dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
+                    *(uint64_t *)(g.dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
+                }
+                part = wave_sum(cok ? part : 0.f);
+                if (lane == 0) g.dw_part[m * nN + t.nt] = part;
             }
-        // lanes l and l+32 hold the same row
-        part += __shfl_xor(part, 32, 64);
-        if (lane < 32) red[wn * C::BM + rl] = part;
-    }
-    __syncthreads();
-    for (int rl = tid; rl < C::BM; rl += C::NT) {
-        const int64_t m = t.m0 + rl;
-        if (m >= t.seg_end) continue;
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < C::WAVES_N; ++w) v += red[w * C::BM + rl];
-        g.dw_part[m * nN + t.nt] = v;
+        }
+        __syncthreads();
     }
 }
 
@@ -302,9 +315,7 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     lb.init(w1e, H, n0, H, wave0, lane0);
     Acc<C> acc;
     mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    store_rows_f32<C>(acc, g.dxp, t.m0, t.seg_end, n0, H, wm, wn, lane);
+    store_tile_f32<C>(acc, lds, g.dxp, t.m0, t.seg_end, n0, H);
 }
 
 // =========================================================================
@@ -358,33 +369,52 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     lb.init(Bb, Cc, c0, Cc, wave_uniform_id(), lane);
     Acc<C> acc;
     mainloop<C, true, true, true>(lds, cnt, la, lb, acc);
+    // out through the LDS staging tile, whole rows of dW at a time; in
+    // accumulate mode the old values of RB rows are loaded together
+    const int64_t cc = c0 + 4 * lane;
+    const bool cok = cc < Cc;
+    const int64_t ccc = cok ? cc : 0;
+    constexpr int NW = C::NT / 64, RB = 4;
+    static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int64_t rr = r0 + acc_row<C>(wm, i, lane);
-        if (rr >= R) continue;
+    for (int half = 0; half < 2; ++half) {
+        if (r0 + half * EPI_ROWS >= R) break;
+        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
+        __syncthreads();
+        for (int rb = wave; rb < EPI_ROWS; rb += RB * NW) {
+            f32x4_t v[RB], old[RB];
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int64_t cc = c0 + acc_col<C>(wn, j, rg, lane);
-                if (cc >= Cc) continue;
-                const int64_t o = dW_off + rr * Cc + cc;
-                f32x4_t v = {acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
-                             acc.v[i][j][rg * 4 + 3]};
-                if (g.dw_bf16) {
-                    uint64_t *p = (uint64_t *)((uint16_t *)dWv + o);
-                    if (g.dw_acc) {
-                        float old[4];
-                        unpack_bf4(*p, old);
-                        v[0] += old[0]; v[1] += old[1]; v[2] += old[2]; v[3] += old[3];
+            for (int b = 0; b < RB; ++b) {
+                const int r = rb + b * NW;
+                int64_t rr = r0 + half * EPI_ROWS + r;
+                if (rr >= R) rr = R - 1;
+                const int64_t o = dW_off + rr * Cc + ccc;
+                v[b] = epi_read_f32(lds, r, lane);
+                old[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (g.dw_acc) {
+                    if (g.dw_bf16) {
+                        float t4[4];
+                        unpack_bf4(*(const uint64_t *)((const uint16_t *)dWv + o), t4);
+                        old[b] = f32x4_t{t4[0], t4[1], t4[2], t4[3]};
+                    } else {
+                        old[b] = *(const f32x4_t *)((const float *)dWv + o);
                     }
-                    *p = pack_bf4(v[0], v[1], v[2], v[3]);
-                } else {
-                    f32x4_t *p = (f32x4_t *)((float *)dWv + o);
-                    if (g.dw_acc) v += *p;
-                    *p = v;
                 }
             }
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
+                if (rr >= R) break;
+                if (!cok) continue;
+                const int64_t o = dW_off + rr * Cc + cc;
+                const f32x4_t w = v[b] + old[b];
+                if (g.dw_bf16)
+                    *(uint64_t *)((uint16_t *)dWv + o) = pack_bf4(w[0], w[1], w[2], w[3]);
+                else
+                    *(f32x4_t *)((float *)dWv + o) = w;
+            }
+        }
+        __syncthreads();
     }
 }
 

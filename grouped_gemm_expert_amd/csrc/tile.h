@@ -194,39 +194,59 @@ MOE_DEV bf16x8_t frag_nmaj(const lds_t *T, int rbase, int kk, int lane)
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// One 64-deep LDS stage: 4 MFMA k-steps of 16.
+// MFMA operand fragments of one 16-deep k-step for a wave's tile.
+template <class C>
+struct Frags {
+    bf16x8_t a[C::FM], b[C::FN];
+};
+
 template <class C, bool A_NMAJ, bool B_NMAJ>
-MOE_DEV void mma_stage(const lds_t *As, const lds_t *Bs, Acc<C> &acc, int wm, int wn, int lane)
+MOE_DEV void read_frags(const lds_t *As, const lds_t *Bs, int kk, Frags<C> &f, int wm, int wn,
+                        int lane)
 {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        bf16x8_t a[C::FM], b[C::FN];
+    for (int i = 0; i < C::FM; ++i)
+        f.a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
+                        : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
-                          : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
-                          : frag_kmaj(Bs, wn * C::WN + j * 32, kk, lane);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc.v[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < C::FN; ++j)
+        f.b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
+                        : frag_kmaj(Bs, wn * C::WN + j * 32, kk, lane);
 }
 
-// Software pipeline over stages v0 .. v1-1 with two LDS buffers.  Stage v:
-// issue the copies of stage v+1 into the other buffer (free: every wave passed
-// the barrier that ended stage v-1), run the MFMAs of stage v, wait for this
-// wave's copies, let `tail` fix up the landed stage (a partial stage zeroes
-// its rows past the valid k), barrier.  One barrier a stage covers both
-// hazards: the next stage's data has landed for every wave, and no wave still
-// reads the buffer that the stage after will overwrite.
-// fill(v, As, Bs) issues stage v's copies; tail(v, As, Bs) runs after they
-// landed.
-template <class C, bool A_NMAJ, bool B_NMAJ, class Fill, class Tail>
+template <class C>
+MOE_DEV void mfma_step(const Frags<C> &f, Acc<C> &acc)
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.v[i][j], 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with the other counters at their maxima (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+MOE_DEV void wait_copies_le()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Software pipeline over stages v0 .. v1-1 (64 k each) with two LDS buffers
+// and two fragment register sets.  Stage v computes k-steps 0..3 from buffer
+// v%2, reading the fragments of step kk+1 while the MFMAs of step kk run.
+// Once the fragments of step 3 are in registers the wave no longer needs the
+// buffer, so the barrier comes before step 3's MFMAs: each wave first waits
+// for its own copies of stage v+1 (and lets `tail` fix that stage up), then
+// the barrier publishes stage v+1 and frees buffer v%2; after it the wave
+// reads step 0 of stage v+1 and issues the copies of stage v+2 into the freed
+// buffer while step 3's MFMAs execute.  The copies of a stage thus have a
+// whole stage of MFMAs to land in, and no wave idles on LDS latency right
+// after the barrier.
+// fill(v, As, Bs) issues stage v's copies (NCOPY per wave); tail(v, As, Bs)
+// runs after they landed.
+template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class Fill, class Tail>
 MOE_DEV void pipeline(lds_t *lds, int v0, int v1, Fill &&fill, Tail &&tail, Acc<C> &acc)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -236,20 +256,34 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, Fill &&fill, Tail &&tail, Acc<
     acc.zero();
     if (v1 <= v0) return;
     fill(v0, As[0], Bs[0]);
-    wait_copies();
+    if (v0 + 1 < v1) {
+        fill(v0 + 1, As[1], Bs[1]);
+        wait_copies_le<NCOPY>();
+    } else {
+        wait_copies();
+    }
     tail(v0, As[0], Bs[0]);
     __syncthreads();
+    Frags<C> f0, f1;
+    read_frags<C, A_NMAJ, B_NMAJ>(As[0], Bs[0], 0, f0, wm, wn, lane);
     for (int v = v0; v < v1; ++v) {
         const int cur = (v - v0) & 1;
-        const bool more = v + 1 < v1;
-        if (more) fill(v + 1, As[cur ^ 1], Bs[cur ^ 1]);
-        mma_stage<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], acc, wm, wn, lane);
-        if (more) {
+        read_frags<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], 1, f1, wm, wn, lane);
+        mfma_step<C>(f0, acc);
+        read_frags<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], 2, f0, wm, wn, lane);
+        mfma_step<C>(f1, acc);
+        read_frags<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], 3, f1, wm, wn, lane);
+        mfma_step<C>(f0, acc);
+        if (v + 1 < v1) {
             wait_copies();
             tail(v + 1, As[cur ^ 1], Bs[cur ^ 1]);
         }
         __syncthreads();
+        if (v + 1 < v1) read_frags<C, A_NMAJ, B_NMAJ>(As[cur ^ 1], Bs[cur ^ 1], 0, f0, wm, wn, lane);
+        if (v + 2 < v1) fill(v + 2, As[cur], Bs[cur]);
+        mfma_step<C>(f1, acc);
     }
+    __syncthreads();  // callers may reuse the LDS
 }
 
 // C = A . B^T over K with two loaders of fixed base: stages of 64 k, the last
@@ -261,7 +295,7 @@ MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> 
         const int64_t rem = K - (int64_t)s * BK;
         return KTAIL ? (rem < BK ? (int)rem : BK) : BK;
     };
-    pipeline<C, A_NMAJ, B_NMAJ>(
+    pipeline<C, A_NMAJ, B_NMAJ, LA::NI + LB::NI>(
         lds, 0, (int)ceil_div(K, BK),
         [&](int s, lds_t *As, lds_t *Bs) {
             la.issue(As, (int64_t)s * BK, kvalid(s));
@@ -300,6 +334,69 @@ MOE_DEV void unpack_bf4(uint64_t v, float (&o)[4])
     o[1] = bf2f((uint16_t)((v >> 16) & 0xffffu));
     o[2] = bf2f((uint16_t)((v >> 32) & 0xffffu));
     o[3] = bf2f((uint16_t)(v >> 48));
+}
+
+// ------------------------------------------------------------ epilogue ----
+// The accumulators leave the block through LDS, one 128-row half of the
+// 256-row tile at a time: the waves holding that half write their fragments
+// into a [128][256] fp32 staging tile (1 KB a row, 16-byte chunks XOR-swizzled
+// by row so that both the fragment writes and the row reads are free of bank
+// conflicts), then every wave takes whole rows, lane l owning columns
+// 4l .. 4l+3, so global loads and stores are row-contiguous 16-byte (or
+// 8-byte) accesses instead of the fragment layout's scattered 8-byte pieces.
+constexpr int EPI_ROWS = 128;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+
+MOE_DEV int epi_off(int r, int chunk) { return r * 1024 + ((chunk ^ (r & 15)) << 4); }
+
+// Fragments of rows [half*128, half*128 + 128) of the tile into the staging
+// tile (a 32-row fragment block is wholly inside one half).
+template <class C>
+MOE_DEV void epi_stage_f32(const Acc<C> &acc, lds_t *lds, int half, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        if ((wm * C::WM + i * 32) / EPI_ROWS != half) continue;
+        const int r = acc_row<C>(wm, i, lane) - half * EPI_ROWS;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = acc_col<C>(wn, j, rg, lane);
+                f32x4_t v = {acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
+                             acc.v[i][j][rg * 4 + 3]};
+                *(lds_f32x4 *)(lds + epi_off(r, c >> 2)) = v;
+            }
+    }
+}
+
+MOE_DEV f32x4_t epi_read_f32(const lds_t *lds, int r, int lane)
+{
+    return *(const lds_f32x4 *)(lds + epi_off(r, lane));
+}
+
+// out[m][n0 + c] = tile[m - m0][c] for rows m0 <= m < mlim (row stride
+// ncols, ncols a multiple of 4).  Starts and ends on a barrier-free LDS.
+template <class C>
+MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, float *out, int64_t m0, int64_t mlim,
+                            int64_t n0, int64_t ncols)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int64_t col = n0 + 4 * lane;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (m0 + half * EPI_ROWS >= mlim) break;
+        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
+        __syncthreads();
+        for (int r = wave; r < EPI_ROWS; r += C::NT / 64) {
+            const int64_t m = m0 + half * EPI_ROWS + r;
+            if (m >= mlim) break;
+            if (col < ncols) *(f32x4_t *)(out + m * ncols + col) = epi_read_f32(lds, r, lane);
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------- tile schedules ----
