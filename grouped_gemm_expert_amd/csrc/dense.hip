@@ -82,11 +82,14 @@ __global__ __launch_bounds__(C::NT) void k_dense(DenseArgs d)
     Acc<C> acc;
     pipeline<C, A_NMAJ, B_NMAJ, decltype(la)::NI + decltype(lb)::NI>(
         lds, v0, v1,
-        [&](int v, lds_t *As, lds_t *Bs) {
+        [&](int q, int v, lds_t *As, lds_t *Bs) {
             const int t = (int)(v / d.spt);
             const int64_t k0 = (v % d.spt) * BK;
-            la.issue(As, k0, kvalid(v), (const char *)d.A[t]);
-            lb.issue(Bs, k0, kvalid(v), (const char *)d.B[t]);
+            constexpr int NA = decltype(la)::NI;
+            if (q < NA)
+                la.issue_one(q, As, k0, kvalid(v), (const char *)d.A[t]);
+            else
+                lb.issue_one(q - NA, Bs, k0, kvalid(v), (const char *)d.B[t]);
         },
         [&](int v, lds_t *As, lds_t *Bs) {
             // K-major operands are read from rows padded with zeros past K

@@ -79,12 +79,14 @@ struct KLoad {
     {
         off[i] = row_bytes + ((uint32_t)((lane & 7) ^ swz(row(i, lane))) << 4);
     }
-    MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid) const { issue(tile, k0, kvalid, base); }
-    MOE_DEV void issue(lds_t *tile, int64_t k0, int, const char *b) const
+    MOE_DEV void issue_one(int i, lds_t *tile, int64_t k0, int, const char *b) const
     {
-        const char *p = b + k0 * 2;
+        copy16_to_lds(b + k0 * 2 + off[i], tile + (q0 + i) * 1024);
+    }
+    MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid, const char *b) const
+    {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) copy16_to_lds(p + off[i], tile + (q0 + i) * 1024);
+        for (int i = 0; i < NI; ++i) issue_one(i, tile, k0, kvalid, b);
     }
     MOE_DEV void zero_tail(lds_t *, int) const {}
 };
@@ -130,16 +132,16 @@ struct NLoad {
             ncol[i] = (uint32_t)(n * 2);
         }
     }
-    MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid) const { issue(tile, k0, kvalid, base); }
+    MOE_DEV void issue_one(int i, lds_t *tile, int64_t k0, int kvalid, const char *b) const
+    {
+        int k = krow(i);
+        if (k >= kvalid) k = kvalid - 1;
+        copy16_to_lds(b + k0 * (int64_t)ldb + (uint32_t)k * ldb + ncol[i], tile + (q0 + i) * 1024);
+    }
     MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid, const char *b) const
     {
-        const char *p = b + k0 * (int64_t)ldb;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            int k = krow(i);
-            if (k >= kvalid) k = kvalid - 1;
-            copy16_to_lds(p + (uint32_t)k * ldb + ncol[i], tile + (q0 + i) * 1024);
-        }
+        for (int i = 0; i < NI; ++i) issue_one(i, tile, k0, kvalid, b);
     }
     MOE_DEV void zero_tail(lds_t *tile, int kvalid) const
     {
@@ -233,6 +235,49 @@ MOE_DEV void wait_copies_le()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Read number r of a k-step's fragments, in the order a0, b0 .. b(FN-1),
+// a1 .. a(FM-1): the order in which the (i, j)-ordered MFMAs first need them.
+template <class C, bool A_NMAJ, bool B_NMAJ>
+MOE_DEV void read_one(int r, const lds_t *As, const lds_t *Bs, int kk, Frags<C> &f, int wm, int wn,
+                      int lane)
+{
+    if (r == 0 || r > C::FN) {
+        const int i = r == 0 ? 0 : r - C::FN;
+        f.a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
+                        : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
+    } else {
+        const int j = r - 1;
+        f.b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
+                        : frag_kmaj(Bs, wn * C::WN + j * 32, kk, lane);
+    }
+}
+
+// The MFMAs of one k-step (fragments `cur`) in (i, j) order.  Before MFMA n
+// the wave issues fragment read n of the next k-step into `nxt` (n < FM+FN)
+// and the copies q of the next-but-one stage with q*NMF/NCOPY == n (when
+// `copy`), so LDS reads and global->LDS copies are spread evenly over the
+// MFMAs instead of arriving in bursts; sched_barrier pins that order.
+template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class CopyOne>
+MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const lds_t *Bs, int kk_next,
+                   bool copy, CopyOne &&copy_one, Acc<C> &acc, int wm, int wn, int lane)
+{
+    constexpr int NMF = C::FM * C::FN, NR = C::FM + C::FN;
+    static_assert(NR <= NMF, "one read per MFMA at most");
+#pragma unroll
+    for (int n = 0; n < NMF; ++n) {
+        if (n < NR) read_one<C, A_NMAJ, B_NMAJ>(n, As, Bs, kk_next, nxt, wm, wn, lane);
+        if (copy) {
+#pragma unroll
+            for (int q = 0; q < NCOPY; ++q)
+                if (q * NMF / NCOPY == n) copy_one(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = n / C::FN, j = n % C::FN;
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc.v[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Software pipeline over stages v0 .. v1-1 (64 k each) with two LDS buffers
 // and two fragment register sets.  Stage v computes k-steps 0..3 from buffer
 // v%2, reading the fragments of step kk+1 while the MFMAs of step kk run.
@@ -244,10 +289,10 @@ MOE_DEV void wait_copies_le()
 // buffer while step 3's MFMAs execute.  The copies of a stage thus have a
 // whole stage of MFMAs to land in, and no wave idles on LDS latency right
 // after the barrier.
-// fill(v, As, Bs) issues stage v's copies (NCOPY per wave); tail(v, As, Bs)
-// runs after they landed.
-template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class Fill, class Tail>
-MOE_DEV void pipeline(lds_t *lds, int v0, int v1, Fill &&fill, Tail &&tail, Acc<C> &acc)
+// copy_one(q, v, As, Bs) issues copy q (of NCOPY per wave) of stage v;
+// tail(v, As, Bs) runs after they landed.
+template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class CopyOne, class Tail>
+MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyOne &&copy_one, Tail &&tail, Acc<C> &acc)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -255,9 +300,11 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, Fill &&fill, Tail &&tail, Acc<
     lds_t *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
     acc.zero();
     if (v1 <= v0) return;
-    fill(v0, As[0], Bs[0]);
+#pragma unroll
+    for (int q = 0; q < NCOPY; ++q) copy_one(q, v0, As[0], Bs[0]);
     if (v0 + 1 < v1) {
-        fill(v0 + 1, As[1], Bs[1]);
+#pragma unroll
+        for (int q = 0; q < NCOPY; ++q) copy_one(q, v0 + 1, As[1], Bs[1]);
         wait_copies_le<NCOPY>();
     } else {
         wait_copies();
@@ -266,22 +313,23 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, Fill &&fill, Tail &&tail, Acc<
     __syncthreads();
     Frags<C> f0, f1;
     read_frags<C, A_NMAJ, B_NMAJ>(As[0], Bs[0], 0, f0, wm, wn, lane);
+    auto none = [](int) {};
     for (int v = v0; v < v1; ++v) {
         const int cur = (v - v0) & 1;
-        read_frags<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], 1, f1, wm, wn, lane);
-        mfma_step<C>(f0, acc);
-        read_frags<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], 2, f0, wm, wn, lane);
-        mfma_step<C>(f1, acc);
-        read_frags<C, A_NMAJ, B_NMAJ>(As[cur], Bs[cur], 3, f1, wm, wn, lane);
-        mfma_step<C>(f0, acc);
+        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f0, f1, As[cur], Bs[cur], 1, false, none, acc, wm, wn, lane);
+        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f1, f0, As[cur], Bs[cur], 2, false, none, acc, wm, wn, lane);
+        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f0, f1, As[cur], Bs[cur], 3, false, none, acc, wm, wn, lane);
         if (v + 1 < v1) {
             wait_copies();
             tail(v + 1, As[cur ^ 1], Bs[cur ^ 1]);
         }
         __syncthreads();
-        if (v + 1 < v1) read_frags<C, A_NMAJ, B_NMAJ>(As[cur ^ 1], Bs[cur ^ 1], 0, f0, wm, wn, lane);
-        if (v + 2 < v1) fill(v + 2, As[cur], Bs[cur]);
-        mfma_step<C>(f1, acc);
+        // step 0 of stage v+1 (in the last stage a harmless read of the other
+        // buffer), copies of stage v+2 into this stage's buffer
+        const int vn = v + 2;
+        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(
+            f1, f0, As[cur ^ 1], Bs[cur ^ 1], 0, vn < v1,
+            [&](int q) { copy_one(q, vn, As[cur], Bs[cur]); }, acc, wm, wn, lane);
     }
     __syncthreads();  // callers may reuse the LDS
 }
@@ -297,9 +345,11 @@ MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> 
     };
     pipeline<C, A_NMAJ, B_NMAJ, LA::NI + LB::NI>(
         lds, 0, (int)ceil_div(K, BK),
-        [&](int s, lds_t *As, lds_t *Bs) {
-            la.issue(As, (int64_t)s * BK, kvalid(s));
-            lb.issue(Bs, (int64_t)s * BK, kvalid(s));
+        [&](int q, int s, lds_t *As, lds_t *Bs) {
+            if (q < LA::NI)
+                la.issue_one(q, As, (int64_t)s * BK, kvalid(s), la.base);
+            else
+                lb.issue_one(q - LA::NI, Bs, (int64_t)s * BK, kvalid(s), lb.base);
         },
         [&](int s, lds_t *As, lds_t *Bs) {
             if (KTAIL && kvalid(s) < BK) {
