@@ -324,13 +324,16 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyOne &&copy_one, Tail &&tai
             tail(v + 1, As[cur ^ 1], Bs[cur ^ 1]);
         }
         __syncthreads();
-        // step 0 of stage v+1 (in the last stage a harmless read of the other
-        // buffer), copies of stage v+2 into this stage's buffer
-        const int vn = v + 2;
+        // step 0 of stage v+1 and the copies of stage v+2 into this stage's
+        // buffer.  Past the end both are harmless and branch-free: the reads
+        // fetch stale fragments that are never used, and the last stage is
+        // copied again into a buffer that nothing reads any more.
+        const int vn = v + 2 < v1 ? v + 2 : v1 - 1;
         kstep<C, A_NMAJ, B_NMAJ, NCOPY>(
-            f1, f0, As[cur ^ 1], Bs[cur ^ 1], 0, vn < v1,
+            f1, f0, As[cur ^ 1], Bs[cur ^ 1], 0, true,
             [&](int q) { copy_one(q, vn, As[cur], Bs[cur]); }, acc, wm, wn, lane);
     }
+    wait_copies();    // the repeated copies of the last stages
     __syncthreads();  // callers may reuse the LDS
 }
 
