@@ -379,10 +379,29 @@ static moe_status check_saved(const moe_saved *s)
                        s->pos, s->h, s->a});
 }
 
-moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
-                       const float *bias, const uint16_t *w1, const uint16_t *w2, float *y,
-                       float *aux, const moe_saved *saved, void *ws, size_t ws_bytes,
-                       hipStream_t stream)
+static moe_gemm_args saved_gemm_args(const moe_saved *saved)
+{
+    moe_gemm_args a;
+    memset(&a, 0, sizeof a);
+    a.counts = saved->counts;
+    a.offsets = saved->offsets;
+    a.row_map = saved->row_map;
+    a.topk_w = saved->topk_w;
+    a.h = saved->h;
+    a.a = saved->a;
+    return a;
+}
+
+// ----------------------------------------------------------- two stages ----
+// The MegaMoE design section splits the layer into two stages that each own
+// one weight: stage 1 (router, dispatch, GEMM1 + SwiGLU; w1) and stage 2
+// (GEMM2 + combine; w2).  The backward runs stage 2 first (dW2), then stage 1
+// (dW1, router).  moe_forward / moe_backward are these stages back to back.
+
+moe_status moe_stage1_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                              const float *bias, const uint16_t *w1, float *aux,
+                              const moe_saved *saved, void *ws, size_t ws_bytes,
+                              hipStream_t stream)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
@@ -398,7 +417,7 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
         return MOE_OK;
     }
     MOE_CHECK(check_saved(saved));
-    MOE_CHECK(check_ptrs({x, w1, w2, y}));
+    MOE_CHECK(check_ptrs({x, w1}));
     MOE_CHECK(moe_router(cfg, x, Wr, bias, saved->logits, nullptr, saved->topk_idx,
                          saved->topk_w, saved->counts, aux, ws, ws_bytes, stream));
     {
@@ -407,37 +426,92 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
                                saved->row_map, saved->pos, w.chunk_hist, stream));
         MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
     }
-    moe_gemm_args a;
-    memset(&a, 0, sizeof a);
+    moe_gemm_args a = saved_gemm_args(saved);
     a.x = x;
     a.w1 = w1;
-    a.w2 = w2;
-    a.counts = saved->counts;
-    a.offsets = saved->offsets;
-    a.row_map = saved->row_map;
-    a.topk_w = saved->topk_w;
-    a.h = saved->h;
-    a.a = saved->a;
-    a.o = w.o;
     GemmArgs g = gemm_args(c, a, w.sched);
     MOE_TRY(run_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
+    return MOE_OK;
+}
+
+moe_status moe_stage2_forward(const moe_config *cfg, const uint16_t *w2, const moe_saved *saved,
+                              float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    if (!saved) return MOE_EINVAL;
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    if (c.T == 0) return MOE_OK;
+    MOE_CHECK(check_saved(saved));
+    MOE_CHECK(check_ptrs({w2, y}));
+    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    moe_gemm_args a = saved_gemm_args(saved);
+    a.w2 = w2;
+    a.o = w.o;
+    GemmArgs g = gemm_args(c, a, w.sched);
     MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));
     StageMark mark(MOE_STAGE_COMBINE, stream);
     MOE_TRY(launch_combine(c.T, c.k, c.H, w.o, saved->topk_w, saved->pos, y, stream));
     return MOE_OK;
 }
 
-moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
-                        const float *Wr, const uint16_t *w1, const uint16_t *w2,
-                        const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
-                        float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
-                        int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream)
+moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                       const float *bias, const uint16_t *w1, const uint16_t *w2, float *y,
+                       float *aux, const moe_saved *saved, void *ws, size_t ws_bytes,
+                       hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    if (cfg->T > 0) MOE_CHECK(check_ptrs({w2, y}));
+    MOE_CHECK(moe_stage1_forward(cfg, x, Wr, bias, w1, aux, saved, ws, ws_bytes, stream));
+    return moe_stage2_forward(cfg, w2, saved, y, ws, ws_bytes, stream);
+}
+
+moe_status moe_stage2_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
+                               const uint16_t *dy, void *dW2, int32_t dw_dtype,
+                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                               hipStream_t stream)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
     if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
     MOE_CHECK(check_saved(saved));
-    MOE_CHECK(check_ptrs({x, w1, w2, dy, dx, dlogits, dW1, dW2}));
+    MOE_CHECK(check_ptrs({w2, dy, dW2}));
+    size_t need = 0;
+    BwdWs w = carve_bwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    moe_gemm_args a = saved_gemm_args(saved);
+    a.dy = dy;
+    a.w2 = w2;
+    a.dh = w.dh;
+    a.dw_part = w.dw_part;
+    a.dW2 = dW2;
+    a.dw_dtype = dw_dtype;
+    a.dw_accumulate = dw_accumulate;
+    GemmArgs g = gemm_args(c, a, w.sched);
+    g.wrow = w.wrow;
+    g.dyw = w.dyw;
+    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, nullptr, dy,
+                               nullptr, w.dyw, w.wrow, stream));
+    // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
+    if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
+    MOE_TRY(run_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
+    return MOE_OK;
+}
+
+moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                               const float *Wr, const uint16_t *w1, const float *d_aux, float *dx,
+                               float *dlogits, float *dWr, void *dW1, int32_t dw_dtype,
+                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                               hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
+    MOE_CHECK(check_saved(saved));
+    MOE_CHECK(check_ptrs({x, w1, dx, dlogits, dW1}));
     MOE_CHECK(check_opt_ptr(Wr));
     MOE_CHECK(check_opt_ptr(dWr));
     MOE_CHECK(check_opt_ptr(d_aux));
@@ -445,42 +519,28 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
     BwdWs w = carve_bwd(c, ws, &need);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
-    moe_gemm_args a;
-    memset(&a, 0, sizeof a);
+    moe_gemm_args a = saved_gemm_args(saved);
     a.x = x;
-    a.dy = dy;
     a.w1 = w1;
-    a.w2 = w2;
-    a.counts = saved->counts;
-    a.offsets = saved->offsets;
-    a.row_map = saved->row_map;
-    a.topk_w = saved->topk_w;
-    a.h = saved->h;
-    a.a = saved->a;
     a.dh = w.dh;
     a.dw_part = w.dw_part;
     a.dxp = w.dxp;
     a.dW1 = dW1;
-    a.dW2 = dW2;
     a.dw_dtype = dw_dtype;
     a.dw_accumulate = dw_accumulate;
     GemmArgs g = gemm_args(c, a, w.sched);
-    g.wrow = w.wrow;
     g.xg = w.xg;
-    g.dyw = w.dyw;
-    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, x, dy, w.xg,
-                               w.dyw, w.wrow, stream));
-    // GEMM2 stage: dgrad (+ SwiGLU backward, routing-weight row-dots), dW2
-    if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
-    MOE_TRY(run_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
-    // GEMM1 stage: dgrad, dW1
+    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, x, nullptr,
+                               w.xg, nullptr, nullptr, stream));
+    // dgrad, then dW1
     if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_UP_DGRAD, g, stream));
     MOE_TRY(run_gemm(MOE_GEMM_UP_WGRAD, g, stream));
     if (c.T == 0) {
         if (dWr && Wr) MOE_TRY(launch_fill_f32(dWr, (int64_t)c.E * c.H, 0.f, stream));
         return MOE_OK;
     }
-    // router: d logits, then dx = un-permute(dxp) + dlogits . Wr, dWr = dlogits^T . x
+    // router: d logits (from the routing-weight row-dots stage 2 left in the
+    // workspace), then dx = un-permute(dxp) + dlogits . Wr, dWr = dlogits^T . x
     RouterBwdArgs rb;
     rb.T = c.T;
     rb.E = c.E;
@@ -511,6 +571,24 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
         MOE_TRY(launch_router_grads(c.T, c.E, c.H, dlogits, x, Wr, dx, dWr, w.router, stream));
     }
     return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                        const float *Wr, const uint16_t *w1, const uint16_t *w2,
+                        const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
+                        float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
+                        int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    // everything stage 1 validates, checked before stage 2 launches anything
+    MOE_CHECK(check_ptrs({x, w1, dx, dlogits, dW1}));
+    MOE_CHECK(check_opt_ptr(Wr));
+    MOE_CHECK(check_opt_ptr(dWr));
+    MOE_CHECK(check_opt_ptr(d_aux));
+    MOE_CHECK(moe_stage2_backward(cfg, saved, w2, dy, dW2, dw_dtype, dw_accumulate, ws, ws_bytes,
+                                  stream));
+    return moe_stage1_backward(cfg, saved, x, Wr, w1, d_aux, dx, dlogits, dWr, dW1, dw_dtype,
+                               dw_accumulate, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -83,6 +83,16 @@ def _load():
     lib.moe_backward.argtypes = ([CFG, ctypes.POINTER(MoeSaved)] + [_P] * 11
                                  + [ctypes.c_int32, ctypes.c_int32, _P, sz, _P])
     lib.moe_backward.restype = S
+    SP = ctypes.POINTER(MoeSaved)
+    I32 = ctypes.c_int32
+    lib.moe_stage1_forward.argtypes = [CFG] + [_P] * 5 + [SP, _P, sz, _P]
+    lib.moe_stage1_forward.restype = S
+    lib.moe_stage2_forward.argtypes = [CFG, _P, SP, _P, _P, sz, _P]
+    lib.moe_stage2_forward.restype = S
+    lib.moe_stage2_backward.argtypes = [CFG, SP, _P, _P, _P, I32, I32, _P, sz, _P]
+    lib.moe_stage2_backward.restype = S
+    lib.moe_stage1_backward.argtypes = [CFG, SP] + [_P] * 8 + [I32, I32, _P, sz, _P]
+    lib.moe_stage1_backward.restype = S
     lib.moe_set_stage_events.argtypes = [ctypes.c_int32, _P, _P]
     lib.moe_set_stage_events.restype = S
     return lib
@@ -92,7 +102,9 @@ _lib = _load()
 
 SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspace_size",
            "moe_dw_part_cols", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_swiglu",
-           "moe_combine", "moe_forward", "moe_backward", "moe_set_stage_events")
+           "moe_combine", "moe_forward", "moe_backward", "moe_stage1_forward",
+           "moe_stage2_forward", "moe_stage2_backward", "moe_stage1_backward",
+           "moe_set_stage_events")
 
 STAGES = {"up_swiglu": 0, "down": 1, "down_dgrad": 2, "up_dgrad": 3, "down_wgrad": 4,
           "up_wgrad": 5, "router_proj": 6, "router": 7, "permute": 8, "combine": 9,
@@ -243,3 +255,34 @@ def moe_backward(cfg, saved: dict, x, Wr, w1, w2, dy, d_aux, dx, dlogits, dWr, d
                              _ptr(w2), _ptr(dy), _ptr(d_aux), _ptr(dx), _ptr(dlogits), _ptr(dWr),
                              _ptr(dW1), _ptr(dW2), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
                              ws.numel(), _stream(stream)), "moe_backward")
+
+
+def moe_stage1_forward(cfg, x, Wr, bias, w1, aux, saved: dict, ws, stream=None):
+    s = _saved_struct(saved)
+    _check(_lib.moe_stage1_forward(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias), _ptr(w1),
+                                   _ptr(aux), ctypes.byref(s), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "moe_stage1_forward")
+
+
+def moe_stage2_forward(cfg, w2, saved: dict, y, ws, stream=None):
+    s = _saved_struct(saved)
+    _check(_lib.moe_stage2_forward(ctypes.byref(cfg), _ptr(w2), ctypes.byref(s), _ptr(y),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_stage2_forward")
+
+
+def moe_stage2_backward(cfg, saved: dict, w2, dy, dW2, ws, dw_accumulate=False, stream=None):
+    s = _saved_struct(saved)
+    dw_dtype = MOE_BF16 if dW2.dtype == torch.bfloat16 else MOE_F32
+    _check(_lib.moe_stage2_backward(ctypes.byref(cfg), ctypes.byref(s), _ptr(w2), _ptr(dy),
+                                    _ptr(dW2), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "moe_stage2_backward")
+
+
+def moe_stage1_backward(cfg, saved: dict, x, Wr, w1, d_aux, dx, dlogits, dWr, dW1, ws,
+                        dw_accumulate=False, stream=None):
+    s = _saved_struct(saved)
+    dw_dtype = MOE_BF16 if dW1.dtype == torch.bfloat16 else MOE_F32
+    _check(_lib.moe_stage1_backward(ctypes.byref(cfg), ctypes.byref(s), _ptr(x), _ptr(Wr),
+                                    _ptr(w1), _ptr(d_aux), _ptr(dx), _ptr(dlogits), _ptr(dWr),
+                                    _ptr(dW1), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "moe_stage1_backward")

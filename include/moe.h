@@ -268,6 +268,38 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
                         int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The same layer as two stages that each own one weight (MegaMoE page,
+ * "Design: two stages + weight modules"): stage 1 = router, dispatch and
+ * GEMM1 + SwiGLU (w1); stage 2 = GEMM2 and combine (w2).  moe_forward is
+ * moe_stage1_forward then moe_stage2_forward; moe_backward is
+ * moe_stage2_backward (dW2 first, as the page orders it) then
+ * moe_stage1_backward.  Results are bit-identical to the one-call forms.
+ *  - The forward stages take the forward workspace, the backward stages the
+ *    backward workspace (moe_workspace_size); a pair must get the same `ws`
+ *    on the same stream, in this order: moe_stage1_backward reads the
+ *    routing-weight row-dots and dh that moe_stage2_backward leaves in the
+ *    backward workspace.
+ *  - Arguments mean what they mean in moe_forward / moe_backward;
+ *    dw_dtype and dw_accumulate apply to the one weight gradient a stage
+ *    writes.  Errors as for the one-call forms.
+ */
+moe_status moe_stage1_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                              const float *bias, const uint16_t *w1, float *aux,
+                              const moe_saved *saved, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+moe_status moe_stage2_forward(const moe_config *cfg, const uint16_t *w2, const moe_saved *saved,
+                              float *y, void *ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_stage2_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
+                               const uint16_t *dy, void *dW2, int32_t dw_dtype,
+                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                               const float *Wr, const uint16_t *w1, const float *d_aux, float *dx,
+                               float *dlogits, float *dWr, void *dW1, int32_t dw_dtype,
+                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
  * Profiling hook.  Stages of the path that moe_forward / moe_backward (and the
  * single-stage entry points) launch; the six grouped-GEMM ops use their
  * MOE_GEMM_* values.  When an event pair is registered for a stage, the
