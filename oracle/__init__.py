@@ -16,6 +16,8 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
   weights              -- pinned: sum identities, E=1 closed form
   permute              -- pinned: `even` routing closed form (MegaMoE page,
                           force-load-balancing table), golden fixture
+  even_topk            -- pinned: the same hand-worked golden fixture (its idx
+                          lines), equal counts, weights against numpy softmax
   aux                  -- pinned: uniform-probability closed form (aux == coeff),
                           E=1 closed form.  The formula itself is a reading (the
                           pages name a "standard aux_loss" without a formula).
@@ -69,6 +71,7 @@ def _load():
         "oracle_logits": [i64, i32, i32, P, P, P],
         "oracle_selection_scores": [i64, i32, i32, P, P, P],
         "oracle_topk": [i64, i32, i32, i32, i32, P, P],
+        "oracle_even_topk": [i64, i32, i32, P],
         "oracle_weights": [i64, i32, i32, i32, i32, f64, P, P, P],
         "oracle_permute": [i64, i32, i32, P, P, P, P, P],
         "oracle_aux": [i64, i32, i32, i32, f64, P, P],
@@ -128,6 +131,13 @@ def topk(S: np.ndarray, k: int, n_groups: int = 1, topk_groups: int = 1) -> np.n
     T, E = S.shape
     out = np.empty((T, k), np.int32)
     _load().oracle_topk(T, E, k, n_groups, topk_groups, _p(S), _p(out))
+    return out
+
+
+def even_topk(T: int, E: int, k: int) -> np.ndarray:
+    """`even` forced routing: slot (t, j) -> expert (t*k + j) % E, int32 [T,k]."""
+    out = np.empty((T, k), np.int32)
+    _load().oracle_even_topk(T, E, k, _p(out))
     return out
 
 
@@ -281,15 +291,21 @@ def router_weight_grad(x, dlogits64) -> np.ndarray:
 
 def route(logits64: np.ndarray, *, score: int, k: int, n_groups: int = 1, topk_groups: int = 1,
           bias=None, renorm: bool = False, scale: float = 1.0, coeff: float = 0.0,
-          logits32: Optional[np.ndarray] = None):
+          logits32: Optional[np.ndarray] = None, route_mode: str = "learned"):
     """Full router of the oracle: fp32 selection, top-k, weights, permutation, aux.
 
     ``logits32`` is the fp32 logits tensor the decision is taken on; by default
-    the double logits rounded to fp32.
+    the double logits rounded to fp32.  ``route_mode="even"`` replaces the
+    decision by the `even` forced routing (groups then play no part).
     """
     l32 = np.asarray(logits64, np.float32) if logits32 is None else np.asarray(logits32, np.float32)
     S = selection_scores(l32, score, bias)
-    idx = topk(S, k, n_groups, topk_groups)
+    if route_mode == "even":
+        idx = even_topk(l32.shape[0], l32.shape[1], k)
+    elif route_mode == "learned":
+        idx = topk(S, k, n_groups, topk_groups)
+    else:
+        raise ValueError(f"unknown route_mode {route_mode}")
     E = l32.shape[1]
     w = weights(logits64, idx, score, renorm, scale)
     counts, offsets, row_map, pos = permute(idx, E)

@@ -164,6 +164,19 @@ void oracle_topk(int64_t T, int32_t E, int32_t k, int32_t G, int32_t kg,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* `even` forced routing (MegaMoE page, "Router force load balancing",      */
+/* table row `even`): the router's choice is discarded and slot j of token  */
+/* t goes to expert (t * k + j) mod E, so every expert gets the same number */
+/* of slots (to within one).  Weights, counts and aux then follow from      */
+/* these indices exactly as for a learned choice.                           */
+/* ------------------------------------------------------------------------ */
+void oracle_even_topk(int64_t T, int32_t E, int32_t k, int32_t *idx)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) idx[t * k + j] = (int32_t)((t * k + j) % E);
+}
+
 /* Router probabilities of one token over all E experts (double):            */
 /*   softmax router: p = softmax(l);  sigmoid router: s = sigmoid(l).        */
 static void token_scores(int32_t E, int32_t score, const double *l, double *out)

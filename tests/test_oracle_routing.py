@@ -173,6 +173,52 @@ def test_permute_even_routing_closed_form(oracle_lib, T, k, E):
         assert np.array_equal(row_map[offsets[e]:offsets[e + 1]], e + np.arange(n) * E)
 
 
+def test_even_route_golden(oracle_lib):
+    """The oracle's `even` forced routing against the hand-worked cases."""
+    for c in _read_even_cases():
+        T, k, E = c["T"], c["k"], c["E"]
+        l64 = np.random.default_rng(T * 100 + E).normal(size=(T, E))
+        r = oracle_lib.route(l64, score=oracle_lib.SOFTMAX, k=k, renorm=True, coeff=0.01,
+                             route_mode="even")
+        assert np.array_equal(r["idx"].ravel(), c["idx"])
+        assert np.array_equal(r["counts"], c["counts"])
+        assert np.array_equal(r["offsets"], c["offsets"])
+        assert np.array_equal(r["row_map"], c["row_map"])
+        assert np.array_equal(r["pos"], c["pos"])
+
+
+@pytest.mark.parametrize("score,renorm", [(0, False), (0, True), (1, True)])
+def test_even_route_weights(oracle_lib, score, renorm):
+    """Forced indices, learned weight rule: softmax p at the forced experts
+    (renormalised or not), or scale * s / sum(s) for the sigmoid router;
+    groups play no part."""
+    T, E, k = 37, 16, 4
+    rng = np.random.default_rng(11)
+    l64 = rng.normal(size=(T, E))
+    r = oracle_lib.route(l64, score=score, k=k, n_groups=4, topk_groups=1, renorm=renorm,
+                         scale=2.5, coeff=0.01, route_mode="even")
+    idx = r["idx"]
+    # the forced experts, whatever the scores of their groups
+    assert idx[1].tolist() == [4, 5, 6, 7] and idx[4].tolist() == [0, 1, 2, 3]
+    if score == oracle_lib.SOFTMAX:
+        p = np.exp(l64 - l64.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        ref = np.take_along_axis(p, idx, 1)
+        if renorm:
+            ref = ref / ref.sum(1, keepdims=True)
+    else:
+        s = 1.0 / (1.0 + np.exp(-l64))
+        ref = np.take_along_axis(s, idx, 1)
+        ref = 2.5 * ref / ref.sum(1, keepdims=True)
+    assert np.allclose(r["w"], ref, rtol=1e-12, atol=1e-15)
+
+
+def test_even_route_counts_equal(oracle_lib):
+    T, E, k = 96, 24, 8
+    r = oracle_lib.route(np.zeros((T, E)), score=oracle_lib.SOFTMAX, k=k, route_mode="even")
+    assert (r["counts"] == T * k // E).all()
+
+
 def test_permute_matches_stable_argsort(oracle_lib):
     rng = np.random.default_rng(4)
     for E, T, k in [(8, 300, 2), (64, 257, 6), (5, 1, 5)]:
