@@ -202,6 +202,7 @@ moe_status moe_check_config(const moe_config *cfg)
     const moe_config &c = *cfg;
     if (c.T < 0 || c.H <= 0 || c.I <= 0 || c.E <= 0 || c.k <= 0) return MOE_EINVAL;
     if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID) return MOE_EINVAL;
+    if (c.route_mode != MOE_ROUTE_LEARNED && c.route_mode != MOE_ROUTE_EVEN) return MOE_EINVAL;
     if (c.k > c.E || c.k > 32 || c.E > 1024) return MOE_EUNSUPPORTED;
     if (c.n_groups < 1 || c.n_groups > 64 || c.E % c.n_groups != 0) return MOE_EUNSUPPORTED;
     if (c.topk_groups < 1 || c.topk_groups > c.n_groups) return MOE_EUNSUPPORTED;
@@ -261,6 +262,7 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
     ra.renorm = c.renorm;
     ra.scale = c.scale;
     ra.aux_coeff = c.aux_coeff;
+    ra.even = c.route_mode == MOE_ROUTE_EVEN;
     ra.logits = logits;
     ra.bias = bias;
     ra.sel = sel_scores;

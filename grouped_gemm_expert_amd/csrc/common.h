@@ -89,7 +89,7 @@ hipError_t launch_router_grads(int64_t T, int32_t E, int32_t H, const float *dl,
 // router: selection + weights + counts + aux partial sums; then aux finalize
 struct RouterArgs {
     int64_t T;
-    int32_t E, k, G, kg, score, renorm;
+    int32_t E, k, G, kg, score, renorm, even;
     float scale, aux_coeff;
     const float *logits, *bias;
     float *sel, *topk_w;

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
         bool elig[EPL];
 #pragma unroll
         for (int q = 0; q < EPL; ++q) elig[q] = ok[q];
-        if (p.G > 1) {
+        if (p.G > 1 && !p.even) {
             const int gsz = E / p.G;
 #pragma unroll
             for (int q = 0; q < EPL; ++q)
@@ -139,19 +139,23 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
             }
             __builtin_amdgcn_wave_barrier();
         }
-        // top-k by repeated wave arg-max
+        // top-k by repeated wave arg-max, or the `even` forced experts
         int my_idx = -1;
         float my_val = 0.f;
         float zsel = 0.f;
         for (int j = 0; j < k; ++j) {
             float bv = 0.f;
             int bi = -1;
+            if (p.even) {
+                bi = (int)((t * k + j) % E);
+            } else {
 #pragma unroll
-            for (int q = 0; q < EPL; ++q) {
-                int e = lane + 64 * q;
-                if (elig[q] && ranks_before(S[q], e, bv, bi)) { bv = S[q]; bi = e; }
+                for (int q = 0; q < EPL; ++q) {
+                    int e = lane + 64 * q;
+                    if (elig[q] && ranks_before(S[q], e, bv, bi)) { bv = S[q]; bi = e; }
+                }
+                wave_argmax(bv, bi);
             }
-            wave_argmax(bv, bi);
             // owner lane removes the winner and publishes its prob / sigmoid
             float pv = 0.f;
             if ((bi & 63) == lane) {

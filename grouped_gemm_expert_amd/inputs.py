@@ -38,6 +38,7 @@ class Workload:
     w_std: float = 0.02
     bias_std: Optional[float] = None
     logits: Optional[str] = None    # None: router weight; "zipf" / "normal": logits supplied
+    route: str = "learned"          # "learned" | "even" (forced round-robin experts)
     backward: bool = True
     description: str = ""
 
@@ -82,6 +83,14 @@ WORKLOADS = {
         "mid_sigmoid", T=500, H=384, I=320, E=32, k=6, n_groups=4, topk_groups=2,
         score="sigmoid", scale=2.5, x_std=1.0, bias_std=0.1,
         description="parity shape, sigmoid + bias, group-limited"),
+    "mid_even": Workload(
+        "mid_even", T=530, H=256, I=192, E=24, k=4, n_groups=4, topk_groups=2,
+        score="sigmoid", scale=2.5, x_std=1.0, bias_std=0.1, route="even",
+        description="parity shape, even forced routing (sigmoid, groups ignored)"),
+    "even_softmax": Workload(
+        "even_softmax", T=333, H=128, I=128, E=8, k=2, score="softmax", renorm=False,
+        x_std=1.0, route="even",
+        description="parity shape, even forced routing, softmax without renorm"),
     "mid_skewed": Workload(
         "mid_skewed", T=700, H=256, I=128, E=64, k=4, n_groups=8, topk_groups=4,
         score="sigmoid", scale=2.5, x_std=1.0, logits="zipf",

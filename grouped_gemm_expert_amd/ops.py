@@ -20,6 +20,7 @@ _LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
 
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
+MOE_ROUTE_LEARNED, MOE_ROUTE_EVEN = 0, 1
 (MOE_GEMM_UP_SWIGLU, MOE_GEMM_DOWN, MOE_GEMM_DOWN_DGRAD, MOE_GEMM_UP_DGRAD,
  MOE_GEMM_DOWN_WGRAD, MOE_GEMM_UP_WGRAD) = range(6)
 
@@ -31,7 +32,7 @@ class MoeConfig(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("aux_coeff", ctypes.c_float)]
+                ("aux_coeff", ctypes.c_float), ("route_mode", ctypes.c_int32)]
 
 
 class MoeSaved(ctypes.Structure):
@@ -142,15 +143,16 @@ def _check(status: int, what: str):
 
 
 def config(T, H, I, E, k, n_groups=1, topk_groups=1, score="softmax", renorm=False,
-           scale=1.0, aux_coeff=0.01) -> MoeConfig:
+           scale=1.0, aux_coeff=0.01, route="learned") -> MoeConfig:
     sc = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}.get(score, score)
+    rm = {"learned": MOE_ROUTE_LEARNED, "even": MOE_ROUTE_EVEN}.get(route, route)
     return MoeConfig(int(T), int(H), int(I), int(E), int(k), int(n_groups), int(topk_groups),
-                     int(sc), int(bool(renorm)), float(scale), float(aux_coeff))
+                     int(sc), int(bool(renorm)), float(scale), float(aux_coeff), int(rm))
 
 
 def config_from_workload(w, T=None) -> MoeConfig:
     return config(w.T if T is None else T, w.H, w.I, w.E, w.k, w.n_groups, w.topk_groups,
-                  w.score, w.renorm, w.scale, w.aux_coeff)
+                  w.score, w.renorm, w.scale, w.aux_coeff, w.route)
 
 
 def moe_version() -> str:

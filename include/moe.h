@@ -54,6 +54,7 @@ typedef enum {
 
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };      /* router score function */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };             /* dtype of weight gradients */
+enum { MOE_ROUTE_LEARNED = 0, MOE_ROUTE_EVEN = 1 }; /* expert choice (route_mode) */
 
 /*
  * Layer configuration (host struct, read during the call only).
@@ -69,6 +70,14 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };             /* dtype of weight gradients */
  *   aux_coeff    load-balancing aux loss
  *                aux = aux_coeff * E / (k*T^2) * sum_e counts[e] * sum_t p[t,e]
  *                with p the softmax probabilities, or s / sum_e s for sigmoid.
+ *   route_mode   MOE_ROUTE_LEARNED: the (group-limited) top-k above.
+ *                MOE_ROUTE_EVEN: forced load balancing, `even` form (MegaMoE
+ *                page, "Router force load balancing"): slot j of token t goes
+ *                to expert (t*k + j) mod E whatever the scores; groups play no
+ *                part, and the weights, counts and aux follow from these
+ *                experts by the rules above.  (The page's other form,
+ *                `uniform`, replaces the logits by random values: pass seeded
+ *                random logits with Wr = NULL and MOE_ROUTE_LEARNED.)
  * Ties in any ranking go to the lower index (expert or group).
  * Supported: 1 <= k <= E <= 1024, k <= 32, n_groups divides E,
  * 1 <= topk_groups <= n_groups, k <= topk_groups * E / n_groups,
@@ -82,6 +91,7 @@ typedef struct {
     int32_t renorm;
     float scale;
     float aux_coeff;
+    int32_t route_mode;
 } moe_config;
 
 /*

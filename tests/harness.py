@@ -112,7 +112,7 @@ def oracle_route(w: inputs.Workload, dc: dict):
     bias = None if dc["bias"] is None else dc["bias"].numpy()
     r = oracle.route(l64, score=SCORE[w.score], k=w.k, n_groups=w.n_groups,
                      topk_groups=w.topk_groups, bias=bias, renorm=w.renorm, scale=w.scale,
-                     coeff=w.aux_coeff)
+                     coeff=w.aux_coeff, route_mode=w.route)
     return l64, r
 
 

@@ -49,6 +49,7 @@ BAD = [
     (dict(score=7), 1),
     (dict(T=-1), 1),
     (dict(H=0), 1),
+    (dict(route=7), 1),                       # unknown route mode
 ]
 
 

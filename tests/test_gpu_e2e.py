@@ -13,7 +13,7 @@ from tests import harness as hz
 
 pytestmark = pytest.mark.gpu
 
-E2E = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed"]
+E2E = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "mid_even", "even_softmax"]
 
 
 def _oracle_logits32(w, dc):
@@ -29,7 +29,7 @@ def _compare_all(w, dc, got, tol_f=hz.FWD_TOL, tol_g=hz.GRAD_TOL, backward=True,
     bias = None if dc["bias"] is None else dc["bias"].numpy()
     r = oracle.route(l64, score=hz.SCORE[w.score], k=w.k, n_groups=w.n_groups,
                      topk_groups=w.topk_groups, bias=bias, renorm=w.renorm, scale=w.scale,
-                     coeff=w.aux_coeff, logits32=l32)
+                     coeff=w.aux_coeff, logits32=l32, route_mode=w.route)
     sv = got["saved"]
     assert np.array_equal(sv["topk_idx"].cpu().numpy(), r["idx"])
     assert np.array_equal(sv["counts"].cpu().numpy(), r["counts"])

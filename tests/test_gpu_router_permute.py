@@ -14,7 +14,7 @@ from tests import harness as hz
 pytestmark = pytest.mark.gpu
 
 ROUTER_CASES = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "deepseek_v3", "skewed",
-                "uniform", "fine_grained"]
+                "uniform", "fine_grained", "mid_even", "even_softmax"]
 
 
 def _logits_for(w, seed=0):
@@ -49,7 +49,10 @@ def test_router_bit_exact_given_logits(name):
     torch.cuda.synchronize()
 
     S_ref = oracle.selection_scores(l32, hz.SCORE[w.score], bias)
-    idx_ref = oracle.topk(S_ref, w.k, w.n_groups, w.topk_groups)
+    if w.route == "even":
+        idx_ref = oracle.even_topk(w.T, w.E, w.k)
+    else:
+        idx_ref = oracle.topk(S_ref, w.k, w.n_groups, w.topk_groups)
     l64 = l32.astype(np.float64)
     w_ref = oracle.weights(l64, idx_ref, hz.SCORE[w.score], w.renorm, w.scale)
     counts_ref, *_ = oracle.permute(idx_ref, w.E)
