@@ -140,7 +140,10 @@ moe_status moe_workspace_size(const moe_config *cfg, size_t *fwd_bytes, size_t *
  *   x          [T,H] bf16 tokens (read only when Wr != NULL)
  *   Wr         [E,H] fp32 router weight, or NULL: then `logits` is an input
  *   bias       [E]   fp32 selection-only bias, or NULL
- *   logits     [T,E] fp32: output (x . Wr^T) when Wr != NULL, else input
+ *   logits     [T,E] fp32: output (x . Wr^T) when Wr != NULL, else input.
+ *              The product is formed on bf16 MFMA from an exact three-way
+ *              bf16 split of Wr (x is bf16), so every product is exact in
+ *              fp32 and the sum carries fp32 accumulation error only.
  *   sel_scores [T,E] fp32 selection scores, or NULL: S = logits (softmax) or
  *              fp32(sigmoid(logits)) + bias (sigmoid).  The top-k is decided
  *              on exactly these fp32 values.
@@ -263,7 +266,9 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
  *   saved      the forward's saved tensors
  *   dy [T,H] bf16, d_aux [1] fp32 device scalar or NULL (= 0)
  *   dx [T,H] fp32 out: expert path plus router path (dlogits . Wr) when
- *              Wr != NULL
+ *              Wr != NULL (dlogits and Wr split into bf16 parts as for the
+ *              logits; the part-products below 2^-24 of the result are
+ *              dropped)
  *   dlogits [T,E] fp32 out
  *   dWr [E,H] fp32 out, or NULL (skipped; also skipped when Wr == NULL)
  *   dW1 [E,2I,H], dW2 [E,H,I] fp32 or bf16 (dw_dtype), overwritten or
