@@ -48,12 +48,21 @@ MOE_DEV int wave_uniform_id() { return __builtin_amdgcn_readfirstlane((int)(thre
 // buffer (it cannot prove that those do not alias the copy's destination);
 // the main loop waits for its copies itself (wait_copies) before the barrier
 // that publishes them.  M0 carries the LDS block address.
-MOE_DEV void copy16_to_lds(const char *src, lds_t *dst_block)
+// The global address is a wave-uniform base (SGPR pair, advanced once per
+// stage) plus a per-lane 32-bit byte offset, so issuing a copy costs no
+// vector address arithmetic.
+MOE_DEV void copy16_to_lds(const char *base, uint32_t off, lds_t *dst_block)
 {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_block);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    // readfirstlane yields a signed int: widen through uint32_t so that a low
+    // word with bit 31 set is not sign-extended into the high word
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(m0v)
+                 : "v"(off), "s"(sb), "s"(m0v)
                  : "memory", "m0");
 }
 
@@ -81,7 +90,7 @@ struct KLoad {
     }
     MOE_DEV void issue_one(int i, lds_t *tile, int64_t k0, int, const char *b) const
     {
-        copy16_to_lds(b + k0 * 2 + off[i], tile + (q0 + i) * 1024);
+        copy16_to_lds(b + k0 * 2, off[i], tile + (q0 + i) * 1024);
     }
     MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid, const char *b) const
     {
@@ -136,7 +145,7 @@ struct NLoad {
     {
         int k = krow(i);
         if (k >= kvalid) k = kvalid - 1;
-        copy16_to_lds(b + k0 * (int64_t)ldb + (uint32_t)k * ldb + ncol[i], tile + (q0 + i) * 1024);
+        copy16_to_lds(b + k0 * (int64_t)ldb, (uint32_t)k * ldb + ncol[i], tile + (q0 + i) * 1024);
     }
     MOE_DEV void issue(lds_t *tile, int64_t k0, int kvalid, const char *b) const
     {
@@ -278,6 +287,11 @@ MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const ld
     }
 }
 
+template <int S>
+struct SetTag {
+    static constexpr int value = S;
+};
+
 // Software pipeline over stages v0 .. v1-1 (64 k each) with two LDS buffers
 // and two fragment register sets.  Stage v computes k-steps 0..3 from buffer
 // v%2, reading the fragments of step kk+1 while the MFMAs of step kk run.
@@ -314,8 +328,10 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyOne &&copy_one, Tail &&tai
     Frags<C> f0, f1;
     read_frags<C, A_NMAJ, B_NMAJ>(As[0], Bs[0], 0, f0, wm, wn, lane);
     auto none = [](int) {};
-    for (int v = v0; v < v1; ++v) {
-        const int cur = (v - v0) & 1;
+    // one stage; CUR (the buffer it computes from) is a compile-time
+    // constant, so LDS addresses fold into instruction offsets
+    auto stage = [&](auto tag, int v) {
+        constexpr int cur = decltype(tag)::value;
         kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f0, f1, As[cur], Bs[cur], 1, false, none, acc, wm, wn, lane);
         kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f1, f0, As[cur], Bs[cur], 2, false, none, acc, wm, wn, lane);
         kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f0, f1, As[cur], Bs[cur], 3, false, none, acc, wm, wn, lane);
@@ -332,7 +348,13 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyOne &&copy_one, Tail &&tai
         kstep<C, A_NMAJ, B_NMAJ, NCOPY>(
             f1, f0, As[cur ^ 1], Bs[cur ^ 1], 0, true,
             [&](int q) { copy_one(q, vn, As[cur], Bs[cur]); }, acc, wm, wn, lane);
+    };
+    int v = v0;
+    for (; v + 1 < v1; v += 2) {
+        stage(SetTag<0>(), v);
+        stage(SetTag<1>(), v + 1);
     }
+    if (v < v1) stage(SetTag<0>(), v);
     wait_copies();    // the repeated copies of the last stages
     __syncthreads();  // callers may reuse the LDS
 }
