@@ -80,16 +80,13 @@ __global__ __launch_bounds__(C::NT) void k_dense(DenseArgs d)
         return rem < BK ? (int)rem : BK;
     };
     Acc<C> acc;
-    pipeline<C, A_NMAJ, B_NMAJ, decltype(la)::NI + decltype(lb)::NI>(
+    pipeline<C, A_NMAJ, B_NMAJ, decltype(la)::NI, decltype(lb)::NI>(
         lds, v0, v1,
-        [&](int q, int v, lds_t *As, lds_t *Bs) {
-            const int t = (int)(v / d.spt);
-            const int64_t k0 = (v % d.spt) * BK;
-            constexpr int NA = decltype(la)::NI;
-            if (q < NA)
-                la.issue_one(q, As, k0, kvalid(v), (const char *)d.A[t]);
-            else
-                lb.issue_one(q - NA, Bs, k0, kvalid(v), (const char *)d.B[t]);
+        [&](int q, int v, lds_t *As) {
+            la.issue_one(q, As, (v % d.spt) * BK, kvalid(v), (const char *)d.A[v / d.spt]);
+        },
+        [&](int q, int v, lds_t *Bs) {
+            lb.issue_one(q, Bs, (v % d.spt) * BK, kvalid(v), (const char *)d.B[v / d.spt]);
         },
         [&](int v, lds_t *As, lds_t *Bs) {
             // K-major operands are read from rows padded with zeros past K

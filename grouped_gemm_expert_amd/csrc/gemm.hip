@@ -117,7 +117,7 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
     static_assert(3 * GCOLS == 48 * 8, "staging row = 48 chunks");
     auto soff = [](int r, int chunk) { return r * (3 * GCOLS * 2) + ((chunk ^ (r & 15)) << 4); };
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     constexpr int NW = C::NT / 64, RB = 4;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
         epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
         __syncthreads();
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     constexpr int NW = C::NT / 64, RB = 4;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (r0 + half * EPI_ROWS >= R) break;
         epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
         __syncthreads();
@@ -446,11 +446,20 @@ hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *count
 // 256x256 output tiles computed by 8 waves (two a SIMD).  Wave tiles are
 // 128 rows x 64 columns where the column operand is read with transposing LDS
 // reads (down_dgrad, up_dgrad: the transposed operand then supplies the
-// smaller fragment count) and for up_swiglu; 64 x 128 elsewhere.
-using Tall = TileCfg<256, 256, 128, 64>;
+// smaller fragment count) and for up_swiglu; 64 x 128 elsewhere.  The
+// M-grouped ops stream expert weights as their B operand and get three B
+// stage buffers (all 160 KB of LDS); the weight gradients keep two (a third
+// would spill their registers).
+using Tall = TileCfg<256, 256, 128, 64, 3>;
+using Wide3 = TileCfg<256, 256, 64, 128, 3>;
 using Wide = TileCfg<256, 256, 64, 128>;
+using UpCfg = Tall;
+using DownCfg = Wide3;
+using DownDgradCfg = Tall;
+using UpDgradCfg = Tall;
+using WgradCfg = Wide;
 
-int32_t dgrad2_cols(int32_t I) { return (int32_t)ceil_div(I, Tall::BN); }
+int32_t dgrad2_cols(int32_t I) { return (int32_t)ceil_div(I, DownDgradCfg::BN); }
 
 template <class K>
 static hipError_t launch_k(K kern, int64_t blocks, const GemmArgs &g, hipStream_t s, int nt)
@@ -464,31 +473,31 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
 {
     switch (op) {
     case MOE_GEMM_UP_SWIGLU: {
-        using C = Tall;
+        using C = UpCfg;
         return launch_k(k_up_swiglu<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2)),
                         g, s, C::NT);
     }
     case MOE_GEMM_DOWN: {
-        using C = Wide;
+        using C = DownCfg;
         return launch_k(k_down<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
     }
     case MOE_GEMM_DOWN_DGRAD: {
-        using C = Tall;
+        using C = DownDgradCfg;
         return launch_k(k_down_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN)),
                         g, s, C::NT);
     }
     case MOE_GEMM_UP_DGRAD: {
-        using C = Tall;
+        using C = UpDgradCfg;
         return launch_k(k_up_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
     }
     case MOE_GEMM_DOWN_WGRAD: {
-        using C = Wide;
+        using C = WgradCfg;
         const int64_t act = g.M < g.E ? g.M : g.E;  // non-empty experts, at most
         int64_t total = act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN);
         return launch_k(k_wgrad<C, false>, grid_for(total), g, s, C::NT);
     }
     case MOE_GEMM_UP_WGRAD: {
-        using C = Wide;
+        using C = WgradCfg;
         const int64_t act = g.M < g.E ? g.M : g.E;
         int64_t total = act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN);
         return launch_k(k_wgrad<C, true>, grid_for(total), g, s, C::NT);

@@ -5,6 +5,8 @@
 // (dense.hip).
 #pragma once
 
+#include <utility>
+
 #include "common.h"
 
 namespace moe {
@@ -21,13 +23,22 @@ typedef __attribute__((address_space(3))) float lds_f32;
 MOE_DEV int swz(int r) { return (r ^ (r >> 3)) & 7; }
 MOE_DEV int lds_off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
-template <int BM_, int BN_, int WM_, int WN_>
+// BM x BN output tile computed by waves of WM x WN.  The A operand (rows)
+// has two LDS stage buffers of 64 k, the B operand (columns) NBB of them:
+// the copies of a B stage get NBB-1 stages to land, which matters when B
+// streams from HBM (the expert weights of the forward and dgrad ops).  The
+// LDS also holds the epilogue's 128 KB staging tile.
+template <int BM_, int BN_, int WM_, int WN_, int NBB_ = 2>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NBB = NBB_;
     static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
     static constexpr int NT = WAVES_M * WAVES_N * 64;
     static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int LDS_BYTES = 2 * (BM + BN) * 128;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+    static constexpr int RING_BYTES = 2 * A_BYTES + NBB * B_BYTES;
+    static constexpr int LDS_BYTES = RING_BYTES > 131072 ? RING_BYTES : 131072;
+    static_assert(NBB == 2 || NBB == 3, "two or three B stage buffers");
+    static_assert(LDS_BYTES <= 163840, "LDS of one CU");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
     static_assert(BM == 256 || BM == 128, "m-tile prefix sums exist for 256 and 128 rows");
 };
@@ -263,9 +274,9 @@ MOE_DEV void read_one(int r, const lds_t *As, const lds_t *Bs, int kk, Frags<C> 
 
 // The MFMAs of one k-step (fragments `cur`) in (i, j) order.  Before MFMA n
 // the wave issues fragment read n of the next k-step into `nxt` (n < FM+FN)
-// and the copies q of the next-but-one stage with q*NMF/NCOPY == n (when
-// `copy`), so LDS reads and global->LDS copies are spread evenly over the
-// MFMAs instead of arriving in bursts; sched_barrier pins that order.
+// and the copies q (of NCOPY) with q*NMF/NCOPY == n (when `copy`), so LDS
+// reads and global->LDS copies are spread evenly over the MFMAs instead of
+// arriving in bursts; sched_barrier pins that order.
 template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class CopyOne>
 MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const lds_t *Bs, int kk_next,
                    bool copy, CopyOne &&copy_one, Acc<C> &acc, int wm, int wn, int lane)
@@ -292,69 +303,92 @@ struct SetTag {
     static constexpr int value = S;
 };
 
-// Software pipeline over stages v0 .. v1-1 (64 k each) with two LDS buffers
-// and two fragment register sets.  Stage v computes k-steps 0..3 from buffer
-// v%2, reading the fragments of step kk+1 while the MFMAs of step kk run.
-// Once the fragments of step 3 are in registers the wave no longer needs the
-// buffer, so the barrier comes before step 3's MFMAs: each wave first waits
-// for its own copies of stage v+1 (and lets `tail` fix that stage up), then
-// the barrier publishes stage v+1 and frees buffer v%2; after it the wave
-// reads step 0 of stage v+1 and issues the copies of stage v+2 into the freed
-// buffer while step 3's MFMAs execute.  The copies of a stage thus have a
-// whole stage of MFMAs to land in, and no wave idles on LDS latency right
-// after the barrier.
-// copy_one(q, v, As, Bs) issues copy q (of NCOPY per wave) of stage v;
-// tail(v, As, Bs) runs after they landed.
-template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class CopyOne, class Tail>
-MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyOne &&copy_one, Tail &&tail, Acc<C> &acc)
+// f(SetTag<I>(), v + I) for I = 0 .. P-1, stopping at v1.
+template <class F, int... I>
+MOE_DEV void stage_run(F &&f, int v, int v1, std::integer_sequence<int, I...>)
 {
+    ((v + I < v1 ? f(SetTag<I>(), v + I) : void()), ...);
+}
+
+// Software pipeline over stages v0 .. v1-1 (64 k each): two LDS buffers for
+// A, NBB for B, two fragment register sets.  Stage v computes k-steps 0..3
+// from A buffer v%2 and B buffer v%NBB, reading the fragments of step kk+1
+// while the MFMAs of step kk run.  Once the fragments of step 3 are in
+// registers the wave no longer needs those buffers, so the barrier comes
+// before step 3's MFMAs: each wave first waits for its own copies of stage
+// v+1 (and lets `tail` fix that stage up), then the barrier publishes stage
+// v+1 and frees the stage-v buffers; after it the wave reads step 0 of stage
+// v+1 and, while step 3's MFMAs execute, issues the A copies of stage v+2 and
+// the B copies of stage v+NBB into the freed buffers.  A copies thus have one
+// stage of MFMAs to land in, B copies NBB-1, and no wave idles on LDS
+// latency right after the barrier.
+// copy_a(q, v, As) / copy_b(q, v, Bs) issue copy q (of NCA / NCB per wave)
+// of stage v's A / B tile; tail(v, As, Bs) runs after stage v landed.
+template <class C, bool A_NMAJ, bool B_NMAJ, int NCA, int NCB, class CopyA, class CopyB, class Tail>
+MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b, Tail &&tail,
+                      Acc<C> &acc)
+{
+    constexpr int NB = C::NBB;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    lds_t *As[2] = {lds, lds + C::BM * 128};
-    lds_t *Bs[2] = {lds + 2 * C::BM * 128, lds + 2 * C::BM * 128 + C::BN * 128};
+    lds_t *As[2] = {lds, lds + C::A_BYTES};
+    lds_t *Bs[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) Bs[b] = lds + 2 * C::A_BYTES + b * C::B_BYTES;
     acc.zero();
     if (v1 <= v0) return;
+    // A and B of stages v0, v0+1, then B of stages up to v0+NB-1 (past the
+    // end: the last stage again, into buffers nothing reads); wait for stage
+    // v0 only
+    auto clampv = [&](int v) { return v < v1 ? v : v1 - 1; };
 #pragma unroll
-    for (int q = 0; q < NCOPY; ++q) copy_one(q, v0, As[0], Bs[0]);
-    if (v0 + 1 < v1) {
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int q = 0; q < NCOPY; ++q) copy_one(q, v0 + 1, As[1], Bs[1]);
-        wait_copies_le<NCOPY>();
-    } else {
-        wait_copies();
+        for (int q = 0; q < NCA; ++q) copy_a(q, clampv(v0 + s), As[s]);
+#pragma unroll
+        for (int q = 0; q < NCB; ++q) copy_b(q, clampv(v0 + s), Bs[s]);
     }
+#pragma unroll
+    for (int s = 2; s < NB; ++s) {
+#pragma unroll
+        for (int q = 0; q < NCB; ++q) copy_b(q, clampv(v0 + s), Bs[s]);
+    }
+    wait_copies_le<NCA + (NB - 1) * NCB>();
     tail(v0, As[0], Bs[0]);
     __syncthreads();
     Frags<C> f0, f1;
     read_frags<C, A_NMAJ, B_NMAJ>(As[0], Bs[0], 0, f0, wm, wn, lane);
     auto none = [](int) {};
-    // one stage; CUR (the buffer it computes from) is a compile-time
-    // constant, so LDS addresses fold into instruction offsets
+    // one stage; the buffers it uses are compile-time constants, so LDS
+    // addresses fold into instruction offsets
     auto stage = [&](auto tag, int v) {
-        constexpr int cur = decltype(tag)::value;
-        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f0, f1, As[cur], Bs[cur], 1, false, none, acc, wm, wn, lane);
-        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f1, f0, As[cur], Bs[cur], 2, false, none, acc, wm, wn, lane);
-        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(f0, f1, As[cur], Bs[cur], 3, false, none, acc, wm, wn, lane);
-        if (v + 1 < v1) {
-            wait_copies();
-            tail(v + 1, As[cur ^ 1], Bs[cur ^ 1]);
-        }
+        constexpr int I = decltype(tag)::value;
+        constexpr int a = I % 2, an = (I + 1) % 2, b = I % NB, bn = (I + 1) % NB;
+        kstep<C, A_NMAJ, B_NMAJ, 1>(f0, f1, As[a], Bs[b], 1, false, none, acc, wm, wn, lane);
+        kstep<C, A_NMAJ, B_NMAJ, 1>(f1, f0, As[a], Bs[b], 2, false, none, acc, wm, wn, lane);
+        kstep<C, A_NMAJ, B_NMAJ, 1>(f0, f1, As[a], Bs[b], 3, false, none, acc, wm, wn, lane);
+        // each stage issues NCA A copies then NCB B copies, so "stage v+1
+        // landed" is "at most the B copies of stages v+2 .. v+NB-1 outstanding"
+        wait_copies_le<(NB - 2) * NCB>();
+        if (v + 1 < v1) tail(v + 1, As[an], Bs[bn]);
         __syncthreads();
-        // step 0 of stage v+1 and the copies of stage v+2 into this stage's
-        // buffer.  Past the end both are harmless and branch-free: the reads
-        // fetch stale fragments that are never used, and the last stage is
-        // copied again into a buffer that nothing reads any more.
-        const int vn = v + 2 < v1 ? v + 2 : v1 - 1;
-        kstep<C, A_NMAJ, B_NMAJ, NCOPY>(
-            f1, f0, As[cur ^ 1], Bs[cur ^ 1], 0, true,
-            [&](int q) { copy_one(q, vn, As[cur], Bs[cur]); }, acc, wm, wn, lane);
+        // step 0 of stage v+1; A copies of stage v+2 and B copies of stage
+        // v+NB into the freed buffers.  Past the end both are harmless and
+        // branch-free: the reads fetch stale fragments that are never used,
+        // and the last stage is copied again into buffers nothing reads.
+        const int va = clampv(v + 2), vb = clampv(v + NB);
+        kstep<C, A_NMAJ, B_NMAJ, NCA + NCB>(
+            f1, f0, As[an], Bs[bn], 0, true,
+            [&](int q) {
+                if (q < NCA) copy_a(q, va, As[a]);
+                else copy_b(q - NCA, vb, Bs[b]);
+            },
+            acc, wm, wn, lane);
     };
+    constexpr int P = NB == 3 ? 6 : 2;  // buffer pattern period
     int v = v0;
-    for (; v + 1 < v1; v += 2) {
-        stage(SetTag<0>(), v);
-        stage(SetTag<1>(), v + 1);
-    }
-    if (v < v1) stage(SetTag<0>(), v);
+    for (; v + P <= v1; v += P) stage_run(stage, v, v1, std::make_integer_sequence<int, P>());
+    stage_run(stage, v, v1, std::make_integer_sequence<int, P - 1>());
     wait_copies();    // the repeated copies of the last stages
     __syncthreads();  // callers may reuse the LDS
 }
@@ -368,14 +402,10 @@ MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> 
         const int64_t rem = K - (int64_t)s * BK;
         return KTAIL ? (rem < BK ? (int)rem : BK) : BK;
     };
-    pipeline<C, A_NMAJ, B_NMAJ, LA::NI + LB::NI>(
+    pipeline<C, A_NMAJ, B_NMAJ, LA::NI, LB::NI>(
         lds, 0, (int)ceil_div(K, BK),
-        [&](int q, int s, lds_t *As, lds_t *Bs) {
-            if (q < LA::NI)
-                la.issue_one(q, As, (int64_t)s * BK, kvalid(s), la.base);
-            else
-                lb.issue_one(q - LA::NI, Bs, (int64_t)s * BK, kvalid(s), lb.base);
-        },
+        [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * BK, kvalid(s), la.base); },
+        [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * BK, kvalid(s), lb.base); },
         [&](int s, lds_t *As, lds_t *Bs) {
             if (KTAIL && kvalid(s) < BK) {
                 la.zero_tail(As, kvalid(s));
@@ -461,7 +491,7 @@ MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, float *out, int64_t m
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t col = n0 + 4 * lane;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (m0 + half * EPI_ROWS >= mlim) break;
         epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
         __syncthreads();
