@@ -274,23 +274,21 @@ MOE_DEV void read_one(int r, const lds_t *As, const lds_t *Bs, int kk, Frags<C> 
 
 // The MFMAs of one k-step (fragments `cur`) in (i, j) order.  Before MFMA n
 // the wave issues fragment read n of the next k-step into `nxt` (n < FM+FN)
-// and the copies q (of NCOPY) with q*NMF/NCOPY == n (when `copy`), so LDS
-// reads and global->LDS copies are spread evenly over the MFMAs instead of
-// arriving in bursts; sched_barrier pins that order.
-template <class C, bool A_NMAJ, bool B_NMAJ, int NCOPY, class CopyOne>
+// and the copies i (of NC) with i*NMF/NC == n, so LDS reads and
+// global->LDS copies are spread evenly over the MFMAs instead of arriving in
+// bursts; sched_barrier pins that order.
+template <class C, bool A_NMAJ, bool B_NMAJ, int NC, class Copy>
 MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const lds_t *Bs, int kk_next,
-                   bool copy, CopyOne &&copy_one, Acc<C> &acc, int wm, int wn, int lane)
+                   Copy &&copy, Acc<C> &acc, int wm, int wn, int lane)
 {
     constexpr int NMF = C::FM * C::FN, NR = C::FM + C::FN;
     static_assert(NR <= NMF, "one read per MFMA at most");
 #pragma unroll
     for (int n = 0; n < NMF; ++n) {
         if (n < NR) read_one<C, A_NMAJ, B_NMAJ>(n, As, Bs, kk_next, nxt, wm, wn, lane);
-        if (copy) {
 #pragma unroll
-            for (int q = 0; q < NCOPY; ++q)
-                if (q * NMF / NCOPY == n) copy_one(q);
-        }
+        for (int i = 0; i < NC; ++i)
+            if (i * NMF / NC == n) copy(i);
         __builtin_amdgcn_sched_barrier(0);
         const int i = n / C::FN, j = n % C::FN;
         acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc.v[i][j], 0, 0, 0);
@@ -318,10 +316,14 @@ MOE_DEV void stage_run(F &&f, int v, int v1, std::integer_sequence<int, I...>)
 // before step 3's MFMAs: each wave first waits for its own copies of stage
 // v+1 (and lets `tail` fix that stage up), then the barrier publishes stage
 // v+1 and frees the stage-v buffers; after it the wave reads step 0 of stage
-// v+1 and, while step 3's MFMAs execute, issues the A copies of stage v+2 and
-// the B copies of stage v+NBB into the freed buffers.  A copies thus have one
-// stage of MFMAs to land in, B copies NBB-1, and no wave idles on LDS
-// latency right after the barrier.
+// v+1 while step 3's MFMAs execute, and no wave idles on LDS latency right
+// after the barrier.
+// The copies into the freed buffers are spread so that the CU's vector
+// memory path (64 bytes a clock; one copy is 1 KB) never gets them in a
+// burst: the A copies of stage v+2 go into step 3 of stage v; with three B
+// buffers the B copies of stage v+3 are split into four slots, one in step 3
+// of stage v and one in each of steps 0..2 of stage v+1 (they still have a
+// stage to land); with two B buffers they all go into step 3 of stage v.
 // copy_a(q, v, As) / copy_b(q, v, Bs) issue copy q (of NCA / NCB per wave)
 // of stage v's A / B tile; tail(v, As, Bs) runs after stage v landed.
 template <class C, bool A_NMAJ, bool B_NMAJ, int NCA, int NCB, class CopyA, class CopyB, class Tail>
@@ -329,6 +331,9 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
                       Acc<C> &acc)
 {
     constexpr int NB = C::NBB;
+    constexpr bool SPREAD = NB == 3;
+    constexpr int SB = SPREAD ? (NCB + 3) / 4 : NCB;  // B copies per slot (slot 0: after the barrier)
+    static_assert(!SPREAD || NCB % 4 == 0, "B copies split into four equal slots");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     lds_t *As[2] = {lds, lds + C::A_BYTES};
@@ -337,10 +342,10 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
     for (int b = 0; b < NB; ++b) Bs[b] = lds + 2 * C::A_BYTES + b * C::B_BYTES;
     acc.zero();
     if (v1 <= v0) return;
-    // A and B of stages v0, v0+1, then B of stages up to v0+NB-1 (past the
-    // end: the last stage again, into buffers nothing reads); wait for stage
-    // v0 only
     auto clampv = [&](int v) { return v < v1 ? v : v1 - 1; };
+    // A and B of stages v0, v0+1, then slot 0 of stage v0+2's B copies (its
+    // other slots go into stage v0's first steps); past the end the last stage
+    // again, into buffers nothing reads.  Wait for stage v0 only.
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -348,37 +353,48 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
 #pragma unroll
         for (int q = 0; q < NCB; ++q) copy_b(q, clampv(v0 + s), Bs[s]);
     }
+    if constexpr (SPREAD) {
 #pragma unroll
-    for (int s = 2; s < NB; ++s) {
-#pragma unroll
-        for (int q = 0; q < NCB; ++q) copy_b(q, clampv(v0 + s), Bs[s]);
+        for (int q = 0; q < SB; ++q) copy_b(q, clampv(v0 + 2), Bs[2]);
     }
-    wait_copies_le<NCA + (NB - 1) * NCB>();
+    wait_copies_le<NCA + NCB + (SPREAD ? SB : 0)>();
     tail(v0, As[0], Bs[0]);
     __syncthreads();
     Frags<C> f0, f1;
     read_frags<C, A_NMAJ, B_NMAJ>(As[0], Bs[0], 0, f0, wm, wn, lane);
-    auto none = [](int) {};
     // one stage; the buffers it uses are compile-time constants, so LDS
     // addresses fold into instruction offsets
     auto stage = [&](auto tag, int v) {
         constexpr int I = decltype(tag)::value;
         constexpr int a = I % 2, an = (I + 1) % 2, b = I % NB, bn = (I + 1) % NB;
-        kstep<C, A_NMAJ, B_NMAJ, 1>(f0, f1, As[a], Bs[b], 1, false, none, acc, wm, wn, lane);
-        kstep<C, A_NMAJ, B_NMAJ, 1>(f1, f0, As[a], Bs[b], 2, false, none, acc, wm, wn, lane);
-        kstep<C, A_NMAJ, B_NMAJ, 1>(f0, f1, As[a], Bs[b], 3, false, none, acc, wm, wn, lane);
-        // each stage issues NCA A copies then NCB B copies, so "stage v+1
-        // landed" is "at most the B copies of stages v+2 .. v+NB-1 outstanding"
+        constexpr int bp = (I + NB - 1) % NB;  // buffer of stage v-1: gets stage v-1+NB
+        const int vp = clampv(v - 1 + NB);
+        auto slot = [&](int s) {  // B copies of slot s of stage v-1+NB
+            return [&, s](int i) { copy_b(s * SB + i, vp, Bs[bp]); };
+        };
+        auto none = [](int) {};
+        if constexpr (SPREAD) {
+            kstep<C, A_NMAJ, B_NMAJ, SB>(f0, f1, As[a], Bs[b], 1, slot(1), acc, wm, wn, lane);
+            kstep<C, A_NMAJ, B_NMAJ, SB>(f1, f0, As[a], Bs[b], 2, slot(2), acc, wm, wn, lane);
+            kstep<C, A_NMAJ, B_NMAJ, SB>(f0, f1, As[a], Bs[b], 3, slot(3), acc, wm, wn, lane);
+        } else {
+            kstep<C, A_NMAJ, B_NMAJ, 0>(f0, f1, As[a], Bs[b], 1, none, acc, wm, wn, lane);
+            kstep<C, A_NMAJ, B_NMAJ, 0>(f1, f0, As[a], Bs[b], 2, none, acc, wm, wn, lane);
+            kstep<C, A_NMAJ, B_NMAJ, 0>(f0, f1, As[a], Bs[b], 3, none, acc, wm, wn, lane);
+        }
+        // every stage issues the same copies, and stage v+1's were all issued
+        // before the last A copies; only the B copies of stage v+2 (three B
+        // buffers) may still be outstanding
         wait_copies_le<(NB - 2) * NCB>();
         if (v + 1 < v1) tail(v + 1, As[an], Bs[bn]);
         __syncthreads();
-        // step 0 of stage v+1; A copies of stage v+2 and B copies of stage
+        // step 0 of stage v+1; A copies of stage v+2 and B slot 0 of stage
         // v+NB into the freed buffers.  Past the end both are harmless and
         // branch-free: the reads fetch stale fragments that are never used,
         // and the last stage is copied again into buffers nothing reads.
         const int va = clampv(v + 2), vb = clampv(v + NB);
-        kstep<C, A_NMAJ, B_NMAJ, NCA + NCB>(
-            f1, f0, As[an], Bs[bn], 0, true,
+        kstep<C, A_NMAJ, B_NMAJ, NCA + SB>(
+            f1, f0, As[an], Bs[bn], 0,
             [&](int q) {
                 if (q < NCA) copy_a(q, va, As[a]);
                 else copy_b(q - NCA, vb, Bs[b]);
