@@ -27,6 +27,16 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
   backward_tokens, weight_grads, weight_grad_elements, router_weight_grad
                        -- pinned: central finite differences of the forward and
                           an independent torch fp64 autograd formulation
+  e4m3_values          -- pinned: the E4M3 points the OCP MX format fixes (zero,
+                          smallest subnormal, smallest normal, one, 448, NaN),
+                          strict monotonicity over all finite codes
+  mx_quantize          -- pinned: hand-worked golden blocks, round trip of every
+                          finite code, the half-spacing error bound and the
+                          scale range, exactness on representable inputs
+  mx_expert_rows, mx_forward
+                       -- pinned: exact integer GEMMs on MX-representable inputs,
+                          y = sum_j w_j o_j against mx_forward, the MX error
+                          bound against the exact forward
 """
 from __future__ import annotations
 
@@ -84,12 +94,17 @@ def _load():
                                         P, P, P, P, P],
         "oracle_router_weight_grad": [i64, i32, i32, P, P, P],
         "oracle_expert_rows": [i32, i32, i32, P, P, P, P, i64, P, P, P, P, P],
+        "oracle_mx_quantize": [i64, i64, P, P, P],
+        "oracle_mx_expert_rows": [i32, i32, i32, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P],
+        "oracle_mx_forward": [i32, i32, i32, P, P, P, P, P, P, P, P, i64, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = None
     lib.oracle_aux.restype = f64
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = f64
     _lib = lib
     return lib
 
@@ -312,3 +327,76 @@ def route(logits64: np.ndarray, *, score: int, k: int, n_groups: int = 1, topk_g
     a = aux(logits64, counts, k, score, coeff)
     return dict(S=S, idx=idx, w=w, counts=counts, offsets=offsets, row_map=row_map,
                 pos=pos, aux=a)
+
+
+# ------------------------------------------------------------------ MXFP8 ----
+
+def e4m3_values() -> np.ndarray:
+    """The value of every E4M3 code 0..255 (NaN for 0x7F / 0xFF)."""
+    lib = _load()
+    return np.array([lib.oracle_e4m3_value(c) for c in range(256)], np.float64)
+
+
+def mx_quantize(src: np.ndarray):
+    """Row-wise MXFP8 of a bf16 matrix [R, K] (K % 32 == 0): codes [R, K] uint8,
+    scales [R, K/32] uint8 (E8M0, 2^(s-127)), blocks in natural order."""
+    src = _c(src, np.uint16)
+    R, K = src.shape
+    assert K % 32 == 0
+    codes = np.empty((R, K), np.uint8)
+    scales = np.empty((R, K // 32), np.uint8)
+    _load().oracle_mx_quantize(R, K, _p(src), _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The values an MX matrix stands for (double)."""
+    vals = e4m3_values()[codes]
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return vals * np.repeat(sc, 32, axis=-1)
+
+
+class MxOperands:
+    """x, w1 and w2 quantised along their contraction dimensions."""
+
+    def __init__(self, x, w1, w2):
+        x = _c(x, np.uint16)
+        w1 = _c(w1, np.uint16)
+        w2 = _c(w2, np.uint16)
+        T, H = x.shape
+        E, twoI, _ = w1.shape
+        self.H, self.I, self.E = H, twoI // 2, E
+        self.xq, self.xs = mx_quantize(x)
+        self.w1q, self.w1s = mx_quantize(w1.reshape(E * twoI, H))
+        self.w2q, self.w2s = mx_quantize(w2.reshape(E * H, self.I))
+
+    def ptrs(self):
+        return (_p(self.xq), _p(self.xs), _p(self.w1q), _p(self.w1s), _p(self.w2q),
+                _p(self.w2s))
+
+
+def mx_expert_rows(ops: MxOperands, idx, slots):
+    """Per flat slot f = t*k + j of the MXFP8 path: g, u, a (double [n, I]),
+    aq [n, I], as [n, I/32] (a rounded to bf16 and MX-quantised), o [n, H]."""
+    idx = _c(idx, np.int32)
+    sl = _c(np.asarray(slots), np.int64)
+    k = idx.shape[1]
+    n = sl.shape[0]
+    H, I = ops.H, ops.I
+    g = np.empty((n, I)); u = np.empty((n, I)); a = np.empty((n, I)); o = np.empty((n, H))
+    aq = np.empty((n, I), np.uint8)
+    as_ = np.empty((n, I // 32), np.uint8)
+    _load().oracle_mx_expert_rows(H, I, k, *ops.ptrs(), _p(idx), n, _p(sl), _p(g), _p(u), _p(a),
+                                  _p(aq), _p(as_), _p(o))
+    return g, u, a, aq, as_, o
+
+
+def mx_forward(ops: MxOperands, idx, w, toks=None) -> np.ndarray:
+    """y [ntok, H] (double) of the MXFP8 path for the listed tokens."""
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    T, k = idx.shape
+    tk, n = _toks(toks, T)
+    y = np.empty((n, ops.H), np.float64)
+    _load().oracle_mx_forward(ops.H, ops.I, k, *ops.ptrs(), _p(idx), _p(w), n, _p(tk), _p(y))
+    return y

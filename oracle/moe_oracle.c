@@ -624,3 +624,193 @@ void oracle_expert_rows(int32_t H, int32_t I, int32_t k, const uint16_t *x,
                    o + q * H);
     }
 }
+
+/* ======================================================================== */
+/* MXFP8 expert precision (page "MegaMoE", "Expert precision": the two      */
+/* expert stages run in MXFP8).  The pages name the format only; MXFP8 is    */
+/* read as the OCP Microscaling (MX) v1.0 format:                           */
+/*   - a block is 32 consecutive elements along the contraction dimension;   */
+/*   - the block shares one E8M0 scale 2^X, X = floor(log2(amax)) - 8, where */
+/*     8 is the exponent of E4M3's largest normal (448 = 1.75 * 2^8); X is   */
+/*     clamped to E8M0's range [-127, 127]; an all-zero block takes X = -127;*/
+/*   - each element is v / 2^X rounded to nearest-even E4M3, saturating to   */
+/*     +-448 (E4M3 has no infinity; 0x7F / 0xFF are NaN and never produced). */
+/* E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0   */
+/* is subnormal, m * 2^-9.                                                   */
+/* ======================================================================== */
+
+double oracle_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+/* Nearest-even E4M3 code of q (already divided by the block scale),         */
+/* saturating.  The grid spacing around |q| is 2^(max(floor(log2|q|),-6)-3). */
+static uint8_t e4m3_encode(double q)
+{
+    int neg = signbit(q) ? 1 : 0, ex, e, m;
+    double a = fabs(q), step, r;
+    if (a == 0.0) return (uint8_t)(neg << 7);
+    frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+    e = ex - 1;
+    if (e < -6) e = -6;
+    step = ldexp(1.0, e - 3);
+    r = nearbyint(a / step) * step; /* a / step is exact; ties to even */
+    if (r > 448.0) r = 448.0;
+    if (r == 0.0) return (uint8_t)(neg << 7);
+    if (r < ldexp(1.0, -6)) {
+        m = (int)ldexp(r, 9); /* subnormal: r = m * 2^-9 */
+        return (uint8_t)((neg << 7) | m);
+    }
+    frexp(r, &ex);
+    e = ex - 1;
+    m = (int)((ldexp(r, -e) - 1.0) * 8.0);
+    return (uint8_t)((neg << 7) | ((e + 7) << 3) | m);
+}
+
+/* One block of n values (n = 32): scale code X + 127 and the element codes. */
+static uint8_t mx_block(const double *v, int n, uint8_t *codes)
+{
+    double amax = 0.0;
+    int X, ex, i;
+    for (i = 0; i < n; ++i)
+        if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    if (amax == 0.0) {
+        X = -127;
+    } else {
+        frexp(amax, &ex);
+        X = (ex - 1) - 8;
+        if (X < -127) X = -127;
+        if (X > 127) X = 127;
+    }
+    for (i = 0; i < n; ++i) codes[i] = e4m3_encode(ldexp(v[i], -X));
+    return (uint8_t)(X + 127);
+}
+
+static double mx_scale(uint8_t s) { return ldexp(1.0, (int)s - 127); }
+
+/* Row-wise MXFP8 quantisation of a bf16 matrix src [rows, K] (K a multiple  */
+/* of 32): codes [rows, K], scales [rows, K/32] (block b of row r covers     */
+/* columns 32b .. 32b+31).                                                   */
+void oracle_mx_quantize(int64_t rows, int64_t K, const uint16_t *src, uint8_t *codes,
+                        uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double v[32];
+        for (int64_t b = 0; b < K / 32; ++b) {
+            for (int i = 0; i < 32; ++i) v[i] = bf(src[r * K + b * 32 + i]);
+            scales[r * (K / 32) + b] = mx_block(v, 32, codes + r * K + b * 32);
+        }
+    }
+}
+
+/* The value an MX element stands for: E4M3 value times the block scale.    */
+static double mx_value(const uint8_t *codes, const uint8_t *scales, int64_t K, int64_t r,
+                       int64_t c)
+{
+    return oracle_e4m3_value(codes[r * K + c]) * mx_scale(scales[r * (K / 32) + c / 32]);
+}
+
+/* fp32 -> bf16, nearest-even (finite values). */
+static uint16_t f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* One (token, expert) slot of the MXFP8 expert MLP.  Operands are MX        */
+/* matrices quantised along their contraction dimension:                    */
+/*   x  [T, H]      (blocks along H)     w1 [E*2I, H] (blocks along H)      */
+/*   w2 [E*H, I]    (blocks along I)                                        */
+/*   g, u = gate / up halves of X . W1[e]^T (double, from the MX values)     */
+/*   a    = silu(g) * u, then rounded to fp32 and to bf16 (the precision in  */
+/*          which the path holds its activations) and MX-quantised along I   */
+/*          into aq [I], as_ [I/32]                                          */
+/*   o    = A . W2[e]^T from the MX values of a                              */
+static void mx_slot(int32_t H, int32_t I, int64_t t, int32_t e, const uint8_t *xq,
+                    const uint8_t *xs, const uint8_t *w1q, const uint8_t *w1s,
+                    const uint8_t *w2q, const uint8_t *w2s, double *g, double *u, double *a,
+                    uint8_t *aq, uint8_t *as_, double *o)
+{
+    double *ab = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int32_t i = 0; i < I; ++i) {
+        double sg = 0.0, su = 0.0;
+        for (int32_t h = 0; h < H; ++h) {
+            double xv = mx_value(xq, xs, H, t, h);
+            sg += xv * mx_value(w1q, w1s, H, (int64_t)e * 2 * I + i, h);
+            su += xv * mx_value(w1q, w1s, H, (int64_t)e * 2 * I + I + i, h);
+        }
+        g[i] = sg;
+        u[i] = su;
+        a[i] = silu(sg) * su;
+        ab[i] = bf(f32_to_bf16((float)a[i]));
+    }
+    for (int32_t b = 0; b < I / 32; ++b) as_[b] = mx_block(ab + b * 32, 32, aq + b * 32);
+    if (o)
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < I; ++i)
+                acc += mx_value(w2q, w2s, I, (int64_t)e * H + h, i) *
+                       oracle_e4m3_value(aq[i]) * mx_scale(as_[i / 32]);
+            o[h] = acc;
+        }
+    free(ab);
+}
+
+/* Per-slot intermediates of the MXFP8 expert MLP for listed flat slots      */
+/* f = t*k + j: g, u, a [n, I] (double), aq [n, I], as_ [n, I/32], o [n, H]. */
+void oracle_mx_expert_rows(int32_t H, int32_t I, int32_t k, const uint8_t *xq,
+                           const uint8_t *xs, const uint8_t *w1q, const uint8_t *w1s,
+                           const uint8_t *w2q, const uint8_t *w2s, const int32_t *idx, int64_t n,
+                           const int64_t *slots, double *g, double *u, double *a, uint8_t *aq,
+                           uint8_t *as_, double *o)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < n; ++q) {
+        int64_t f = slots[q];
+        mx_slot(H, I, f / k, idx[f], xq, xs, w1q, w1s, w2q, w2s, g + q * I, u + q * I,
+                a + q * I, aq + q * I, as_ + q * (I / 32), o + q * H);
+    }
+}
+
+/* MXFP8 expert forward for a list of tokens (toks == NULL: 0..ntok-1):      */
+/*   y[t] = sum_{j ascending} w[t,j] * o(t, idx[t,j])                        */
+void oracle_mx_forward(int32_t H, int32_t I, int32_t k, const uint8_t *xq, const uint8_t *xs,
+                       const uint8_t *w1q, const uint8_t *w1s, const uint8_t *w2q,
+                       const uint8_t *w2s, const int32_t *idx, const double *w, int64_t ntok,
+                       const int64_t *toks, double *y)
+{
+#pragma omp parallel
+    {
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        uint8_t *aq = (uint8_t *)malloc((size_t)I);
+        uint8_t *as_ = (uint8_t *)malloc((size_t)I / 32 + 1);
+        double *o = (double *)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < ntok; ++q) {
+            int64_t t = toks ? toks[q] : q;
+            double *yt = y + q * H;
+            for (int32_t h = 0; h < H; ++h) yt[h] = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                mx_slot(H, I, t, idx[t * k + j], xq, xs, w1q, w1s, w2q, w2s, g, u, a, aq, as_,
+                        o);
+                for (int32_t h = 0; h < H; ++h) yt[h] += w[t * k + j] * o[h];
+            }
+        }
+        free(g);
+        free(u);
+        free(a);
+        free(aq);
+        free(as_);
+        free(o);
+    }
+}
