@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "router.hip", "permute.hip", "gemm.hip", "dense.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "router.hip", "permute.hip", "gemm.hip", "dense.hip", "elementwise.hip",
+           "mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # No packed fp32 instructions: keep every fp32 op scalar on this target.
@@ -41,7 +42,7 @@ def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 5, out: str = OUT, defines=()) -> str:
+def build(verbose: bool = False, jobs: int = 7, out: str = OUT, defines=()) -> str:
     """Compile every source and link `out`.  `defines` (NAME=VALUE strings) and
     `out` exist for building tuning variants outside the package."""
     build_dir = BUILD_DIR if out == OUT else out + ".objs"

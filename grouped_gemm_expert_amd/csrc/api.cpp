@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "mxfmt.h"
 
 using namespace moe;
 
@@ -29,6 +30,9 @@ struct Carver {
     }
 };
 
+// Bytes of an MX matrix [rows, K]: codes [rows, Kp] then scales [rows, Kp/32].
+int64_t mx_bytes(int64_t rows, int64_t K) { return rows * mx_kp(K) + rows * (mx_kp(K) / 32); }
+
 struct FwdWs {
     float *prob_part;
     int32_t *chunk_hist;
@@ -36,6 +40,8 @@ struct FwdWs {
     float *wrow;
     float *o;   // [M,H] fp32; the single-op grouped GEMMs reuse it for xg / dyw
     void *router;  // router GEMM scratch (router_ws_bytes_fwd)
+    uint8_t *xmx;  // MXFP8 forward: MX matrix of x [T, Hp]
+    uint8_t *amx;  // MXFP8 forward: MX matrix of a [M, Ip]
 };
 
 struct BwdWs {
@@ -62,6 +68,8 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     w.wrow = cv.take<float>(M);
     w.o = cv.take<float>(M * c.H);
     w.router = cv.take<char>((int64_t)router_ws_bytes_fwd(c.T, c.E, c.H));
+    w.xmx = cv.take<uint8_t>(mx_bytes(c.T, c.H));
+    w.amx = cv.take<uint8_t>(mx_bytes(M, c.I));
     if (bytes) *bytes = cv.used;
     return w;
 }
@@ -400,10 +408,23 @@ static moe_gemm_args saved_gemm_args(const moe_saved *saved)
 // (GEMM2 + combine; w2).  The backward runs stage 2 first (dW2), then stage 1
 // (dW1, router).  moe_forward / moe_backward are these stages back to back.
 
-moe_status moe_stage1_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
-                              const float *bias, const uint16_t *w1, float *aux,
-                              const moe_saved *saved, void *ws, size_t ws_bytes,
-                              hipStream_t stream)
+// The forward stages in bf16 (w1 / w2) or MXFP8 (w1_mx / w2_mx: MX matrices
+// of w1 as [E*2I, H] and w2 as [E*H, I]); exactly one of each pair is given.
+static void set_mx(GemmArgs &g, const moe_config &c, const FwdWs &w)
+{
+    const int64_t M = c.T * c.k;
+    g.Hp = mx_kp(c.H);
+    g.Ip = mx_kp(c.I);
+    g.xq = w.xmx;
+    g.xs = w.xmx + c.T * g.Hp;
+    g.aq = w.amx;
+    g.as_ = w.amx + M * g.Ip;
+}
+
+static moe_status stage1_fwd(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                             const float *bias, const uint16_t *w1, const uint8_t *w1_mx,
+                             float *aux, const moe_saved *saved, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
@@ -419,7 +440,7 @@ moe_status moe_stage1_forward(const moe_config *cfg, const uint16_t *x, const fl
         return MOE_OK;
     }
     MOE_CHECK(check_saved(saved));
-    MOE_CHECK(check_ptrs({x, w1}));
+    MOE_CHECK(check_ptrs({x, w1_mx ? (const void *)w1_mx : (const void *)w1}));
     MOE_CHECK(moe_router(cfg, x, Wr, bias, saved->logits, nullptr, saved->topk_idx,
                          saved->topk_w, saved->counts, aux, ws, ws_bytes, stream));
     {
@@ -432,12 +453,25 @@ moe_status moe_stage1_forward(const moe_config *cfg, const uint16_t *x, const fl
     a.x = x;
     a.w1 = w1;
     GemmArgs g = gemm_args(c, a, w.sched);
-    MOE_TRY(run_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
+    if (!w1_mx) {
+        MOE_TRY(run_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
+        return MOE_OK;
+    }
+    set_mx(g, c, w);
+    g.w1q = w1_mx;
+    g.w1s = w1_mx + (int64_t)c.E * 2 * c.I * g.Hp;
+    {
+        StageMark mark(MOE_STAGE_MX_QUANT, stream);
+        MOE_TRY(launch_mx_quantize(x, c.T, c.H, w.xmx, stream));
+    }
+    StageMark mark(MOE_GEMM_UP_SWIGLU, stream);
+    MOE_TRY(launch_mx_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
     return MOE_OK;
 }
 
-moe_status moe_stage2_forward(const moe_config *cfg, const uint16_t *w2, const moe_saved *saved,
-                              float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const uint8_t *w2_mx,
+                             const moe_saved *saved, float *y, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
@@ -447,16 +481,38 @@ moe_status moe_stage2_forward(const moe_config *cfg, const uint16_t *w2, const m
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     if (c.T == 0) return MOE_OK;
     MOE_CHECK(check_saved(saved));
-    MOE_CHECK(check_ptrs({w2, y}));
+    MOE_CHECK(check_ptrs({w2_mx ? (const void *)w2_mx : (const void *)w2, y}));
     MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
     moe_gemm_args a = saved_gemm_args(saved);
     a.w2 = w2;
     a.o = w.o;
     GemmArgs g = gemm_args(c, a, w.sched);
-    MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));
+    if (!w2_mx) {
+        MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));
+    } else {
+        set_mx(g, c, w);
+        g.w2q = w2_mx;
+        g.w2s = w2_mx + (int64_t)c.E * c.H * g.Ip;
+        StageMark mark(MOE_GEMM_DOWN, stream);
+        MOE_TRY(launch_mx_gemm(MOE_GEMM_DOWN, g, stream));
+    }
     StageMark mark(MOE_STAGE_COMBINE, stream);
     MOE_TRY(launch_combine(c.T, c.k, c.H, w.o, saved->topk_w, saved->pos, y, stream));
     return MOE_OK;
+}
+
+moe_status moe_stage1_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                              const float *bias, const uint16_t *w1, float *aux,
+                              const moe_saved *saved, void *ws, size_t ws_bytes,
+                              hipStream_t stream)
+{
+    return stage1_fwd(cfg, x, Wr, bias, w1, nullptr, aux, saved, ws, ws_bytes, stream);
+}
+
+moe_status moe_stage2_forward(const moe_config *cfg, const uint16_t *w2, const moe_saved *saved,
+                              float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return stage2_fwd(cfg, w2, nullptr, saved, y, ws, ws_bytes, stream);
 }
 
 moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr,
@@ -468,6 +524,102 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
     if (cfg->T > 0) MOE_CHECK(check_ptrs({w2, y}));
     MOE_CHECK(moe_stage1_forward(cfg, x, Wr, bias, w1, aux, saved, ws, ws_bytes, stream));
     return moe_stage2_forward(cfg, w2, saved, y, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- MXFP8 ----
+
+moe_status moe_mx_size(int64_t rows, int64_t K, size_t *bytes)
+{
+    if (!bytes || rows < 0 || K <= 0 || K % 32 != 0) return MOE_EINVAL;
+    *bytes = (size_t)mx_bytes(rows, K);
+    return MOE_OK;
+}
+
+moe_status moe_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, void *dst,
+                           size_t dst_bytes, hipStream_t stream)
+{
+    size_t need = 0;
+    MOE_CHECK(moe_mx_size(rows, K, &need));
+    if (rows == 0) return MOE_OK;
+    MOE_CHECK(check_ptrs({src, dst}));
+    if (dst_bytes < need) return MOE_EINVAL;
+    StageMark mark(MOE_STAGE_MX_QUANT, stream);
+    MOE_TRY(launch_mx_quantize(src, rows, K, (uint8_t *)dst, stream));
+    return MOE_OK;
+}
+
+moe_status moe_grouped_gemm_mx(int32_t op, const moe_config *cfg, const moe_gemm_mx_args *args,
+                               void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    if (!args) return MOE_EINVAL;
+    const moe_config &c = *cfg;
+    const moe_gemm_mx_args &a = *args;
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    MOE_CHECK(check_ptrs({a.counts, a.offsets}));
+    if (op == MOE_GEMM_UP_SWIGLU) {
+        MOE_CHECK(check_ptrs({a.x_mx, a.w1_mx, a.a_mx, a.row_map, a.a}));
+        MOE_CHECK(check_opt_ptr(a.h));
+    } else if (op == MOE_GEMM_DOWN) {
+        MOE_CHECK(check_ptrs({a.a_mx, a.w2_mx, a.o}));
+    } else {
+        return MOE_EINVAL;
+    }
+    if (c.T == 0) return MOE_OK;
+    MOE_TRY(launch_schedule(c.E, a.counts, w.sched, stream));
+    moe_gemm_args b;
+    memset(&b, 0, sizeof b);
+    b.counts = a.counts;
+    b.offsets = a.offsets;
+    b.row_map = a.row_map;
+    b.h = a.h;
+    b.a = a.a;
+    b.o = a.o;
+    GemmArgs g = gemm_args(c, b, w.sched);
+    const int64_t M = c.T * c.k;
+    g.Hp = mx_kp(c.H);
+    g.Ip = mx_kp(c.I);
+    g.xq = (const uint8_t *)a.x_mx;
+    g.xs = g.xq ? g.xq + c.T * g.Hp : nullptr;
+    g.w1q = (const uint8_t *)a.w1_mx;
+    g.w1s = g.w1q ? g.w1q + (int64_t)c.E * 2 * c.I * g.Hp : nullptr;
+    g.w2q = (const uint8_t *)a.w2_mx;
+    g.w2s = g.w2q ? g.w2q + (int64_t)c.E * c.H * g.Ip : nullptr;
+    g.aq = (uint8_t *)a.a_mx;
+    g.as_ = g.aq + M * g.Ip;
+    StageMark mark(op, stream);
+    MOE_TRY(launch_mx_gemm(op, g, stream));
+    return MOE_OK;
+}
+
+moe_status moe_stage1_forward_mx(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                                 const float *bias, const void *w1_mx, float *aux,
+                                 const moe_saved *saved, void *ws, size_t ws_bytes,
+                                 hipStream_t stream)
+{
+    if (!w1_mx) return MOE_EINVAL;
+    return stage1_fwd(cfg, x, Wr, bias, nullptr, (const uint8_t *)w1_mx, aux, saved, ws, ws_bytes,
+                      stream);
+}
+
+moe_status moe_stage2_forward_mx(const moe_config *cfg, const void *w2_mx, const moe_saved *saved,
+                                 float *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!w2_mx) return MOE_EINVAL;
+    return stage2_fwd(cfg, nullptr, (const uint8_t *)w2_mx, saved, y, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_mx(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                          const float *bias, const void *w1_mx, const void *w2_mx, float *y,
+                          float *aux, const moe_saved *saved, void *ws, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    if (cfg->T > 0) MOE_CHECK(check_ptrs({w2_mx, y}));
+    MOE_CHECK(moe_stage1_forward_mx(cfg, x, Wr, bias, w1_mx, aux, saved, ws, ws_bytes, stream));
+    return moe_stage2_forward_mx(cfg, w2_mx, saved, y, ws, ws_bytes, stream);
 }
 
 moe_status moe_stage2_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,

@@ -127,9 +127,21 @@ struct GemmArgs {
     void *dW1, *dW2;
     int32_t dw_bf16, dw_acc;
     Sched sched;
+    // MXFP8 forward: MX matrices (codes, scales; layout in mxfmt.h) of x
+    // [T, Hp], w1 [E*2I, Hp], w2 [E*H, Ip] and a [M, Ip]; Hp, Ip = H, I
+    // rounded up to 128
+    const uint8_t *xq, *xs, *w1q, *w1s, *w2q, *w2s;
+    uint8_t *aq, *as_;
+    int64_t Hp, Ip;
 };
 int32_t dgrad2_cols(int32_t I);
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
+// MXFP8: quantise a bf16 matrix [rows, K] (K % 32 == 0) into the MX matrix at
+// dst (codes [rows, Kp] then scales [rows, Kp/32]); the forward GEMMs on MX
+// operands (op MOE_GEMM_UP_SWIGLU or MOE_GEMM_DOWN)
+hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint8_t *dst,
+                              hipStream_t s);
+hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
 // zero the weight gradient of every expert without rows (overwrite mode)
 hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *counts, void *dW,
                              int32_t bf16, hipStream_t s);

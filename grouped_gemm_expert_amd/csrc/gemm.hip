@@ -22,49 +22,16 @@
 // (accumulate).  Block
 // indices are remapped so that each of the 8 XCDs works on a contiguous run
 // of tiles (neighbouring tiles share operand panels in that XCD's L2).
-#include "tile.h"
+#include "swiglu_epi.h"
 
 namespace moe {
-
-
-struct MTile {
-    int e;
-    int64_t m0, seg_end;
-    int nt;
-};
-
-// M-grouped tile L: groups of GM m-tiles sweep all n-tiles before moving on.
-template <int BM>
-MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offsets, int E,
-                          int nN, MTile &t)
-{
-    constexpr int GM = 4;
-    const int64_t total_mt = mt_off[E];
-    const int64_t total = total_mt * nN;
-    int64_t L = xcd_remap(b, total);
-    if (L < 0) return false;
-    int64_t grp = L / ((int64_t)GM * nN);
-    int64_t first = grp * GM;
-    int64_t gm = total_mt - first < GM ? total_mt - first : GM;
-    int64_t in = L - grp * (int64_t)GM * nN;
-    int64_t mt = first + in % gm;
-    t.nt = (int)(in / gm);
-    int lo = 0, hi = E;  // largest e with mt_off[e] <= mt
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (mt_off[mid] <= mt) lo = mid; else hi = mid;
-    }
-    t.e = lo;
-    t.m0 = offsets[lo] + (mt - mt_off[lo]) * BM;
-    t.seg_end = offsets[lo + 1];
-    return true;
-}
 
 int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
 {
     int64_t mt = M / BM + (M < E ? M : E) + 1;
     return grid_for(mt * nN);
 }
+
 
 // =========================================================================
 // GEMM1 + SwiGLU:  h[r, n] = x[tok(r)] . w1[e, n, :],  a = silu(g) * u
@@ -106,57 +73,7 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
     Acc<C> acc;
     mainloop<C, false, false, false>(lds, H, la, lb, acc);
 
-    // SwiGLU on the fp32 accumulators, then out through LDS: staging row r
-    // holds the tile's 128 gate | 128 up | 128 a values of that row as bf16
-    // (48 chunks of 16 bytes, XOR-swizzled by row), and lane l < 48 writes
-    // chunk l of a row to h (gate, up) or a with one 16-byte store.
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    constexpr int HF = C::FN / 2;
-    constexpr int GCOLS = C::BN / 2;  // gate columns of the tile
-    static_assert(3 * GCOLS == 48 * 8, "staging row = 48 chunks");
-    auto soff = [](int r, int chunk) { return r * (3 * GCOLS * 2) + ((chunk ^ (r & 15)) << 4); };
-#pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
-        if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            if ((wm * C::WM + i * 32) / EPI_ROWS != half) continue;
-            const int r = acc_row<C>(wm, i, lane) - half * EPI_ROWS;
-#pragma unroll
-            for (int j = 0; j < HF; ++j)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    // gate column (tile-local) of wave column wn starts at wn*WN/2
-                    const int gc = wn * (C::WN / 2) + j * 32 + rg * 8 + (lane >> 5) * 4;
-                    float gv[4], uv[4], av[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        gv[q] = acc.v[i][j][rg * 4 + q];
-                        uv[q] = acc.v[i][j + HF][rg * 4 + q];
-                        av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
-                    }
-                    const int sub = (lane >> 5) << 3;  // byte offset inside the 16-byte chunk
-                    *(lds_u64 *)(lds + soff(r, gc >> 3) + sub) = pack_bf4(gv[0], gv[1], gv[2], gv[3]);
-                    *(lds_u64 *)(lds + soff(r, 16 + (gc >> 3)) + sub) = pack_bf4(uv[0], uv[1], uv[2], uv[3]);
-                    *(lds_u64 *)(lds + soff(r, 32 + (gc >> 3)) + sub) = pack_bf4(av[0], av[1], av[2], av[3]);
-                }
-        }
-        __syncthreads();
-        const int seg = lane >> 4;                     // 0 gate, 1 up, 2 a
-        const int64_t col = i0 + 8 * (lane & 15);      // column within I
-        const bool live = lane < 48 && col < I && (seg == 2 || g.h != nullptr);
-        for (int r = wave; r < EPI_ROWS; r += C::NT / 64) {
-            const int64_t m = t.m0 + half * EPI_ROWS + r;
-            if (m >= t.seg_end) break;
-            if (live) {
-                const u32x4_t v = *(const lds_u32x4 *)(lds + soff(r, lane));
-                uint16_t *dst = seg == 2 ? g.a + m * I + col : g.h + m * 2 * I + (seg ? I : 0) + col;
-                *(u32x4_t *)dst = v;
-            }
-        }
-        __syncthreads();
-    }
+    swiglu_epilogue<C, false>(acc, lds, t, i0, I, g.h, g.a, nullptr, nullptr, 0);
 }
 
 // =========================================================================

@@ -1,0 +1,367 @@
+// MXFP8 expert GEMMs on gfx950 block-scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, one E8M0 scale per
+// 32-deep block of each row and column, fp32 accumulation), and the
+// quantiser that produces their MX operands.  (MegaMoE page, "Expert
+// precision": the mxfp8 mode runs the expert stages in MXFP8 while the
+// parameters stay bf16 and their quantised copies are cached.)
+//
+// Forward kernels:
+//   k_up_swiglu_mx  h = X . W1[e]^T from the MX forms of x (token rows,
+//                   gathered through row_map) and w1; SwiGLU from the fp32
+//                   accumulators; writes h and a (bf16) and a's MX form.
+//   k_down_mx       o = A . W2[e]^T from the MX forms of a and w2 (fp32 out).
+// Both operands are K-major, so the tiles reuse the bf16 kernels' [rows][128 B]
+// swizzled LDS layout and direct global->LDS copies: a 128-byte row slice is
+// 128 fp8 of k here (one scale group, two MFMA k-steps) instead of 64 bf16.
+// The block scales of a stage (4 bytes per row, for 256 A rows and 256 B
+// rows) travel through LDS too, as 4-byte-per-lane copies in which lanes
+// 0..31 copy 32 A rows and lanes 32..63 the matching 32 B rows.
+//
+// MFMA operand layout (32x32x64, 32 bytes per lane): lane half g of
+// row r holds, for k-step s of a stage, bytes [64 s + 16 g, +16) (block 2s)
+// and [64 s + 32 + 16 g, +16) (block 2s+1) of the row's stage slice, and
+// supplies the scale of block 2s + g; the instruction applies the scale given
+// by half b to the bytes of block 2s + b in both halves.  With the scales of
+// a group stored as blocks 0, 2, 1, 3, half g reads the 16-bit word at byte
+// 2g of the row's 4 scale bytes: low byte for step 0, high byte for step 1
+// (selected by the instruction's op_sel).
+#include "swiglu_epi.h"
+
+namespace moe {
+
+typedef int v8i32_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// ------------------------------------------------------------ quantiser ----
+// Row-wise MX quantisation of a bf16 matrix src [rows, K] (K % 32 == 0) into
+// codes [rows, Kp] and scales [rows, Kp/32] (layout in mxfmt.h).  Sixteen
+// lanes take one 128-column group of a row, 8 columns each.
+__global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *src, int64_t rows, int64_t K,
+                                                     int64_t Kp, uint8_t *codes, uint8_t *scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t gpr = Kp / MX_GROUP;
+    const int64_t grp = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+    const bool valid = grp < rows * gpr;
+    const int64_t row = valid ? grp / gpr : 0, j = valid ? grp % gpr : 0;
+    const int64_t col = j * MX_GROUP + (lane & 15) * 8;
+    float v[8];
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (valid && col < K) w = *(const u32x4_t *)(src + row * K + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf2f((uint16_t)(w[q] & 0xffffu));
+        v[2 * q + 1] = bf2f((uint16_t)(w[q] >> 16));
+    }
+    uint32_t sc;
+    const uint64_t c = mx_quant8(v, sc);
+    const uint32_t word = mx_group_word(sc, lane);
+    if (valid) {
+        *(uint64_t *)(codes + row * Kp + col) = c;
+        if ((lane & 15) == 0) *(uint32_t *)(scales + row * (Kp / 32) + j * 4) = word;
+    }
+}
+
+hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint8_t *dst,
+                              hipStream_t s)
+{
+    if (rows <= 0) return hipSuccess;
+    const int64_t Kp = mx_kp(K);
+    const int64_t groups = rows * (Kp / MX_GROUP);
+    hipLaunchKernelGGL(k_mx_quantize, dim3((unsigned)ceil_div(groups, 16)), dim3(256), 0, s, src,
+                       rows, K, Kp, dst, dst + rows * Kp);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- tiles ----
+// BM x BN output tile of waves WM x WN; per stage 128 fp8 of k: A and B tiles
+// of 128 bytes a row (as the bf16 tiles) plus the stage's scales, a 256-byte
+// block per 32 rows (A rows 32q .. 32q+31 in its first half, the same B rows
+// in its second).  Two stage buffers of each.
+template <int BM_, int BN_, int WM_, int WN_>
+struct MxCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+    static constexpr int NT = WAVES_M * WAVES_N * 64;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128, S_BYTES = BM / 32 * 256;
+    static constexpr int NS = BM / 32 / (NT / 64);  // scale blocks each wave copies
+    static constexpr int RING_BYTES = 2 * (A_BYTES + B_BYTES + S_BYTES);
+    static constexpr int LDS_BYTES = RING_BYTES > 131072 ? RING_BYTES : 131072;
+    static_assert(BM == BN && NS * (NT / 64) * 32 == BM, "scale blocks split evenly over the waves");
+    static_assert(LDS_BYTES <= 163840, "LDS of one CU");
+};
+// Eight waves of 128 x 64 (two a SIMD, 256 registers each): 128 accumulator
+// registers and one in-place set of six 32-byte fragments.
+using MxTile = MxCfg<256, 256, 128, 64>;
+
+// 4 bytes per lane from a per-lane global address into LDS: lane l writes
+// bytes [4 l, 4 l + 4) of the 256-byte block at dst (address in M0).  Issued
+// from inline assembly for the same reason as copy16_to_lds.
+MOE_DEV void copy4_to_lds(const void *src, lds_t *dst)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(m0v)
+                 : "memory", "m0");
+}
+
+// The fragments of one k-step: one register set, refilled in place.
+template <class C>
+struct MxFrags {
+    v8i32_t a[C::FM], b[C::FN];
+    int32_t sa[C::FM], sb[C::FN];
+};
+
+// Operand fragment of rows rbase + lane%32 for k-step kk (0 or 1) of a stage.
+MOE_DEV v8i32_t frag_mx(const lds_t *T, int rbase, int kk, int lane)
+{
+    const int r = rbase + (lane & 31), g = lane >> 5;
+    const u32x4_t lo = *(const lds_u32x4 *)(T + lds_off(r, 4 * kk + g));
+    const u32x4_t hi = *(const lds_u32x4 *)(T + lds_off(r, 4 * kk + 2 + g));
+    const v8i32_t v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return v;
+}
+
+// Scale word of rows rbase + lane%32 for this lane's half (side 0: A, 1: B).
+MOE_DEV int32_t scale_mx(const lds_t *S, int rbase, int side, int lane)
+{
+    const int r = rbase + (lane & 31);
+    return (int32_t) * (const lds_u16 *)(S + (r >> 5) * 256 + side * 128 + (r & 31) * 4 +
+                                         (lane >> 5) * 2);
+}
+
+// Refill A fragment i / B fragment j with k-step kk of the given buffers; the
+// scales change once per stage, so only step 0 reads them.
+template <class C>
+MOE_DEV void read_a_mx(int i, const lds_t *As, const lds_t *Ss, int kk, MxFrags<C> &f, int wm,
+                       int lane)
+{
+    const int rb = wm * C::WM + i * 32;
+    f.a[i] = frag_mx(As, rb, kk, lane);
+    if (kk == 0) f.sa[i] = scale_mx(Ss, rb, 0, lane);
+}
+template <class C>
+MOE_DEV void read_b_mx(int j, const lds_t *Bs, const lds_t *Ss, int kk, MxFrags<C> &f, int wn,
+                       int lane)
+{
+    const int rb = wn * C::WN + j * 32;
+    f.b[j] = frag_mx(Bs, rb, kk, lane);
+    if (kk == 0) f.sb[j] = scale_mx(Ss, rb, 1, lane);
+}
+
+// The MFMAs of one k-step (scale byte OPSEL) in j-major order: MFMA n is
+// (i, j) = (n % FM, n / FM).  Right after the last MFMA that uses a fragment
+// the wave refills its registers with k-step kk_next from the given buffers
+// (B fragment j after MFMA FM*j + FM-1, A fragment i after the last column's
+// MFMA), so one register set serves both steps and every refill still has
+// at least FM-1 MFMAs before its first use.  The NC copies are spread evenly
+// over the MFMAs; sched_barrier pins the order.
+template <class C, int OPSEL, int NC, class Copy>
+MOE_DEV void kstep_mx(MxFrags<C> &f, const lds_t *As, const lds_t *Bs, const lds_t *Ss, int kk_next,
+                      Copy &&copy, Acc<C> &acc, int wm, int wn, int lane)
+{
+    constexpr int NMF = C::FM * C::FN;
+#pragma unroll
+    for (int n = 0; n < NMF; ++n) {
+        if constexpr (NC > 0) {
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+                if (q * NMF / NC == n) copy(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = n % C::FM, j = n / C::FM;
+        acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.b[j], f.a[i], acc.v[i][j], 0, 0, OPSEL, f.sb[j], OPSEL, f.sa[i]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == C::FM - 1) read_b_mx<C>(j, Bs, Ss, kk_next, f, wn, lane);
+        if (j == C::FN - 1) read_a_mx<C>(i, As, Ss, kk_next, f, wm, lane);
+    }
+}
+
+// Software pipeline over stages 0 .. nst-1 (128 k each), two buffers per
+// operand.  Stage v: step 0's MFMAs run while step 1's fragments are read
+// (all of them before the step ends); then each wave waits for its copies of
+// stage v+1, the barrier publishes them and frees stage v's buffers, and step
+// 1's MFMAs run while step 0 of stage v+1 is read and stage v+2 is copied
+// into the freed buffers (past the
+// end the last stage again, into buffers nothing reads).  copy_a(q, v, As) /
+// copy_b(q, v, Bs) issue data copy q of stage v, copy_s(q, v, Ss) scale copy q.
+template <class C, int NCA, int NCB, class CopyA, class CopyB, class CopyS>
+MOE_DEV void mx_pipeline(lds_t *lds, int nst, CopyA &&copy_a, CopyB &&copy_b, CopyS &&copy_s,
+                         Acc<C> &acc)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    lds_t *As[2] = {lds, lds + C::A_BYTES};
+    lds_t *Bs[2] = {lds + 2 * C::A_BYTES, lds + 2 * C::A_BYTES + C::B_BYTES};
+    lds_t *Ss[2] = {lds + 2 * (C::A_BYTES + C::B_BYTES),
+                    lds + 2 * (C::A_BYTES + C::B_BYTES) + C::S_BYTES};
+    acc.zero();
+    if (nst <= 0) return;
+    constexpr int NC = NCA + NCB + C::NS;
+    auto clampv = [&](int v) { return v < nst ? v : nst - 1; };
+    auto issue = [&](int q, int v, int b) {
+        if (q < NCA) copy_a(q, v, As[b]);
+        else if (q < NCA + NCB) copy_b(q - NCA, v, Bs[b]);
+        else copy_s(q - NCA - NCB, v, Ss[b]);
+    };
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int q = 0; q < NC; ++q) issue(q, clampv(s), s);
+    wait_copies_le<NC>();
+    __syncthreads();
+    MxFrags<C> f;
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) read_b_mx<C>(j, Bs[0], Ss[0], 0, f, wn, lane);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) read_a_mx<C>(i, As[0], Ss[0], 0, f, wm, lane);
+    auto stage = [&](auto tag, int v) {
+        constexpr int I = decltype(tag)::value;
+        constexpr int b = I % 2, bn = (I + 1) % 2;
+        kstep_mx<C, 0, 0>(f, As[b], Bs[b], Ss[b], 1, [](int) {}, acc, wm, wn, lane);
+        wait_copies();  // stage v+1 (the only copies in flight)
+        __syncthreads();
+        const int vc = clampv(v + 2);
+        kstep_mx<C, 1, NC>(f, As[bn], Bs[bn], Ss[bn], 0, [&](int q) { issue(q, vc, b); }, acc,
+                           wm, wn, lane);
+    };
+    int v = 0;
+    for (; v + 2 <= nst; v += 2) stage_run(stage, v, nst, std::make_integer_sequence<int, 2>());
+    stage_run(stage, v, nst, std::make_integer_sequence<int, 1>());
+    wait_copies();
+    __syncthreads();
+}
+
+// Tile-local row of scale copy q of a wave: block wave*NS + q, lanes 0..31
+// copy its A rows, lanes 32..63 its B rows.
+template <class C>
+MOE_DEV int scale_row(int wave, int q, int lane) { return (wave * C::NS + q) * 32 + (lane & 31); }
+
+// =========================================================================
+// GEMM1 (MXFP8) + SwiGLU
+// =========================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_up_swiglu_mx(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
+    const int I = g.I;
+    const int64_t Hp = g.Hp;
+    const int nN = (int)ceil_div(I, C::BN / 2);
+    MTile t;
+    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    const int lane0 = threadIdx.x & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(g.xq, wave0);
+    lb.init(g.w1q + (int64_t)t.e * 2 * I * Hp, wave0);
+    const int64_t i0 = (int64_t)t.nt * (C::BN / 2);
+    auto tok_of = [&](int rr) {
+        int64_t m = t.m0 + rr;
+        if (m >= t.seg_end) m = t.seg_end - 1;
+        return (int64_t)(g.row_map[m] / g.k);
+    };
+    // B tile row -> w1 row: wave column wn takes gate rows i0 + wn*WN/2 + [0, WN/2)
+    // then the matching up rows
+    auto w1_row = [&](int rr) {
+        const int wn = rr / C::WN, qq = rr % C::WN, half = C::WN / 2;
+        int64_t i = i0 + wn * half + (qq < half ? qq : qq - half);
+        if (i >= I) i = I - 1;
+        return qq < half ? i : I + i;
+    };
+#pragma unroll
+    for (int q = 0; q < la.NI; ++q) la.set(q, lane0, (uint32_t)(tok_of(la.row(q, lane0)) * Hp));
+#pragma unroll
+    for (int q = 0; q < lb.NI; ++q) lb.set(q, lane0, (uint32_t)(w1_row(lb.row(q, lane0)) * Hp));
+    const uint8_t *sp[C::NS];
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const int sr = scale_row<C>(wave0, q, lane0);
+        sp[q] = lane0 < 32 ? g.xs + tok_of(sr) * (Hp / 32)
+                           : g.w1s + ((int64_t)t.e * 2 * I + w1_row(sr)) * (Hp / 32);
+    }
+    Acc<C> acc;
+    mx_pipeline<C, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
+        lds, (int)(Hp / MX_GROUP),
+        [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * 64, 0, la.base); },
+        [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * 64, 0, lb.base); },
+        [&](int q, int s, lds_t *Ss) {
+            copy4_to_lds(sp[q] + 4 * s, Ss + (wave0 * C::NS + q) * 256);
+        },
+        acc);
+    swiglu_epilogue<C, true>(acc, lds, t, i0, I, g.h, g.a, g.aq, g.as_, g.Ip);
+}
+
+// =========================================================================
+// GEMM2 (MXFP8):  o[r, c] = A[r] . W2[e, c, :]   (fp32 out)
+// =========================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_down_mx(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
+    const int H = g.H;
+    const int64_t Ip = g.Ip;
+    const int nN = (int)ceil_div(H, C::BN);
+    MTile t;
+    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    const int lane0 = threadIdx.x & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(g.aq, wave0);
+    lb.init(g.w2q + (int64_t)t.e * H * Ip, wave0);
+    const int64_t n0 = (int64_t)t.nt * C::BN;
+    auto a_row = [&](int rr) {
+        int64_t m = t.m0 + rr;
+        return m < t.seg_end ? m : t.seg_end - 1;
+    };
+    auto w2_row = [&](int rr) {
+        int64_t n = n0 + rr;
+        return n < H ? n : (int64_t)H - 1;
+    };
+#pragma unroll
+    for (int q = 0; q < la.NI; ++q) la.set(q, lane0, (uint32_t)(a_row(la.row(q, lane0)) * Ip));
+#pragma unroll
+    for (int q = 0; q < lb.NI; ++q) lb.set(q, lane0, (uint32_t)(w2_row(lb.row(q, lane0)) * Ip));
+    const uint8_t *sp[C::NS];
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const int sr = scale_row<C>(wave0, q, lane0);
+        sp[q] = lane0 < 32 ? g.as_ + a_row(sr) * (Ip / 32)
+                           : g.w2s + ((int64_t)t.e * H + w2_row(sr)) * (Ip / 32);
+    }
+    Acc<C> acc;
+    mx_pipeline<C, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
+        lds, (int)(Ip / MX_GROUP),
+        [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * 64, 0, la.base); },
+        [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * 64, 0, lb.base); },
+        [&](int q, int s, lds_t *Ss) {
+            copy4_to_lds(sp[q] + 4 * s, Ss + (wave0 * C::NS + q) * 256);
+        },
+        acc);
+    store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
+}
+
+hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
+{
+    using C = MxTile;
+    if (op == MOE_GEMM_UP_SWIGLU) {
+        hipLaunchKernelGGL(k_up_swiglu_mx<C>,
+                           dim3((unsigned)mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2))),
+                           dim3(C::NT), 0, s, g);
+        return hipGetLastError();
+    }
+    if (op == MOE_GEMM_DOWN) {
+        hipLaunchKernelGGL(k_down_mx<C>,
+                           dim3((unsigned)mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN))),
+                           dim3(C::NT), 0, s, g);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -537,4 +537,44 @@ MOE_DEV int64_t xcd_remap(int64_t b, int64_t total)
 
 inline int64_t grid_for(int64_t total) { return ceil_div(total, 8 * XCD_CHUNK) * 8 * XCD_CHUNK; }
 
+// ------------------------------------------------------------ schedule ----
+// Forward and dgrad GEMMs tile the sorted rows of each expert (M-grouped):
+// the per-expert m-tile prefix sums live on the device and surplus blocks of
+// the host-sized grid exit.
+struct MTile {
+    int e;
+    int64_t m0, seg_end;
+    int nt;
+};
+
+// M-grouped tile L: groups of GM m-tiles sweep all n-tiles before moving on.
+template <int BM>
+MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offsets, int E,
+                          int nN, MTile &t)
+{
+    constexpr int GM = 4;
+    const int64_t total_mt = mt_off[E];
+    const int64_t total = total_mt * nN;
+    int64_t L = xcd_remap(b, total);
+    if (L < 0) return false;
+    int64_t grp = L / ((int64_t)GM * nN);
+    int64_t first = grp * GM;
+    int64_t gm = total_mt - first < GM ? total_mt - first : GM;
+    int64_t in = L - grp * (int64_t)GM * nN;
+    int64_t mt = first + in % gm;
+    t.nt = (int)(in / gm);
+    int lo = 0, hi = E;  // largest e with mt_off[e] <= mt
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (mt_off[mid] <= mt) lo = mid; else hi = mid;
+    }
+    t.e = lo;
+    t.m0 = offsets[lo] + (mt - mt_off[lo]) * BM;
+    t.seg_end = offsets[lo + 1];
+    return true;
+}
+
+// Upper bound on the blocks an M-grouped launch needs (host side).
+int64_t mgrid_blocks(int64_t M, int E, int BM, int nN);
+
 }  // namespace moe

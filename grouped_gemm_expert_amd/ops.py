@@ -47,6 +47,11 @@ class MoeGemmArgs(ctypes.Structure):
                                              ("dw_accumulate", ctypes.c_int32)]
 
 
+class MoeGemmMxArgs(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x_mx", "w1_mx", "w2_mx", "a_mx", "counts", "offsets",
+                                  "row_map", "h", "a", "o")]
+
+
 class MoeError(RuntimeError):
     pass
 
@@ -96,6 +101,19 @@ def _load():
     lib.moe_stage1_backward.restype = S
     lib.moe_set_stage_events.argtypes = [ctypes.c_int32, _P, _P]
     lib.moe_set_stage_events.restype = S
+    lib.moe_grouped_gemm_mx.argtypes = [ctypes.c_int32, CFG, ctypes.POINTER(MoeGemmMxArgs), _P,
+                                         sz, _P]
+    lib.moe_grouped_gemm_mx.restype = S
+    lib.moe_mx_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(sz)]
+    lib.moe_mx_size.restype = S
+    lib.moe_mx_quantize.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, _P, sz, _P]
+    lib.moe_mx_quantize.restype = S
+    lib.moe_stage1_forward_mx.argtypes = [CFG] + [_P] * 5 + [SP, _P, sz, _P]
+    lib.moe_stage1_forward_mx.restype = S
+    lib.moe_stage2_forward_mx.argtypes = [CFG, _P, SP, _P, _P, sz, _P]
+    lib.moe_stage2_forward_mx.restype = S
+    lib.moe_forward_mx.argtypes = [CFG] + [_P] * 7 + [SP, _P, sz, _P]
+    lib.moe_forward_mx.restype = S
     return lib
 
 
@@ -105,11 +123,12 @@ SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspac
            "moe_dw_part_cols", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_swiglu",
            "moe_combine", "moe_forward", "moe_backward", "moe_stage1_forward",
            "moe_stage2_forward", "moe_stage2_backward", "moe_stage1_backward",
-           "moe_set_stage_events")
+           "moe_set_stage_events", "moe_grouped_gemm_mx", "moe_mx_size", "moe_mx_quantize", "moe_stage1_forward_mx",
+           "moe_stage2_forward_mx", "moe_forward_mx")
 
 STAGES = {"up_swiglu": 0, "down": 1, "down_dgrad": 2, "up_dgrad": 3, "down_wgrad": 4,
           "up_wgrad": 5, "router_proj": 6, "router": 7, "permute": 8, "combine": 9,
-          "router_bwd": 10, "unpermute": 11, "router_grads": 12}
+          "router_bwd": 10, "unpermute": 11, "router_grads": 12, "mx_quant": 13}
 
 
 def moe_set_stage_events(stage: int, start, stop):
@@ -288,3 +307,105 @@ def moe_stage1_backward(cfg, saved: dict, x, Wr, w1, d_aux, dx, dlogits, dWr, dW
                                     _ptr(w1), _ptr(d_aux), _ptr(dx), _ptr(dlogits), _ptr(dWr),
                                     _ptr(dW1), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
                                     ws.numel(), _stream(stream)), "moe_stage1_backward")
+
+
+# ------------------------------------------------------------------ MXFP8 ----
+
+def mx_kp(K: int) -> int:
+    """K rounded up to the 128-column groups of an MX matrix."""
+    return (K + 127) // 128 * 128
+
+
+def moe_mx_size(rows: int, K: int) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.moe_mx_size(int(rows), int(K), ctypes.byref(b)), "moe_mx_size")
+    return int(b.value)
+
+
+def mx_alloc(rows: int, K: int, device="cuda") -> torch.Tensor:
+    """An uninitialised MX-matrix buffer for a [rows, K] matrix (uint8)."""
+    return torch.empty(max(moe_mx_size(rows, K), 1), dtype=torch.uint8, device=device)
+
+
+def mx_views(buf: torch.Tensor, rows: int, K: int):
+    """(codes [rows, Kp], scales [rows, Kp/32]) views of an MX-matrix buffer;
+    the scales of each 128-column group are in block order 0, 2, 1, 3."""
+    Kp = mx_kp(K)
+    codes = buf[:rows * Kp].view(rows, Kp)
+    scales = buf[rows * Kp:rows * Kp + rows * Kp // 32].view(rows, Kp // 32)
+    return codes, scales
+
+
+def moe_mx_quantize(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """MX matrix of a bf16 matrix src [rows, K] (any leading shape is flattened
+    into rows) into dst (uint8, moe_mx_size bytes)."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    _check(_lib.moe_mx_quantize(_ptr(src), rows, K, _ptr(dst), dst.numel(), _stream(stream)),
+           "moe_mx_quantize")
+
+
+class MxWeightCache:
+    """The MXFP8 forms of w1 and w2, rebuilt when either weight changes.
+
+    The key is each weight's storage, shape and in-place version counter; as
+    with the pages' cache, that is not enough when an optimizer writes the
+    weights without bumping the version, so `drop()` (once per optimizer step)
+    forces the next `get` to quantise again."""
+
+    def __init__(self):
+        self._key = None
+        self.w1_mx = None
+        self.w2_mx = None
+        self.builds = 0
+
+    @staticmethod
+    def _k(w):
+        return (w.data_ptr(), tuple(w.shape), w._version)
+
+    def drop(self):
+        self._key = None
+
+    def get(self, w1: torch.Tensor, w2: torch.Tensor, stream=None):
+        key = (self._k(w1), self._k(w2))
+        if key != self._key:
+            E, twoI, H = w1.shape
+            I = w2.shape[2]
+            if self.w1_mx is None or self.w1_mx.numel() != moe_mx_size(E * twoI, H):
+                self.w1_mx = mx_alloc(E * twoI, H, w1.device)
+            if self.w2_mx is None or self.w2_mx.numel() != moe_mx_size(E * H, I):
+                self.w2_mx = mx_alloc(E * H, I, w2.device)
+            moe_mx_quantize(w1, self.w1_mx, stream)
+            moe_mx_quantize(w2, self.w2_mx, stream)
+            self._key = key
+            self.builds += 1
+        return self.w1_mx, self.w2_mx
+
+
+def moe_forward_mx(cfg, x, Wr, bias, w1_mx, w2_mx, y, aux, saved: dict, ws, stream=None):
+    s = _saved_struct(saved)
+    _check(_lib.moe_forward_mx(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias), _ptr(w1_mx),
+                               _ptr(w2_mx), _ptr(y), _ptr(aux), ctypes.byref(s), _ptr(ws),
+                               ws.numel(), _stream(stream)), "moe_forward_mx")
+
+
+def moe_stage1_forward_mx(cfg, x, Wr, bias, w1_mx, aux, saved: dict, ws, stream=None):
+    s = _saved_struct(saved)
+    _check(_lib.moe_stage1_forward_mx(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias),
+                                      _ptr(w1_mx), _ptr(aux), ctypes.byref(s), _ptr(ws),
+                                      ws.numel(), _stream(stream)), "moe_stage1_forward_mx")
+
+
+def moe_stage2_forward_mx(cfg, w2_mx, saved: dict, y, ws, stream=None):
+    s = _saved_struct(saved)
+    _check(_lib.moe_stage2_forward_mx(ctypes.byref(cfg), _ptr(w2_mx), ctypes.byref(s), _ptr(y),
+                                      _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_stage2_forward_mx")
+
+
+def moe_grouped_gemm_mx(op: int, cfg, *, ws, counts, offsets, row_map=None, x_mx=None,
+                        w1_mx=None, w2_mx=None, a_mx=None, h=None, a=None, o=None, stream=None):
+    args = MoeGemmMxArgs(*[_ptr(t) for t in (x_mx, w1_mx, w2_mx, a_mx, counts, offsets, row_map,
+                                              h, a, o)])
+    _check(_lib.moe_grouped_gemm_mx(int(op), ctypes.byref(cfg), ctypes.byref(args), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "moe_grouped_gemm_mx")

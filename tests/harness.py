@@ -22,6 +22,10 @@ SCORE = {"softmax": 0, "sigmoid": 1}
 # error bounds for floating-point outputs (max abs, relative Frobenius)
 FWD_TOL = (2e-2, 1e-2)
 GRAD_TOL = (3e-2, 1.5e-2)
+# the MXFP8 forward against the oracle's MXFP8 forward: both quantise the same
+# bf16 inputs the same way, so only fp32 accumulation and rare one-step code
+# flips of a (from the kernel's fp32 SwiGLU value) separate them
+MX_FWD_TOL = (2e-2, 1e-3)
 
 
 def say(msg: str):

@@ -1,0 +1,172 @@
+"""Parity at the full DeepSeek-V3-style size (T=8192, H=7168, I=2048, E=256 in
+8 groups, top-4 groups, top-8 sigmoid + bias, scale 2.5), in the launch
+configuration the benchmark times: moe_forward from the router weight, then
+moe_backward accumulating into zeroed fp32 weight gradients; and the MXFP8
+forward on the same inputs.  The oracle cannot run the whole layer at this
+size, so it is checked on sampled outputs that it computes one by one:
+  - routing of every token (bit-exact on all tokens whose fp32 selection is
+    not a near-tie under the projection's rounding),
+  - y and dx of sampled tokens, sampled dW1 / dW2 elements of busy experts,
+  - the MX forward's y on sampled tokens against the oracle's MXFP8 forward.
+Only the experts the samples touch are copied to the host: into full-shape
+zero arrays (np.zeros maps untouched pages lazily, so only those experts take
+memory) for the bf16 oracle, which reads no other expert, and into compact
+arrays with remapped expert ids for the MXFP8 oracle, whose quantiser would
+otherwise touch every expert."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from grouped_gemm_expert_amd import inputs
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+N_TOK = 4      # sampled tokens
+N_EL = 12      # sampled dW elements per weight and expert
+
+
+@pytest.fixture(scope="module")
+def ds():
+    from grouped_gemm_expert_amd import ops
+    w = inputs.WORKLOADS["deepseek_v3"]
+    hz.say(f"fullsize: generating {inputs.describe(w)} on the GPU")
+    d = inputs.make_inputs(w, device="cuda", seed=0)
+    cfg = ops.config_from_workload(w)
+    saved = ops.alloc_saved(cfg)
+    y = torch.empty((w.T, w.H), device="cuda")
+    aux = torch.empty((1,), device="cuda")
+    wsf = ops.workspace(cfg, "fwd")
+    wsb = ops.workspace(cfg, "bwd")
+    dx = torch.empty((w.T, w.H), device="cuda")
+    dl = torch.empty((w.T, w.E), device="cuda")
+    dWr = torch.empty((w.E, w.H), device="cuda")
+    dW1 = torch.zeros((w.E, 2 * w.I, w.H), device="cuda")
+    dW2 = torch.zeros((w.E, w.H, w.I), device="cuda")
+    d_aux = torch.ones((1,), device="cuda")
+    hz.say("fullsize: moe_forward + moe_backward")
+    ops.moe_forward(cfg, d["x"], d["Wr"], d["bias"], d["w1"], d["w2"], y, aux, saved, wsf)
+    ops.moe_backward(cfg, saved, d["x"], d["Wr"], d["w1"], d["w2"], d["dy"], d_aux, dx, dl, dWr,
+                     dW1, dW2, wsb, dw_accumulate=True)
+    torch.cuda.synchronize()
+    hz.say("fullsize: oracle logits and routing")
+    X = hz.bits(d["x"])
+    Wr = d["Wr"].cpu().numpy()
+    bias = d["bias"].cpu().numpy()
+    l64 = oracle.logits(X, Wr)
+    r = oracle.route(l64, score=hz.SCORE[w.score], k=w.k, n_groups=w.n_groups,
+                     topk_groups=w.topk_groups, bias=bias, renorm=w.renorm, scale=w.scale,
+                     coeff=w.aux_coeff, route_mode=w.route)
+    idx_gpu = saved["topk_idx"].cpu().numpy()
+    same = (idx_gpu == r["idx"]).all(1)
+    rng = np.random.default_rng(1)
+    toks = np.sort(rng.choice(np.nonzero(same)[0], size=N_TOK, replace=False))
+    return dict(w=w, d=d, cfg=cfg, saved=saved, y=y, aux=aux, dx=dx, dl=dl, dW1=dW1, dW2=dW2,
+                X=X, Wr=Wr, bias=bias, l64=l64, r=r, idx_gpu=idx_gpu, same=same, toks=toks)
+
+
+def _sparse_full(d, experts):
+    """Full-shape host bf16 bits of w1 / w2 holding only the listed experts."""
+    w1 = np.zeros(tuple(d["w1"].shape), np.uint16)
+    w2 = np.zeros(tuple(d["w2"].shape), np.uint16)
+    c1, c2 = _compact(d, experts)
+    w1[np.asarray(experts)] = c1
+    w2[np.asarray(experts)] = c2
+    return w1, w2
+
+
+def _compact(d, experts):
+    """Host bf16 bits of w1 / w2 for the listed experts only."""
+    ex = torch.as_tensor(np.asarray(experts), device="cuda")
+    return hz.bits(d["w1"].index_select(0, ex)), hz.bits(d["w2"].index_select(0, ex))
+
+
+def _remap(idx, experts):
+    m = np.full(int(idx.max()) + 1, -1, np.int32)
+    m[np.asarray(experts)] = np.arange(len(experts), dtype=np.int32)
+    return m[idx]
+
+
+def test_fullsize_routing(ds):
+    w, r = ds["w"], ds["r"]
+    hz.say(f"fullsize routing: identical on {int(ds['same'].sum())} of {w.T} tokens")
+    assert ds["same"].mean() >= 0.99
+    bad = ~ds["same"]
+    if bad.any():   # the rest must be a valid top-k within the projection's error bound
+        eps = hz.projection_error_bound(ds["d"]["x"][torch.as_tensor(np.nonzero(bad)[0], device="cuda")].cpu().float(),
+                                        torch.from_numpy(ds["Wr"]))
+        ok = hz.routing_valid_under_perturbation(w, ds["l64"][bad], ds["bias"], ds["idx_gpu"][bad], eps)
+        assert ok.all()
+    aux_g = float(ds["aux"].cpu())
+    assert abs(aux_g - r["aux"]) <= 1e-3 * abs(r["aux"]) + 1e-9, (aux_g, r["aux"])
+
+
+def test_fullsize_sampled_tokens(ds):
+    w, r, toks = ds["w"], ds["r"], ds["toks"]
+    ex = np.unique(r["idx"][toks])
+    hz.say(f"fullsize tokens {toks.tolist()}: {len(ex)} experts to the host")
+    W1s, W2s = _sparse_full(ds["d"], ex)
+    DY = hz.bits(ds["d"]["dy"])
+    y_ref = oracle.forward(ds["X"], W1s, W2s, r["idx"], r["w"], toks=toks)
+    hz.assert_close("fullsize y", ds["y"][torch.as_tensor(toks, device="cuda")].cpu().numpy(),
+                    y_ref, hz.FWD_TOL)
+    dx_ref, dl_ref = oracle.backward_tokens(ds["X"], ds["Wr"], ds["l64"], W1s, W2s, r["idx"],
+                                            r["counts"], DY, score=hz.SCORE[w.score],
+                                            renorm=w.renorm, scale=w.scale, coeff=w.aux_coeff,
+                                            d_aux=1.0, toks=toks)
+    tk = torch.as_tensor(toks, device="cuda")
+    hz.assert_close("fullsize dx", ds["dx"][tk].cpu().numpy(), dx_ref, hz.GRAD_TOL)
+    hz.assert_close("fullsize dlogits", ds["dl"][tk].cpu().numpy(), dl_ref, hz.GRAD_TOL)
+
+
+def test_fullsize_sampled_weight_grads(ds):
+    w, r = ds["w"], ds["r"]
+    counts = r["counts"]
+    ex = np.argsort(-counts, kind="stable")[:2]          # the two busiest experts
+    hz.say(f"fullsize dW: experts {ex.tolist()} with {counts[ex].tolist()} rows")
+    W1s, W2s = _sparse_full(ds["d"], ex)
+    DY = hz.bits(ds["d"]["dy"])
+    rng = np.random.default_rng(2)
+    which, ee, rr, cc = [], [], [], []
+    for c_e in range(len(ex)):
+        for wh, nr, nc in ((1, 2 * w.I, w.H), (2, w.H, w.I)):
+            which += [wh] * N_EL
+            ee += [int(ex[c_e])] * N_EL
+            rr += rng.integers(0, nr, N_EL).tolist()
+            cc += rng.integers(0, nc, N_EL).tolist()
+    which, ee, rr, cc = (np.array(v, np.int32) for v in (which, ee, rr, cc))
+    ref = oracle.weight_grad_elements(ds["X"], W1s, W2s, r["idx"], r["w"], DY, which, ee, rr, cc)
+    for wh, dW, name in ((1, ds["dW1"], "dW1"), (2, ds["dW2"], "dW2")):
+        sel = which == wh
+        e_, r_, c_ = ee[sel], rr[sel], cc[sel]
+        # indices checked on the host: the gather below does not check them
+        assert (e_ < dW.shape[0]).all() and (r_ < dW.shape[1]).all() and (c_ < dW.shape[2]).all()
+        got = dW[torch.as_tensor(e_, device="cuda"), torch.as_tensor(r_, device="cuda"),
+                 torch.as_tensor(c_, device="cuda")].cpu().numpy()
+        hz.assert_close(f"fullsize {name} elements", got, ref[sel], hz.GRAD_TOL)
+
+
+def test_fullsize_mx_forward_sampled_tokens(ds):
+    from grouped_gemm_expert_amd import ops
+    w, r, toks = ds["w"], ds["r"], ds["toks"]
+    d, cfg = ds["d"], ds["cfg"]
+    hz.say("fullsize mx: quantising the weights")
+    cache = ops.MxWeightCache()
+    w1_mx, w2_mx = cache.get(d["w1"], d["w2"])
+    saved = ops.alloc_saved(cfg)
+    y = torch.empty((w.T, w.H), device="cuda")
+    aux = torch.empty((1,), device="cuda")
+    ws = ops.workspace(cfg, "fwd")
+    hz.say("fullsize mx: moe_forward_mx")
+    ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], w1_mx, w2_mx, y, aux, saved, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(saved["topk_idx"].cpu().numpy(), ds["idx_gpu"])
+    ex = np.unique(r["idx"][toks])
+    W1c, W2c = _compact(d, ex)
+    ops_o = oracle.MxOperands(ds["X"][toks], W1c, W2c)
+    idx_c = _remap(r["idx"][toks], ex)
+    hz.say(f"fullsize mx: oracle on tokens {toks.tolist()}")
+    y_ref = oracle.mx_forward(ops_o, idx_c, r["w"][toks])
+    hz.assert_close("fullsize mx y", y[torch.as_tensor(toks, device="cuda")].cpu().numpy(),
+                    y_ref, hz.MX_FWD_TOL)

@@ -1,0 +1,371 @@
+"""GPU parity of the MXFP8 expert path (page "MegaMoE", "Expert precision":
+the mxfp8 mode runs the expert stages in MXFP8; parameters stay bf16 and their
+quantised copies are cached).
+
+  - moe_mx_quantize against the oracle's quantiser, bit for bit, including the
+    hand-worked golden blocks, subnormal and saturating values, ragged row
+    counts and K not a multiple of the 128-column groups;
+  - moe_forward_mx against the oracle's MXFP8 forward (which quantises x, w1,
+    w2 and a itself from the bf16 inputs);
+  - the two MX stages against the one-call form, and the weight cache.
+
+The block-scaled MFMA forms each E4M3 x E4M3 product (and its scales)
+exactly, adds the products of each group of 8 consecutive k in a fixed-point
+window about 13 bits below the group's largest product (lower bits dropped),
+and adds the group sums in fp32 (measured with in-bounds probes of the
+instruction).  Each group therefore loses less than 7 * 2^-13 of its largest
+product, and an output of the MX GEMMs is within
+    2^-10 * sum |products| + (K/8 + 1) * 2^-24 * sum |products|
+of the exact sum of its MX products, and equal to it when every group's
+products lie within the window -- as they do for the narrow-range operands
+below, where the GEMMs must match the oracle bit for bit.  End to end, the MX
+forward is held to the forward bounds of the bf16 path against its own
+(MXFP8) oracle.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from grouped_gemm_expert_amd import inputs
+from tests import harness as hz
+
+pytestmark = pytest.mark.gpu
+
+MX_TOL = hz.FWD_TOL
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mx_blocks.txt")
+
+
+def _natural_scales(sc: np.ndarray) -> np.ndarray:
+    """Stored scales (blocks 0, 2, 1, 3 of every 128-column group) -> block order."""
+    r, n = sc.shape
+    return sc.reshape(r, n // 4, 4)[:, :, [0, 2, 1, 3]].reshape(r, n)
+
+
+def _gpu_quantize(src_bits: np.ndarray):
+    from grouped_gemm_expert_amd import ops
+    rows, K = src_bits.shape
+    src = torch.from_numpy(src_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    buf = ops.mx_alloc(rows, K)
+    buf.fill_(0xAB)                                   # no byte may survive from before
+    ops.moe_mx_quantize(src, buf)
+    torch.cuda.synchronize()
+    codes, scales = ops.mx_views(buf, rows, K)
+    return codes.cpu().numpy(), _natural_scales(scales.cpu().numpy())
+
+
+def _bf16_bits_of(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits by truncation (input generation: any bf16 will do)."""
+    return (np.ascontiguousarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_rne(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, nearest-even (as the kernels round)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _matrix(kind: str, rows: int, K: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        v = rng.normal(0, 1, (rows, K))
+    elif kind == "weights":
+        v = rng.normal(0, 0.02, (rows, K))
+    elif kind == "wide":
+        # magnitudes spread over 2^-140 .. 2^120 (bf16 subnormals included),
+        # random signs, some exact zeros and whole zero blocks
+        v = np.ldexp(rng.uniform(1, 2, (rows, K)), rng.integers(-140, 121, (rows, K)))
+        v *= rng.choice([-1.0, 1.0], (rows, K))
+        v[rng.random((rows, K)) < 0.05] = 0.0
+        if K >= 64:
+            v[::3, 32:64] = 0.0
+        # blocks whose values span only a few binades, so most elements land in
+        # E4M3's normal, subnormal and saturation ranges rather than rounding to 0
+        v[1::4] = np.ldexp(rng.uniform(1, 2, (len(v[1::4]), K)),
+                           rng.integers(-12, 1, (len(v[1::4]), K))) * rng.choice([-1.0, 1.0], (len(v[1::4]), K))
+    else:
+        raise ValueError(kind)
+    return _bf16_bits_of(v.astype(np.float32))
+
+
+QUANT = [("normal", 37, 96), ("normal", 64, 128), ("weights", 5, 192), ("wide", 130, 384),
+         ("wide", 33, 32), ("normal", 3, 7168), ("weights", 300, 2048)]
+
+
+@pytest.mark.parametrize("kind,rows,K", QUANT)
+def test_mx_quantize_bit_exact(kind, rows, K):
+    hz.say(f"mx quantize {kind} rows={rows} K={K}")
+    src = _matrix(kind, rows, K, seed=rows * 7 + K)
+    codes, scales = _gpu_quantize(src)
+    ref_c, ref_s = oracle.mx_quantize(src)
+    assert np.array_equal(codes[:, :K], ref_c)
+    assert np.array_equal(scales[:, :K // 32], ref_s)
+    # padding up to the 128-column group: zero codes, all-zero blocks (scale code 0)
+    assert not codes[:, K:].any()
+    assert not scales[:, K // 32:].any()
+
+
+def test_mx_quantize_golden_blocks():
+    """The kernel against the hand-worked blocks directly (not via the oracle)."""
+    blocks = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            p = line.split()
+            if p[0] == "block":
+                blocks.append((p[1], int(p[2]), np.zeros(32, np.uint16), np.zeros(32, np.uint8)))
+            else:
+                blocks[-1][2][int(p[0])] = int(p[1], 16)
+                blocks[-1][3][int(p[0])] = int(p[2], 16)
+    hz.say(f"mx golden: {len(blocks)} blocks")
+    src = np.stack([b[2] for b in blocks])
+    codes, scales = _gpu_quantize(src)
+    for i, (name, sc, _, want) in enumerate(blocks):
+        assert scales[i, 0] == sc, name
+        assert np.array_equal(codes[i, :32], want), (name, codes[i, :32], want)
+
+
+# ------------------------------------------------------------ MX GEMMs ----
+
+def _within_mfma_bound(name, got, exact, absum, K, bf16_out=False):
+    """|got - exact| <= 2^-10 sum|p| + (K/8+1) 2^-24 sum|p| (+ bf16 rounding
+    of the output, 2^-9 of it, when the kernel stores bf16)."""
+    acc = 2.0 ** -10 * absum + (K / 8 + 1) * 2.0 ** -24 * absum
+    bound = acc + (2.0 ** -9 * (np.abs(exact) + acc) if bf16_out else 0.0) + 1e-30
+    err = np.abs(np.asarray(got, np.float64) - exact)
+    worst = float((err / bound).max()) if err.size else 0.0
+    mx, fro = hz.errors(got, exact)
+    hz.say(f"{name}: max_abs={mx:.3e} rel_fro={fro:.3e}; worst error / derived bound = {worst:.3f}")
+    assert worst <= 1.0, (name, worst)
+
+
+def _within_swiglu_bound(name, a_bits, g, u, dg, du):
+    """a = silu(g) * u from fp32 accumulators within dg / du of g / u, then
+    rounded to bf16: |silu'| <= 1.1, so |a - a_exact| <= 1.1 dg |u| +
+    |silu(g)| du + dg du + 2^-8 |a| (fp32 evaluation and the bf16 rounding)
+    + 2^-120 |g u| (the fp32 sigmoid is 0 once exp(-g) overflows, g < -88)."""
+    silu = g / (1.0 + np.exp(-np.clip(g, -700, 700)))
+    a_ex = silu * u
+    bound = (1.1 * dg * np.abs(u) + np.abs(silu) * du + dg * du + 2.0 ** -8 * np.abs(a_ex)
+             + 2.0 ** -120 * np.abs(g * u) + 1e-38)
+    a_g = (a_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    worst = float((np.abs(a_g - a_ex) / bound).max()) if a_g.size else 0.0
+    same = float(np.mean(a_bits == _bf16_rne(a_ex.astype(np.float32))))
+    hz.say(f"{name}: bf16 equal to the exact value's rounding {same:.5f}; "
+           f"worst error / derived bound = {worst:.3f}")
+    assert worst <= 1.0, (name, worst)
+    return a_ex
+
+
+def _narrow(rng, shape, jspan=1):
+    """Values exactly representable in MX whose products stay inside the
+    MFMA's window: integers in [-7, 7] with |v| in 4..7 at the head of every
+    32-block (so X = j + 2 - 8 and 7 * 2^6 = 448 is exact), each block times
+    its own 2^j, |j| <= jspan.  bf16 bits."""
+    a = rng.integers(-7, 8, size=shape).astype(np.float64)
+    f = a.reshape(-1, shape[-1] // 32, 32)
+    f[:, :, 0] = rng.choice([-7, -6, -5, -4, 4, 5, 6, 7], size=f.shape[:2])
+    f *= np.ldexp(1.0, rng.integers(-jspan, jspan + 1, size=f.shape[:2]))[:, :, None]
+    return _bf16_bits_of(f.reshape(shape).astype(np.float32))
+
+
+def _random(rng, shape, std):
+    return _bf16_rne(rng.normal(0, std, shape).astype(np.float32))
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _deq(bits2d):
+    c, sc = oracle.mx_quantize(bits2d)
+    return oracle.mx_dequantize(c, sc)
+
+
+MXG_SHAPES = [(300, 384, 320, 8, 3), (97, 128, 64, 4, 2), (513, 256, 192, 16, 4)]
+
+
+@pytest.mark.parametrize("narrow", [True, False], ids=["exact", "bound"])
+@pytest.mark.parametrize("shape", MXG_SHAPES)
+def test_mx_gemm_ops(shape, narrow):
+    from grouped_gemm_expert_amd import ops
+    T, H, I, E, k = shape
+    hz.say(f"mx gemm {'exact' if narrow else 'bound'} T={T} H={H} I={I} E={E} k={k}")
+    rng = np.random.default_rng(T + H)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p[E // 2] = 0.0                                   # one empty expert
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    counts, offsets, row_map, pos = oracle.permute(idx.astype(np.int32), E)
+    M = T * k
+    if narrow:
+        x, w1, w2 = _narrow(rng, (T, H)), _narrow(rng, (E * 2 * I, H)), _narrow(rng, (E * H, I))
+        a_in = _narrow(rng, (M, I))
+    else:
+        x, w1 = _random(rng, (T, H), 1.0), _random(rng, (E * 2 * I, H), 0.05)
+        w2, a_in = _random(rng, (E * H, I), 0.05), _random(rng, (M, I), 0.5)
+    cfg = ops.config(T=T, H=H, I=I, E=E, k=k)
+    ws = ops.workspace(cfg, "fwd")
+    dev = lambda v: torch.from_numpy(v).cuda()
+    mx = {}
+    for name, m, rows, K in (("x", x, T, H), ("w1", w1, E * 2 * I, H), ("w2", w2, E * H, I),
+                             ("a_in", a_in, M, I)):
+        mx[name] = ops.mx_alloc(rows, K)
+        ops.moe_mx_quantize(_dev_bf16(m), mx[name])
+    a_mx = ops.mx_alloc(M, I)
+    h = torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    common = dict(ws=ws, counts=dev(counts), offsets=dev(offsets))
+    ops.moe_grouped_gemm_mx(ops.MOE_GEMM_UP_SWIGLU, cfg, row_map=dev(row_map), x_mx=mx["x"],
+                            w1_mx=mx["w1"], a_mx=a_mx, h=h, a=a, **common)
+    ops.moe_grouped_gemm_mx(ops.MOE_GEMM_DOWN, cfg, a_mx=mx["a_in"], w2_mx=mx["w2"], o=o, **common)
+    torch.cuda.synchronize()
+    # oracle: dequantised MX operands, fp64 matmuls per expert segment
+    Xd, W1d, W2d, Ad = _deq(x), _deq(w1), _deq(w2), _deq(a_in)
+    tok = row_map // k
+    h_ex = np.zeros((M, 2 * I)); h_abs = np.zeros((M, 2 * I))
+    o_ex = np.zeros((M, H)); o_abs = np.zeros((M, H))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r0 == r1:
+            continue
+        W1e, W2e = W1d[e * 2 * I:(e + 1) * 2 * I], W2d[e * H:(e + 1) * H]
+        xs = Xd[tok[r0:r1]]
+        h_ex[r0:r1] = xs @ W1e.T
+        h_abs[r0:r1] = np.abs(xs) @ np.abs(W1e).T
+        o_ex[r0:r1] = Ad[r0:r1] @ W2e.T
+        o_abs[r0:r1] = np.abs(Ad[r0:r1]) @ np.abs(W2e).T
+    h_g = h.float().cpu().numpy()
+    o_g = o.cpu().numpy()
+    g_ex, u_ex = h_ex[:, :I], h_ex[:, I:]
+    if narrow:
+        # every group inside the window: fp32 sums are exact
+        assert np.array_equal(hz.bits(h.cpu()), _bf16_rne(h_ex.astype(np.float32)))
+        assert np.array_equal(o_g.astype(np.float64), o_ex)
+        dg = du = 0.0
+    else:
+        _within_mfma_bound("mx up h", h_g, h_ex, h_abs, H, bf16_out=True)
+        _within_mfma_bound("mx down o", o_g, o_ex, o_abs, I)
+        acc = (2.0 ** -10 + (H / 8 + 1) * 2.0 ** -24) * h_abs
+        dg, du = acc[:, :I], acc[:, I:]
+    # a (bf16) from the kernel's fp32 SwiGLU of its own accumulators
+    a_ex = _within_swiglu_bound("mx up a", hz.bits(a.cpu()), g_ex, u_ex, dg, du)
+    # a's MX matrix: the quantisation of the kernel's own bf16 a, bit for bit
+    # where that a equals the rounding of the exact value (always, up to the
+    # rare one-ulp flips, in the exact case)
+    codes, scales = ops.mx_views(a_mx, M, I)
+    codes, scales = codes.cpu().numpy(), _natural_scales(scales.cpu().numpy())
+    assert not codes[:, I:].any() and not scales[:, I // 32:].any()
+    ref_c, ref_s = oracle.mx_quantize(_bf16_rne(a_ex.astype(np.float32)))
+    same_c = np.mean(codes[:, :I] == ref_c)
+    same_s = np.mean(scales[:, :I // 32] == ref_s)
+    hz.say(f"mx up a_mx: codes equal {same_c:.5f}, scales equal {same_s:.5f}")
+    assert same_c >= (0.999 if narrow else 0.95) and same_s >= (0.999 if narrow else 0.95)
+
+
+# --------------------------------------------------------------- forward ----
+
+def _mx_weights(d):
+    from grouped_gemm_expert_amd import ops
+    E, twoI, H = d["w1"].shape
+    I = d["w2"].shape[2]
+    w1_mx = ops.mx_alloc(E * twoI, H)
+    w2_mx = ops.mx_alloc(E * H, I)
+    ops.moe_mx_quantize(d["w1"], w1_mx)
+    ops.moe_mx_quantize(d["w2"], w2_mx)
+    return w1_mx, w2_mx
+
+
+def _run_mx(w, d, l32, staged=False):
+    from grouped_gemm_expert_amd import ops
+    cfg = ops.config_from_workload(w)
+    saved = ops.alloc_saved(cfg)
+    saved["logits"].copy_(torch.from_numpy(l32).cuda())
+    y = torch.full((w.T, w.H), float("nan"), device="cuda")
+    aux = torch.empty((1,), device="cuda")
+    ws = ops.workspace(cfg, "fwd")
+    w1_mx, w2_mx = _mx_weights(d)
+    if staged:
+        ops.moe_stage1_forward_mx(cfg, d["x"], None, d["bias"], w1_mx, aux, saved, ws)
+        ops.moe_stage2_forward_mx(cfg, w2_mx, saved, y, ws)
+    else:
+        ops.moe_forward_mx(cfg, d["x"], None, d["bias"], w1_mx, w2_mx, y, aux, saved, ws)
+    torch.cuda.synchronize()
+    return dict(y=y, aux=aux, saved=saved)
+
+
+MX_E2E = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "mid_even"]
+
+
+@pytest.mark.parametrize("name", MX_E2E)
+def test_mx_forward_matches_oracle(name):
+    w = inputs.WORKLOADS[name]
+    hz.say(f"mx forward {inputs.describe(w)}")
+    dc = inputs.make_inputs(w)
+    d = hz.to_device(dc)
+    l64, r = hz.oracle_route(w, dc)
+    l32 = l64.astype(np.float32) if dc["Wr"] is not None else dc["logits"].numpy()
+    if dc["Wr"] is not None:               # route on the fp32 logits both sides share
+        bias = None if dc["bias"] is None else dc["bias"].numpy()
+        r = oracle.route(l64, score=hz.SCORE[w.score], k=w.k, n_groups=w.n_groups,
+                         topk_groups=w.topk_groups, bias=bias, renorm=w.renorm, scale=w.scale,
+                         coeff=w.aux_coeff, logits32=l32, route_mode=w.route)
+    got = _run_mx(w, d, l32)
+    sv = got["saved"]
+    assert np.array_equal(sv["topk_idx"].cpu().numpy(), r["idx"])
+    assert np.array_equal(sv["row_map"].cpu().numpy()[:w.M], r["row_map"])
+    X, W1, W2 = hz.bits(dc["x"]), hz.bits(dc["w1"]), hz.bits(dc["w2"])
+    ops_o = oracle.MxOperands(X, W1, W2)
+    y_ref = oracle.mx_forward(ops_o, r["idx"], r["w"])
+    hz.assert_close(f"{name} mx y", got["y"].cpu().numpy(), y_ref, MX_TOL)
+    # h (bf16 of the fp32 GEMM1 accumulators) and a (bf16) per sorted row
+    g, u, a, aq, as_, _ = oracle.mx_expert_rows(ops_o, r["idx"], r["row_map"])
+    ops_abs = oracle.MxOperands(X & 0x7FFF, W1 & 0x7FFF, W2 & 0x7FFF)
+    ga, ua, *_ = oracle.mx_expert_rows(ops_abs, r["idx"], r["row_map"])
+    h = sv["h"][:w.M].float().cpu().numpy()
+    _within_mfma_bound(f"{name} mx h", h, np.concatenate([g, u], 1), np.concatenate([ga, ua], 1),
+                       w.H, bf16_out=True)
+    acc = (2.0 ** -10 + (w.H / 8 + 1) * 2.0 ** -24)
+    _within_swiglu_bound(f"{name} mx a", hz.bits(sv["a"][:w.M].cpu()), g, u, acc * ga, acc * ua)
+    # the MX path really quantises: it is not the bf16 forward
+    y_bf16 = oracle.forward(X, W1, W2, r["idx"], r["w"])
+    _, fro = hz.errors(got["y"].cpu().numpy(), y_bf16)
+    hz.say(f"{name} mx y vs exact bf16 forward: rel_fro={fro:.3e}")
+    assert 1e-3 < fro < 0.1
+
+
+def test_mx_two_stages_equal_one_call():
+    w = inputs.WORKLOADS["mid_sigmoid"]
+    hz.say(f"mx stages {inputs.describe(w)}")
+    dc = inputs.make_inputs(w)
+    d = hz.to_device(dc)
+    l32 = oracle.logits(hz.bits(dc["x"]), dc["Wr"].numpy()).astype(np.float32)
+    a = _run_mx(w, d, l32)
+    b = _run_mx(w, d, l32, staged=True)
+    assert torch.equal(a["y"], b["y"]) and torch.equal(a["aux"], b["aux"])
+    for k in ("topk_idx", "row_map", "h", "a"):
+        assert torch.equal(a["saved"][k], b["saved"][k]), k
+
+
+def test_mx_weight_cache_follows_weight_versions():
+    from grouped_gemm_expert_amd import ops
+    w = inputs.WORKLOADS["tiny"]
+    hz.say(f"mx cache {inputs.describe(w)}")
+    d = hz.to_device(inputs.make_inputs(w))
+    cache = ops.MxWeightCache()
+    m1, m2 = cache.get(d["w1"], d["w2"])
+    first = m1.clone()
+    cache.get(d["w1"], d["w2"])
+    assert cache.builds == 1
+    d["w1"].mul_(2)                        # in-place update: the version changes
+    n1, _ = cache.get(d["w1"], d["w2"])
+    assert cache.builds == 2
+    ref1, _ = _mx_weights(d)
+    assert torch.equal(n1, ref1) and not torch.equal(n1, first)
+    cache.drop()                           # optimizer-step invalidation
+    cache.get(d["w1"], d["w2"])
+    assert cache.builds == 3
