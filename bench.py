@@ -13,6 +13,11 @@ that the library records on its own stream around each stage
 (moe_set_stage_events); the roofline entry is for the slowest grouped GEMM.
 The CPU baseline is the oracle, timed on a bounded token sample of the same
 workload on the host cores.
+
+The "mxfp8" object times the layer's MXFP8 forward (the mxfp8 expert precision:
+both expert GEMMs on block-scaled fp8 MFMA) on the same inputs, after the bf16
+steps: the weight-cache fill (quantising w1 and w2), then forwards whose
+grouped GEMMs are priced against the fp8 MFMA peak.
 """
 from __future__ import annotations
 
@@ -28,17 +33,19 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer fwd+bwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the MX block-scaled ops run at it)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_wgrad"]
 # kernel-name fragment of each grouped-GEMM op in a rocprofv3 trace
 GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k_down_dgrad<",
-                "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<"}
+                "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<",
+                "up_swiglu_mx": "k_up_swiglu_mx<", "down_mx": "k_down_mx<"}
 # The measured HBM traffic of the grouped GEMMs lives in this file, next to a
 # hash of the kernel sources it was taken with; a changed kernel reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
-                  for f in ("gemm.hip", "tile.h", "common.h")]
+                  for f in ("gemm.hip", "tile.h", "common.h", "swiglu_epi.h", "mxfmt.h", "mx.hip")]
 COPY_BYTES = 1 << 30        # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
@@ -128,12 +135,94 @@ def run_gpu(args, w):
             continue
         if s == "router_grads" and d["Wr"] is None:
             continue
+        if s == "mx_quant":               # not part of the bf16 step
+            continue
         times = [a.elapsed_time(b) for a, b in ev[s]]
         stage_ms[s] = sum(times) / len(times)
     counts = saved["counts"].cpu()
     log(f"[bench] step {elapsed / K * 1e3:.3f} ms; active experts {(counts > 0).sum().item()}, "
         f"max rows {counts.max().item()}")
     return dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved)
+
+
+MX_FWD_STAGES = ["router_proj", "router", "permute", "mx_quant", "up_swiglu", "down", "combine"]
+
+
+def run_mx(args, w, g):
+    """MXFP8 forward on the bf16 run's inputs: the weight-cache fill once, then
+    W warmup and K timed forwards with per-stage events."""
+    import torch
+    from grouped_gemm_expert_amd import ops
+
+    d = g["d"]
+    dev = d["x"].device
+    cfg = ops.config_from_workload(w)
+    saved = ops.alloc_saved(cfg, dev)
+    if d["logits"] is not None:
+        saved["logits"].copy_(d["logits"])
+    y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = ops.workspace(cfg, "fwd", dev)
+    cache = ops.MxWeightCache()
+    log("[bench] mxfp8: quantising w1, w2 (weight cache fill)")
+    cache.get(d["w1"], d["w2"])      # first fill allocates the cache
+    torch.cuda.synchronize()
+    cache.drop()                     # the timed fill: both quantiser launches
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    w1_mx, w2_mx = cache.get(d["w1"], d["w2"])
+    c1.record()
+    torch.cuda.synchronize()
+    fill_ms = c0.elapsed_time(c1)
+
+    def fwd():
+        ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], w1_mx, w2_mx, y, aux, saved, ws)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    K = args.steps
+    stages = [s for s in MX_FWD_STAGES if not (s == "router_proj" and d["Wr"] is None)]
+    ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)] for s in stages}
+    for pairs in ev.values():
+        for a, b in pairs:
+            a.record()
+            b.record()
+    torch.cuda.synchronize()
+    log(f"[bench] mxfp8: timing {K} forwards")
+    t0 = time.perf_counter()
+    for i in range(K):
+        for s in stages:
+            ops.moe_set_stage_events(ops.STAGES[s], *ev[s][i])
+        fwd()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in stages:
+        ops.moe_set_stage_events(ops.STAGES[s], None, None)
+    st = {s: sum(a.elapsed_time(b) for a, b in ev[s]) / K for s in stages}
+    gemm = {"up_swiglu": gemm_flops(w, "up_swiglu"), "down": gemm_flops(w, "down")}
+    tf = {s: gemm[s] / (st[s] * 1e-3) / 1e12 for s in gemm}
+    dom = max(gemm, key=lambda s: st[s])
+    bf16_fwd = sum(g["stage_ms"][s] for s in stages if s != "mx_quant")
+    out = {
+        "ms_per_forward": round((t1 - t0) / K * 1e3, 4),
+        "tokens_per_s_forward": round(w.T * K / (t1 - t0), 1),
+        "bf16_forward_ms": round(bf16_fwd, 4),
+        "weight_cache_fill_ms": round(fill_ms, 3),
+        "stages": {s: {"ms": round(st[s], 4), **({"TFLOP/s": round(tf[s], 1)} if s in tf else {})}
+                   for s in stages},
+        "grouped_gemm": {"TFLOP/s": round(sum(gemm.values()) / (sum(st[s] for s in gemm) * 1e-3) / 1e12, 1),
+                         "pct_of_fp8_peak": round(100 * sum(gemm.values()) / (sum(st[s] for s in gemm) * 1e-3)
+                                                  / 1e12 / PEAK_FP8_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "kernel": dom + "_mx", "achieved": round(tf[dom], 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf[dom] / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic(dom + "_mx")},
+    }
+    log(f"[bench] mxfp8 forward {out['ms_per_forward']:.3f} ms (bf16 forward stages "
+        f"{bf16_fwd:.3f} ms); GEMMs {tf}")
+    return out
 
 
 def kernel_source_hash():
@@ -300,6 +389,7 @@ def main():
     ap.add_argument("--workload", default="deepseek_v3")
     ap.add_argument("--dw-mode", choices=["accumulate", "overwrite"], default="accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy that calibrates the PMC byte counters")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -372,6 +462,8 @@ def main():
         "stages": stages,
         "active_experts": sum(1 for c in g["counts"] if c > 0),
     }
+    if not args.no_mx:
+        out["mxfp8"] = run_mx(args, w, g)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, g["d"])
     print(json.dumps(out), flush=True)
