@@ -30,8 +30,8 @@ struct Carver {
     }
 };
 
-// Bytes of an MX matrix [rows, K]: codes [rows, Kp] then scales [rows, Kp/32].
-int64_t mx_bytes(int64_t rows, int64_t K) { return rows * mx_kp(K) + rows * (mx_kp(K) / 32); }
+// Bytes of an MX matrix [rows, K]: codes [rows, Kp] then the scale area.
+int64_t mx_bytes(int64_t rows, int64_t K) { return rows * mx_kp(K) + mx_scale_bytes(rows, K); }
 
 struct FwdWs {
     float *prob_part;

@@ -12,7 +12,11 @@
 //   k_down_mx       o = A . W2[e]^T from the MX forms of a and w2 (fp32 out).
 // Both operands are K-major, so the tiles reuse the bf16 kernels' [rows][128 B]
 // swizzled LDS layout and direct global->LDS copies: a 128-byte row slice is
-// 128 fp8 of k here (one scale group, two MFMA k-steps) instead of 64 bf16.
+// 128 fp8 of k here (one scale group, two MFMA k-steps) instead of 64 bf16,
+// so every copy still moves whole 128-byte lines.  (Stages of 64 fp8 in a
+// four-deep ring were measured too: they halve the bytes per line request,
+// and a CU's copy rate is set by how many line requests it keeps in flight
+// against the L2 latency, so they were slower.)
 // The block scales of a stage (4 bytes per row, for 256 A rows and 256 B
 // rows) travel through LDS too, as 4-byte-per-lane copies in which lanes
 // 0..31 copy 32 A rows and lanes 32..63 the matching 32 B rows.
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *src, int64_
     const uint32_t word = mx_group_word(sc, lane);
     if (valid) {
         *(uint64_t *)(codes + row * Kp + col) = c;
-        if ((lane & 15) == 0) *(uint32_t *)(scales + row * (Kp / 32) + j * 4) = word;
+        if ((lane & 15) == 0) *(uint32_t *)(scales + mx_scale_off(row, j, gpr)) = word;
     }
 }
 
@@ -281,8 +285,8 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu_mx(GemmArgs g)
 #pragma unroll
     for (int q = 0; q < C::NS; ++q) {
         const int sr = scale_row<C>(wave0, q, lane0);
-        sp[q] = lane0 < 32 ? g.xs + tok_of(sr) * (Hp / 32)
-                           : g.w1s + ((int64_t)t.e * 2 * I + w1_row(sr)) * (Hp / 32);
+        sp[q] = lane0 < 32 ? g.xs + mx_scale_off(tok_of(sr), 0, Hp / MX_GROUP)
+                           : g.w1s + mx_scale_off((int64_t)t.e * 2 * I + w1_row(sr), 0, Hp / MX_GROUP);
     }
     Acc<C> acc;
     mx_pipeline<C, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu_mx(GemmArgs g)
         [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * 64, 0, la.base); },
         [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * 64, 0, lb.base); },
         [&](int q, int s, lds_t *Ss) {
-            copy4_to_lds(sp[q] + 4 * s, Ss + (wave0 * C::NS + q) * 256);
+            copy4_to_lds(sp[q] + s * 128, Ss + (wave0 * C::NS + q) * 256);
         },
         acc);
     swiglu_epilogue<C, true>(acc, lds, t, i0, I, g.h, g.a, g.aq, g.as_, g.Ip);
@@ -331,8 +335,8 @@ __global__ __launch_bounds__(C::NT) void k_down_mx(GemmArgs g)
 #pragma unroll
     for (int q = 0; q < C::NS; ++q) {
         const int sr = scale_row<C>(wave0, q, lane0);
-        sp[q] = lane0 < 32 ? g.as_ + a_row(sr) * (Ip / 32)
-                           : g.w2s + ((int64_t)t.e * H + w2_row(sr)) * (Ip / 32);
+        sp[q] = lane0 < 32 ? g.as_ + mx_scale_off(a_row(sr), 0, Ip / MX_GROUP)
+                           : g.w2s + mx_scale_off((int64_t)t.e * H + w2_row(sr), 0, Ip / MX_GROUP);
     }
     Acc<C> acc;
     mx_pipeline<C, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(C::NT) void k_down_mx(GemmArgs g)
         [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * 64, 0, la.base); },
         [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * 64, 0, lb.base); },
         [&](int q, int s, lds_t *Ss) {
-            copy4_to_lds(sp[q] + 4 * s, Ss + (wave0 * C::NS + q) * 256);
+            copy4_to_lds(sp[q] + s * 128, Ss + (wave0 * C::NS + q) * 256);
         },
         acc);
     store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);

@@ -7,19 +7,32 @@
 //
 // MX matrix layout used by the library: a bf16 matrix [rows, K] quantised
 // along K becomes codes [rows, Kp] (Kp = K rounded up to 128, padding codes 0)
-// followed by scales [rows, Kp/32].  Within every 128-column group the four
-// block scales of a row are stored in the order of blocks 0, 2, 1, 3: one
-// 16-bit read then yields, for one half of a wave, the scales of both 64-deep
-// MFMA steps of that group (low byte: first step, high byte: second).
+// followed by the scales.  A row has one 4-byte scale word per 128-column
+// group, holding the group's four block scales in the order of blocks 0, 2,
+// 1, 3: one 16-bit read then yields, for one half of a wave, the scales of
+// both 64-deep MFMA steps of that group (low byte: first step, high byte:
+// second).  The words are stored in 32-row blocks, [ceil(rows/32)][Kp/128]
+// [32][4 bytes], so that the words of 32 consecutive rows for one group are
+// one contiguous 128-byte line (one line per copy instead of 32).
 #pragma once
 
 #include "common.h"
 
 namespace moe {
 
-constexpr int MX_GROUP = 128;  // columns per scale word / per LDS stage
+constexpr int MX_GROUP = 128;  // columns per scale word
 
 inline int64_t mx_kp(int64_t K) { return (K + MX_GROUP - 1) / MX_GROUP * MX_GROUP; }
+
+// Byte offset of the scale word of (row, group) in the scale area, gpr =
+// Kp / 128 groups per row.
+__host__ __device__ inline int64_t mx_scale_off(int64_t row, int64_t group, int64_t gpr)
+{
+    return ((row >> 5) * gpr + group) * 128 + (row & 31) * 4;
+}
+
+// Bytes of the scale area of an MX matrix with `rows` rows.
+inline int64_t mx_scale_bytes(int64_t rows, int64_t K) { return (rows + 31) / 32 * 32 * (mx_kp(K) / 32); }
 
 // X of a block with largest magnitude amax (finite, >= 0).
 MOE_DEV int mx_block_exp(float amax)

@@ -82,7 +82,8 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
                 const uint32_t w = mx_group_word(sc, lane);
                 if (achunk) {
                     *(uint64_t *)(aq + m * Ip + col) = c;
-                    if (lane == 32) *(uint32_t *)(as_ + m * (Ip / 32) + i0 / 32) = w;
+                    if (lane == 32)
+                        *(uint32_t *)(as_ + mx_scale_off(m, i0 / MX_GROUP, Ip / MX_GROUP)) = w;
                 }
             }
         }

@@ -328,11 +328,16 @@ def mx_alloc(rows: int, K: int, device="cuda") -> torch.Tensor:
 
 
 def mx_views(buf: torch.Tensor, rows: int, K: int):
-    """(codes [rows, Kp], scales [rows, Kp/32]) views of an MX-matrix buffer;
-    the scales of each 128-column group are in block order 0, 2, 1, 3."""
+    """(codes [rows, Kp], scales [rows, Kp/32]) of an MX-matrix buffer: the
+    codes as a view, the scales gathered from their 32-row-block layout into
+    block order (a new tensor)."""
     Kp = mx_kp(K)
+    gpr = Kp // 128
+    rows_p = (rows + 31) // 32 * 32
     codes = buf[:rows * Kp].view(rows, Kp)
-    scales = buf[rows * Kp:rows * Kp + rows * Kp // 32].view(rows, Kp // 32)
+    raw = buf[rows * Kp:rows * Kp + rows_p * Kp // 32].view(rows_p // 32, gpr, 32, 4)
+    words = raw.permute(0, 2, 1, 3).reshape(rows_p, gpr, 4)[:rows]   # [row][group][0, 2, 1, 3]
+    scales = words[:, :, [0, 2, 1, 3]].reshape(rows, Kp // 32)
     return codes, scales
 
 

@@ -326,9 +326,12 @@ moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, co
  *
  * MX matrix: the quantised form of a bf16 matrix [rows, K] along K, in one
  * buffer: codes [rows, Kp] (E4M3 bytes, Kp = K rounded up to 128, padding
- * codes 0) followed by scales [rows, Kp/32] (E8M0 bytes, 2^(s - 127)); within
- * each 128-column group the four block scales of a row are stored as blocks
- * 0, 2, 1, 3 (the order the block-scaled MFMA consumes them).
+ * codes 0) followed by the scales (E8M0 bytes, 2^(s - 127)).  A row has one
+ * 4-byte word per 128-column group g holding the group's four block scales
+ * as blocks 0, 2, 1, 3 (the order the block-scaled MFMA consumes them); the
+ * word of (row, g) is at byte ((row/32) * (Kp/128) + g) * 128 + (row%32) * 4
+ * of the scale area, which has ceil(rows/32) * 32 * Kp/32 bytes (32-row
+ * blocks, so that a 32-row tile slice is one 128-byte line).
  *
  * moe_mx_size       bytes of the MX matrix of [rows, K]; K % 32 == 0, else
  *                   MOE_EINVAL.
