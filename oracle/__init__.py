@@ -37,6 +37,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
                        -- pinned: exact integer GEMMs on MX-representable inputs,
                           y = sum_j w_j o_j against mx_forward, the MX error
                           bound against the exact forward
+  mx_backward_tokens, mx_weight_grad_elements
+                       -- pinned: a numpy formulation from the quantiser and
+                          dense matmuls (expert part of dx, dW1, dW2), the
+                          router part through the bf16 oracle's pinned code,
+                          and the distance to the exact backward
 """
 from __future__ import annotations
 
@@ -97,6 +102,10 @@ def _load():
         "oracle_mx_quantize": [i64, i64, P, P, P],
         "oracle_mx_expert_rows": [i32, i32, i32, P, P, P, P, P, P, P, i64, P, P, P, P, P, P, P],
         "oracle_mx_forward": [i32, i32, i32, P, P, P, P, P, P, P, P, i64, P, P],
+        "oracle_mx_backward_tokens": [i64, i32, i32, i32, i32, i32, i32, f64, f64, f64,
+                                      P, P, P, P, P] + [P] * 12 + [i64, P, P, P],
+        "oracle_mx_weight_grad_elements": [i64, i32, i32, i32, P, P, P, P] + [P] * 8
+                                          + [i64, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -400,3 +409,59 @@ def mx_forward(ops: MxOperands, idx, w, toks=None) -> np.ndarray:
     y = np.empty((n, ops.H), np.float64)
     _load().oracle_mx_forward(ops.H, ops.I, k, *ops.ptrs(), _p(idx), _p(w), n, _p(tk), _p(y))
     return y
+
+
+class MxBackwardOperands(MxOperands):
+    """The forward's MX operands plus the backward's: dy along H, and the
+    transposed weights w2[e]^T [I, H] along H and w1[e]^T [H, 2I] along 2I."""
+
+    def __init__(self, x, w1, w2, dy):
+        super().__init__(x, w1, w2)
+        dy = _c(dy, np.uint16)
+        w1 = _c(w1, np.uint16)
+        w2 = _c(w2, np.uint16)
+        E, H, I = self.E, self.H, self.I
+        self.dyq, self.dys = mx_quantize(dy)
+        self.w2cq, self.w2cs = mx_quantize(np.ascontiguousarray(w2.transpose(0, 2, 1)).reshape(E * I, H))
+        self.w1cq, self.w1cs = mx_quantize(np.ascontiguousarray(w1.transpose(0, 2, 1)).reshape(E * H, 2 * I))
+
+    def bwd_ptrs(self):
+        return (_p(self.dyq), _p(self.dys), _p(self.w2cq), _p(self.w2cs), _p(self.w1cq),
+                _p(self.w1cs))
+
+
+def mx_backward_tokens(ops: MxBackwardOperands, Wr, logits64, idx, counts, w, *, score, renorm,
+                       scale, coeff, d_aux=1.0, toks=None):
+    """-> dx [ntok,H], dlogits [ntok,E] (double) of the MXFP8 backward."""
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    l = _c(logits64, np.float64)
+    counts = _c(counts, np.int32)
+    Wr = _c(Wr, np.float32)
+    T, k = idx.shape
+    E = l.shape[1]
+    tk, n = _toks(toks, T)
+    dx = np.empty((n, ops.H), np.float64)
+    dl = np.empty((n, E), np.float64)
+    _load().oracle_mx_backward_tokens(T, ops.H, ops.I, E, k, score, int(bool(renorm)), float(scale),
+                                      float(coeff), float(d_aux), _p(Wr), _p(l), _p(idx),
+                                      _p(counts), _p(w), *ops.ptrs(), *ops.bwd_ptrs(), n, _p(tk),
+                                      _p(dx), _p(dl))
+    return dx, dl
+
+
+def mx_weight_grad_elements(ops: MxBackwardOperands, x, dy, idx, w, which, ee, rr, cc):
+    """Single elements of the MXFP8 dW1 (which=1, [e,n,h]) or dW2 (which=2, [e,h,i])."""
+    x = _c(x, np.uint16)
+    dy = _c(dy, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    which, ee, rr, cc = (_c(np.asarray(v), np.int32) for v in (which, ee, rr, cc))
+    T, k = idx.shape
+    out = np.empty(which.shape[0], np.float64)
+    _load().oracle_mx_weight_grad_elements(T, ops.H, ops.I, k, _p(x), _p(dy), _p(idx), _p(w),
+                                           _p(ops.xq), _p(ops.xs), _p(ops.w1q), _p(ops.w1s),
+                                           _p(ops.dyq), _p(ops.dys), _p(ops.w2cq), _p(ops.w2cs),
+                                           which.shape[0], _p(which), _p(ee), _p(rr), _p(cc),
+                                           _p(out))
+    return out

@@ -340,6 +340,65 @@ void oracle_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
     }
 }
 
+/* Router part of the backward for one token, given the gradient dw[j] of  */
+/* the loss w.r.t. each routing weight (the expert path's row-dots):        */
+/*   softmax: dp at selected e_j = renorm ? (dw_j - sum dw w)/sum p_sel      */
+/*                                        : dw_j                             */
+/*            plus aux: d_aux*coeff*E/(k T^2)*counts[e] at every e;         */
+/*            dl = p * (dp - <dp, p>)                                        */
+/*   sigmoid: ds at selected e_j = scale/sum s_sel * (dw_j - sum dw w/scale) */
+/*            plus aux through p = s/sum s: (a_e - sum a p)/sum s;           */
+/*            dl = ds * s * (1 - s)                                          */
+/*   dxt += sum_e dl[e] Wr[e,:]   (when Wr != NULL)                          */
+/* lt: the token's logits [E]; it: its experts [k]; p, dp: scratch [E].     */
+static void router_token_backward(int64_t T, int32_t H, int32_t E, int32_t k, int32_t score,
+                                  int32_t renorm, double scale, double coeff, double d_aux,
+                                  const float *Wr, const double *lt, const int32_t *it,
+                                  const int32_t *counts, const double *dw, double *p,
+                                  double *dp, double *dl, double *dxt)
+{
+    double wt[32];
+    token_scores(E, score, lt, p);
+    double zsel = 0.0;
+    for (int32_t j = 0; j < k; ++j) zsel += p[it[j]];
+    for (int32_t j = 0; j < k; ++j) {
+        double v = p[it[j]];
+        if (score == OR_SOFTMAX) wt[j] = renorm ? v / zsel : v;
+        else wt[j] = scale * v / zsel;
+    }
+    double sdw = 0.0;
+    for (int32_t j = 0; j < k; ++j) sdw += dw[j] * wt[j];
+    for (int32_t e = 0; e < E; ++e) dp[e] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+        int32_t e = it[j];
+        if (score == OR_SOFTMAX)
+            dp[e] += renorm ? (dw[j] - sdw) / zsel : dw[j];
+        else
+            dp[e] += scale / zsel * (dw[j] - sdw / scale);
+    }
+    double aux_scale = (T > 0) ? d_aux * coeff * (double)E /
+                                     ((double)k * (double)T * (double)T)
+                               : 0.0;
+    if (score == OR_SOFTMAX) {
+        for (int32_t e = 0; e < E; ++e) dp[e] += aux_scale * (double)counts[e];
+        double dot = 0.0;
+        for (int32_t e = 0; e < E; ++e) dot += dp[e] * p[e];
+        for (int32_t e = 0; e < E; ++e) dl[e] = p[e] * (dp[e] - dot);
+    } else {
+        double q = 0.0;
+        for (int32_t e = 0; e < E; ++e) q += p[e];
+        double ap = 0.0;
+        for (int32_t e = 0; e < E; ++e) ap += aux_scale * (double)counts[e] * (p[e] / q);
+        for (int32_t e = 0; e < E; ++e)
+            dp[e] += (aux_scale * (double)counts[e] - ap) / q;
+        for (int32_t e = 0; e < E; ++e) dl[e] = dp[e] * p[e] * (1.0 - p[e]);
+    }
+    if (Wr)
+        for (int32_t e = 0; e < E; ++e)
+            for (int32_t h = 0; h < H; ++h)
+                dxt[h] += dl[e] * (double)Wr[(int64_t)e * H + h];
+}
+
 /* ------------------------------------------------------------------------ */
 /* Backward for a list of tokens: dx [ntok,H] and dlogits [ntok,E] (double). */
 /* Loss = sum_t <dy[t], y[t]> + d_aux * aux.                                 */
@@ -421,38 +480,9 @@ void oracle_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E,
             }
 
             /* router */
-            double sdw = 0.0;
-            for (int32_t j = 0; j < k; ++j) sdw += dw[j] * wt[j];
-            for (int32_t e = 0; e < E; ++e) dp[e] = 0.0;
-            for (int32_t j = 0; j < k; ++j) {
-                int32_t e = idx[t * k + j];
-                if (score == OR_SOFTMAX)
-                    dp[e] += renorm ? (dw[j] - sdw) / zsel : dw[j];
-                else
-                    dp[e] += scale / zsel * (dw[j] - sdw / scale);
-            }
-            double *dl = dlogits + n * E;
-            double aux_scale = (T > 0) ? d_aux * coeff * (double)E /
-                                             ((double)k * (double)T * (double)T)
-                                       : 0.0;
-            if (score == OR_SOFTMAX) {
-                for (int32_t e = 0; e < E; ++e) dp[e] += aux_scale * (double)counts[e];
-                double dot = 0.0;
-                for (int32_t e = 0; e < E; ++e) dot += dp[e] * p[e];
-                for (int32_t e = 0; e < E; ++e) dl[e] = p[e] * (dp[e] - dot);
-            } else {
-                double q = 0.0;
-                for (int32_t e = 0; e < E; ++e) q += p[e];
-                double ap = 0.0;
-                for (int32_t e = 0; e < E; ++e) ap += aux_scale * (double)counts[e] * (p[e] / q);
-                for (int32_t e = 0; e < E; ++e)
-                    dp[e] += (aux_scale * (double)counts[e] - ap) / q;
-                for (int32_t e = 0; e < E; ++e) dl[e] = dp[e] * p[e] * (1.0 - p[e]);
-            }
-            if (Wr)
-                for (int32_t e = 0; e < E; ++e)
-                    for (int32_t h = 0; h < H; ++h)
-                        dxt[h] += dl[e] * (double)Wr[(int64_t)e * H + h];
+            router_token_backward(T, H, E, k, score, renorm, scale, coeff, d_aux, Wr,
+                                  logits + t * E, idx + t * k, counts, dw, p, dp,
+                                  dlogits + n * E, dxt);
         }
         free(g);
         free(u);
@@ -812,5 +842,194 @@ void oracle_mx_forward(int32_t H, int32_t I, int32_t k, const uint8_t *xq, const
         free(aq);
         free(as_);
         free(o);
+    }
+}
+
+/* ======================================================================== */
+/* MXFP8 backward (page "MegaMoE", "Expert precision": the backward of the   */
+/* expert stages and the dW1 / dW2 weight gradients run in MXFP8 too).       */
+/* Every GEMM takes its operands in MX form, quantised along its own         */
+/* contraction dimension:                                                    */
+/*   dA' = DY . W2c^T    DY: dy per token along H;                           */
+/*                       W2c: w2[e]^T [I, H] along H (rows e*I + i)          */
+/*   dx  = DH . W1c^T    DH: dh per slot along 2I;                           */
+/*                       W1c: w1[e]^T [H, 2I] along 2I (rows e*H + h)        */
+/*   dW2[e] = DYW_e^T . A_e,  dW1[e] = DH_e^T . XG_e: both operands along    */
+/*            the expert's routed rows, in blocks of 32 from its first row   */
+/*            (ascending flat slot), the last block padded with zeros.       */
+/* Tensors are rounded to the precision the path holds them in before they   */
+/* are quantised: dh = bf16(fp32(dg | du)), dyw = bf16(fp32(w * dy)),        */
+/* a = bf16(fp32(a)); xg is the bf16 input x.  g, u, a come from the MXFP8   */
+/* forward (mx_slot).  The routing weight's gradient is the row-dot          */
+/* dw_j = sum_i dA'_i a_i with the bf16 a.                                   */
+/* ======================================================================== */
+
+/* dA' of one slot (t, e): dAp[i] = sum_h DY[t,h] W2c[e*I+i, h]. */
+static void mx_dA(int32_t H, int32_t I, int64_t t, int32_t e, const uint8_t *dyq,
+                  const uint8_t *dys, const uint8_t *w2cq, const uint8_t *w2cs, double *dAp)
+{
+    for (int32_t i = 0; i < I; ++i) {
+        double acc = 0.0;
+        for (int32_t h = 0; h < H; ++h)
+            acc += mx_value(dyq, dys, H, t, h) * mx_value(w2cq, w2cs, H, (int64_t)e * I + i, h);
+        dAp[i] = acc;
+    }
+}
+
+static double bf16_of(double v) { return bf(f32_to_bf16((float)v)); }
+
+/* SwiGLU backward of one element: dg, du from dA = w * dA', g, u. */
+static void swiglu_bwd(double dA, double g, double u, double *dg, double *du)
+{
+    double sg = sigmoid(g);
+    *dg = dA * u * sg * (1.0 + g * (1.0 - sg));
+    *du = dA * silu(g);
+}
+
+/* Backward for a list of tokens: dx [ntok,H], dlogits [ntok,E] (double).    */
+/* fwd MX operands: xq/xs [T,H], w1q/w1s [E*2I,H], w2q/w2s [E*H,I];          */
+/* backward ones: dyq/dys [T,H], w2cq/w2cs [E*I,H], w1cq/w1cs [E*H,2I].      */
+/* w [T,k] routing weights (double); logits [T,E]; Wr [E,H] or NULL.         */
+void oracle_mx_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                               int32_t score, int32_t renorm, double scale, double coeff,
+                               double d_aux, const float *Wr, const double *logits,
+                               const int32_t *idx, const int32_t *counts, const double *w,
+                               const uint8_t *xq, const uint8_t *xs, const uint8_t *w1q,
+                               const uint8_t *w1s, const uint8_t *w2q, const uint8_t *w2s,
+                               const uint8_t *dyq, const uint8_t *dys, const uint8_t *w2cq,
+                               const uint8_t *w2cs, const uint8_t *w1cq, const uint8_t *w1cs,
+                               int64_t ntok, const int64_t *toks, double *dx, double *dlogits)
+{
+#pragma omp parallel
+    {
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        uint8_t *aq = (uint8_t *)malloc((size_t)I);
+        uint8_t *as_ = (uint8_t *)malloc((size_t)I / 32 + 1);
+        double *dAp = (double *)malloc(sizeof(double) * (size_t)I);
+        double *dh = (double *)malloc(sizeof(double) * 2 * (size_t)I);
+        uint8_t *dhq = (uint8_t *)malloc(2 * (size_t)I);
+        uint8_t *dhs = (uint8_t *)malloc(2 * (size_t)I / 32 + 1);
+        double *p = (double *)malloc(sizeof(double) * (size_t)E);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)E);
+        double dw[32];
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < ntok; ++n) {
+            int64_t t = toks ? toks[n] : n;
+            double *dxt = dx + n * H;
+            for (int32_t h = 0; h < H; ++h) dxt[h] = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t e = idx[t * k + j];
+                mx_slot(H, I, t, e, xq, xs, w1q, w1s, w2q, w2s, g, u, a, aq, as_, NULL);
+                mx_dA(H, I, t, e, dyq, dys, w2cq, w2cs, dAp);
+                double acc = 0.0;
+                for (int32_t i = 0; i < I; ++i) acc += dAp[i] * bf16_of(a[i]);
+                dw[j] = acc;
+                for (int32_t i = 0; i < I; ++i) {
+                    double dg, du;
+                    swiglu_bwd(w[t * k + j] * dAp[i], g[i], u[i], &dg, &du);
+                    dh[i] = bf16_of(dg);
+                    dh[I + i] = bf16_of(du);
+                }
+                for (int32_t b = 0; b < 2 * I / 32; ++b) dhs[b] = mx_block(dh + b * 32, 32, dhq + b * 32);
+                for (int32_t h = 0; h < H; ++h) {
+                    double s = 0.0;
+                    for (int32_t c = 0; c < 2 * I; ++c)
+                        s += oracle_e4m3_value(dhq[c]) * mx_scale(dhs[c / 32]) *
+                             mx_value(w1cq, w1cs, 2 * I, (int64_t)e * H + h, c);
+                    dxt[h] += s;
+                }
+            }
+            router_token_backward(T, H, E, k, score, renorm, scale, coeff, d_aux, Wr,
+                                  logits + t * E, idx + t * k, counts, dw, p, dp,
+                                  dlogits + n * E, dxt);
+        }
+        free(g);
+        free(u);
+        free(a);
+        free(aq);
+        free(as_);
+        free(dAp);
+        free(dh);
+        free(dhq);
+        free(dhs);
+        free(p);
+        free(dp);
+    }
+}
+
+/* MX value of entry q of a column held as n doubles, quantised in blocks of */
+/* 32 from its first entry (the last block padded with zeros).               */
+static void mx_column(const double *col, int64_t n, double *out)
+{
+    double v[32];
+    uint8_t c[32];
+    for (int64_t b = 0; b < n; b += 32) {
+        int64_t m = n - b < 32 ? n - b : 32;
+        for (int i = 0; i < 32; ++i) v[i] = i < m ? col[b + i] : 0.0;
+        uint8_t s = mx_block(v, 32, c);
+        for (int i = 0; i < m; ++i) out[b + i] = oracle_e4m3_value(c[i]) * mx_scale(s);
+    }
+}
+
+/* Single elements of the MXFP8 weight gradients (the rows of expert e are   */
+/* the flat slots f with idx[f] == e, ascending):                            */
+/*   which 2: dW2[e, h, i] = sum_r MX(dyw[:, h])_r MX(a[:, i])_r              */
+/*   which 1: dW1[e, n, h] = sum_r MX(dh[:, n])_r  MX(xg[:, h])_r             */
+/* x, dy raw bf16 [T,H]; w [T,k] double; MX operands as in the backward.     */
+void oracle_mx_weight_grad_elements(int64_t T, int32_t H, int32_t I, int32_t k,
+                                    const uint16_t *x, const uint16_t *dy, const int32_t *idx,
+                                    const double *w, const uint8_t *xq, const uint8_t *xs,
+                                    const uint8_t *w1q, const uint8_t *w1s, const uint8_t *dyq,
+                                    const uint8_t *dys, const uint8_t *w2cq,
+                                    const uint8_t *w2cs, int64_t nel, const int32_t *which,
+                                    const int32_t *ee, const int32_t *rr, const int32_t *cc,
+                                    double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nel; ++q) {
+        int32_t e = ee[q];
+        int64_t n = 0;
+        for (int64_t f = 0; f < T * k; ++f) n += idx[f] == e;
+        double *c1 = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        double *c2 = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        double *m1 = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        double *m2 = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        int64_t r = 0;
+        for (int64_t f = 0; f < T * k; ++f) {
+            if (idx[f] != e) continue;
+            int64_t t = f / k;
+            int32_t i = which[q] == 2 ? cc[q] : rr[q] % I;
+            /* g_i, u_i of this row from the MXFP8 forward */
+            double sg = 0.0, su = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                double xv = mx_value(xq, xs, H, t, h);
+                sg += xv * mx_value(w1q, w1s, H, (int64_t)e * 2 * I + i, h);
+                su += xv * mx_value(w1q, w1s, H, (int64_t)e * 2 * I + I + i, h);
+            }
+            if (which[q] == 2) {
+                c1[r] = bf16_of(w[f] * bf(dy[t * H + rr[q]]));
+                c2[r] = bf16_of(silu(sg) * su);
+            } else {
+                double dAp = 0.0;
+                for (int32_t h = 0; h < H; ++h)
+                    dAp += mx_value(dyq, dys, H, t, h) * mx_value(w2cq, w2cs, H, (int64_t)e * I + i, h);
+                double dg, du;
+                swiglu_bwd(w[f] * dAp, sg, su, &dg, &du);
+                c1[r] = bf16_of(rr[q] < I ? dg : du);
+                c2[r] = bf(x[t * H + cc[q]]);
+            }
+            ++r;
+        }
+        mx_column(c1, n, m1);
+        mx_column(c2, n, m2);
+        double acc = 0.0;
+        for (int64_t i = 0; i < n; ++i) acc += m1[i] * m2[i];
+        out[q] = acc;
+        free(c1);
+        free(c2);
+        free(m1);
+        free(m2);
     }
 }

@@ -231,3 +231,127 @@ def test_mx_forward_within_the_format_error_of_the_exact_forward():
     y = oracle.forward(x, w1, w2, idx, w)
     rel = np.linalg.norm(y_mx - y) / np.linalg.norm(y)
     assert 1e-3 < rel < 0.08, rel
+
+
+# ------------------------------------------------------------- backward ----
+
+def _deq(bits2d):
+    c, s = oracle.mx_quantize(bits2d)
+    return oracle.mx_dequantize(c, s)
+
+
+def _deq_cols(mat):
+    """MX values of a [n, C] float matrix quantised along its rows (down each
+    column) in blocks of 32 from row 0, the last block padded with zeros: the
+    columns are transposed, padded and fed to the row quantiser."""
+    n, C = mat.shape
+    npad = (n + 31) // 32 * 32
+    t = np.zeros((C, npad), np.float32)
+    t[:, :n] = mat.T
+    return _deq(_round_bf16(t))[:, :n].T      # values already bf16: RNE is exact
+
+
+def _bwd_setup(seed, T=12, H=64, I=64, E=3, k=2):
+    rng = np.random.default_rng(seed)
+    x = _round_bf16(rng.normal(0, 1, (T, H)).astype(np.float32))
+    w1 = _round_bf16(rng.normal(0, 0.05, (E, 2 * I, H)).astype(np.float32))
+    w2 = _round_bf16(rng.normal(0, 0.05, (E, H, I)).astype(np.float32))
+    dy = _round_bf16(rng.normal(0, 1, (T, H)).astype(np.float32))
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, (T, k))
+    return x, w1, w2, dy, idx, w
+
+
+def _numpy_mx_backward(x, w1, w2, dy, idx, w):
+    """dx (expert part), dw [T,k], dW1, dW2 of the MXFP8 backward from the
+    quantiser and dense fp64 matmuls."""
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    k = idx.shape[1]
+    Xd, DYd = _deq(x), _deq(dy)
+    W1d = _deq(w1.reshape(E * twoI, H)).reshape(E, twoI, H)
+    W2d = _deq(w2.reshape(E * H, I)).reshape(E, H, I)
+    W2c = _deq(np.ascontiguousarray(w2.transpose(0, 2, 1)).reshape(E * I, H)).reshape(E, I, H)
+    W1c = _deq(np.ascontiguousarray(w1.transpose(0, 2, 1)).reshape(E * H, twoI)).reshape(E, H, twoI)
+    dx = np.zeros((T, H))
+    dw = np.zeros((T, k))
+    rows = {e: [] for e in range(E)}
+    for f in range(T * k):
+        t, j = divmod(f, k)
+        e = idx[t, j]
+        h = Xd[t] @ W1d[e].T
+        g, u = h[:I], h[I:]
+        ab = _bf16_value(_round_bf16((g * scipy.special.expit(g) * u).astype(np.float32)))
+        dAp = DYd[t] @ W2c[e].T
+        dw[t, j] = dAp @ ab
+        dA = w[t, j] * dAp
+        sg = scipy.special.expit(g)
+        dh = np.concatenate([dA * u * sg * (1 + g * (1 - sg)), dA * g * sg])
+        dhb = _round_bf16(dh.astype(np.float32))
+        dx[t] += _deq(dhb[None, :])[0] @ W1c[e].T
+        dyw = _bf16_value(_round_bf16((w[t, j] * _bf16_value(dy[t])).astype(np.float32)))
+        rows[e].append((_bf16_value(dhb), ab, dyw, _bf16_value(x[t])))
+    dW1 = np.zeros((E, twoI, H))
+    dW2 = np.zeros((E, H, I))
+    for e, rs in rows.items():
+        if not rs:
+            continue
+        DH, A, DYW, XG = (np.stack([r[q] for r in rs]) for q in range(4))
+        dW1[e] = _deq_cols(DH).T @ _deq_cols(XG)
+        dW2[e] = _deq_cols(DYW).T @ _deq_cols(A)
+    return dx, dw, dW1, dW2
+
+
+def test_mx_backward_tokens_against_numpy():
+    x, w1, w2, dy, idx, w = _bwd_setup(21)
+    T, E, k = x.shape[0], w1.shape[0], idx.shape[1]
+    ops = oracle.MxBackwardOperands(x, w1, w2, dy)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    logits = np.random.default_rng(4).normal(0, 1, (T, E))
+    # softmax router, no renorm, no aux: dp at the chosen experts is dw itself
+    dx, dl = oracle.mx_backward_tokens(ops, None, logits, idx, counts, w, score=oracle.SOFTMAX,
+                                       renorm=False, scale=1.0, coeff=0.0, d_aux=0.0)
+    dx_ref, dw_ref, _, _ = _numpy_mx_backward(x, w1, w2, dy, idx, w)
+    assert np.allclose(dx, dx_ref, rtol=1e-9, atol=1e-12)
+    p = scipy.special.softmax(logits, axis=1)
+    dp = np.zeros((T, E))
+    np.put_along_axis(dp, idx.astype(np.int64), dw_ref, axis=1)
+    dl_ref = p * (dp - (dp * p).sum(1, keepdims=True))
+    assert np.allclose(dl, dl_ref, rtol=1e-9, atol=1e-12)
+
+
+def test_mx_weight_grad_elements_against_numpy():
+    x, w1, w2, dy, idx, w = _bwd_setup(22, T=40, E=3, k=2)     # ~27 rows per expert: a ragged block
+    E, twoI, H = w1.shape
+    I = twoI // 2
+    ops = oracle.MxBackwardOperands(x, w1, w2, dy)
+    _, _, dW1, dW2 = _numpy_mx_backward(x, w1, w2, dy, idx, w)
+    rng = np.random.default_rng(5)
+    which, ee, rr, cc = [], [], [], []
+    for e in range(E):
+        for wh, nr, nc in ((1, twoI, H), (2, H, I)):
+            which += [wh] * 16
+            ee += [e] * 16
+            rr += rng.integers(0, nr, 16).tolist()
+            cc += rng.integers(0, nc, 16).tolist()
+    got = oracle.mx_weight_grad_elements(ops, x, dy, idx, w, which, ee, rr, cc)
+    which, ee, rr, cc = map(np.array, (which, ee, rr, cc))
+    ref = np.where(which == 1, dW1[ee, np.minimum(rr, twoI - 1), np.minimum(cc, H - 1)],
+                   dW2[ee, np.minimum(rr, H - 1), np.minimum(cc, I - 1)])
+    assert np.allclose(got, ref, rtol=1e-9, atol=1e-12)
+
+
+def test_mx_backward_within_the_format_error_of_the_exact_backward():
+    x, w1, w2, dy, idx, w = _bwd_setup(23, T=16, H=128, I=128, E=4, k=2)
+    T, E = x.shape[0], w1.shape[0]
+    ops = oracle.MxBackwardOperands(x, w1, w2, dy)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+    logits = np.random.default_rng(6).normal(0, 1, (T, E))
+    # the routing weights the bf16 oracle derives from the logits (softmax, no renorm)
+    w = np.take_along_axis(scipy.special.softmax(logits, axis=1), idx.astype(np.int64), axis=1)
+    kw = dict(score=oracle.SOFTMAX, renorm=False, scale=1.0, coeff=0.01, d_aux=1.0)
+    dx_mx, _ = oracle.mx_backward_tokens(ops, None, logits, idx, counts, w, **kw)
+    dx, _ = oracle.backward_tokens(x, None, logits, w1, w2, idx, counts, dy, **kw)
+    rel = np.linalg.norm(dx_mx - dx) / np.linalg.norm(dx)
+    assert 1e-3 < rel < 0.1, rel
