@@ -429,6 +429,33 @@ class MxBackwardOperands(MxOperands):
         return (_p(self.dyq), _p(self.dys), _p(self.w2cq), _p(self.w2cs), _p(self.w1cq),
                 _p(self.w1cs))
 
+    @classmethod
+    def from_experts(cls, x, dy, E, experts, w1_parts, w2_parts):
+        """Operands of a layer with E experts of which only `experts` are
+        given (w1_parts [n, 2I, H], w2_parts [n, H, I], bf16 bits); the
+        others stay zero.  The arrays have the full shapes, but np.zeros maps
+        untouched pages lazily, so only the given experts take memory.  For
+        outputs that read no other expert."""
+        x, dy = _c(x, np.uint16), _c(dy, np.uint16)
+        w1_parts, w2_parts = _c(w1_parts, np.uint16), _c(w2_parts, np.uint16)
+        n, twoI, H = w1_parts.shape
+        I = twoI // 2
+        self = cls.__new__(cls)
+        self.H, self.I, self.E = H, I, E
+        self.xq, self.xs = mx_quantize(x)
+        self.dyq, self.dys = mx_quantize(dy)
+        for name, rows, K in (("w1", twoI, H), ("w2", H, I), ("w2c", I, H), ("w1c", H, twoI)):
+            setattr(self, name + "q", np.zeros((E * rows, K), np.uint8))
+            setattr(self, name + "s", np.zeros((E * rows, K // 32), np.uint8))
+        for j, e in enumerate(np.asarray(experts).tolist()):
+            parts = (("w1", w1_parts[j]), ("w2", w2_parts[j]), ("w2c", w2_parts[j].T),
+                     ("w1c", w1_parts[j].T))
+            for name, m in parts:
+                q, sc = mx_quantize(np.ascontiguousarray(m))
+                getattr(self, name + "q")[e * m.shape[0]:(e + 1) * m.shape[0]] = q
+                getattr(self, name + "s")[e * m.shape[0]:(e + 1) * m.shape[0]] = sc
+        return self
+
 
 def mx_backward_tokens(ops: MxBackwardOperands, Wr, logits64, idx, counts, w, *, score, renorm,
                        scale, coeff, d_aux=1.0, toks=None):

@@ -860,8 +860,9 @@ void oracle_mx_forward(int32_t H, int32_t I, int32_t k, const uint8_t *xq, const
 /* Tensors are rounded to the precision the path holds them in before they   */
 /* are quantised: dh = bf16(fp32(dg | du)), dyw = bf16(fp32(w * dy)),        */
 /* a = bf16(fp32(a)); xg is the bf16 input x.  g, u, a come from the MXFP8   */
-/* forward (mx_slot).  The routing weight's gradient is the row-dot          */
-/* dw_j = sum_i dA'_i a_i with the bf16 a.                                   */
+/* forward (mx_slot); the SwiGLU backward takes g and u as the forward       */
+/* saves them, in h: bf16(fp32(g)), bf16(fp32(u)).  The routing weight's     */
+/* gradient is the row-dot dw_j = sum_i dA'_i a_i with the bf16 a.           */
 /* ======================================================================== */
 
 /* dA' of one slot (t, e): dAp[i] = sum_h DY[t,h] W2c[e*I+i, h]. */
@@ -928,7 +929,8 @@ void oracle_mx_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E, int32
                 dw[j] = acc;
                 for (int32_t i = 0; i < I; ++i) {
                     double dg, du;
-                    swiglu_bwd(w[t * k + j] * dAp[i], g[i], u[i], &dg, &du);
+                    /* g, u as the forward saved them: h in bf16 */
+                    swiglu_bwd(w[t * k + j] * dAp[i], bf16_of(g[i]), bf16_of(u[i]), &dg, &du);
                     dh[i] = bf16_of(dg);
                     dh[I + i] = bf16_of(du);
                 }
@@ -1016,7 +1018,7 @@ void oracle_mx_weight_grad_elements(int64_t T, int32_t H, int32_t I, int32_t k,
                 for (int32_t h = 0; h < H; ++h)
                     dAp += mx_value(dyq, dys, H, t, h) * mx_value(w2cq, w2cs, H, (int64_t)e * I + i, h);
                 double dg, du;
-                swiglu_bwd(w[f] * dAp, sg, su, &dg, &du);
+                swiglu_bwd(w[f] * dAp, bf16_of(sg), bf16_of(su), &dg, &du);
                 c1[r] = bf16_of(rr[q] < I ? dg : du);
                 c2[r] = bf(x[t * H + cc[q]]);
             }

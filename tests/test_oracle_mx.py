@@ -286,8 +286,11 @@ def _numpy_mx_backward(x, w1, w2, dy, idx, w):
         dAp = DYd[t] @ W2c[e].T
         dw[t, j] = dAp @ ab
         dA = w[t, j] * dAp
-        sg = scipy.special.expit(g)
-        dh = np.concatenate([dA * u * sg * (1 + g * (1 - sg)), dA * g * sg])
+        # the SwiGLU backward reads h as saved: g, u rounded to fp32, then bf16
+        gb = _bf16_value(_round_bf16(g.astype(np.float32)))
+        ub = _bf16_value(_round_bf16(u.astype(np.float32)))
+        sg = scipy.special.expit(gb)
+        dh = np.concatenate([dA * ub * sg * (1 + gb * (1 - sg)), dA * gb * sg])
         dhb = _round_bf16(dh.astype(np.float32))
         dx[t] += _deq(dhb[None, :])[0] @ W1c[e].T
         dyw = _bf16_value(_round_bf16((w[t, j] * _bf16_value(dy[t])).astype(np.float32)))
@@ -355,3 +358,23 @@ def test_mx_backward_within_the_format_error_of_the_exact_backward():
     dx, _ = oracle.backward_tokens(x, None, logits, w1, w2, idx, counts, dy, **kw)
     rel = np.linalg.norm(dx_mx - dx) / np.linalg.norm(dx)
     assert 1e-3 < rel < 0.1, rel
+
+
+def test_backward_operands_from_experts_match_full():
+    """The sparse-expert operands equal the full ones on the given experts and
+    are zero elsewhere (so outputs that read only those experts agree)."""
+    rng = np.random.default_rng(0)
+    T, H, I, E = 20, 64, 64, 4
+    bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x, dy = bits(rng.normal(0, 1, (T, H))), bits(rng.normal(0, 1, (T, H)))
+    w1, w2 = bits(rng.normal(0, .05, (E, 2 * I, H))), bits(rng.normal(0, .05, (E, H, I)))
+    full = oracle.MxBackwardOperands(x, w1, w2, dy)
+    ex = np.array([1, 3])
+    sp = oracle.MxBackwardOperands.from_experts(x, dy, E, ex, w1[ex], w2[ex])
+    for n in ("xq", "xs", "dyq", "dys"):
+        assert np.array_equal(getattr(full, n), getattr(sp, n)), n
+    for n, rows in (("w1", 2 * I), ("w2", H), ("w2c", I), ("w1c", H)):
+        for suf in "qs":
+            a = getattr(full, n + suf).reshape(E, rows, -1)
+            b = getattr(sp, n + suf).reshape(E, rows, -1)
+            assert np.array_equal(a[ex], b[ex]) and not b[[0, 2]].any(), n + suf
