@@ -40,12 +40,16 @@ GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_
 # kernel-name fragment of each grouped-GEMM op in a rocprofv3 trace
 GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k_down_dgrad<",
                 "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<",
-                "up_swiglu_mx": "k_up_swiglu_mx<", "down_mx": "k_down_mx<"}
+                "up_swiglu_mx": "k_up_swiglu_mx<", "down_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 64>, 1>",
+                "down_dgrad_mx": "k_down_dgrad_mx<",
+                "up_dgrad_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 64>, 3>",
+                "down_wgrad_mx": "k_wgrad_mx<", "up_wgrad_mx": "k_wgrad_mx<"}
 # The measured HBM traffic of the grouped GEMMs lives in this file, next to a
 # hash of the kernel sources it was taken with; a changed kernel reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
-                  for f in ("gemm.hip", "tile.h", "common.h", "swiglu_epi.h", "mxfmt.h", "mx.hip")]
+                  for f in ("gemm.hip", "tile.h", "common.h", "swiglu_epi.h", "bwd_epi.h", "mxfmt.h",
+                            "mx.hip")]
 COPY_BYTES = 1 << 30        # plain device copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
@@ -290,10 +294,11 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
     fetch, write = rows(fetch_dir, "FETCH_SIZE"), rows(write_dir, "WRITE_SIZE")
     kern = {}
     for stage, frag in GEMM_KERNELS.items():
-        want_up = stage == "up_wgrad"
+        want_up = stage.startswith("up_wgrad")
+        wgrad = stage.startswith(("down_wgrad", "up_wgrad"))
         def pick(rs):
             v = [x for _, n, x in rs if frag in n and
-                 (stage not in ("down_wgrad", "up_wgrad") or n.split(">")[-2].strip().endswith("true") == want_up)]
+                 (not wgrad or n.split(">")[-2].strip().endswith("true") == want_up)]
             return sum(v) / len(v) if v else None
         f, wr = pick(fetch), pick(write)
         if f is None or wr is None:

@@ -53,6 +53,9 @@ struct BwdWs {
     uint16_t *xg;
     uint16_t *dyw;
     void *router;  // router GEMM scratch (router_ws_bytes_bwd)
+    uint8_t *dymx;  // MXFP8 backward: MX matrix of dy [T, H]
+    uint8_t *dhmx;  // MXFP8 backward: MX matrix of dh [M, 2I]
+    uint8_t *segA, *segB;  // MXFP8 weight gradients: per-expert transposed operands
 };
 
 FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
@@ -89,6 +92,15 @@ BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
     w.xg = cv.take<uint16_t>(M * c.H);
     w.dyw = cv.take<uint16_t>(M * c.H);
     w.router = cv.take<char>((int64_t)router_ws_bytes_bwd(c.T, c.E, c.H));
+    w.dymx = cv.take<uint8_t>(mx_bytes(c.T, c.H));
+    w.dhmx = cv.take<uint8_t>(mx_bytes(M, 2 * (int64_t)c.I));
+    // per-expert MX matrices of the weight-gradient operands: rows R, K = the
+    // expert's rows padded to 128; sum over experts <= (M/128 + E) 128-row chunks
+    const int64_t chunks = M / 128 + c.E;
+    const int64_t ra = c.H > 2 * (int64_t)c.I ? c.H : 2 * (int64_t)c.I;
+    const int64_t rb = c.H > c.I ? c.H : c.I;
+    w.segA = cv.take<uint8_t>(ra * 132 * chunks);
+    w.segB = cv.take<uint8_t>(rb * 132 * chunks);
     if (bytes) *bytes = cv.used;
     return w;
 }
@@ -389,6 +401,15 @@ static moe_status check_saved(const moe_saved *s)
                        s->pos, s->h, s->a});
 }
 
+// The backward reads only counts and offsets of a forward over no tokens (the
+// other saved tensors are empty and may be NULL).
+static moe_status check_saved_bwd(const moe_saved *s, int64_t T)
+{
+    if (!s) return MOE_EINVAL;
+    if (T == 0) return check_ptrs({s->counts, s->offsets});
+    return check_saved(s);
+}
+
 static moe_gemm_args saved_gemm_args(const moe_saved *saved)
 {
     moe_gemm_args a;
@@ -622,16 +643,139 @@ moe_status moe_forward_mx(const moe_config *cfg, const uint16_t *x, const float 
     return moe_stage2_forward_mx(cfg, w2_mx, saved, y, ws, ws_bytes, stream);
 }
 
-moe_status moe_stage2_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
-                               const uint16_t *dy, void *dW2, int32_t dw_dtype,
-                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
-                               hipStream_t stream)
+static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
+                             const uint8_t *w2t_mx, const uint16_t *dy, void *dW2,
+                             int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                             const float *Wr, const uint16_t *w1, const uint8_t *w1t_mx,
+                             const float *d_aux, float *dx, float *dlogits, float *dWr, void *dW1,
+                             int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+moe_status moe_mx_quantize_t(const uint16_t *src, int64_t batches, int64_t R, int64_t C, void *dst,
+                             size_t dst_bytes, hipStream_t stream)
+{
+    if (batches < 0 || C <= 0 || C % 64 != 0) return MOE_EINVAL;
+    size_t need = 0;
+    MOE_CHECK(moe_mx_size(batches * C, R, &need));
+    if (batches == 0) return MOE_OK;
+    MOE_CHECK(check_ptrs({src, dst}));
+    if (dst_bytes < need) return MOE_EINVAL;
+    ColQuant q;
+    q.src = src;
+    q.C = C;
+    q.gather = nullptr;
+    q.gk = 1;
+    q.nseg = (int32_t)batches;
+    q.R = R;
+    q.offsets = nullptr;
+    q.mt128 = nullptr;
+    q.dst = (uint8_t *)dst;
+    StageMark mark(MOE_STAGE_MX_QUANT, stream);
+    MOE_TRY(launch_mx_quantize_cols(q, batches * (mx_kp(R) / MX_GROUP), stream));
+    return MOE_OK;
+}
+
+moe_status moe_stage2_backward_mx(const moe_config *cfg, const moe_saved *saved,
+                                  const void *w2t_mx, const uint16_t *dy, void *dW2,
+                                  int32_t dw_dtype, int32_t dw_accumulate, void *ws,
+                                  size_t ws_bytes, hipStream_t stream)
+{
+    if (!w2t_mx) return MOE_EINVAL;
+    return stage2_bwd(cfg, saved, nullptr, (const uint8_t *)w2t_mx, dy, dW2, dw_dtype,
+                      dw_accumulate, ws, ws_bytes, stream);
+}
+
+moe_status moe_stage1_backward_mx(const moe_config *cfg, const moe_saved *saved,
+                                  const uint16_t *x, const float *Wr, const void *w1t_mx,
+                                  const float *d_aux, float *dx, float *dlogits, float *dWr,
+                                  void *dW1, int32_t dw_dtype, int32_t dw_accumulate, void *ws,
+                                  size_t ws_bytes, hipStream_t stream)
+{
+    if (!w1t_mx) return MOE_EINVAL;
+    return stage1_bwd(cfg, saved, x, Wr, nullptr, (const uint8_t *)w1t_mx, d_aux, dx, dlogits,
+                      dWr, dW1, dw_dtype, dw_accumulate, ws, ws_bytes, stream);
+}
+
+moe_status moe_backward_mx(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                           const float *Wr, const void *w1t_mx, const void *w2t_mx,
+                           const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
+                           float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
+                           int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    // everything stage 1 validates, checked before stage 2 launches anything
+    MOE_CHECK(check_ptrs({w1t_mx, dW1}));
+    if (cfg->T > 0) MOE_CHECK(check_ptrs({x, dx, dlogits}));
+    MOE_CHECK(check_opt_ptr(Wr));
+    MOE_CHECK(check_opt_ptr(dWr));
+    MOE_CHECK(check_opt_ptr(d_aux));
+    MOE_CHECK(moe_stage2_backward_mx(cfg, saved, w2t_mx, dy, dW2, dw_dtype, dw_accumulate, ws,
+                                     ws_bytes, stream));
+    return moe_stage1_backward_mx(cfg, saved, x, Wr, w1t_mx, d_aux, dx, dlogits, dWr, dW1,
+                                  dw_dtype, dw_accumulate, ws, ws_bytes, stream);
+}
+
+// The backward stages in bf16 (w2 / w1) or MXFP8 (w2t_mx / w1t_mx: MX
+// matrices of w2[e]^T as [E*I, H] and w1[e]^T as [E*H, 2I]).
+static void set_mx_bwd(GemmArgs &g, const moe_config &c, const BwdWs &w)
+{
+    const int64_t M = c.T * c.k;
+    g.Hp = mx_kp(c.H);
+    g.Ip = mx_kp(c.I);
+    g.dyq = w.dymx;
+    g.dys = w.dymx + c.T * g.Hp;
+    g.dhq = w.dhmx;
+    g.dhs = w.dhmx + M * mx_kp(2 * (int64_t)c.I);
+    g.segA = w.segA;
+    g.segB = w.segB;
+}
+
+static hipError_t run_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
+{
+    StageMark mark(op, s);
+    if (!g.dw_acc && (op == MOE_GEMM_DOWN_WGRAD || op == MOE_GEMM_UP_WGRAD)) {
+        const bool up = op == MOE_GEMM_UP_WGRAD;
+        hipError_t e = launch_zero_empty(g.E, (int64_t)2 * g.I * g.H / (up ? 1 : 2), g.counts,
+                                         up ? g.dW1 : g.dW2, g.dw_bf16, s);
+        if (e != hipSuccess) return e;
+    }
+    if (g.T == 0) return hipSuccess;
+    return launch_mx_gemm(op, g, s);
+}
+
+// per-expert MX matrices of the transposes of a [M, C] sorted-row operand
+static hipError_t quantize_segments(const moe_config &c, const BwdWs &w, const Sched &sc,
+                                    const int32_t *offsets, const uint16_t *src, int64_t C,
+                                    const int32_t *gather, uint8_t *dst, hipStream_t s)
+{
+    ColQuant q;
+    q.src = src;
+    q.C = C;
+    q.gather = gather;
+    q.gk = c.k;
+    q.nseg = c.E;
+    q.R = 0;
+    q.offsets = offsets;
+    q.mt128 = sc.mt_off128;
+    q.dst = dst;
+    (void)w;
+    StageMark mark(MOE_STAGE_MX_QUANT, s);
+    return launch_mx_quantize_cols(q, c.T * c.k / 128 + c.E, s);
+}
+
+static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
+                             const uint8_t *w2t_mx, const uint16_t *dy, void *dW2,
+                             int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
     if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
-    MOE_CHECK(check_saved(saved));
-    MOE_CHECK(check_ptrs({w2, dy, dW2}));
+    MOE_CHECK(check_saved_bwd(saved, c.T));
+    MOE_CHECK(check_ptrs({w2t_mx ? (const void *)w2t_mx : (const void *)w2, dW2}));
+    if (c.T > 0) MOE_CHECK(check_ptrs({dy}));
     size_t need = 0;
     BwdWs w = carve_bwd(c, ws, &need);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
@@ -649,23 +793,42 @@ moe_status moe_stage2_backward(const moe_config *cfg, const moe_saved *saved, co
     g.dyw = w.dyw;
     MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, nullptr, dy,
                                nullptr, w.dyw, w.wrow, stream));
-    // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
-    if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
-    MOE_TRY(run_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
+    if (!w2t_mx) {
+        // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
+        if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
+        MOE_TRY(run_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
+        return MOE_OK;
+    }
+    set_mx_bwd(g, c, w);
+    g.w2cq = w2t_mx;
+    g.w2cs = w2t_mx + (int64_t)c.E * c.I * g.Hp;
+    if (c.T > 0) {
+        {
+            StageMark mark(MOE_STAGE_MX_QUANT, stream);
+            MOE_TRY(launch_mx_quantize(dy, c.T, c.H, w.dymx, stream));
+        }
+        MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
+        MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dyw, c.H, nullptr, w.segA,
+                                  stream));
+        MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, saved->a, c.I, nullptr, w.segB,
+                                  stream));
+    }
+    MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
     return MOE_OK;
 }
 
-moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
-                               const float *Wr, const uint16_t *w1, const float *d_aux, float *dx,
-                               float *dlogits, float *dWr, void *dW1, int32_t dw_dtype,
-                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
-                               hipStream_t stream)
+static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                             const float *Wr, const uint16_t *w1, const uint8_t *w1t_mx,
+                             const float *d_aux, float *dx, float *dlogits, float *dWr, void *dW1,
+                             int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
     if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
-    MOE_CHECK(check_saved(saved));
-    MOE_CHECK(check_ptrs({x, w1, dx, dlogits, dW1}));
+    MOE_CHECK(check_saved_bwd(saved, c.T));
+    MOE_CHECK(check_ptrs({w1t_mx ? (const void *)w1t_mx : (const void *)w1, dW1}));
+    if (c.T > 0) MOE_CHECK(check_ptrs({x, dx, dlogits}));
     MOE_CHECK(check_opt_ptr(Wr));
     MOE_CHECK(check_opt_ptr(dWr));
     MOE_CHECK(check_opt_ptr(d_aux));
@@ -684,11 +847,29 @@ moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, co
     a.dw_accumulate = dw_accumulate;
     GemmArgs g = gemm_args(c, a, w.sched);
     g.xg = w.xg;
-    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, x, nullptr,
-                               w.xg, nullptr, nullptr, stream));
-    // dgrad, then dW1
-    if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_UP_DGRAD, g, stream));
-    MOE_TRY(run_gemm(MOE_GEMM_UP_WGRAD, g, stream));
+    if (!w1t_mx) {
+        MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, x,
+                                   nullptr, w.xg, nullptr, nullptr, stream));
+        // dgrad, then dW1
+        if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_UP_DGRAD, g, stream));
+        MOE_TRY(run_gemm(MOE_GEMM_UP_WGRAD, g, stream));
+    } else {
+        set_mx_bwd(g, c, w);
+        g.w1cq = w1t_mx;
+        g.w1cs = w1t_mx + (int64_t)c.E * c.H * mx_kp(2 * (int64_t)c.I);
+        if (c.T > 0) {
+            {
+                StageMark mark(MOE_STAGE_MX_QUANT, stream);
+                MOE_TRY(launch_mx_quantize(w.dh, c.T * c.k, 2 * (int64_t)c.I, w.dhmx, stream));
+            }
+            MOE_TRY(run_mx_gemm(MOE_GEMM_UP_DGRAD, g, stream));
+            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I,
+                                      nullptr, w.segA, stream));
+            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, x, c.H, saved->row_map,
+                                      w.segB, stream));
+        }
+        MOE_TRY(run_mx_gemm(MOE_GEMM_UP_WGRAD, g, stream));
+    }
     if (c.T == 0) {
         if (dWr && Wr) MOE_TRY(launch_fill_f32(dWr, (int64_t)c.E * c.H, 0.f, stream));
         return MOE_OK;
@@ -727,6 +908,25 @@ moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, co
     return MOE_OK;
 }
 
+moe_status moe_stage2_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
+                               const uint16_t *dy, void *dW2, int32_t dw_dtype,
+                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                               hipStream_t stream)
+{
+    return stage2_bwd(cfg, saved, w2, nullptr, dy, dW2, dw_dtype, dw_accumulate, ws, ws_bytes,
+                      stream);
+}
+
+moe_status moe_stage1_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                               const float *Wr, const uint16_t *w1, const float *d_aux, float *dx,
+                               float *dlogits, float *dWr, void *dW1, int32_t dw_dtype,
+                               int32_t dw_accumulate, void *ws, size_t ws_bytes,
+                               hipStream_t stream)
+{
+    return stage1_bwd(cfg, saved, x, Wr, w1, nullptr, d_aux, dx, dlogits, dWr, dW1, dw_dtype,
+                      dw_accumulate, ws, ws_bytes, stream);
+}
+
 moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
                         const float *Wr, const uint16_t *w1, const uint16_t *w2,
                         const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
@@ -735,7 +935,8 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
 {
     MOE_CHECK(moe_check_config(cfg));
     // everything stage 1 validates, checked before stage 2 launches anything
-    MOE_CHECK(check_ptrs({x, w1, dx, dlogits, dW1}));
+    MOE_CHECK(check_ptrs({w1, dW1}));
+    if (cfg->T > 0) MOE_CHECK(check_ptrs({x, dx, dlogits}));
     MOE_CHECK(check_opt_ptr(Wr));
     MOE_CHECK(check_opt_ptr(dWr));
     MOE_CHECK(check_opt_ptr(d_aux));

@@ -133,6 +133,13 @@ struct GemmArgs {
     const uint8_t *xq, *xs, *w1q, *w1s, *w2q, *w2s;
     uint8_t *aq, *as_;
     int64_t Hp, Ip;
+    // MXFP8 backward: MX matrices of dy [T, Hp], dh [M, 2Ip], w2^T per expert
+    // [E*I, Hp] and w1^T per expert [E*H, 2Ip]; for the weight gradients, the
+    // per-expert MX matrices of the two operands transposed (segA: rows of
+    // dW, segB: its columns; expert e at R * 132 * mt_off128[e] bytes, R the
+    // operand's row count, K = its routed rows padded to 128)
+    const uint8_t *dyq, *dys, *dhq, *dhs, *w2cq, *w2cs, *w1cq, *w1cs;
+    const uint8_t *segA, *segB;
 };
 int32_t dgrad2_cols(int32_t I);
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
@@ -142,6 +149,24 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint8_t *dst,
                               hipStream_t s);
 hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
+// MXFP8: the transposes of column segments of a bf16 matrix src (row stride
+// C elements, C % 64 == 0) as MX matrices along the segment's rows.  Either
+// nseg uniform segments of R rows, written as one MX matrix [nseg*C, Rp]
+// (offsets == NULL), or the E expert segments of sorted rows given by
+// offsets / mt128 (the 128-row m-tile prefix sums), each its own MX matrix
+// [C, Kp_e] at C * 132 * mt128[e] bytes; gather (optional) maps a sorted row
+// r to source row gather[r] / gk.  max_chunks bounds the 128-row chunks.
+struct ColQuant {
+    const uint16_t *src;
+    int64_t C;
+    const int32_t *gather;
+    int32_t gk;
+    int32_t nseg;
+    int64_t R;
+    const int32_t *offsets, *mt128;
+    uint8_t *dst;
+};
+hipError_t launch_mx_quantize_cols(const ColQuant &q, int64_t max_chunks, hipStream_t s);
 // zero the weight gradient of every expert without rows (overwrite mode)
 hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *counts, void *dW,
                              int32_t bf16, hipStream_t s);

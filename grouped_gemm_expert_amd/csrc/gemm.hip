@@ -22,6 +22,7 @@
 // (accumulate).  Block
 // indices are remapped so that each of the 8 XCDs works on a contiguous run
 // of tiles (neighbouring tiles share operand panels in that XCD's L2).
+#include "bwd_epi.h"
 #include "swiglu_epi.h"
 
 namespace moe {
@@ -142,66 +143,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     lb.init(w2e, I, n0, I, wave0, lane0);
     Acc<C> acc;
     mainloop<C, false, true, false>(lds, H, la, lb, acc);
-    // dA' leaves through the LDS staging tile; lane l then owns columns
-    // n0 + 4l .. n0 + 4l + 3 of a row: it loads h (gate, up) and a there,
-    // applies the routing weight and the SwiGLU backward, stores dh, and the
-    // wave sums dA'.a over the tile's columns of the row (dw_part[m, nt]).
-    // The loads of RB rows are issued together (addresses clamped to valid
-    // rows) so that their latencies overlap.
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int64_t col = n0 + 4 * lane;
-    const bool cok = col < I;
-    const int64_t colc = cok ? col : 0;
-    constexpr int NW = C::NT / 64, RB = 4;
-    static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
-#pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
-        if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
-        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
-        __syncthreads();
-        for (int r0 = wave; r0 < EPI_ROWS; r0 += RB * NW) {
-            uint64_t hg[RB], hu[RB], hv[RB];
-            float wgt[RB];
-            f32x4_t dap[RB];
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int r = r0 + b * NW;
-                int64_t m = t.m0 + half * EPI_ROWS + r;
-                if (m >= t.seg_end) m = t.seg_end - 1;
-                hg[b] = *(const uint64_t *)(g.h + m * 2 * I + colc);
-                hu[b] = *(const uint64_t *)(g.h + m * 2 * I + I + colc);
-                hv[b] = *(const uint64_t *)(g.a + m * I + colc);
-                wgt[b] = g.wrow[m];
-                dap[b] = epi_read_f32(lds, r, lane);
-            }
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
-                if (m >= t.seg_end) break;
-                float gv[4], uv[4], av[4], dg[4], du[4];
-                unpack_bf4(hg[b], gv);
-                unpack_bf4(hu[b], uv);
-                unpack_bf4(hv[b], av);
-                float part = 0.f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    part += dap[b][q] * av[q];
-                    const float da = wgt[b] * dap[b][q];
-                    const float sg = sigmoidf_(gv[q]);
-                    dg[q] = da * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-                    du[q] = da * gv[q] * sg;
-                }
-                if (cok) {
-                    *(uint64_t *)(g.dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
-                    *(uint64_t *)(g.dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
-                }
-                part = wave_sum(cok ? part : 0.f);
-                if (lane == 0) g.dw_part[m * nN + t.nt] = part;
-            }
-        }
-        __syncthreads();
-    }
+    dgrad2_epilogue<C>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
 }
 
 // =========================================================================
@@ -270,9 +212,7 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     const int64_t seg0 = g.offsets[e], seg1 = g.offsets[e + 1];
     const int64_t cnt = seg1 - seg0;
     const int64_t r0 = (int64_t)rt * C::BM, c0 = (int64_t)ct * C::BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int lane = threadIdx.x & 63;
     const int64_t dW_off = (int64_t)e * R * Cc;
     void *dWv = UP ? g.dW1 : g.dW2;
     // Operands are row-major per sorted row: A rows of length R, B rows of
@@ -286,53 +226,7 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     lb.init(Bb, Cc, c0, Cc, wave_uniform_id(), lane);
     Acc<C> acc;
     mainloop<C, true, true, true>(lds, cnt, la, lb, acc);
-    // out through the LDS staging tile, whole rows of dW at a time; in
-    // accumulate mode the old values of RB rows are loaded together
-    const int64_t cc = c0 + 4 * lane;
-    const bool cok = cc < Cc;
-    const int64_t ccc = cok ? cc : 0;
-    constexpr int NW = C::NT / 64, RB = 4;
-    static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
-#pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
-        if (r0 + half * EPI_ROWS >= R) break;
-        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
-        __syncthreads();
-        for (int rb = wave; rb < EPI_ROWS; rb += RB * NW) {
-            f32x4_t v[RB], old[RB];
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int r = rb + b * NW;
-                int64_t rr = r0 + half * EPI_ROWS + r;
-                if (rr >= R) rr = R - 1;
-                const int64_t o = dW_off + rr * Cc + ccc;
-                v[b] = epi_read_f32(lds, r, lane);
-                old[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (g.dw_acc) {
-                    if (g.dw_bf16) {
-                        float t4[4];
-                        unpack_bf4(*(const uint64_t *)((const uint16_t *)dWv + o), t4);
-                        old[b] = f32x4_t{t4[0], t4[1], t4[2], t4[3]};
-                    } else {
-                        old[b] = *(const f32x4_t *)((const float *)dWv + o);
-                    }
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
-                if (rr >= R) break;
-                if (!cok) continue;
-                const int64_t o = dW_off + rr * Cc + cc;
-                const f32x4_t w = v[b] + old[b];
-                if (g.dw_bf16)
-                    *(uint64_t *)((uint16_t *)dWv + o) = pack_bf4(w[0], w[1], w[2], w[3]);
-                else
-                    *(f32x4_t *)((float *)dWv + o) = w;
-            }
-        }
-        __syncthreads();
-    }
+    wgrad_epilogue<C>(acc, lds, r0, c0, R, Cc, dW_off, dWv, g.dw_acc, g.dw_bf16);
 }
 
 // ---------------------------------------------------------- empty experts ----

@@ -6,11 +6,22 @@
 // parameters stay bf16 and their quantised copies are cached.)
 //
 // Forward kernels:
-//   k_up_swiglu_mx  h = X . W1[e]^T from the MX forms of x (token rows,
-//                   gathered through row_map) and w1; SwiGLU from the fp32
-//                   accumulators; writes h and a (bf16) and a's MX form.
-//   k_down_mx       o = A . W2[e]^T from the MX forms of a and w2 (fp32 out).
-// Both operands are K-major, so the tiles reuse the bf16 kernels' [rows][128 B]
+//   k_up_swiglu_mx   h = X . W1[e]^T from the MX forms of x (token rows,
+//                    gathered through row_map) and w1; SwiGLU from the fp32
+//                    accumulators; writes h and a (bf16) and a's MX form.
+//   k_rows_mx<DOWN>  o = A . W2[e]^T from the MX forms of a and w2 (fp32 out).
+// Backward kernels (the data gradients take the transposed weights' MX forms,
+// w2[e]^T along H and w1[e]^T along 2I, which the weight cache keeps):
+//   k_down_dgrad_mx  dA' = dY[tok] . W2[e] from dy's MX form (token rows) and
+//                    w2^T's; the SwiGLU backward, the routing-weight row-dots
+//                    and dh (bf16) in the bf16 kernel's epilogue.
+//   k_rows_mx<UP_DGRAD>  dxp = dH . W1[e] from dh's MX form and w1^T's.
+//   k_wgrad_mx       dW2[e] = (w dY)^T A and dW1[e] = dH^T X: both operands are
+//                    the transposes of sorted-row matrices, quantised along the
+//                    expert's rows (k_mx_quantize_cols: one MX matrix per
+//                    expert, K = its rows padded to 128, 32-row blocks from
+//                    the expert's first row).
+// Every operand is K-major, so the tiles reuse the bf16 kernels' [rows][128 B]
 // swizzled LDS layout and direct global->LDS copies: a 128-byte row slice is
 // 128 fp8 of k here (one scale group, two MFMA k-steps) instead of 64 bf16,
 // so every copy still moves whole 128-byte lines.  (Stages of 64 fp8 in a
@@ -29,6 +40,7 @@
 // a group stored as blocks 0, 2, 1, 3, half g reads the 16-bit word at byte
 // 2g of the row's 4 scale bytes: low byte for step 0, high byte for step 1
 // (selected by the instruction's op_sel).
+#include "bwd_epi.h"
 #include "swiglu_epi.h"
 
 namespace moe {
@@ -74,6 +86,90 @@ hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint
     const int64_t groups = rows * (Kp / MX_GROUP);
     hipLaunchKernelGGL(k_mx_quantize, dim3((unsigned)ceil_div(groups, 16)), dim3(256), 0, s, src,
                        rows, K, Kp, dst, dst + rows * Kp);
+    return hipGetLastError();
+}
+
+// Column quantiser: a block takes 128 rows (one scale group of the output's
+// k) by 64 columns of a segment into LDS, then each thread quantises one
+// (column, 32-row block): 32 codes, contiguous in the output row of that
+// column, and its scale, gathered through LDS into the group's word.
+__global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tile[128][64];
+    __shared__ uint32_t sc[4][64];
+    const int nct = (int)(q.C / 64);
+    const int64_t L = blockIdx.x / nct;
+    const int ct = blockIdx.x % nct;
+    int64_t j, r0, len, Kp, rowbase;
+    uint8_t *codes, *scales;
+    if (!q.offsets) {
+        Kp = ceil_div(q.R, MX_GROUP) * MX_GROUP;
+        const int64_t per = Kp / MX_GROUP;
+        if (L >= (int64_t)q.nseg * per) return;
+        const int64_t sg = L / per;
+        j = L % per;
+        r0 = sg * q.R + j * MX_GROUP;
+        len = q.R - j * MX_GROUP < MX_GROUP ? q.R - j * MX_GROUP : MX_GROUP;
+        rowbase = sg * q.C;
+        codes = q.dst;
+        scales = q.dst + (int64_t)q.nseg * q.C * Kp;
+    } else {
+        if (L >= q.mt128[q.nseg]) return;
+        int lo = 0, hi = q.nseg;  // largest e with mt128[e] <= L
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (q.mt128[mid] <= L) lo = mid; else hi = mid;
+        }
+        j = L - q.mt128[lo];
+        r0 = q.offsets[lo] + j * MX_GROUP;
+        const int64_t rem = q.offsets[lo + 1] - r0;
+        len = rem < MX_GROUP ? rem : MX_GROUP;
+        Kp = (int64_t)MX_GROUP * (q.mt128[lo + 1] - q.mt128[lo]);
+        rowbase = 0;
+        codes = q.dst + q.C * 132 * (int64_t)q.mt128[lo];
+        scales = codes + q.C * Kp;
+    }
+    const int t = threadIdx.x;
+    for (int i = t; i < 128 * 8; i += 256) {
+        const int r = i >> 3, qd = i & 7;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (r < len) {
+            int64_t sr = r0 + r;
+            if (q.gather) sr = q.gather[sr] / q.gk;
+            v = *(const u32x4_t *)(q.src + sr * q.C + ct * 64 + qd * 8);
+        }
+        *(u32x4_t *)&tile[r][qd * 8] = v;
+    }
+    __syncthreads();
+    const int c = t & 63, b = t >> 6;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = bf2f(tile[32 * b + i][c]);
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    const int X = mx_block_exp(amax);
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i >> 2] |= e4m3_code(v[i], X) << (8 * (i & 3));
+    const int64_t orow = rowbase + ct * 64 + c;
+    uint8_t *dstc = codes + orow * Kp + j * MX_GROUP + b * 32;
+    *(u32x4_t *)dstc = u32x4_t{w[0], w[1], w[2], w[3]};
+    *(u32x4_t *)(dstc + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+    sc[b][c] = (uint32_t)(X + 127);
+    __syncthreads();
+    if (b == 0) {
+        const uint32_t word = sc[0][c] | (sc[2][c] << 8) | (sc[1][c] << 16) | (sc[3][c] << 24);
+        *(uint32_t *)(scales + mx_scale_off(orow, j, Kp / MX_GROUP)) = word;
+    }
+}
+
+hipError_t launch_mx_quantize_cols(const ColQuant &q, int64_t max_chunks, hipStream_t s)
+{
+    const int64_t blocks = max_chunks * (q.C / 64);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_mx_quantize_cols, dim3((unsigned)blocks), dim3(256), 0, s, q);
     return hipGetLastError();
 }
 
@@ -300,72 +396,214 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu_mx(GemmArgs g)
     swiglu_epilogue<C, true>(acc, lds, t, i0, I, g.h, g.a, g.aq, g.as_, g.Ip);
 }
 
-// =========================================================================
-// GEMM2 (MXFP8):  o[r, c] = A[r] . W2[e, c, :]   (fp32 out)
-// =========================================================================
+// The main loop of an MX tile: stages of 128 k from the two loaders, the
+// scale copies from the per-lane scale rows sp (one per scale block the wave
+// copies; the stage adds its group's 128-byte line).
 template <class C>
-__global__ __launch_bounds__(C::NT) void k_down_mx(GemmArgs g)
+MOE_DEV void mx_mainloop(lds_t *lds, int nst, const KLoad<C::BM, C::NT> &la,
+                         const KLoad<C::BN, C::NT> &lb, const uint8_t *const (&sp)[C::NS],
+                         int wave0, Acc<C> &acc)
 {
-    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
-    lds_t *lds = (lds_t *)lds_raw;
-    const int H = g.H;
-    const int64_t Ip = g.Ip;
-    const int nN = (int)ceil_div(H, C::BN);
-    MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
-    const int lane0 = threadIdx.x & 63, wave0 = wave_uniform_id();
-    KLoad<C::BM, C::NT> la;
-    KLoad<C::BN, C::NT> lb;
-    la.init(g.aq, wave0);
-    lb.init(g.w2q + (int64_t)t.e * H * Ip, wave0);
-    const int64_t n0 = (int64_t)t.nt * C::BN;
-    auto a_row = [&](int rr) {
-        int64_t m = t.m0 + rr;
-        return m < t.seg_end ? m : t.seg_end - 1;
-    };
-    auto w2_row = [&](int rr) {
-        int64_t n = n0 + rr;
-        return n < H ? n : (int64_t)H - 1;
-    };
-#pragma unroll
-    for (int q = 0; q < la.NI; ++q) la.set(q, lane0, (uint32_t)(a_row(la.row(q, lane0)) * Ip));
-#pragma unroll
-    for (int q = 0; q < lb.NI; ++q) lb.set(q, lane0, (uint32_t)(w2_row(lb.row(q, lane0)) * Ip));
-    const uint8_t *sp[C::NS];
-#pragma unroll
-    for (int q = 0; q < C::NS; ++q) {
-        const int sr = scale_row<C>(wave0, q, lane0);
-        sp[q] = lane0 < 32 ? g.as_ + mx_scale_off(a_row(sr), 0, Ip / MX_GROUP)
-                           : g.w2s + mx_scale_off((int64_t)t.e * H + w2_row(sr), 0, Ip / MX_GROUP);
-    }
-    Acc<C> acc;
     mx_pipeline<C, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
-        lds, (int)(Ip / MX_GROUP),
-        [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * 64, 0, la.base); },
+        lds, nst, [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * 64, 0, la.base); },
         [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * 64, 0, lb.base); },
         [&](int q, int s, lds_t *Ss) {
             copy4_to_lds(sp[q] + s * 128, Ss + (wave0 * C::NS + q) * 256);
         },
         acc);
-    store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
+}
+
+// =========================================================================
+// Sorted rows against per-expert weight rows, fp32 out:
+//   DOWN       o[r, c]   = A[r] . W2[e, c, :]       (A: a's MX matrix, K = I)
+//   UP_DGRAD   dxp[r, c] = DH[r] . W1[e, :, c]      (DH: dh's MX matrix, B:
+//              w1[e]^T's rows e*H + c, K = 2I)
+// =========================================================================
+template <class C, int OP>
+__global__ __launch_bounds__(C::NT) void k_rows_mx(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
+    constexpr bool DN = OP == MOE_GEMM_DOWN;
+    const int N = g.H;
+    const int64_t Kp = DN ? g.Ip : mx_kp(2 * (int64_t)g.I);
+    const uint8_t *aq = DN ? g.aq : g.dhq, *as_ = DN ? g.as_ : g.dhs;
+    const uint8_t *bq = DN ? g.w2q : g.w1cq, *bs = DN ? g.w2s : g.w1cs;
+    float *out = DN ? g.o : g.dxp;
+    const int nN = (int)ceil_div(N, C::BN);
+    MTile t;
+    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    const int lane0 = threadIdx.x & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(aq, wave0);
+    lb.init(bq + (int64_t)t.e * N * Kp, wave0);
+    const int64_t n0 = (int64_t)t.nt * C::BN;
+    auto a_row = [&](int rr) {
+        int64_t m = t.m0 + rr;
+        return m < t.seg_end ? m : t.seg_end - 1;
+    };
+    auto b_row = [&](int rr) {
+        int64_t n = n0 + rr;
+        return n < N ? n : (int64_t)N - 1;
+    };
+#pragma unroll
+    for (int q = 0; q < la.NI; ++q) la.set(q, lane0, (uint32_t)(a_row(la.row(q, lane0)) * Kp));
+#pragma unroll
+    for (int q = 0; q < lb.NI; ++q) lb.set(q, lane0, (uint32_t)(b_row(lb.row(q, lane0)) * Kp));
+    const uint8_t *sp[C::NS];
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const int sr = scale_row<C>(wave0, q, lane0);
+        sp[q] = lane0 < 32 ? as_ + mx_scale_off(a_row(sr), 0, Kp / MX_GROUP)
+                           : bs + mx_scale_off((int64_t)t.e * N + b_row(sr), 0, Kp / MX_GROUP);
+    }
+    Acc<C> acc;
+    mx_mainloop<C>(lds, (int)(Kp / MX_GROUP), la, lb, sp, wave0, acc);
+    store_tile_f32<C>(acc, lds, out, t.m0, t.seg_end, n0, N);
+}
+
+// =========================================================================
+// dgrad of GEMM2 (MXFP8) + row-dot + SwiGLU backward:
+//   dA'[r, i] = DY[tok(r)] . W2[e, :, i]   (DY: dy's MX matrix along H,
+//   B: w2[e]^T's rows e*I + i, K = H); epilogue as the bf16 kernel's
+// =========================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_down_dgrad_mx(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
+    const int I = g.I;
+    const int64_t Hp = g.Hp;
+    const int nN = (int)ceil_div(I, C::BN);
+    MTile t;
+    if (!decode_mtile<C::BM>(blockIdx.x, g.sched.mt_off256, g.offsets, g.E, nN, t)) return;
+    const int lane0 = threadIdx.x & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(g.dyq, wave0);
+    lb.init(g.w2cq + (int64_t)t.e * I * Hp, wave0);
+    const int64_t n0 = (int64_t)t.nt * C::BN;
+    auto tok_of = [&](int rr) {
+        int64_t m = t.m0 + rr;
+        if (m >= t.seg_end) m = t.seg_end - 1;
+        return (int64_t)(g.row_map[m] / g.k);
+    };
+    auto b_row = [&](int rr) {
+        int64_t n = n0 + rr;
+        return n < I ? n : (int64_t)I - 1;
+    };
+#pragma unroll
+    for (int q = 0; q < la.NI; ++q) la.set(q, lane0, (uint32_t)(tok_of(la.row(q, lane0)) * Hp));
+#pragma unroll
+    for (int q = 0; q < lb.NI; ++q) lb.set(q, lane0, (uint32_t)(b_row(lb.row(q, lane0)) * Hp));
+    const uint8_t *sp[C::NS];
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const int sr = scale_row<C>(wave0, q, lane0);
+        sp[q] = lane0 < 32 ? g.dys + mx_scale_off(tok_of(sr), 0, Hp / MX_GROUP)
+                           : g.w2cs + mx_scale_off((int64_t)t.e * I + b_row(sr), 0, Hp / MX_GROUP);
+    }
+    Acc<C> acc;
+    mx_mainloop<C>(lds, (int)(Hp / MX_GROUP), la, lb, sp, wave0, acc);
+    dgrad2_epilogue<C>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
+}
+
+// =========================================================================
+// Weight gradients (MXFP8), K-grouped over each expert's routed rows:
+//   DOWN:  dW2[e, hh, i] (+)= sum_r DYW[r, hh] A[r, i]
+//   UP:    dW1[e, n, hh] (+)= sum_r DH[r, n] XG[r, hh]
+// Both operands are the per-expert MX matrices of their transposes (rows =
+// the output's rows / columns, K = the expert's rows padded to 128), so the
+// tile is K-major on both sides like the forward ones.
+// =========================================================================
+template <class C, bool UP>
+__global__ __launch_bounds__(C::NT) void k_wgrad_mx(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    lds_t *lds = (lds_t *)lds_raw;
+    const int I = g.I, H = g.H;
+    const int R = UP ? 2 * I : H;   // output rows
+    const int Cc = UP ? H : I;      // output cols
+    const int nR = (int)ceil_div(R, C::BM), nC = (int)ceil_div(Cc, C::BN);
+    const int64_t tpe = (int64_t)nR * nC;
+    const int64_t total = (int64_t)g.sched.order[g.E] * tpe;  // non-empty experts only
+    const int64_t L = xcd_remap(blockIdx.x, total);
+    if (L < 0) return;
+    const int e = g.sched.order[L / tpe];
+    constexpr int GR = 4;  // groups of GR row tiles sweep all column tiles
+    const int64_t rest = L % tpe;
+    const int64_t grp = rest / ((int64_t)GR * nC);
+    const int64_t first = grp * GR;
+    const int64_t gr = nR - first < GR ? nR - first : GR;
+    const int64_t in = rest - grp * (int64_t)GR * nC;
+    const int rt = (int)(first + in % gr), ct = (int)(in / gr);
+    const int64_t r0 = (int64_t)rt * C::BM, c0 = (int64_t)ct * C::BN;
+    const int32_t *mt = g.sched.mt_off128;
+    const int64_t Kp = (int64_t)MX_GROUP * (mt[e + 1] - mt[e]);
+    const uint8_t *Aq = g.segA + (int64_t)R * 132 * mt[e], *As_ = Aq + (int64_t)R * Kp;
+    const uint8_t *Bq = g.segB + (int64_t)Cc * 132 * mt[e], *Bs_ = Bq + (int64_t)Cc * Kp;
+    const int lane0 = threadIdx.x & 63, wave0 = wave_uniform_id();
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(Aq, wave0);
+    lb.init(Bq, wave0);
+    auto a_row = [&](int rr) { return r0 + rr < R ? r0 + rr : (int64_t)R - 1; };
+    auto b_row = [&](int rr) { return c0 + rr < Cc ? c0 + rr : (int64_t)Cc - 1; };
+#pragma unroll
+    for (int q = 0; q < la.NI; ++q) la.set(q, lane0, (uint32_t)(a_row(la.row(q, lane0)) * Kp));
+#pragma unroll
+    for (int q = 0; q < lb.NI; ++q) lb.set(q, lane0, (uint32_t)(b_row(lb.row(q, lane0)) * Kp));
+    const uint8_t *sp[C::NS];
+#pragma unroll
+    for (int q = 0; q < C::NS; ++q) {
+        const int sr = scale_row<C>(wave0, q, lane0);
+        sp[q] = lane0 < 32 ? As_ + mx_scale_off(a_row(sr), 0, Kp / MX_GROUP)
+                           : Bs_ + mx_scale_off(b_row(sr), 0, Kp / MX_GROUP);
+    }
+    Acc<C> acc;
+    mx_mainloop<C>(lds, (int)(Kp / MX_GROUP), la, lb, sp, wave0, acc);
+    wgrad_epilogue<C>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2, g.dw_acc,
+                      g.dw_bf16);
 }
 
 hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
 {
     using C = MxTile;
-    if (op == MOE_GEMM_UP_SWIGLU) {
-        hipLaunchKernelGGL(k_up_swiglu_mx<C>,
-                           dim3((unsigned)mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2))),
-                           dim3(C::NT), 0, s, g);
-        return hipGetLastError();
+    auto mgrid = [&](int64_t ncols, int per) {
+        return dim3((unsigned)mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(ncols, per)));
+    };
+    auto wgrid = [&](int64_t R, int64_t Cc) {
+        const int64_t tiles = ceil_div(R, C::BM) * ceil_div(Cc, C::BN);
+        return dim3((unsigned)grid_for(tiles * g.E));
+    };
+    switch (op) {
+    case MOE_GEMM_UP_SWIGLU:
+        hipLaunchKernelGGL(k_up_swiglu_mx<C>, mgrid(g.I, C::BN / 2), dim3(C::NT), 0, s, g);
+        break;
+    case MOE_GEMM_DOWN:
+        hipLaunchKernelGGL((k_rows_mx<C, MOE_GEMM_DOWN>), mgrid(g.H, C::BN), dim3(C::NT), 0, s, g);
+        break;
+    case MOE_GEMM_DOWN_DGRAD:
+        // the router backward reads dgrad2_cols(I) row-dot partials per row
+        if (ceil_div(g.I, C::BN) != dgrad2_cols(g.I)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_down_dgrad_mx<C>, mgrid(g.I, C::BN), dim3(C::NT), 0, s, g);
+        break;
+    case MOE_GEMM_UP_DGRAD:
+        hipLaunchKernelGGL((k_rows_mx<C, MOE_GEMM_UP_DGRAD>), mgrid(g.H, C::BN), dim3(C::NT), 0, s,
+                           g);
+        break;
+    case MOE_GEMM_DOWN_WGRAD:
+        hipLaunchKernelGGL((k_wgrad_mx<C, false>), wgrid(g.H, g.I), dim3(C::NT), 0, s, g);
+        break;
+    case MOE_GEMM_UP_WGRAD:
+        hipLaunchKernelGGL((k_wgrad_mx<C, true>), wgrid(2 * (int64_t)g.I, g.H), dim3(C::NT), 0, s,
+                           g);
+        break;
+    default:
+        return hipErrorInvalidValue;
     }
-    if (op == MOE_GEMM_DOWN) {
-        hipLaunchKernelGGL(k_down_mx<C>,
-                           dim3((unsigned)mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN))),
-                           dim3(C::NT), 0, s, g);
-        return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace moe

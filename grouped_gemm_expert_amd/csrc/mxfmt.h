@@ -22,7 +22,7 @@ namespace moe {
 
 constexpr int MX_GROUP = 128;  // columns per scale word
 
-inline int64_t mx_kp(int64_t K) { return (K + MX_GROUP - 1) / MX_GROUP * MX_GROUP; }
+__host__ __device__ inline int64_t mx_kp(int64_t K) { return (K + MX_GROUP - 1) / MX_GROUP * MX_GROUP; }
 
 // Byte offset of the scale word of (row, group) in the scale area, gpr =
 // Kp / 128 groups per row.

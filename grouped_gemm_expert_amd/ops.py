@@ -114,6 +114,14 @@ def _load():
     lib.moe_stage2_forward_mx.restype = S
     lib.moe_forward_mx.argtypes = [CFG] + [_P] * 7 + [SP, _P, sz, _P]
     lib.moe_forward_mx.restype = S
+    lib.moe_mx_quantize_t.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, sz, _P]
+    lib.moe_mx_quantize_t.restype = S
+    lib.moe_stage2_backward_mx.argtypes = [CFG, SP, _P, _P, _P, I32, I32, _P, sz, _P]
+    lib.moe_stage2_backward_mx.restype = S
+    lib.moe_stage1_backward_mx.argtypes = [CFG, SP] + [_P] * 8 + [I32, I32, _P, sz, _P]
+    lib.moe_stage1_backward_mx.restype = S
+    lib.moe_backward_mx.argtypes = [CFG, SP] + [_P] * 11 + [I32, I32, _P, sz, _P]
+    lib.moe_backward_mx.restype = S
     return lib
 
 
@@ -124,7 +132,8 @@ SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspac
            "moe_combine", "moe_forward", "moe_backward", "moe_stage1_forward",
            "moe_stage2_forward", "moe_stage2_backward", "moe_stage1_backward",
            "moe_set_stage_events", "moe_grouped_gemm_mx", "moe_mx_size", "moe_mx_quantize", "moe_stage1_forward_mx",
-           "moe_stage2_forward_mx", "moe_forward_mx")
+           "moe_stage2_forward_mx", "moe_forward_mx", "moe_mx_quantize_t",
+           "moe_stage2_backward_mx", "moe_stage1_backward_mx", "moe_backward_mx")
 
 STAGES = {"up_swiglu": 0, "down": 1, "down_dgrad": 2, "up_dgrad": 3, "down_wgrad": 4,
           "up_wgrad": 5, "router_proj": 6, "router": 7, "permute": 8, "combine": 9,
@@ -350,18 +359,32 @@ def moe_mx_quantize(src: torch.Tensor, dst: torch.Tensor, stream=None):
            "moe_mx_quantize")
 
 
+def moe_mx_quantize_t(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """MX matrix of every batch's transpose of src [batches, R, C] (bf16),
+    stacked as [batches*C, R] along R, into dst (moe_mx_size bytes)."""
+    B, R, C = src.shape
+    _check(_lib.moe_mx_quantize_t(_ptr(src), B, R, C, _ptr(dst), dst.numel(), _stream(stream)),
+           "moe_mx_quantize_t")
+
+
 class MxWeightCache:
-    """The MXFP8 forms of w1 and w2, rebuilt when either weight changes.
+    """The MXFP8 forms of w1 and w2, rebuilt when either weight changes: the
+    forward's (w1 along H, w2 along I) and, with backward=True, the
+    transposed ones the backward's data gradients use (w1[e]^T along 2I,
+    w2[e]^T along H).
 
     The key is each weight's storage, shape and in-place version counter; as
     with the pages' cache, that is not enough when an optimizer writes the
     weights without bumping the version, so `drop()` (once per optimizer step)
     forces the next `get` to quantise again."""
 
-    def __init__(self):
+    def __init__(self, backward: bool = False):
         self._key = None
+        self.backward = backward
         self.w1_mx = None
         self.w2_mx = None
+        self.w1t_mx = None
+        self.w2t_mx = None
         self.builds = 0
 
     @staticmethod
@@ -382,6 +405,13 @@ class MxWeightCache:
                 self.w2_mx = mx_alloc(E * H, I, w2.device)
             moe_mx_quantize(w1, self.w1_mx, stream)
             moe_mx_quantize(w2, self.w2_mx, stream)
+            if self.backward:
+                if self.w1t_mx is None or self.w1t_mx.numel() != moe_mx_size(E * H, twoI):
+                    self.w1t_mx = mx_alloc(E * H, twoI, w1.device)
+                if self.w2t_mx is None or self.w2t_mx.numel() != moe_mx_size(E * I, H):
+                    self.w2t_mx = mx_alloc(E * I, H, w2.device)
+                moe_mx_quantize_t(w1, self.w1t_mx, stream)
+                moe_mx_quantize_t(w2, self.w2t_mx, stream)
             self._key = key
             self.builds += 1
         return self.w1_mx, self.w2_mx
@@ -414,3 +444,34 @@ def moe_grouped_gemm_mx(op: int, cfg, *, ws, counts, offsets, row_map=None, x_mx
                                               h, a, o)])
     _check(_lib.moe_grouped_gemm_mx(int(op), ctypes.byref(cfg), ctypes.byref(args), _ptr(ws),
                                     ws.numel(), _stream(stream)), "moe_grouped_gemm_mx")
+
+
+def moe_backward_mx(cfg, saved: dict, x, Wr, w1t_mx, w2t_mx, dy, d_aux, dx, dlogits, dWr, dW1, dW2,
+                    ws, dw_accumulate=False, stream=None):
+    s = _saved_struct(saved)
+    dw_dtype = MOE_BF16 if dW1.dtype == torch.bfloat16 else MOE_F32
+    _check(_lib.moe_backward_mx(ctypes.byref(cfg), ctypes.byref(s), _ptr(x), _ptr(Wr),
+                                _ptr(w1t_mx), _ptr(w2t_mx), _ptr(dy), _ptr(d_aux), _ptr(dx),
+                                _ptr(dlogits), _ptr(dWr), _ptr(dW1), _ptr(dW2), dw_dtype,
+                                int(bool(dw_accumulate)), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_backward_mx")
+
+
+def moe_stage2_backward_mx(cfg, saved: dict, w2t_mx, dy, dW2, ws, dw_accumulate=False,
+                           stream=None):
+    s = _saved_struct(saved)
+    dw_dtype = MOE_BF16 if dW2.dtype == torch.bfloat16 else MOE_F32
+    _check(_lib.moe_stage2_backward_mx(ctypes.byref(cfg), ctypes.byref(s), _ptr(w2t_mx), _ptr(dy),
+                                       _ptr(dW2), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
+                                       ws.numel(), _stream(stream)), "moe_stage2_backward_mx")
+
+
+def moe_stage1_backward_mx(cfg, saved: dict, x, Wr, w1t_mx, d_aux, dx, dlogits, dWr, dW1, ws,
+                           dw_accumulate=False, stream=None):
+    s = _saved_struct(saved)
+    dw_dtype = MOE_BF16 if dW1.dtype == torch.bfloat16 else MOE_F32
+    _check(_lib.moe_stage1_backward_mx(ctypes.byref(cfg), ctypes.byref(s), _ptr(x), _ptr(Wr),
+                                       _ptr(w1t_mx), _ptr(d_aux), _ptr(dx), _ptr(dlogits),
+                                       _ptr(dWr), _ptr(dW1), dw_dtype, int(bool(dw_accumulate)),
+                                       _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_stage1_backward_mx")

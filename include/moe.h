@@ -386,6 +386,47 @@ typedef struct {
 
 moe_status moe_grouped_gemm_mx(int32_t op, const moe_config *cfg, const moe_gemm_mx_args *args,
                                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * MXFP8 backward (the same page: the backward of both expert stages and the
+ * dW1 / dW2 weight gradients in MXFP8).  Every GEMM takes MX operands
+ * quantised along its own contraction dimension:
+ *   dgrad of GEMM2: dy along H (per token) against w2[e]^T along H, then the
+ *                   epilogue of the bf16 path (SwiGLU backward from the saved
+ *                   h, routing weight, row-dots against the saved a; dh bf16);
+ *   dgrad of GEMM1: dh along 2I against w1[e]^T along 2I;
+ *   dW2[e], dW1[e]: both operands transposed and quantised down the expert's
+ *                   routed rows (blocks of 32 from its first sorted row, the
+ *                   last block padded with zeros): w*dy and a for dW2, dh and
+ *                   the gathered x for dW1.
+ * The router part, the un-permute and dWr are those of the bf16 backward.
+ * moe_mx_quantize_t  src [batches, R, C] bf16 -> the MX matrix of every
+ *                   batch's transpose, stacked: [batches*C, R] along R (C %
+ *                   64 == 0, R % 32 == 0; dst_bytes >= moe_mx_size(batches*C,
+ *                   R), MOE_EINVAL otherwise).  The transposed weights of the
+ *                   cache: w2 as [E, H, I] -> w2t_mx [E*I, H]; w1 as
+ *                   [E, 2I, H] -> w1t_mx [E*H, 2I].
+ * moe_stage2_backward_mx, moe_stage1_backward_mx, moe_backward_mx
+ *                   moe_stage2_backward / moe_stage1_backward / moe_backward
+ *                   with those GEMMs; arguments, order, workspace and errors
+ *                   as for the bf16 forms, w2t_mx / w1t_mx in place of w2 / w1.
+ */
+moe_status moe_mx_quantize_t(const uint16_t *src, int64_t batches, int64_t R, int64_t C, void *dst,
+                             size_t dst_bytes, hipStream_t stream);
+moe_status moe_stage2_backward_mx(const moe_config *cfg, const moe_saved *saved,
+                                  const void *w2t_mx, const uint16_t *dy, void *dW2,
+                                  int32_t dw_dtype, int32_t dw_accumulate, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
+moe_status moe_stage1_backward_mx(const moe_config *cfg, const moe_saved *saved,
+                                  const uint16_t *x, const float *Wr, const void *w1t_mx,
+                                  const float *d_aux, float *dx, float *dlogits, float *dWr,
+                                  void *dW1, int32_t dw_dtype, int32_t dw_accumulate, void *ws,
+                                  size_t ws_bytes, hipStream_t stream);
+moe_status moe_backward_mx(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
+                           const float *Wr, const void *w1t_mx, const void *w2t_mx,
+                           const uint16_t *dy, const float *d_aux, float *dx, float *dlogits,
+                           float *dWr, void *dW1, void *dW2, int32_t dw_dtype,
+                           int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream);
 moe_status moe_mx_size(int64_t rows, int64_t K, size_t *bytes);
 moe_status moe_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, void *dst,
                            size_t dst_bytes, hipStream_t stream);

@@ -26,6 +26,11 @@ GRAD_TOL = (3e-2, 1.5e-2)
 # bf16 inputs the same way, so only fp32 accumulation and rare one-step code
 # flips of a (from the kernel's fp32 SwiGLU value) separate them
 MX_FWD_TOL = (2e-2, 1e-3)
+# the MXFP8 backward against the oracle's MXFP8 backward: as for the forward,
+# only fp32 accumulation and rare one-step code flips (of dh, quantised from
+# the kernel's fp32 SwiGLU backward) separate them; measured relative
+# Frobenius errors stay below 2e-3
+MX_GRAD_TOL = (3e-2, 5e-3)
 
 
 def say(msg: str):

@@ -147,6 +147,17 @@ def test_zero_tokens_is_a_noop():
     torch.cuda.synchronize()
     assert float(aux.cpu()) == 0.0
     assert int(saved["counts"].sum()) == 0
+    # the backward of no tokens: every weight gradient is zero (overwrite mode)
+    dx = torch.empty((0, w.H), device="cuda")
+    dl = torch.empty((0, w.E), device="cuda")
+    dWr = torch.full((w.E, w.H), 5.0, device="cuda")
+    dW1 = torch.full((w.E, 2 * w.I, w.H), 5.0, device="cuda")
+    dW2 = torch.full((w.E, w.H, w.I), 5.0, device="cuda")
+    da = torch.ones((1,), device="cuda")
+    ops.moe_backward(cfg, saved, x, Wr, w1, w2, x, da, dx, dl, dWr, dW1, dW2,
+                     ops.workspace(cfg, "bwd"))
+    torch.cuda.synchronize()
+    assert not dW1.any() and not dW2.any() and not dWr.any()
 
 
 def test_accumulate_mode_and_bf16_weight_grads():

@@ -2,17 +2,19 @@
 8 groups, top-4 groups, top-8 sigmoid + bias, scale 2.5), in the launch
 configuration the benchmark times: moe_forward from the router weight, then
 moe_backward accumulating into zeroed fp32 weight gradients; and the MXFP8
-forward on the same inputs.  The oracle cannot run the whole layer at this
-size, so it is checked on sampled outputs that it computes one by one:
+forward and backward on the same inputs.  The oracle cannot run the whole
+layer at this size, so it is checked on sampled outputs that it computes one
+by one:
   - routing of every token (bit-exact on all tokens whose fp32 selection is
     not a near-tie under the projection's rounding),
   - y and dx of sampled tokens, sampled dW1 / dW2 elements of busy experts,
-  - the MX forward's y on sampled tokens against the oracle's MXFP8 forward.
+  - the MX forward's y, dx and dlogits on sampled tokens, and sampled MX dW1 /
+    dW2 elements, against the oracle's MXFP8 path.
 Only the experts the samples touch are copied to the host: into full-shape
 zero arrays (np.zeros maps untouched pages lazily, so only those experts take
-memory) for the bf16 oracle, which reads no other expert, and into compact
-arrays with remapped expert ids for the MXFP8 oracle, whose quantiser would
-otherwise touch every expert."""
+memory) for the bf16 oracle and the MXFP8 backward's oracle, which read no
+other expert, and into compact arrays with remapped expert ids for the MXFP8
+forward's oracle."""
 import numpy as np
 import pytest
 import torch
@@ -147,26 +149,93 @@ def test_fullsize_sampled_weight_grads(ds):
         hz.assert_close(f"fullsize {name} elements", got, ref[sel], hz.GRAD_TOL)
 
 
-def test_fullsize_mx_forward_sampled_tokens(ds):
+@pytest.fixture(scope="module")
+def dsmx(ds):
+    """The MXFP8 forward and backward on the same inputs, in the benchmark's
+    launch configuration (router weight, fp32 weight gradients accumulated
+    into zeros)."""
     from grouped_gemm_expert_amd import ops
-    w, r, toks = ds["w"], ds["r"], ds["toks"]
-    d, cfg = ds["d"], ds["cfg"]
-    hz.say("fullsize mx: quantising the weights")
-    cache = ops.MxWeightCache()
-    w1_mx, w2_mx = cache.get(d["w1"], d["w2"])
+    w, d, cfg = ds["w"], ds["d"], ds["cfg"]
+    hz.say("fullsize mx: quantising the weights (forward and transposed forms)")
+    cache = ops.MxWeightCache(backward=True)
+    cache.get(d["w1"], d["w2"])
     saved = ops.alloc_saved(cfg)
     y = torch.empty((w.T, w.H), device="cuda")
     aux = torch.empty((1,), device="cuda")
-    ws = ops.workspace(cfg, "fwd")
-    hz.say("fullsize mx: moe_forward_mx")
-    ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], w1_mx, w2_mx, y, aux, saved, ws)
+    hz.say("fullsize mx: moe_forward_mx + moe_backward_mx")
+    ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], cache.w1_mx, cache.w2_mx, y, aux, saved,
+                       ops.workspace(cfg, "fwd"))
+    dx = torch.empty((w.T, w.H), device="cuda")
+    dl = torch.empty((w.T, w.E), device="cuda")
+    dWr = torch.empty((w.E, w.H), device="cuda")
+    dW1 = torch.zeros((w.E, 2 * w.I, w.H), device="cuda")
+    dW2 = torch.zeros((w.E, w.H, w.I), device="cuda")
+    d_aux = torch.ones((1,), device="cuda")
+    ops.moe_backward_mx(cfg, saved, d["x"], d["Wr"], cache.w1t_mx, cache.w2t_mx, d["dy"], d_aux,
+                        dx, dl, dWr, dW1, dW2, ops.workspace(cfg, "bwd"), dw_accumulate=True)
     torch.cuda.synchronize()
-    assert np.array_equal(saved["topk_idx"].cpu().numpy(), ds["idx_gpu"])
+    return dict(saved=saved, y=y, dx=dx, dl=dl, dW1=dW1, dW2=dW2)
+
+
+def test_fullsize_mx_forward_sampled_tokens(ds, dsmx):
+    w, r, toks = ds["w"], ds["r"], ds["toks"]
+    d = ds["d"]
+    assert np.array_equal(dsmx["saved"]["topk_idx"].cpu().numpy(), ds["idx_gpu"])
     ex = np.unique(r["idx"][toks])
     W1c, W2c = _compact(d, ex)
     ops_o = oracle.MxOperands(ds["X"][toks], W1c, W2c)
     idx_c = _remap(r["idx"][toks], ex)
     hz.say(f"fullsize mx: oracle on tokens {toks.tolist()}")
     y_ref = oracle.mx_forward(ops_o, idx_c, r["w"][toks])
-    hz.assert_close("fullsize mx y", y[torch.as_tensor(toks, device="cuda")].cpu().numpy(),
+    hz.assert_close("fullsize mx y", dsmx["y"][torch.as_tensor(toks, device="cuda")].cpu().numpy(),
                     y_ref, hz.MX_FWD_TOL)
+
+
+def test_fullsize_mx_backward_sampled_tokens(ds, dsmx):
+    """dx and dlogits of two tokens against the oracle's MXFP8 backward, with
+    operands that hold only the experts those tokens use (the router part
+    needs every logit, so the expert ids are kept)."""
+    w, r = ds["w"], ds["r"]
+    toks = ds["toks"][:2]
+    ex = np.unique(r["idx"][toks])
+    hz.say(f"fullsize mx backward tokens {toks.tolist()}: quantising {len(ex)} experts")
+    W1c, W2c = _compact(ds["d"], ex)
+    DY = hz.bits(ds["d"]["dy"])
+    ops_o = oracle.MxBackwardOperands.from_experts(ds["X"], DY, w.E, ex, W1c, W2c)
+    del W1c, W2c
+    dx_ref, dl_ref = oracle.mx_backward_tokens(ops_o, ds["Wr"], ds["l64"], r["idx"], r["counts"],
+                                               r["w"], score=hz.SCORE[w.score], renorm=w.renorm,
+                                               scale=w.scale, coeff=w.aux_coeff, d_aux=1.0,
+                                               toks=toks)
+    tk = torch.as_tensor(toks, device="cuda")
+    hz.assert_close("fullsize mx dx", dsmx["dx"][tk].cpu().numpy(), dx_ref, hz.MX_GRAD_TOL)
+    hz.assert_close("fullsize mx dlogits", dsmx["dl"][tk].cpu().numpy(), dl_ref, hz.MX_GRAD_TOL)
+
+
+def test_fullsize_mx_backward_sampled_weight_grads(ds, dsmx):
+    w, r = ds["w"], ds["r"]
+    counts = r["counts"]
+    ex = np.argsort(-counts, kind="stable")[:2]          # the two busiest experts
+    hz.say(f"fullsize mx dW: experts {ex.tolist()} with {counts[ex].tolist()} rows")
+    W1c, W2c = _compact(ds["d"], ex)
+    DY = hz.bits(ds["d"]["dy"])
+    ops_o = oracle.MxBackwardOperands.from_experts(ds["X"], DY, w.E, ex, W1c, W2c)
+    rng = np.random.default_rng(3)
+    which, ee, rr, cc = [], [], [], []
+    for e in ex:
+        for wh, nr, nc in ((1, 2 * w.I, w.H), (2, w.H, w.I)):
+            which += [wh] * N_EL
+            ee += [int(e)] * N_EL
+            rr += rng.integers(0, nr, N_EL).tolist()
+            cc += rng.integers(0, nc, N_EL).tolist()
+    which, ee, rr, cc = (np.array(v, np.int32) for v in (which, ee, rr, cc))
+    ref = oracle.mx_weight_grad_elements(ops_o, ds["X"], DY, r["idx"], r["w"], which, ee, rr, cc)
+    for wh, name in ((1, "dW1"), (2, "dW2")):
+        sel = which == wh
+        dW = dsmx[name]
+        e_, r_, c_ = ee[sel], rr[sel], cc[sel]
+        # indices checked on the host: the gather below does not check them
+        assert (e_ < dW.shape[0]).all() and (r_ < dW.shape[1]).all() and (c_ < dW.shape[2]).all()
+        got = dW[torch.as_tensor(e_, device="cuda"), torch.as_tensor(r_, device="cuda"),
+                 torch.as_tensor(c_, device="cuda")].cpu().numpy()
+        hz.assert_close(f"fullsize mx {name} elements", got, ref[sel], hz.MX_GRAD_TOL)
