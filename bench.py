@@ -14,10 +14,13 @@ that the library records on its own stream around each stage
 The CPU baseline is the oracle, timed on a bounded token sample of the same
 workload on the host cores.
 
-The "mxfp8" object times the layer's MXFP8 forward (the mxfp8 expert precision:
-both expert GEMMs on block-scaled fp8 MFMA) on the same inputs, after the bf16
-steps: the weight-cache fill (quantising w1 and w2), then forwards whose
-grouped GEMMs are priced against the fp8 MFMA peak.
+The "mxfp8" object times the layer's MXFP8 step (the mxfp8 expert precision:
+moe_forward_mx + moe_backward_mx, all six expert GEMMs on block-scaled fp8
+MFMA) on the same inputs and buffers, after the bf16 steps: the weight-cache
+fill (w1, w2 and their transposes quantised) once, then steps whose grouped
+GEMMs are priced against the fp8 MFMA peak.  The cache is dropped once per
+optimizer step, so a step without gradient accumulation also pays the fill:
+both rates are reported.
 """
 from __future__ import annotations
 
@@ -139,93 +142,100 @@ def run_gpu(args, w):
             continue
         if s == "router_grads" and d["Wr"] is None:
             continue
-        if s == "mx_quant":               # not part of the bf16 step
+        if s.startswith("mx_quant"):      # not part of the bf16 step
             continue
         times = [a.elapsed_time(b) for a, b in ev[s]]
         stage_ms[s] = sum(times) / len(times)
     counts = saved["counts"].cpu()
     log(f"[bench] step {elapsed / K * 1e3:.3f} ms; active experts {(counts > 0).sum().item()}, "
         f"max rows {counts.max().item()}")
-    return dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved)
+    return dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved,
+                bufs=dict(y=y, aux=aux, wsf=wsf, wsb=wsb, dx=dx, dl=dl, dWr=dWr, dW1=dW1, dW2=dW2,
+                          d_aux=d_aux))
 
 
-MX_FWD_STAGES = ["router_proj", "router", "permute", "mx_quant", "up_swiglu", "down", "combine"]
+MX_STAGES = ["router_proj", "router", "permute", "mx_quant", "up_swiglu", "down", "combine",
+             "mx_quant_bwd2", "down_dgrad", "down_wgrad", "mx_quant_bwd1", "up_dgrad", "up_wgrad",
+             "router_bwd", "unpermute", "router_grads"]
 
 
 def run_mx(args, w, g):
-    """MXFP8 forward on the bf16 run's inputs: the weight-cache fill once, then
-    W warmup and K timed forwards with per-stage events."""
+    """The MXFP8 step (moe_forward_mx + moe_backward_mx) on the bf16 run's
+    inputs and buffers: the weight-cache fill (all four MX forms) timed once,
+    then W warmup and K timed steps with per-stage events."""
     import torch
     from grouped_gemm_expert_amd import ops
 
-    d = g["d"]
+    d, b = g["d"], g["bufs"]
     dev = d["x"].device
     cfg = ops.config_from_workload(w)
-    saved = ops.alloc_saved(cfg, dev)
-    if d["logits"] is not None:
-        saved["logits"].copy_(d["logits"])
-    y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
-    aux = torch.empty((1,), dtype=torch.float32, device=dev)
-    ws = ops.workspace(cfg, "fwd", dev)
-    cache = ops.MxWeightCache()
-    log("[bench] mxfp8: quantising w1, w2 (weight cache fill)")
+    saved = g["saved"]
+    acc = args.dw_mode == "accumulate"
+    cache = ops.MxWeightCache(backward=True)
+    log("[bench] mxfp8: quantising w1, w2 and their transposes (weight cache fill)")
     cache.get(d["w1"], d["w2"])      # first fill allocates the cache
     torch.cuda.synchronize()
-    cache.drop()                     # the timed fill: both quantiser launches
+    cache.drop()                     # the timed fill: the four quantiser launches
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     c0.record()
-    w1_mx, w2_mx = cache.get(d["w1"], d["w2"])
+    cache.get(d["w1"], d["w2"])
     c1.record()
     torch.cuda.synchronize()
     fill_ms = c0.elapsed_time(c1)
 
-    def fwd():
-        ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], w1_mx, w2_mx, y, aux, saved, ws)
+    def step():
+        ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], cache.w1_mx, cache.w2_mx, b["y"],
+                           b["aux"], saved, b["wsf"])
+        ops.moe_backward_mx(cfg, saved, d["x"], d["Wr"], cache.w1t_mx, cache.w2t_mx, d["dy"],
+                            b["d_aux"], b["dx"], b["dl"], b["dWr"], b["dW1"], b["dW2"], b["wsb"],
+                            dw_accumulate=acc)
 
     for _ in range(args.warmup):
-        fwd()
+        step()
     torch.cuda.synchronize()
     K = args.steps
-    stages = [s for s in MX_FWD_STAGES if not (s == "router_proj" and d["Wr"] is None)]
+    stages = [s for s in MX_STAGES if not (s in ("router_proj", "router_grads") and d["Wr"] is None)]
     ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(K)] for s in stages}
     for pairs in ev.values():
-        for a, b in pairs:
+        for a, z in pairs:
             a.record()
-            b.record()
+            z.record()
     torch.cuda.synchronize()
-    log(f"[bench] mxfp8: timing {K} forwards")
+    log(f"[bench] mxfp8: timing {K} steps")
     t0 = time.perf_counter()
     for i in range(K):
         for s in stages:
             ops.moe_set_stage_events(ops.STAGES[s], *ev[s][i])
-        fwd()
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for s in stages:
         ops.moe_set_stage_events(ops.STAGES[s], None, None)
-    st = {s: sum(a.elapsed_time(b) for a, b in ev[s]) / K for s in stages}
-    gemm = {"up_swiglu": gemm_flops(w, "up_swiglu"), "down": gemm_flops(w, "down")}
+    st = {s: sum(a.elapsed_time(z) for a, z in ev[s]) / K for s in stages}
+    gemm = {s: gemm_flops(w, s) for s in GEMM_STAGES}
     tf = {s: gemm[s] / (st[s] * 1e-3) / 1e12 for s in gemm}
     dom = max(gemm, key=lambda s: st[s])
-    bf16_fwd = sum(g["stage_ms"][s] for s in stages if s != "mx_quant")
+    gemm_tf = sum(gemm.values()) / (sum(st[s] for s in gemm) * 1e-3) / 1e12
+    ms = (t1 - t0) / K * 1e3
     out = {
-        "ms_per_forward": round((t1 - t0) / K * 1e3, 4),
-        "tokens_per_s_forward": round(w.T * K / (t1 - t0), 1),
-        "bf16_forward_ms": round(bf16_fwd, 4),
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(w.T * K / (t1 - t0), 1),
+        "bf16_ms_per_step": round(g["elapsed"] / K * 1e3, 4),
         "weight_cache_fill_ms": round(fill_ms, 3),
+        "tokens_per_s_with_cache_fill": round(w.T / ((ms + fill_ms) * 1e-3), 1),
         "stages": {s: {"ms": round(st[s], 4), **({"TFLOP/s": round(tf[s], 1)} if s in tf else {})}
                    for s in stages},
-        "grouped_gemm": {"TFLOP/s": round(sum(gemm.values()) / (sum(st[s] for s in gemm) * 1e-3) / 1e12, 1),
-                         "pct_of_fp8_peak": round(100 * sum(gemm.values()) / (sum(st[s] for s in gemm) * 1e-3)
-                                                  / 1e12 / PEAK_FP8_TFLOPS, 2)},
+        "grouped_gemm": {"TFLOP/s": round(gemm_tf, 1),
+                         "pct_of_fp8_peak": round(100 * gemm_tf / PEAK_FP8_TFLOPS, 2),
+                         "ms_per_step": round(sum(st[s] for s in gemm), 4)},
         "roofline": {"bound": "mfma", "kernel": dom + "_mx", "achieved": round(tf[dom], 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf[dom] / PEAK_FP8_TFLOPS, 4),
                      "traffic": measured_traffic(dom + "_mx")},
     }
-    log(f"[bench] mxfp8 forward {out['ms_per_forward']:.3f} ms (bf16 forward stages "
-        f"{bf16_fwd:.3f} ms); GEMMs {tf}")
+    log(f"[bench] mxfp8 step {ms:.3f} ms (bf16 {out['bf16_ms_per_step']:.3f} ms); cache fill "
+        f"{fill_ms:.2f} ms; GEMMs " + ", ".join(f"{s} {tf[s]:.0f}" for s in GEMM_STAGES))
     return out
 
 
@@ -394,7 +404,7 @@ def main():
     ap.add_argument("--workload", default="deepseek_v3")
     ap.add_argument("--dw-mode", choices=["accumulate", "overwrite"], default="accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 forward leg")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy that calibrates the PMC byte counters")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),

@@ -761,7 +761,6 @@ static hipError_t quantize_segments(const moe_config &c, const BwdWs &w, const S
     q.mt128 = sc.mt_off128;
     q.dst = dst;
     (void)w;
-    StageMark mark(MOE_STAGE_MX_QUANT, s);
     return launch_mx_quantize_cols(q, c.T * c.k / 128 + c.E, s);
 }
 
@@ -804,14 +803,16 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
     g.w2cs = w2t_mx + (int64_t)c.E * c.I * g.Hp;
     if (c.T > 0) {
         {
-            StageMark mark(MOE_STAGE_MX_QUANT, stream);
+            // dy along H for the dgrad; dyw and a along each expert's rows
+            // for dW2 (all three are ready here)
+            StageMark mark(MOE_STAGE_MX_QUANT_BWD2, stream);
             MOE_TRY(launch_mx_quantize(dy, c.T, c.H, w.dymx, stream));
+            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dyw, c.H, nullptr, w.segA,
+                                      stream));
+            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, saved->a, c.I, nullptr,
+                                      w.segB, stream));
         }
         MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
-        MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dyw, c.H, nullptr, w.segA,
-                                  stream));
-        MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, saved->a, c.I, nullptr, w.segB,
-                                  stream));
     }
     MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
     return MOE_OK;
@@ -859,14 +860,16 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
         g.w1cs = w1t_mx + (int64_t)c.E * c.H * mx_kp(2 * (int64_t)c.I);
         if (c.T > 0) {
             {
-                StageMark mark(MOE_STAGE_MX_QUANT, stream);
+                // dh along 2I for the dgrad; dh and x (gathered) along each
+                // expert's rows for dW1
+                StageMark mark(MOE_STAGE_MX_QUANT_BWD1, stream);
                 MOE_TRY(launch_mx_quantize(w.dh, c.T * c.k, 2 * (int64_t)c.I, w.dhmx, stream));
+                MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I,
+                                          nullptr, w.segA, stream));
+                MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, x, c.H, saved->row_map,
+                                          w.segB, stream));
             }
             MOE_TRY(run_mx_gemm(MOE_GEMM_UP_DGRAD, g, stream));
-            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I,
-                                      nullptr, w.segA, stream));
-            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, x, c.H, saved->row_map,
-                                      w.segB, stream));
         }
         MOE_TRY(run_mx_gemm(MOE_GEMM_UP_WGRAD, g, stream));
     }
