@@ -662,11 +662,12 @@ moe_status moe_mx_quantize_t(const uint16_t *src, int64_t batches, int64_t R, in
     if (batches == 0) return MOE_OK;
     MOE_CHECK(check_ptrs({src, dst}));
     if (dst_bytes < need) return MOE_EINVAL;
-    ColQuant q;
+    ColQuant q = {};
     q.src = src;
     q.C = C;
     q.gather = nullptr;
     q.gk = 1;
+    q.rw = nullptr;
     q.nseg = (int32_t)batches;
     q.R = R;
     q.offsets = nullptr;
@@ -748,13 +749,15 @@ static hipError_t run_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
 // per-expert MX matrices of the transposes of a [M, C] sorted-row operand
 static hipError_t quantize_segments(const moe_config &c, const BwdWs &w, const Sched &sc,
                                     const int32_t *offsets, const uint16_t *src, int64_t C,
-                                    const int32_t *gather, uint8_t *dst, hipStream_t s)
+                                    const int32_t *gather, const float *rw, uint8_t *dst,
+                                    hipStream_t s)
 {
-    ColQuant q;
+    ColQuant q = {};
     q.src = src;
     q.C = C;
     q.gather = gather;
     q.gk = c.k;
+    q.rw = rw;
     q.nseg = c.E;
     q.R = 0;
     q.offsets = offsets;
@@ -790,8 +793,10 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
     GemmArgs g = gemm_args(c, a, w.sched);
     g.wrow = w.wrow;
     g.dyw = w.dyw;
-    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, nullptr, dy,
-                               nullptr, w.dyw, w.wrow, stream));
+    // the MX path quantises w * dy straight from dy: only the row weights here
+    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, nullptr,
+                               w2t_mx ? nullptr : dy, nullptr, w2t_mx ? nullptr : w.dyw, w.wrow,
+                               stream));
     if (!w2t_mx) {
         // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
         if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
@@ -807,10 +812,10 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
             // for dW2 (all three are ready here)
             StageMark mark(MOE_STAGE_MX_QUANT_BWD2, stream);
             MOE_TRY(launch_mx_quantize(dy, c.T, c.H, w.dymx, stream));
-            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dyw, c.H, nullptr, w.segA,
-                                      stream));
+            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, dy, c.H, saved->row_map,
+                                      w.wrow, w.segA, stream));
             MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, saved->a, c.I, nullptr,
-                                      w.segB, stream));
+                                      nullptr, w.segB, stream));
         }
         MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
     }
@@ -865,9 +870,9 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
                 StageMark mark(MOE_STAGE_MX_QUANT_BWD1, stream);
                 MOE_TRY(launch_mx_quantize(w.dh, c.T * c.k, 2 * (int64_t)c.I, w.dhmx, stream));
                 MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I,
-                                          nullptr, w.segA, stream));
+                                          nullptr, nullptr, w.segA, stream));
                 MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, x, c.H, saved->row_map,
-                                          w.segB, stream));
+                                          nullptr, w.segB, stream));
             }
             MOE_TRY(run_mx_gemm(MOE_GEMM_UP_DGRAD, g, stream));
         }

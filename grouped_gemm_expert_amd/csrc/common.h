@@ -155,12 +155,15 @@ hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
 // (offsets == NULL), or the E expert segments of sorted rows given by
 // offsets / mt128 (the 128-row m-tile prefix sums), each its own MX matrix
 // [C, Kp_e] at C * 132 * mt128[e] bytes; gather (optional) maps a sorted row
-// r to source row gather[r] / gk.  max_chunks bounds the 128-row chunks.
+// r to source row gather[r] / gk, and rw (optional) scales sorted row r by
+// rw[r] first (the product rounded to bf16).  max_chunks bounds the 128-row
+// chunks.
 struct ColQuant {
     const uint16_t *src;
     int64_t C;
     const int32_t *gather;
     int32_t gk;
+    const float *rw;
     int32_t nseg;
     int64_t R;
     const int32_t *offsets, *mt128;

@@ -50,31 +50,62 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // ------------------------------------------------------------ quantiser ----
 // Row-wise MX quantisation of a bf16 matrix src [rows, K] (K % 32 == 0) into
-// codes [rows, Kp] and scales [rows, Kp/32] (layout in mxfmt.h).  Sixteen
-// lanes take one 128-column group of a row, 8 columns each.
+// codes [rows, Kp] and the scale area (layout in mxfmt.h).  Sixteen lanes
+// take one 128-column group of a row, 8 columns each.  Row-groups are
+// numbered (32-row block, group, row) and a block takes 16 consecutive ones:
+// 16 rows of one group, whose scale words fill half of one 128-byte line.
+// The grid strides over these tiles, loading the next tile before encoding
+// the current one.
 __global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *src, int64_t rows, int64_t K,
-                                                     int64_t Kp, uint8_t *codes, uint8_t *scales)
+                                                     int64_t Kp, uint8_t *codes, uint8_t *scales,
+                                                     int64_t ntiles)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t gpr = Kp / MX_GROUP;
-    const int64_t grp = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
-    const bool valid = grp < rows * gpr;
-    const int64_t row = valid ? grp / gpr : 0, j = valid ? grp % gpr : 0;
-    const int64_t col = j * MX_GROUP + (lane & 15) * 8;
-    float v[8];
-    u32x4_t w = {0u, 0u, 0u, 0u};
-    if (valid && col < K) w = *(const u32x4_t *)(src + row * K + col);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint32_t gpr = (uint32_t)(Kp / MX_GROUP);
+    const int sub = (lane & 15) * 8;
+    auto locate = [&](int64_t tile, int64_t &row, int64_t &j) {
+        const int64_t rg = tile * 16 + wv * 4 + (lane >> 4);
+        const uint32_t t = (uint32_t)(rg >> 5);
+        const uint32_t rb = t / gpr;
+        j = t - rb * gpr;
+        row = (int64_t)rb * 32 + (rg & 31);
+    };
+    auto load = [&](int64_t row, int64_t j) {
+        const int64_t col = j * MX_GROUP + sub;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row < rows && col < K) v = *(const u32x4_t *)(src + row * K + col);
+        return v;
+    };
+    int64_t tile = blockIdx.x;
+    int64_t row, j;
+    locate(tile, row, j);
+    u32x4_t cur = load(row, j);
+    for (;;) {
+        const int64_t next = tile + gridDim.x;
+        int64_t nrow = 0, nj = 0;
+        u32x4_t nxt = {0u, 0u, 0u, 0u};
+        if (next < ntiles) {
+            locate(next, nrow, nj);
+            nxt = load(nrow, nj);
+        }
+        float v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        v[2 * q] = bf2f((uint16_t)(w[q] & 0xffffu));
-        v[2 * q + 1] = bf2f((uint16_t)(w[q] >> 16));
-    }
-    uint32_t sc;
-    const uint64_t c = mx_quant8(v, sc);
-    const uint32_t word = mx_group_word(sc, lane);
-    if (valid) {
-        *(uint64_t *)(codes + row * Kp + col) = c;
-        if ((lane & 15) == 0) *(uint32_t *)(scales + mx_scale_off(row, j, gpr)) = word;
+        for (int q = 0; q < 4; ++q) {
+            v[2 * q] = bf2f((uint16_t)(cur[q] & 0xffffu));
+            v[2 * q + 1] = bf2f((uint16_t)(cur[q] >> 16));
+        }
+        uint32_t sc;
+        const uint64_t c = mx_quant8(v, sc);
+        const uint32_t word = mx_group_word(sc, lane);
+        if (row < rows) {
+            *(uint64_t *)(codes + row * Kp + j * MX_GROUP + sub) = c;
+            if ((lane & 15) == 0) *(uint32_t *)(scales + mx_scale_off(row, j, gpr)) = word;
+        }
+        if (next >= ntiles) break;
+        tile = next;
+        row = nrow;
+        j = nj;
+        cur = nxt;
     }
 }
 
@@ -83,16 +114,20 @@ hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint
 {
     if (rows <= 0) return hipSuccess;
     const int64_t Kp = mx_kp(K);
-    const int64_t groups = rows * (Kp / MX_GROUP);
-    hipLaunchKernelGGL(k_mx_quantize, dim3((unsigned)ceil_div(groups, 16)), dim3(256), 0, s, src,
-                       rows, K, Kp, dst, dst + rows * Kp);
+    // 16 row-groups a tile; row-groups numbered over ceil(rows/32)*32 rows
+    const int64_t ntiles = ceil_div(rows, 32) * (Kp / MX_GROUP) * 2;
+    if (ceil_div(rows, 32) * (Kp / MX_GROUP) >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+    const int64_t grid = ntiles < 4096 ? ntiles : 4096;
+    hipLaunchKernelGGL(k_mx_quantize, dim3((unsigned)grid), dim3(256), 0, s, src, rows, K, Kp, dst,
+                       dst + rows * Kp, ntiles);
     return hipGetLastError();
 }
 
 // Column quantiser: a block takes 128 rows (one scale group of the output's
-// k) by 64 columns of a segment into LDS, then each thread quantises one
-// (column, 32-row block): 32 codes, contiguous in the output row of that
-// column, and its scale, gathered through LDS into the group's word.
+// k) by 64 columns of a segment into LDS (rows gathered and scaled by a row
+// weight on the way when asked), then each thread quantises one (column,
+// 32-row block): 32 codes, contiguous in the output row of that column, and
+// its scale, gathered through LDS into the group's word.
 __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
 {
     __shared__ __attribute__((aligned(16))) uint16_t tile[128][64];
@@ -135,8 +170,14 @@ __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (r < len) {
             int64_t sr = r0 + r;
+            const float wr = q.rw ? q.rw[sr] : 1.f;
             if (q.gather) sr = q.gather[sr] / q.gk;
             v = *(const u32x4_t *)(q.src + sr * q.C + ct * 64 + qd * 8);
+            if (q.rw) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = pack_bf2(wr * bf2f((uint16_t)(v[e] & 0xffffu)), wr * bf2f((uint16_t)(v[e] >> 16)));
+            }
         }
         *(u32x4_t *)&tile[r][qd * 8] = v;
     }
@@ -150,9 +191,14 @@ __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
         amax = fmaxf(amax, fabsf(v[i]));
     }
     const int X = mx_block_exp(amax);
-    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) w[i >> 2] |= e4m3_code(v[i], X) << (8 * (i & 3));
+    for (int p = 0; p < 4; ++p) {
+        const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * p]);
+        const uint64_t c8 = e4m3_codes8(v8, X);
+        w[2 * p] = (uint32_t)c8;
+        w[2 * p + 1] = (uint32_t)(c8 >> 32);
+    }
     const int64_t orow = rowbase + ct * 64 + c;
     uint8_t *dstc = codes + orow * Kp + j * MX_GROUP + b * 32;
     *(u32x4_t *)dstc = u32x4_t{w[0], w[1], w[2], w[3]};

@@ -51,38 +51,35 @@ MOE_DEV int mx_block_exp(float amax)
     return X < -127 ? -127 : X;
 }
 
-// E4M3 code of v / 2^X, nearest-even, saturating; exact integer arithmetic on
-// the fp32 bits.  |v| / 2^X = sig * 2^E0; the E4M3 grid around it has spacing
-// 2^kq, kq = max(floor(log2 |v / 2^X|), -6) - 3 (the -6 floor is the subnormal
-// range), so the code's magnitude is sig / 2^(kq - E0) rounded to an integer n
-// and placed into the exponent / mantissa fields.
-MOE_DEV uint32_t e4m3_code(float v, int X)
+// E4M3 codes of v[0..7] / 2^X (byte q: v[q]).  Dividing by 2^X is an exact
+// multiplication by a power of two (the inputs are bf16 values, and a result
+// below fp32's normal range lies far below half of E4M3's smallest subnormal,
+// so it becomes zero either way); the clamp to +-448 is the format's
+// saturation; v_cvt_pk_fp8_f32 then rounds to nearest even onto the OCP E4M3
+// grid, subnormals included.
+MOE_DEV uint64_t e4m3_codes8(const float (&v)[8], int X)
 {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const int ev = (int)((u >> 23) & 255u);
-    uint32_t sig = u & 0x7FFFFFu;
-    if (ev) sig |= 0x800000u;
-    if (!sig) return sign;
-    const int E0 = (ev ? ev : 1) - 150 - X;
-    const int eq = E0 + (31 - __builtin_clz(sig));
-    const int kq = (eq > -6 ? eq : -6) - 3;
-    const int sh = kq - E0;
-    uint32_t n;
-    if (sh <= 0) {
-        n = sig << (-sh);  // only tiny subnormal inputs: exact
-    } else if (sh > 25) {
-        n = 0;
-    } else {
-        n = sig >> sh;
-        const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
-        n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;
+    const float f = __uint_as_float((uint32_t)(127 - X) << 23);
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float s[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s[q] = fminf(fmaxf(v[4 * h + q] * f, -448.f), 448.f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], p, true);
+        w[h] = (uint32_t)p;
     }
-    // normal: n in [8, 16] at exponent eq = kq + 3 (n = 16 carries into the
-    // next exponent); subnormal: n in [0, 8], which is the code itself
-    uint32_t c = eq >= -6 ? ((uint32_t)(kq + 10) << 3) + n - 8u : n;
-    c = c < 0x7Eu ? c : 0x7Eu;
-    return sign | c;
+    return (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+}
+
+// Largest of a over each group of 4 lanes (4b .. 4b+3), by DPP quad
+// permutations (lanes 1,0,3,2 then 2,3,0,1).
+MOE_DEV float quad_max(float a)
+{
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false)));
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false)));
+    return a;
 }
 
 // Lanes 4b .. 4b+3 of a wave hold the 32 values of one block, 8 each (in
@@ -93,25 +90,21 @@ MOE_DEV uint64_t mx_quant8(const float (&v)[8], uint32_t &scale)
     float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const int X = mx_block_exp(amax);
-    uint64_t c = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) c |= (uint64_t)e4m3_code(v[q], X) << (8 * q);
+    const int X = mx_block_exp(quad_max(amax));
     scale = (uint32_t)(X + 127);
-    return c;
+    return e4m3_codes8(v, X);
 }
 
 // Lanes 16g .. 16g+15 hold one 128-column group (blocks b = lane/4 % 4): the
 // group's scale word with block b at byte 2*(b%2) + b/2.  Every lane of the
-// wave must call it; all 16 lanes of a group receive the word.
+// wave must call it; all 16 lanes of a group receive the word.  (ds_swizzle
+// in bit-mask mode: lane l reads lane l ^ 4, then l ^ 8.)
 MOE_DEV uint32_t mx_group_word(uint32_t scale, int lane)
 {
     const int b = (lane >> 2) & 3;
     uint32_t w = scale << (8 * ((b & 1) * 2 + (b >> 1)));
-    w |= __shfl_xor(w, 4, 64);
-    w |= __shfl_xor(w, 8, 64);
+    w |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)w, 0x101F);
+    w |= (uint32_t)__builtin_amdgcn_ds_swizzle((int)w, 0x201F);
     return w;
 }
 

@@ -76,6 +76,11 @@ WORKLOADS = {
         score="sigmoid", scale=2.5, x_std=0.02, logits="normal",
         description="DeepSeek-V3 shapes, i.i.d. N(0,1) logits (balanced routing)"),
     # test shapes: several GEMM tiles and ragged tails, small enough for the oracle
+    "ep8_share": Workload(
+        "ep8_share", T=8192, H=7168, I=2048, E=32, k=8, score="sigmoid", scale=2.5, x_std=0.02,
+        route="even",
+        description="one GPU's share of DeepSeek-V3 under EP8: 32 local experts, 65536 rows "
+                    "split evenly (even routing)"),
     "mid_softmax": Workload(
         "mid_softmax", T=600, H=256, I=192, E=16, k=4, score="softmax", renorm=True,
         x_std=1.0, description="parity shape, softmax renorm"),

@@ -73,6 +73,7 @@ def _matrix(kind: str, rows: int, K: int, seed: int) -> np.ndarray:
         v = np.ldexp(rng.uniform(1, 2, (rows, K)), rng.integers(-140, 121, (rows, K)))
         v *= rng.choice([-1.0, 1.0], (rows, K))
         v[rng.random((rows, K)) < 0.05] = 0.0
+        v[rng.random((rows, K)) < 0.02] = -0.0          # negative zeros keep their sign
         if K >= 64:
             v[::3, 32:64] = 0.0
         # blocks whose values span only a few binades, so most elements land in

@@ -49,7 +49,10 @@ def test_mx_quantize_t_bit_exact(B, R, C):
     v = np.ldexp(rng.uniform(1, 2, (B, R, C)), rng.integers(-20, 6, (B, R, C)))
     v *= rng.choice([-1.0, 1.0], (B, R, C))
     v[rng.random((B, R, C)) < 0.05] = 0.0
+    v[rng.random((B, R, C)) < 0.02] = -0.0        # negative zeros keep their sign
     v[:, :32, :C // 2] = 0.0                      # whole zero blocks
+    sub = v[:, -32:, -8:]                         # blocks of bf16 subnormals
+    sub[...] = np.ldexp(rng.uniform(1, 2, sub.shape), rng.integers(-133, -126, sub.shape))
     src = _bf16_bits_of(v.astype(np.float32))
     dev = torch.from_numpy(src.view(np.int16)).view(torch.bfloat16).cuda()
     buf = ops.mx_alloc(B * C, R)

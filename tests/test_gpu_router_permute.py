@@ -14,7 +14,7 @@ from tests import harness as hz
 pytestmark = pytest.mark.gpu
 
 ROUTER_CASES = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "deepseek_v3", "skewed",
-                "uniform", "fine_grained", "mid_even", "even_softmax"]
+                "uniform", "fine_grained", "mid_even", "even_softmax", "ep8_share"]
 
 
 def _logits_for(w, seed=0):
