@@ -142,7 +142,7 @@ def run_gpu(args, w):
             continue
         if s == "router_grads" and d["Wr"] is None:
             continue
-        if s.startswith("mx_quant"):      # not part of the bf16 step
+        if s == "mx_quant":               # not part of the bf16 step
             continue
         times = [a.elapsed_time(b) for a, b in ev[s]]
         stage_ms[s] = sum(times) / len(times)
@@ -155,7 +155,7 @@ def run_gpu(args, w):
 
 
 MX_STAGES = ["router_proj", "router", "permute", "mx_quant", "up_swiglu", "down", "combine",
-             "mx_quant_bwd2", "down_dgrad", "down_wgrad", "mx_quant_bwd1", "up_dgrad", "up_wgrad",
+             "operands_bwd2", "down_dgrad", "down_wgrad", "operands_bwd1", "up_dgrad", "up_wgrad",
              "router_bwd", "unpermute", "router_grads"]
 
 

@@ -38,7 +38,7 @@ struct FwdWs {
     int32_t *chunk_hist;
     Sched sched;
     float *wrow;
-    float *o;   // [M,H] fp32; the single-op grouped GEMMs reuse it for xg / dyw
+    float *o;   // [M,H] fp32; the single-op weight gradients reuse it (see carve_fwd)
     void *router;  // router GEMM scratch (router_ws_bytes_fwd)
     uint8_t *xmx;  // MXFP8 forward: MX matrix of x [T, Hp]
     uint8_t *amx;  // MXFP8 forward: MX matrix of a [M, Ip]
@@ -50,13 +50,42 @@ struct BwdWs {
     float *dw_part;
     float *dxp;
     float *wrow;
-    uint16_t *xg;
-    uint16_t *dyw;
     void *router;  // router GEMM scratch (router_ws_bytes_bwd)
     uint8_t *dymx;  // MXFP8 backward: MX matrix of dy [T, H]
     uint8_t *dhmx;  // MXFP8 backward: MX matrix of dh [M, 2I]
-    uint8_t *segA, *segB;  // MXFP8 weight gradients: per-expert transposed operands
+    // the weight gradients' operands, each expert's rows transposed: bf16
+    // (tA: w*dy or dh; tB: a or x), or in MX form in the same memory
+    uint16_t *tA, *tB;
+    uint8_t *segA, *segB;
 };
+
+// Elements of the two transposed weight-gradient operand areas: rows R times
+// the 128-row chunks of all experts (at most M/128 + E).
+static int64_t seg_chunks(const moe_config &c) { return c.T * c.k / 128 + c.E; }
+static int64_t seg_rows_a(const moe_config &c) { return c.H > 2 * (int64_t)c.I ? c.H : 2 * (int64_t)c.I; }
+static int64_t seg_rows_b(const moe_config &c) { return c.H > c.I ? c.H : c.I; }
+
+// Each expert's rows of a sorted-row operand [M, C] (rows gathered through
+// `gather` / k and scaled by `rw` when given), transposed for the weight
+// gradients: bf16 into dst (uint16_t), or as MX matrices (mx).
+static hipError_t prepare_segments(const moe_config &c, const Sched &sc, const int32_t *offsets,
+                                   const uint16_t *src, int64_t C, const int32_t *gather,
+                                   const float *rw, bool mx, void *dst, hipStream_t s)
+{
+    ColQuant q = {};
+    q.src = src;
+    q.C = C;
+    q.gather = gather;
+    q.gk = c.k;
+    q.rw = rw;
+    q.nseg = c.E;
+    q.R = 0;
+    q.offsets = offsets;
+    q.mt128 = sc.mt_off128;
+    q.dst = (uint8_t *)dst;
+    return mx ? launch_mx_quantize_cols(q, seg_chunks(c), s)
+              : launch_transpose_segments(q, seg_chunks(c), (uint16_t *)dst, s);
+}
 
 FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
 {
@@ -69,7 +98,10 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
     w.sched.order = cv.take<int32_t>(c.E + 1);
     w.wrow = cv.take<float>(M);
-    w.o = cv.take<float>(M * c.H);
+    // o [M,H] fp32; the single-op weight-gradient GEMMs put their transposed
+    // operands here instead
+    const int64_t t_elems = (seg_rows_a(c) + seg_rows_b(c)) * 128 * seg_chunks(c);
+    w.o = cv.take<float>(M * c.H > (t_elems + 1) / 2 ? M * c.H : (t_elems + 1) / 2);
     w.router = cv.take<char>((int64_t)router_ws_bytes_fwd(c.T, c.E, c.H));
     w.xmx = cv.take<uint8_t>(mx_bytes(c.T, c.H));
     w.amx = cv.take<uint8_t>(mx_bytes(M, c.I));
@@ -89,18 +121,16 @@ BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
     w.dw_part = cv.take<float>(M * dgrad2_cols(c.I));
     w.dxp = cv.take<float>(M * c.H);
     w.wrow = cv.take<float>(M);
-    w.xg = cv.take<uint16_t>(M * c.H);
-    w.dyw = cv.take<uint16_t>(M * c.H);
     w.router = cv.take<char>((int64_t)router_ws_bytes_bwd(c.T, c.E, c.H));
     w.dymx = cv.take<uint8_t>(mx_bytes(c.T, c.H));
     w.dhmx = cv.take<uint8_t>(mx_bytes(M, 2 * (int64_t)c.I));
-    // per-expert MX matrices of the weight-gradient operands: rows R, K = the
-    // expert's rows padded to 128; sum over experts <= (M/128 + E) 128-row chunks
-    const int64_t chunks = M / 128 + c.E;
-    const int64_t ra = c.H > 2 * (int64_t)c.I ? c.H : 2 * (int64_t)c.I;
-    const int64_t rb = c.H > c.I ? c.H : c.I;
-    w.segA = cv.take<uint8_t>(ra * 132 * chunks);
-    w.segB = cv.take<uint8_t>(rb * 132 * chunks);
+    // per-expert transposes of the weight-gradient operands: rows R, K = the
+    // expert's rows padded to 128, <= (M/128 + E) 128-row chunks in all; the
+    // MX forms (132 bytes per 128 elements) fit in the bf16 ones
+    w.tA = cv.take<uint16_t>(seg_rows_a(c) * 128 * seg_chunks(c));
+    w.tB = cv.take<uint16_t>(seg_rows_b(c) * 128 * seg_chunks(c));
+    w.segA = (uint8_t *)w.tA;
+    w.segB = (uint8_t *)w.tB;
     if (bytes) *bytes = cv.used;
     return w;
 }
@@ -232,6 +262,8 @@ moe_status moe_check_config(const moe_config *cfg)
     const int64_t M = c.T * (int64_t)c.k;
     const int64_t widest = c.H > 2 * c.I ? c.H : 2 * (int64_t)c.I;
     if (M >= (1ll << 31) || M * widest >= (1ll << 31)) return MOE_EUNSUPPORTED;
+    // an expert's transposed weight-gradient operands: widest x (rows + pad)
+    if (widest * (c.T + 128) >= (1ll << 31)) return MOE_EUNSUPPORTED;
     if ((int64_t)2 * c.I * c.H >= (1ll << 31)) return MOE_EUNSUPPORTED;
     return MOE_OK;
 }
@@ -351,21 +383,27 @@ moe_status moe_grouped_gemm(int32_t op, const moe_config *cfg, const moe_gemm_ar
     if (c.T == 0 && !wgrad) return MOE_OK;
     MOE_TRY(launch_schedule(c.E, a.counts, w.sched, stream));
     GemmArgs g = gemm_args(c, a, w.sched);
-    // per-sorted-row operands the op reads (see launch_gather_rows)
     const int64_t M = c.T * c.k;
-    uint16_t *xg = (uint16_t *)w.o, *dyw = (uint16_t *)w.o + M * c.H;
-    if (op == MOE_GEMM_DOWN_DGRAD)
-        MOE_TRY(launch_gather_rows(M, c.k, c.H, a.row_map, a.topk_w, nullptr, nullptr, nullptr,
-                                   nullptr, w.wrow, stream));
-    if (op == MOE_GEMM_DOWN_WGRAD)
-        MOE_TRY(launch_gather_rows(M, c.k, c.H, a.row_map, a.topk_w, nullptr, a.dy, nullptr, dyw,
-                                   w.wrow, stream));
-    if (op == MOE_GEMM_UP_WGRAD)
-        MOE_TRY(launch_gather_rows(M, c.k, c.H, a.row_map, a.topk_w, a.x,
-                                   nullptr, xg, nullptr, nullptr, stream));
+    // the routing weight per sorted row (dgrad2, and w*dy for dW2)
+    if (op == MOE_GEMM_DOWN_DGRAD || op == MOE_GEMM_DOWN_WGRAD)
+        MOE_TRY(launch_row_weights(M, a.row_map, a.topk_w, w.wrow, stream));
+    // the weight gradients' operands, transposed per expert (in the area of o)
+    uint16_t *tA = (uint16_t *)w.o, *tB = tA + seg_rows_a(c) * 128 * seg_chunks(c);
+    if (op == MOE_GEMM_DOWN_WGRAD && c.T > 0) {
+        MOE_TRY(prepare_segments(c, w.sched, a.offsets, a.dy, c.H, a.row_map, w.wrow, false, tA,
+                                 stream));
+        MOE_TRY(prepare_segments(c, w.sched, a.offsets, a.a, c.I, nullptr, nullptr, false, tB,
+                                 stream));
+    }
+    if (op == MOE_GEMM_UP_WGRAD && c.T > 0) {
+        MOE_TRY(prepare_segments(c, w.sched, a.offsets, a.dh, 2 * (int64_t)c.I, nullptr, nullptr,
+                                 false, tA, stream));
+        MOE_TRY(prepare_segments(c, w.sched, a.offsets, a.x, c.H, a.row_map, nullptr, false, tB,
+                                 stream));
+    }
     g.wrow = w.wrow;
-    g.xg = xg;
-    g.dyw = dyw;
+    g.tA = tA;
+    g.tB = tB;
     MOE_TRY(run_gemm(op, g, stream));
     return MOE_OK;
 }
@@ -746,26 +784,7 @@ static hipError_t run_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
     return launch_mx_gemm(op, g, s);
 }
 
-// per-expert MX matrices of the transposes of a [M, C] sorted-row operand
-static hipError_t quantize_segments(const moe_config &c, const BwdWs &w, const Sched &sc,
-                                    const int32_t *offsets, const uint16_t *src, int64_t C,
-                                    const int32_t *gather, const float *rw, uint8_t *dst,
-                                    hipStream_t s)
-{
-    ColQuant q = {};
-    q.src = src;
-    q.C = C;
-    q.gather = gather;
-    q.gk = c.k;
-    q.rw = rw;
-    q.nseg = c.E;
-    q.R = 0;
-    q.offsets = offsets;
-    q.mt128 = sc.mt_off128;
-    q.dst = dst;
-    (void)w;
-    return launch_mx_quantize_cols(q, c.T * c.k / 128 + c.E, s);
-}
+
 
 static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
                              const uint8_t *w2t_mx, const uint16_t *dy, void *dW2,
@@ -792,34 +811,33 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
     a.dw_accumulate = dw_accumulate;
     GemmArgs g = gemm_args(c, a, w.sched);
     g.wrow = w.wrow;
-    g.dyw = w.dyw;
-    // the MX path quantises w * dy straight from dy: only the row weights here
-    MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, nullptr,
-                               w2t_mx ? nullptr : dy, nullptr, w2t_mx ? nullptr : w.dyw, w.wrow,
-                               stream));
-    if (!w2t_mx) {
-        // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
+    g.tA = w.tA;
+    g.tB = w.tB;
+    const bool mx = w2t_mx != nullptr;
+    if (mx) {
+        set_mx_bwd(g, c, w);
+        g.w2cq = w2t_mx;
+        g.w2cs = w2t_mx + (int64_t)c.E * c.I * g.Hp;
+    }
+    MOE_TRY(launch_row_weights(c.T * c.k, saved->row_map, saved->topk_w, w.wrow, stream));
+    if (c.T > 0) {
+        // dW2's operands, w*dy (dy gathered, times the routing weight) and a,
+        // along each expert's rows; with MX also dy along H for the dgrad
+        StageMark mark(MOE_STAGE_OPERANDS_BWD2, stream);
+        if (mx) MOE_TRY(launch_mx_quantize(dy, c.T, c.H, w.dymx, stream));
+        MOE_TRY(prepare_segments(c, w.sched, saved->offsets, dy, c.H, saved->row_map, w.wrow, mx,
+                                 w.tA, stream));
+        MOE_TRY(prepare_segments(c, w.sched, saved->offsets, saved->a, c.I, nullptr, nullptr, mx,
+                                 w.tB, stream));
+    }
+    // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
+    if (mx) {
+        if (c.T > 0) MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
+        MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
+    } else {
         if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
         MOE_TRY(run_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
-        return MOE_OK;
     }
-    set_mx_bwd(g, c, w);
-    g.w2cq = w2t_mx;
-    g.w2cs = w2t_mx + (int64_t)c.E * c.I * g.Hp;
-    if (c.T > 0) {
-        {
-            // dy along H for the dgrad; dyw and a along each expert's rows
-            // for dW2 (all three are ready here)
-            StageMark mark(MOE_STAGE_MX_QUANT_BWD2, stream);
-            MOE_TRY(launch_mx_quantize(dy, c.T, c.H, w.dymx, stream));
-            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, dy, c.H, saved->row_map,
-                                      w.wrow, w.segA, stream));
-            MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, saved->a, c.I, nullptr,
-                                      nullptr, w.segB, stream));
-        }
-        MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_DGRAD, g, stream));
-    }
-    MOE_TRY(run_mx_gemm(MOE_GEMM_DOWN_WGRAD, g, stream));
     return MOE_OK;
 }
 
@@ -852,31 +870,31 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
     a.dw_dtype = dw_dtype;
     a.dw_accumulate = dw_accumulate;
     GemmArgs g = gemm_args(c, a, w.sched);
-    g.xg = w.xg;
-    if (!w1t_mx) {
-        MOE_TRY(launch_gather_rows(c.T * c.k, c.k, c.H, saved->row_map, saved->topk_w, x,
-                                   nullptr, w.xg, nullptr, nullptr, stream));
-        // dgrad, then dW1
-        if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_UP_DGRAD, g, stream));
-        MOE_TRY(run_gemm(MOE_GEMM_UP_WGRAD, g, stream));
-    } else {
+    g.tA = w.tA;
+    g.tB = w.tB;
+    const bool mx = w1t_mx != nullptr;
+    if (mx) {
         set_mx_bwd(g, c, w);
         g.w1cq = w1t_mx;
         g.w1cs = w1t_mx + (int64_t)c.E * c.H * mx_kp(2 * (int64_t)c.I);
-        if (c.T > 0) {
-            {
-                // dh along 2I for the dgrad; dh and x (gathered) along each
-                // expert's rows for dW1
-                StageMark mark(MOE_STAGE_MX_QUANT_BWD1, stream);
-                MOE_TRY(launch_mx_quantize(w.dh, c.T * c.k, 2 * (int64_t)c.I, w.dhmx, stream));
-                MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I,
-                                          nullptr, nullptr, w.segA, stream));
-                MOE_TRY(quantize_segments(c, w, w.sched, saved->offsets, x, c.H, saved->row_map,
-                                          nullptr, w.segB, stream));
-            }
-            MOE_TRY(run_mx_gemm(MOE_GEMM_UP_DGRAD, g, stream));
-        }
+    }
+    if (c.T > 0) {
+        // dW1's operands, dh and x (gathered), along each expert's rows; with
+        // MX also dh along 2I for the dgrad
+        StageMark mark(MOE_STAGE_OPERANDS_BWD1, stream);
+        if (mx) MOE_TRY(launch_mx_quantize(w.dh, c.T * c.k, 2 * (int64_t)c.I, w.dhmx, stream));
+        MOE_TRY(prepare_segments(c, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I, nullptr,
+                                 nullptr, mx, w.tA, stream));
+        MOE_TRY(prepare_segments(c, w.sched, saved->offsets, x, c.H, saved->row_map, nullptr, mx,
+                                 w.tB, stream));
+    }
+    // dgrad, then dW1
+    if (mx) {
+        if (c.T > 0) MOE_TRY(run_mx_gemm(MOE_GEMM_UP_DGRAD, g, stream));
         MOE_TRY(run_mx_gemm(MOE_GEMM_UP_WGRAD, g, stream));
+    } else {
+        if (c.T > 0) MOE_TRY(run_gemm(MOE_GEMM_UP_DGRAD, g, stream));
+        MOE_TRY(run_gemm(MOE_GEMM_UP_WGRAD, g, stream));
     }
     if (c.T == 0) {
         if (dWr && Wr) MOE_TRY(launch_fill_f32(dWr, (int64_t)c.E * c.H, 0.f, stream));

@@ -120,7 +120,6 @@ struct GemmArgs {
     const int32_t *counts, *offsets, *row_map;
     const float *topk_w;
     const uint16_t *x, *dy, *w1, *w2;
-    const uint16_t *xg, *dyw;  // per sorted row: x[tok], bf16(topk_w * dy[tok])
     const float *wrow;         // per sorted row: topk_w of its slot
     uint16_t *h, *a, *dh;
     float *o, *dw_part, *dxp;
@@ -140,6 +139,11 @@ struct GemmArgs {
     // operand's row count, K = its routed rows padded to 128)
     const uint8_t *dyq, *dys, *dhq, *dhs, *w2cq, *w2cs, *w1cq, *w1cs;
     const uint8_t *segA, *segB;
+    // bf16 weight gradients: each expert's rows of the two operands
+    // transposed into K-major 128-deep chunks, [R][128] and [C][128] each,
+    // expert e's first at R (C) * 128 * mt_off128[e] elements (see
+    // launch_transpose_segments)
+    const uint16_t *tA, *tB;
 };
 int32_t dgrad2_cols(int32_t I);
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
@@ -170,16 +174,18 @@ struct ColQuant {
     uint8_t *dst;
 };
 hipError_t launch_mx_quantize_cols(const ColQuant &q, int64_t max_chunks, hipStream_t s);
+// bf16: the same expert segments (offsets / mt128 mode) transposed without
+// quantising, into dst in 128-row chunks: chunk j of expert e is [C][128]
+// at C * 128 * (mt128[e] + j) elements, rows past its count zero.
+hipError_t launch_transpose_segments(const ColQuant &q, int64_t max_chunks, uint16_t *dst,
+                                     hipStream_t s);
 // zero the weight gradient of every expert without rows (overwrite mode)
 hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *counts, void *dW,
                              int32_t bf16, hipStream_t s);
 
-// backward pre-pass: per sorted row r (slot f = row_map[r], token f / k):
-// wrow[r] = topk_w[f] (1 when topk_w is null; stored if wrow); xg[r] = x[token]
-// (if xg); dyw[r] = bf16(wrow * dy[token]) (if dyw)
-hipError_t launch_gather_rows(int64_t M, int32_t k, int32_t H, const int32_t *row_map,
-                              const float *topk_w, const uint16_t *x, const uint16_t *dy,
-                              uint16_t *xg, uint16_t *dyw, float *wrow, hipStream_t s);
+// wrow[r] = topk_w[row_map[r]], the routing weight of each sorted row
+hipError_t launch_row_weights(int64_t M, const int32_t *row_map, const float *topk_w, float *wrow,
+                              hipStream_t s);
 
 // elementwise / reductions
 hipError_t launch_combine(int64_t T, int32_t k, int32_t H, const float *o, const float *w,

@@ -40,41 +40,20 @@ hipError_t launch_combine(int64_t T, int32_t k, int32_t H, const float *o, const
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------- gather rows ----
-// One block per sorted row; 16-byte columns.
-__global__ __launch_bounds__(256) void k_gather_rows(int32_t k, int32_t H, const int32_t *row_map,
-                                                     const float *topk_w, const uint16_t *x,
-                                                     const uint16_t *dy, uint16_t *xg,
-                                                     uint16_t *dyw, float *wrow)
+// ---------------------------------------------------------- row weights ----
+// wrow[r] = topk_w[row_map[r]]: the routing weight of each sorted row.
+__global__ __launch_bounds__(256) void k_row_weights(int64_t M, const int32_t *row_map,
+                                                     const float *topk_w, float *wrow)
 {
-    const int64_t r = blockIdx.x;
-    const int32_t f = row_map[r];
-    const int64_t t = f / k;
-    const float w = topk_w ? topk_w[f] : 1.0f;
-    if (threadIdx.x == 0 && wrow) wrow[r] = w;
-    const int H8 = H / 8;
-    const u32x4_t *xs = (const u32x4_t *)(x + t * H);
-    const u32x4_t *ds = (const u32x4_t *)(dy + t * H);
-    u32x4_t *xo = (u32x4_t *)(xg + r * H);
-    u32x4_t *dout = (u32x4_t *)(dyw + r * H);
-    for (int c = threadIdx.x; c < H8; c += blockDim.x) {
-        if (xg) xo[c] = xs[c];
-        if (dyw) {
-            u32x4_t v = ds[c], o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                o[q] = pack_bf2(bf2f((uint16_t)(v[q] & 0xffffu)) * w, bf2f((uint16_t)(v[q] >> 16)) * w);
-            dout[c] = o;
-        }
-    }
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r < M) wrow[r] = topk_w[row_map[r]];
 }
 
-hipError_t launch_gather_rows(int64_t M, int32_t k, int32_t H, const int32_t *row_map,
-                              const float *topk_w, const uint16_t *x, const uint16_t *dy,
-                              uint16_t *xg, uint16_t *dyw, float *wrow, hipStream_t s)
+hipError_t launch_row_weights(int64_t M, const int32_t *row_map, const float *topk_w, float *wrow,
+                              hipStream_t s)
 {
     if (M <= 0) return hipSuccess;
-    k_gather_rows<<<(unsigned)M, 256, 0, s>>>(k, H, row_map, topk_w, x, dy, xg, dyw, wrow);
+    k_row_weights<<<(unsigned)ceil_div(M, 256), 256, 0, s>>>(M, row_map, topk_w, wrow);
     return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@
 // indices are remapped so that each of the 8 XCDs works on a contiguous run
 // of tiles (neighbouring tiles share operand panels in that XCD's L2).
 #include "bwd_epi.h"
+#include "segtile.h"
 #include "swiglu_epi.h"
 
 namespace moe {
@@ -178,13 +179,61 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
 }
 
 // =========================================================================
+// Weight-gradient operands: the rows of each expert, transposed into a
+// K-major matrix in 128-deep chunks: chunk j of expert e is [C][128]
+// (element (c, k) at c * 128 + k; rows past the expert's count zero), at
+// C * 128 * (mt128[e] + j) elements.  A block takes one chunk's 128 rows x
+// 64 columns through LDS (rows gathered and scaled on the way when asked)
+// and writes 16 contiguous KB.  Four lanes share an output row (one column
+// of the source): lane b of the four holds rows 32 i + 8 b .. 32 i + 8 b + 7
+// for i = 0..3, so each 16-byte store of a wave writes sixteen 64-byte runs
+// of one 4 KB span.  The LDS rows are padded to 66 elements so that the
+// column reads of the four lanes fall in different banks.
+// =========================================================================
+__global__ __launch_bounds__(256) void k_transpose_segments(ColQuant q, uint16_t *dst)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tile[SEG_ROWS][66];
+    const int nct = (int)(q.C / 64);
+    const int ct = blockIdx.x % nct;
+    __shared__ int32_t mt_s[SEG_MAX_E + 1];
+    seg_stage_table(q, mt_s);
+    __syncthreads();
+    SegPos p;
+    if (!seg_locate(q, mt_s, blockIdx.x / nct, p)) return;
+    seg_load_tile(q, p, ct, tile);
+    __syncthreads();
+    const int b = threadIdx.x & 3, c = threadIdx.x >> 2;
+    uint16_t *o = dst + q.C * SEG_ROWS * (p.chunk0 + p.j) + (ct * 64 + c) * SEG_ROWS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r0 = 32 * i + 8 * b;
+        uint32_t z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            z[e] = (uint32_t)tile[r0 + 2 * e][c] | ((uint32_t)tile[r0 + 2 * e + 1][c] << 16);
+        *(u32x4_t *)(o + r0) = u32x4_t{z[0], z[1], z[2], z[3]};
+    }
+}
+
+hipError_t launch_transpose_segments(const ColQuant &q, int64_t max_chunks, uint16_t *dst,
+                                     hipStream_t s)
+{
+    const int64_t blocks = max_chunks * (q.C / 64);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_transpose_segments, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    return hipGetLastError();
+}
+
+// =========================================================================
 // Weight gradients (K-grouped over each expert's rows).
 //   DOWN:  dW2[e, hh, i] (+)= sum_r topk_w(r) dy[tok(r), hh] a[r, i]
 //   UP:    dW1[e, n, hh] (+)= sum_r dh[r, n] x[tok(r), hh]
-// Output tile rows come from operand A, columns from operand B; both are
-// transposed loads over k = routed row.  The token rows are read from
-// per-sorted-row copies (dyw = topk_w * dy[tok], xg = x[tok]) written by the
-// gather pre-pass, so the k loop has no index loads.
+// Output tile rows come from operand A (tA: w*dy or dh), columns from
+// operand B (tB: a or x), both the expert's K-major chunks written by
+// k_transpose_segments, so the tile is the forward one: row-contiguous
+// copies and 16-byte fragment reads, no index loads, no partial stage.
+// Stage s (64 k) of a row r lies at byte (s/2) * rows * 256 + r * 256 +
+// (s%2) * 128 of the expert's area.
 // =========================================================================
 template <class C, bool UP>
 __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
@@ -209,24 +258,35 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     const int64_t gr = nR - first < GR ? nR - first : GR;
     const int64_t in = rest - grp * (int64_t)GR * nC;
     const int rt = (int)(first + in % gr), ct = (int)(in / gr);
-    const int64_t seg0 = g.offsets[e], seg1 = g.offsets[e + 1];
-    const int64_t cnt = seg1 - seg0;
     const int64_t r0 = (int64_t)rt * C::BM, c0 = (int64_t)ct * C::BN;
-    const int lane = threadIdx.x & 63;
-    const int64_t dW_off = (int64_t)e * R * Cc;
-    void *dWv = UP ? g.dW1 : g.dW2;
-    // Operands are row-major per sorted row: A rows of length R, B rows of
-    // length Cc (DOWN: w*dy gathered, a;  UP: dh, x gathered); k = sorted row
-    // of this expert, so the loaders start at row seg0 and stop at seg1.
-    const uint16_t *Ab = (UP ? g.dh : g.dyw) + seg0 * R;
-    const uint16_t *Bb = (UP ? g.xg : g.a) + seg0 * Cc;
-    NLoad<C::BM, C::NT> la;
-    NLoad<C::BN, C::NT> lb;
-    la.init(Ab, R, r0, R, wave_uniform_id(), lane);
-    lb.init(Bb, Cc, c0, Cc, wave_uniform_id(), lane);
+    const int lane = threadIdx.x & 63, wave = wave_uniform_id();
+    const int32_t *mt = g.sched.mt_off128;
+    const int nst = 2 * (mt[e + 1] - mt[e]);  // 64-k stages
+    KLoad<C::BM, C::NT> la;
+    KLoad<C::BN, C::NT> lb;
+    la.init(g.tA + (int64_t)R * SEG_ROWS * mt[e], wave);
+    lb.init(g.tB + (int64_t)Cc * SEG_ROWS * mt[e], wave);
+#pragma unroll
+    for (int q = 0; q < la.NI; ++q) {
+        int64_t r = r0 + la.row(q, lane);
+        if (r >= R) r = R - 1;
+        la.set(q, lane, (uint32_t)(r * SEG_ROWS * 2));
+    }
+#pragma unroll
+    for (int q = 0; q < lb.NI; ++q) {
+        int64_t n = c0 + lb.row(q, lane);
+        if (n >= Cc) n = Cc - 1;
+        lb.set(q, lane, (uint32_t)(n * SEG_ROWS * 2));
+    }
+    auto stage_off = [](int s, int64_t rows) { return (int64_t)(s >> 1) * rows * 256 + (s & 1) * 128; };
     Acc<C> acc;
-    mainloop<C, true, true, true>(lds, cnt, la, lb, acc);
-    wgrad_epilogue<C>(acc, lds, r0, c0, R, Cc, dW_off, dWv, g.dw_acc, g.dw_bf16);
+    pipeline<C, false, false, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
+        lds, 0, nst,
+        [&](int q, int s, lds_t *As) { la.issue_one(q, As, 0, BK, la.base + stage_off(s, R)); },
+        [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, 0, BK, lb.base + stage_off(s, Cc)); },
+        [](int, lds_t *, lds_t *) {}, acc);
+    wgrad_epilogue<C>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2, g.dw_acc,
+                      g.dw_bf16);
 }
 
 // ---------------------------------------------------------- empty experts ----
@@ -257,18 +317,16 @@ hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *count
 // 256x256 output tiles computed by 8 waves (two a SIMD).  Wave tiles are
 // 128 rows x 64 columns where the column operand is read with transposing LDS
 // reads (down_dgrad, up_dgrad: the transposed operand then supplies the
-// smaller fragment count) and for up_swiglu; 64 x 128 elsewhere.  The
-// M-grouped ops stream expert weights as their B operand and get three B
-// stage buffers (all 160 KB of LDS); the weight gradients keep two (a third
-// would spill their registers).
+// smaller fragment count), for up_swiglu and for the weight gradients;
+// 64 x 128 for down.  Every op takes three B stage buffers (all 160 KB of
+// LDS): the B copies of a stage get two stages to land.
 using Tall = TileCfg<256, 256, 128, 64, 3>;
 using Wide3 = TileCfg<256, 256, 64, 128, 3>;
-using Wide = TileCfg<256, 256, 64, 128>;
 using UpCfg = Tall;
 using DownCfg = Wide3;
 using DownDgradCfg = Tall;
 using UpDgradCfg = Tall;
-using WgradCfg = Wide;
+using WgradCfg = Tall;
 
 int32_t dgrad2_cols(int32_t I) { return (int32_t)ceil_div(I, DownDgradCfg::BN); }
 

@@ -41,6 +41,7 @@
 // 2g of the row's 4 scale bytes: low byte for step 0, high byte for step 1
 // (selected by the instruction's op_sel).
 #include "bwd_epi.h"
+#include "segtile.h"
 #include "swiglu_epi.h"
 
 namespace moe {
@@ -130,57 +131,23 @@ hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint
 // its scale, gathered through LDS into the group's word.
 __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[128][64];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[SEG_ROWS][64];
     __shared__ uint32_t sc[4][64];
     const int nct = (int)(q.C / 64);
-    const int64_t L = blockIdx.x / nct;
     const int ct = blockIdx.x % nct;
-    int64_t j, r0, len, Kp, rowbase;
-    uint8_t *codes, *scales;
-    if (!q.offsets) {
-        Kp = ceil_div(q.R, MX_GROUP) * MX_GROUP;
-        const int64_t per = Kp / MX_GROUP;
-        if (L >= (int64_t)q.nseg * per) return;
-        const int64_t sg = L / per;
-        j = L % per;
-        r0 = sg * q.R + j * MX_GROUP;
-        len = q.R - j * MX_GROUP < MX_GROUP ? q.R - j * MX_GROUP : MX_GROUP;
-        rowbase = sg * q.C;
-        codes = q.dst;
-        scales = q.dst + (int64_t)q.nseg * q.C * Kp;
-    } else {
-        if (L >= q.mt128[q.nseg]) return;
-        int lo = 0, hi = q.nseg;  // largest e with mt128[e] <= L
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (q.mt128[mid] <= L) lo = mid; else hi = mid;
-        }
-        j = L - q.mt128[lo];
-        r0 = q.offsets[lo] + j * MX_GROUP;
-        const int64_t rem = q.offsets[lo + 1] - r0;
-        len = rem < MX_GROUP ? rem : MX_GROUP;
-        Kp = (int64_t)MX_GROUP * (q.mt128[lo + 1] - q.mt128[lo]);
-        rowbase = 0;
-        codes = q.dst + q.C * 132 * (int64_t)q.mt128[lo];
-        scales = codes + q.C * Kp;
-    }
+    __shared__ int32_t mt_s[SEG_MAX_E + 1];
+    seg_stage_table(q, mt_s);
+    __syncthreads();
+    SegPos p;
+    if (!seg_locate(q, mt_s, blockIdx.x / nct, p)) return;
+    // uniform batches form one MX matrix [nseg*C, Kp]; experts one each, at
+    // C * 132 bytes per 128-row chunk before them
+    const int64_t rowbase = q.offsets ? 0 : p.seg * q.C;
+    uint8_t *codes = q.offsets ? q.dst + q.C * 132 * p.chunk0 : q.dst;
+    uint8_t *scales = codes + (q.offsets ? q.C : (int64_t)q.nseg * q.C) * p.Kp;
+    const int64_t j = p.j, Kp = p.Kp;
     const int t = threadIdx.x;
-    for (int i = t; i < 128 * 8; i += 256) {
-        const int r = i >> 3, qd = i & 7;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (r < len) {
-            int64_t sr = r0 + r;
-            const float wr = q.rw ? q.rw[sr] : 1.f;
-            if (q.gather) sr = q.gather[sr] / q.gk;
-            v = *(const u32x4_t *)(q.src + sr * q.C + ct * 64 + qd * 8);
-            if (q.rw) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = pack_bf2(wr * bf2f((uint16_t)(v[e] & 0xffffu)), wr * bf2f((uint16_t)(v[e] >> 16)));
-            }
-        }
-        *(u32x4_t *)&tile[r][qd * 8] = v;
-    }
+    seg_load_tile(q, p, ct, tile);
     __syncthreads();
     const int c = t & 63, b = t >> 6;
     float v[32];
@@ -193,11 +160,11 @@ __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
     const int X = mx_block_exp(amax);
     uint32_t w[8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * p]);
+    for (int h = 0; h < 4; ++h) {
+        const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * h]);
         const uint64_t c8 = e4m3_codes8(v8, X);
-        w[2 * p] = (uint32_t)c8;
-        w[2 * p + 1] = (uint32_t)(c8 >> 32);
+        w[2 * h] = (uint32_t)c8;
+        w[2 * h + 1] = (uint32_t)(c8 >> 32);
     }
     const int64_t orow = rowbase + ct * 64 + c;
     uint8_t *dstc = codes + orow * Kp + j * MX_GROUP + b * 32;

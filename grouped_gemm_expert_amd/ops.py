@@ -138,7 +138,7 @@ SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspac
 STAGES = {"up_swiglu": 0, "down": 1, "down_dgrad": 2, "up_dgrad": 3, "down_wgrad": 4,
           "up_wgrad": 5, "router_proj": 6, "router": 7, "permute": 8, "combine": 9,
           "router_bwd": 10, "unpermute": 11, "router_grads": 12, "mx_quant": 13,
-          "mx_quant_bwd2": 14, "mx_quant_bwd1": 15}
+          "operands_bwd2": 14, "operands_bwd1": 15}
 
 
 def moe_set_stage_events(stage: int, start, stop):

@@ -460,8 +460,8 @@ enum {
     MOE_STAGE_UNPERMUTE = 11,    /* dx from the expert path */
     MOE_STAGE_ROUTER_GRADS = 12, /* dx += dlogits . Wr, dWr */
     MOE_STAGE_MX_QUANT = 13,     /* MXFP8 quantisation (moe_mx_quantize / _t; x in the MX forward) */
-    MOE_STAGE_MX_QUANT_BWD2 = 14, /* MXFP8 backward stage 2: dy, and dW2's operands */
-    MOE_STAGE_MX_QUANT_BWD1 = 15, /* MXFP8 backward stage 1: dh, and dW1's operands */
+    MOE_STAGE_OPERANDS_BWD2 = 14, /* backward stage 2: dW2's operands per expert (MX: and dy) */
+    MOE_STAGE_OPERANDS_BWD1 = 15, /* backward stage 1: dW1's operands per expert (MX: and dh) */
     MOE_STAGE_COUNT = 16
 };
 
