@@ -188,7 +188,9 @@ moe_status moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *
  *   MOE_GEMM_UP_WGRAD    dW1[e] (+)= sum_r dh[r]^T x[tok(r)]
  * Weight gradients are fp32 or bf16 (dw_dtype) and overwritten
  * (dw_accumulate = 0; empty experts get exact zeros) or accumulated into
- * (dw_accumulate = 1; empty experts untouched).
+ * (dw_accumulate = 1; empty experts untouched).  The two weight-gradient ops
+ * first write each expert's rows of their operands (dy gathered and scaled
+ * by topk_w, and a; or dh and x gathered), transposed, into the workspace.
  * dw_part has moe_dw_part_cols(cfg) columns per row.
  */
 enum {
