@@ -35,6 +35,7 @@ int64_t mx_bytes(int64_t rows, int64_t K) { return rows * mx_kp(K) + mx_scale_by
 
 struct FwdWs {
     float *prob_part;
+    int32_t *cnt_part;
     int32_t *chunk_hist;
     Sched sched;
     float *wrow;
@@ -93,6 +94,7 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     const int64_t M = c.T * c.k;
     FwdWs w;
     w.prob_part = cv.take<float>(router_blocks(c.T) * c.E);
+    w.cnt_part = cv.take<int32_t>(router_blocks(c.T) * c.E);
     w.chunk_hist = cv.take<int32_t>(permute_chunks(M) * c.E);
     w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
@@ -323,6 +325,7 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
     ra.counts = counts;
     ra.aux = aux;
     ra.prob_part = w.prob_part;
+    ra.cnt_part = w.cnt_part;
     StageMark mark(MOE_STAGE_ROUTER, stream);
     MOE_TRY(launch_router(ra, stream));
     return MOE_OK;

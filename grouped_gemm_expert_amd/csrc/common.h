@@ -94,7 +94,8 @@ struct RouterArgs {
     const float *logits, *bias;
     float *sel, *topk_w;
     int32_t *topk_idx, *counts;
-    float *aux, *prob_part;  // prob_part [nblk, E]
+    float *aux, *prob_part;  // prob_part [nblk, E]: per-block aux column sums
+    int32_t *cnt_part;       // [nblk, E]: per-block expert counts
 };
 int64_t router_blocks(int64_t T);
 hipError_t launch_router(const RouterArgs &a, hipStream_t s);

@@ -39,10 +39,12 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s)
 
 // -------------------------------------------------------------- router ----
 // One wavefront per token; a block holds 4 waves and walks TOK_PER_BLOCK
-// tokens, accumulating the aux column sums of its tokens in registers.
+// tokens, accumulating the aux column sums of its tokens in registers and
+// their expert counts in LDS (no global atomics: a skewed router would
+// serialise them on a few addresses); both go out as per-block partials.
 // Expert e lives in lane e % 64, register slot e / 64.
 constexpr int RT_WAVES = 4;
-constexpr int RT_TOK_PER_WAVE = 8;
+constexpr int RT_TOK_PER_WAVE = 2;  // a token is a serial chain: keep many waves
 constexpr int RT_TOK_PER_BLOCK = RT_WAVES * RT_TOK_PER_WAVE;
 
 int64_t router_blocks(int64_t T) { return ceil_div(T, RT_TOK_PER_BLOCK); }
@@ -52,8 +54,11 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
 {
     __shared__ float sS[RT_WAVES][64 * EPL];
     __shared__ float red[RT_WAVES][64 * EPL];
+    __shared__ int32_t bcnt[64 * EPL];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = p.E, k = p.k;
+    for (int e = threadIdx.x; e < 64 * EPL; e += blockDim.x) bcnt[e] = 0;
+    __syncthreads();
     float colsum[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) colsum[q] = 0.f;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
             else w = p.scale * my_val / zsel;
             p.topk_idx[t * k + lane] = my_idx;
             p.topk_w[t * k + lane] = w;
-            if (my_idx >= 0) atomicAdd(&p.counts[my_idx], 1);
+            if (my_idx >= 0) atomicAdd(&bcnt[my_idx], 1);
         }
         // aux probabilities: softmax p, or s / sum_e s for the sigmoid router
         if (p.score == MOE_SOFTMAX) {
@@ -198,27 +203,53 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
 #pragma unroll
         for (int w = 0; w < RT_WAVES; ++w) v += red[w][e];
         p.prob_part[(int64_t)blockIdx.x * E + e] = v;
+        p.cnt_part[(int64_t)blockIdx.x * E + e] = bcnt[e];
     }
 }
 
-// aux = coeff * E / (k T^2) * sum_e counts[e] * P[e],  P[e] = sum of the
-// block partials in block order.  One block of 1024 threads.
+// counts[e] = the sum of the block counts; aux = coeff * E / (k T^2) *
+// sum_e counts[e] * P[e],  P[e] = the sum of the block column sums.  One
+// block of 1024 threads: expert e's partials are split into S = 1024 / E
+// slices (block b in slice b % S), each summed by one thread, and the slices
+// are added in slice order; then the experts' terms by a fixed-order tree.
+// Deterministic.
 __global__ __launch_bounds__(1024) void k_aux_finalize(RouterArgs p, int64_t nblk)
 {
+    __shared__ float part[1024];
+    __shared__ int32_t cpart[1024];
     __shared__ double red[1024];
-    double v = 0.0;
-    for (int e = threadIdx.x; e < p.E; e += blockDim.x) {
+    const int E = p.E, S = 1024 / E;  // E <= 1024 (moe_check_config)
+    const int i = threadIdx.x;
+    if (i < E * S) {
+        const int e = i / S, sl = i % S;
         float P = 0.f;
-        for (int64_t b = 0; b < nblk; ++b) P += p.prob_part[b * p.E + e];
-        v += (double)p.counts[e] * (double)P;
+        int32_t n = 0;
+        for (int64_t b = sl; b < nblk; b += S) {
+            P += p.prob_part[b * E + e];
+            n += p.cnt_part[b * E + e];
+        }
+        part[i] = P;
+        cpart[i] = n;
     }
-    red[threadIdx.x] = v;
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    double v = 0.0;
+    if (i < E) {
+        float P = 0.f;
+        int32_t n = 0;
+        for (int sl = 0; sl < S; ++sl) {
+            P += part[i * S + sl];
+            n += cpart[i * S + sl];
+        }
+        p.counts[i] = n;
+        v = (double)n * (double)P;
+    }
+    red[i] = v;
+    __syncthreads();
+    for (int st = 512; st > 0; st >>= 1) {
+        if (i < st) red[i] += red[i + st];
         __syncthreads();
     }
-    if (threadIdx.x == 0) {
+    if (i == 0) {
         double T = (double)p.T;
         p.aux[0] = (float)((double)p.aux_coeff * (double)p.E / ((double)p.k * T * T) * red[0]);
     }
@@ -226,8 +257,7 @@ __global__ __launch_bounds__(1024) void k_aux_finalize(RouterArgs p, int64_t nbl
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 {
-    hipError_t err = launch_fill_i32(a.counts, a.E, 0, s);
-    if (err != hipSuccess) return err;
+    hipError_t err;
     int64_t nblk = router_blocks(a.T);
     int epl = (int)ceil_div(a.E, 64);
     if (epl <= 1) k_router_select<1><<<(unsigned)nblk, 256, 0, s>>>(a);
