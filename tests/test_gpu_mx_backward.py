@@ -286,3 +286,67 @@ def test_mx_backward_zero_tokens():
                         dW2, ws)
     torch.cuda.synchronize()
     assert not dW1.any() and not dW2.any() and not dWr.any()
+
+
+def test_mx_graph_capture_replays_to_eager():
+    """The MXFP8 forward + backward captured into one HIP graph (stages, on
+    the cached MX weights) replays to the eager one-call results, replay
+    after replay, with eager work in between.  (Unlike the pages' fp8 op,
+    which holds a cross-rank handshake, nothing here keeps the path out of a
+    graph.)"""
+    from grouped_gemm_expert_amd import ops
+    w = inputs.WORKLOADS["mid_sigmoid"]
+    hz.say(f"mx graph {inputs.describe(w)}")
+    d = hz.to_device(inputs.make_inputs(w, seed=7))
+    cfg = ops.config_from_workload(w)
+    cache = ops.MxWeightCache(backward=True)
+    cache.get(d["w1"], d["w2"])
+    outs = ["y", "aux", "dx", "dl", "dWr", "dW1", "dW2"]
+
+    def alloc():
+        return dict(saved=ops.alloc_saved(cfg), y=torch.empty((w.T, w.H), device="cuda"),
+                    aux=torch.empty((1,), device="cuda"), dx=torch.empty((w.T, w.H), device="cuda"),
+                    dl=torch.empty((w.T, w.E), device="cuda"), dWr=torch.empty((w.E, w.H), device="cuda"),
+                    dW1=torch.empty((w.E, 2 * w.I, w.H), device="cuda"),
+                    dW2=torch.empty((w.E, w.H, w.I), device="cuda"), da=torch.ones((1,), device="cuda"),
+                    wsf=ops.workspace(cfg, "fwd"), wsb=ops.workspace(cfg, "bwd"))
+
+    def one_call(t):
+        ops.moe_forward_mx(cfg, d["x"], d["Wr"], d["bias"], cache.w1_mx, cache.w2_mx, t["y"], t["aux"],
+                           t["saved"], t["wsf"])
+        ops.moe_backward_mx(cfg, t["saved"], d["x"], d["Wr"], cache.w1t_mx, cache.w2t_mx, d["dy"],
+                            t["da"], t["dx"], t["dl"], t["dWr"], t["dW1"], t["dW2"], t["wsb"])
+
+    def staged(t):
+        ops.moe_stage1_forward_mx(cfg, d["x"], d["Wr"], d["bias"], cache.w1_mx, t["aux"], t["saved"],
+                                  t["wsf"])
+        ops.moe_stage2_forward_mx(cfg, cache.w2_mx, t["saved"], t["y"], t["wsf"])
+        ops.moe_stage2_backward_mx(cfg, t["saved"], cache.w2t_mx, d["dy"], t["dW2"], t["wsb"])
+        ops.moe_stage1_backward_mx(cfg, t["saved"], d["x"], d["Wr"], cache.w1t_mx, t["da"], t["dx"],
+                                   t["dl"], t["dWr"], t["dW1"], t["wsb"])
+
+    ref = alloc()
+    one_call(ref)
+    torch.cuda.synchronize()
+    t = alloc()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up off the default stream before capture
+        staged(t)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        staged(t)
+    torch.cuda.synchronize()
+    other = alloc()
+    for rep in range(3):
+        for k in outs:                       # poison every output before the replay
+            t[k].fill_(float("nan"))
+        g.replay()
+        one_call(other)                      # eager work of the program between replays
+        torch.cuda.synchronize()
+        hz.say(f"mx graph replay {rep}")
+        for k in outs:
+            assert torch.equal(t[k], ref[k]), f"replay {rep} {k}"
+            assert torch.equal(other[k], ref[k]), f"eager {rep} {k}"
