@@ -43,9 +43,9 @@ GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_
 # kernel-name fragment of each grouped-GEMM op in a rocprofv3 trace
 GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k_down_dgrad<",
                 "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<",
-                "up_swiglu_mx": "k_up_swiglu_mx<", "down_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 64>, 1>",
+                "up_swiglu_mx": "k_up_swiglu_mx<", "down_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 128>, 1>",
                 "down_dgrad_mx": "k_down_dgrad_mx<",
-                "up_dgrad_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 64>, 3>",
+                "up_dgrad_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 128>, 3>",
                 "down_wgrad_mx": "k_wgrad_mx<", "up_wgrad_mx": "k_wgrad_mx<"}
 # The measured HBM traffic of the grouped GEMMs lives in this file, next to a
 # hash of the kernel sources it was taken with; a changed kernel reports null.

@@ -207,6 +207,12 @@ struct MxCfg {
 // Eight waves of 128 x 64 (two a SIMD, 256 registers each): 128 accumulator
 // registers and one in-place set of six 32-byte fragments.
 using MxTile = MxCfg<256, 256, 128, 64>;
+// Four waves of 128 x 128 (one a SIMD; 256 accumulators in AGPRs, eight
+// fragments): a third fewer fragment bytes read from LDS per MFMA.  Faster
+// for the kernels whose epilogue is a plain fp32 store (GEMM2, dgrad1:
+// +10% / +6%), slower where the epilogue does per-row work that eight waves
+// share (GEMM1's SwiGLU and MX quantisation, dgrad2, the weight gradients).
+using MxTile4 = MxCfg<256, 256, 128, 128>;
 
 // 4 bytes per lane from a per-lane global address into LDS: lane l writes
 // bytes [4 l, 4 l + 4) of the 256-byte block at dst (address in M0).  Issued
@@ -595,7 +601,8 @@ hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
         hipLaunchKernelGGL(k_up_swiglu_mx<C>, mgrid(g.I, C::BN / 2), dim3(C::NT), 0, s, g);
         break;
     case MOE_GEMM_DOWN:
-        hipLaunchKernelGGL((k_rows_mx<C, MOE_GEMM_DOWN>), mgrid(g.H, C::BN), dim3(C::NT), 0, s, g);
+        hipLaunchKernelGGL((k_rows_mx<MxTile4, MOE_GEMM_DOWN>), mgrid(g.H, MxTile4::BN),
+                           dim3(MxTile4::NT), 0, s, g);
         break;
     case MOE_GEMM_DOWN_DGRAD:
         // the router backward reads dgrad2_cols(I) row-dot partials per row
@@ -603,8 +610,8 @@ hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
         hipLaunchKernelGGL(k_down_dgrad_mx<C>, mgrid(g.I, C::BN), dim3(C::NT), 0, s, g);
         break;
     case MOE_GEMM_UP_DGRAD:
-        hipLaunchKernelGGL((k_rows_mx<C, MOE_GEMM_UP_DGRAD>), mgrid(g.H, C::BN), dim3(C::NT), 0, s,
-                           g);
+        hipLaunchKernelGGL((k_rows_mx<MxTile4, MOE_GEMM_UP_DGRAD>), mgrid(g.H, MxTile4::BN),
+                           dim3(MxTile4::NT), 0, s, g);
         break;
     case MOE_GEMM_DOWN_WGRAD:
         hipLaunchKernelGGL((k_wgrad_mx<C, false>), wgrid(g.H, g.I), dim3(C::NT), 0, s, g);
