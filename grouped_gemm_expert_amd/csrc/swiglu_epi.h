@@ -59,31 +59,42 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
         const int seg = lane >> 4;                     // 0 gate, 1 up, 2 a
         const int64_t col = i0 + 8 * (lane & 15);      // column within I
         const bool live = lane < 48 && col < I && (seg == 2 || h != nullptr);
-        for (int r = wave; r < EPI_ROWS; r += C::NT / 64) {
-            const int64_t m = t.m0 + half * EPI_ROWS + r;
-            if (m >= t.seg_end) break;
-            if (live) {
-                const u32x4_t v = *(const lds_u32x4 *)(lds + soff(r, lane));
-                uint16_t *dst = seg == 2 ? a + m * I + col : h + m * 2 * I + (seg ? I : 0) + col;
-                *(u32x4_t *)dst = v;
-            }
-            if constexpr (MX) {
-                const bool achunk = seg == 2;
-                float f[8];
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (achunk && col < I) v = *(const lds_u32x4 *)(lds + soff(r, lane));
+        // RB rows a wave per pass: their LDS reads issued together, then the
+        // stores (and the MX encoding, which every lane runs: rows past the
+        // segment are only masked at the store)
+        constexpr int NW = C::NT / 64, RB = 4;
+        static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
+        for (int r0 = wave; r0 < EPI_ROWS; r0 += NW * RB) {
+            if (t.m0 + half * EPI_ROWS + r0 >= t.seg_end) break;  // wave-uniform
+            u32x4_t v[RB];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f[2 * q] = bf2f((uint16_t)(v[q] & 0xffffu));
-                    f[2 * q + 1] = bf2f((uint16_t)(v[q] >> 16));
+            for (int b = 0; b < RB; ++b) v[b] = *(const lds_u32x4 *)(lds + soff(r0 + b * NW, lane));
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
+                const bool row_ok = m < t.seg_end;
+                if (live && row_ok) {
+                    uint16_t *dst = seg == 2 ? a + m * I + col : h + m * 2 * I + (seg ? I : 0) + col;
+                    *(u32x4_t *)dst = v[b];
                 }
-                uint32_t sc;
-                const uint64_t c = mx_quant8(f, sc);
-                const uint32_t w = mx_group_word(sc, lane);
-                if (achunk) {
-                    *(uint64_t *)(aq + m * Ip + col) = c;
-                    if (lane == 32)
-                        *(uint32_t *)(as_ + mx_scale_off(m, i0 / MX_GROUP, Ip / MX_GROUP)) = w;
+                if constexpr (MX) {
+                    const bool achunk = seg == 2;
+                    float f[8];
+                    const u32x4_t z = {0u, 0u, 0u, 0u};
+                    const u32x4_t va = (achunk && col < I) ? v[b] : z;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f[2 * q] = bf2f((uint16_t)(va[q] & 0xffffu));
+                        f[2 * q + 1] = bf2f((uint16_t)(va[q] >> 16));
+                    }
+                    uint32_t sc;
+                    const uint64_t c = mx_quant8(f, sc);
+                    const uint32_t w = mx_group_word(sc, lane);
+                    if (achunk && row_ok) {
+                        *(uint64_t *)(aq + m * Ip + col) = c;
+                        if (lane == 32)
+                            *(uint32_t *)(as_ + mx_scale_off(m, i0 / MX_GROUP, Ip / MX_GROUP)) = w;
+                    }
                 }
             }
         }
