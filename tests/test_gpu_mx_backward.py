@@ -200,6 +200,21 @@ def test_mx_backward_matches_oracle(name):
     _check_against_oracle(w, dc, got, r, l64)
 
 
+def test_mx_backward_padded_hidden():
+    """H = 320 and I = 192: both contraction dimensions padded to 128 in the MX
+    matrices (x, dy and the transposed w2 along H; a and dh along I, 2I)."""
+    w = _wl("mid_sigmoid", H=320, I=192, T=300)
+    hz.say(f"mx backward padded {inputs.describe(w)}")
+    dc = inputs.make_inputs(w, seed=9)
+    d = hz.to_device(dc)
+    l32, l64, r = _route(w, dc)
+    got = _run_mx_bwd(w, d, l32)
+    X, W1, W2 = hz.bits(dc["x"]), hz.bits(dc["w1"]), hz.bits(dc["w2"])
+    y_ref = oracle.mx_forward(oracle.MxOperands(X, W1, W2), r["idx"], r["w"])
+    hz.assert_close("padded mx y", got["y"].cpu().numpy(), y_ref, hz.FWD_TOL)  # as the MX forward tests
+    _check_against_oracle(w, dc, got, r, l64, seed=2)
+
+
 def test_mx_backward_two_stages_equal_one_call():
     w = inputs.WORKLOADS["mid_sigmoid"]
     hz.say(f"mx backward stages {inputs.describe(w)}")
