@@ -21,12 +21,20 @@ MOE_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 // fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
 MOE_DEV uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+// Two fp32 -> two bf16 in one 32-bit word (lo in the low half), both rounded
+// to nearest even by a single v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 MOE_DEV uint32_t pack_bf2(float lo, float hi)
 {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){lo, hi}, bf16x2_v));
 }
 
-MOE_DEV float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic function of the SwiGLU activation and its derivative.  The
+// hardware reciprocal (about 1 ulp) replaces the IEEE division's ten-odd
+// instructions: every value it feeds is rounded to bf16 afterwards, and in the
+// GEMM epilogues this arithmetic runs while the matrix cores idle.
+MOE_DEV float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Ranking used everywhere in the router: larger value first, equal values
 // -> lower index first.  idx < 0 marks an empty candidate that never wins.
