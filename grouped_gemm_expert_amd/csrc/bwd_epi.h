@@ -82,35 +82,32 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
 
 // Weight-gradient tile rows r0 .. r0+BM-1 (of R) and columns c0 .. c0+BN-1
 // (of Cc) of the expert whose gradient starts at dW_off elements: dW (+)= the
-// tile, fp32 or bf16, accumulating when acc_mode.
-template <class C>
+// tile, fp32 or bf16, accumulating when acc_mode.  Each wave takes RB rows of
+// a 128-row half.  In accumulate mode the old values of all of a wave's rows
+// of the half are loaded before that half's accumulators go through LDS, so
+// one memory round trip per half overlaps the staging.
+template <class C, int RB = EPI_ROWS / (C::NT / 64)>
 MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c0, int R, int Cc,
                             int64_t dW_off, void *dWv, int32_t acc_mode, int32_t bf16)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    // out through the LDS staging tile, whole rows of dW at a time; in
-    // accumulate mode the old values of RB rows are loaded together
     const int64_t cc = c0 + 4 * lane;
     const bool cok = cc < Cc;
     const int64_t ccc = cok ? cc : 0;
-    constexpr int NW = C::NT / 64, RB = 4;
+    constexpr int NW = C::NT / 64;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
     for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (r0 + half * EPI_ROWS >= R) break;
-        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
-        __syncthreads();
         for (int rb = wave; rb < EPI_ROWS; rb += RB * NW) {
-            f32x4_t v[RB], old[RB];
+            f32x4_t old[RB];
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
-                const int r = rb + b * NW;
-                int64_t rr = r0 + half * EPI_ROWS + r;
+                int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
                 if (rr >= R) rr = R - 1;
                 const int64_t o = dW_off + rr * Cc + ccc;
-                v[b] = epi_read_f32(lds, r, lane);
                 old[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 if (acc_mode) {
                     if (bf16) {
@@ -122,13 +119,17 @@ MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c
                     }
                 }
             }
+            if (rb == wave) {  // first batch: the half goes through LDS meanwhile
+                epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
+                __syncthreads();
+            }
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
                 if (rr >= R) break;
                 if (!cok) continue;
                 const int64_t o = dW_off + rr * Cc + cc;
-                const f32x4_t w = v[b] + old[b];
+                const f32x4_t w = epi_read_f32(lds, rb + b * NW, lane) + old[b];
                 if (bf16)
                     *(uint64_t *)((uint16_t *)dWv + o) = pack_bf4(w[0], w[1], w[2], w[3]);
                 else

@@ -582,8 +582,8 @@ __global__ __launch_bounds__(C::NT) void k_wgrad_mx(GemmArgs g)
     }
     Acc<C> acc;
     mx_mainloop<C>(lds, (int)(Kp / MX_GROUP), la, lb, sp, wave0, acc);
-    wgrad_epilogue<C>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2, g.dw_acc,
-                      g.dw_bf16);
+    wgrad_epilogue<C, 4>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2,
+                         g.dw_acc, g.dw_bf16);
 }
 
 hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
