@@ -12,69 +12,79 @@ namespace moe {
 //   dw_part[m, t.nt] = sum over the tile's columns of dA'[m, i] a[m, i]
 //   dA = wrow[m] dA';  dh[m, i] = dA u sig(g)(1 + g(1 - sig(g))),
 //   dh[m, I + i] = dA silu(g)   (g, u from h; bf16 out)
-template <class C>
+// dA' leaves through the LDS staging tile; lane l then owns columns
+// n0 + 4l .. n0 + 4l + 3 of a row: it loads h (gate, up) and a there, applies
+// the routing weight and the SwiGLU backward, stores dh, and the wave sums
+// dA'.a over the tile's columns of the row (dw_part[m, nt]).  Each wave takes
+// RB rows of a 128-row half at a time; the loads of a batch are issued
+// together (addresses clamped to valid rows), the first batch's before the
+// half is staged, so their latency overlaps the staging.
+template <class C, int RB = EPI_ROWS / (C::NT / 64)>
 MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int64_t n0, int nN,
                              int I, const uint16_t *h, const uint16_t *a, const float *wrow,
                              uint16_t *dh, float *dw_part)
 {
     const int tid = threadIdx.x;
-    // dA' leaves through the LDS staging tile; lane l then owns columns
-    // n0 + 4l .. n0 + 4l + 3 of a row: it loads h (gate, up) and a there,
-    // applies the routing weight and the SwiGLU backward, stores dh, and the
-    // wave sums dA'.a over the tile's columns of the row (dw_part[m, nt]).
-    // The loads of RB rows are issued together (addresses clamped to valid
-    // rows) so that their latencies overlap.
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t col = n0 + 4 * lane;
     const bool cok = col < I;
     const int64_t colc = cok ? col : 0;
-    constexpr int NW = C::NT / 64, RB = 4;
+    constexpr int NW = C::NT / 64;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
+    struct Batch {
+        uint64_t hg[RB], hu[RB], hv[RB];
+        float wgt[RB];
+    };
+    auto load = [&](int half, int r0, Batch &bt) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
+            if (m >= t.seg_end) m = t.seg_end - 1;
+            bt.hg[b] = *(const uint64_t *)(h + m * 2 * I + colc);
+            bt.hu[b] = *(const uint64_t *)(h + m * 2 * I + I + colc);
+            bt.hv[b] = *(const uint64_t *)(a + m * I + colc);
+            bt.wgt[b] = wrow[m];
+        }
+    };
+    auto process = [&](int half, int r0, const Batch &bt) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
+            if (m >= t.seg_end) break;
+            const f32x4_t dap = epi_read_f32(lds, r0 + b * NW, lane);
+            float gv[4], uv[4], av[4], dg[4], du[4];
+            unpack_bf4(bt.hg[b], gv);
+            unpack_bf4(bt.hu[b], uv);
+            unpack_bf4(bt.hv[b], av);
+            float part = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                part += dap[q] * av[q];
+                const float da = bt.wgt[b] * dap[q];
+                const float sg = sigmoidf_(gv[q]);
+                dg[q] = da * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                du[q] = da * gv[q] * sg;
+            }
+            if (cok) {
+                *(uint64_t *)(dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
+                *(uint64_t *)(dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
+            }
+            part = wave_sum(cok ? part : 0.f);
+            if (lane == 0) dw_part[m * nN + t.nt] = part;
+        }
+    };
 #pragma unroll
     for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
+        Batch bt;
+        load(half, wave, bt);  // first batch, in flight while the half is staged
         epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
         __syncthreads();
-        for (int r0 = wave; r0 < EPI_ROWS; r0 += RB * NW) {
-            uint64_t hg[RB], hu[RB], hv[RB];
-            float wgt[RB];
-            f32x4_t dap[RB];
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int r = r0 + b * NW;
-                int64_t m = t.m0 + half * EPI_ROWS + r;
-                if (m >= t.seg_end) m = t.seg_end - 1;
-                hg[b] = *(const uint64_t *)(h + m * 2 * I + colc);
-                hu[b] = *(const uint64_t *)(h + m * 2 * I + I + colc);
-                hv[b] = *(const uint64_t *)(a + m * I + colc);
-                wgt[b] = wrow[m];
-                dap[b] = epi_read_f32(lds, r, lane);
-            }
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
-                if (m >= t.seg_end) break;
-                float gv[4], uv[4], av[4], dg[4], du[4];
-                unpack_bf4(hg[b], gv);
-                unpack_bf4(hu[b], uv);
-                unpack_bf4(hv[b], av);
-                float part = 0.f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    part += dap[b][q] * av[q];
-                    const float da = wgt[b] * dap[b][q];
-                    const float sg = sigmoidf_(gv[q]);
-                    dg[q] = da * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-                    du[q] = da * gv[q] * sg;
-                }
-                if (cok) {
-                    *(uint64_t *)(dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
-                    *(uint64_t *)(dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
-                }
-                part = wave_sum(cok ? part : 0.f);
-                if (lane == 0) dw_part[m * nN + t.nt] = part;
-            }
+        process(half, wave, bt);
+        for (int r0 = wave + RB * NW; r0 < EPI_ROWS; r0 += RB * NW) {
+            load(half, r0, bt);
+            process(half, r0, bt);
         }
         __syncthreads();
     }
@@ -98,43 +108,49 @@ MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c
     const int64_t ccc = cok ? cc : 0;
     constexpr int NW = C::NT / 64;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
+    auto load = [&](int half, int rb, f32x4_t (&old)[RB]) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
+            if (rr >= R) rr = R - 1;
+            const int64_t o = dW_off + rr * Cc + ccc;
+            old[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (acc_mode) {
+                if (bf16) {
+                    float t4[4];
+                    unpack_bf4(*(const uint64_t *)((const uint16_t *)dWv + o), t4);
+                    old[b] = f32x4_t{t4[0], t4[1], t4[2], t4[3]};
+                } else {
+                    old[b] = *(const f32x4_t *)((const float *)dWv + o);
+                }
+            }
+        }
+    };
+    auto store = [&](int half, int rb, const f32x4_t (&old)[RB]) {
+        if (!cok) return;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
+            if (rr >= R) break;
+            const int64_t o = dW_off + rr * Cc + cc;
+            const f32x4_t w = epi_read_f32(lds, rb + b * NW, lane) + old[b];
+            if (bf16)
+                *(uint64_t *)((uint16_t *)dWv + o) = pack_bf4(w[0], w[1], w[2], w[3]);
+            else
+                *(f32x4_t *)((float *)dWv + o) = w;
+        }
+    };
 #pragma unroll
     for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (r0 + half * EPI_ROWS >= R) break;
-        for (int rb = wave; rb < EPI_ROWS; rb += RB * NW) {
-            f32x4_t old[RB];
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
-                if (rr >= R) rr = R - 1;
-                const int64_t o = dW_off + rr * Cc + ccc;
-                old[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (acc_mode) {
-                    if (bf16) {
-                        float t4[4];
-                        unpack_bf4(*(const uint64_t *)((const uint16_t *)dWv + o), t4);
-                        old[b] = f32x4_t{t4[0], t4[1], t4[2], t4[3]};
-                    } else {
-                        old[b] = *(const f32x4_t *)((const float *)dWv + o);
-                    }
-                }
-            }
-            if (rb == wave) {  // first batch: the half goes through LDS meanwhile
-                epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
-                __syncthreads();
-            }
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int64_t rr = r0 + half * EPI_ROWS + rb + b * NW;
-                if (rr >= R) break;
-                if (!cok) continue;
-                const int64_t o = dW_off + rr * Cc + cc;
-                const f32x4_t w = epi_read_f32(lds, rb + b * NW, lane) + old[b];
-                if (bf16)
-                    *(uint64_t *)((uint16_t *)dWv + o) = pack_bf4(w[0], w[1], w[2], w[3]);
-                else
-                    *(f32x4_t *)((float *)dWv + o) = w;
-            }
+        f32x4_t old[RB];
+        load(half, wave, old);  // first batch, in flight while the half is staged
+        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
+        __syncthreads();
+        store(half, wave, old);
+        for (int rb = wave + RB * NW; rb < EPI_ROWS; rb += RB * NW) {
+            load(half, rb, old);
+            store(half, rb, old);
         }
         __syncthreads();
     }

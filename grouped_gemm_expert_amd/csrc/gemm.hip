@@ -144,7 +144,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     lb.init(w2e, I, n0, I, wave0, lane0);
     Acc<C> acc;
     mainloop<C, false, true, false>(lds, H, la, lb, acc);
-    dgrad2_epilogue<C>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
+    dgrad2_epilogue<C, 8>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
 }
 
 // =========================================================================
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
         [&](int q, int s, lds_t *As) { la.issue_one(q, As, 0, BK, la.base + stage_off(s, R)); },
         [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, 0, BK, lb.base + stage_off(s, Cc)); },
         [](int, lds_t *, lds_t *) {}, acc);
-    wgrad_epilogue<C>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2, g.dw_acc,
+    wgrad_epilogue<C, 8>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2, g.dw_acc,
                       g.dw_bf16);
 }
 

@@ -525,7 +525,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad_mx(GemmArgs g)
     }
     Acc<C> acc;
     mx_mainloop<C>(lds, (int)(Hp / MX_GROUP), la, lb, sp, wave0, acc);
-    dgrad2_epilogue<C>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
+    dgrad2_epilogue<C, 4>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
 }
 
 // =========================================================================

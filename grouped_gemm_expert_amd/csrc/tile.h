@@ -499,6 +499,8 @@ MOE_DEV f32x4_t epi_read_f32(const lds_t *lds, int r, int lane)
 
 // out[m][n0 + c] = tile[m - m0][c] for rows m0 <= m < mlim (row stride
 // ncols, ncols a multiple of 4).  Starts and ends on a barrier-free LDS.
+// A wave reads 8 of its rows from LDS at once, then stores them, so the LDS
+// latency is paid once per 8 rows.
 template <class C>
 MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, float *out, int64_t m0, int64_t mlim,
                             int64_t n0, int64_t ncols)
@@ -506,16 +508,25 @@ MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, float *out, int64_t m
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t col = n0 + 4 * lane;
+    constexpr int NW = C::NT / 64, RB = 8;
+    static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
     for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (m0 + half * EPI_ROWS >= mlim) break;
         epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
         __syncthreads();
-        for (int r = wave; r < EPI_ROWS; r += C::NT / 64) {
-            const int64_t m = m0 + half * EPI_ROWS + r;
-            if (m >= mlim) break;
-            if (col < ncols) *(f32x4_t *)(out + m * ncols + col) = epi_read_f32(lds, r, lane);
-        }
+        if (col < ncols)
+            for (int r0 = wave; r0 < EPI_ROWS; r0 += RB * NW) {
+                f32x4_t v[RB];
+#pragma unroll
+                for (int b = 0; b < RB; ++b) v[b] = epi_read_f32(lds, r0 + b * NW, lane);
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    const int64_t m = m0 + half * EPI_ROWS + r0 + b * NW;
+                    if (m >= mlim) break;
+                    *(f32x4_t *)(out + m * ncols + col) = v[b];
+                }
+            }
         __syncthreads();
     }
 }
