@@ -19,16 +19,31 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int32_t k, int32_t H
         wts[threadIdx.x] = w ? w[t * k + threadIdx.x] : 1.0f;
     }
     __syncthreads();
+    // o is read once and y written once: non-temporal accesses keep them
+    // from displacing cached data; two column chunks per thread keep twice
+    // the loads in flight
     const int H4 = H / 4;
     const f32x4_t *o4 = (const f32x4_t *)o;
     f32x4_t *y4 = (f32x4_t *)(y + t * H);
-    for (int c = threadIdx.x; c < H4; c += blockDim.x) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int nt = blockDim.x;
+    int c = threadIdx.x;
+    for (; c + nt < H4; c += 2 * nt) {
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
-            f32x4_t v = o4[(int64_t)rows[j] * H4 + c];
-            acc += wts[j] * v;
+            const f32x4_t *src = o4 + (int64_t)rows[j] * H4 + c;
+            const f32x4_t v0 = __builtin_nontemporal_load(src);
+            const f32x4_t v1 = __builtin_nontemporal_load(src + nt);
+            acc0 += wts[j] * v0;
+            acc1 += wts[j] * v1;
         }
-        y4[c] = acc;
+        __builtin_nontemporal_store(acc0, y4 + c);
+        __builtin_nontemporal_store(acc1, y4 + c + nt);
+    }
+    for (; c < H4; c += nt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j)
+            acc += wts[j] * __builtin_nontemporal_load(o4 + (int64_t)rows[j] * H4 + c);
+        __builtin_nontemporal_store(acc, y4 + c);
     }
 }
 
