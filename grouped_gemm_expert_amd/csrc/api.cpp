@@ -875,6 +875,9 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
     GemmArgs g = gemm_args(c, a, w.sched);
     g.tA = w.tA;
     g.tB = w.tB;
+    // dgrad1's per-row partials of dx go out in bf16 (half the bytes for the
+    // GEMM's epilogue and the un-permute); dx itself is summed in fp32
+    g.dxp_bf16 = (uint16_t *)w.dxp;
     const bool mx = w1t_mx != nullptr;
     if (mx) {
         set_mx_bwd(g, c, w);
@@ -928,7 +931,7 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
     }
     {
         StageMark mark(MOE_STAGE_UNPERMUTE, stream);
-        MOE_TRY(launch_combine(c.T, c.k, c.H, w.dxp, nullptr, saved->pos, dx, stream));
+        MOE_TRY(launch_combine_bf16(c.T, c.k, c.H, g.dxp_bf16, nullptr, saved->pos, dx, stream));
     }
     if (Wr) {
         StageMark mark(MOE_STAGE_ROUTER_GRADS, stream);

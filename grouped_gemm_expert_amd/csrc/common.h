@@ -132,6 +132,9 @@ struct GemmArgs {
     const float *wrow;         // per sorted row: topk_w of its slot
     uint16_t *h, *a, *dh;
     float *o, *dw_part, *dxp;
+    // when set, dgrad1 writes its per-row partials of dx here in bf16
+    // instead of to dxp (the fused backward; the per-op entry point keeps fp32)
+    uint16_t *dxp_bf16;
     void *dW1, *dW2;
     int32_t dw_bf16, dw_acc;
     Sched sched;
@@ -199,6 +202,9 @@ hipError_t launch_row_weights(int64_t M, const int32_t *row_map, const float *to
 // elementwise / reductions
 hipError_t launch_combine(int64_t T, int32_t k, int32_t H, const float *o, const float *w,
                           const int32_t *pos, float *y, hipStream_t s);
+// the same with bf16 rows o (the backward's un-permute of bf16 dx partials)
+hipError_t launch_combine_bf16(int64_t T, int32_t k, int32_t H, const uint16_t *o, const float *w,
+                               const int32_t *pos, float *y, hipStream_t s);
 hipError_t launch_swiglu(int32_t backward, int64_t M, int32_t I, const uint16_t *h,
                          const float *da, uint16_t *out, hipStream_t s);
 struct RouterBwdArgs {

@@ -8,7 +8,17 @@ namespace moe {
 // --------------------------------------------------------------- combine ----
 // y[t, :] = sum_j w[t, j] * o[pos[t*k + j], :], j ascending, fp32.
 // One block per token, float4 columns.  Deterministic (no atomics).
-__global__ __launch_bounds__(256) void k_combine(int64_t T, int32_t k, int32_t H, const float *o,
+// Rows of o in fp32 or bf16 (InT = uint16_t: 8-byte loads of 4 values).
+MOE_DEV f32x4_t load4_nt(const float *p) { return __builtin_nontemporal_load((const f32x4_t *)p); }
+MOE_DEV f32x4_t load4_nt(const uint16_t *p)
+{
+    const uint64_t v = __builtin_nontemporal_load((const uint64_t *)p);
+    return f32x4_t{bf2f((uint16_t)(v & 0xffffu)), bf2f((uint16_t)((v >> 16) & 0xffffu)),
+                   bf2f((uint16_t)((v >> 32) & 0xffffu)), bf2f((uint16_t)(v >> 48))};
+}
+
+template <class InT>
+__global__ __launch_bounds__(256) void k_combine(int64_t T, int32_t k, int32_t H, const InT *o,
                                                  const float *w, const int32_t *pos, float *y)
 {
     __shared__ int32_t rows[32];
@@ -23,16 +33,15 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int32_t k, int32_t H
     // from displacing cached data; two column chunks per thread keep twice
     // the loads in flight
     const int H4 = H / 4;
-    const f32x4_t *o4 = (const f32x4_t *)o;
     f32x4_t *y4 = (f32x4_t *)(y + t * H);
     const int nt = blockDim.x;
     int c = threadIdx.x;
     for (; c + nt < H4; c += 2 * nt) {
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < k; ++j) {
-            const f32x4_t *src = o4 + (int64_t)rows[j] * H4 + c;
-            const f32x4_t v0 = __builtin_nontemporal_load(src);
-            const f32x4_t v1 = __builtin_nontemporal_load(src + nt);
+            const InT *src = o + (int64_t)rows[j] * H + 4 * c;
+            const f32x4_t v0 = load4_nt(src);
+            const f32x4_t v1 = load4_nt(src + 4 * nt);
             acc0 += wts[j] * v0;
             acc1 += wts[j] * v1;
         }
@@ -41,8 +50,7 @@ __global__ __launch_bounds__(256) void k_combine(int64_t T, int32_t k, int32_t H
     }
     for (; c < H4; c += nt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j)
-            acc += wts[j] * __builtin_nontemporal_load(o4 + (int64_t)rows[j] * H4 + c);
+        for (int j = 0; j < k; ++j) acc += wts[j] * load4_nt(o + (int64_t)rows[j] * H + 4 * c);
         __builtin_nontemporal_store(acc, y4 + c);
     }
 }
@@ -51,7 +59,15 @@ hipError_t launch_combine(int64_t T, int32_t k, int32_t H, const float *o, const
                           const int32_t *pos, float *y, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    k_combine<<<(unsigned)T, 256, 0, s>>>(T, k, H, o, w, pos, y);
+    k_combine<float><<<(unsigned)T, 256, 0, s>>>(T, k, H, o, w, pos, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(int64_t T, int32_t k, int32_t H, const uint16_t *o, const float *w,
+                               const int32_t *pos, float *y, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    k_combine<uint16_t><<<(unsigned)T, 256, 0, s>>>(T, k, H, o, w, pos, y);
     return hipGetLastError();
 }
 

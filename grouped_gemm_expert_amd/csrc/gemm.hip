@@ -148,7 +148,8 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
 }
 
 // =========================================================================
-// dgrad of GEMM1:  dxp[r, c] = dh[r] . w1[e, :, c]   (fp32 out)
+// dgrad of GEMM1:  dxp[r, c] = dh[r] . w1[e, :, c]   (fp32 out, or bf16 to
+// g.dxp_bf16)
 // =========================================================================
 template <class C>
 __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
@@ -175,7 +176,8 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     lb.init(w1e, H, n0, H, wave0, lane0);
     Acc<C> acc;
     mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
-    store_tile_f32<C>(acc, lds, g.dxp, t.m0, t.seg_end, n0, H);
+    if (g.dxp_bf16) store_tile_f32<C>(acc, lds, g.dxp_bf16, t.m0, t.seg_end, n0, H);
+    else store_tile_f32<C>(acc, lds, g.dxp, t.m0, t.seg_end, n0, H);
 }
 
 // =========================================================================

@@ -498,11 +498,14 @@ MOE_DEV f32x4_t epi_read_f32(const lds_t *lds, int r, int lane)
 }
 
 // out[m][n0 + c] = tile[m - m0][c] for rows m0 <= m < mlim (row stride
-// ncols, ncols a multiple of 4).  Starts and ends on a barrier-free LDS.
-// A wave reads 8 of its rows from LDS at once, then stores them, so the LDS
-// latency is paid once per 8 rows.
-template <class C>
-MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, float *out, int64_t m0, int64_t mlim,
+// ncols, ncols a multiple of 4), fp32 or (OutT = uint16_t) bf16 with
+// nearest-even rounding.  Starts and ends on a barrier-free LDS.  A wave
+// reads 8 of its rows from LDS at once, then stores them, so the LDS latency
+// is paid once per 8 rows.
+MOE_DEV void store4(float *p, f32x4_t v) { *(f32x4_t *)p = v; }
+MOE_DEV void store4(uint16_t *p, f32x4_t v) { *(uint64_t *)p = pack_bf4(v[0], v[1], v[2], v[3]); }
+template <class C, class OutT = float>
+MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, OutT *out, int64_t m0, int64_t mlim,
                             int64_t n0, int64_t ncols)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -524,7 +527,7 @@ MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, float *out, int64_t m
                 for (int b = 0; b < RB; ++b) {
                     const int64_t m = m0 + half * EPI_ROWS + r0 + b * NW;
                     if (m >= mlim) break;
-                    *(f32x4_t *)(out + m * ncols + col) = v[b];
+                    store4(out + m * ncols + col, v[b]);
                 }
             }
         __syncthreads();
