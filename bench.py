@@ -79,7 +79,7 @@ def stage_bytes(w, stage, with_router_weight):
         "permute": 2 * M * 4 + 2 * M * 4 + 2 * (E + 1) * 4,
         "combine": M * H * 4 + T * H * 4 + M * 8,
         "router_bwd": T * E * 4 * 2 + M * 12,
-        "unpermute": M * H * 4 + T * H * 4 + M * 4,
+        "unpermute": M * H * 2 + T * H * 4 + M * 4,   # dx partials in bf16
     }.get(stage)
 
 
