@@ -40,6 +40,9 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (the MX block-scaled ops run
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_wgrad"]
+# a forward workload (the few-large experts one): the forward's stages only
+FWD_STAGES = ["router_proj", "router", "permute", "up_swiglu", "down", "combine"]
+METRIC_FWD = "MoE layer fwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
 # kernel-name fragment of each grouped-GEMM op in a rocprofv3 trace
 GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k_down_dgrad<",
                 "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<",
@@ -97,19 +100,23 @@ def run_gpu(args, w):
     y = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
     aux = torch.empty((1,), dtype=torch.float32, device=dev)
     wsf = ops.workspace(cfg, "fwd", dev)
-    wsb = ops.workspace(cfg, "bwd", dev)
-    dx = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
-    dl = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
-    dWr = torch.empty((w.E, w.H), dtype=torch.float32, device=dev) if d["Wr"] is not None else None
-    dW1 = torch.zeros((w.E, 2 * w.I, w.H), dtype=torch.float32, device=dev)
-    dW2 = torch.zeros((w.E, w.H, w.I), dtype=torch.float32, device=dev)
+    bwd = w.backward
+    wsb = ops.workspace(cfg, "bwd", dev) if bwd else None
+    dx = torch.empty((w.T, w.H), dtype=torch.float32, device=dev) if bwd else None
+    dl = torch.empty((w.T, w.E), dtype=torch.float32, device=dev) if bwd else None
+    dWr = (torch.empty((w.E, w.H), dtype=torch.float32, device=dev)
+           if bwd and d["Wr"] is not None else None)
+    dW1 = torch.zeros((w.E, 2 * w.I, w.H), dtype=torch.float32, device=dev) if bwd else None
+    dW2 = torch.zeros((w.E, w.H, w.I), dtype=torch.float32, device=dev) if bwd else None
     d_aux = torch.ones((1,), dtype=torch.float32, device=dev)
     acc = args.dw_mode == "accumulate"
+    stage_list = list(ops.STAGES) if bwd else FWD_STAGES
 
     def step():
         ops.moe_forward(cfg, d["x"], d["Wr"], d["bias"], d["w1"], d["w2"], y, aux, saved, wsf)
-        ops.moe_backward(cfg, saved, d["x"], d["Wr"], d["w1"], d["w2"], d["dy"], d_aux, dx, dl,
-                         dWr, dW1, dW2, wsb, dw_accumulate=acc)
+        if bwd:
+            ops.moe_backward(cfg, saved, d["x"], d["Wr"], d["w1"], d["w2"], d["dy"], d_aux, dx,
+                             dl, dWr, dW1, dW2, wsb, dw_accumulate=acc)
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -118,7 +125,7 @@ def run_gpu(args, w):
 
     K = args.steps
     ev = {s: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(K)] for s in ops.STAGES}
+              for _ in range(K)] for s in stage_list}
     for pairs in ev.values():          # torch creates its HIP events on first record
         for a, b in pairs:
             a.record()
@@ -127,17 +134,17 @@ def run_gpu(args, w):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        for s, sid in ops.STAGES.items():
-            ops.moe_set_stage_events(sid, *ev[s][i])
+        for s in stage_list:
+            ops.moe_set_stage_events(ops.STAGES[s], *ev[s][i])
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for sid in ops.STAGES.values():
-        ops.moe_set_stage_events(sid, None, None)
+    for s in stage_list:
+        ops.moe_set_stage_events(ops.STAGES[s], None, None)
     elapsed = t1 - t0
 
     stage_ms = {}
-    for s in ops.STAGES:
+    for s in stage_list:
         if s == "router_proj" and d["Wr"] is None:
             continue
         if s == "router_grads" and d["Wr"] is None:
@@ -426,15 +433,15 @@ def main():
 
     from grouped_gemm_expert_amd import inputs
     w = inputs.WORKLOADS[args.workload]
-    if not w.backward:
-        raise SystemExit(f"workload {w.name} is forward-only; the metric is fwd+bwd")
     g = run_gpu(args, w)
     K = args.steps
     elapsed = g["elapsed"]
     stage_ms = g["stage_ms"]
+    # a forward workload reports forward tokens/s (not the headline metric)
+    gemm_stages = GEMM_STAGES if w.backward else ["up_swiglu", "down"]
 
-    gemm_ms = {s: stage_ms[s] for s in GEMM_STAGES}
-    total_gemm_flops = sum(gemm_flops(w, s) for s in GEMM_STAGES)
+    gemm_ms = {s: stage_ms[s] for s in gemm_stages}
+    total_gemm_flops = sum(gemm_flops(w, s) for s in gemm_stages)
     gemm_tflops = total_gemm_flops / (sum(gemm_ms.values()) * 1e-3) / 1e12
     dom = max(gemm_ms, key=gemm_ms.get)
     dom_tflops = gemm_flops(w, dom) / (gemm_ms[dom] * 1e-3) / 1e12
@@ -442,7 +449,7 @@ def main():
     stages = {}
     for s, ms in stage_ms.items():
         e = {"ms": round(ms, 4)}
-        if s in GEMM_STAGES:
+        if s in gemm_stages:
             e["TFLOP/s"] = round(gemm_flops(w, s) / (ms * 1e-3) / 1e12, 1)
         else:
             b = stage_bytes(w, s, g["d"]["Wr"] is not None)
@@ -451,7 +458,7 @@ def main():
         stages[s] = e
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.backward else METRIC_FWD,
         "value": round(w.T * K / elapsed, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -465,7 +472,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
                    "n_groups": w.n_groups, "topk_groups": w.topk_groups, "score": w.score,
-                   "dw": f"fp32 {args.dw_mode}", "outputs": "fp32 y/dx, bf16 operands"},
+                   "dw": f"fp32 {args.dw_mode}" if w.backward else "none (forward)",
+                   "outputs": "fp32 y/dx, bf16 operands"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
@@ -477,9 +485,9 @@ def main():
         "stages": stages,
         "active_experts": sum(1 for c in g["counts"] if c > 0),
     }
-    if not args.no_mx:
+    if not args.no_mx and w.backward:
         out["mxfp8"] = run_mx(args, w, g)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.backward:
         out["cpu_baseline"] = cpu_baseline(w, g["d"])
     print(json.dumps(out), flush=True)
 
