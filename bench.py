@@ -53,6 +53,7 @@ GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k
 # The measured HBM traffic of the grouped GEMMs lives in this file, next to a
 # hash of the kernel sources it was taken with; a changed kernel reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
+BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy_deepseek_v3.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
                   for f in ("gemm.hip", "tile.h", "common.h", "swiglu_epi.h", "bwd_epi.h", "mxfmt.h",
                             "mx.hip")]
@@ -286,6 +287,69 @@ def copy_calibration():
     log(f"[bench] copied {COPY_BYTES} bytes 3 times")
 
 
+MEM_KERNELS = ["k_router_select", "k_aux_finalize", "k_hist", "k_scan", "k_scatter", "k_schedule",
+               "k_combine<float>", "k_combine<unsigned short>", "k_row_weights",
+               "k_transpose_segments", "k_router_bwd", "k_mx_quantize(", "k_mx_quantize_cols"]
+
+
+def counter_rows(d, counter):
+    """(dispatch id, kernel name, value, duration us) of one counter in a rocprofv3 --pmc run."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]), us))
+    out.sort()
+    return out
+
+
+def durations(d, counter):
+    return [(n, us) for _, n, _, us in counter_rows(d, counter)]
+
+
+def pmc_busy_summary(busy_dir, out_path, cmds):
+    """MFMA utilisation and clock of the grouped GEMMs from one rocprofv3 --pmc
+    run of SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) and
+    GRBM_GUI_ACTIVE (summed over the 8 XCDs): busy fraction =
+    MFMA_BUSY / (GUI_ACTIVE / 8 * 1024), clock = GUI_ACTIVE / 8 / duration."""
+    busy = counter_rows(busy_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = {i: (n, v, us) for i, n, v, us in counter_rows(busy_dir, "GRBM_GUI_ACTIVE")}
+    L = ["# MFMA utilisation of the grouped GEMMs: DeepSeek-V3-style MoE layer (T=8192 H=7168 "
+         "I=2048 E=256 G=8 kg=4 k=8), MI355X", "", "Commands (from the repository root on the GPU box):",
+         "", "```"] + cmds + ["```", "",
+         "Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+         "clock = GRBM_GUI_ACTIVE / 8 / launch duration. The MFMA-bound rate at that clock is "
+         "4096 bf16 (8192 fp8) flops per CU per clock x 256 CUs; the nominal 2.5 (5.0) PFLOP/s "
+         "assume 2.4 GHz.", "",
+         "| op | launches | MFMA busy | clock (GHz) | peak at that clock (TFLOP/s) |",
+         "|---|---:|---:|---:|---:|"]
+    for stage, frag in GEMM_KERNELS.items():
+        want_up = stage.startswith("up_wgrad")
+        wgrad = stage.startswith(("down_wgrad", "up_wgrad"))
+        sel = [(i, v) for i, n, v, _ in busy if frag in n and
+               (not wgrad or n.split(">")[-2].strip().endswith("true") == want_up)]
+        if not sel:
+            continue
+        fr, ck = [], []
+        for i, v in sel:
+            if i not in gui:
+                continue
+            _, g, us = gui[i]
+            fr.append(v / (g / 8 * 1024))
+            ck.append(g / 8 / (us * 1e3))
+        if not fr:
+            continue
+        f, c = sum(fr) / len(fr), sum(ck) / len(ck)
+        per_clk = 8192 if stage.endswith("_mx") else 4096   # fp8 MFMA: twice the bf16 rate
+        L.append(f"| {stage} | {len(fr)} | {100 * f:.1f}% | {c:.2f} | {per_clk * 256 * c / 1e3:.0f} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
     """Turn four rocprofv3 --pmc runs (bench FETCH_SIZE, bench WRITE_SIZE, copy
     FETCH_SIZE, copy WRITE_SIZE) into the traffic record bench.py reads."""
@@ -322,6 +386,17 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
             continue
         kern[stage] = {"fetch_kib": round(f, 1), "write_kib": round(wr, 1),
                        "hbm_bytes": int(round((f * sf + wr * sw) * 1024))}
+    # the memory-bound kernels of the path: measured bytes per launch and the
+    # rate over the launch's duration in the counter run
+    mem = {}
+    for frag in MEM_KERNELS:
+        fr = [(x, n) for _, n, x in fetch if frag in n]
+        wr_ = [x for _, n, x in write if frag in n]
+        dur = [t for n, t in durations(fetch_dir, "FETCH_SIZE") if frag in n]
+        if not fr or not wr_ or not dur:
+            continue
+        b = (sum(x for x, _ in fr) / len(fr) * sf + sum(wr_) / len(wr_) * sw) * 1024
+        mem[frag] = (b, sum(dur) / len(dur))
     rec = {"source_hash": kernel_source_hash(), "copy_scale_fetch": round(sf, 4),
            "copy_scale_write": round(sw, 4), "kernels": kern}
     L = ["# HBM traffic of the grouped GEMMs: DeepSeek-V3-style MoE layer (T=8192 H=7168 I=2048 "
@@ -334,6 +409,12 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
          "|---|---:|---:|---:|"]
     for k, v in kern.items():
         L.append(f"| {k} | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | {v['hbm_bytes']:,} |")
+    L += ["", "Memory-bound kernels of the path (bytes per launch as above; GB/s over each "
+          "launch's duration in the FETCH_SIZE run, against the 8 TB/s HBM peak):", "",
+          "| kernel | HBM bytes/launch | us/launch | GB/s | % of HBM peak |", "|---|---:|---:|---:|---:|"]
+    for frag, (b, us) in mem.items():
+        L.append(f"| `{frag}` | {b:,.0f} | {us:.1f} | {b / (us * 1e-6) / 1e9:.0f} | "
+                 f"{100 * b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f} |")
     L += ["", "traffic-record: " + json.dumps(rec)]
     with open(out_path, "w") as fh:
         fh.write("\n".join(L) + "\n")
@@ -416,6 +497,9 @@ def main():
                     help="only run the 1 GiB copy that calibrates the PMC byte counters")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the traffic record from four rocprofv3 --pmc output folders")
+    ap.add_argument("--pmc-busy-summary", metavar="DIR",
+                    help="write the MFMA-busy profile from a rocprofv3 --pmc run of "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
     ap.add_argument("--pmc-commands", default="", help="commands recorded with --pmc-summary (;-separated)")
     args = ap.parse_args()
     if args.copy_calibration:
@@ -423,6 +507,10 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, TRAFFIC_FILE, [c.strip() for c in args.pmc_commands.split(";") if c.strip()])
+        return
+    if args.pmc_busy_summary:
+        pmc_busy_summary(args.pmc_busy_summary, BUSY_FILE,
+                         [c.strip() for c in args.pmc_commands.split(";") if c.strip()])
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
