@@ -185,44 +185,53 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
 // K-major matrix in 128-deep chunks: chunk j of expert e is [C][128]
 // (element (c, k) at c * 128 + k; rows past the expert's count zero), at
 // C * 128 * (mt128[e] + j) elements.  A block takes one chunk's 128 rows x
-// 64 columns through LDS (rows gathered and scaled on the way when asked)
-// and writes 16 contiguous KB.  Four lanes share an output row (one column
-// of the source): lane b of the four holds rows 32 i + 8 b .. 32 i + 8 b + 7
-// for i = 0..3, so each 16-byte store of a wave writes sixteen 64-byte runs
-// of one 4 KB span.  The LDS rows are padded to 66 elements so that the
-// column reads of the four lanes fall in different banks.
+// NCT*64 columns through LDS (rows gathered and scaled on the way when
+// asked; each source row gives NCT*128 contiguous bytes) and writes NCT*16
+// contiguous KB.  Four lanes share an output row (one column of the
+// source): lane b of the four holds rows 32 i + 8 b .. 32 i + 8 b + 7 for
+// i = 0..3, so each 16-byte store of a wave writes sixteen 64-byte runs of
+// one 4 KB span.  The LDS rows are padded to 66 elements so that the column
+// reads of the four lanes fall in different banks.
 // =========================================================================
+template <int NCT>
 __global__ __launch_bounds__(256) void k_transpose_segments(ColQuant q, uint16_t *dst)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[SEG_ROWS][66];
-    const int nct = (int)(q.C / 64);
-    const int ct = blockIdx.x % nct;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[NCT * SEG_ROWS][66];
+    const int nct = (int)(q.C / (64 * NCT));
+    const int ct = (blockIdx.x % nct) * NCT;
     __shared__ int32_t mt_s[SEG_MAX_E + 1];
     seg_stage_table(q, mt_s);
     __syncthreads();
     SegPos p;
     if (!seg_locate(q, mt_s, blockIdx.x / nct, p)) return;
-    seg_load_tile(q, p, ct, tile);
+    seg_load_tile<66, NCT>(q, p, ct, tile);
     __syncthreads();
     const int b = threadIdx.x & 3, c = threadIdx.x >> 2;
-    uint16_t *o = dst + q.C * SEG_ROWS * (p.chunk0 + p.j) + (ct * 64 + c) * SEG_ROWS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r0 = 32 * i + 8 * b;
-        uint32_t z[4];
+    for (int t = 0; t < NCT; ++t) {
+        uint16_t *o = dst + q.C * SEG_ROWS * (p.chunk0 + p.j) + ((ct + t) * 64 + c) * SEG_ROWS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            z[e] = (uint32_t)tile[r0 + 2 * e][c] | ((uint32_t)tile[r0 + 2 * e + 1][c] << 16);
-        *(u32x4_t *)(o + r0) = u32x4_t{z[0], z[1], z[2], z[3]};
+        for (int i = 0; i < 4; ++i) {
+            const int r0 = 32 * i + 8 * b;
+            uint32_t z[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                z[e] = (uint32_t)tile[t * SEG_ROWS + r0 + 2 * e][c] |
+                       ((uint32_t)tile[t * SEG_ROWS + r0 + 2 * e + 1][c] << 16);
+            *(u32x4_t *)(o + r0) = u32x4_t{z[0], z[1], z[2], z[3]};
+        }
     }
 }
 
 hipError_t launch_transpose_segments(const ColQuant &q, int64_t max_chunks, uint16_t *dst,
                                      hipStream_t s)
 {
-    const int64_t blocks = max_chunks * (q.C / 64);
+    // two column tiles a block where the columns allow it
+    const bool two = (q.C / 64) % 2 == 0;
+    const int64_t blocks = max_chunks * (q.C / (two ? 128 : 64));
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_transpose_segments, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    if (two) hipLaunchKernelGGL(k_transpose_segments<2>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    else hipLaunchKernelGGL(k_transpose_segments<1>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
     return hipGetLastError();
 }
 

@@ -71,10 +71,12 @@ MOE_DEV bool seg_locate(const ColQuant &q, const int32_t *mt_s, int64_t L, SegPo
 // thread waits for two memory round trips, not eight.  The caller
 // synchronises before reading the tile.  W = 64: 16-byte LDS writes; a
 // padded W (66) takes 4-byte ones.
-template <int W>
+template <int W, int NCT = 1>
 MOE_DEV void seg_load_tile(const ColQuant &q, const SegPos &p, int ct, uint16_t (*tile)[W])
 {
-    constexpr int NU = SEG_ROWS * 8 / 256;
+    // NCT adjacent column tiles (ct .. ct+NCT-1) into tile[NCT*128][W]: one
+    // source row then yields NCT*128 contiguous bytes, all loads issued together
+    constexpr int NU = SEG_ROWS * 8 / 256 * NCT;
     // row indices: the branches are uniform and outside the unrolled loops,
     // so each batch of loads issues back to back; rows past len read row 0
     // of the chunk and are zeroed below
@@ -82,7 +84,7 @@ MOE_DEV void seg_load_tile(const ColQuant &q, const SegPos &p, int ct, uint16_t 
     float wr[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int r = (threadIdx.x + 256 * u) >> 3;
+        const int r = ((threadIdx.x + 256 * u) >> 3) % SEG_ROWS;
         rr[u] = p.r0 + (r < p.len ? r : 0);
         sr[u] = rr[u];
         wr[u] = 1.f;
@@ -101,14 +103,15 @@ MOE_DEV void seg_load_tile(const ColQuant &q, const SegPos &p, int ct, uint16_t 
     u32x4_t v[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-        const int qd = (threadIdx.x + 256 * u) & 7;
-        v[u] = *(const u32x4_t *)(q.src + sr[u] * q.C + ct * 64 + qd * 8);
+        const int qd = (threadIdx.x + 256 * u) & 7, t = (threadIdx.x + 256 * u) / (SEG_ROWS * 8);
+        v[u] = *(const u32x4_t *)(q.src + sr[u] * q.C + (ct + t) * 64 + qd * 8);
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u)
-        if (((threadIdx.x + 256 * u) >> 3) >= p.len) v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if ((((threadIdx.x + 256 * u) >> 3) % SEG_ROWS) >= p.len) v[u] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+        // tile row r of column tile t lands in row t*128 + r
         const int i = threadIdx.x + 256 * u, r = i >> 3, qd = i & 7;
         u32x4_t x = v[u];
         if (q.rw) {
