@@ -125,16 +125,18 @@ hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint
 }
 
 // Column quantiser: a block takes 128 rows (one scale group of the output's
-// k) by 64 columns of a segment into LDS (rows gathered and scaled by a row
-// weight on the way when asked), then each thread quantises one (column,
-// 32-row block): 32 codes, contiguous in the output row of that column, and
-// its scale, gathered through LDS into the group's word.
+// k) by NCT*64 columns of a segment into LDS (rows gathered and scaled by a
+// row weight on the way when asked; each source row gives NCT*128
+// contiguous bytes), then each thread quantises one (column, 32-row block)
+// per column tile: 32 codes, contiguous in the output row of that column,
+// and its scale, gathered through LDS into the group's word.
+template <int NCT>
 __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[SEG_ROWS][64];
-    __shared__ uint32_t sc[4][64];
-    const int nct = (int)(q.C / 64);
-    const int ct = blockIdx.x % nct;
+    __shared__ __attribute__((aligned(16))) uint16_t tile[NCT * SEG_ROWS][64];
+    __shared__ uint32_t sc[NCT][4][64];
+    const int nct = (int)(q.C / (64 * NCT));
+    const int ct = (blockIdx.x % nct) * NCT;
     __shared__ int32_t mt_s[SEG_MAX_E + 1];
     seg_stage_table(q, mt_s);
     __syncthreads();
@@ -147,42 +149,50 @@ __global__ __launch_bounds__(256) void k_mx_quantize_cols(ColQuant q)
     uint8_t *scales = codes + (q.offsets ? q.C : (int64_t)q.nseg * q.C) * p.Kp;
     const int64_t j = p.j, Kp = p.Kp;
     const int t = threadIdx.x;
-    seg_load_tile(q, p, ct, tile);
+    seg_load_tile<64, NCT>(q, p, ct, tile);
     __syncthreads();
     const int c = t & 63, b = t >> 6;
-    float v[32];
-    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        v[i] = bf2f(tile[32 * b + i][c]);
-        amax = fmaxf(amax, fabsf(v[i]));
-    }
-    const int X = mx_block_exp(amax);
-    uint32_t w[8];
+    for (int tt = 0; tt < NCT; ++tt) {
+        float v[32];
+        float amax = 0.f;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * h]);
-        const uint64_t c8 = e4m3_codes8(v8, X);
-        w[2 * h] = (uint32_t)c8;
-        w[2 * h + 1] = (uint32_t)(c8 >> 32);
+        for (int i = 0; i < 32; ++i) {
+            v[i] = bf2f(tile[tt * SEG_ROWS + 32 * b + i][c]);
+            amax = fmaxf(amax, fabsf(v[i]));
+        }
+        const int X = mx_block_exp(amax);
+        uint32_t w[8];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const float (&v8)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * h]);
+            const uint64_t c8 = e4m3_codes8(v8, X);
+            w[2 * h] = (uint32_t)c8;
+            w[2 * h + 1] = (uint32_t)(c8 >> 32);
+        }
+        const int64_t orow = rowbase + (ct + tt) * 64 + c;
+        uint8_t *dstc = codes + orow * Kp + j * MX_GROUP + b * 32;
+        *(u32x4_t *)dstc = u32x4_t{w[0], w[1], w[2], w[3]};
+        *(u32x4_t *)(dstc + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+        sc[tt][b][c] = (uint32_t)(X + 127);
     }
-    const int64_t orow = rowbase + ct * 64 + c;
-    uint8_t *dstc = codes + orow * Kp + j * MX_GROUP + b * 32;
-    *(u32x4_t *)dstc = u32x4_t{w[0], w[1], w[2], w[3]};
-    *(u32x4_t *)(dstc + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
-    sc[b][c] = (uint32_t)(X + 127);
     __syncthreads();
-    if (b == 0) {
-        const uint32_t word = sc[0][c] | (sc[2][c] << 8) | (sc[1][c] << 16) | (sc[3][c] << 24);
+    if (b < NCT) {
+        const int64_t orow = rowbase + (ct + b) * 64 + c;
+        const uint32_t word =
+            sc[b][0][c] | (sc[b][2][c] << 8) | (sc[b][1][c] << 16) | (sc[b][3][c] << 24);
         *(uint32_t *)(scales + mx_scale_off(orow, j, Kp / MX_GROUP)) = word;
     }
 }
 
 hipError_t launch_mx_quantize_cols(const ColQuant &q, int64_t max_chunks, hipStream_t s)
 {
-    const int64_t blocks = max_chunks * (q.C / 64);
+    // two column tiles a block where the columns allow it
+    const bool two = (q.C / 64) % 2 == 0;
+    const int64_t blocks = max_chunks * (q.C / (two ? 128 : 64));
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_mx_quantize_cols, dim3((unsigned)blocks), dim3(256), 0, s, q);
+    if (two) hipLaunchKernelGGL(k_mx_quantize_cols<2>, dim3((unsigned)blocks), dim3(256), 0, s, q);
+    else hipLaunchKernelGGL(k_mx_quantize_cols<1>, dim3((unsigned)blocks), dim3(256), 0, s, q);
     return hipGetLastError();
 }
 
