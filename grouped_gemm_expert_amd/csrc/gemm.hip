@@ -186,12 +186,13 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
 // (element (c, k) at c * 128 + k; rows past the expert's count zero), at
 // C * 128 * (mt128[e] + j) elements.  A block takes one chunk's 128 rows x
 // NCT*64 columns through LDS (rows gathered and scaled on the way when
-// asked; each source row gives NCT*128 contiguous bytes) and writes NCT*16
-// contiguous KB.  Four lanes share an output row (one column of the
-// source): lane b of the four holds rows 32 i + 8 b .. 32 i + 8 b + 7 for
-// i = 0..3, so each 16-byte store of a wave writes sixteen 64-byte runs of
-// one 4 KB span.  The LDS rows are padded to 66 elements so that the column
-// reads of the four lanes fall in different banks.
+// asked; each source row gives NCT*128 contiguous bytes; NCT = 4 where the
+// column count allows) and writes NCT*16 contiguous KB.  Four lanes share an
+// output row (one column of the source): lane b of the four holds rows
+// 32 i + 8 b .. 32 i + 8 b + 7 for i = 0..3, so each 16-byte store of a wave
+// writes sixteen 64-byte runs of one 4 KB span.  The LDS rows are padded to
+// 66 elements so that the column reads of the four lanes fall in different
+// banks.
 // =========================================================================
 template <int NCT>
 __global__ __launch_bounds__(256) void k_transpose_segments(ColQuant q, uint16_t *dst)
@@ -226,12 +227,16 @@ __global__ __launch_bounds__(256) void k_transpose_segments(ColQuant q, uint16_t
 hipError_t launch_transpose_segments(const ColQuant &q, int64_t max_chunks, uint16_t *dst,
                                      hipStream_t s)
 {
-    // two column tiles a block where the columns allow it
-    const bool two = (q.C / 64) % 2 == 0;
-    const int64_t blocks = max_chunks * (q.C / (two ? 128 : 64));
+    // four (else two) column tiles a block where the columns allow it
+    const int nct = (q.C / 64) % 4 == 0 ? 4 : (q.C / 64) % 2 == 0 ? 2 : 1;
+    const int64_t blocks = max_chunks * (q.C / (64 * nct));
     if (blocks <= 0) return hipSuccess;
-    if (two) hipLaunchKernelGGL(k_transpose_segments<2>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
-    else hipLaunchKernelGGL(k_transpose_segments<1>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    if (nct == 4)
+        hipLaunchKernelGGL(k_transpose_segments<4>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    else if (nct == 2)
+        hipLaunchKernelGGL(k_transpose_segments<2>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    else
+        hipLaunchKernelGGL(k_transpose_segments<1>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
     return hipGetLastError();
 }
 
