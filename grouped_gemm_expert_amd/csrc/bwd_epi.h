@@ -93,9 +93,10 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
 // Weight-gradient tile rows r0 .. r0+BM-1 (of R) and columns c0 .. c0+BN-1
 // (of Cc) of the expert whose gradient starts at dW_off elements: dW (+)= the
 // tile, fp32 or bf16, accumulating when acc_mode.  Each wave takes RB rows of
-// a 128-row half.  In accumulate mode the old values of all of a wave's rows
-// of the half are loaded before that half's accumulators go through LDS, so
-// one memory round trip per half overlaps the staging.
+// a 128-row half at a time.  In accumulate mode the old values of a wave's
+// first RB rows are loaded before that half's accumulators go through LDS,
+// so that memory round trip overlaps the staging; the later batches load
+// and store in turn.
 template <class C, int RB = EPI_ROWS / (C::NT / 64)>
 MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c0, int R, int Cc,
                             int64_t dW_off, void *dWv, int32_t acc_mode, int32_t bf16)
