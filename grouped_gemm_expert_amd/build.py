@@ -25,9 +25,16 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
           "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
+# Host-code sanitizers (a CPU test build of the host layer; device code is
+# built as always): every -fsanitize= goes to the host pass only.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def _compile(src: str, verbose: bool, build_dir: str, defines, extra=()) -> str:
     obj = os.path.join(build_dir, src + ".o")
-    cmd = [HIPCC] + COMMON + [f"-D{d}" for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([HIPCC] + COMMON + list(extra) + [f"-D{d}" for d in defines]
+           + ["-c", os.path.join(CSRC, src), "-o", obj])
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -42,15 +49,24 @@ def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 7, out: str = OUT, defines=()) -> str:
+def build(verbose: bool = False, jobs: int = 7, out: str = OUT, defines=(),
+          sanitize_host: bool = False) -> str:
     """Compile every source and link `out`.  `defines` (NAME=VALUE strings) and
-    `out` exist for building tuning variants outside the package."""
+    `out` exist for building variants outside the package; sanitize_host
+    builds the host code with AddressSanitizer and UndefinedBehaviorSanitizer
+    (for CPU tests of the host layer; the process must preload clang's ASan
+    runtime)."""
+    if sanitize_host and out == OUT:
+        raise ValueError("the sanitizer build goes to its own path")
     build_dir = BUILD_DIR if out == OUT else out + ".objs"
     os.makedirs(build_dir, exist_ok=True)
+    extra = HOST_SANITIZE if sanitize_host else ()
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines, extra), SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if sanitize_host:
+        cmd += ["-shared-libsan"] + HOST_SANITIZE
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -36,6 +36,8 @@ int64_t mx_bytes(int64_t rows, int64_t K) { return rows * mx_kp(K) + mx_scale_by
 struct FwdWs {
     float *prob_part;
     int32_t *cnt_part;
+    float *prob_slice;
+    int32_t *cnt_slice;
     int32_t *chunk_hist;
     Sched sched;
     float *wrow;
@@ -95,7 +97,9 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     FwdWs w;
     w.prob_part = cv.take<float>(router_blocks(c.T) * c.E);
     w.cnt_part = cv.take<int32_t>(router_blocks(c.T) * c.E);
-    w.chunk_hist = cv.take<int32_t>(permute_chunks(M) * c.E);
+    w.prob_slice = cv.take<float>(aux_slices(c.T) * c.E);
+    w.cnt_slice = cv.take<int32_t>(aux_slices(c.T) * c.E);
+    w.chunk_hist = cv.take<int32_t>(permute_chunks(M) * (c.E + 1));
     w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
     w.sched.order = cv.take<int32_t>(c.E + 1);
@@ -326,6 +330,8 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
     ra.aux = aux;
     ra.prob_part = w.prob_part;
     ra.cnt_part = w.cnt_part;
+    ra.prob_slice = w.prob_slice;
+    ra.cnt_slice = w.cnt_slice;
     StageMark mark(MOE_STAGE_ROUTER, stream);
     MOE_TRY(launch_router(ra, stream));
     return MOE_OK;
@@ -344,6 +350,41 @@ moe_status moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     MOE_TRY(launch_permute(c.T * c.k, c.E, topk_idx, counts, offsets, row_map, pos, w.chunk_hist,
                            stream));
+    return MOE_OK;
+}
+
+moe_status moe_permute_checked(const moe_config *cfg, const int32_t *topk_idx, int32_t *counts,
+                               int32_t *offsets, int32_t *row_map, int32_t *pos, int32_t *n_bad,
+                               void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const moe_config &c = *cfg;
+    MOE_CHECK(check_ptrs({counts, offsets, n_bad}));
+    if (c.T > 0) MOE_CHECK(check_ptrs({topk_idx, row_map, pos}));
+    size_t need = 0;
+    FwdWs w = carve_fwd(c, ws, &need);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
+    MOE_TRY(launch_permute_checked(c.T * c.k, c.E, topk_idx, counts, offsets, row_map, pos,
+                                   w.chunk_hist, n_bad, stream));
+    return MOE_OK;
+}
+
+moe_status moe_saved_sizes(const moe_config *cfg, size_t sizes[MOE_SAVED_N])
+{
+    MOE_CHECK(moe_check_config(cfg));
+    if (!sizes) return MOE_EINVAL;
+    const moe_config &c = *cfg;
+    const size_t T = (size_t)c.T, E = (size_t)c.E, k = (size_t)c.k, M = T * k;
+    const size_t I = (size_t)c.I;
+    sizes[0] = T * E * sizeof(float);        // logits
+    sizes[1] = M * sizeof(int32_t);          // topk_idx
+    sizes[2] = M * sizeof(float);            // topk_w
+    sizes[3] = E * sizeof(int32_t);          // counts
+    sizes[4] = (E + 1) * sizeof(int32_t);    // offsets
+    sizes[5] = M * sizeof(int32_t);          // row_map
+    sizes[6] = M * sizeof(int32_t);          // pos
+    sizes[7] = M * 2 * I * sizeof(uint16_t); // h
+    sizes[8] = M * I * sizeof(uint16_t);     // a
     return MOE_OK;
 }
 

@@ -104,8 +104,11 @@ struct RouterArgs {
     int32_t *topk_idx, *counts;
     float *aux, *prob_part;  // prob_part [nblk, E]: per-block aux column sums
     int32_t *cnt_part;       // [nblk, E]: per-block expert counts
+    float *prob_slice;       // [aux_slices, E]: the partials summed in slices
+    int32_t *cnt_slice;      // [aux_slices, E]
 };
 int64_t router_blocks(int64_t T);
+int64_t aux_slices(int64_t T);
 hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 
 // permute: histogram / scan / stable scatter
@@ -113,6 +116,12 @@ int64_t permute_chunks(int64_t M);
 hipError_t launch_permute(int64_t M, int32_t E, const int32_t *idx, int32_t *counts,
                           int32_t *offsets, int32_t *row_map, int32_t *pos,
                           int32_t *chunk_hist, hipStream_t s);
+// the same with expert ids checked: a slot whose expert is outside [0, E) is
+// placed nowhere (pos = -1; row_map holds -1 past the placed rows) and
+// counted in *n_bad (device); chunk_hist has E + 1 rows of permute_chunks(M)
+hipError_t launch_permute_checked(int64_t M, int32_t E, const int32_t *idx, int32_t *counts,
+                                  int32_t *offsets, int32_t *row_map, int32_t *pos,
+                                  int32_t *chunk_hist, int32_t *n_bad, hipStream_t s);
 
 // schedule: m-tile prefix sums for the grouped GEMMs and experts sorted by
 // count (descending, ties -> lower index) for the weight-gradient GEMMs

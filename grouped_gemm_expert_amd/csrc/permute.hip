@@ -17,21 +17,30 @@ constexpr int PM_EMAX = 1024;
 
 int64_t permute_chunks(int64_t M) { return ceil_div(M, PM_CHUNK); }
 
-// chunk_hist[e * nchunks + c] = slots of chunk c routed to expert e
+// chunk_hist[e * nchunks + c] = slots of chunk c routed to expert e.
+// CHECKED: a slot whose expert lies outside [0, E) is read as data only and
+// counted in row E (the caller's histogram area then has E + 1 rows); no
+// address is ever formed from it.
+template <bool CHECKED>
 __global__ __launch_bounds__(PM_THREADS) void k_hist(int64_t M, int32_t E, const int32_t *idx,
                                                       int32_t *chunk_hist, int64_t nchunks)
 {
-    __shared__ int32_t hist[PM_EMAX];
-    for (int e = threadIdx.x; e < E; e += PM_THREADS) hist[e] = 0;
+    __shared__ int32_t hist[PM_EMAX + 1];
+    for (int e = threadIdx.x; e <= E; e += PM_THREADS) hist[e] = 0;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * PM_CHUNK;
 #pragma unroll
     for (int i = 0; i < PM_CHUNK / PM_THREADS; ++i) {
         int64_t f = base + threadIdx.x + i * PM_THREADS;
-        if (f < M) atomicAdd(&hist[idx[f]], 1);
+        if (f < M) {
+            int32_t v = idx[f];
+            if (CHECKED && (uint32_t)v >= (uint32_t)E) v = E;
+            atomicAdd(&hist[v], 1);
+        }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += PM_THREADS)
+    const int rows = CHECKED ? E + 1 : E;
+    for (int e = threadIdx.x; e < rows; e += PM_THREADS)
         chunk_hist[(int64_t)e * nchunks + blockIdx.x] = hist[e];
 }
 
@@ -58,104 +67,151 @@ MOE_DEV int32_t block_excl_scan_1024(int32_t v, int32_t *tmp /* >= 16 */, int32_
     return wbase + incl - v;
 }
 
-// One block of 1024 threads: thread e turns its row of chunk_hist into
-// exclusive chunk bases (in place) and its count; then offsets = exclusive
-// scan of counts.
-__global__ __launch_bounds__(1024) void k_scan(int32_t E, int64_t M, int32_t *chunk_hist,
-                                               int64_t nchunks, int32_t *counts,
-                                               int32_t *offsets)
+// One wave per histogram row (expert e, or with CHECKED the out-of-range row
+// E): the row's chunk counts become exclusive chunk bases in place, 64
+// chunks per step with a running carry, and its total goes to counts[e]
+// (row E: *n_bad).
+constexpr int SC_WAVES = 4;
+__global__ __launch_bounds__(64 * SC_WAVES) void k_scan_rows(int32_t rows, int32_t E,
+                                                             int32_t *chunk_hist, int64_t nchunks,
+                                                             int32_t *counts, int32_t *n_bad)
 {
-    __shared__ int32_t tmp[16];
-    const int e = threadIdx.x;
-    int32_t run = 0;
-    if (e < E) {
-        int32_t *row = chunk_hist + (int64_t)e * nchunks;
-        for (int64_t c = 0; c < nchunks; ++c) {
-            int32_t v = row[c];
-            row[c] = run;
-            run += v;
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * SC_WAVES + (threadIdx.x >> 6);
+    if (e >= rows) return;  // wave-uniform
+    int32_t *row = chunk_hist + (int64_t)e * nchunks;
+    int32_t carry = 0;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += 64) {
+        const int64_t c = c0 + lane;
+        const int32_t v = c < nchunks ? row[c] : 0;
+        int32_t incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int32_t o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
         }
-        counts[e] = run;
+        if (c < nchunks) row[c] = carry + incl - v;
+        carry += __shfl(incl, 63, 64);
     }
-    int32_t total;
-    int32_t off = block_excl_scan_1024(e < E ? run : 0, tmp, total);
-    if (e < E) offsets[e] = off;
-    if (e == 0) offsets[E] = (int32_t)M;
+    if (lane == 0) {
+        if (e < E) counts[e] = carry;
+        else *n_bad = carry;
+    }
 }
 
-// Stable scatter.  Wave w of block c handles flat slots
+// Stable scatter.  Every block first turns counts into the exclusive expert
+// offsets in LDS (block 0 also writes them out, offsets[E] = the number of
+// slots placed).  Wave w of block c then handles flat slots
 // [c*1024 + w*256, +256) in 4 rounds of 64 lanes; ranks inside a round come
 // from a match mask built with one ballot per key bit, ranks across rounds
 // from per-wave running counters in LDS, ranks across waves from a prefix
 // over those counters, and ranks across chunks from the scanned histogram.
-__global__ __launch_bounds__(PM_THREADS) void k_scatter(int64_t M, int32_t E,
-                                                         const int32_t *idx,
-                                                         const int32_t *chunk_base,
-                                                         int64_t nchunks,
-                                                         const int32_t *offsets,
-                                                         int32_t *row_map, int32_t *pos)
+// CHECKED: a slot whose expert lies outside [0, E) takes the key of "no
+// slot" (it is placed nowhere) and gets pos = -1.
+template <bool CHECKED>
+__global__ __launch_bounds__(1024) void k_scatter(int64_t M, int32_t E, const int32_t *idx,
+                                                  const int32_t *chunk_base, int64_t nchunks,
+                                                  const int32_t *counts, int32_t *offsets,
+                                                  int32_t *row_map, int32_t *pos)
 {
-    __shared__ int32_t cnt[4][PM_EMAX];
+    __shared__ int32_t cnt[16][PM_EMAX];
+    __shared__ int32_t off_s[PM_EMAX];
+    __shared__ int32_t tmp[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int e = threadIdx.x; e < E; e += PM_THREADS)
+    const int e0 = threadIdx.x;
+    {
+        int32_t total;
+        const int32_t o = block_excl_scan_1024(e0 < E ? counts[e0] : 0, tmp, total);
+        if (e0 < E) off_s[e0] = o;
+        if (blockIdx.x == 0) {
+            if (e0 < E) offsets[e0] = o;
+            if (e0 == 0) offsets[E] = total;
+        }
+    }
+    for (int e = threadIdx.x; e < E; e += 1024)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) cnt[w][e] = 0;
+        for (int w = 0; w < 16; ++w) cnt[w][e] = 0;
     __syncthreads();
 
-    const int64_t base = (int64_t)blockIdx.x * PM_CHUNK + wave * 256;
+    // 16 waves x 64 slots: one round of 64 lanes each
+    const int64_t f = (int64_t)blockIdx.x * PM_CHUNK + wave * 64 + lane;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int32_t key[4], rank[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        int64_t f = base + r * 64 + lane;
-        int32_t kv = (f < M) ? idx[f] : PM_EMAX;  // 11-bit key; PM_EMAX = no slot
-        uint64_t match = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 11; ++b) {
-            uint64_t bb = __ballot((kv >> b) & 1);
-            match &= ((kv >> b) & 1) ? bb : ~bb;
+    int32_t kv = PM_EMAX;  // 11-bit key; PM_EMAX = no slot
+    if (f < M) {
+        kv = idx[f];
+        if (CHECKED && (uint32_t)kv >= (uint32_t)E) {
+            kv = PM_EMAX;
+            pos[f] = -1;
         }
-        int32_t before = __popcll(match & lt_mask);
-        int32_t run = (kv < PM_EMAX) ? cnt[wave][kv] : 0;
-        __builtin_amdgcn_wave_barrier();
-        // the lowest lane of each key group advances the wave's counter
-        if (kv < PM_EMAX && before == 0) cnt[wave][kv] = run + __popcll(match);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        key[r] = kv;
-        rank[r] = run + before;
     }
-    __syncthreads();
+    uint64_t match = ~0ull;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        int32_t kv = key[r];
-        if (kv >= PM_EMAX) continue;
-        int32_t wb = 0;
-        for (int w = 0; w < wave; ++w) wb += cnt[w][kv];
-        int64_t f = base + r * 64 + lane;
-        int32_t dst = offsets[kv] + chunk_base[(int64_t)kv * nchunks + blockIdx.x] + wb + rank[r];
-        row_map[dst] = (int32_t)f;
-        pos[f] = dst;
+    for (int b = 0; b < 11; ++b) {
+        uint64_t bb = __ballot((kv >> b) & 1);
+        match &= ((kv >> b) & 1) ? bb : ~bb;
     }
+    const int32_t rank = __popcll(match & lt_mask);
+    // the lowest lane of each key group writes the wave's count of that key
+    if (kv < PM_EMAX && rank == 0) cnt[wave][kv] = __popcll(match);
+    __syncthreads();
+    if (kv >= PM_EMAX) return;
+    int32_t wb = 0;
+    for (int w = 0; w < wave; ++w) wb += cnt[w][kv];
+    const int32_t dst = off_s[kv] + chunk_base[(int64_t)kv * nchunks + blockIdx.x] + wb + rank;
+    row_map[dst] = (int32_t)f;
+    pos[f] = dst;
+}
+
+template <bool CHECKED>
+static hipError_t permute_impl(int64_t M, int32_t E, const int32_t *idx, int32_t *counts,
+                               int32_t *offsets, int32_t *row_map, int32_t *pos,
+                               int32_t *chunk_hist, int32_t *n_bad, hipStream_t s)
+{
+    const int64_t nch = permute_chunks(M);
+    if (nch > 0) {
+        k_hist<CHECKED><<<(unsigned)nch, PM_THREADS, 0, s>>>(M, E, idx, chunk_hist, nch);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    const int32_t rows = CHECKED ? E + 1 : E;
+    if (nch > 0) {
+        k_scan_rows<<<(unsigned)ceil_div(rows, SC_WAVES), 64 * SC_WAVES, 0, s>>>(
+            rows, E, chunk_hist, nch, counts, n_bad);
+    } else {
+        // no slots: zero counts (and the out-of-range count)
+        hipError_t err = launch_fill_i32(counts, E, 0, s);
+        if (err != hipSuccess) return err;
+        if (CHECKED) err = launch_fill_i32(n_bad, 1, 0, s);
+        if (err != hipSuccess) return err;
+        // offsets from the zero counts
+        k_scatter<CHECKED><<<1, 1024, 0, s>>>(0, E, idx, chunk_hist, 0, counts, offsets,
+                                              row_map, pos);
+        return hipGetLastError();
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (CHECKED) {
+        // rows past the placed slots hold -1
+        err = launch_fill_i32(row_map, M, -1, s);
+        if (err != hipSuccess) return err;
+    }
+    k_scatter<CHECKED><<<(unsigned)nch, 1024, 0, s>>>(M, E, idx, chunk_hist, nch, counts, offsets,
+                                                      row_map, pos);
+    return hipGetLastError();
 }
 
 hipError_t launch_permute(int64_t M, int32_t E, const int32_t *idx, int32_t *counts,
                           int32_t *offsets, int32_t *row_map, int32_t *pos,
                           int32_t *chunk_hist, hipStream_t s)
 {
-    int64_t nch = permute_chunks(M);
-    if (nch > 0) {
-        k_hist<<<(unsigned)nch, PM_THREADS, 0, s>>>(M, E, idx, chunk_hist, nch);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    k_scan<<<1, 1024, 0, s>>>(E, M, chunk_hist, nch, counts, offsets);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess || nch == 0) return err;
-    k_scatter<<<(unsigned)nch, PM_THREADS, 0, s>>>(M, E, idx, chunk_hist, nch, offsets, row_map,
-                                                    pos);
-    return hipGetLastError();
+    return permute_impl<false>(M, E, idx, counts, offsets, row_map, pos, chunk_hist, nullptr, s);
+}
+
+hipError_t launch_permute_checked(int64_t M, int32_t E, const int32_t *idx, int32_t *counts,
+                                  int32_t *offsets, int32_t *row_map, int32_t *pos,
+                                  int32_t *chunk_hist, int32_t *n_bad, hipStream_t s)
+{
+    return permute_impl<true>(M, E, idx, counts, offsets, row_map, pos, chunk_hist, n_bad, s);
 }
 
 // ------------------------------------------------------------- schedule ----

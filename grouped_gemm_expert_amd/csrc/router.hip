@@ -207,13 +207,37 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
     }
 }
 
-// counts[e] = the sum of the block counts; aux = coeff * E / (k T^2) *
-// sum_e counts[e] * P[e],  P[e] = the sum of the block column sums.  One
-// block of 1024 threads: expert e's partials are split into S = 1024 / E
-// slices (block b in slice b % S), each summed by one thread, and the slices
-// are added in slice order; then the experts' terms by a fixed-order tree.
-// Deterministic.
-__global__ __launch_bounds__(1024) void k_aux_finalize(RouterArgs p, int64_t nblk)
+// The router blocks' partials are reduced in two fixed-order steps, so the
+// result is deterministic and no single block walks all of them.
+// Step 1 (k_aux_slices): block s sums router blocks [s*AUX_SLICE,
+// (s+1)*AUX_SLICE) in ascending order, for every expert.
+constexpr int AUX_SLICE = 32;
+
+int64_t aux_slices(int64_t T) { return ceil_div(router_blocks(T), AUX_SLICE); }
+
+__global__ __launch_bounds__(256) void k_aux_slices(RouterArgs p, int64_t nblk)
+{
+    const int E = p.E;
+    const int64_t b0 = (int64_t)blockIdx.x * AUX_SLICE;
+    const int64_t b1 = b0 + AUX_SLICE < nblk ? b0 + AUX_SLICE : nblk;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        float P = 0.f;
+        int32_t n = 0;
+        for (int64_t b = b0; b < b1; ++b) {
+            P += p.prob_part[b * E + e];
+            n += p.cnt_part[b * E + e];
+        }
+        p.prob_slice[blockIdx.x * (int64_t)E + e] = P;
+        p.cnt_slice[blockIdx.x * (int64_t)E + e] = n;
+    }
+}
+
+// Step 2 (one block of 1024 threads): counts[e] = the sum of expert e's
+// slices, P[e] likewise; expert e's slices are split into S = 1024 / E
+// groups (slice s in group s % S), each summed by one thread, and the
+// groups are added in group order; then aux = coeff * E / (k T^2) *
+// sum_e counts[e] * P[e] by a fixed-order tree.
+__global__ __launch_bounds__(1024) void k_aux_finalize(RouterArgs p, int64_t nslice)
 {
     __shared__ float part[1024];
     __shared__ int32_t cpart[1024];
@@ -224,9 +248,9 @@ __global__ __launch_bounds__(1024) void k_aux_finalize(RouterArgs p, int64_t nbl
         const int e = i / S, sl = i % S;
         float P = 0.f;
         int32_t n = 0;
-        for (int64_t b = sl; b < nblk; b += S) {
-            P += p.prob_part[b * E + e];
-            n += p.cnt_part[b * E + e];
+        for (int64_t b = sl; b < nslice; b += S) {
+            P += p.prob_slice[b * E + e];
+            n += p.cnt_slice[b * E + e];
         }
         part[i] = P;
         cpart[i] = n;
@@ -267,7 +291,11 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t s)
     else k_router_select<16><<<(unsigned)nblk, 256, 0, s>>>(a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    k_aux_finalize<<<1, 1024, 0, s>>>(a, nblk);
+    const int64_t nsl = aux_slices(a.T);
+    k_aux_slices<<<(unsigned)nsl, 256, 0, s>>>(a, nblk);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k_aux_finalize<<<1, 1024, 0, s>>>(a, nsl);
     return hipGetLastError();
 }
 

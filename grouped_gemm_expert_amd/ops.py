@@ -78,6 +78,10 @@ def _load():
     lib.moe_router.restype = S
     lib.moe_permute.argtypes = [CFG] + [_P] * 5 + [_P, sz, _P]
     lib.moe_permute.restype = S
+    lib.moe_permute_checked.argtypes = [CFG] + [_P] * 6 + [_P, sz, _P]
+    lib.moe_permute_checked.restype = S
+    lib.moe_saved_sizes.argtypes = [CFG, ctypes.POINTER(sz)]
+    lib.moe_saved_sizes.restype = S
     lib.moe_grouped_gemm.argtypes = [ctypes.c_int32, CFG, ctypes.POINTER(MoeGemmArgs), _P, sz, _P]
     lib.moe_grouped_gemm.restype = S
     lib.moe_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
@@ -128,7 +132,8 @@ def _load():
 _lib = _load()
 
 SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspace_size",
-           "moe_dw_part_cols", "moe_router", "moe_permute", "moe_grouped_gemm", "moe_swiglu",
+           "moe_saved_sizes", "moe_dw_part_cols", "moe_router", "moe_permute",
+           "moe_permute_checked", "moe_grouped_gemm", "moe_swiglu",
            "moe_combine", "moe_forward", "moe_backward", "moe_stage1_forward",
            "moe_stage2_forward", "moe_stage2_backward", "moe_stage1_backward",
            "moe_set_stage_events", "moe_grouped_gemm_mx", "moe_mx_size", "moe_mx_quantize", "moe_stage1_forward_mx",
@@ -222,6 +227,22 @@ def moe_permute(cfg, topk_idx, counts, offsets, row_map, pos, ws, stream=None):
            "moe_permute")
 
 
+def moe_permute_checked(cfg, topk_idx, counts, offsets, row_map, pos, n_bad, ws, stream=None):
+    _check(_lib.moe_permute_checked(ctypes.byref(cfg), _ptr(topk_idx), _ptr(counts),
+                                    _ptr(offsets), _ptr(row_map), _ptr(pos), _ptr(n_bad),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "moe_permute_checked")
+
+
+SAVED_N = 9
+
+
+def moe_saved_sizes(cfg: MoeConfig) -> dict:
+    """Bytes of each tensor of moe_saved, by name."""
+    arr = (ctypes.c_size_t * SAVED_N)()
+    _check(_lib.moe_saved_sizes(ctypes.byref(cfg), arr), "moe_saved_sizes")
+    return {name: int(arr[i]) for i, (name, _) in enumerate(MoeSaved._fields_)}
+
+
 def moe_grouped_gemm(op, cfg, ws, stream=None, dw_dtype=MOE_F32, dw_accumulate=False, **tensors):
     args = MoeGemmArgs()
     for name, t in tensors.items():
@@ -254,21 +275,26 @@ def _saved_struct(saved: dict) -> MoeSaved:
 
 
 def alloc_saved(cfg: MoeConfig, device="cuda") -> dict:
-    """The forward's saved tensors (caller-owned; see moe_saved in moe.h)."""
+    """The forward's saved tensors (caller-owned; see moe_saved in moe.h),
+    sized by moe_saved_sizes and shaped for use from torch."""
     T, E, k, I = cfg.T, cfg.E, cfg.k, cfg.I
     M = T * k
-    i32 = dict(dtype=torch.int32, device=device)
-    return {
-        "logits": torch.empty((T, E), dtype=torch.float32, device=device),
-        "topk_idx": torch.empty((T, k), **i32),
-        "topk_w": torch.empty((T, k), dtype=torch.float32, device=device),
-        "counts": torch.empty((E,), **i32),
-        "offsets": torch.empty((E + 1,), **i32),
-        "row_map": torch.empty((max(M, 1),), **i32),
-        "pos": torch.empty((max(M, 1),), **i32),
-        "h": torch.empty((max(M, 1), 2 * I), dtype=torch.bfloat16, device=device),
-        "a": torch.empty((max(M, 1), I), dtype=torch.bfloat16, device=device),
-    }
+    shapes = {"logits": ((T, E), torch.float32), "topk_idx": ((T, k), torch.int32),
+              "topk_w": ((T, k), torch.float32), "counts": ((E,), torch.int32),
+              "offsets": ((E + 1,), torch.int32), "row_map": ((M,), torch.int32),
+              "pos": ((M,), torch.int32), "h": ((M, 2 * I), torch.bfloat16),
+              "a": ((M, I), torch.bfloat16)}
+    sizes = moe_saved_sizes(cfg)
+    out = {}
+    for name, (shape, dt) in shapes.items():
+        n = 1
+        for d in shape:
+            n *= d
+        if n * torch.tensor([], dtype=dt).element_size() != sizes[name]:
+            raise MoeError(f"moe_saved_sizes disagrees on {name}")
+        # empty tensors still get one element so that every pointer is valid
+        out[name] = torch.empty(shape if n else (1,) + tuple(shape[1:]), dtype=dt, device=device)
+    return out
 
 
 def moe_forward(cfg, x, Wr, bias, w1, w2, y, aux, saved: dict, ws, stream=None):

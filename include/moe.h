@@ -79,9 +79,17 @@ enum { MOE_ROUTE_LEARNED = 0, MOE_ROUTE_EVEN = 1 }; /* expert choice (route_mode
  *                `uniform`, replaces the logits by random values: pass seeded
  *                random logits with Wr = NULL and MOE_ROUTE_LEARNED.)
  * Ties in any ranking go to the lower index (expert or group).
- * Supported: 1 <= k <= E <= 1024, k <= 32, n_groups divides E,
- * 1 <= topk_groups <= n_groups, k <= topk_groups * E / n_groups,
- * H % 64 == 0, I % 64 == 0, T * k < 2^31.
+ * Supported (moe_check_config; anything else returns MOE_EUNSUPPORTED):
+ *   1 <= k <= E <= 1024, k <= 32;
+ *   1 <= n_groups <= 64, n_groups divides E, 1 <= topk_groups <= n_groups,
+ *   and k <= topk_groups * E / n_groups when n_groups > 1;
+ *   H % 64 == 0, I % 64 == 0;
+ *   with M = T*k and W = max(H, 2I):  M * W < 2^31 and W * (T + 128) < 2^31
+ *   (the kernels index a routed-row activation tensor and an expert's
+ *   transposed weight-gradient operands with 32-bit element offsets), and
+ *   2 * I * H < 2^31 (one expert's w1).  At H = 7168 and I = 2048 that is
+ *   T*k <= 299593 and T <= 299465.
+ * Negative sizes, an unknown score or route_mode return MOE_EINVAL.
  */
 typedef struct {
     int64_t T;
@@ -107,6 +115,7 @@ typedef struct {
  *   h        [M,2I] bf16  GEMM1 output per sorted row: gate | up
  *   a        [M,I]  bf16  SwiGLU output per sorted row
  */
+#define MOE_SAVED_N 9  /* tensors in moe_saved, in declaration order */
 typedef struct {
     float *logits;
     int32_t *topk_idx;
@@ -126,6 +135,14 @@ const char *moe_version(void);
 
 /* Validate cfg (returns the status moe_forward would return for it). */
 moe_status moe_check_config(const moe_config *cfg);
+
+/*
+ * Bytes of each tensor of moe_saved for cfg, in declaration order (logits,
+ * topk_idx, topk_w, counts, offsets, row_map, pos, h, a) into sizes[0..8]:
+ * the allocations a caller makes before moe_forward.  MOE_EINVAL when sizes
+ * is NULL; config errors as moe_check_config.
+ */
+moe_status moe_saved_sizes(const moe_config *cfg, size_t sizes[MOE_SAVED_N]);
 
 /*
  * Workspace bytes needed by moe_forward (fwd_bytes) and moe_backward
@@ -166,6 +183,23 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
 moe_status moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *counts,
                        int32_t *offsets, int32_t *row_map, int32_t *pos,
                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_permute with the caller's expert ids checked on the device, for
+ * topk_idx that does not come from moe_router (moe_permute treats an id
+ * outside [0, E) as undefined behaviour).  Every id is read as data only and
+ * never used to form an address unless it lies in [0, E):
+ *   - a slot whose id is outside [0, E) is placed nowhere: pos[f] = -1, it
+ *     adds to no count, and offsets[E] is the number of slots placed;
+ *   - row_map holds -1 at sorted rows past offsets[E];
+ *   - n_bad [1] int32 (device) receives the number of such slots (plain
+ *     store, 0 when every id is valid).
+ * With valid ids every output equals moe_permute's, bit for bit.  Tensors,
+ * workspace and errors as moe_permute; n_bad must be a valid pointer.
+ */
+moe_status moe_permute_checked(const moe_config *cfg, const int32_t *topk_idx, int32_t *counts,
+                               int32_t *offsets, int32_t *row_map, int32_t *pos, int32_t *n_bad,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Grouped GEMMs over the sorted rows of each expert (bf16 MFMA, fp32

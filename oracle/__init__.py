@@ -24,8 +24,8 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
   forward              -- pinned: E=1/k=1 dense SwiGLU MLP, token-permutation
                           invariance, linearity in w2
   expert_rows          -- pinned: y = sum_j w_j o_j against forward
-  backward_tokens, weight_grads, weight_grad_elements, router_weight_grad
-                       -- pinned: central finite differences of the forward and
+  backward_tokens, weight_grads, weight_grad_elements, weight_grad_lines,
+  router_weight_grad   -- pinned: central finite differences of the forward and
                           an independent torch fp64 autograd formulation
   e4m3_values          -- pinned: the E4M3 points the OCP MX format fixes (zero,
                           smallest subnormal, smallest normal, one, 448, NaN),
@@ -37,7 +37,7 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
                        -- pinned: exact integer GEMMs on MX-representable inputs,
                           y = sum_j w_j o_j against mx_forward, the MX error
                           bound against the exact forward
-  mx_backward_tokens, mx_weight_grad_elements
+  mx_backward_tokens, mx_weight_grad_elements, mx_weight_grad_lines
                        -- pinned: a numpy formulation from the quantiser and
                           dense matmuls (expert part of dx, dW1, dW2), the
                           router part through the bf16 oracle's pinned code,
@@ -54,7 +54,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIBRARY may name another build of the same source (the
+# sanitizer build of tests/test_sanitizers.py); it is loaded as it is.
+_LIB_ENV = os.environ.get("MOE_ORACLE_LIBRARY")
+_LIB = _LIB_ENV or os.path.join(_HERE, "libmoe_oracle.so")
 
 SOFTMAX = 0
 SIGMOID = 1
@@ -62,22 +65,30 @@ SIGMOID = 1
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile moe_oracle.c into libmoe_oracle.so (gcc, OpenMP, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+def build(force: bool = True, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile moe_oracle.c into libmoe_oracle.so (gcc, OpenMP, no fast-math),
+    or with sanitize=True into `out` with AddressSanitizer and
+    UndefinedBehaviorSanitizer (a CPU build for tests/test_sanitizers.py)."""
+    lib = out or _LIB
+    if _LIB_ENV and out is None:
+        return lib
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        opt = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"]
+        cmd = (["gcc"] + opt + ["-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+                                "-o", tmp, _SRC, "-lm"])
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if not _LIB_ENV and (not os.path.exists(_LIB) or
+                         os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
         build(force=True)
     lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
@@ -97,6 +108,7 @@ def _load():
                                 i64, P, P, P],
         "oracle_weight_grad_elements": [i64, i32, i32, i32, P, P, P, P, P, P, i64,
                                         P, P, P, P, P],
+        "oracle_weight_grad_lines": [i64, i32, i32, i32, P, P, P, P, P, P, i64, P, P, P, P],
         "oracle_router_weight_grad": [i64, i32, i32, P, P, P],
         "oracle_expert_rows": [i32, i32, i32, P, P, P, P, i64, P, P, P, P, P],
         "oracle_mx_quantize": [i64, i64, P, P, P],
@@ -106,6 +118,8 @@ def _load():
                                       P, P, P, P, P] + [P] * 12 + [i64, P, P, P],
         "oracle_mx_weight_grad_elements": [i64, i32, i32, i32, P, P, P, P] + [P] * 8
                                           + [i64, P, P, P, P, P],
+        "oracle_mx_weight_grad_lines": [i64, i32, i32, i32, P, P, P, P] + [P] * 8
+                                       + [i64, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -283,6 +297,25 @@ def weight_grad_elements(x, w1, w2, idx, w, dy, which, ee, rr, cc) -> np.ndarray
     out = np.empty(which.shape[0], np.float64)
     _load().oracle_weight_grad_elements(T, H, I, k, _p(x), _p(w1), _p(w2), _p(idx), _p(w), _p(dy),
                                         which.shape[0], _p(which), _p(ee), _p(rr), _p(cc), _p(out))
+    return out
+
+
+def weight_grad_lines(x, w1, w2, idx, w, dy, which, ee, rr) -> np.ndarray:
+    """Whole lines of the weight gradients, [n, H] double: row rr of dW1[ee]
+    (which=1) or column rr of dW2[ee] (which=2)."""
+    x = _c(x, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    dy = _c(dy, np.uint16)
+    which, ee, rr = (_c(np.asarray(v), np.int32) for v in (which, ee, rr))
+    T, H = x.shape
+    I = w2.shape[2]
+    k = idx.shape[1]
+    out = np.empty((which.shape[0], H), np.float64)
+    _load().oracle_weight_grad_lines(T, H, I, k, _p(x), _p(w1), _p(w2), _p(idx), _p(w), _p(dy),
+                                     which.shape[0], _p(which), _p(ee), _p(rr), _p(out))
     return out
 
 
@@ -491,4 +524,21 @@ def mx_weight_grad_elements(ops: MxBackwardOperands, x, dy, idx, w, which, ee, r
                                            _p(ops.dyq), _p(ops.dys), _p(ops.w2cq), _p(ops.w2cs),
                                            which.shape[0], _p(which), _p(ee), _p(rr), _p(cc),
                                            _p(out))
+    return out
+
+
+def mx_weight_grad_lines(ops: MxBackwardOperands, x, dy, idx, w, which, ee, rr):
+    """Whole lines of the MXFP8 weight gradients, [n, H] double: row rr of
+    dW1[ee] (which=1) or column rr of dW2[ee] (which=2)."""
+    x = _c(x, np.uint16)
+    dy = _c(dy, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    which, ee, rr = (_c(np.asarray(v), np.int32) for v in (which, ee, rr))
+    T, k = idx.shape
+    out = np.empty((which.shape[0], ops.H), np.float64)
+    _load().oracle_mx_weight_grad_lines(T, ops.H, ops.I, k, _p(x), _p(dy), _p(idx), _p(w),
+                                        _p(ops.xq), _p(ops.xs), _p(ops.w1q), _p(ops.w1s),
+                                        _p(ops.dyq), _p(ops.dys), _p(ops.w2cq), _p(ops.w2cs),
+                                        which.shape[0], _p(which), _p(ee), _p(rr), _p(out))
     return out

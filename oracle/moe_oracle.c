@@ -350,14 +350,14 @@ void oracle_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
 /*            plus aux through p = s/sum s: (a_e - sum a p)/sum s;           */
 /*            dl = ds * s * (1 - s)                                          */
 /*   dxt += sum_e dl[e] Wr[e,:]   (when Wr != NULL)                          */
-/* lt: the token's logits [E]; it: its experts [k]; p, dp: scratch [E].     */
+/* lt: the token's logits [E]; it: its experts [k]; wt: scratch [k];        */
+/* p, dp: scratch [E].                                                       */
 static void router_token_backward(int64_t T, int32_t H, int32_t E, int32_t k, int32_t score,
                                   int32_t renorm, double scale, double coeff, double d_aux,
                                   const float *Wr, const double *lt, const int32_t *it,
-                                  const int32_t *counts, const double *dw, double *p,
-                                  double *dp, double *dl, double *dxt)
+                                  const int32_t *counts, const double *dw, double *wt,
+                                  double *p, double *dp, double *dl, double *dxt)
 {
-    double wt[32];
     token_scores(E, score, lt, p);
     double zsel = 0.0;
     for (int32_t j = 0; j < k; ++j) zsel += p[it[j]];
@@ -481,7 +481,7 @@ void oracle_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E,
 
             /* router */
             router_token_backward(T, H, E, k, score, renorm, scale, coeff, d_aux, Wr,
-                                  logits + t * E, idx + t * k, counts, dw, p, dp,
+                                  logits + t * E, idx + t * k, counts, dw, wt, p, dp,
                                   dlogits + n * E, dxt);
         }
         free(g);
@@ -614,6 +614,60 @@ void oracle_weight_grad_elements(int64_t T, int32_t H, int32_t I, int32_t k,
                 }
             }
         out[q] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole lines of the expert weight gradients, each H long (for full-size    */
+/* shapes: a few lines per expert reach every output tile of its gradient):  */
+/*   which[q] == 1: out[q, h] = dW1[ee[q], rr[q], h]   (a row, n = rr[q])    */
+/*   which[q] == 2: out[q, h] = dW2[ee[q], h, rr[q]]   (a column, i = rr[q]) */
+/* summed over all T tokens; same definitions as oracle_weight_grads:       */
+/*   dW1[e,i,h] = sum dg_i x_t[h], dW1[e,I+i,h] = sum du_i x_t[h],           */
+/*   dW2[e,h,i] = sum w_tj dy_t[h] a_i, over the slots (t,j) with idx = e.   */
+/* out [nl, H] double, overwritten.                                          */
+/* ------------------------------------------------------------------------ */
+void oracle_weight_grad_lines(int64_t T, int32_t H, int32_t I, int32_t k,
+                              const uint16_t *x, const uint16_t *w1,
+                              const uint16_t *w2, const int32_t *idx,
+                              const double *w, const uint16_t *dy, int64_t nl,
+                              const int32_t *which, const int32_t *ee,
+                              const int32_t *rr, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nl; ++q) {
+        const int32_t e = ee[q];
+        const uint16_t *w1e = w1 + (int64_t)e * 2 * I * H;
+        const uint16_t *w2e = w2 + (int64_t)e * H * I;
+        const int32_t i = (which[q] == 2) ? rr[q] : (rr[q] % I);
+        double *line = out + q * H;
+        for (int32_t h = 0; h < H; ++h) line[h] = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t j = 0; j < k; ++j) {
+                if (idx[t * k + j] != e) continue;
+                const uint16_t *xt = x + t * H;
+                const uint16_t *dyt = dy + t * H;
+                const double wj = w[t * k + j];
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; ++h) {
+                    double xv = bf(xt[h]);
+                    g += xv * bf(w1e[(int64_t)i * H + h]);
+                    u += xv * bf(w1e[(int64_t)(I + i) * H + h]);
+                }
+                if (which[q] == 2) {
+                    const double ai = silu(g) * u;
+                    for (int32_t h = 0; h < H; ++h) line[h] += wj * bf(dyt[h]) * ai;
+                } else {
+                    double dA = 0.0;
+                    for (int32_t h = 0; h < H; ++h)
+                        dA += bf(w2e[(int64_t)h * I + i]) * bf(dyt[h]);
+                    dA *= wj;
+                    const double sg = sigmoid(g);
+                    const double d = (rr[q] < I) ? dA * u * sg * (1.0 + g * (1.0 - sg))
+                                                 : dA * silu(g);
+                    for (int32_t h = 0; h < H; ++h) line[h] += d * bf(xt[h]);
+                }
+            }
     }
 }
 
@@ -914,7 +968,8 @@ void oracle_mx_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E, int32
         uint8_t *dhs = (uint8_t *)malloc(2 * (size_t)I / 32 + 1);
         double *p = (double *)malloc(sizeof(double) * (size_t)E);
         double *dp = (double *)malloc(sizeof(double) * (size_t)E);
-        double dw[32];
+        double *dw = (double *)malloc(sizeof(double) * (size_t)k);
+        double *wt = (double *)malloc(sizeof(double) * (size_t)k);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t n = 0; n < ntok; ++n) {
             int64_t t = toks ? toks[n] : n;
@@ -944,7 +999,7 @@ void oracle_mx_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E, int32
                 }
             }
             router_token_backward(T, H, E, k, score, renorm, scale, coeff, d_aux, Wr,
-                                  logits + t * E, idx + t * k, counts, dw, p, dp,
+                                  logits + t * E, idx + t * k, counts, dw, wt, p, dp,
                                   dlogits + n * E, dxt);
         }
         free(g);
@@ -958,6 +1013,8 @@ void oracle_mx_backward_tokens(int64_t T, int32_t H, int32_t I, int32_t E, int32
         free(dhs);
         free(p);
         free(dp);
+        free(dw);
+        free(wt);
     }
 }
 
@@ -1033,5 +1090,76 @@ void oracle_mx_weight_grad_elements(int64_t T, int32_t H, int32_t I, int32_t k,
         free(c2);
         free(m1);
         free(m2);
+    }
+}
+
+/* Whole lines of the MXFP8 weight gradients, each H long:                  */
+/*   which[q] == 1: out[q, h] = dW1[ee[q], rr[q], h]                         */
+/*                            = sum_r MX(dh[:, n])_r MX(xg[:, h])_r          */
+/*   which[q] == 2: out[q, h] = dW2[ee[q], h, rr[q]]                         */
+/*                            = sum_r MX(dyw[:, h])_r MX(a[:, i])_r          */
+/* with the rows r of expert e (its flat slots, ascending) and the same      */
+/* operands and roundings as oracle_mx_weight_grad_elements; every column    */
+/* is quantised in blocks of 32 from the expert's first row.                 */
+void oracle_mx_weight_grad_lines(int64_t T, int32_t H, int32_t I, int32_t k,
+                                 const uint16_t *x, const uint16_t *dy, const int32_t *idx,
+                                 const double *w, const uint8_t *xq, const uint8_t *xs,
+                                 const uint8_t *w1q, const uint8_t *w1s, const uint8_t *dyq,
+                                 const uint8_t *dys, const uint8_t *w2cq, const uint8_t *w2cs,
+                                 int64_t nl, const int32_t *which, const int32_t *ee,
+                                 const int32_t *rr, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nl; ++q) {
+        const int32_t e = ee[q];
+        const int32_t i = which[q] == 2 ? rr[q] : rr[q] % I;
+        int64_t n = 0;
+        for (int64_t f = 0; f < T * k; ++f) n += idx[f] == e;
+        int64_t *slot = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n + 1));
+        double *fixed = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        double *mfixed = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        double *col = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        double *mcol = (double *)malloc(sizeof(double) * (size_t)(n + 1));
+        int64_t r = 0;
+        for (int64_t f = 0; f < T * k; ++f)
+            if (idx[f] == e) slot[r++] = f;
+        /* the column shared by the whole line: a[:, i] or dh[:, n] */
+        for (r = 0; r < n; ++r) {
+            const int64_t f = slot[r], t = f / k;
+            double sg = 0.0, su = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                double xv = mx_value(xq, xs, H, t, h);
+                sg += xv * mx_value(w1q, w1s, H, (int64_t)e * 2 * I + i, h);
+                su += xv * mx_value(w1q, w1s, H, (int64_t)e * 2 * I + I + i, h);
+            }
+            if (which[q] == 2) {
+                fixed[r] = bf16_of(silu(sg) * su);
+            } else {
+                double dAp = 0.0;
+                for (int32_t h = 0; h < H; ++h)
+                    dAp += mx_value(dyq, dys, H, t, h) *
+                           mx_value(w2cq, w2cs, H, (int64_t)e * I + i, h);
+                double dg, du;
+                swiglu_bwd(w[f] * dAp, bf16_of(sg), bf16_of(su), &dg, &du);
+                fixed[r] = bf16_of(rr[q] < I ? dg : du);
+            }
+        }
+        mx_column(fixed, n, mfixed);
+        /* the other operand's column h, for every h */
+        for (int32_t h = 0; h < H; ++h) {
+            for (r = 0; r < n; ++r) {
+                const int64_t f = slot[r], t = f / k;
+                col[r] = which[q] == 2 ? bf16_of(w[f] * bf(dy[t * H + h])) : bf(x[t * H + h]);
+            }
+            mx_column(col, n, mcol);
+            double acc = 0.0;
+            for (r = 0; r < n; ++r) acc += mfixed[r] * mcol[r];
+            out[q * H + h] = acc;
+        }
+        free(slot);
+        free(fixed);
+        free(mfixed);
+        free(col);
+        free(mcol);
     }
 }

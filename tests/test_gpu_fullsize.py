@@ -3,18 +3,22 @@
 configuration the benchmark times: moe_forward from the router weight, then
 moe_backward accumulating into zeroed fp32 weight gradients; and the MXFP8
 forward and backward on the same inputs.  The oracle cannot run the whole
-layer at this size, so it is checked on sampled outputs that it computes one
-by one:
+layer at this size, so it is checked on outputs it computes one by one,
+chosen to reach every tile the kernels compute:
   - routing of every token (bit-exact on all tokens whose fp32 selection is
     not a near-tie under the projection's rounding),
-  - y and dx of sampled tokens, sampled dW1 / dW2 elements of busy experts,
-  - the MX forward's y, dx and dlogits on sampled tokens, and sampled MX dW1 /
-    dW2 elements, against the oracle's MXFP8 path.
+  - y, dx and dlogits of tokens whose slots are the first and last sorted row
+    of every active expert and of 256-row tiles inside them,
+  - whole weight-gradient lines of every active expert: a dW1 row in every
+    256-row band and a dW2 column in every 256-column band (together they
+    reach every 256 x 256 output tile), and exact zeros for every expert
+    without rows,
+  - the MX forward's y, dx and dlogits on fewer of those tokens, and whole MX
+    dW lines of three experts, against the oracle's MXFP8 path.
 Only the experts the samples touch are copied to the host: into full-shape
 zero arrays (np.zeros maps untouched pages lazily, so only those experts take
-memory) for the bf16 oracle and the MXFP8 backward's oracle, which read no
-other expert, and into compact arrays with remapped expert ids for the MXFP8
-forward's oracle."""
+memory) for the oracle calls that index experts by their ids, and into
+compact arrays with remapped expert ids elsewhere."""
 import numpy as np
 import pytest
 import torch
@@ -25,8 +29,8 @@ from tests import harness as hz
 
 pytestmark = pytest.mark.gpu
 
-N_TOK = 4      # sampled tokens
-N_EL = 12      # sampled dW elements per weight and expert
+N_TOK = (64, 32)   # tile-edge tokens: at most, at least
+N_TOK_MX = 16      # tokens of the MXFP8 forward check
 
 
 @pytest.fixture(scope="module")
@@ -63,9 +67,11 @@ def ds():
     idx_gpu = saved["topk_idx"].cpu().numpy()
     same = (idx_gpu == r["idx"]).all(1)
     rng = np.random.default_rng(1)
-    toks = np.sort(rng.choice(np.nonzero(same)[0], size=N_TOK, replace=False))
+    toks = hz.tile_edge_tokens(r, w.k, N_TOK[0], N_TOK[1], rng, allowed=same)
+    toks_mx = toks[np.unique(np.linspace(0, len(toks) - 1, N_TOK_MX).round().astype(int))]
     return dict(w=w, d=d, cfg=cfg, saved=saved, y=y, aux=aux, dx=dx, dl=dl, dW1=dW1, dW2=dW2,
-                X=X, Wr=Wr, bias=bias, l64=l64, r=r, idx_gpu=idx_gpu, same=same, toks=toks)
+                X=X, Wr=Wr, bias=bias, l64=l64, r=r, idx_gpu=idx_gpu, same=same, toks=toks,
+                toks_mx=toks_mx)
 
 
 def _sparse_full(d, experts):
@@ -122,31 +128,26 @@ def test_fullsize_sampled_tokens(ds):
     hz.assert_close("fullsize dlogits", ds["dl"][tk].cpu().numpy(), dl_ref, hz.GRAD_TOL)
 
 
-def test_fullsize_sampled_weight_grads(ds):
+def test_fullsize_weight_grad_lines(ds):
+    """Whole dW lines of every active expert, reaching all its 256 x 256 output
+    tiles, and exact zeros for every expert without rows."""
     w, r = ds["w"], ds["r"]
     counts = r["counts"]
-    ex = np.argsort(-counts, kind="stable")[:2]          # the two busiest experts
-    hz.say(f"fullsize dW: experts {ex.tolist()} with {counts[ex].tolist()} rows")
-    W1s, W2s = _sparse_full(ds["d"], ex)
+    active = np.nonzero(counts)[0]
+    which, ee, rr = hz.weight_grad_line_spec(active, w.I, np.random.default_rng(2))
+    hz.say(f"fullsize dW: {len(which)} lines over {len(active)} active experts "
+           f"({counts[active].tolist()} rows)")
     DY = hz.bits(ds["d"]["dy"])
-    rng = np.random.default_rng(2)
-    which, ee, rr, cc = [], [], [], []
-    for c_e in range(len(ex)):
-        for wh, nr, nc in ((1, 2 * w.I, w.H), (2, w.H, w.I)):
-            which += [wh] * N_EL
-            ee += [int(ex[c_e])] * N_EL
-            rr += rng.integers(0, nr, N_EL).tolist()
-            cc += rng.integers(0, nc, N_EL).tolist()
-    which, ee, rr, cc = (np.array(v, np.int32) for v in (which, ee, rr, cc))
-    ref = oracle.weight_grad_elements(ds["X"], W1s, W2s, r["idx"], r["w"], DY, which, ee, rr, cc)
-    for wh, dW, name in ((1, ds["dW1"], "dW1"), (2, ds["dW2"], "dW2")):
+    ref = hz.oracle_lines(ds["d"], ds["X"], DY, r, which, ee, rr)
+    got = hz.gather_lines(ds["dW1"], ds["dW2"], which, ee, rr)
+    for wh, name in ((1, "dW1"), (2, "dW2")):
         sel = which == wh
-        e_, r_, c_ = ee[sel], rr[sel], cc[sel]
-        # indices checked on the host: the gather below does not check them
-        assert (e_ < dW.shape[0]).all() and (r_ < dW.shape[1]).all() and (c_ < dW.shape[2]).all()
-        got = dW[torch.as_tensor(e_, device="cuda"), torch.as_tensor(r_, device="cuda"),
-                 torch.as_tensor(c_, device="cuda")].cpu().numpy()
-        hz.assert_close(f"fullsize {name} elements", got, ref[sel], hz.GRAD_TOL)
+        hz.assert_close(f"fullsize {name} lines", got[sel], ref[sel], hz.GRAD_TOL)
+    empty = np.nonzero(counts == 0)[0]
+    for e in empty.tolist():
+        for dW in (ds["dW1"], ds["dW2"]):
+            assert float(dW[e].abs().max().cpu()) == 0.0, e
+    hz.say(f"fullsize: {len(empty)} experts without rows have exact-zero dW")
 
 
 @pytest.fixture(scope="module")
@@ -178,17 +179,18 @@ def dsmx(ds):
 
 
 def test_fullsize_mx_forward_sampled_tokens(ds, dsmx):
-    w, r, toks = ds["w"], ds["r"], ds["toks"]
+    """y of tile-edge tokens against the oracle's MXFP8 forward, per element
+    within the block-scaled MFMA's summation-window bound (see
+    harness.assert_mx_y_within_window)."""
+    w, r, toks = ds["w"], ds["r"], ds["toks_mx"]
     d = ds["d"]
     assert np.array_equal(dsmx["saved"]["topk_idx"].cpu().numpy(), ds["idx_gpu"])
     ex = np.unique(r["idx"][toks])
     W1c, W2c = _compact(d, ex)
-    ops_o = oracle.MxOperands(ds["X"][toks], W1c, W2c)
-    idx_c = _remap(r["idx"][toks], ex)
     hz.say(f"fullsize mx: oracle on tokens {toks.tolist()}")
-    y_ref = oracle.mx_forward(ops_o, idx_c, r["w"][toks])
-    hz.assert_close("fullsize mx y", dsmx["y"][torch.as_tensor(toks, device="cuda")].cpu().numpy(),
-                    y_ref, hz.MX_FWD_TOL)
+    y_gpu = dsmx["y"][torch.as_tensor(toks, device="cuda")].cpu().numpy()
+    hz.assert_mx_y_within_window("fullsize mx y", w.I, ds["X"][toks], W1c, W2c,
+                                 _remap(r["idx"][toks], ex), r["w"][toks], y_gpu)
 
 
 def test_fullsize_mx_backward_sampled_tokens(ds, dsmx):
@@ -196,7 +198,7 @@ def test_fullsize_mx_backward_sampled_tokens(ds, dsmx):
     operands that hold only the experts those tokens use (the router part
     needs every logit, so the expert ids are kept)."""
     w, r = ds["w"], ds["r"]
-    toks = ds["toks"][:2]
+    toks = ds["toks_mx"][::max(1, len(ds["toks_mx"]) // 4)][:4]
     ex = np.unique(r["idx"][toks])
     hz.say(f"fullsize mx backward tokens {toks.tolist()}: quantising {len(ex)} experts")
     W1c, W2c = _compact(ds["d"], ex)
@@ -212,30 +214,22 @@ def test_fullsize_mx_backward_sampled_tokens(ds, dsmx):
     hz.assert_close("fullsize mx dlogits", dsmx["dl"][tk].cpu().numpy(), dl_ref, hz.MX_GRAD_TOL)
 
 
-def test_fullsize_mx_backward_sampled_weight_grads(ds, dsmx):
+def test_fullsize_mx_backward_weight_grad_lines(ds, dsmx):
+    """Whole MX dW lines (a dW1 row in every 256-row band, a dW2 column in every
+    256-column band) of the busiest, a median and the least busy active
+    expert, against the oracle's MXFP8 backward."""
     w, r = ds["w"], ds["r"]
     counts = r["counts"]
-    ex = np.argsort(-counts, kind="stable")[:2]          # the two busiest experts
-    hz.say(f"fullsize mx dW: experts {ex.tolist()} with {counts[ex].tolist()} rows")
-    W1c, W2c = _compact(ds["d"], ex)
+    active = np.nonzero(counts)[0]
+    by = active[np.argsort(-counts[active], kind="stable")]
+    experts = np.unique([by[0], by[len(by) // 2], by[-1]])
+    hz.say(f"fullsize mx dW lines: experts {experts.tolist()} with {counts[experts].tolist()} rows")
+    W1c, W2c = _compact(ds["d"], experts)
     DY = hz.bits(ds["d"]["dy"])
-    ops_o = oracle.MxBackwardOperands.from_experts(ds["X"], DY, w.E, ex, W1c, W2c)
-    rng = np.random.default_rng(3)
-    which, ee, rr, cc = [], [], [], []
-    for e in ex:
-        for wh, nr, nc in ((1, 2 * w.I, w.H), (2, w.H, w.I)):
-            which += [wh] * N_EL
-            ee += [int(e)] * N_EL
-            rr += rng.integers(0, nr, N_EL).tolist()
-            cc += rng.integers(0, nc, N_EL).tolist()
-    which, ee, rr, cc = (np.array(v, np.int32) for v in (which, ee, rr, cc))
-    ref = oracle.mx_weight_grad_elements(ops_o, ds["X"], DY, r["idx"], r["w"], which, ee, rr, cc)
+    ops_o = oracle.MxBackwardOperands.from_experts(ds["X"], DY, w.E, experts, W1c, W2c)
+    which, ee, rr = hz.weight_grad_line_spec(experts, w.I, np.random.default_rng(3))
+    ref = oracle.mx_weight_grad_lines(ops_o, ds["X"], DY, r["idx"], r["w"], which, ee, rr)
+    got = hz.gather_lines(dsmx["dW1"], dsmx["dW2"], which, ee, rr)
     for wh, name in ((1, "dW1"), (2, "dW2")):
         sel = which == wh
-        dW = dsmx[name]
-        e_, r_, c_ = ee[sel], rr[sel], cc[sel]
-        # indices checked on the host: the gather below does not check them
-        assert (e_ < dW.shape[0]).all() and (r_ < dW.shape[1]).all() and (c_ < dW.shape[2]).all()
-        got = dW[torch.as_tensor(e_, device="cuda"), torch.as_tensor(r_, device="cuda"),
-                 torch.as_tensor(c_, device="cuda")].cpu().numpy()
-        hz.assert_close(f"fullsize mx {name} elements", got, ref[sel], hz.MX_GRAD_TOL)
+        hz.assert_close(f"fullsize mx {name} lines", got[sel], ref[sel], hz.MX_GRAD_TOL)

@@ -8,15 +8,20 @@ gradients accumulated in fp32 into zeros):
   - skewed        the DeepSeek-V3 shapes with Zipf(1.2) logits supplied
                   (about 20% of the experts get no token, one more than 10%)
 The oracle cannot run these layers whole, so it checks what it can compute one
-output at a time:
+output at a time, chosen to reach every tile the kernels compute:
   - the routing of every token: bit-exact given the same fp32 logits, else
     (router projection on the GPU) explained by the projection's rounding;
-  - aux, and y of sampled tokens;
-  - with the backward: dx and dlogits of sampled tokens, sampled dW1 / dW2
-    elements of the two busiest experts, and exact zeros in the weight
-    gradients of experts without tokens;
+  - aux; y (and with the backward dx, dlogits) of the tokens whose slots are
+    the first and last sorted row of every active expert and of every
+    256-row tile inside it (few_large: all of them, padded to 256 tokens);
+  - whole weight-gradient lines of every active expert: a dW1 row in every
+    256-row band and a dW2 column in every 256-column band, which together
+    reach every 256 x 256 output tile; fine_grained also the complete dW1 and
+    dW2 of its two busiest experts and of its least busy active one;
+  - exact zeros in the weight gradients of every expert without tokens;
   - the same layers through the MXFP8 path against the oracle's MXFP8
-    forward and backward.
+    forward and backward, on fewer samples (the MX oracle decodes every
+    operand element).
 Only the experts the samples touch are copied to the host, into full-shape
 zero arrays (np.zeros maps untouched pages lazily) or compact arrays."""
 import numpy as np
@@ -29,8 +34,9 @@ from tests import harness as hz
 
 pytestmark = pytest.mark.gpu
 
-N_TOK = 4      # sampled tokens
-N_EL = 12      # sampled dW elements per weight and expert
+# tile-edge tokens per configuration: (at most, at least)
+N_TOK = {"few_large": (256, 256), "fine_grained": (256, 64), "skewed": (64, 32)}
+N_TOK_MX = 16   # tokens of the MXFP8 forward check (every config)
 
 
 def _sparse_full(d, experts):
@@ -66,9 +72,11 @@ def run(request):
     idx_gpu = out["saved"]["topk_idx"].cpu().numpy()
     same = (idx_gpu == r["idx"]).all(1)
     rng = np.random.default_rng(1)
-    toks = np.sort(rng.choice(np.nonzero(same)[0], size=N_TOK, replace=False))
+    n_max, n_min = N_TOK[w.name]
+    toks = hz.tile_edge_tokens(r, w.k, n_max, n_min, rng, allowed=same)
+    toks_mx = toks[np.unique(np.linspace(0, len(toks) - 1, N_TOK_MX).round().astype(int))]
     yield dict(w=w, d=d, out=out, X=X, Wr=Wr, bias=bias, l64=l64, r=r, idx_gpu=idx_gpu,
-               same=same, toks=toks)
+               same=same, toks=toks, toks_mx=toks_mx)
     del out, d
     torch.cuda.empty_cache()
 
@@ -119,38 +127,44 @@ def test_fullsize_config_sampled_tokens(run):
 
 
 def test_fullsize_config_weight_grads(run):
+    """Whole dW lines of every active expert, reaching all its 256 x 256 output
+    tiles; fine_grained also three complete experts; exact zeros for every
+    expert without rows."""
     w, r = run["w"], run["r"]
     if not w.backward:
         pytest.skip(f"{w.name} is a forward workload")
     counts = r["counts"]
-    ex = np.argsort(-counts, kind="stable")[:2]          # the two busiest experts
-    hz.say(f"fullsize {w.name} dW: experts {ex.tolist()} with {counts[ex].tolist()} rows")
-    W1s, W2s = _sparse_full(run["d"], ex)
-    DY = hz.bits(run["d"]["dy"])
+    active = np.nonzero(counts)[0]
     rng = np.random.default_rng(2)
-    which, ee, rr, cc = [], [], [], []
-    for e in ex:
-        for wh, nr, nc in ((1, 2 * w.I, w.H), (2, w.H, w.I)):
-            which += [wh] * N_EL
-            ee += [int(e)] * N_EL
-            rr += rng.integers(0, nr, N_EL).tolist()
-            cc += rng.integers(0, nc, N_EL).tolist()
-    which, ee, rr, cc = (np.array(v, np.int32) for v in (which, ee, rr, cc))
-    ref = oracle.weight_grad_elements(run["X"], W1s, W2s, r["idx"], r["w"], DY, which, ee, rr, cc)
+    which, ee, rr = hz.weight_grad_line_spec(active, w.I, rng,
+                                             per_band=2 if w.name == "fine_grained" else 1)
+    hz.say(f"fullsize {w.name} dW: {len(which)} lines over {len(active)} active experts")
+    DY = hz.bits(run["d"]["dy"])
+    ref = hz.oracle_lines(run["d"], run["X"], DY, r, which, ee, rr)
+    got = hz.gather_lines(run["out"]["dW1"], run["out"]["dW2"], which, ee, rr)
     for wh, name in ((1, "dW1"), (2, "dW2")):
-        dW = run["out"][name]
         sel = which == wh
-        e_, r_, c_ = ee[sel], rr[sel], cc[sel]
-        # indices checked on the host: the gather below does not check them
-        assert (e_ < dW.shape[0]).all() and (r_ < dW.shape[1]).all() and (c_ < dW.shape[2]).all()
-        got = dW[torch.as_tensor(e_, device="cuda"), torch.as_tensor(r_, device="cuda"),
-                 torch.as_tensor(c_, device="cuda")].cpu().numpy()
-        hz.assert_close(f"fullsize {w.name} {name} elements", got, ref[sel], hz.GRAD_TOL)
+        hz.assert_close(f"fullsize {w.name} {name} lines", got[sel], ref[sel], hz.GRAD_TOL)
+    if w.name == "fine_grained":
+        order = np.argsort(-counts, kind="stable")
+        full = [int(order[0]), int(order[1]), int(active[np.argmin(counts[active])])]
+        hz.say(f"fullsize {w.name} complete dW of experts {full} with "
+               f"{counts[full].tolist()} rows")
+        W1c, W2c = hz.compact_weights(run["d"], full)
+        dW1_ref, dW2_ref = oracle.weight_grads(run["X"], W1c, W2c, hz.remap_experts(r["idx"], full),
+                                               r["w"], DY, experts=[0, 1, 2])
+        ex = torch.as_tensor(full, device="cuda")
+        hz.assert_close(f"fullsize {w.name} dW1 complete experts",
+                        run["out"]["dW1"].index_select(0, ex).cpu().numpy(), dW1_ref,
+                        hz.GRAD_TOL)
+        hz.assert_close(f"fullsize {w.name} dW2 complete experts",
+                        run["out"]["dW2"].index_select(0, ex).cpu().numpy(), dW2_ref,
+                        hz.GRAD_TOL)
     empty = np.nonzero(counts == 0)[0]
-    if len(empty):
-        ez = torch.as_tensor(empty[:4], device="cuda")
+    for e in empty.tolist():
         for name in ("dW1", "dW2"):
-            assert float(run["out"][name].index_select(0, ez).abs().max().cpu()) == 0.0
+            assert float(run["out"][name][e].abs().max().cpu()) == 0.0, (name, e)
+    hz.say(f"fullsize {w.name}: {len(empty)} experts without rows have exact-zero dW")
 
 
 # ---------------------------------------------------------------- MXFP8 ----
@@ -213,41 +227,24 @@ def test_fullsize_config_mx_forward(run, runmx):
     exceeds the fixed MX tolerance.  Each element is held to that bound
     (summed over the token's slots with their weights) plus the forward's
     absolute bound, and the whole to the forward's relative bound."""
-    w, r, toks = run["w"], run["r"], run["toks"]
+    w, r, toks = run["w"], run["r"], run["toks_mx"]
     assert np.array_equal(runmx["saved"]["topk_idx"].cpu().numpy(), run["idx_gpu"])
     ex = np.unique(r["idx"][toks])
     W1c, W2c = _compact(run["d"], ex)
-    ops_o = oracle.MxOperands(run["X"][toks], W1c, W2c)
-    idx_c = _remap(r["idx"][toks], ex)
-    wt = r["w"][toks]
-    y_ref = oracle.mx_forward(ops_o, idx_c, wt)
-    y_gpu = runmx["y"][torch.as_tensor(toks, device="cuda")].cpu().numpy().astype(np.float64)
-    # sum_i |a_i w2[e, h, i]| per slot, from the oracle's MX a and MX w2
-    k = idx_c.shape[1]
-    _, _, _, aq, as_, _ = oracle.mx_expert_rows(ops_o, idx_c, np.arange(len(toks) * k))
-    A = np.abs(oracle.mx_dequantize(aq, as_)).astype(np.float32)          # [n*k, I]
-    win = 2.0 ** -10 + (w.I / 8 + 1) * 2.0 ** -24
-    bound = np.zeros_like(y_ref)
-    for c_e in range(len(ex)):
-        rows = slice(c_e * w.H, (c_e + 1) * w.H)
-        W2 = np.abs(oracle.mx_dequantize(ops_o.w2q[rows], ops_o.w2s[rows])).astype(np.float32)
-        for p in range(len(toks)):
-            for j in range(k):
-                if idx_c[p, j] == c_e:
-                    bound[p] += wt[p, j] * win * (W2 @ A[p * k + j]).astype(np.float64)
-    err = np.abs(y_gpu - y_ref)
-    hz.say(f"fullsize {w.name} mx y: max_abs={err.max():.3e}, largest share of the window "
-           f"bound {float((err / (bound + hz.FWD_TOL[0])).max()):.3f}")
-    assert (err <= bound + hz.FWD_TOL[0]).all()
-    rel = np.linalg.norm(y_gpu - y_ref) / np.linalg.norm(y_ref)
-    assert rel <= hz.FWD_TOL[1], rel
+    y_gpu = runmx["y"][torch.as_tensor(toks, device="cuda")].cpu().numpy()
+    hz.assert_mx_y_within_window(f"fullsize {w.name} mx y", w.I, run["X"][toks], W1c, W2c,
+                                 _remap(r["idx"][toks], ex), r["w"][toks], y_gpu)
 
 
 def test_fullsize_config_mx_backward(run, runmx):
+    """dx and dlogits of four tile-edge tokens, and whole MX dW lines (a dW1
+    row in every 256-row band, a dW2 column in every 256-column band) of the
+    busiest, a median and the least busy active expert, against the oracle's
+    MXFP8 backward."""
     w, r = run["w"], run["r"]
     if not w.backward:
         pytest.skip(f"{w.name} is a forward workload")
-    toks = run["toks"][:2]
+    toks = run["toks_mx"][::max(1, len(run["toks_mx"]) // 4)][:4]
     ex = np.unique(r["idx"][toks])
     W1c, W2c = _compact(run["d"], ex)
     DY = hz.bits(run["d"]["dy"])
@@ -256,28 +253,24 @@ def test_fullsize_config_mx_backward(run, runmx):
                                                r["counts"], r["w"], score=hz.SCORE[w.score],
                                                renorm=w.renorm, scale=w.scale,
                                                coeff=w.aux_coeff, d_aux=1.0, toks=toks)
+    del ops_o
     tk = torch.as_tensor(toks, device="cuda")
     hz.assert_close(f"fullsize {w.name} mx dx", runmx["dx"][tk].cpu().numpy(), dx_ref,
                     hz.MX_GRAD_TOL)
     hz.assert_close(f"fullsize {w.name} mx dlogits", runmx["dl"][tk].cpu().numpy(), dl_ref,
                     hz.MX_GRAD_TOL)
-    e = int(np.argmax(r["counts"]))                      # the busiest expert
-    W1c, W2c = _compact(run["d"], [e])
-    ops_w = oracle.MxBackwardOperands.from_experts(run["X"], DY, w.E, np.array([e]), W1c, W2c)
-    rng = np.random.default_rng(3)
-    which, ee, rr, cc = [], [], [], []
-    for wh, nr, nc in ((1, 2 * w.I, w.H), (2, w.H, w.I)):
-        which += [wh] * N_EL
-        ee += [e] * N_EL
-        rr += rng.integers(0, nr, N_EL).tolist()
-        cc += rng.integers(0, nc, N_EL).tolist()
-    which, ee, rr, cc = (np.array(v, np.int32) for v in (which, ee, rr, cc))
-    ref = oracle.mx_weight_grad_elements(ops_w, run["X"], DY, r["idx"], r["w"], which, ee, rr, cc)
+    counts = r["counts"]
+    active = np.nonzero(counts)[0]
+    by = active[np.argsort(-counts[active], kind="stable")]
+    experts = np.unique([by[0], by[len(by) // 2], by[-1]])
+    hz.say(f"fullsize {w.name} mx dW lines: experts {experts.tolist()} with "
+           f"{counts[experts].tolist()} rows")
+    W1c, W2c = _compact(run["d"], experts)
+    ops_w = oracle.MxBackwardOperands.from_experts(run["X"], DY, w.E, experts, W1c, W2c)
+    which, ee, rr = hz.weight_grad_line_spec(experts, w.I, np.random.default_rng(3))
+    ref = oracle.mx_weight_grad_lines(ops_w, run["X"], DY, r["idx"], r["w"], which, ee, rr)
+    got = hz.gather_lines(runmx["dW1"], runmx["dW2"], which, ee, rr)
     for wh, name in ((1, "dW1"), (2, "dW2")):
         sel = which == wh
-        dW = runmx[name]
-        e_, r_, c_ = ee[sel], rr[sel], cc[sel]
-        assert (e_ < dW.shape[0]).all() and (r_ < dW.shape[1]).all() and (c_ < dW.shape[2]).all()
-        got = dW[torch.as_tensor(e_, device="cuda"), torch.as_tensor(r_, device="cuda"),
-                 torch.as_tensor(c_, device="cuda")].cpu().numpy()
-        hz.assert_close(f"fullsize {w.name} mx {name} elements", got, ref[sel], hz.MX_GRAD_TOL)
+        hz.assert_close(f"fullsize {w.name} mx {name} lines", got[sel], ref[sel],
+                        hz.MX_GRAD_TOL)

@@ -206,6 +206,37 @@ def test_weight_grad_elements_agree_with_full(oracle_lib):
     assert np.array_equal(sub1[0], dW1[3]) and np.array_equal(sub2[1], dW2[0])
 
 
+@pytest.mark.parametrize("case", CASES[:3], ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_weight_grad_lines_match_autograd_of_dense_formulation(oracle_lib, case):
+    """Rows of dW1 and columns of dW2 (whole lines, the form the full-size
+    parity tests use) against torch.autograd of the dense formulation."""
+    d, w = _small(**case)
+    l64, r = _route(oracle_lib, d, w)
+    X, W1, W2, DY = _bits(d["x"]), _bits(d["w1"]), _bits(d["w2"]), _bits(d["dy"])
+    x = d["x"].double()
+    w1 = d["w1"].double().requires_grad_()
+    w2 = d["w2"].double().requires_grad_()
+    kw = dict(score=w.score, renorm=w.renorm, scale=w.scale, coeff=0.0, d_aux=0.0,
+              counts=torch.from_numpy(r["counts"]))
+    # routing weights are inputs of the lines: take the oracle's, as the
+    # dense formulation derives the same ones from the same logits
+    loss, _, _, _ = dense_loss(x, w1, w2, torch.from_numpy(r["idx"]).long(), d["dy"].double(),
+                               logits=torch.from_numpy(l64), **kw)
+    loss.backward()
+    g1, g2 = w1.grad.numpy(), w2.grad.numpy()
+    ee = np.repeat(np.arange(w.E), 4)
+    rows = np.tile([0, w.I - 1, w.I, 2 * w.I - 1], w.E)        # gate and up halves, both ends
+    cols = np.tile([0, 5, w.I // 2, w.I - 1], w.E)
+    lines1 = oracle_lib.weight_grad_lines(X, W1, W2, r["idx"], r["w"], DY, np.ones_like(ee), ee,
+                                          rows)
+    lines2 = oracle_lib.weight_grad_lines(X, W1, W2, r["idx"], r["w"], DY, np.full_like(ee, 2),
+                                          ee, cols)
+    tol = lambda a: 1e-10 * max(1e-30, float(np.abs(a).max()))
+    assert np.abs(lines1 - g1[ee, rows, :]).max() <= tol(g1)
+    assert np.abs(lines2 - g2[ee, :, cols]).max() <= tol(g2)
+    assert np.abs(lines1).max() > 0 and np.abs(lines2).max() > 0
+
+
 def test_weight_grads_linear_in_dy_and_token_permutation(oracle_lib):
     d, w = _small("softmax", True)
     l64, r = _route(oracle_lib, d, w)

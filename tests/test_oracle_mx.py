@@ -345,6 +345,23 @@ def test_mx_weight_grad_elements_against_numpy():
     assert np.allclose(got, ref, rtol=1e-9, atol=1e-12)
 
 
+def test_mx_weight_grad_lines_against_numpy():
+    """Whole rows of dW1 and columns of dW2 of the MXFP8 backward against the
+    numpy formulation (ragged last 32-row block included)."""
+    x, w1, w2, dy, idx, w = _bwd_setup(24, T=40, E=3, k=2)
+    E, twoI, H = w1.shape
+    I = twoI // 2
+    ops = oracle.MxBackwardOperands(x, w1, w2, dy)
+    _, _, dW1, dW2 = _numpy_mx_backward(x, w1, w2, dy, idx, w)
+    ee = np.repeat(np.arange(E), 3)
+    rows = np.tile([0, I + 3, twoI - 1], E)
+    cols = np.tile([0, 17, I - 1], E)
+    l1 = oracle.mx_weight_grad_lines(ops, x, dy, idx, w, np.ones_like(ee), ee, rows)
+    l2 = oracle.mx_weight_grad_lines(ops, x, dy, idx, w, np.full_like(ee, 2), ee, cols)
+    assert np.allclose(l1, dW1[ee, rows, :], rtol=1e-9, atol=1e-12)
+    assert np.allclose(l2, dW2[ee, :, cols], rtol=1e-9, atol=1e-12)
+
+
 def test_mx_backward_within_the_format_error_of_the_exact_backward():
     x, w1, w2, dy, idx, w = _bwd_setup(23, T=16, H=128, I=128, E=4, k=2)
     T, E = x.shape[0], w1.shape[0]
