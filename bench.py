@@ -53,6 +53,7 @@ GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k
 # The measured HBM traffic of the grouped GEMMs lives in this file, next to a
 # hash of the kernel sources it was taken with; a changed kernel reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
+UNIFORM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_uniform.md")
 BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy_deepseek_v3.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
                   for f in ("gemm.hip", "tile.h", "common.h", "swiglu_epi.h", "bwd_epi.h", "mxfmt.h",
@@ -71,6 +72,29 @@ def gemm_flops(w, stage):
     return {"up_swiglu": 2 * M * two_i * w.H, "down": 2 * M * w.H * w.I,
             "down_dgrad": 2 * M * w.H * w.I, "up_dgrad": 2 * M * two_i * w.H,
             "down_wgrad": 2 * M * w.H * w.I, "up_wgrad": 2 * M * two_i * w.H}[stage]
+
+
+def gemm_bytes(w, stage, counts, dw_accumulate):
+    """Algorithmic HBM bytes of one grouped-GEMM op: each operand once (token
+    tensors once per token, the weights of the experts that have rows once,
+    sorted-row intermediates once per routed row), each output once, and the
+    fp32 weight gradient read and written (accumulate) or written (overwrite,
+    the zero fill of experts without rows included)."""
+    T, H, I, E = w.T, w.H, w.I, w.E
+    M = T * w.k
+    act = sum(1 for c in counts if c > 0)
+    w1b, w2b = act * 2 * I * H * 2, act * H * I * 2
+    rmw = 2 if dw_accumulate else 1
+    dw1 = (act * rmw + (0 if dw_accumulate else E - act)) * 2 * I * H * 4
+    dw2 = (act * rmw + (0 if dw_accumulate else E - act)) * H * I * 4
+    return {
+        "up_swiglu": T * H * 2 + w1b + M * 2 * I * 2 + M * I * 2,
+        "down": M * I * 2 + w2b + M * H * 4,
+        "down_dgrad": T * H * 2 + w2b + M * 2 * I * 2 + M * I * 2 + M * 2 * I * 2,
+        "up_dgrad": M * 2 * I * 2 + w1b + M * H * 2,
+        "down_wgrad": M * H * 2 + M * I * 2 + dw2,
+        "up_wgrad": M * 2 * I * 2 + M * H * 2 + dw1,
+    }[stage]
 
 
 def stage_bytes(w, stage, with_router_weight):
@@ -157,9 +181,23 @@ def run_gpu(args, w):
     counts = saved["counts"].cpu()
     log(f"[bench] step {elapsed / K * 1e3:.3f} ms; active experts {(counts > 0).sum().item()}, "
         f"max rows {counts.max().item()}")
-    return dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved,
-                bufs=dict(y=y, aux=aux, wsf=wsf, wsb=wsb, dx=dx, dl=dl, dWr=dWr, dW1=dW1, dW2=dW2,
-                          d_aux=d_aux))
+    out = dict(elapsed=elapsed, stage_ms=stage_ms, counts=counts.tolist(), d=d, saved=saved,
+               bufs=dict(y=y, aux=aux, wsf=wsf, wsb=wsb, dx=dx, dl=dl, dWr=dWr, dW1=dW1, dW2=dW2,
+                         d_aux=d_aux))
+    if bwd and args.overwrite_steps > 0:
+        # the same step with the weight gradients overwritten (exact zeros for
+        # experts without rows): the parity tests' dW semantics
+        acc = False
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.overwrite_steps):
+            step()
+        torch.cuda.synchronize()
+        out["overwrite_ms"] = (time.perf_counter() - t0) / args.overwrite_steps * 1e3
+        log(f"[bench] overwrite-mode step {out['overwrite_ms']:.3f} ms")
+    return out
 
 
 MX_STAGES = ["router_proj", "router", "permute", "mx_quant", "up_swiglu", "down", "combine",
@@ -256,11 +294,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(stage):
+def measured_traffic(stage, path=None):
     """HBM bytes per launch of `stage` from the committed PMC record, or None
     when there is none or the kernel sources changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path or TRAFFIC_FILE) as fh:
             lines = [l for l in fh if l.startswith("traffic-record: ")]
     except OSError:
         return None
@@ -481,7 +519,22 @@ def cpu_baseline(w, d, target_s=12.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} tokens of the workload as one batch, fwd+bwd incl. weight "
-                      f"gradients of the {len(data[4])} experts they route to; {t:.1f} s"}
+                      f"gradients of the {len(data[4])} experts they route to; {t:.1f} s",
+            "basis": "tokens/s of that sample: an extrapolation to the workload, whose "
+                     "8192-token step is not run on the CPU",
+            "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()}
+
+
+def host_cpu():
+    """The host CPU model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -493,6 +546,10 @@ def main():
     ap.add_argument("--dw-mode", choices=["accumulate", "overwrite"], default="accumulate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 leg")
+    ap.add_argument("--overwrite-steps", type=int, default=5,
+                    help="steps timed again with the weight gradients overwritten (0: skip)")
+    ap.add_argument("--uniform-steps", type=int, default=5,
+                    help="steps of the `uniform` benchmarking leg (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy that calibrates the PMC byte counters")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -531,6 +588,10 @@ def main():
     gemm_ms = {s: stage_ms[s] for s in gemm_stages}
     total_gemm_flops = sum(gemm_flops(w, s) for s in gemm_stages)
     gemm_tflops = total_gemm_flops / (sum(gemm_ms.values()) * 1e-3) / 1e12
+    # the weight gradients' operand transposes exist only to feed their GEMMs:
+    # the rate with them counted as GEMM time too
+    prep_ms = sum(stage_ms.get(s, 0.0) for s in ("operands_bwd1", "operands_bwd2"))
+    gemm_tflops_prep = total_gemm_flops / ((sum(gemm_ms.values()) + prep_ms) * 1e-3) / 1e12
     dom = max(gemm_ms, key=gemm_ms.get)
     dom_tflops = gemm_flops(w, dom) / (gemm_ms[dom] * 1e-3) / 1e12
 
@@ -569,15 +630,75 @@ def main():
         "grouped_gemm": {"TFLOP/s": round(gemm_tflops, 1),
                          "pct_of_bf16_peak": round(100 * gemm_tflops / PEAK_BF16_TFLOPS, 2),
                          "flops_per_step": total_gemm_flops,
-                         "ms_per_step": round(sum(gemm_ms.values()), 4)},
+                         "ms_per_step": round(sum(gemm_ms.values()), 4),
+                         "TFLOP/s_with_operand_prep": round(gemm_tflops_prep, 1),
+                         "pct_of_bf16_peak_with_operand_prep":
+                             round(100 * gemm_tflops_prep / PEAK_BF16_TFLOPS, 2)},
         "stages": stages,
         "active_experts": sum(1 for c in g["counts"] if c > 0),
     }
-    if not args.no_mx and w.backward:
+    if w.precision != "bf16":
+        out["config"]["intermediates"] = w.precision
+    if "overwrite_ms" in g:
+        out["dw_overwrite"] = {"ms_per_step": round(g["overwrite_ms"], 4),
+                               "tokens_per_s": round(w.T / (g["overwrite_ms"] * 1e-3), 1),
+                               "steps": args.overwrite_steps}
+    if not args.no_mx and w.backward and w.precision == "bf16":
         out["mxfp8"] = run_mx(args, w, g)
     if not args.no_cpu_baseline and w.backward:
         out["cpu_baseline"] = cpu_baseline(w, g["d"])
+    if args.uniform_steps > 0 and w.name == "deepseek_v3":
+        del g
+        out["uniform"] = uniform_leg(args)
     print(json.dumps(out), flush=True)
+
+
+def uniform_leg(args):
+    """The pages' benchmarking mode, `uniform` force load balancing: the
+    DeepSeek-V3 shapes with seeded i.i.d. N(0, 1) logits in place of the router
+    projection, so all 256 experts get rows.  Step time, grouped-GEMM rate,
+    and the HBM roofline of the slowest GEMM from its algorithmic bytes (the
+    regime is weight- and weight-gradient-streaming bound)."""
+    import gc
+
+    import torch
+    from grouped_gemm_expert_amd import inputs
+
+    gc.collect()
+    torch.cuda.empty_cache()
+    wu = inputs.WORKLOADS["uniform"]
+    a = argparse.Namespace(**vars(args))
+    a.steps, a.warmup, a.overwrite_steps = args.uniform_steps, 2, 0
+    g = run_gpu(a, wu)
+    st = g["stage_ms"]
+    acc = args.dw_mode == "accumulate"
+    gemm_ms = {s: st[s] for s in GEMM_STAGES}
+    flops = sum(gemm_flops(wu, s) for s in GEMM_STAGES)
+    tf = flops / (sum(gemm_ms.values()) * 1e-3) / 1e12
+    by = {s: gemm_bytes(wu, s, g["counts"], acc) for s in GEMM_STAGES}
+    dom = max(gemm_ms, key=gemm_ms.get)
+    gbs = by[dom] / (gemm_ms[dom] * 1e-3) / 1e9
+    ms = g["elapsed"] / a.steps * 1e3
+    res = {
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(wu.T / (ms * 1e-3), 1),
+        "active_experts": sum(1 for c in g["counts"] if c > 0),
+        "rows_per_expert": [min(g["counts"]), max(g["counts"])],
+        "grouped_gemm": {"TFLOP/s": round(tf, 1),
+                         "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                         "ms_per_step": round(sum(gemm_ms.values()), 4),
+                         "algorithmic_bytes_per_step": sum(by.values()),
+                         "GB/s": round(sum(by.values()) / (sum(gemm_ms.values()) * 1e-3) / 1e9, 1)},
+        "stages": {s: {"ms": round(st[s], 4),
+                       "TFLOP/s": round(gemm_flops(wu, s) / (st[s] * 1e-3) / 1e12, 1),
+                       "GB/s": round(by[s] / (st[s] * 1e-3) / 1e9, 1)} for s in GEMM_STAGES},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": by[dom],
+                     "traffic": measured_traffic(dom, UNIFORM_TRAFFIC_FILE)},
+    }
+    log(f"[bench] uniform step {ms:.3f} ms; GEMMs {tf:.0f} TF/s; {dom} {gbs:.0f} GB/s")
+    return res
 
 
 if __name__ == "__main__":

@@ -60,6 +60,7 @@ struct BwdWs {
     // (tA: w*dy or dh; tB: a or x), or in MX form in the same memory
     uint16_t *tA, *tB;
     uint8_t *segA, *segB;
+    uint16_t *dh_lo, *tA_lo, *tB_lo;  // split intermediates only
 };
 
 // Elements of the two transposed weight-gradient operand areas: rows R times
@@ -73,9 +74,12 @@ static int64_t seg_rows_b(const moe_config &c) { return c.H > c.I ? c.H : c.I; }
 // gradients: bf16 into dst (uint16_t), or as MX matrices (mx).
 static hipError_t prepare_segments(const moe_config &c, const Sched &sc, const int32_t *offsets,
                                    const uint16_t *src, int64_t C, const int32_t *gather,
-                                   const float *rw, bool mx, void *dst, hipStream_t s)
+                                   const float *rw, bool mx, void *dst, hipStream_t s,
+                                   const uint16_t *src_lo = nullptr, int32_t lo_part = 0)
 {
     ColQuant q = {};
+    q.src_lo = src_lo;
+    q.lo_part = lo_part;
     q.src = src;
     q.C = C;
     q.gather = gather;
@@ -90,7 +94,11 @@ static hipError_t prepare_segments(const moe_config &c, const Sched &sc, const i
               : launch_transpose_segments(q, seg_chunks(c), (uint16_t *)dst, s);
 }
 
-FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
+// The forward workspace.  The bf16 forward and its parts (router, permute,
+// the forward GEMMs, combine) use only its first `bf16_bytes`; the rest holds
+// the single-op weight-gradient GEMMs' transposed operands (an extension of
+// o's area, from o's start) and the MXFP8 forward's MX matrices.
+FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes, size_t *bf16_bytes = nullptr)
 {
     Carver cv(ws);
     const int64_t M = c.T * c.k;
@@ -104,15 +112,26 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes)
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
     w.sched.order = cv.take<int32_t>(c.E + 1);
     w.wrow = cv.take<float>(M);
-    // o [M,H] fp32; the single-op weight-gradient GEMMs put their transposed
-    // operands here instead
-    const int64_t t_elems = (seg_rows_a(c) + seg_rows_b(c)) * 128 * seg_chunks(c);
-    w.o = cv.take<float>(M * c.H > (t_elems + 1) / 2 ? M * c.H : (t_elems + 1) / 2);
     w.router = cv.take<char>((int64_t)router_ws_bytes_fwd(c.T, c.E, c.H));
+    w.o = cv.take<float>(M * c.H);   // [M,H] fp32 expert outputs
+    if (bf16_bytes) *bf16_bytes = cv.used;
+    // the single-op weight-gradient GEMMs put their transposed operands where
+    // o starts, extended here to their size
+    const int64_t t_elems = (seg_rows_a(c) + seg_rows_b(c)) * 128 * seg_chunks(c);
+    if ((t_elems + 1) / 2 > M * c.H) cv.take<float>((t_elems + 1) / 2 - M * c.H);
     w.xmx = cv.take<uint8_t>(mx_bytes(c.T, c.H));
     w.amx = cv.take<uint8_t>(mx_bytes(M, c.I));
     if (bytes) *bytes = cv.used;
     return w;
+}
+
+// The forward workspace bytes an entry point needs: the bf16 forward's part,
+// or all of it (the MXFP8 forward, the single-op GEMMs).
+size_t fwd_need(const moe_config &c, bool full)
+{
+    size_t all = 0, part = 0;
+    carve_fwd(c, nullptr, &all, &part);
+    return full ? all : part;
 }
 
 BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
@@ -137,6 +156,12 @@ BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
     w.tB = cv.take<uint16_t>(seg_rows_b(c) * 128 * seg_chunks(c));
     w.segA = (uint8_t *)w.tA;
     w.segB = (uint8_t *)w.tB;
+    // split intermediates: dh's remainder and the remainder halves of the
+    // weight gradients' split operands
+    const bool split = c.precision == MOE_PRECISION_SPLIT;
+    w.dh_lo = split ? cv.take<uint16_t>(M * 2 * c.I) : nullptr;
+    w.tA_lo = split ? cv.take<uint16_t>(seg_rows_a(c) * 128 * seg_chunks(c)) : nullptr;
+    w.tB_lo = split ? cv.take<uint16_t>(seg_rows_b(c) * 128 * seg_chunks(c)) : nullptr;
     if (bytes) *bytes = cv.used;
     return w;
 }
@@ -259,6 +284,7 @@ moe_status moe_check_config(const moe_config *cfg)
     if (c.T < 0 || c.H <= 0 || c.I <= 0 || c.E <= 0 || c.k <= 0) return MOE_EINVAL;
     if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID) return MOE_EINVAL;
     if (c.route_mode != MOE_ROUTE_LEARNED && c.route_mode != MOE_ROUTE_EVEN) return MOE_EINVAL;
+    if (c.precision != MOE_PRECISION_BF16 && c.precision != MOE_PRECISION_SPLIT) return MOE_EINVAL;
     if (c.k > c.E || c.k > 32 || c.E > 1024) return MOE_EUNSUPPORTED;
     if (c.n_groups < 1 || c.n_groups > 64 || c.E % c.n_groups != 0) return MOE_EUNSUPPORTED;
     if (c.topk_groups < 1 || c.topk_groups > c.n_groups) return MOE_EUNSUPPORTED;
@@ -298,8 +324,8 @@ moe_status moe_router(const moe_config *cfg, const uint16_t *x, const float *Wr,
     MOE_CHECK(check_opt_ptr(bias));
     MOE_CHECK(check_opt_ptr(sel_scores));
     if (Wr) MOE_CHECK(check_ptrs({x, Wr}));
-    size_t need = 0;
-    FwdWs w = carve_fwd(c, ws, &need);
+    const size_t need = fwd_need(c, false);
+    FwdWs w = carve_fwd(c, ws, nullptr);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     if (c.T == 0) {
         MOE_TRY(launch_fill_i32(counts, c.E, 0, stream));
@@ -345,8 +371,8 @@ moe_status moe_permute(const moe_config *cfg, const int32_t *topk_idx, int32_t *
     const moe_config &c = *cfg;
     MOE_CHECK(check_ptrs({counts, offsets}));
     if (c.T > 0) MOE_CHECK(check_ptrs({topk_idx, row_map, pos}));
-    size_t need = 0;
-    FwdWs w = carve_fwd(c, ws, &need);
+    const size_t need = fwd_need(c, false);
+    FwdWs w = carve_fwd(c, ws, nullptr);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     MOE_TRY(launch_permute(c.T * c.k, c.E, topk_idx, counts, offsets, row_map, pos, w.chunk_hist,
                            stream));
@@ -361,8 +387,8 @@ moe_status moe_permute_checked(const moe_config *cfg, const int32_t *topk_idx, i
     const moe_config &c = *cfg;
     MOE_CHECK(check_ptrs({counts, offsets, n_bad}));
     if (c.T > 0) MOE_CHECK(check_ptrs({topk_idx, row_map, pos}));
-    size_t need = 0;
-    FwdWs w = carve_fwd(c, ws, &need);
+    const size_t need = fwd_need(c, false);
+    FwdWs w = carve_fwd(c, ws, nullptr);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     MOE_TRY(launch_permute_checked(c.T * c.k, c.E, topk_idx, counts, offsets, row_map, pos,
                                    w.chunk_hist, n_bad, stream));
@@ -385,6 +411,9 @@ moe_status moe_saved_sizes(const moe_config *cfg, size_t sizes[MOE_SAVED_N])
     sizes[6] = M * sizeof(int32_t);          // pos
     sizes[7] = M * 2 * I * sizeof(uint16_t); // h
     sizes[8] = M * I * sizeof(uint16_t);     // a
+    const bool split = c.precision == MOE_PRECISION_SPLIT;
+    sizes[9] = split ? sizes[7] : 0;         // h_lo
+    sizes[10] = split ? sizes[8] : 0;        // a_lo
     return MOE_OK;
 }
 
@@ -395,6 +424,7 @@ moe_status moe_grouped_gemm(int32_t op, const moe_config *cfg, const moe_gemm_ar
     if (!args) return MOE_EINVAL;
     const moe_config &c = *cfg;
     const moe_gemm_args &a = *args;
+    if (c.precision != MOE_PRECISION_BF16) return MOE_EUNSUPPORTED;
     size_t need = 0;
     FwdWs w = carve_fwd(c, ws, &need);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
@@ -476,20 +506,22 @@ moe_status moe_combine(const moe_config *cfg, const float *o, const float *topk_
     return MOE_OK;
 }
 
-static moe_status check_saved(const moe_saved *s)
+static moe_status check_saved(const moe_saved *s, const moe_config &c)
 {
     if (!s) return MOE_EINVAL;
-    return check_ptrs({s->logits, s->topk_idx, s->topk_w, s->counts, s->offsets, s->row_map,
-                       s->pos, s->h, s->a});
+    MOE_CHECK(check_ptrs({s->logits, s->topk_idx, s->topk_w, s->counts, s->offsets, s->row_map,
+                          s->pos, s->h, s->a}));
+    if (c.precision == MOE_PRECISION_SPLIT) MOE_CHECK(check_ptrs({s->h_lo, s->a_lo}));
+    return MOE_OK;
 }
 
 // The backward reads only counts and offsets of a forward over no tokens (the
 // other saved tensors are empty and may be NULL).
-static moe_status check_saved_bwd(const moe_saved *s, int64_t T)
+static moe_status check_saved_bwd(const moe_saved *s, const moe_config &c)
 {
     if (!s) return MOE_EINVAL;
-    if (T == 0) return check_ptrs({s->counts, s->offsets});
-    return check_saved(s);
+    if (c.T == 0) return check_ptrs({s->counts, s->offsets});
+    return check_saved(s, c);
 }
 
 static moe_gemm_args saved_gemm_args(const moe_saved *saved)
@@ -503,6 +535,22 @@ static moe_gemm_args saved_gemm_args(const moe_saved *saved)
     a.h = saved->h;
     a.a = saved->a;
     return a;
+}
+
+// The split intermediates of a config in MOE_PRECISION_SPLIT (saved h_lo,
+// a_lo; the backward's dh_lo and operand remainders).
+static void set_split(GemmArgs &g, const moe_config &c, const moe_saved *saved,
+                      const BwdWs *bw)
+{
+    g.split = c.precision == MOE_PRECISION_SPLIT;
+    if (!g.split) return;
+    g.h_lo = saved->h_lo;
+    g.a_lo = saved->a_lo;
+    if (bw) {
+        g.dh_lo = bw->dh_lo;
+        g.tA_lo = bw->tA_lo;
+        g.tB_lo = bw->tB_lo;
+    }
 }
 
 // ----------------------------------------------------------- two stages ----
@@ -531,9 +579,10 @@ static moe_status stage1_fwd(const moe_config *cfg, const uint16_t *x, const flo
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
+    if (w1_mx && c.precision != MOE_PRECISION_BF16) return MOE_EUNSUPPORTED;
     if (!saved || !aux) return MOE_EINVAL;
-    size_t need = 0;
-    FwdWs w = carve_fwd(c, ws, &need);
+    const size_t need = fwd_need(c, w1_mx != nullptr);
+    FwdWs w = carve_fwd(c, ws, nullptr);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     if (c.T == 0) {
         MOE_CHECK(check_ptrs({saved->counts, saved->offsets, aux}));
@@ -542,7 +591,7 @@ static moe_status stage1_fwd(const moe_config *cfg, const uint16_t *x, const flo
         MOE_TRY(launch_fill_f32(aux, 1, 0.f, stream));
         return MOE_OK;
     }
-    MOE_CHECK(check_saved(saved));
+    MOE_CHECK(check_saved(saved, c));
     MOE_CHECK(check_ptrs({x, w1_mx ? (const void *)w1_mx : (const void *)w1}));
     MOE_CHECK(moe_router(cfg, x, Wr, bias, saved->logits, nullptr, saved->topk_idx,
                          saved->topk_w, saved->counts, aux, ws, ws_bytes, stream));
@@ -556,6 +605,7 @@ static moe_status stage1_fwd(const moe_config *cfg, const uint16_t *x, const flo
     a.x = x;
     a.w1 = w1;
     GemmArgs g = gemm_args(c, a, w.sched);
+    set_split(g, c, saved, nullptr);
     if (!w1_mx) {
         MOE_TRY(run_gemm(MOE_GEMM_UP_SWIGLU, g, stream));
         return MOE_OK;
@@ -578,18 +628,20 @@ static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const ui
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
+    if (w2_mx && c.precision != MOE_PRECISION_BF16) return MOE_EUNSUPPORTED;
     if (!saved) return MOE_EINVAL;
-    size_t need = 0;
-    FwdWs w = carve_fwd(c, ws, &need);
+    const size_t need = fwd_need(c, w2_mx != nullptr);
+    FwdWs w = carve_fwd(c, ws, nullptr);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
     if (c.T == 0) return MOE_OK;
-    MOE_CHECK(check_saved(saved));
+    MOE_CHECK(check_saved(saved, c));
     MOE_CHECK(check_ptrs({w2_mx ? (const void *)w2_mx : (const void *)w2, y}));
     MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
     moe_gemm_args a = saved_gemm_args(saved);
     a.w2 = w2;
     a.o = w.o;
     GemmArgs g = gemm_args(c, a, w.sched);
+    set_split(g, c, saved, nullptr);
     if (!w2_mx) {
         MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));
     } else {
@@ -658,6 +710,7 @@ moe_status moe_grouped_gemm_mx(int32_t op, const moe_config *cfg, const moe_gemm
     if (!args) return MOE_EINVAL;
     const moe_config &c = *cfg;
     const moe_gemm_mx_args &a = *args;
+    if (c.precision != MOE_PRECISION_BF16) return MOE_EUNSUPPORTED;
     size_t need = 0;
     FwdWs w = carve_fwd(c, ws, &need);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
@@ -838,7 +891,8 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
     if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
-    MOE_CHECK(check_saved_bwd(saved, c.T));
+    if (w2t_mx && c.precision != MOE_PRECISION_BF16) return MOE_EUNSUPPORTED;
+    MOE_CHECK(check_saved_bwd(saved, c));
     MOE_CHECK(check_ptrs({w2t_mx ? (const void *)w2t_mx : (const void *)w2, dW2}));
     if (c.T > 0) MOE_CHECK(check_ptrs({dy}));
     size_t need = 0;
@@ -857,6 +911,7 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
     g.wrow = w.wrow;
     g.tA = w.tA;
     g.tB = w.tB;
+    set_split(g, c, saved, &w);
     const bool mx = w2t_mx != nullptr;
     if (mx) {
         set_mx_bwd(g, c, w);
@@ -869,10 +924,20 @@ static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, cons
         // along each expert's rows; with MX also dy along H for the dgrad
         StageMark mark(MOE_STAGE_OPERANDS_BWD2, stream);
         if (mx) MOE_TRY(launch_mx_quantize(dy, c.T, c.H, w.dymx, stream));
-        MOE_TRY(prepare_segments(c, w.sched, saved->offsets, dy, c.H, saved->row_map, w.wrow, mx,
-                                 w.tA, stream));
-        MOE_TRY(prepare_segments(c, w.sched, saved->offsets, saved->a, c.I, nullptr, nullptr, mx,
-                                 w.tB, stream));
+        if (g.split) {
+            // dy exact (gathered); w * (a + a_lo) in fp32, as a hi + lo pair
+            MOE_TRY(prepare_segments(c, w.sched, saved->offsets, dy, c.H, saved->row_map, nullptr,
+                                     false, w.tA, stream));
+            MOE_TRY(prepare_segments(c, w.sched, saved->offsets, saved->a, c.I, nullptr, w.wrow,
+                                     false, w.tB, stream, saved->a_lo, 0));
+            MOE_TRY(prepare_segments(c, w.sched, saved->offsets, saved->a, c.I, nullptr, w.wrow,
+                                     false, w.tB_lo, stream, saved->a_lo, 1));
+        } else {
+            MOE_TRY(prepare_segments(c, w.sched, saved->offsets, dy, c.H, saved->row_map, w.wrow,
+                                     mx, w.tA, stream));
+            MOE_TRY(prepare_segments(c, w.sched, saved->offsets, saved->a, c.I, nullptr, nullptr,
+                                     mx, w.tB, stream));
+        }
     }
     // dgrad (+ SwiGLU backward, routing-weight row-dots), then dW2
     if (mx) {
@@ -894,7 +959,8 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
     if (dw_dtype != MOE_F32 && dw_dtype != MOE_BF16) return MOE_EINVAL;
-    MOE_CHECK(check_saved_bwd(saved, c.T));
+    if (w1t_mx && c.precision != MOE_PRECISION_BF16) return MOE_EUNSUPPORTED;
+    MOE_CHECK(check_saved_bwd(saved, c));
     MOE_CHECK(check_ptrs({w1t_mx ? (const void *)w1t_mx : (const void *)w1, dW1}));
     if (c.T > 0) MOE_CHECK(check_ptrs({x, dx, dlogits}));
     MOE_CHECK(check_opt_ptr(Wr));
@@ -916,6 +982,7 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
     GemmArgs g = gemm_args(c, a, w.sched);
     g.tA = w.tA;
     g.tB = w.tB;
+    set_split(g, c, saved, &w);
     // dgrad1's per-row partials of dx go out in bf16 (half the bytes for the
     // GEMM's epilogue and the un-permute); dx itself is summed in fp32
     g.dxp_bf16 = (uint16_t *)w.dxp;
@@ -932,6 +999,9 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
         if (mx) MOE_TRY(launch_mx_quantize(w.dh, c.T * c.k, 2 * (int64_t)c.I, w.dhmx, stream));
         MOE_TRY(prepare_segments(c, w.sched, saved->offsets, w.dh, 2 * (int64_t)c.I, nullptr,
                                  nullptr, mx, w.tA, stream));
+        if (g.split)  // dh's remainder, for dW1's second pass
+            MOE_TRY(prepare_segments(c, w.sched, saved->offsets, w.dh_lo, 2 * (int64_t)c.I,
+                                     nullptr, nullptr, false, w.tA_lo, stream));
         MOE_TRY(prepare_segments(c, w.sched, saved->offsets, x, c.H, saved->row_map, nullptr, mx,
                                  w.tB, stream));
     }

@@ -19,10 +19,13 @@ namespace moe {
 // RB rows of a 128-row half at a time; the loads of a batch are issued
 // together (addresses clamped to valid rows), the first batch's before the
 // half is staged, so their latency overlaps the staging.
-template <class C, int RB = EPI_ROWS / (C::NT / 64)>
+// SPLIT: g, u and a are read as hi + lo pairs (h + h_lo, a + a_lo) and dh
+// leaves as one too: dh = bf16(v), dh_lo = bf16(v - bf16(v)).
+template <class C, int RB = EPI_ROWS / (C::NT / 64), bool SPLIT = false>
 MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int64_t n0, int nN,
                              int I, const uint16_t *h, const uint16_t *a, const float *wrow,
-                             uint16_t *dh, float *dw_part)
+                             uint16_t *dh, float *dw_part, const uint16_t *h_lo = nullptr,
+                             const uint16_t *a_lo = nullptr, uint16_t *dh_lo = nullptr)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -32,8 +35,10 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
     const int64_t colc = cok ? col : 0;
     constexpr int NW = C::NT / 64;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
+    constexpr int NL = SPLIT ? RB : 1;
     struct Batch {
         uint64_t hg[RB], hu[RB], hv[RB];
+        uint64_t lg[NL], lu[NL], lv[NL];
         float wgt[RB];
     };
     auto load = [&](int half, int r0, Batch &bt) {
@@ -44,6 +49,11 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
             bt.hg[b] = *(const uint64_t *)(h + m * 2 * I + colc);
             bt.hu[b] = *(const uint64_t *)(h + m * 2 * I + I + colc);
             bt.hv[b] = *(const uint64_t *)(a + m * I + colc);
+            if constexpr (SPLIT) {
+                bt.lg[b] = *(const uint64_t *)(h_lo + m * 2 * I + colc);
+                bt.lu[b] = *(const uint64_t *)(h_lo + m * 2 * I + I + colc);
+                bt.lv[b] = *(const uint64_t *)(a_lo + m * I + colc);
+            }
             bt.wgt[b] = wrow[m];
         }
     };
@@ -57,6 +67,18 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
             unpack_bf4(bt.hg[b], gv);
             unpack_bf4(bt.hu[b], uv);
             unpack_bf4(bt.hv[b], av);
+            if constexpr (SPLIT) {
+                float gl[4], ul[4], al[4];
+                unpack_bf4(bt.lg[b], gl);
+                unpack_bf4(bt.lu[b], ul);
+                unpack_bf4(bt.lv[b], al);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    gv[q] += gl[q];
+                    uv[q] += ul[q];
+                    av[q] += al[q];
+                }
+            }
             float part = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -69,6 +91,15 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
             if (cok) {
                 *(uint64_t *)(dh + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
                 *(uint64_t *)(dh + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
+                if constexpr (SPLIT) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        dg[q] -= bf2f(f2bf(dg[q]));
+                        du[q] -= bf2f(f2bf(du[q]));
+                    }
+                    *(uint64_t *)(dh_lo + m * 2 * I + col) = pack_bf4(dg[0], dg[1], dg[2], dg[3]);
+                    *(uint64_t *)(dh_lo + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
+                }
             }
             part = wave_sum(cok ? part : 0.f);
             if (lane == 0) dw_part[m * nN + t.nt] = part;

@@ -165,6 +165,13 @@ struct GemmArgs {
     // expert e's first at R (C) * 128 * mt_off128[e] elements (see
     // launch_transpose_segments)
     const uint16_t *tA, *tB;
+    // split intermediates (MOE_PRECISION_SPLIT): the bf16 remainders of h, a
+    // and dh (v = hi + lo), and the weight gradients' second operand halves:
+    // tA_lo (dh_lo, wgrad1) or tB_lo (the remainder of w*a, wgrad2), laid out
+    // as tA / tB; the other operand's chunks serve both halves
+    int32_t split;
+    uint16_t *h_lo, *a_lo, *dh_lo;
+    const uint16_t *tA_lo, *tB_lo;
 };
 int32_t dgrad2_cols(int32_t I);
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
@@ -183,6 +190,10 @@ hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
 // r to source row gather[r] / gk, and rw (optional) scales sorted row r by
 // rw[r] first (the product rounded to bf16).  max_chunks bounds the 128-row
 // chunks.
+// src_lo (optional, bf16 transposer only): a second source of the same shape
+// whose values are added to src's in fp32 before the scaling (a hi + lo
+// pair); lo_part (bf16 transposer only): 0 stores bf16(v), 1 stores the
+// remainder bf16(v - bf16(v)).
 struct ColQuant {
     const uint16_t *src;
     int64_t C;
@@ -193,6 +204,8 @@ struct ColQuant {
     int64_t R;
     const int32_t *offsets, *mt128;
     uint8_t *dst;
+    const uint16_t *src_lo;
+    int32_t lo_part;
 };
 hipError_t launch_mx_quantize_cols(const ColQuant &q, int64_t max_chunks, hipStream_t s);
 // bf16: the same expert segments (offsets / mt128 mode) transposed without

@@ -40,7 +40,7 @@ int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
 // B tile rows: wave column wn covers gate columns i0 + wn*WN/2 + [0, WN/2)
 // and the matching up columns, so each lane holds g and u of the same (r, i).
 // =========================================================================
-template <class C>
+template <class C, bool SPLIT>
 __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
@@ -75,13 +75,16 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
     Acc<C> acc;
     mainloop<C, false, false, false>(lds, H, la, lb, acc);
 
-    swiglu_epilogue<C, false>(acc, lds, t, i0, I, g.h, g.a, nullptr, nullptr, 0);
+    swiglu_epilogue<C, false, SPLIT>(acc, lds, t, i0, I, g.h, g.a, nullptr, nullptr, 0, g.h_lo,
+                                     g.a_lo);
 }
 
 // =========================================================================
 // GEMM2:  o[r, c] = a[r] . w2[e, c, :]   (fp32 out)
+// SPLIT: a is the pair a + a_lo, so the k loop runs twice over I: stages
+// 0 .. I/64-1 read a, the next I/64 read a_lo, both against the same w2.
 // =========================================================================
-template <class C>
+template <class C, bool SPLIT>
 __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
@@ -110,7 +113,22 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
         lb.set(q, lane0, (uint32_t)(n * I * 2));
     }
     Acc<C> acc;
-    mainloop<C, false, false, false>(lds, I, la, lb, acc);
+    if constexpr (SPLIT) {
+        const int nI = I / BK;  // I % 64 == 0 (moe_check_config)
+        const char *alo = (const char *)g.a_lo;
+        pipeline<C, false, false, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
+            lds, 0, 2 * nI,
+            [&](int q, int st, lds_t *As) {
+                const bool lo = st >= nI;
+                la.issue_one(q, As, (int64_t)(lo ? st - nI : st) * BK, BK, lo ? alo : la.base);
+            },
+            [&](int q, int st, lds_t *Bs) {
+                lb.issue_one(q, Bs, (int64_t)(st >= nI ? st - nI : st) * BK, BK, lb.base);
+            },
+            [](int, lds_t *, lds_t *) {}, acc);
+    } else {
+        mainloop<C, false, false, false>(lds, I, la, lb, acc);
+    }
     store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
 }
 
@@ -119,7 +137,7 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
 //   dA'[r, i] = dy[tok(r)] . w2[e, :, i];  dw_part[r, nt] = sum_i dA' a
 //   dA = topk_w * dA';  dh = (dA u sig(g)(1 + g(1 - sig(g))) | dA silu(g))
 // =========================================================================
-template <class C>
+template <class C, bool SPLIT>
 __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
@@ -144,7 +162,9 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     lb.init(w2e, I, n0, I, wave0, lane0);
     Acc<C> acc;
     mainloop<C, false, true, false>(lds, H, la, lb, acc);
-    dgrad2_epilogue<C, 8>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh, g.dw_part);
+    // the split form loads twice the rows' data: half the rows a batch
+    dgrad2_epilogue<C, SPLIT ? 2 : 8, SPLIT>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh,
+                                             g.dw_part, g.h_lo, g.a_lo, g.dh_lo);
 }
 
 // =========================================================================
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
 // 66 elements so that the column reads of the four lanes fall in different
 // banks.
 // =========================================================================
-template <int NCT>
+template <int NCT, bool SPLIT>
 __global__ __launch_bounds__(256) void k_transpose_segments(ColQuant q, uint16_t *dst)
 {
     __shared__ __attribute__((aligned(16))) uint16_t tile[NCT * SEG_ROWS][66];
@@ -205,7 +225,7 @@ __global__ __launch_bounds__(256) void k_transpose_segments(ColQuant q, uint16_t
     __syncthreads();
     SegPos p;
     if (!seg_locate(q, mt_s, blockIdx.x / nct, p)) return;
-    seg_load_tile<66, NCT>(q, p, ct, tile);
+    seg_load_tile<66, NCT, SPLIT>(q, p, ct, tile);
     __syncthreads();
     const int b = threadIdx.x & 3, c = threadIdx.x >> 2;
 #pragma unroll
@@ -231,12 +251,18 @@ hipError_t launch_transpose_segments(const ColQuant &q, int64_t max_chunks, uint
     const int nct = (q.C / 64) % 4 == 0 ? 4 : (q.C / 64) % 2 == 0 ? 2 : 1;
     const int64_t blocks = max_chunks * (q.C / (64 * nct));
     if (blocks <= 0) return hipSuccess;
-    if (nct == 4)
-        hipLaunchKernelGGL(k_transpose_segments<4>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
-    else if (nct == 2)
-        hipLaunchKernelGGL(k_transpose_segments<2>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
-    else
-        hipLaunchKernelGGL(k_transpose_segments<1>, dim3((unsigned)blocks), dim3(256), 0, s, q, dst);
+    const bool split = q.src_lo != nullptr || q.lo_part != 0;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (nct == 4) {
+        if (split) hipLaunchKernelGGL((k_transpose_segments<4, true>), grid, block, 0, s, q, dst);
+        else hipLaunchKernelGGL((k_transpose_segments<4, false>), grid, block, 0, s, q, dst);
+    } else if (nct == 2) {
+        if (split) hipLaunchKernelGGL((k_transpose_segments<2, true>), grid, block, 0, s, q, dst);
+        else hipLaunchKernelGGL((k_transpose_segments<2, false>), grid, block, 0, s, q, dst);
+    } else {
+        if (split) hipLaunchKernelGGL((k_transpose_segments<1, true>), grid, block, 0, s, q, dst);
+        else hipLaunchKernelGGL((k_transpose_segments<1, false>), grid, block, 0, s, q, dst);
+    }
     return hipGetLastError();
 }
 
@@ -250,8 +276,11 @@ hipError_t launch_transpose_segments(const ColQuant &q, int64_t max_chunks, uint
 // copies and 16-byte fragment reads, no index loads, no partial stage.
 // Stage s (64 k) of a row r lies at byte (s/2) * rows * 256 + r * 256 +
 // (s%2) * 128 of the expert's area.
+// SPLIT: the k loop runs twice over the expert's rows; the second pass reads
+// the remainder half of the split operand (UP: tA_lo, the remainder of dh;
+// DOWN: tB_lo, the remainder of w*a) and the same chunks of the other one.
 // =========================================================================
-template <class C, bool UP>
+template <class C, bool UP, bool SPLIT>
 __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
 {
     __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
@@ -296,11 +325,27 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     }
     auto stage_off = [](int s, int64_t rows) { return (int64_t)(s >> 1) * rows * 256 + (s & 1) * 128; };
     Acc<C> acc;
-    pipeline<C, false, false, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
-        lds, 0, nst,
-        [&](int q, int s, lds_t *As) { la.issue_one(q, As, 0, BK, la.base + stage_off(s, R)); },
-        [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, 0, BK, lb.base + stage_off(s, Cc)); },
-        [](int, lds_t *, lds_t *) {}, acc);
+    if constexpr (SPLIT) {
+        const char *alo = UP ? (const char *)(g.tA_lo + (int64_t)R * SEG_ROWS * mt[e]) : la.base;
+        const char *blo = UP ? lb.base : (const char *)(g.tB_lo + (int64_t)Cc * SEG_ROWS * mt[e]);
+        pipeline<C, false, false, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
+            lds, 0, 2 * nst,
+            [&](int q, int s, lds_t *As) {
+                const bool lo = s >= nst;
+                la.issue_one(q, As, 0, BK, (lo ? alo : la.base) + stage_off(lo ? s - nst : s, R));
+            },
+            [&](int q, int s, lds_t *Bs) {
+                const bool lo = s >= nst;
+                lb.issue_one(q, Bs, 0, BK, (lo ? blo : lb.base) + stage_off(lo ? s - nst : s, Cc));
+            },
+            [](int, lds_t *, lds_t *) {}, acc);
+    } else {
+        pipeline<C, false, false, KLoad<C::BM, C::NT>::NI, KLoad<C::BN, C::NT>::NI>(
+            lds, 0, nst,
+            [&](int q, int s, lds_t *As) { la.issue_one(q, As, 0, BK, la.base + stage_off(s, R)); },
+            [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, 0, BK, lb.base + stage_off(s, Cc)); },
+            [](int, lds_t *, lds_t *) {}, acc);
+    }
     wgrad_epilogue<C, 8>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2, g.dw_acc,
                       g.dw_bf16);
 }
@@ -359,20 +404,25 @@ static hipError_t launch_k(K kern, int64_t blocks, const GemmArgs &g, hipStream_
 
 hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
 {
+    const bool sp = g.split != 0;
     switch (op) {
     case MOE_GEMM_UP_SWIGLU: {
         using C = UpCfg;
-        return launch_k(k_up_swiglu<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2)),
-                        g, s, C::NT);
+        const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2));
+        return sp ? launch_k(k_up_swiglu<C, true>, b, g, s, C::NT)
+                  : launch_k(k_up_swiglu<C, false>, b, g, s, C::NT);
     }
     case MOE_GEMM_DOWN: {
         using C = DownCfg;
-        return launch_k(k_down<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
+        const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN));
+        return sp ? launch_k(k_down<C, true>, b, g, s, C::NT)
+                  : launch_k(k_down<C, false>, b, g, s, C::NT);
     }
     case MOE_GEMM_DOWN_DGRAD: {
         using C = DownDgradCfg;
-        return launch_k(k_down_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN)),
-                        g, s, C::NT);
+        const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN));
+        return sp ? launch_k(k_down_dgrad<C, true>, b, g, s, C::NT)
+                  : launch_k(k_down_dgrad<C, false>, b, g, s, C::NT);
     }
     case MOE_GEMM_UP_DGRAD: {
         using C = UpDgradCfg;
@@ -381,14 +431,16 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
     case MOE_GEMM_DOWN_WGRAD: {
         using C = WgradCfg;
         const int64_t act = g.M < g.E ? g.M : g.E;  // non-empty experts, at most
-        int64_t total = act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN);
-        return launch_k(k_wgrad<C, false>, grid_for(total), g, s, C::NT);
+        const int64_t b = grid_for(act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN));
+        return sp ? launch_k(k_wgrad<C, false, true>, b, g, s, C::NT)
+                  : launch_k(k_wgrad<C, false, false>, b, g, s, C::NT);
     }
     case MOE_GEMM_UP_WGRAD: {
         using C = WgradCfg;
         const int64_t act = g.M < g.E ? g.M : g.E;
-        int64_t total = act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN);
-        return launch_k(k_wgrad<C, true>, grid_for(total), g, s, C::NT);
+        const int64_t b = grid_for(act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN));
+        return sp ? launch_k(k_wgrad<C, true, true>, b, g, s, C::NT)
+                  : launch_k(k_wgrad<C, true, false>, b, g, s, C::NT);
     }
     default:
         return hipErrorInvalidValue;

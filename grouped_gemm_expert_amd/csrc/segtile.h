@@ -71,7 +71,10 @@ MOE_DEV bool seg_locate(const ColQuant &q, const int32_t *mt_s, int64_t L, SegPo
 // thread waits for two memory round trips, not eight.  The caller
 // synchronises before reading the tile.  W = 64: 16-byte LDS writes; a
 // padded W (66) takes 4-byte ones.
-template <int W, int NCT = 1>
+// SPLIT (bf16 transposer): the values are formed in fp32 as
+// (src + src_lo) * rw and stored as bf16(v), or with q.lo_part as the
+// remainder bf16(v - bf16(v)).
+template <int W, int NCT = 1, bool SPLIT = false>
 MOE_DEV void seg_load_tile(const ColQuant &q, const SegPos &p, int ct, uint16_t (*tile)[W])
 {
     // NCT adjacent column tiles (ct .. ct+NCT-1) into tile[NCT*128][W]: one
@@ -100,11 +103,14 @@ MOE_DEV void seg_load_tile(const ColQuant &q, const SegPos &p, int ct, uint16_t 
 #pragma unroll
         for (int u = 0; u < NU; ++u) wr[u] = q.rw[rr[u]];
     }
-    u32x4_t v[NU];
+    u32x4_t v[NU], vl[SPLIT ? NU : 1];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
         const int qd = (threadIdx.x + 256 * u) & 7, t = (threadIdx.x + 256 * u) / (SEG_ROWS * 8);
         v[u] = *(const u32x4_t *)(q.src + sr[u] * q.C + (ct + t) * 64 + qd * 8);
+        if constexpr (SPLIT)
+            vl[u] = q.src_lo ? *(const u32x4_t *)(q.src_lo + sr[u] * q.C + (ct + t) * 64 + qd * 8)
+                             : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u)
@@ -114,7 +120,27 @@ MOE_DEV void seg_load_tile(const ColQuant &q, const SegPos &p, int ct, uint16_t 
         // tile row r of column tile t lands in row t*128 + r
         const int i = threadIdx.x + 256 * u, r = i >> 3, qd = i & 7;
         u32x4_t x = v[u];
-        if (q.rw) {
+        if constexpr (SPLIT) {
+            // v = (src + src_lo) * rw in fp32, then its bf16 part or remainder
+            const bool pad = ((i >> 3) % SEG_ROWS) >= p.len;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float f0 = bf2f((uint16_t)(x[e] & 0xffffu)), f1 = bf2f((uint16_t)(x[e] >> 16));
+                if (q.src_lo && !pad) {
+                    f0 += bf2f((uint16_t)(vl[u][e] & 0xffffu));
+                    f1 += bf2f((uint16_t)(vl[u][e] >> 16));
+                }
+                if (q.rw) {
+                    f0 *= wr[u];
+                    f1 *= wr[u];
+                }
+                if (q.lo_part) {
+                    f0 -= bf2f(f2bf(f0));
+                    f1 -= bf2f(f2bf(f1));
+                }
+                x[e] = pack_bf2(f0, f1);
+            }
+        } else if (q.rw) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 x[e] = pack_bf2(wr[u] * bf2f((uint16_t)(x[e] & 0xffffu)), wr[u] * bf2f((uint16_t)(x[e] >> 16)));

@@ -17,10 +17,15 @@ namespace moe {
 // columns one scale group) also quantise the bf16 a values of the row and
 // write 8 codes each and the group's scale word; columns at or past I are
 // quantised as zeros, so the padding of a's MX rows holds zero codes.
-template <class C, bool MX>
+// SPLIT: each value v also leaves as the bf16 rounding of its remainder,
+// bf16(v - bf16(v)), into h_lo and a_lo (a second pass through the staging
+// tile), so that hi + lo carries v to about 16 significant bits.
+template <class C, bool MX, bool SPLIT = false>
 MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int64_t i0, int I,
-                             uint16_t *h, uint16_t *a, uint8_t *aq, uint8_t *as_, int64_t Ip)
+                             uint16_t *h, uint16_t *a, uint8_t *aq, uint8_t *as_, int64_t Ip,
+                             uint16_t *h_lo = nullptr, uint16_t *a_lo = nullptr)
 {
+    static_assert(!(MX && SPLIT), "the split intermediates are a bf16-path form");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
@@ -32,6 +37,8 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
 #pragma unroll
     for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
         if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
+#pragma unroll
+      for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
             if ((wm * C::WM + i * 32) / EPI_ROWS != half) continue;
@@ -48,6 +55,11 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
                         gv[q] = acc.v[i][j][rg * 4 + q];
                         uv[q] = acc.v[i][j + HF][rg * 4 + q];
                         av[q] = gv[q] * sigmoidf_(gv[q]) * uv[q];
+                        if (SPLIT && part == 1) {  // the remainders below bf16
+                            gv[q] -= bf2f(f2bf(gv[q]));
+                            uv[q] -= bf2f(f2bf(uv[q]));
+                            av[q] -= bf2f(f2bf(av[q]));
+                        }
                     }
                     const int sub = (lane >> 5) << 3;  // byte offset inside the 16-byte chunk
                     *(lds_u64 *)(lds + soff(r, gc >> 3) + sub) = pack_bf4(gv[0], gv[1], gv[2], gv[3]);
@@ -58,7 +70,8 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
         __syncthreads();
         const int seg = lane >> 4;                     // 0 gate, 1 up, 2 a
         const int64_t col = i0 + 8 * (lane & 15);      // column within I
-        const bool live = lane < 48 && col < I && (seg == 2 || h != nullptr);
+        uint16_t *hd = part ? h_lo : h, *ad = part ? a_lo : a;
+        const bool live = lane < 48 && col < I && (seg == 2 || hd != nullptr);
         // RB rows a wave per pass: their LDS reads issued together, then the
         // stores (and the MX encoding, which every lane runs: rows past the
         // segment are only masked at the store)
@@ -74,7 +87,7 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
                 const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
                 const bool row_ok = m < t.seg_end;
                 if (live && row_ok) {
-                    uint16_t *dst = seg == 2 ? a + m * I + col : h + m * 2 * I + (seg ? I : 0) + col;
+                    uint16_t *dst = seg == 2 ? ad + m * I + col : hd + m * 2 * I + (seg ? I : 0) + col;
                     *(u32x4_t *)dst = v[b];
                 }
                 if constexpr (MX) {
@@ -99,6 +112,7 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
             }
         }
         __syncthreads();
+      }
     }
 }
 

@@ -39,6 +39,10 @@ class Workload:
     bias_std: Optional[float] = None
     logits: Optional[str] = None    # None: router weight; "zipf" / "normal": logits supplied
     route: str = "learned"          # "learned" | "even" (forced round-robin experts)
+    # intermediates of the expert path: "bf16", or "split" (hi + lo bf16
+    # pairs) for the layers whose outputs are large enough (|y| or |dW| of
+    # order 10) that one bf16 rounding exceeds the absolute error budget
+    precision: str = "bf16"
     backward: bool = True
     description: str = ""
 
@@ -59,10 +63,11 @@ WORKLOADS = {
         x_std=1.0, description="Tiny MoE fwd+bwd, top-2 softmax, no groups"),
     "few_large": Workload(
         "few_large", T=8192, H=4096, I=14336, E=8, k=2, score="softmax", renorm=True,
-        x_std=1.0, backward=False, description="Few-large-experts MoE fwd, top-2 softmax renorm"),
+        x_std=1.0, backward=False, precision="split",
+        description="Few-large-experts MoE fwd, top-2 softmax renorm"),
     "fine_grained": Workload(
         "fine_grained", T=16384, H=2048, I=768, E=128, k=8, score="softmax", renorm=True,
-        x_std=1.0, description="Fine-grained MoE fwd+bwd, top-8 softmax renorm"),
+        x_std=1.0, precision="split", description="Fine-grained MoE fwd+bwd, top-8 softmax renorm"),
     "deepseek_v3": Workload(
         "deepseek_v3", T=8192, H=7168, I=2048, E=256, k=8, n_groups=8, topk_groups=4,
         score="sigmoid", scale=2.5, x_std=0.02, bias_std=0.1,
@@ -96,6 +101,13 @@ WORKLOADS = {
         "even_softmax", T=333, H=128, I=128, E=8, k=2, score="softmax", renorm=False,
         x_std=1.0, route="even",
         description="parity shape, even forced routing, softmax without renorm"),
+    "mid_split": Workload(
+        "mid_split", T=600, H=256, I=192, E=16, k=4, score="softmax", renorm=True,
+        x_std=1.0, precision="split", description="parity shape, split intermediates"),
+    "mid_sigmoid_split": Workload(
+        "mid_sigmoid_split", T=500, H=384, I=320, E=32, k=6, n_groups=4, topk_groups=2,
+        score="sigmoid", scale=2.5, x_std=1.0, bias_std=0.1, precision="split",
+        description="parity shape, sigmoid + bias, group-limited, split intermediates"),
     "mid_skewed": Workload(
         "mid_skewed", T=700, H=256, I=128, E=64, k=4, n_groups=8, topk_groups=4,
         score="sigmoid", scale=2.5, x_std=1.0, logits="zipf",
@@ -188,4 +200,5 @@ def bf16_bits(t: torch.Tensor):
 def describe(w: Workload) -> str:
     return (f"{w.name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} G={w.n_groups} "
             f"kg={w.topk_groups} {w.score}" + (" renorm" if w.renorm else "")
+            + (" split" if w.precision == "split" else "")
             + (f" scale={w.scale}" if w.score == "sigmoid" else ""))

@@ -21,6 +21,7 @@ _LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_LEARNED, MOE_ROUTE_EVEN = 0, 1
+MOE_PRECISION_BF16, MOE_PRECISION_SPLIT = 0, 1
 (MOE_GEMM_UP_SWIGLU, MOE_GEMM_DOWN, MOE_GEMM_DOWN_DGRAD, MOE_GEMM_UP_DGRAD,
  MOE_GEMM_DOWN_WGRAD, MOE_GEMM_UP_WGRAD) = range(6)
 
@@ -32,12 +33,13 @@ class MoeConfig(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("renorm", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("aux_coeff", ctypes.c_float), ("route_mode", ctypes.c_int32)]
+                ("aux_coeff", ctypes.c_float), ("route_mode", ctypes.c_int32),
+                ("precision", ctypes.c_int32)]
 
 
 class MoeSaved(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("logits", "topk_idx", "topk_w", "counts", "offsets",
-                                  "row_map", "pos", "h", "a")]
+                                  "row_map", "pos", "h", "a", "h_lo", "a_lo")]
 
 
 class MoeGemmArgs(ctypes.Structure):
@@ -177,16 +179,19 @@ def _check(status: int, what: str):
 
 
 def config(T, H, I, E, k, n_groups=1, topk_groups=1, score="softmax", renorm=False,
-           scale=1.0, aux_coeff=0.01, route="learned") -> MoeConfig:
+           scale=1.0, aux_coeff=0.01, route="learned", precision="bf16") -> MoeConfig:
     sc = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}.get(score, score)
     rm = {"learned": MOE_ROUTE_LEARNED, "even": MOE_ROUTE_EVEN}.get(route, route)
+    pr = {"bf16": MOE_PRECISION_BF16, "split": MOE_PRECISION_SPLIT}.get(precision, precision)
     return MoeConfig(int(T), int(H), int(I), int(E), int(k), int(n_groups), int(topk_groups),
-                     int(sc), int(bool(renorm)), float(scale), float(aux_coeff), int(rm))
+                     int(sc), int(bool(renorm)), float(scale), float(aux_coeff), int(rm), int(pr))
 
 
-def config_from_workload(w, T=None) -> MoeConfig:
+def config_from_workload(w, T=None, precision=None) -> MoeConfig:
+    """The layer config of a workload; precision defaults to the workload's."""
     return config(w.T if T is None else T, w.H, w.I, w.E, w.k, w.n_groups, w.topk_groups,
-                  w.score, w.renorm, w.scale, w.aux_coeff, w.route)
+                  w.score, w.renorm, w.scale, w.aux_coeff, w.route,
+                  w.precision if precision is None else precision)
 
 
 def moe_version() -> str:
@@ -233,7 +238,7 @@ def moe_permute_checked(cfg, topk_idx, counts, offsets, row_map, pos, n_bad, ws,
                                     _ptr(ws), ws.numel(), _stream(stream)), "moe_permute_checked")
 
 
-SAVED_N = 9
+SAVED_N = 11
 
 
 def moe_saved_sizes(cfg: MoeConfig) -> dict:
@@ -270,7 +275,8 @@ def moe_combine(cfg, o, topk_w, pos, y, stream=None):
 def _saved_struct(saved: dict) -> MoeSaved:
     s = MoeSaved()
     for name, _ in MoeSaved._fields_:
-        setattr(s, name, saved[name].data_ptr())
+        t = saved.get(name)
+        setattr(s, name, None if t is None else t.data_ptr())
     return s
 
 
@@ -283,10 +289,13 @@ def alloc_saved(cfg: MoeConfig, device="cuda") -> dict:
               "topk_w": ((T, k), torch.float32), "counts": ((E,), torch.int32),
               "offsets": ((E + 1,), torch.int32), "row_map": ((M,), torch.int32),
               "pos": ((M,), torch.int32), "h": ((M, 2 * I), torch.bfloat16),
-              "a": ((M, I), torch.bfloat16)}
+              "a": ((M, I), torch.bfloat16), "h_lo": ((M, 2 * I), torch.bfloat16),
+              "a_lo": ((M, I), torch.bfloat16)}
     sizes = moe_saved_sizes(cfg)
     out = {}
     for name, (shape, dt) in shapes.items():
+        if name in ("h_lo", "a_lo") and sizes[name] == 0:
+            continue                          # not used at this precision
         n = 1
         for d in shape:
             n *= d

@@ -55,6 +55,7 @@ typedef enum {
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };      /* router score function */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };             /* dtype of weight gradients */
 enum { MOE_ROUTE_LEARNED = 0, MOE_ROUTE_EVEN = 1 }; /* expert choice (route_mode) */
+enum { MOE_PRECISION_BF16 = 0, MOE_PRECISION_SPLIT = 1 }; /* intermediates (precision) */
 
 /*
  * Layer configuration (host struct, read during the call only).
@@ -78,6 +79,24 @@ enum { MOE_ROUTE_LEARNED = 0, MOE_ROUTE_EVEN = 1 }; /* expert choice (route_mode
  *                experts by the rules above.  (The page's other form,
  *                `uniform`, replaces the logits by random values: pass seeded
  *                random logits with Wr = NULL and MOE_ROUTE_LEARNED.)
+ *   precision    how the expert path holds the intermediates its GEMMs read
+ *                (the pages fix no precision for them; y, dx and the
+ *                gradients are fp32 either way):
+ *                MOE_PRECISION_BF16: h, a and dh are bf16 values (one
+ *                rounding each, relative error up to 2^-9).
+ *                MOE_PRECISION_SPLIT: each also carries its bf16 remainder,
+ *                v = hi + lo with hi = bf16(v), lo = bf16(v - hi), so v is
+ *                kept to about 16 significant bits.  GEMM2 reads a + a_lo,
+ *                the SwiGLU backward g + g_lo and u + u_lo (h + h_lo), dW1
+ *                reads dh + dh_lo against x, and dW2 reads dy against
+ *                w*(a + a_lo) split again into hi + lo; each of those three
+ *                GEMMs runs its k loop twice (about twice their MFMA work).
+ *                dgrad of GEMM1 reads dh's hi part only.  For layers whose
+ *                outputs are large (|y| or |dW| of order 10), where one bf16
+ *                rounding of the intermediates exceeds an absolute error
+ *                budget of a few 1e-2.  The MXFP8 entry points and the
+ *                per-op GEMM entry points take MOE_PRECISION_BF16 only
+ *                (MOE_EUNSUPPORTED otherwise).
  * Ties in any ranking go to the lower index (expert or group).
  * Supported (moe_check_config; anything else returns MOE_EUNSUPPORTED):
  *   1 <= k <= E <= 1024, k <= 32;
@@ -89,7 +108,8 @@ enum { MOE_ROUTE_LEARNED = 0, MOE_ROUTE_EVEN = 1 }; /* expert choice (route_mode
  *   transposed weight-gradient operands with 32-bit element offsets), and
  *   2 * I * H < 2^31 (one expert's w1).  At H = 7168 and I = 2048 that is
  *   T*k <= 299593 and T <= 299465.
- * Negative sizes, an unknown score or route_mode return MOE_EINVAL.
+ * Negative sizes, an unknown score, route_mode or precision return
+ * MOE_EINVAL.
  */
 typedef struct {
     int64_t T;
@@ -100,6 +120,7 @@ typedef struct {
     float scale;
     float aux_coeff;
     int32_t route_mode;
+    int32_t precision;
 } moe_config;
 
 /*
@@ -114,8 +135,12 @@ typedef struct {
  *   pos      [M]    int32 flat slot -> sorted row
  *   h        [M,2I] bf16  GEMM1 output per sorted row: gate | up
  *   a        [M,I]  bf16  SwiGLU output per sorted row
+ *   h_lo     [M,2I] bf16  MOE_PRECISION_SPLIT: h's remainder (else unused,
+ *                         may be NULL)
+ *   a_lo     [M,I]  bf16  MOE_PRECISION_SPLIT: a's remainder (else unused,
+ *                         may be NULL)
  */
-#define MOE_SAVED_N 9  /* tensors in moe_saved, in declaration order */
+#define MOE_SAVED_N 11  /* tensors in moe_saved, in declaration order */
 typedef struct {
     float *logits;
     int32_t *topk_idx;
@@ -126,6 +151,8 @@ typedef struct {
     int32_t *pos;
     uint16_t *h;
     uint16_t *a;
+    uint16_t *h_lo;
+    uint16_t *a_lo;
 } moe_saved;
 
 const char *moe_status_string(moe_status s);
@@ -138,9 +165,10 @@ moe_status moe_check_config(const moe_config *cfg);
 
 /*
  * Bytes of each tensor of moe_saved for cfg, in declaration order (logits,
- * topk_idx, topk_w, counts, offsets, row_map, pos, h, a) into sizes[0..8]:
- * the allocations a caller makes before moe_forward.  MOE_EINVAL when sizes
- * is NULL; config errors as moe_check_config.
+ * topk_idx, topk_w, counts, offsets, row_map, pos, h, a, h_lo, a_lo) into
+ * sizes[0..10]: the allocations a caller makes before moe_forward (h_lo and
+ * a_lo are 0 unless cfg->precision is MOE_PRECISION_SPLIT).  MOE_EINVAL when
+ * sizes is NULL; config errors as moe_check_config.
  */
 moe_status moe_saved_sizes(const moe_config *cfg, size_t sizes[MOE_SAVED_N]);
 

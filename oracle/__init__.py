@@ -119,7 +119,7 @@ def _load():
         "oracle_mx_weight_grad_elements": [i64, i32, i32, i32, P, P, P, P] + [P] * 8
                                           + [i64, P, P, P, P, P],
         "oracle_mx_weight_grad_lines": [i64, i32, i32, i32, P, P, P, P] + [P] * 8
-                                       + [i64, P, P, P, P],
+                                       + [i64, P, P, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -527,9 +527,11 @@ def mx_weight_grad_elements(ops: MxBackwardOperands, x, dy, idx, w, which, ee, r
     return out
 
 
-def mx_weight_grad_lines(ops: MxBackwardOperands, x, dy, idx, w, which, ee, rr):
+def mx_weight_grad_lines(ops: MxBackwardOperands, x, dy, idx, w, which, ee, rr,
+                         with_magnitude: bool = False):
     """Whole lines of the MXFP8 weight gradients, [n, H] double: row rr of
-    dW1[ee] (which=1) or column rr of dW2[ee] (which=2)."""
+    dW1[ee] (which=1) or column rr of dW2[ee] (which=2).  With
+    with_magnitude, also the sums of the terms' magnitudes (same shape)."""
     x = _c(x, np.uint16)
     dy = _c(dy, np.uint16)
     idx = _c(idx, np.int32)
@@ -537,8 +539,10 @@ def mx_weight_grad_lines(ops: MxBackwardOperands, x, dy, idx, w, which, ee, rr):
     which, ee, rr = (_c(np.asarray(v), np.int32) for v in (which, ee, rr))
     T, k = idx.shape
     out = np.empty((which.shape[0], ops.H), np.float64)
+    mag = np.empty_like(out) if with_magnitude else None
     _load().oracle_mx_weight_grad_lines(T, ops.H, ops.I, k, _p(x), _p(dy), _p(idx), _p(w),
                                         _p(ops.xq), _p(ops.xs), _p(ops.w1q), _p(ops.w1s),
                                         _p(ops.dyq), _p(ops.dys), _p(ops.w2cq), _p(ops.w2cs),
-                                        which.shape[0], _p(which), _p(ee), _p(rr), _p(out))
-    return out
+                                        which.shape[0], _p(which), _p(ee), _p(rr), _p(out),
+                                        _p(mag))
+    return (out, mag) if with_magnitude else out

@@ -1100,14 +1100,16 @@ void oracle_mx_weight_grad_elements(int64_t T, int32_t H, int32_t I, int32_t k,
 /*                            = sum_r MX(dyw[:, h])_r MX(a[:, i])_r          */
 /* with the rows r of expert e (its flat slots, ascending) and the same      */
 /* operands and roundings as oracle_mx_weight_grad_elements; every column    */
-/* is quantised in blocks of 32 from the expert's first row.                 */
+/* is quantised in blocks of 32 from the expert's first row.  abs_out       */
+/* (optional, [nl, H]) receives the sums of the terms' magnitudes,          */
+/* sum_r |MX(.)_r MX(.)_r|, the scale of each sum's rounding.               */
 void oracle_mx_weight_grad_lines(int64_t T, int32_t H, int32_t I, int32_t k,
                                  const uint16_t *x, const uint16_t *dy, const int32_t *idx,
                                  const double *w, const uint8_t *xq, const uint8_t *xs,
                                  const uint8_t *w1q, const uint8_t *w1s, const uint8_t *dyq,
                                  const uint8_t *dys, const uint8_t *w2cq, const uint8_t *w2cs,
                                  int64_t nl, const int32_t *which, const int32_t *ee,
-                                 const int32_t *rr, double *out)
+                                 const int32_t *rr, double *out, double *abs_out)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t q = 0; q < nl; ++q) {
@@ -1152,9 +1154,13 @@ void oracle_mx_weight_grad_lines(int64_t T, int32_t H, int32_t I, int32_t k,
                 col[r] = which[q] == 2 ? bf16_of(w[f] * bf(dy[t * H + h])) : bf(x[t * H + h]);
             }
             mx_column(col, n, mcol);
-            double acc = 0.0;
-            for (r = 0; r < n; ++r) acc += mfixed[r] * mcol[r];
+            double acc = 0.0, mag = 0.0;
+            for (r = 0; r < n; ++r) {
+                acc += mfixed[r] * mcol[r];
+                mag += fabs(mfixed[r] * mcol[r]);
+            }
             out[q * H + h] = acc;
+            if (abs_out) abs_out[q * H + h] = mag;
         }
         free(slot);
         free(fixed);

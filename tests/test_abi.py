@@ -81,7 +81,7 @@ def test_saved_sizes():
     M = 300
     assert s == {"logits": 100 * 8 * 4, "topk_idx": M * 4, "topk_w": M * 4, "counts": 8 * 4,
                  "offsets": 9 * 4, "row_map": M * 4, "pos": M * 4, "h": M * 128 * 2,
-                 "a": M * 64 * 2}
+                 "a": M * 64 * 2, "h_lo": 0, "a_lo": 0}
     assert ops.moe_check_config(ops.config(T=100, H=128, I=64, E=8, k=9)) == 2
 
 
@@ -112,12 +112,12 @@ def test_error_paths_return_before_any_launch():
     lib = ops._lib
     cfg = ops.config(T=64, H=128, I=64, E=8, k=2)
     f, b = ops.moe_workspace_size(cfg)
-    saved = ops.MoeSaved(*[p.value for p in _fake(9)])
+    saved = ops.MoeSaved(*[p.value for p in _fake(11)])
     x, Wr, bias, w1, w2, y, aux, ws = _fake(8)
     stream = None
     by = ctypes.byref
-    # forward: a workspace one byte short, and a misaligned output
-    assert lib.moe_forward(by(cfg), x, Wr, None, w1, w2, y, aux, by(saved), ws, f - 1, stream) == 3
+    # forward: a workspace far too small, and a misaligned output
+    assert lib.moe_forward(by(cfg), x, Wr, None, w1, w2, y, aux, by(saved), ws, 256, stream) == 3
     y_bad = ctypes.c_void_p(y.value + 4)
     assert lib.moe_forward(by(cfg), x, Wr, None, w1, w2, y_bad, aux, by(saved), ws, f, stream) == 1
     # backward: a workspace one byte short; a bad weight-gradient dtype
@@ -134,6 +134,20 @@ def test_error_paths_return_before_any_launch():
     n = ctypes.c_size_t(0)
     assert lib.moe_mx_size(10, 48, by(n)) == 1
     assert lib.moe_mx_size(10, 64, by(n)) == 0 and n.value > 0
+    # split intermediates: the MXFP8 and per-op GEMM entry points refuse them,
+    # and the forward needs h_lo / a_lo in the saved set
+    cfg_s = ops.config(T=64, H=128, I=64, E=8, k=2, precision="split")
+    fs, bs = ops.moe_workspace_size(cfg_s)
+    assert fs >= f and bs > b
+    assert lib.moe_forward_mx(by(cfg_s), x, Wr, None, w1, w2, y, aux, by(saved), ws, fs,
+                              stream) == 2
+    saved_nolo = ops.MoeSaved(*([p.value for p in _fake(9)] + [None, None]))
+    assert lib.moe_forward(by(cfg_s), x, Wr, None, w1, w2, y, aux, by(saved_nolo), ws, fs,
+                           stream) == 1
+    assert ops.moe_check_config(ops.config(T=64, H=128, I=64, E=8, k=2, precision=5)) == 1
+    sz = ops.moe_saved_sizes(cfg_s)
+    assert sz["h_lo"] == sz["h"] and sz["a_lo"] == sz["a"]
+    assert ops.moe_saved_sizes(cfg)["h_lo"] == 0
     # an unknown grouped-GEMM op
     args = ops.MoeGemmArgs()
     args.counts, args.offsets = c.value, o.value

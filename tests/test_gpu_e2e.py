@@ -13,7 +13,8 @@ from tests import harness as hz
 
 pytestmark = pytest.mark.gpu
 
-E2E = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "mid_even", "even_softmax"]
+E2E = ["tiny", "mid_softmax", "mid_sigmoid", "mid_skewed", "mid_even", "even_softmax",
+       "mid_split", "mid_sigmoid_split"]
 
 
 def _oracle_logits32(w, dc):
@@ -96,6 +97,9 @@ EDGE = {
     "sigmoid_no_groups": _wl("mid_sigmoid", n_groups=1, topk_groups=1, T=300),
     "wide_tile_tail": _wl("mid_softmax", H=320, I=448, T=333, E=4, k=2),
     "small_dims": _wl("mid_softmax", H=64, I=64, T=130, E=4, k=2),
+    "split_single_token": _wl("mid_split", T=1),
+    "split_wide_tile_tail": _wl("mid_split", H=320, I=448, T=333, E=4, k=2),
+    "split_small_dims": _wl("mid_split", H=64, I=64, T=130, E=4, k=2),
 }
 
 
@@ -198,3 +202,35 @@ def test_run_to_run_determinism():
         assert torch.equal(a[key], b[key]), key
     for key in ("topk_idx", "row_map", "pos", "h", "a"):
         assert torch.equal(a["saved"][key], b["saved"][key]), key
+
+
+@pytest.mark.parametrize("base", ["mid_softmax", "mid_sigmoid"])
+def test_split_intermediates_remove_the_bf16_rounding(base):
+    """The same layer with bf16 and with split (hi + lo) intermediates, on
+    inputs whose outputs are large (x ~ N(0,1), weights ~ N(0,0.1)): the split
+    form's y, dW1 and dW2 must be several times closer to the oracle (their
+    bf16 errors come from rounding a, h and dh once), and both must meet the
+    bounds where they hold."""
+    from grouped_gemm_expert_amd import ops  # noqa: F401
+    w16 = _wl(base, w_std=0.1, precision="bf16")
+    wsp = _wl(base, w_std=0.1, precision="split")
+    hz.say(f"split vs bf16: {inputs.describe(wsp)}")
+    dc = inputs.make_inputs(w16, seed=5)
+    d = hz.to_device(dc)
+    l32, _ = _oracle_logits32(w16, dc)
+    lin = torch.from_numpy(l32).cuda() if dc["Wr"] is not None else None
+    g16 = hz.run_hip(w16, d, logits_in=lin)
+    gsp = hz.run_hip(wsp, d, logits_in=lin)
+    torch.cuda.synchronize()
+    l64, r = hz.oracle_route(w16, dc)
+    ref = hz.oracle_forward_backward(w16, dc, r, l64)
+    for key in ("y", "dW1", "dW2"):
+        e16 = hz.errors(g16[key].cpu().numpy(), ref[key])
+        esp = hz.errors(gsp[key].cpu().numpy(), ref[key])
+        hz.say(f"{base} {key}: bf16 max_abs={e16[0]:.3e} rel_fro={e16[1]:.3e}; "
+               f"split max_abs={esp[0]:.3e} rel_fro={esp[1]:.3e}")
+        assert esp[1] * 4 <= e16[1], key
+    # the routing and dgrad1's input (dh's hi part) are the same in both forms
+    assert torch.equal(g16["saved"]["topk_idx"], gsp["saved"]["topk_idx"])
+    assert torch.equal(g16["saved"]["h"], gsp["saved"]["h"])
+    assert torch.equal(g16["saved"]["a"], gsp["saved"]["a"])

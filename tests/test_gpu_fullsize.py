@@ -228,8 +228,10 @@ def test_fullsize_mx_backward_weight_grad_lines(ds, dsmx):
     DY = hz.bits(ds["d"]["dy"])
     ops_o = oracle.MxBackwardOperands.from_experts(ds["X"], DY, w.E, experts, W1c, W2c)
     which, ee, rr = hz.weight_grad_line_spec(experts, w.I, np.random.default_rng(3))
-    ref = oracle.mx_weight_grad_lines(ops_o, ds["X"], DY, r["idx"], r["w"], which, ee, rr)
+    ref, mag = oracle.mx_weight_grad_lines(ops_o, ds["X"], DY, r["idx"], r["w"], which, ee, rr,
+                                           with_magnitude=True)
     got = hz.gather_lines(dsmx["dW1"], dsmx["dW2"], which, ee, rr)
     for wh, name in ((1, "dW1"), (2, "dW2")):
         sel = which == wh
-        hz.assert_close(f"fullsize mx {name} lines", got[sel], ref[sel], hz.MX_GRAD_TOL)
+        hz.assert_mx_lines_within_window(f"fullsize mx {name} lines", got[sel], ref[sel],
+                                         mag[sel], counts[ee[sel]])

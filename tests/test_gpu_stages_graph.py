@@ -12,7 +12,7 @@ from tests import harness as hz
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["tiny", "mid_sigmoid", "mid_skewed"]
+NAMES = ["tiny", "mid_sigmoid", "mid_skewed", "mid_split"]
 OUTS = ["y", "aux", "dx", "dlogits", "dWr", "dW1", "dW2"]
 
 

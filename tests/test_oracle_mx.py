@@ -306,6 +306,42 @@ def _numpy_mx_backward(x, w1, w2, dy, idx, w):
     return dx, dw, dW1, dW2
 
 
+def _numpy_mx_backward_abs(x, w1, w2, dy, idx, w):
+    """As _numpy_mx_backward, with dW1 / dW2 formed from the magnitudes of
+    their MX operands (the sums of |terms|)."""
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    k = idx.shape[1]
+    Xd, DYd = _deq(x), _deq(dy)
+    W1d = _deq(w1.reshape(E * twoI, H)).reshape(E, twoI, H)
+    W2c = _deq(np.ascontiguousarray(w2.transpose(0, 2, 1)).reshape(E * I, H)).reshape(E, I, H)
+    rows = {e: [] for e in range(E)}
+    for f in range(T * k):
+        t, j = divmod(f, k)
+        e = idx[t, j]
+        h = Xd[t] @ W1d[e].T
+        g, u = h[:I], h[I:]
+        ab = _bf16_value(_round_bf16((g * scipy.special.expit(g) * u).astype(np.float32)))
+        dA = w[t, j] * (DYd[t] @ W2c[e].T)
+        gb = _bf16_value(_round_bf16(g.astype(np.float32)))
+        ub = _bf16_value(_round_bf16(u.astype(np.float32)))
+        sg = scipy.special.expit(gb)
+        dh = np.concatenate([dA * ub * sg * (1 + gb * (1 - sg)), dA * gb * sg])
+        dyw = _bf16_value(_round_bf16((w[t, j] * _bf16_value(dy[t])).astype(np.float32)))
+        rows[e].append((_bf16_value(_round_bf16(dh.astype(np.float32))), ab, dyw,
+                        _bf16_value(x[t])))
+    aW1 = np.zeros((E, twoI, H))
+    aW2 = np.zeros((E, H, I))
+    for e, rs in rows.items():
+        if not rs:
+            continue
+        DH, A, DYW, XG = (np.stack([r[q] for r in rs]) for q in range(4))
+        aW1[e] = np.abs(_deq_cols(DH)).T @ np.abs(_deq_cols(XG))
+        aW2[e] = np.abs(_deq_cols(DYW)).T @ np.abs(_deq_cols(A))
+    return None, None, aW1, aW2
+
+
 def test_mx_backward_tokens_against_numpy():
     x, w1, w2, dy, idx, w = _bwd_setup(21)
     T, E, k = x.shape[0], w1.shape[0], idx.shape[1]
@@ -356,10 +392,15 @@ def test_mx_weight_grad_lines_against_numpy():
     ee = np.repeat(np.arange(E), 3)
     rows = np.tile([0, I + 3, twoI - 1], E)
     cols = np.tile([0, 17, I - 1], E)
-    l1 = oracle.mx_weight_grad_lines(ops, x, dy, idx, w, np.ones_like(ee), ee, rows)
+    l1, m1 = oracle.mx_weight_grad_lines(ops, x, dy, idx, w, np.ones_like(ee), ee, rows,
+                                         with_magnitude=True)
     l2 = oracle.mx_weight_grad_lines(ops, x, dy, idx, w, np.full_like(ee, 2), ee, cols)
     assert np.allclose(l1, dW1[ee, rows, :], rtol=1e-9, atol=1e-12)
     assert np.allclose(l2, dW2[ee, :, cols], rtol=1e-9, atol=1e-12)
+    # the magnitudes: the same sums over |terms| (numpy formulation, |operands|)
+    _, _, aW1, _ = _numpy_mx_backward_abs(x, w1, w2, dy, idx, w)
+    assert np.allclose(m1, aW1[ee, rows, :], rtol=1e-9, atol=1e-12)
+    assert (m1 >= np.abs(l1) - 1e-12).all()
 
 
 def test_mx_backward_within_the_format_error_of_the_exact_backward():
