@@ -3,6 +3,8 @@
 // allocates, frees or synchronises; every call only enqueues on the stream.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "mxfmt.h"
 
@@ -1087,6 +1089,62 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
                                   stream));
     return moe_stage1_backward(cfg, saved, x, Wr, w1, d_aux, dx, dlogits, dWr, dW1, dw_dtype,
                                dw_accumulate, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------ no allocation ----
+// moe_forward on a scratch area the library owns: a file-scope device array
+// (one copy per GPU, created when the code object loads and held until the
+// process ends).  Host code never passes the array's name to a kernel: it
+// reads the array's device address once per device with hipGetSymbolAddress
+// and passes that.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[MOE_NOALLOC_MAX_DEVICES];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with that device current).
+static moe_status scratch_address(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+    if (dev < 0 || dev >= MOE_NOALLOC_MAX_DEVICES) return MOE_EUNSUPPORTED;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_EHIP;
+        if ((int)sdev != dev) return MOE_EINVAL;  // the stream must belong to the current device
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+moe_status moe_forward_noalloc_bytes(const moe_config *cfg, size_t *bytes)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    if (!bytes) return MOE_EINVAL;
+    *bytes = fwd_need(*cfg, false);
+    return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                               const float *bias, const uint16_t *w1, const uint16_t *w2,
+                               float *y, float *aux, const moe_saved *saved, hipStream_t stream)
+{
+    MOE_CHECK(moe_check_config(cfg));
+    const size_t need = fwd_need(*cfg, false);
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+    void *ws = nullptr;
+    MOE_CHECK(scratch_address(stream, &ws));
+    // every area of the forward workspace is written before it is read in one
+    // call, so nothing is cleared first
+    return moe_forward(cfg, x, Wr, bias, w1, w2, y, aux, saved, ws,
+                       (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

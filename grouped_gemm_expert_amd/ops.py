@@ -84,6 +84,10 @@ def _load():
     lib.moe_permute_checked.restype = S
     lib.moe_saved_sizes.argtypes = [CFG, ctypes.POINTER(sz)]
     lib.moe_saved_sizes.restype = S
+    lib.moe_forward_noalloc.argtypes = [CFG] + [_P] * 7 + [ctypes.POINTER(MoeSaved), _P]
+    lib.moe_forward_noalloc.restype = S
+    lib.moe_forward_noalloc_bytes.argtypes = [CFG, ctypes.POINTER(sz)]
+    lib.moe_forward_noalloc_bytes.restype = S
     lib.moe_grouped_gemm.argtypes = [ctypes.c_int32, CFG, ctypes.POINTER(MoeGemmArgs), _P, sz, _P]
     lib.moe_grouped_gemm.restype = S
     lib.moe_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]
@@ -135,7 +139,8 @@ _lib = _load()
 
 SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspace_size",
            "moe_saved_sizes", "moe_dw_part_cols", "moe_router", "moe_permute",
-           "moe_permute_checked", "moe_grouped_gemm", "moe_swiglu",
+           "moe_permute_checked", "moe_forward_noalloc", "moe_forward_noalloc_bytes",
+           "moe_grouped_gemm", "moe_swiglu",
            "moe_combine", "moe_forward", "moe_backward", "moe_stage1_forward",
            "moe_stage2_forward", "moe_stage2_backward", "moe_stage1_backward",
            "moe_set_stage_events", "moe_grouped_gemm_mx", "moe_mx_size", "moe_mx_quantize", "moe_stage1_forward_mx",
@@ -321,6 +326,24 @@ def moe_backward(cfg, saved: dict, x, Wr, w1, w2, dy, d_aux, dx, dlogits, dWr, d
                              _ptr(w2), _ptr(dy), _ptr(d_aux), _ptr(dx), _ptr(dlogits), _ptr(dWr),
                              _ptr(dW1), _ptr(dW2), dw_dtype, int(bool(dw_accumulate)), _ptr(ws),
                              ws.numel(), _stream(stream)), "moe_backward")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc_bytes(cfg) -> int:
+    b = ctypes.c_size_t(0)
+    _check(_lib.moe_forward_noalloc_bytes(ctypes.byref(cfg), ctypes.byref(b)),
+           "moe_forward_noalloc_bytes")
+    return int(b.value)
+
+
+def moe_forward_noalloc(cfg, x, Wr, bias, w1, w2, y, aux, saved: dict, stream=None):
+    """moe_forward on the library's own scratch array (no workspace argument)."""
+    s = _saved_struct(saved)
+    _check(_lib.moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias), _ptr(w1),
+                                    _ptr(w2), _ptr(y), _ptr(aux), ctypes.byref(s),
+                                    _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_stage1_forward(cfg, x, Wr, bias, w1, aux, saved: dict, ws, stream=None):

@@ -347,6 +347,31 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
                         int32_t dw_accumulate, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory around the call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is a scratch array
+ * of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * (created with the library's code object, kept until the process ends); the
+ * call itself allocates and frees nothing.
+ *   Arguments, results and errors as moe_forward, without ws / ws_bytes.
+ *   MOE_EWORKSPACE when the config needs more than MOE_NOALLOC_SCRATCH_BYTES
+ *   (moe_forward_noalloc_bytes tells what it needs: the bf16 forward's part of
+ *   the forward workspace; e.g. T*k*H*4 bytes plus a few MB for the router at
+ *   the DeepSeek-V3 shape, so up to about 200 tokens there).
+ *   The stream must belong to the current device (MOE_EINVAL otherwise); at
+ *   most MOE_NOALLOC_MAX_DEVICES devices (MOE_EUNSUPPORTED past them).
+ *   Calls on one GPU share its array: calls that overlap in time on one GPU
+ *   (different streams, or threads) race on it and are not supported.  Each
+ *   call writes every part of the array it reads before reading it.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define MOE_NOALLOC_MAX_DEVICES 64
+moe_status moe_forward_noalloc_bytes(const moe_config *cfg, size_t *bytes);
+moe_status moe_forward_noalloc(const moe_config *cfg, const uint16_t *x, const float *Wr,
+                               const float *bias, const uint16_t *w1, const uint16_t *w2,
+                               float *y, float *aux, const moe_saved *saved, hipStream_t stream);
+
+/*
  * The same layer as two stages that each own one weight (MegaMoE page,
  * "Design: two stages + weight modules"): stage 1 = router, dispatch and
  * GEMM1 + SwiGLU (w1); stage 2 = GEMM2 and combine (w2).  moe_forward is
