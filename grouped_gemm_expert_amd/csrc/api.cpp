@@ -644,6 +644,10 @@ static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const ui
     a.o = w.o;
     GemmArgs g = gemm_args(c, a, w.sched);
     set_split(g, c, saved, nullptr);
+    // with bf16 intermediates the expert outputs between GEMM2 and the
+    // combine are bf16 too (the combine sums them in fp32); split keeps fp32
+    const bool o16 = !w2_mx && c.precision == MOE_PRECISION_BF16;
+    if (o16) g.o_bf16 = (uint16_t *)w.o;
     if (!w2_mx) {
         MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));
     } else {
@@ -654,7 +658,11 @@ static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const ui
         MOE_TRY(launch_mx_gemm(MOE_GEMM_DOWN, g, stream));
     }
     StageMark mark(MOE_STAGE_COMBINE, stream);
-    MOE_TRY(launch_combine(c.T, c.k, c.H, w.o, saved->topk_w, saved->pos, y, stream));
+    if (o16)
+        MOE_TRY(launch_combine_bf16(c.T, c.k, c.H, (const uint16_t *)w.o, saved->topk_w, saved->pos,
+                                    y, stream));
+    else
+        MOE_TRY(launch_combine(c.T, c.k, c.H, w.o, saved->topk_w, saved->pos, y, stream));
     return MOE_OK;
 }
 
@@ -812,6 +820,22 @@ moe_status moe_mx_quantize_t(const uint16_t *src, int64_t batches, int64_t R, in
     q.dst = (uint8_t *)dst;
     StageMark mark(MOE_STAGE_MX_QUANT, stream);
     MOE_TRY(launch_mx_quantize_cols(q, batches * (mx_kp(R) / MX_GROUP), stream));
+    return MOE_OK;
+}
+
+moe_status moe_mx_quantize_both(const uint16_t *src, int64_t batches, int64_t R, int64_t C,
+                                void *dst, size_t dst_bytes, void *dst_t, size_t dst_t_bytes,
+                                hipStream_t stream)
+{
+    if (batches < 0 || R <= 0 || C <= 0 || R % 32 != 0 || C % 32 != 0) return MOE_EINVAL;
+    size_t need_f = 0, need_t = 0;
+    MOE_CHECK(moe_mx_size(batches * R, C, &need_f));
+    MOE_CHECK(moe_mx_size(batches * C, R, &need_t));
+    if (batches == 0) return MOE_OK;
+    MOE_CHECK(check_ptrs({src, dst, dst_t}));
+    if (dst_bytes < need_f || dst_t_bytes < need_t) return MOE_EINVAL;
+    StageMark mark(MOE_STAGE_MX_QUANT, stream);
+    MOE_TRY(launch_mx_quantize_both(src, batches, R, C, (uint8_t *)dst, (uint8_t *)dst_t, stream));
     return MOE_OK;
 }
 

@@ -45,11 +45,30 @@ MOE_DEV bool ranks_before(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
-// Wave-wide arg-max under ranks_before (butterfly; every lane gets the winner).
+// One step of a lane-permutation reduction under ranks_before: (v, i) takes
+// the better of itself and the pair DPP control CTRL brings in.
+template <int CTRL>
+MOE_DEV void argmax_dpp_step(float &v, int &i)
+{
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+    if (ranks_before(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Wave-wide arg-max under ranks_before; every lane gets the winner.  Inside
+// each row of 16 lanes by DPP lane permutations (swap neighbours, swap pairs,
+// mirror the half-rows, mirror the row: after each step every lane holds the
+// best of a group twice as large), then across the four rows by two
+// shuffles.  ranks_before is a total order (value descending, index
+// ascending), so the winner does not depend on the reduction order.
 MOE_DEV void wave_argmax(float &v, int &i)
 {
+    argmax_dpp_step<0xB1>(v, i);   // quad_perm(1, 0, 3, 2)
+    argmax_dpp_step<0x4E>(v, i);   // quad_perm(2, 3, 0, 1)
+    argmax_dpp_step<0x141>(v, i);  // row_half_mirror
+    argmax_dpp_step<0x140>(v, i);  // row_mirror
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
+    for (int off = 16; off <= 32; off <<= 1) {
         float ov = __shfl_xor(v, off, 64);
         int oi = __shfl_xor(i, off, 64);
         if (ranks_before(ov, oi, v, i)) { v = ov; i = oi; }
@@ -144,6 +163,9 @@ struct GemmArgs {
     // when set, dgrad1 writes its per-row partials of dx here in bf16
     // instead of to dxp (the fused backward; the per-op entry point keeps fp32)
     uint16_t *dxp_bf16;
+    // when set, GEMM2 writes the expert outputs here in bf16 instead of to o
+    // (the fused forward with bf16 intermediates; the per-op entry keeps fp32)
+    uint16_t *o_bf16;
     void *dW1, *dW2;
     int32_t dw_bf16, dw_acc;
     Sched sched;
@@ -181,6 +203,11 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
 hipError_t launch_mx_quantize(const uint16_t *src, int64_t rows, int64_t K, uint8_t *dst,
                               hipStream_t s);
 hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s);
+// MXFP8: both forms of src [B, R, C] from one read: dst_f the MX matrix of
+// [B*R, C] (along C), dst_t that of the stacked transposes [B*C, R] (along R)
+// (R % 32 == 0, C % 32 == 0)
+hipError_t launch_mx_quantize_both(const uint16_t *src, int64_t B, int64_t R, int64_t C,
+                                   uint8_t *dst_f, uint8_t *dst_t, hipStream_t s);
 // MXFP8: the transposes of column segments of a bf16 matrix src (row stride
 // C elements, C % 64 == 0) as MX matrices along the segment's rows.  Either
 // nseg uniform segments of R rows, written as one MX matrix [nseg*C, Rp]

@@ -14,7 +14,7 @@
 // outputs with few tiles split that list over several blocks (split-K) whose
 // partial sums a second kernel adds in a fixed order, so results are
 // deterministic.
-#include "tile.h"
+#include "bwd_epi.h"
 
 namespace moe {
 
@@ -98,10 +98,16 @@ __global__ __launch_bounds__(C::NT) void k_dense(DenseArgs d)
         },
         acc);
 
-    const int wm = (tid >> 6) / C::WAVES_N, wn = (tid >> 6) % C::WAVES_N;
     float *out = d.splits > 1 ? d.part + (int64_t)s * d.M * d.N : d.C;
     const bool add = d.splits == 1 && d.accumulate;
     const bool vec = (d.N & 3) == 0;
+    if (vec) {
+        // through the LDS staging tile: row-contiguous 16-byte loads (when
+        // adding) and stores, 4 rows a wave at a time
+        wgrad_epilogue<C, 4>(acc, lds, m0, n0, (int)d.M, (int)d.N, 0, out, add ? 1 : 0, 0);
+        return;
+    }
+    const int wm = (tid >> 6) / C::WAVES_N, wn = (tid >> 6) % C::WAVES_N;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
         const int64_t m = m0 + acc_row<C>(wm, i, lane);

@@ -28,6 +28,18 @@
 
 namespace moe {
 
+// Weight-gradient tile walk: tiles dealt to the XCDs in chunks of
+// WGRAD_XCD_CHUNK, and inside an expert groups of WGRAD_GR row tiles sweep
+// the column tiles (compile-time overridable for tuning builds).
+#ifndef MOE_WGRAD_XCD_CHUNK
+#define MOE_WGRAD_XCD_CHUNK 16
+#endif
+#ifndef MOE_WGRAD_GR
+#define MOE_WGRAD_GR 4
+#endif
+constexpr int64_t WGRAD_XCD_CHUNK = MOE_WGRAD_XCD_CHUNK;
+constexpr int WGRAD_GR = MOE_WGRAD_GR;
+
 int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
 {
     int64_t mt = M / BM + (M < E ? M : E) + 1;
@@ -129,7 +141,8 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
     } else {
         mainloop<C, false, false, false>(lds, I, la, lb, acc);
     }
-    store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
+    if (g.o_bf16) store_tile_f32<C>(acc, lds, g.o_bf16, t.m0, t.seg_end, n0, H);
+    else store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
 }
 
 // =========================================================================
@@ -291,12 +304,12 @@ __global__ __launch_bounds__(C::NT) void k_wgrad(GemmArgs g)
     const int nR = (int)ceil_div(R, C::BM), nC = (int)ceil_div(Cc, C::BN);
     const int64_t tpe = (int64_t)nR * nC;
     const int64_t total = (int64_t)g.sched.order[g.E] * tpe;  // non-empty experts only
-    const int64_t L = xcd_remap(blockIdx.x, total);
+    const int64_t L = xcd_remap<WGRAD_XCD_CHUNK>(blockIdx.x, total);
     if (L < 0) return;
     const int e = g.sched.order[L / tpe];
     // inside one expert: groups of GR row tiles sweep all column tiles, so
     // the tiles running together share A and B panels in L2
-    constexpr int GR = 4;
+    constexpr int GR = WGRAD_GR;
     const int64_t rest = L % tpe;
     const int64_t grp = rest / ((int64_t)GR * nC);
     const int64_t first = grp * GR;
@@ -431,14 +444,14 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
     case MOE_GEMM_DOWN_WGRAD: {
         using C = WgradCfg;
         const int64_t act = g.M < g.E ? g.M : g.E;  // non-empty experts, at most
-        const int64_t b = grid_for(act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN));
+        const int64_t b = grid_for<WGRAD_XCD_CHUNK>(act * ceil_div(g.H, C::BM) * ceil_div(g.I, C::BN));
         return sp ? launch_k(k_wgrad<C, false, true>, b, g, s, C::NT)
                   : launch_k(k_wgrad<C, false, false>, b, g, s, C::NT);
     }
     case MOE_GEMM_UP_WGRAD: {
         using C = WgradCfg;
         const int64_t act = g.M < g.E ? g.M : g.E;
-        const int64_t b = grid_for(act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN));
+        const int64_t b = grid_for<WGRAD_XCD_CHUNK>(act * ceil_div(2 * g.I, C::BM) * ceil_div(g.H, C::BN));
         return sp ? launch_k(k_wgrad<C, true, true>, b, g, s, C::NT)
                   : launch_k(k_wgrad<C, true, false>, b, g, s, C::NT);
     }

@@ -196,6 +196,113 @@ hipError_t launch_mx_quantize_cols(const ColQuant &q, int64_t max_chunks, hipStr
     return hipGetLastError();
 }
 
+// Both MX forms of a batch of matrices src [B, R, C] (bf16) from one read:
+// the rows' form along C (dst_f, the MX matrix of [B*R, C]) and the
+// transposes' form along R (dst_t, the MX matrix of the stacked transposes
+// [B*C, R]).  A block takes a 128 x 128 tile of one batch into LDS (values
+// past R or C read as zero), then
+//   - along C: sixteen lanes a row, 8 values each (as k_mx_quantize), codes
+//     and the row's scale word for that 128-column group;
+//   - along R: one thread per (column, 32-row block) (as
+//     k_mx_quantize_cols), 32 codes contiguous in the transposed row and the
+//     scale bytes gathered through LDS into the group's word.
+// Rows past R and columns past C are not written (they belong to the next
+// batch); the codes and scales are those the two separate quantisers give.
+constexpr int QB_PAD = 136;  // LDS row of the tile: 128 values + 16 bytes
+__global__ __launch_bounds__(256) void k_mx_quantize_both(const uint16_t *src, int64_t B, int64_t R,
+                                                          int64_t C, uint8_t *dst_f,
+                                                          uint8_t *dst_t, int64_t ntiles)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tile[128][QB_PAD];
+    __shared__ uint32_t sc[4][128];
+    const int t = threadIdx.x, lane = t & 63;
+    const int64_t nr = ceil_div(R, 128), nc = ceil_div(C, 128);
+    const int64_t Cp = mx_kp(C), Rp = mx_kp(R);
+    uint8_t *codes_f = dst_f, *scales_f = dst_f + B * R * Cp;
+    uint8_t *codes_t = dst_t, *scales_t = dst_t + B * C * Rp;
+    for (int64_t L = blockIdx.x; L < ntiles; L += gridDim.x) {
+        const int64_t b = L / (nr * nc), rem = L % (nr * nc);
+        const int64_t rj = rem / nc, cj = rem % nc;   // 128-row and 128-column group
+        const int64_t r0 = rj * 128, c0 = cj * 128;
+        const uint16_t *sb = src + b * R * C;
+        // load: 16 lanes a row (16 bytes each), 16 rows per pass, 8 passes
+        u32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t r = r0 + (t >> 4) + 16 * u, c = c0 + (t & 15) * 8;
+            v[u] = (r < R && c < C) ? *(const u32x4_t *)(sb + r * C + c) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            *(u32x4_t *)&tile[(t >> 4) + 16 * u][(t & 15) * 8] = v[u];
+        __syncthreads();
+        // along C: row (t/16 + 16 u) of the tile, columns 8 (t%16) .. +7
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const u32x4_t x = v[u];
+            float f[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f[2 * q] = bf2f((uint16_t)(x[q] & 0xffffu));
+                f[2 * q + 1] = bf2f((uint16_t)(x[q] >> 16));
+            }
+            uint32_t s8;
+            const uint64_t cw = mx_quant8(f, s8);
+            const uint32_t word = mx_group_word(s8, lane);
+            const int64_t r = r0 + (t >> 4) + 16 * u;
+            if (r < R) {
+                const int64_t orow = b * R + r;
+                *(uint64_t *)(codes_f + orow * Cp + c0 + (t & 15) * 8) = cw;
+                if ((t & 15) == 0) *(uint32_t *)(scales_f + mx_scale_off(orow, cj, Cp / MX_GROUP)) = word;
+            }
+        }
+        // along R: column (task % 128), 32-row block (task / 128)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int task = t + 256 * k2, c = task & 127, blk = task >> 7;
+            float f[32];
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                f[i] = bf2f(tile[32 * blk + i][c]);
+                amax = fmaxf(amax, fabsf(f[i]));
+            }
+            const int X = mx_block_exp(amax);
+            uint32_t w[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float (&f8)[8] = *reinterpret_cast<const float(*)[8]>(&f[8 * h]);
+                const uint64_t c8 = e4m3_codes8(f8, X);
+                w[2 * h] = (uint32_t)c8;
+                w[2 * h + 1] = (uint32_t)(c8 >> 32);
+            }
+            if (c0 + c < C) {
+                uint8_t *d = codes_t + (b * C + c0 + c) * Rp + r0 + blk * 32;
+                *(u32x4_t *)d = u32x4_t{w[0], w[1], w[2], w[3]};
+                *(u32x4_t *)(d + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+            }
+            sc[blk][c] = (uint32_t)(X + 127);
+        }
+        __syncthreads();
+        if (t < 128 && c0 + t < C) {
+            const uint32_t word = sc[0][t] | (sc[2][t] << 8) | (sc[1][t] << 16) | (sc[3][t] << 24);
+            *(uint32_t *)(scales_t + mx_scale_off(b * C + c0 + t, rj, Rp / MX_GROUP)) = word;
+        }
+        __syncthreads();  // the tile and sc are reused by the next iteration
+    }
+}
+
+hipError_t launch_mx_quantize_both(const uint16_t *src, int64_t B, int64_t R, int64_t C,
+                                   uint8_t *dst_f, uint8_t *dst_t, hipStream_t s)
+{
+    const int64_t ntiles = B * ceil_div(R, 128) * ceil_div(C, 128);
+    if (ntiles <= 0) return hipSuccess;
+    const int64_t grid = ntiles < 65536 ? ntiles : 65536;
+    hipLaunchKernelGGL(k_mx_quantize_both, dim3((unsigned)grid), dim3(256), 0, s, src, B, R, C,
+                       dst_f, dst_t, ntiles);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- tiles ----
 // BM x BN output tile of waves WM x WN; per stage 128 fp8 of k: A and B tiles
 // of 128 bytes a row (as the bf16 tiles) plus the stage's scales, a 256-byte

@@ -542,14 +542,16 @@ MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, OutT *out, int64_t m0
 // while tiles of unequal cost spread evenly over all XCDs.  The grid is a
 // multiple of 8 * XCD_CHUNK and at least `total` rounded up to that.
 constexpr int64_t XCD_CHUNK = 16;  // measured faster overall than 8, 32 or 64
+template <int64_t CH = XCD_CHUNK>
 MOE_DEV int64_t xcd_remap(int64_t b, int64_t total)
 {
     const int64_t x = b & 7, j = b >> 3;
-    const int64_t L = ((j / XCD_CHUNK) * 8 + x) * XCD_CHUNK + (j % XCD_CHUNK);
+    const int64_t L = ((j / CH) * 8 + x) * CH + (j % CH);
     return L < total ? L : -1;
 }
 
-inline int64_t grid_for(int64_t total) { return ceil_div(total, 8 * XCD_CHUNK) * 8 * XCD_CHUNK; }
+template <int64_t CH = XCD_CHUNK>
+inline int64_t grid_for(int64_t total) { return ceil_div(total, 8 * CH) * 8 * CH; }
 
 // ------------------------------------------------------------ schedule ----
 // Forward and dgrad GEMMs tile the sorted rows of each expert (M-grouped):

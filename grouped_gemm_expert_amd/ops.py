@@ -126,6 +126,9 @@ def _load():
     lib.moe_forward_mx.restype = S
     lib.moe_mx_quantize_t.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, sz, _P]
     lib.moe_mx_quantize_t.restype = S
+    lib.moe_mx_quantize_both.argtypes = [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, sz,
+                                         _P, sz, _P]
+    lib.moe_mx_quantize_both.restype = S
     lib.moe_stage2_backward_mx.argtypes = [CFG, SP, _P, _P, _P, I32, I32, _P, sz, _P]
     lib.moe_stage2_backward_mx.restype = S
     lib.moe_stage1_backward_mx.argtypes = [CFG, SP] + [_P] * 8 + [I32, I32, _P, sz, _P]
@@ -144,7 +147,7 @@ SYMBOLS = ("moe_status_string", "moe_version", "moe_check_config", "moe_workspac
            "moe_combine", "moe_forward", "moe_backward", "moe_stage1_forward",
            "moe_stage2_forward", "moe_stage2_backward", "moe_stage1_backward",
            "moe_set_stage_events", "moe_grouped_gemm_mx", "moe_mx_size", "moe_mx_quantize", "moe_stage1_forward_mx",
-           "moe_stage2_forward_mx", "moe_forward_mx", "moe_mx_quantize_t",
+           "moe_stage2_forward_mx", "moe_forward_mx", "moe_mx_quantize_t", "moe_mx_quantize_both",
            "moe_stage2_backward_mx", "moe_stage1_backward_mx", "moe_backward_mx")
 
 STAGES = {"up_swiglu": 0, "down": 1, "down_dgrad": 2, "up_dgrad": 3, "down_wgrad": 4,
@@ -426,6 +429,15 @@ def moe_mx_quantize_t(src: torch.Tensor, dst: torch.Tensor, stream=None):
            "moe_mx_quantize_t")
 
 
+def moe_mx_quantize_both(src: torch.Tensor, dst: torch.Tensor, dst_t: torch.Tensor, stream=None):
+    """Both MX forms of src [batches, R, C] (bf16) from one read: dst the MX
+    matrix of [batches*R, C] along C, dst_t that of the stacked transposes
+    [batches*C, R] along R (each moe_mx_size bytes)."""
+    B, R, C = src.shape
+    _check(_lib.moe_mx_quantize_both(_ptr(src), B, R, C, _ptr(dst), dst.numel(), _ptr(dst_t),
+                                     dst_t.numel(), _stream(stream)), "moe_mx_quantize_both")
+
+
 class MxWeightCache:
     """The MXFP8 forms of w1 and w2, rebuilt when either weight changes: the
     forward's (w1 along H, w2 along I) and, with backward=True, the
@@ -462,15 +474,17 @@ class MxWeightCache:
                 self.w1_mx = mx_alloc(E * twoI, H, w1.device)
             if self.w2_mx is None or self.w2_mx.numel() != moe_mx_size(E * H, I):
                 self.w2_mx = mx_alloc(E * H, I, w2.device)
-            moe_mx_quantize(w1, self.w1_mx, stream)
-            moe_mx_quantize(w2, self.w2_mx, stream)
             if self.backward:
+                # both forms of each weight from one read of it
                 if self.w1t_mx is None or self.w1t_mx.numel() != moe_mx_size(E * H, twoI):
                     self.w1t_mx = mx_alloc(E * H, twoI, w1.device)
                 if self.w2t_mx is None or self.w2t_mx.numel() != moe_mx_size(E * I, H):
                     self.w2t_mx = mx_alloc(E * I, H, w2.device)
-                moe_mx_quantize_t(w1, self.w1t_mx, stream)
-                moe_mx_quantize_t(w2, self.w2t_mx, stream)
+                moe_mx_quantize_both(w1, self.w1_mx, self.w1t_mx, stream)
+                moe_mx_quantize_both(w2, self.w2_mx, self.w2t_mx, stream)
+            else:
+                moe_mx_quantize(w1, self.w1_mx, stream)
+                moe_mx_quantize(w2, self.w2_mx, stream)
             self._key = key
             self.builds += 1
         return self.w1_mx, self.w2_mx

@@ -502,6 +502,19 @@ moe_status moe_grouped_gemm_mx(int32_t op, const moe_config *cfg, const moe_gemm
  */
 moe_status moe_mx_quantize_t(const uint16_t *src, int64_t batches, int64_t R, int64_t C, void *dst,
                              size_t dst_bytes, hipStream_t stream);
+/*
+ * moe_mx_quantize_both  both cache forms of one weight from a single read of
+ *                   src [batches, R, C] (bf16): dst gets the MX matrix of
+ *                   [batches*R, C] along C (what moe_mx_quantize writes) and
+ *                   dst_t that of the stacked transposes [batches*C, R] along R
+ *                   (what moe_mx_quantize_t writes), bit for bit.  R % 32 == 0
+ *                   and C % 32 == 0; each destination at least its
+ *                   moe_mx_size, MOE_EINVAL otherwise.  The weight-cache fill
+ *                   of the MXFP8 backward: w1 as [E, 2I, H], w2 as [E, H, I].
+ */
+moe_status moe_mx_quantize_both(const uint16_t *src, int64_t batches, int64_t R, int64_t C,
+                                void *dst, size_t dst_bytes, void *dst_t, size_t dst_t_bytes,
+                                hipStream_t stream);
 moe_status moe_stage2_backward_mx(const moe_config *cfg, const moe_saved *saved,
                                   const void *w2t_mx, const uint16_t *dy, void *dW2,
                                   int32_t dw_dtype, int32_t dw_accumulate, void *ws,

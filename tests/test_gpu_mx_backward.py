@@ -67,6 +67,59 @@ def test_mx_quantize_t_bit_exact(B, R, C):
     assert not codes[:, R:].any() and not scales[:, R // 32:].any()
 
 
+QB = [(4, 64, 128), (3, 96, 192), (2, 384, 320), (5, 32, 64), (2, 64, 160), (1, 2048, 896)]
+
+
+@pytest.mark.parametrize("B,R,C", QB)
+def test_mx_quantize_both_bit_exact(B, R, C):
+    """Both cache forms from one read: the row form along C equals
+    moe_mx_quantize's and the oracle's, the transposed form along R equals
+    moe_mx_quantize_t's (where it takes the shape) and the oracle's; ragged
+    128-groups in R and C, zero blocks, negative zeros and subnormals."""
+    from grouped_gemm_expert_amd import ops
+    hz.say(f"mx quantize_both batches={B} R={R} C={C}")
+    rng = np.random.default_rng(B * 7 + R + 3 * C)
+    v = np.ldexp(rng.uniform(1, 2, (B, R, C)), rng.integers(-20, 6, (B, R, C)))
+    v *= rng.choice([-1.0, 1.0], (B, R, C))
+    v[rng.random((B, R, C)) < 0.05] = 0.0
+    v[rng.random((B, R, C)) < 0.02] = -0.0
+    v[:, :32, :32] = 0.0
+    sub = v[:, -32:, -8:]
+    sub[...] = np.ldexp(rng.uniform(1, 2, sub.shape), rng.integers(-133, -126, sub.shape))
+    src = _bf16_bits_of(v.astype(np.float32))
+    dev = torch.from_numpy(src.view(np.int16)).view(torch.bfloat16).cuda()
+    f = ops.mx_alloc(B * R, C)
+    t = ops.mx_alloc(B * C, R)
+    f.fill_(0xAB)
+    t.fill_(0xCD)
+    ops.moe_mx_quantize_both(dev, f, t)
+    torch.cuda.synchronize()
+    # the row form along C
+    c_f, s_f = ops.mx_views(f, B * R, C)
+    ref_c, ref_s = oracle.mx_quantize(src.reshape(B * R, C))
+    c_f, s_f = c_f.cpu().numpy(), s_f.cpu().numpy()
+    assert np.array_equal(c_f[:, :C], ref_c) and np.array_equal(s_f[:, :C // 32], ref_s)
+    assert not c_f[:, C:].any() and not s_f[:, C // 32:].any()
+    f2 = ops.mx_alloc(B * R, C)
+    f2.fill_(0xAB)
+    ops.moe_mx_quantize(dev, f2)
+    # the transposed form along R
+    c_t, s_t = ops.mx_views(t, B * C, R)
+    ref_c, ref_s = oracle.mx_quantize(np.ascontiguousarray(src.transpose(0, 2, 1)).reshape(B * C, R))
+    c_t, s_t = c_t.cpu().numpy(), s_t.cpu().numpy()
+    assert np.array_equal(c_t[:, :R], ref_c) and np.array_equal(s_t[:, :R // 32], ref_s)
+    assert not c_t[:, R:].any() and not s_t[:, R // 32:].any()
+    torch.cuda.synchronize()
+    # the whole buffers equal the separate quantisers' (scale padding included)
+    assert torch.equal(f[:f2.numel()], f2)
+    if C % 64 == 0:
+        t2 = ops.mx_alloc(B * C, R)
+        t2.fill_(0xCD)
+        ops.moe_mx_quantize_t(dev, t2)
+        torch.cuda.synchronize()
+        assert torch.equal(t, t2)
+
+
 def test_mx_weight_cache_backward_forms():
     from grouped_gemm_expert_amd import ops
     w = inputs.WORKLOADS["mid_sigmoid"]
@@ -75,6 +128,11 @@ def test_mx_weight_cache_backward_forms():
     cache.get(d["w1"], d["w2"])
     torch.cuda.synchronize()
     E, H, I = w.E, w.H, w.I
+    for buf, src, rows, K in ((cache.w1_mx, d["w1"], E * 2 * I, H), (cache.w2_mx, d["w2"], E * H, I)):
+        c, s = ops.mx_views(buf, rows, K)
+        ref_c, ref_s = oracle.mx_quantize(hz.bits(src).reshape(rows, K))
+        assert np.array_equal(c.cpu().numpy()[:, :K], ref_c)
+        assert np.array_equal(s.cpu().numpy()[:, :K // 32], ref_s)
     for buf, src, rows, K in ((cache.w2t_mx, d["w2"], E * I, H), (cache.w1t_mx, d["w1"], E * H, 2 * I)):
         c, s = ops.mx_views(buf, rows, K)
         ref_c, ref_s = oracle.mx_quantize(np.ascontiguousarray(hz.bits(src).transpose(0, 2, 1)).reshape(rows, K))
