@@ -85,11 +85,12 @@ def gemm_bytes(w, stage, counts, dw_accumulate):
     act = sum(1 for c in counts if c > 0)
     w1b, w2b = act * 2 * I * H * 2, act * H * I * 2
     rmw = 2 if dw_accumulate else 1
+    ob = 2 if w.precision == "bf16" else 4   # GEMM2's expert outputs o: bf16 with bf16 intermediates
     dw1 = (act * rmw + (0 if dw_accumulate else E - act)) * 2 * I * H * 4
     dw2 = (act * rmw + (0 if dw_accumulate else E - act)) * H * I * 4
     return {
         "up_swiglu": T * H * 2 + w1b + M * 2 * I * 2 + M * I * 2,
-        "down": M * I * 2 + w2b + M * H * 4,
+        "down": M * I * 2 + w2b + M * H * ob,
         "down_dgrad": T * H * 2 + w2b + M * 2 * I * 2 + M * I * 2 + M * 2 * I * 2,
         "up_dgrad": M * 2 * I * 2 + w1b + M * H * 2,
         "down_wgrad": M * H * 2 + M * I * 2 + dw2,
@@ -101,11 +102,12 @@ def stage_bytes(w, stage, with_router_weight):
     """Algorithmic HBM bytes of the memory-bound stages (each operand once)."""
     T, E, k, H = w.T, w.E, w.k, w.H
     M = T * k
+    ob = 2 if w.precision == "bf16" else 4   # expert outputs o (bf16 with bf16 intermediates)
     return {
         "router_proj": T * H * 2 + E * H * 4 + T * E * 4,
         "router": T * E * 4 + E * 4 + T * k * 8 + E * 4,
         "permute": 2 * M * 4 + 2 * M * 4 + 2 * (E + 1) * 4,
-        "combine": M * H * 4 + T * H * 4 + M * 8,
+        "combine": M * H * ob + T * H * 4 + M * 8,
         "router_bwd": T * E * 4 * 2 + M * 12,
         "unpermute": M * H * 2 + T * H * 4 + M * 4,   # dx partials in bf16
     }.get(stage)
@@ -348,6 +350,14 @@ def durations(d, counter):
     return [(n, us) for _, n, _, us in counter_rows(d, counter)]
 
 
+def wgrad_is_up(name):
+    """The UP flag of a weight-gradient kernel's name: the first template
+    argument after the tile configuration (k_wgrad<Cfg<...>, UP, SPLIT>,
+    k_wgrad_mx<Cfg<...>, UP>)."""
+    rest = name.split(">, ", 1)[1] if ">, " in name else ""
+    return rest.lstrip().startswith("true")
+
+
 def pmc_busy_summary(busy_dir, out_path, cmds):
     """MFMA utilisation and clock of the grouped GEMMs from one rocprofv3 --pmc
     run of SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) and
@@ -368,7 +378,7 @@ def pmc_busy_summary(busy_dir, out_path, cmds):
         want_up = stage.startswith("up_wgrad")
         wgrad = stage.startswith(("down_wgrad", "up_wgrad"))
         sel = [(i, v) for i, n, v, _ in busy if frag in n and
-               (not wgrad or n.split(">")[-2].strip().endswith("true") == want_up)]
+               (not wgrad or wgrad_is_up(n) == want_up)]
         if not sel:
             continue
         fr, ck = [], []
@@ -388,7 +398,15 @@ def pmc_busy_summary(busy_dir, out_path, cmds):
     print("\n".join(L))
 
 
-def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
+TRAFFIC_TITLES = {
+    "deepseek_v3": "DeepSeek-V3-style MoE layer (T=8192 H=7168 I=2048 E=256 G=8 kg=4 k=8)",
+    "uniform": "DeepSeek-V3 shapes under `uniform` force load balancing (T=8192 H=7168 I=2048 "
+               "E=256 k=8, seeded N(0, 1) logits: every expert gets rows)",
+}
+
+
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds,
+                workload="deepseek_v3"):
     """Turn four rocprofv3 --pmc runs (bench FETCH_SIZE, bench WRITE_SIZE, copy
     FETCH_SIZE, copy WRITE_SIZE) into the traffic record bench.py reads."""
     import csv
@@ -417,7 +435,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
         wgrad = stage.startswith(("down_wgrad", "up_wgrad"))
         def pick(rs):
             v = [x for _, n, x in rs if frag in n and
-                 (not wgrad or n.split(">")[-2].strip().endswith("true") == want_up)]
+                 (not wgrad or wgrad_is_up(n) == want_up)]
             return sum(v) / len(v) if v else None
         f, wr = pick(fetch), pick(write)
         if f is None or wr is None:
@@ -437,8 +455,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds):
         mem[frag] = (b, sum(dur) / len(dur))
     rec = {"source_hash": kernel_source_hash(), "copy_scale_fetch": round(sf, 4),
            "copy_scale_write": round(sw, 4), "kernels": kern}
-    L = ["# HBM traffic of the grouped GEMMs: DeepSeek-V3-style MoE layer (T=8192 H=7168 I=2048 "
-         "E=256 G=8 kg=4 k=8), MI355X", "",
+    L = [f"# HBM traffic of the grouped GEMMs: {TRAFFIC_TITLES[workload]}, MI355X", "",
          "Commands (from the repository root on the GPU box):", "", "```"] + cmds + ["```", "",
          f"Calibration: a plain {COPY_BYTES} byte device copy reads FETCH_SIZE x {sf:.4f} and "
          f"WRITE_SIZE x {sw:.4f} of its true size; the per-launch figures below are scaled by "
@@ -558,12 +575,16 @@ def main():
                     help="write the MFMA-busy profile from a rocprofv3 --pmc run of "
                          "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
     ap.add_argument("--pmc-commands", default="", help="commands recorded with --pmc-summary (;-separated)")
+    ap.add_argument("--pmc-workload", default="deepseek_v3", choices=sorted(TRAFFIC_TITLES),
+                    help="the workload the --pmc-summary runs measured (picks the record file)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
         return
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, TRAFFIC_FILE, [c.strip() for c in args.pmc_commands.split(";") if c.strip()])
+        out_path = UNIFORM_TRAFFIC_FILE if args.pmc_workload == "uniform" else TRAFFIC_FILE
+        pmc_summary(*args.pmc_summary, out_path,
+                    [c.strip() for c in args.pmc_commands.split(";") if c.strip()], args.pmc_workload)
         return
     if args.pmc_busy_summary:
         pmc_busy_summary(args.pmc_busy_summary, BUSY_FILE,

@@ -7,6 +7,51 @@
 
 namespace moe {
 
+// Sums over the wave of RB row partials at once: p[b] is this lane's part of
+// row b.  log2(RB) halving exchanges (lane ^ 32, ^ 16, ...: after the one
+// with mask m, lanes with bit m set keep the upper half of the rows, adding
+// their partner's copies), then the lanes that share a row add up over the
+// remaining low lane bits by DPP (quad swaps, half-row and row mirrors) and
+// at most one shuffle.  Every lane returns the total of row `row`.
+// One halving level, N rows still held (compile-time, so p stays in registers).
+template <int RB, int N>
+MOE_DEV void rows_halve(float (&p)[RB], int lane, int &row)
+{
+    if constexpr (N > 1) {
+        constexpr int m = 32 * N / RB;
+        const bool up = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float send = up ? p[i] : p[N / 2 + i];
+            const float keep = up ? p[N / 2 + i] : p[i];
+            p[i] = keep + __shfl_xor(send, m, 64);
+        }
+        if (up) row += N / 2;
+        rows_halve<RB, N / 2>(p, lane, row);
+    }
+}
+
+template <int CTRL>
+MOE_DEV float dpp_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int RB>
+MOE_DEV float rows_sum(float (&p)[RB], int lane, int &row)
+{
+    static_assert(RB == 2 || RB == 4 || RB == 8, "two, four or eight rows");
+    row = 0;
+    rows_halve<RB, RB>(p, lane, row);
+    // the lanes of a row: bits 0 .. 5 - log2(RB) of the lane index
+    float v = dpp_add<0xB1>(p[0]);              // quad_perm(1, 0, 3, 2)
+    v = dpp_add<0x4E>(v);                       // quad_perm(2, 3, 0, 1)
+    v = dpp_add<0x141>(v);                      // row_half_mirror: 8 lanes
+    if constexpr (RB <= 4) v = dpp_add<0x140>(v);           // row_mirror: 16
+    if constexpr (RB == 2) v += __shfl_xor(v, 16, 64);      // 32
+    return v;
+}
+
 // dgrad of GEMM2, for the tile of sorted rows [t.m0, t.seg_end) and columns
 // n0 .. n0+BN-1 of I (column tile t.nt of nN):
 //   dw_part[m, t.nt] = sum over the tile's columns of dA'[m, i] a[m, i]
@@ -15,10 +60,11 @@ namespace moe {
 // dA' leaves through the LDS staging tile; lane l then owns columns
 // n0 + 4l .. n0 + 4l + 3 of a row: it loads h (gate, up) and a there, applies
 // the routing weight and the SwiGLU backward, stores dh, and the wave sums
-// dA'.a over the tile's columns of the row (dw_part[m, nt]).  Each wave takes
-// RB rows of a 128-row half at a time; the loads of a batch are issued
-// together (addresses clamped to valid rows), the first batch's before the
-// half is staged, so their latency overlaps the staging.
+// dA'.a over the tile's columns of the row (dw_part[m, nt]; the RB rows of a
+// batch in one rows_sum).  Each wave takes RB rows of a 128-row half at a
+// time; the loads of a batch are issued together (addresses clamped to valid
+// rows), the first batch's before the half is staged, so their latency
+// overlaps the staging.
 // SPLIT: g, u and a are read as hi + lo pairs (h + h_lo, a + a_lo) and dh
 // leaves as one too: dh = bf16(v), dh_lo = bf16(v - bf16(v)).
 template <class C, int RB = EPI_ROWS / (C::NT / 64), bool SPLIT = false>
@@ -58,6 +104,9 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
         }
     };
     auto process = [&](int half, int r0, const Batch &bt) {
+        float part[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) part[b] = 0.f;
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
             const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
@@ -79,10 +128,9 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
                     av[q] += al[q];
                 }
             }
-            float part = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                part += dap[q] * av[q];
+                part[b] += dap[q] * av[q];
                 const float da = bt.wgt[b] * dap[q];
                 const float sg = sigmoidf_(gv[q]);
                 dg[q] = da * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
@@ -101,9 +149,14 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
                     *(uint64_t *)(dh_lo + m * 2 * I + I + col) = pack_bf4(du[0], du[1], du[2], du[3]);
                 }
             }
-            part = wave_sum(cok ? part : 0.f);
-            if (lane == 0) dw_part[m * nN + t.nt] = part;
+            if (!cok) part[b] = 0.f;
         }
+        // one lane per row writes its total (rows past the segment: none)
+        int row;
+        const float tot = rows_sum<RB>(part, lane, row);
+        const int64_t m = t.m0 + half * EPI_ROWS + r0 + row * NW;
+        if ((lane & (63 >> (31 - __builtin_clz(RB)))) == 0 && m < t.seg_end)
+            dw_part[m * nN + t.nt] = tot;
     };
 #pragma unroll
     for (int half = 0; half < C::BM / EPI_ROWS; ++half) {

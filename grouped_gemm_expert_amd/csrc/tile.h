@@ -563,29 +563,34 @@ struct MTile {
     int nt;
 };
 
-// M-grouped tile L: groups of GM m-tiles sweep all n-tiles before moving on.
+// M-grouped tile L: inside each expert, groups of GM of its m-tiles sweep
+// all n-tiles before moving on; a group never spans two experts, so the
+// tiles an XCD runs together share the expert's weight panels and their
+// token rows in its L2 (an expert with few rows is one group).
 template <int BM>
 MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offsets, int E,
                           int nN, MTile &t)
 {
     constexpr int GM = 4;
-    const int64_t total_mt = mt_off[E];
-    const int64_t total = total_mt * nN;
+    const int64_t total = (int64_t)mt_off[E] * nN;
     int64_t L = xcd_remap(b, total);
     if (L < 0) return false;
-    int64_t grp = L / ((int64_t)GM * nN);
-    int64_t first = grp * GM;
-    int64_t gm = total_mt - first < GM ? total_mt - first : GM;
-    int64_t in = L - grp * (int64_t)GM * nN;
-    int64_t mt = first + in % gm;
-    t.nt = (int)(in / gm);
-    int lo = 0, hi = E;  // largest e with mt_off[e] <= mt
+    // expert e owns tiles [mt_off[e] nN, mt_off[e + 1] nN): the largest e
+    // with mt_off[e] nN <= L has m-tiles (mte >= 1)
+    int lo = 0, hi = E;
     while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
-        if (mt_off[mid] <= mt) lo = mid; else hi = mid;
+        if ((int64_t)mt_off[mid] * nN <= L) lo = mid; else hi = mid;
     }
+    const int64_t mte = mt_off[lo + 1] - mt_off[lo];
+    const int64_t in0 = L - (int64_t)mt_off[lo] * nN;
+    const int64_t grp = in0 / ((int64_t)GM * nN);
+    const int64_t first = grp * GM;
+    const int64_t gm = mte - first < GM ? mte - first : GM;
+    const int64_t in = in0 - grp * (int64_t)GM * nN;
+    t.nt = (int)(in / gm);
     t.e = lo;
-    t.m0 = offsets[lo] + (mt - mt_off[lo]) * BM;
+    t.m0 = offsets[lo] + (first + in % gm) * BM;
     t.seg_end = offsets[lo + 1];
     return true;
 }
