@@ -5,11 +5,13 @@
 // split exactly into three bf16 parts, v = hi + mid + lo (each part the
 // round-to-nearest bf16 of what the previous parts leave), so that every
 // product of two parts is exact in fp32 and the MFMA's fp32 accumulation
-// gives the sum with fp32 rounding, as a plain fp32 GEMM would:
+// gives the sum with fp32 rounding, as a plain fp32 GEMM would.  The logits
+// decide the routing and take all three parts; the gradients feed no
+// decision and take the first two (hi + mid holds 16 of the 24 significand
+// bits: each product is within 2^-15 of its fp32 value, relative):
 //   l   = sum_p  x  . Wr_p^T                      (3 products)
-//   dWr = sum_p  dl_p^T . x                        (3 products)
-//   dx += sum_{p+q<=2} dl_p . Wr_q                 (6 products; the dropped
-//         ones are below 2^-24 of the result)
+//   dWr = sum_{p<2}  dl_p^T . x                    (2 products)
+//   dx += sum_{p+q<=1} dl_p . Wr_q                 (3 products)
 // The products run as one pipeline over a concatenated list of K stages;
 // outputs with few tiles split that list over several blocks (split-K) whose
 // partial sums a second kernel adds in a fixed order, so results are
@@ -221,7 +223,7 @@ size_t router_ws_bytes_fwd(int64_t T, int32_t E, int32_t H)
 
 size_t router_ws_bytes_bwd(int64_t T, int32_t E, int32_t H)
 {
-    const int32_t sp = dense_splits(E, H, 3 * ceil_div(T, BK));
+    const int32_t sp = dense_splits(E, H, 2 * ceil_div(T, BK));
     return al256((size_t)3 * E * H * 2) + al256((size_t)3 * T * pad64(E) * 2) +
            (sp > 1 ? al256((size_t)sp * E * H * 4) : 0);
 }
@@ -278,9 +280,9 @@ hipError_t launch_router_grads(int64_t T, int32_t E, int32_t H, const float *dl,
     d.K = E;
     d.lda = Ep;
     d.ldb = H;
-    const int pq[6][2] = {{0, 0}, {0, 1}, {1, 0}, {0, 2}, {1, 1}, {2, 0}};
-    d.nterms = 6;
-    for (int t = 0; t < 6; ++t) {
+    const int pq[3][2] = {{0, 0}, {0, 1}, {1, 0}};
+    d.nterms = 3;
+    for (int t = 0; t < 3; ++t) {
         d.A[t] = Dp[pq[t][0]];
         d.B[t] = Wp[pq[t][1]];
     }
@@ -298,13 +300,13 @@ hipError_t launch_router_grads(int64_t T, int32_t E, int32_t H, const float *dl,
     g.K = T;
     g.lda = Ep;
     g.ldb = H;
-    g.nterms = 3;
-    for (int t = 0; t < 3; ++t) {
+    g.nterms = 2;
+    for (int t = 0; t < 2; ++t) {
         g.A[t] = Dp[t];
         g.B[t] = x;
     }
     g.spt = ceil_div(T, BK);
-    g.splits = dense_splits(E, H, 3 * g.spt);
+    g.splits = dense_splits(E, H, 2 * g.spt);
     g.C = dWr;
     g.accumulate = 0;
     g.part = (float *)p;

@@ -236,14 +236,21 @@ __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *cou
     if (e < E) mt128[e] = o128;
     if (e == E - 1) mt128[E] = total;
     __syncthreads();
-    if (e < E) {
-        int32_t rank = 0;
-        for (int j = 0; j < E; ++j) {
-            int32_t cj = sc[j];
-            rank += (cj > c) || (cj == c && j < e);
+    // rank of expert er: S threads (consecutive lanes of one wave) each count
+    // the experts ahead of it among every S-th one, then add up by shuffles
+    int S = 1;
+    while (S < 64 && 2 * S * E <= 1024) S *= 2;
+    const int er = e / S, part = e % S;
+    int32_t rank = 0;
+    if (er < E) {
+        const int32_t ce = sc[er];
+        for (int j = part; j < E; j += S) {
+            const int32_t cj = sc[j];
+            rank += (cj > ce) || (cj == ce && j < er);
         }
-        order[rank] = e;
     }
+    for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off, 64);
+    if (er < E && part == 0) order[rank] = er;
     int32_t nact;
     block_excl_scan_1024((e < E && c > 0) ? 1 : 0, tmp, nact);
     if (e == 0) order[E] = nact;

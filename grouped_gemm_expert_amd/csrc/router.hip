@@ -44,7 +44,7 @@ hipError_t launch_fill_f32(float *p, int64_t n, float v, hipStream_t s)
 // serialise them on a few addresses); both go out as per-block partials.
 // Expert e lives in lane e % 64, register slot e / 64.
 constexpr int RT_WAVES = 4;
-constexpr int RT_TOK_PER_WAVE = 2;  // a token is a serial chain: keep many waves
+constexpr int RT_TOK_PER_WAVE = 1;  // a token is a serial chain: keep many waves
 constexpr int RT_TOK_PER_BLOCK = RT_WAVES * RT_TOK_PER_WAVE;
 
 int64_t router_blocks(int64_t T) { return ceil_div(T, RT_TOK_PER_BLOCK); }

@@ -330,11 +330,12 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
  *   saved      the forward's saved tensors
  *   dy [T,H] bf16, d_aux [1] fp32 device scalar or NULL (= 0)
  *   dx [T,H] fp32 out: expert path plus router path (dlogits . Wr) when
- *              Wr != NULL (dlogits and Wr split into bf16 parts as for the
- *              logits; the part-products below 2^-24 of the result are
- *              dropped)
+ *              Wr != NULL (dlogits and Wr each taken as the sum of their
+ *              first two bf16 parts, hi + mid, on bf16 MFMA: every product
+ *              within 2^-15 of its fp32 value, relative)
  *   dlogits [T,E] fp32 out
- *   dWr [E,H] fp32 out, or NULL (skipped; also skipped when Wr == NULL)
+ *   dWr [E,H] fp32 out, or NULL (skipped; also skipped when Wr == NULL);
+ *              dlogits as hi + mid parts, as for dx
  *   dW1 [E,2I,H], dW2 [E,H,I] fp32 or bf16 (dw_dtype), overwritten or
  *              accumulated (dw_accumulate) as in moe_grouped_gemm
  * The selection itself and the bias carry no gradient; counts are constants
