@@ -28,10 +28,28 @@ def _logits_for(w, seed=0):
     return dc, l64.astype(np.float32)
 
 
-@pytest.mark.parametrize("name", ROUTER_CASES)
+# Router shapes outside the workloads: the selection runs on 16 lanes a token
+# up to E = 256, G = 16 and k = 16 and on a whole wave a token beyond; these
+# cover the wide kernel and the narrow one at its limits.
+WIDE_ROUTER = {
+    "wide_E384": dict(base="mid_sigmoid", E=384, n_groups=24, topk_groups=6, k=18),
+    "wide_k20": dict(base="mid_sigmoid", E=64, n_groups=4, topk_groups=3, k=20),
+    "wide_softmax_E512": dict(base="mid_softmax", E=512, n_groups=1, topk_groups=1, k=8),
+    "narrow_limits": dict(base="mid_sigmoid", E=256, n_groups=16, topk_groups=5, k=16),
+}
+
+
+def _router_workload(name):
+    if name in WIDE_ROUTER:
+        kw = dict(WIDE_ROUTER[name])
+        return dataclasses.replace(inputs.WORKLOADS[kw.pop("base")], name=name, **kw)
+    return inputs.WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", ROUTER_CASES + sorted(WIDE_ROUTER))
 def test_router_bit_exact_given_logits(name):
     from grouped_gemm_expert_amd import ops
-    w = inputs.WORKLOADS[name]
+    w = _router_workload(name)
     hz.say(f"router {inputs.describe(w)}")
     dc, l32 = _logits_for(w)
     bias = None if dc["bias"] is None else dc["bias"].numpy()
