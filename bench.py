@@ -55,6 +55,8 @@ GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
 UNIFORM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_uniform.md")
 BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy_deepseek_v3.md")
+UNIFORM_BUSY_FILE = os.path.join(ROOT, "profiles", "mfma_busy_uniform.md")
+TRACE_FILE = os.path.join(ROOT, "profiles", "moe_step_deepseek_v3_kernel_trace.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_gemm_expert_amd", "csrc", f)
                   for f in ("gemm.hip", "tile.h", "common.h", "swiglu_epi.h", "bwd_epi.h", "mxfmt.h",
                             "mx.hip")]
@@ -358,15 +360,15 @@ def wgrad_is_up(name):
     return rest.lstrip().startswith("true")
 
 
-def pmc_busy_summary(busy_dir, out_path, cmds):
+def pmc_busy_summary(busy_dir, out_path, cmds, workload="deepseek_v3"):
     """MFMA utilisation and clock of the grouped GEMMs from one rocprofv3 --pmc
     run of SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) and
     GRBM_GUI_ACTIVE (summed over the 8 XCDs): busy fraction =
     MFMA_BUSY / (GUI_ACTIVE / 8 * 1024), clock = GUI_ACTIVE / 8 / duration."""
     busy = counter_rows(busy_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
     gui = {i: (n, v, us) for i, n, v, us in counter_rows(busy_dir, "GRBM_GUI_ACTIVE")}
-    L = ["# MFMA utilisation of the grouped GEMMs: DeepSeek-V3-style MoE layer (T=8192 H=7168 "
-         "I=2048 E=256 G=8 kg=4 k=8), MI355X", "", "Commands (from the repository root on the GPU box):",
+    L = [f"# MFMA utilisation of the grouped GEMMs: {TRAFFIC_TITLES[workload]}, MI355X", "",
+         "Commands (from the repository root on the GPU box):",
          "", "```"] + cmds + ["```", "",
          "Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
          "clock = GRBM_GUI_ACTIVE / 8 / launch duration. The MFMA-bound rate at that clock is "
@@ -403,6 +405,46 @@ TRAFFIC_TITLES = {
     "uniform": "DeepSeek-V3 shapes under `uniform` force load balancing (T=8192 H=7168 I=2048 "
                "E=256 k=8, seeded N(0, 1) logits: every expert gets rows)",
 }
+
+
+def trace_summary(stats_csv, bench_log, out_path, cmds):
+    """The per-kernel table of a rocprofv3 --kernel-trace --stats run of the
+    bench, with the stage times of the bench line that run printed."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    line = [l for l in open(bench_log) if l.startswith('{"metric"')][-1]
+    bench = json.loads(line)
+    L = [f"# Kernel trace: {TRAFFIC_TITLES['deepseek_v3']}, MI355X: bf16 fwd+bwd steps, then the "
+         "MXFP8 weight-cache fill and MXFP8 fwd+bwd steps", "",
+         "Commands (from the repository root on the GPU box; the CSV lands in gpurun_out/prof):",
+         "", "```"] + cmds + ["```", "", "| kernel | calls | avg us | total ms | % |",
+                              "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        L.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                 f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
+    L += ["", f"bench.py stage times (HIP events on the library stream, the same run): "
+              f"{bench['ms_per_step']} ms per bf16 step", ""]
+    for st, v in bench["stages"].items():
+        extra = (f", {v['TFLOP/s']} TFLOP/s" if "TFLOP/s" in v
+                 else (f", {v['GB/s']} GB/s" if "GB/s" in v else ""))
+        L.append(f"- {st}: {v['ms']} ms{extra}")
+    m = bench.get("mxfp8")
+    if m:
+        L += ["", f"MXFP8 step (moe_forward_mx + moe_backward_mx) stage times, same run: "
+                  f"{m['ms_per_step']} ms per step (bf16 step {m['bf16_ms_per_step']} ms); MX grouped "
+                  f"GEMMs {m['grouped_gemm']['TFLOP/s']} TFLOP/s ({m['grouped_gemm']['pct_of_fp8_peak']}% "
+                  "of the fp8 peak)", ""]
+        for st, v in m["stages"].items():
+            extra = f", {v['TFLOP/s']} TFLOP/s" if "TFLOP/s" in v else ""
+            L.append(f"- {st}: {v['ms']} ms{extra}")
+        L.append(f"- weight-cache fill (w1, w2 and their transposes quantised): "
+                 f"{m['weight_cache_fill_ms']} ms")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L[:24]))
 
 
 def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds,
@@ -576,7 +618,11 @@ def main():
                          "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
     ap.add_argument("--pmc-commands", default="", help="commands recorded with --pmc-summary (;-separated)")
     ap.add_argument("--pmc-workload", default="deepseek_v3", choices=sorted(TRAFFIC_TITLES),
-                    help="the workload the --pmc-summary runs measured (picks the record file)")
+                    help="the workload the --pmc-summary / --pmc-busy-summary runs measured "
+                         "(picks the record file)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="write the kernel-trace profile from a rocprofv3 --stats CSV and the "
+                         "bench line of the same run")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -587,8 +633,14 @@ def main():
                     [c.strip() for c in args.pmc_commands.split(";") if c.strip()], args.pmc_workload)
         return
     if args.pmc_busy_summary:
-        pmc_busy_summary(args.pmc_busy_summary, BUSY_FILE,
-                         [c.strip() for c in args.pmc_commands.split(";") if c.strip()])
+        out_path = UNIFORM_BUSY_FILE if args.pmc_workload == "uniform" else BUSY_FILE
+        pmc_busy_summary(args.pmc_busy_summary, out_path,
+                         [c.strip() for c in args.pmc_commands.split(";") if c.strip()],
+                         args.pmc_workload)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary, TRACE_FILE,
+                      [c.strip() for c in args.pmc_commands.split(";") if c.strip()])
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
