@@ -174,7 +174,12 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     // B(n = i, k = hh) = w2[e, hh, i]: k-row hh starts at w2e + hh*I
     lb.init(w2e, I, n0, I, wave0, lane0);
     Acc<C> acc;
-    mainloop<C, false, true, false>(lds, H, la, lb, acc);
+    // a segment's last m-tile may be part-filled: the partial main loop skips
+    // the A copies and MFMAs of its empty rows (3-4% on the dgrad GEMMs
+    // under uniform routing; it does not pay in GEMM1 and GEMM2)
+    const int64_t rows = t.seg_end - t.m0;
+    if (rows >= C::BM) mainloop<C, false, true, false>(lds, H, la, lb, acc);
+    else mainloop<C, false, true, false, true>(lds, H, la, lb, acc, (int)rows);
     // the split form loads twice the rows' data: half the rows a batch
     dgrad2_epilogue<C, SPLIT ? 2 : 8, SPLIT>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh,
                                              g.dw_part, g.h_lo, g.a_lo, g.dh_lo);
@@ -208,7 +213,9 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     // B(n = hh, k = nn) = w1[e, nn, hh]: k-row nn starts at w1e + nn*H
     lb.init(w1e, H, n0, H, wave0, lane0);
     Acc<C> acc;
-    mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
+    const int64_t rows = t.seg_end - t.m0;  // part-filled last m-tile: as in k_down_dgrad
+    if (rows >= C::BM) mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
+    else mainloop<C, false, true, false, true>(lds, 2 * I, la, lb, acc, (int)rows);
     if (g.dxp_bf16) store_tile_f32<C>(acc, lds, g.dxp_bf16, t.m0, t.seg_end, n0, H);
     else store_tile_f32<C>(acc, lds, g.dxp, t.m0, t.seg_end, n0, H);
 }

@@ -222,14 +222,17 @@ struct Frags {
     bf16x8_t a[C::FM], b[C::FN];
 };
 
-template <class C, bool A_NMAJ, bool B_NMAJ>
+// PARTIAL: only the wave's first na row fragments hold rows of the tile; the
+// others are neither read nor multiplied (na is wave-uniform).
+template <class C, bool A_NMAJ, bool B_NMAJ, bool PARTIAL = false>
 MOE_DEV void read_frags(const lds_t *As, const lds_t *Bs, int kk, Frags<C> &f, int wm, int wn,
-                        int lane)
+                        int lane, int na = C::FM)
 {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
-        f.a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
-                        : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
+        if (!PARTIAL || i < na)
+            f.a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
+                            : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
         f.b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
@@ -257,14 +260,15 @@ MOE_DEV void wait_copies_le()
 
 // Read number r of a k-step's fragments, in the order a0, b0 .. b(FN-1),
 // a1 .. a(FM-1): the order in which the (i, j)-ordered MFMAs first need them.
-template <class C, bool A_NMAJ, bool B_NMAJ>
+template <class C, bool A_NMAJ, bool B_NMAJ, bool PARTIAL>
 MOE_DEV void read_one(int r, const lds_t *As, const lds_t *Bs, int kk, Frags<C> &f, int wm, int wn,
-                      int lane)
+                      int lane, int na)
 {
     if (r == 0 || r > C::FN) {
         const int i = r == 0 ? 0 : r - C::FN;
-        f.a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
-                        : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
+        if (!PARTIAL || i < na)
+            f.a[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk, lane)
+                            : frag_kmaj(As, wm * C::WM + i * 32, kk, lane);
     } else {
         const int j = r - 1;
         f.b[j] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + j * 32, kk, lane)
@@ -276,22 +280,24 @@ MOE_DEV void read_one(int r, const lds_t *As, const lds_t *Bs, int kk, Frags<C> 
 // the wave issues fragment read n of the next k-step into `nxt` (n < FM+FN)
 // and the copies i (of NC) with i*NMF/NC == n, so LDS reads and
 // global->LDS copies are spread evenly over the MFMAs instead of arriving in
-// bursts; sched_barrier pins that order.
-template <class C, bool A_NMAJ, bool B_NMAJ, int NC, class Copy>
+// bursts; sched_barrier pins that order.  PARTIAL: row fragments i >= na
+// are skipped, reads and MFMAs alike.
+template <class C, bool A_NMAJ, bool B_NMAJ, bool PARTIAL, int NC, class Copy>
 MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const lds_t *Bs, int kk_next,
-                   Copy &&copy, Acc<C> &acc, int wm, int wn, int lane)
+                   Copy &&copy, Acc<C> &acc, int wm, int wn, int lane, int na)
 {
     constexpr int NMF = C::FM * C::FN, NR = C::FM + C::FN;
     static_assert(NR <= NMF, "one read per MFMA at most");
 #pragma unroll
     for (int n = 0; n < NMF; ++n) {
-        if (n < NR) read_one<C, A_NMAJ, B_NMAJ>(n, As, Bs, kk_next, nxt, wm, wn, lane);
+        if (n < NR) read_one<C, A_NMAJ, B_NMAJ, PARTIAL>(n, As, Bs, kk_next, nxt, wm, wn, lane, na);
 #pragma unroll
         for (int i = 0; i < NC; ++i)
             if (i * NMF / NC == n) copy(i);
         __builtin_amdgcn_sched_barrier(0);
         const int i = n / C::FN, j = n % C::FN;
-        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc.v[i][j], 0, 0, 0);
+        if (!PARTIAL || i < na)
+            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.b[j], cur.a[i], acc.v[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -326,9 +332,12 @@ MOE_DEV void stage_run(F &&f, int v, int v1, std::integer_sequence<int, I...>)
 // stage to land); with two B buffers they all go into step 3 of stage v.
 // copy_a(q, v, As) / copy_b(q, v, Bs) issue copy q (of NCA / NCB per wave)
 // of stage v's A / B tile; tail(v, As, Bs) runs after stage v landed.
-template <class C, bool A_NMAJ, bool B_NMAJ, int NCA, int NCB, class CopyA, class CopyB, class Tail>
+// PARTIAL / na: the wave multiplies only its first na row fragments
+// (read_frags); its copies are the callers' business.
+template <class C, bool A_NMAJ, bool B_NMAJ, int NCA, int NCB, bool PARTIAL = false, class CopyA,
+          class CopyB, class Tail>
 MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b, Tail &&tail,
-                      Acc<C> &acc)
+                      Acc<C> &acc, int na = C::FM)
 {
     constexpr int NB = C::NBB;
     constexpr bool SPREAD = NB == 3;
@@ -361,7 +370,7 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
     tail(v0, As[0], Bs[0]);
     __syncthreads();
     Frags<C> f0, f1;
-    read_frags<C, A_NMAJ, B_NMAJ>(As[0], Bs[0], 0, f0, wm, wn, lane);
+    read_frags<C, A_NMAJ, B_NMAJ, PARTIAL>(As[0], Bs[0], 0, f0, wm, wn, lane, na);
     // one stage; the buffers it uses are compile-time constants, so LDS
     // addresses fold into instruction offsets
     auto stage = [&](auto tag, int v) {
@@ -374,13 +383,13 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
         };
         auto none = [](int) {};
         if constexpr (SPREAD) {
-            kstep<C, A_NMAJ, B_NMAJ, SB>(f0, f1, As[a], Bs[b], 1, slot(1), acc, wm, wn, lane);
-            kstep<C, A_NMAJ, B_NMAJ, SB>(f1, f0, As[a], Bs[b], 2, slot(2), acc, wm, wn, lane);
-            kstep<C, A_NMAJ, B_NMAJ, SB>(f0, f1, As[a], Bs[b], 3, slot(3), acc, wm, wn, lane);
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, SB>(f0, f1, As[a], Bs[b], 1, slot(1), acc, wm, wn, lane, na);
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, SB>(f1, f0, As[a], Bs[b], 2, slot(2), acc, wm, wn, lane, na);
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, SB>(f0, f1, As[a], Bs[b], 3, slot(3), acc, wm, wn, lane, na);
         } else {
-            kstep<C, A_NMAJ, B_NMAJ, 0>(f0, f1, As[a], Bs[b], 1, none, acc, wm, wn, lane);
-            kstep<C, A_NMAJ, B_NMAJ, 0>(f1, f0, As[a], Bs[b], 2, none, acc, wm, wn, lane);
-            kstep<C, A_NMAJ, B_NMAJ, 0>(f0, f1, As[a], Bs[b], 3, none, acc, wm, wn, lane);
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, 0>(f0, f1, As[a], Bs[b], 1, none, acc, wm, wn, lane, na);
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, 0>(f1, f0, As[a], Bs[b], 2, none, acc, wm, wn, lane, na);
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, 0>(f0, f1, As[a], Bs[b], 3, none, acc, wm, wn, lane, na);
         }
         // every stage issues the same copies, and stage v+1's were all issued
         // before the last A copies; only the B copies of stage v+2 (three B
@@ -393,13 +402,13 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
         // branch-free: the reads fetch stale fragments that are never used,
         // and the last stage is copied again into buffers nothing reads.
         const int va = clampv(v + 2), vb = clampv(v + NB);
-        kstep<C, A_NMAJ, B_NMAJ, NCA + SB>(
+        kstep<C, A_NMAJ, B_NMAJ, PARTIAL, NCA + SB>(
             f1, f0, As[an], Bs[bn], 0,
             [&](int q) {
                 if (q < NCA) copy_a(q, va, As[a]);
                 else copy_b(q - NCA, vb, Bs[b]);
             },
-            acc, wm, wn, lane);
+            acc, wm, wn, lane, na);
     };
     constexpr int P = NB == 3 ? 6 : 2;  // buffer pattern period
     int v = v0;
@@ -409,26 +418,54 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
     __syncthreads();  // callers may reuse the LDS
 }
 
-// C = A . B^T over K with two loaders of fixed base: stages of 64 k, the last
-// one partial when KTAIL (its rows past K are zeroed).
-template <class C, bool A_NMAJ, bool B_NMAJ, bool KTAIL, class LA, class LB>
-MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> &acc)
+// The row fragments of this wave that start below `rows` (tile rows 0 ..
+// rows-1 hold data): 0 .. FM.  Wave-uniform.
+template <class C>
+MOE_DEV int partial_row_frags(int rows)
 {
+    const int rel = rows - (wave_uniform_id() / C::WAVES_N) * C::WM;
+    return rel <= 0 ? 0 : (rel >= C::FM * 32 ? C::FM : (rel + 31) / 32);
+}
+
+// C = A . B^T over K with two loaders of fixed base: stages of 64 k, the last
+// one partial when KTAIL (its rows past K are zeroed).  PARTIAL: the tile
+// holds only `rows` < BM rows of A (a segment's last m-tile; A K-major).
+// Wave w copies A rows [w*RPW, (w+1)*RPW), RPW = BM/NW (KLoad): a wave whose
+// rows all lie past `rows` copies no A at all (its own pipeline
+// instantiation with no A copies, so that every wait counts exactly the
+// copies issued), and each wave multiplies only the row fragments that start
+// below `rows`: fragment i of wave tile row wm covers rows wm*WM + 32 i ..
+// + 31, copied by wave (wm*WM + 32 i) / RPW, which starts below `rows` too.
+// The rows skipped feed no stored output.
+template <class C, bool A_NMAJ, bool B_NMAJ, bool KTAIL, bool PARTIAL = false, class LA, class LB>
+MOE_DEV void mainloop(lds_t *lds, int64_t K, const LA &la, const LB &lb, Acc<C> &acc,
+                      int rows = C::BM)
+{
+    static_assert(!PARTIAL || !A_NMAJ, "partial tiles skip the copies of K-major A rows");
+    constexpr int RPW = C::BM / (C::NT / 64);
+    static_assert(RPW % 8 == 0, "a wave copies whole 1 KB blocks of A rows");
     auto kvalid = [&](int s) -> int {
         const int64_t rem = K - (int64_t)s * BK;
         return KTAIL ? (rem < BK ? (int)rem : BK) : BK;
     };
-    pipeline<C, A_NMAJ, B_NMAJ, LA::NI, LB::NI>(
-        lds, 0, (int)ceil_div(K, BK),
-        [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * BK, kvalid(s), la.base); },
-        [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * BK, kvalid(s), lb.base); },
-        [&](int s, lds_t *As, lds_t *Bs) {
-            if (KTAIL && kvalid(s) < BK) {
-                la.zero_tail(As, kvalid(s));
-                lb.zero_tail(Bs, kvalid(s));
-            }
-        },
-        acc);
+    const int nst = (int)ceil_div(K, BK);
+    auto cpa = [&](int q, int s, lds_t *As) { la.issue_one(q, As, (int64_t)s * BK, kvalid(s), la.base); };
+    auto cpb = [&](int q, int s, lds_t *Bs) { lb.issue_one(q, Bs, (int64_t)s * BK, kvalid(s), lb.base); };
+    auto tail = [&](int s, lds_t *As, lds_t *Bs) {
+        if (KTAIL && kvalid(s) < BK) {
+            la.zero_tail(As, kvalid(s));
+            lb.zero_tail(Bs, kvalid(s));
+        }
+    };
+    if constexpr (!PARTIAL) {
+        pipeline<C, A_NMAJ, B_NMAJ, LA::NI, LB::NI>(lds, 0, nst, cpa, cpb, tail, acc);
+    } else {
+        const int na = partial_row_frags<C>(rows);
+        if (wave_uniform_id() * RPW < rows)
+            pipeline<C, A_NMAJ, B_NMAJ, LA::NI, LB::NI, true>(lds, 0, nst, cpa, cpb, tail, acc, na);
+        else
+            pipeline<C, A_NMAJ, B_NMAJ, 0, LB::NI, true>(lds, 0, nst, cpa, cpb, tail, acc, na);
+    }
 }
 
 // The MFMA takes the B fragment as its first operand, so each 32x32 block
