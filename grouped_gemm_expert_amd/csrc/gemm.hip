@@ -181,7 +181,7 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     if (rows >= C::BM) mainloop<C, false, true, false>(lds, H, la, lb, acc);
     else mainloop<C, false, true, false, true>(lds, H, la, lb, acc, (int)rows);
     // the split form loads twice the rows' data: half the rows a batch
-    dgrad2_epilogue<C, SPLIT ? 2 : 8, SPLIT>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh,
+    dgrad2_epilogue<C, SPLIT ? 2 : 4, SPLIT>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh,
                                              g.dw_part, g.h_lo, g.a_lo, g.dh_lo);
 }
 

@@ -535,16 +535,59 @@ MOE_DEV f32x4_t epi_read_f32(const lds_t *lds, int r, int lane)
 }
 
 // out[m][n0 + c] = tile[m - m0][c] for rows m0 <= m < mlim (row stride
-// ncols, ncols a multiple of 4), fp32 or (OutT = uint16_t) bf16 with
-// nearest-even rounding.  Starts and ends on a barrier-free LDS.  A wave
+// ncols, ncols a multiple of 4; of 8 for bf16), fp32 or (OutT = uint16_t)
+// bf16 with nearest-even rounding.  Starts and ends on a barrier-free LDS.  A wave
 // reads 8 of its rows from LDS at once, then stores them, so the LDS latency
 // is paid once per 8 rows.
 MOE_DEV void store4(float *p, f32x4_t v) { *(f32x4_t *)p = v; }
 MOE_DEV void store4(uint16_t *p, f32x4_t v) { *(uint64_t *)p = pack_bf4(v[0], v[1], v[2], v[3]); }
+// bf16 out (ncols a multiple of 8): lane l takes columns 8 (l % 32) ..
+// + 7 of one of two rows (l / 32), so each store is 16 bytes and a wave
+// covers two rows per instruction.
+template <class C>
+MOE_DEV void store_tile_bf16(const Acc<C> &acc, lds_t *lds, uint16_t *out, int64_t m0,
+                             int64_t mlim, int64_t n0, int64_t ncols)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    const int c = lane & 31;
+    const int64_t col = n0 + 8 * c;
+    constexpr int NW = C::NT / 64, RB = 8;
+    static_assert(EPI_ROWS % (2 * NW * RB) == 0, "row batches tile the half");
+#pragma unroll
+    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
+        if (m0 + half * EPI_ROWS >= mlim) break;
+        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
+        __syncthreads();
+        if (col < ncols)
+            for (int r0 = 2 * wave + (lane >> 5); r0 < EPI_ROWS; r0 += 2 * NW * RB) {
+                f32x4_t lo[RB], hi[RB];
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    lo[b] = *(const lds_f32x4 *)(lds + epi_off(r0 + b * 2 * NW, 2 * c));
+                    hi[b] = *(const lds_f32x4 *)(lds + epi_off(r0 + b * 2 * NW, 2 * c + 1));
+                }
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    const int64_t m = m0 + half * EPI_ROWS + r0 + b * 2 * NW;
+                    if (m >= mlim) break;
+                    const u32x4_t v = {pack_bf2(lo[b][0], lo[b][1]), pack_bf2(lo[b][2], lo[b][3]),
+                                       pack_bf2(hi[b][0], hi[b][1]), pack_bf2(hi[b][2], hi[b][3])};
+                    *(u32x4_t *)(out + m * ncols + col) = v;
+                }
+            }
+        __syncthreads();
+    }
+}
+
 template <class C, class OutT = float>
 MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, OutT *out, int64_t m0, int64_t mlim,
                             int64_t n0, int64_t ncols)
 {
+    if constexpr (sizeof(OutT) == 2) {
+        store_tile_bf16<C>(acc, lds, out, m0, mlim, n0, ncols);
+        return;
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int64_t col = n0 + 4 * lane;
