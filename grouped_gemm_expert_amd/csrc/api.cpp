@@ -644,9 +644,10 @@ static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const ui
     a.o = w.o;
     GemmArgs g = gemm_args(c, a, w.sched);
     set_split(g, c, saved, nullptr);
-    // with bf16 intermediates the expert outputs between GEMM2 and the
-    // combine are bf16 too (the combine sums them in fp32); split keeps fp32
-    const bool o16 = !w2_mx && c.precision == MOE_PRECISION_BF16;
+    // with bf16 intermediates (and on the MXFP8 path, which has no other
+    // form) the expert outputs between GEMM2 and the combine are bf16 too
+    // (the combine sums them in fp32); split keeps fp32
+    const bool o16 = c.precision == MOE_PRECISION_BF16;
     if (o16) g.o_bf16 = (uint16_t *)w.o;
     if (!w2_mx) {
         MOE_TRY(run_gemm(MOE_GEMM_DOWN, g, stream));

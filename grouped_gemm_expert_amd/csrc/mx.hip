@@ -596,7 +596,8 @@ __global__ __launch_bounds__(C::NT) void k_rows_mx(GemmArgs g)
     }
     Acc<C> acc;
     mx_mainloop<C>(lds, (int)(Kp / MX_GROUP), la, lb, sp, wave0, acc);
-    if (!DN && g.dxp_bf16) store_tile_f32<C>(acc, lds, g.dxp_bf16, t.m0, t.seg_end, n0, N);
+    if (DN && g.o_bf16) store_tile_f32<C>(acc, lds, g.o_bf16, t.m0, t.seg_end, n0, N);
+    else if (!DN && g.dxp_bf16) store_tile_f32<C>(acc, lds, g.dxp_bf16, t.m0, t.seg_end, n0, N);
     else store_tile_f32<C>(acc, lds, out, t.m0, t.seg_end, n0, N);
 }
 
