@@ -38,6 +38,10 @@ MOE_DEV float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z
 
 // Ranking used everywhere in the router: larger value first, equal values
 // -> lower index first.  idx < 0 marks an empty candidate that never wins.
+// The router forms its selection scores through sel_key, so that NaN (a NaN
+// input) ranks as -inf and the order stays total: every lane of an arg-max
+// then agrees on the winner, and the top-k yields k valid experts.
+MOE_DEV float sel_key(float v) { return v != v ? -INFINITY : v; }
 MOE_DEV bool ranks_before(float va, int ia, float vb, int ib)
 {
     if (ib < 0) return ia >= 0;

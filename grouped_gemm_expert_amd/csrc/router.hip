@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
                 sc[q] = s;
                 S[q] = s + ((p.bias && ok[q]) ? p.bias[e] : 0.f);
             }
+            S[q] = sel_key(S[q]);  // a NaN score ranks as -inf
             if (p.sel && ok[q]) p.sel[t * E + e] = S[q];
         }
         // softmax probabilities (fp32) of all experts
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void k_router_select(RouterArgs p)
                         b2 = v; i2 = e;
                     }
                 }
-                gsv = (i2 >= 0) ? b1 + b2 : b1;
+                gsv = sel_key((i2 >= 0) ? b1 + b2 : b1);  // inf - inf ranks as -inf
                 gid = lane;
             }
             uint64_t kept = 0;
@@ -279,6 +280,7 @@ __global__ __launch_bounds__(256) void k_router_select16(RouterArgs p)
             sc[q] = sg;
             S[q] = sg + ((p.bias && ok[q]) ? p.bias[e] : 0.f);
         }
+        S[q] = sel_key(S[q]);  // a NaN score ranks as -inf
         if (p.sel && ok[q] && tok) p.sel[t * E + e] = S[q];
     }
     if (p.score == MOE_SOFTMAX) {
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(256) void k_router_select16(RouterArgs p)
                     b2 = v; i2 = e;
                 }
             }
-            gsv = (i2 >= 0) ? b1 + b2 : b1;
+            gsv = sel_key((i2 >= 0) ? b1 + b2 : b1);  // inf - inf ranks as -inf
             gid = j;
         }
         uint32_t kept = 0;

@@ -190,8 +190,11 @@ moe_status moe_workspace_size(const moe_config *cfg, size_t *fwd_bytes, size_t *
  *              bf16 split of Wr (x is bf16), so every product is exact in
  *              fp32 and the sum carries fp32 accumulation error only.
  *   sel_scores [T,E] fp32 selection scores, or NULL: S = logits (softmax) or
- *              fp32(sigmoid(logits)) + bias (sigmoid).  The top-k is decided
- *              on exactly these fp32 values.
+ *              fp32(sigmoid(logits)) + bias (sigmoid), with a NaN score taken
+ *              as -inf (it ranks below every number; equal scores go to the
+ *              lower expert index).  The top-k is decided on exactly these
+ *              fp32 values, so every slot gets a valid expert whatever the
+ *              input.
  *   topk_idx   [T,k] int32 out;  topk_w [T,k] fp32 out
  *   counts     [E] int32 out (rows routed to each expert)
  *   aux        [1] fp32 out (load-balancing aux loss)

@@ -93,9 +93,16 @@ void oracle_selection_scores(int64_t T, int32_t E, int32_t score,
         }
 }
 
-/* a ranks before b: larger value first, equal values -> lower index first. */
+/* The ranking key of a selection score: the score itself, with NaN taken as
+   -inf (reading: the pages rank scores only; a NaN score ranks below every
+   number, ties by lower index as for any equal scores). */
+static float sel_key(float v) { return isnan(v) ? -INFINITY : v; }
+
+/* a ranks before b: larger key first, equal keys -> lower index first. */
 static int ranks_before(float va, int32_t ia, float vb, int32_t ib)
 {
+    va = sel_key(va);
+    vb = sel_key(vb);
     return va > vb || (va == vb && ia < ib);
 }
 
@@ -131,7 +138,8 @@ void oracle_topk(int64_t T, int32_t E, int32_t k, int32_t G, int32_t kg,
                         if (e != best &&
                             (second < 0 || ranks_before(s[e], e, s[second], second)))
                             second = e;
-                    gs[g] = (second >= 0) ? s[best] + s[second] : s[best];
+                    gs[g] = sel_key((second >= 0) ? sel_key(s[best]) + sel_key(s[second])
+                                                  : sel_key(s[best]));
                     gtaken[g] = 0;
                 }
                 for (int32_t e = 0; e < E; ++e) eligible[e] = 0;

@@ -101,6 +101,50 @@ def test_router_bit_exact_given_logits(name):
            f"empty={(counts_ref == 0).sum()} aux={aux_ref:.6g}")
 
 
+@pytest.mark.parametrize("name", ["mid_sigmoid", "mid_softmax", "mid_skewed", "wide_E384"])
+def test_router_nan_scores_give_valid_experts(name):
+    """Regression: NaN logits (from a NaN input) made the arg-max lanes
+    disagree, which could leave a slot without an expert.  A NaN selection
+    score now ranks as -inf on both sides: every slot gets a valid, distinct
+    expert, the oracle's top-k on the exported scores gives the same experts,
+    and a NaN logit exports as -inf.  Only the router runs here; its output
+    is checked on the host before anything would use it."""
+    from grouped_gemm_expert_amd import ops
+    w = _router_workload(name)
+    hz.say(f"router with NaN logits {inputs.describe(w)}")
+    dc, l32 = _logits_for(w)
+    l32 = l32.copy()
+    rng = np.random.default_rng(3)
+    l32[rng.random(l32.shape) < 0.1] = np.nan
+    l32[0, :] = np.nan                 # a token with no number at all
+    l32[1, : w.E - 1] = np.nan         # one finite expert
+    bias = None if dc["bias"] is None else dc["bias"].numpy()
+    cfg = ops.config_from_workload(w)
+    dev = "cuda"
+    logits = torch.from_numpy(l32).to(dev)
+    bias_d = None if dc["bias"] is None else dc["bias"].to(dev)
+    sel = torch.empty_like(logits)
+    idx = torch.full((w.T, w.k), -7, dtype=torch.int32, device=dev)
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+    counts = torch.empty((w.E,), dtype=torch.int32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    ops.moe_router(cfg, None, None, bias_d, logits, sel, idx, wts, counts, aux,
+                   ops.workspace(cfg, "fwd", dev))
+    torch.cuda.synchronize()
+    idx_g = idx.cpu().numpy()
+    assert ((idx_g >= 0) & (idx_g < w.E)).all()
+    assert all(len(set(r.tolist())) == w.k for r in idx_g)
+    sel_g = sel.cpu().numpy()
+    S_ref = oracle.selection_scores(l32, hz.SCORE[w.score], bias)
+    nan_ref = np.isnan(S_ref)
+    assert np.array_equal(np.isneginf(sel_g), nan_ref | np.isneginf(S_ref))
+    fin = ~nan_ref
+    ulp = np.spacing(np.abs(S_ref[fin]).astype(np.float32)).astype(np.float64)
+    assert (np.abs(sel_g[fin].astype(np.float64) - S_ref[fin].astype(np.float64)) <= 4 * ulp).all()
+    assert np.array_equal(idx_g, oracle.topk(sel_g, w.k, w.n_groups, w.topk_groups))
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(idx_g.ravel(), minlength=w.E))
+
+
 @pytest.mark.parametrize("name", ["tiny", "mid_softmax", "mid_sigmoid", "fine_grained"])
 def test_router_projection_and_routing_with_router_weight(name):
     """The GPU computes its own fp32 logits; they must sit within the fp32

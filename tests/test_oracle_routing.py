@@ -73,6 +73,30 @@ def test_topk_signed_zero_is_a_tie(oracle_lib):
     assert list(oracle_lib.topk(S, 2)[0]) == [0, 1]
 
 
+def test_topk_nan_scores_rank_below_every_number(oracle_lib):
+    """Reading: a NaN selection score ranks as -inf (below every number; equal
+    keys by lower index), so the order stays total and k valid experts come
+    out.  Hand example, then subset enumeration with NaN taken as -inf, a
+    whole NaN group, and an all-NaN row."""
+    import oracle
+    nan = np.float32("nan")
+    S = np.array([[nan, 0.5, nan, 0.2]], np.float32)
+    assert oracle.topk(S, 3, 1, 1).tolist() == [[1, 3, 0]]
+    assert oracle.topk(np.full((1, 4), nan, np.float32), 2, 1, 1).tolist() == [[0, 1]]
+    # group 1 (experts 2, 3) all NaN: its score is -inf and it is not kept
+    S = np.array([[0.1, 0.2, nan, nan, 0.3, 0.05, 0.4, 0.0]], np.float32)
+    assert oracle.topk(S, 3, 4, 2).tolist() == [[6, 4, 5]]   # kept: groups 3 and 2
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        E, G = 8, int(rng.choice([1, 2, 4]))
+        kg = int(rng.integers(1, G + 1))
+        k = int(rng.integers(1, kg * (E // G) + 1))
+        S = rng.standard_normal((1, E)).astype(np.float32)
+        S[rng.random((1, E)) < 0.3] = nan
+        keyed = np.where(np.isnan(S), -np.inf, S).astype(np.float32)
+        assert oracle.topk(S, k, G, kg)[0].tolist() == _brute_topk(keyed[0], k, G, kg)
+
+
 def test_topk_group_limit_excludes_higher_experts(oracle_lib):
     # group 1 holds the single best expert but a weak second; groups 0 and 2 win
     E, G, kg, k = 6, 3, 2, 2
