@@ -541,43 +541,58 @@ MOE_DEV f32x4_t epi_read_f32(const lds_t *lds, int r, int lane)
 // is paid once per 8 rows.
 MOE_DEV void store4(float *p, f32x4_t v) { *(f32x4_t *)p = v; }
 MOE_DEV void store4(uint16_t *p, f32x4_t v) { *(uint64_t *)p = pack_bf4(v[0], v[1], v[2], v[3]); }
-// bf16 out (ncols a multiple of 8): lane l takes columns 8 (l % 32) ..
-// + 7 of one of two rows (l / 32), so each store is 16 bytes and a wave
-// covers two rows per instruction.
+// bf16 out (ncols a multiple of 8).  The accumulators are rounded to bf16 as
+// they are staged (the one rounding the output gets either way), so the
+// whole tile fits the LDS at once: row r holds its BN values in 16-byte
+// chunks, chunk c at r * BN * 2 + ((c ^ (r % 32)) << 4).  Then lane l takes
+// chunk l % 32 (8 columns) of one of two rows (l / 32): every store is 16
+// bytes and a wave covers two rows per instruction.
+template <class C>
+MOE_DEV int epi16_off(int r, int chunk)
+{
+    return r * (C::BN * 2) + ((chunk ^ (r & 31)) << 4);
+}
+
 template <class C>
 MOE_DEV void store_tile_bf16(const Acc<C> &acc, lds_t *lds, uint16_t *out, int64_t m0,
                              int64_t mlim, int64_t n0, int64_t ncols)
 {
+    static_assert(C::BN == 256, "a staged row is 32 chunks: one per lane of a half wave");
+    static_assert(C::BM * C::BN * 2 <= C::LDS_BYTES, "the bf16 tile fits the LDS");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int r = acc_row<C>(wm, i, lane);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = acc_col<C>(wn, j, rg, lane);
+                *(lds_u64 *)(lds + epi16_off<C>(r, c >> 3) + (c & 4) * 2) =
+                    pack_bf4(acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
+                             acc.v[i][j][rg * 4 + 3]);
+            }
+    }
+    __syncthreads();
     const int c = lane & 31;
     const int64_t col = n0 + 8 * c;
     constexpr int NW = C::NT / 64, RB = 8;
-    static_assert(EPI_ROWS % (2 * NW * RB) == 0, "row batches tile the half");
+    static_assert(C::BM % (2 * NW * RB) == 0, "row batches tile the tile");
+    if (col < ncols)
+        for (int r0 = 2 * wave + (lane >> 5); r0 < C::BM; r0 += 2 * NW * RB) {
+            if (m0 + r0 >= mlim) break;  // rows past the segment (no barrier in the loop)
+            u32x4_t v[RB];
 #pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
-        if (m0 + half * EPI_ROWS >= mlim) break;
-        epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
-        __syncthreads();
-        if (col < ncols)
-            for (int r0 = 2 * wave + (lane >> 5); r0 < EPI_ROWS; r0 += 2 * NW * RB) {
-                f32x4_t lo[RB], hi[RB];
+            for (int b = 0; b < RB; ++b) v[b] = *(const lds_u32x4 *)(lds + epi16_off<C>(r0 + b * 2 * NW, c));
 #pragma unroll
-                for (int b = 0; b < RB; ++b) {
-                    lo[b] = *(const lds_f32x4 *)(lds + epi_off(r0 + b * 2 * NW, 2 * c));
-                    hi[b] = *(const lds_f32x4 *)(lds + epi_off(r0 + b * 2 * NW, 2 * c + 1));
-                }
-#pragma unroll
-                for (int b = 0; b < RB; ++b) {
-                    const int64_t m = m0 + half * EPI_ROWS + r0 + b * 2 * NW;
-                    if (m >= mlim) break;
-                    const u32x4_t v = {pack_bf2(lo[b][0], lo[b][1]), pack_bf2(lo[b][2], lo[b][3]),
-                                       pack_bf2(hi[b][0], hi[b][1]), pack_bf2(hi[b][2], hi[b][3])};
-                    *(u32x4_t *)(out + m * ncols + col) = v;
-                }
+            for (int b = 0; b < RB; ++b) {
+                const int64_t m = m0 + r0 + b * 2 * NW;
+                if (m >= mlim) break;
+                *(u32x4_t *)(out + m * ncols + col) = v[b];
             }
-        __syncthreads();
-    }
+        }
+    __syncthreads();
 }
 
 template <class C, class OutT = float>
