@@ -368,7 +368,7 @@ def pmc_busy_summary(busy_dir, out_path, cmds, workload="deepseek_v3"):
     busy = counter_rows(busy_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
     gui = {i: (n, v, us) for i, n, v, us in counter_rows(busy_dir, "GRBM_GUI_ACTIVE")}
     L = [f"# MFMA utilisation of the grouped GEMMs: {TRAFFIC_TITLES[workload]}, MI355X", "",
-         "Commands (from the repository root on the GPU box):",
+         "Commands (from the repository root, on an MI355X):",
          "", "```"] + cmds + ["```", "",
          "Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
          "clock = GRBM_GUI_ACTIVE / 8 / launch duration. The MFMA-bound rate at that clock is "
@@ -416,7 +416,7 @@ def trace_summary(stats_csv, bench_log, out_path, cmds):
     bench = json.loads(line)
     L = [f"# Kernel trace: {TRAFFIC_TITLES['deepseek_v3']}, MI355X: bf16 fwd+bwd steps, then the "
          "MXFP8 weight-cache fill and MXFP8 fwd+bwd steps", "",
-         "Commands (from the repository root on the GPU box; the CSV lands in gpurun_out/prof):",
+         "Commands (from the repository root, on an MI355X; the CSV lands in the -d folder):",
          "", "```"] + cmds + ["```", "", "| kernel | calls | avg us | total ms | % |",
                               "|---|---:|---:|---:|---:|"]
     for r in rows:
@@ -498,7 +498,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds,
     rec = {"source_hash": kernel_source_hash(), "copy_scale_fetch": round(sf, 4),
            "copy_scale_write": round(sw, 4), "kernels": kern}
     L = [f"# HBM traffic of the grouped GEMMs: {TRAFFIC_TITLES[workload]}, MI355X", "",
-         "Commands (from the repository root on the GPU box):", "", "```"] + cmds + ["```", "",
+         "Commands (from the repository root, on an MI355X):", "", "```"] + cmds + ["```", "",
          f"Calibration: a plain {COPY_BYTES} byte device copy reads FETCH_SIZE x {sf:.4f} and "
          f"WRITE_SIZE x {sw:.4f} of its true size; the per-launch figures below are scaled by "
          "those factors.", "",
@@ -645,7 +645,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         sys.exit(2)
 
