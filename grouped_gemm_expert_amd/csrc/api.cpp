@@ -624,9 +624,11 @@ static moe_status stage1_fwd(const moe_config *cfg, const uint16_t *x, const flo
     return MOE_OK;
 }
 
+// sched_ready: the schedule in `ws` is already this call's (the one-call
+// forward runs stage 1, which computes it, on the same workspace just before)
 static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const uint8_t *w2_mx,
                              const moe_saved *saved, float *y, void *ws, size_t ws_bytes,
-                             hipStream_t stream)
+                             hipStream_t stream, bool sched_ready = false)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
@@ -638,7 +640,7 @@ static moe_status stage2_fwd(const moe_config *cfg, const uint16_t *w2, const ui
     if (c.T == 0) return MOE_OK;
     MOE_CHECK(check_saved(saved, c));
     MOE_CHECK(check_ptrs({w2_mx ? (const void *)w2_mx : (const void *)w2, y}));
-    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    if (!sched_ready) MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
     moe_gemm_args a = saved_gemm_args(saved);
     a.w2 = w2;
     a.o = w.o;
@@ -689,7 +691,7 @@ moe_status moe_forward(const moe_config *cfg, const uint16_t *x, const float *Wr
     MOE_CHECK(moe_check_config(cfg));
     if (cfg->T > 0) MOE_CHECK(check_ptrs({w2, y}));
     MOE_CHECK(moe_stage1_forward(cfg, x, Wr, bias, w1, aux, saved, ws, ws_bytes, stream));
-    return moe_stage2_forward(cfg, w2, saved, y, ws, ws_bytes, stream);
+    return stage2_fwd(cfg, w2, nullptr, saved, y, ws, ws_bytes, stream, true);
 }
 
 // ---------------------------------------------------------------- MXFP8 ----
@@ -786,18 +788,20 @@ moe_status moe_forward_mx(const moe_config *cfg, const uint16_t *x, const float 
     MOE_CHECK(moe_check_config(cfg));
     if (cfg->T > 0) MOE_CHECK(check_ptrs({w2_mx, y}));
     MOE_CHECK(moe_stage1_forward_mx(cfg, x, Wr, bias, w1_mx, aux, saved, ws, ws_bytes, stream));
-    return moe_stage2_forward_mx(cfg, w2_mx, saved, y, ws, ws_bytes, stream);
+    return stage2_fwd(cfg, nullptr, (const uint8_t *)w2_mx, saved, y, ws, ws_bytes, stream, true);
 }
 
 static moe_status stage2_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *w2,
                              const uint8_t *w2t_mx, const uint16_t *dy, void *dW2,
                              int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
                              hipStream_t stream);
+// sched_ready: the schedule in `ws` is already this call's (the one-call
+// backward runs stage 2, which computes it, on the same workspace just before)
 static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, const uint16_t *x,
                              const float *Wr, const uint16_t *w1, const uint8_t *w1t_mx,
                              const float *d_aux, float *dx, float *dlogits, float *dWr, void *dW1,
                              int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
-                             hipStream_t stream);
+                             hipStream_t stream, bool sched_ready = false);
 
 moe_status moe_mx_quantize_t(const uint16_t *src, int64_t batches, int64_t R, int64_t C, void *dst,
                              size_t dst_bytes, hipStream_t stream)
@@ -876,8 +880,8 @@ moe_status moe_backward_mx(const moe_config *cfg, const moe_saved *saved, const 
     MOE_CHECK(check_opt_ptr(d_aux));
     MOE_CHECK(moe_stage2_backward_mx(cfg, saved, w2t_mx, dy, dW2, dw_dtype, dw_accumulate, ws,
                                      ws_bytes, stream));
-    return moe_stage1_backward_mx(cfg, saved, x, Wr, w1t_mx, d_aux, dx, dlogits, dWr, dW1,
-                                  dw_dtype, dw_accumulate, ws, ws_bytes, stream);
+    return stage1_bwd(cfg, saved, x, Wr, nullptr, (const uint8_t *)w1t_mx, d_aux, dx, dlogits,
+                      dWr, dW1, dw_dtype, dw_accumulate, ws, ws_bytes, stream, true);
 }
 
 // The backward stages in bf16 (w2 / w1) or MXFP8 (w2t_mx / w1t_mx: MX
@@ -981,7 +985,7 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
                              const float *Wr, const uint16_t *w1, const uint8_t *w1t_mx,
                              const float *d_aux, float *dx, float *dlogits, float *dWr, void *dW1,
                              int32_t dw_dtype, int32_t dw_accumulate, void *ws, size_t ws_bytes,
-                             hipStream_t stream)
+                             hipStream_t stream, bool sched_ready)
 {
     MOE_CHECK(moe_check_config(cfg));
     const moe_config &c = *cfg;
@@ -996,7 +1000,7 @@ static moe_status stage1_bwd(const moe_config *cfg, const moe_saved *saved, cons
     size_t need = 0;
     BwdWs w = carve_bwd(c, ws, &need);
     if (ws_bytes < need || (need && !ws)) return MOE_EWORKSPACE;
-    MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
+    if (!sched_ready) MOE_TRY(launch_schedule(c.E, saved->counts, w.sched, stream));
     moe_gemm_args a = saved_gemm_args(saved);
     a.x = x;
     a.w1 = w1;
@@ -1112,8 +1116,8 @@ moe_status moe_backward(const moe_config *cfg, const moe_saved *saved, const uin
     MOE_CHECK(check_opt_ptr(d_aux));
     MOE_CHECK(moe_stage2_backward(cfg, saved, w2, dy, dW2, dw_dtype, dw_accumulate, ws, ws_bytes,
                                   stream));
-    return moe_stage1_backward(cfg, saved, x, Wr, w1, d_aux, dx, dlogits, dWr, dW1, dw_dtype,
-                               dw_accumulate, ws, ws_bytes, stream);
+    return stage1_bwd(cfg, saved, x, Wr, w1, nullptr, d_aux, dx, dlogits, dWr, dW1, dw_dtype,
+                      dw_accumulate, ws, ws_bytes, stream, true);
 }
 
 // ------------------------------------------------------ no allocation ----
