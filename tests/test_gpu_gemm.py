@@ -19,13 +19,14 @@ SHAPES = [
 ]
 
 
-def _setup(T, H, I, E, k, seed=0):
+def _setup(T, H, I, E, k, seed=0, idx=None):
     g = torch.Generator().manual_seed(seed)
     rng = np.random.default_rng(seed)
-    p = 1.0 / np.arange(1, E + 1) ** 1.1
-    p[E // 2] = 0.0                                  # one empty expert
-    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
-    idx = idx.astype(np.int32)
+    if idx is None:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p[E // 2] = 0.0                              # one empty expert
+        idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
     counts, offsets, row_map, pos = oracle.permute(idx, E)
     M = T * k
     bf = lambda *s, std=1.0: (torch.randn(*s, generator=g) * std).to(torch.bfloat16)
@@ -87,10 +88,36 @@ def test_up_swiglu_and_down(shape):
 
 @pytest.mark.parametrize("shape", SHAPES)
 def test_dgrad_ops(shape):
-    from grouped_gemm_expert_amd import ops
     T, H, I, E, k = shape
     hz.say(f"gemm dgrad T={T} H={H} I={I} E={E} k={k}")
     t, maps = _setup(T, H, I, E, k, seed=1)
+    _check_dgrad(T, H, I, E, k, t, maps)
+
+
+# Rows per expert around the points where a segment's last 256-row m-tile
+# changes shape in the dgrad kernels' partial main loop: a wave copies 32
+# rows of A and multiplies 32-row fragments, so 1, 31..33, 63..65, 127..129,
+# 224, 225, 255..257 and 511 rows, and an empty expert.
+BOUNDARY_ROWS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 224, 225, 255, 256, 257,
+                 0, 511]
+
+
+def test_dgrad_partial_tiles_at_wave_boundaries():
+    E, H, I = len(BOUNDARY_ROWS), 128, 64
+    idx = np.repeat(np.arange(E, dtype=np.int32), BOUNDARY_ROWS)
+    np.random.default_rng(4).shuffle(idx)            # tokens of an expert scattered
+    T = len(idx)
+    hz.say(f"gemm dgrad, segment ends at wave boundaries: T={T} E={E} k=1")
+    t, maps = _setup(T, H, I, E, 1, seed=4, idx=idx[:, None])
+    assert maps["counts"].tolist() == BOUNDARY_ROWS
+    _check_dgrad(T, H, I, E, 1, t, maps)
+
+
+def _check_dgrad(T, H, I, E, k, t, maps):
+    """dgrad2 (with the SwiGLU backward and row-dot epilogue) and dgrad1 of the
+    given routing against an fp64 evaluation of their definitions, per
+    expert segment."""
+    from grouped_gemm_expert_amd import ops
     d = _dev(t, maps)
     cfg = ops.config(T=T, H=H, I=I, E=E, k=k)
     M = T * k
