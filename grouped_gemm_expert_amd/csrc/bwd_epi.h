@@ -202,7 +202,11 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
 // a 128-row half at a time.  In accumulate mode the old values of a wave's
 // first RB rows are loaded before that half's accumulators go through LDS,
 // so that memory round trip overlaps the staging; the later batches load
-// and store in turn.
+// and store in turn.  The fp32 gradient is read and written non-temporally:
+// nothing reads it again during the pass, and keeping it out of the caches
+// leaves them to the operand panels: the weight gradients are 2-8% faster
+// where this read-modify-write bounds them (many experts with few rows),
+// unchanged where the MFMAs do.
 template <class C, int RB = EPI_ROWS / (C::NT / 64)>
 MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c0, int R, int Cc,
                             int64_t dW_off, void *dWv, int32_t acc_mode, int32_t bf16)
@@ -228,7 +232,7 @@ MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c
                     unpack_bf4(*(const uint64_t *)((const uint16_t *)dWv + o), t4);
                     old[b] = f32x4_t{t4[0], t4[1], t4[2], t4[3]};
                 } else {
-                    old[b] = *(const f32x4_t *)((const float *)dWv + o);
+                    old[b] = __builtin_nontemporal_load((const f32x4_t *)((const float *)dWv + o));
                 }
             }
         }
@@ -244,7 +248,7 @@ MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c
             if (bf16)
                 *(uint64_t *)((uint16_t *)dWv + o) = pack_bf4(w[0], w[1], w[2], w[3]);
             else
-                *(f32x4_t *)((float *)dWv + o) = w;
+                __builtin_nontemporal_store(w, (f32x4_t *)((float *)dWv + o));
         }
     };
 #pragma unroll

@@ -216,9 +216,23 @@ hipError_t launch_permute_checked(int64_t M, int32_t E, const int32_t *idx, int3
 
 // ------------------------------------------------------------- schedule ----
 // mt_off*[e] = sum_{e' < e} ceil(counts[e'] / BM) for BM = 256 and 128,
-// order[] = experts by count descending (ties -> lower expert index), so the
-// weight-gradient GEMMs start the longest K loops first, and order[E] = the
-// number of experts with at least one row (they come first in order[]).
+// order[] = the experts with rows in the order the weight-gradient GEMMs
+// visit them, and order[E] = their number (the empty experts follow).
+// Experts are ranked by count descending (ties -> lower expert index).  With
+// SHORT_ROWS > 0 the experts with fewer rows than that (their tiles are
+// mostly the fp32 read-modify-write of dW, memory-bound) are spread among
+// the longer ones (MFMA-bound) instead of all coming last: short expert j
+// goes after long expert ceil((j+1) nb / ns) - 1 (nb long, ns short), so
+// the memory-bound tiles run beside MFMA-bound ones and the launch still
+// ends on short tiles.  Measured against all short experts last: the
+// DeepSeek-V3-style routing's dW2 pass 1.5% faster (5 short experts of 14;
+// with a 1024-row threshold, 4 of them, 2% slower), the Zipf-skewed one's
+// weight gradients 2-5% faster.
+#ifndef MOE_WGRAD_SHORT_ROWS
+#define MOE_WGRAD_SHORT_ROWS 2048
+#endif
+constexpr int32_t WGRAD_SHORT_ROWS = MOE_WGRAD_SHORT_ROWS;
+
 __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *counts,
                                                    int32_t *mt256, int32_t *mt128,
                                                    int32_t *order)
@@ -250,9 +264,23 @@ __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *cou
         }
     }
     for (int off = 1; off < S; off <<= 1) rank += __shfl_xor(rank, off, 64);
-    if (er < E && part == 0) order[rank] = er;
-    int32_t nact;
+    int32_t nact, nlong;
     block_excl_scan_1024((e < E && c > 0) ? 1 : 0, tmp, nact);
+    block_excl_scan_1024((e < E && c >= WGRAD_SHORT_ROWS && c > 0) ? 1 : 0, tmp, nlong);
+    if (er < E && part == 0) {
+        int32_t p = rank;
+        const int32_t ns = nact - nlong;
+        if (WGRAD_SHORT_ROWS > 0 && nlong > 0 && ns > 0 && rank < nact) {
+            if (rank < nlong) {
+                const int32_t sb = (int32_t)(((int64_t)rank * ns) / nlong);  // short ones before
+                p = rank + (sb < ns ? sb : ns);
+            } else {
+                const int32_t j = rank - nlong;
+                p = (int32_t)(((int64_t)(j + 1) * nlong + ns - 1) / ns) + j;
+            }
+        }
+        order[p] = er;
+    }
     if (e == 0) order[E] = nact;
 }
 
