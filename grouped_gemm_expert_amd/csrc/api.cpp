@@ -113,6 +113,8 @@ FwdWs carve_fwd(const moe_config &c, void *ws, size_t *bytes, size_t *bf16_bytes
     w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
     w.sched.order = cv.take<int32_t>(c.E + 1);
+    w.sched.mt_a = cv.take<int32_t>(c.E + 1);
+    w.sched.mt_b = cv.take<int32_t>(c.E + 1);
     w.wrow = cv.take<float>(M);
     w.router = cv.take<char>((int64_t)router_ws_bytes_fwd(c.T, c.E, c.H));
     w.o = cv.take<float>(M * c.H);   // [M,H] fp32 expert outputs
@@ -144,6 +146,8 @@ BwdWs carve_bwd(const moe_config &c, void *ws, size_t *bytes)
     w.sched.mt_off256 = cv.take<int32_t>(c.E + 1);
     w.sched.mt_off128 = cv.take<int32_t>(c.E + 1);
     w.sched.order = cv.take<int32_t>(c.E + 1);
+    w.sched.mt_a = cv.take<int32_t>(c.E + 1);
+    w.sched.mt_b = cv.take<int32_t>(c.E + 1);
     w.dh = cv.take<uint16_t>(M * 2 * c.I);
     w.dw_part = cv.take<float>(M * dgrad2_cols(c.I));
     w.dxp = cv.take<float>(M * c.H);

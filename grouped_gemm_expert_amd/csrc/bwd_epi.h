@@ -180,7 +180,7 @@ MOE_DEV void dgrad2_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
         if ((lane & (32 / RB - 1)) == 0 && m < t.seg_end) dw_part[m * nN + t.nt] = tot;
     };
 #pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
+    for (int half = 0; half < C::NHALF; ++half) {
         if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
         const int rb = 2 * wave + (lane >> 5);
         Batch bt;
@@ -252,7 +252,7 @@ MOE_DEV void wgrad_epilogue(const Acc<C> &acc, lds_t *lds, int64_t r0, int64_t c
         }
     };
 #pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
+    for (int half = 0; half < C::NHALF; ++half) {
         if (r0 + half * EPI_ROWS >= R) break;
         f32x4_t old[RB];
         load(half, wave, old);  // first batch, in flight while the half is staged

@@ -152,7 +152,14 @@ struct Sched {
     int32_t *mt_off256;  // [E+1]
     int32_t *mt_off128;  // [E+1]
     int32_t *order;      // [E+1]; order[E] = number of non-empty experts
+    int32_t *mt_a;       // [E+1] mixed m-tiling: 256-row tiles (decode_mtile_mixed)
+    int32_t *mt_b;       // [E+1] mixed m-tiling: 257..320-row tiles
 };
+
+// Mixed m-tiling of an expert with c rows: its 257..320-row tile count (0 or
+// 1: c > 256 leaving 1..64 rows past a multiple of 256) and its 256-row one.
+MOE_DEV int mixed_tail_tiles(int c) { return c > 256 && (c & 255) >= 1 && (c & 255) <= 64 ? 1 : 0; }
+MOE_DEV int mixed_head_tiles(int c) { return mixed_tail_tiles(c) ? c / 256 - 1 : (c + 255) / 256; }
 hipError_t launch_schedule(int32_t E, const int32_t *counts, const Sched &sc, hipStream_t s);
 
 struct GemmArgs {

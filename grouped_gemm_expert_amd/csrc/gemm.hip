@@ -14,8 +14,10 @@
 // the first grouped GEMM.
 //
 // Scheduling: forward and dgrad GEMMs tile the sorted rows of each expert
-// (M-grouped); the per-expert m-tile prefix sums live on the device, the
-// grid is sized from a host-side upper bound and surplus blocks exit.  The
+// (M-grouped), in 256-row tiles except that an expert's last tile may hold
+// 257..320 rows (the mixed m-tiling, decode_mtile_mixed); the per-expert
+// m-tile prefix sums live on the device, the grid is sized from a host-side
+// upper bound and surplus blocks exit.  The
 // weight-gradient GEMMs tile the [rows x cols] output of each expert that has
 // rows and loop over those rows (K-grouped), longest experts first; experts
 // without rows are zeroed by a separate fill (overwrite) or left untouched
@@ -53,14 +55,9 @@ int64_t mgrid_blocks(int64_t M, int E, int BM, int nN)
 // and the matching up columns, so each lane holds g and u of the same (r, i).
 // =========================================================================
 template <class C, bool SPLIT>
-__global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
+MOE_DEV void up_swiglu_tile(const GemmArgs &g, const MTile &t, lds_t *lds)
 {
-    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
-    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
-    const int nN = (int)ceil_div(I, C::BN / 2);
-    MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
     KLoad<C::BM, C::NT> la;
     KLoad<C::BN, C::NT> lb;
@@ -96,15 +93,10 @@ __global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
 // SPLIT: a is the pair a + a_lo, so the k loop runs twice over I: stages
 // 0 .. I/64-1 read a, the next I/64 read a_lo, both against the same w2.
 // =========================================================================
-template <class C, bool SPLIT>
-__global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
+template <class C, bool SPLIT, bool BF16OUT = false>
+MOE_DEV void down_tile(const GemmArgs &g, const MTile &t, lds_t *lds)
 {
-    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
-    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
-    const int nN = (int)ceil_div(H, C::BN);
-    MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
     KLoad<C::BM, C::NT> la;
     KLoad<C::BN, C::NT> lb;
@@ -141,7 +133,7 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
     } else {
         mainloop<C, false, false, false>(lds, I, la, lb, acc);
     }
-    if (g.o_bf16) store_tile_f32<C>(acc, lds, g.o_bf16, t.m0, t.seg_end, n0, H);
+    if (BF16OUT || g.o_bf16) store_tile_f32<C>(acc, lds, g.o_bf16, t.m0, t.seg_end, n0, H);
     else store_tile_f32<C>(acc, lds, g.o, t.m0, t.seg_end, n0, H);
 }
 
@@ -151,14 +143,10 @@ __global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
 //   dA = topk_w * dA';  dh = (dA u sig(g)(1 + g(1 - sig(g))) | dA silu(g))
 // =========================================================================
 template <class C, bool SPLIT>
-__global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
+MOE_DEV void down_dgrad_tile(const GemmArgs &g, const MTile &t, lds_t *lds)
 {
-    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
-    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
     const int nN = (int)ceil_div(I, C::BN);
-    MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
     KLoad<C::BM, C::NT> la;
     NLoad<C::BN, C::NT> lb;
@@ -176,12 +164,15 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
     Acc<C> acc;
     // a segment's last m-tile may be part-filled: the partial main loop skips
     // the A copies and MFMAs of its empty rows (3-4% on the dgrad GEMMs
-    // under uniform routing; it does not pay in GEMM1 and GEMM2)
+    // under uniform routing; it does not pay in GEMM1 and GEMM2).  A 320-row
+    // tile (257..320 rows) runs the full loop: its rows past the segment
+    // repeat the last one.
     const int64_t rows = t.seg_end - t.m0;
-    if (rows >= C::BM) mainloop<C, false, true, false>(lds, H, la, lb, acc);
-    else mainloop<C, false, true, false, true>(lds, H, la, lb, acc, (int)rows);
-    // the split form loads twice the rows' data: half the rows a batch
-    dgrad2_epilogue<C, SPLIT ? 2 : 4, SPLIT>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh,
+    if (rows >= C::BM || C::BM == 320) mainloop<C, false, true, false>(lds, H, la, lb, acc);
+    else mainloop<C, false, true, false, C::BM != 320>(lds, H, la, lb, acc, (int)rows);
+    // the split form loads twice the rows' data, and the 320-row tile has
+    // 32 more accumulators: half the rows a batch
+    dgrad2_epilogue<C, SPLIT || C::BM == 320 ? 2 : 4, SPLIT>(acc, lds, t, n0, nN, I, g.h, g.a, g.wrow, g.dh,
                                              g.dw_part, g.h_lo, g.a_lo, g.dh_lo);
 }
 
@@ -189,15 +180,10 @@ __global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
 // dgrad of GEMM1:  dxp[r, c] = dh[r] . w1[e, :, c]   (fp32 out, or bf16 to
 // g.dxp_bf16)
 // =========================================================================
-template <class C>
-__global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
+template <class C, bool BF16OUT = false>
+MOE_DEV void up_dgrad_tile(const GemmArgs &g, const MTile &t, lds_t *lds)
 {
-    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
-    lds_t *lds = (lds_t *)lds_raw;
     const int I = g.I, H = g.H;
-    const int nN = (int)ceil_div(H, C::BN);
-    MTile t;
-    if (!decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128, g.offsets, g.E, nN, t)) return;
     const int tid = threadIdx.x, lane0 = tid & 63, wave0 = wave_uniform_id();
     KLoad<C::BM, C::NT> la;
     NLoad<C::BN, C::NT> lb;
@@ -213,12 +199,86 @@ __global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
     // B(n = hh, k = nn) = w1[e, nn, hh]: k-row nn starts at w1e + nn*H
     lb.init(w1e, H, n0, H, wave0, lane0);
     Acc<C> acc;
-    const int64_t rows = t.seg_end - t.m0;  // part-filled last m-tile: as in k_down_dgrad
-    if (rows >= C::BM) mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
-    else mainloop<C, false, true, false, true>(lds, 2 * I, la, lb, acc, (int)rows);
-    if (g.dxp_bf16) store_tile_f32<C>(acc, lds, g.dxp_bf16, t.m0, t.seg_end, n0, H);
+    const int64_t rows = t.seg_end - t.m0;  // part-filled last m-tile: as in down_dgrad_tile
+    if (rows >= C::BM || C::BM == 320) mainloop<C, false, true, false>(lds, 2 * I, la, lb, acc);
+    else mainloop<C, false, true, false, C::BM != 320>(lds, 2 * I, la, lb, acc, (int)rows);
+    if (BF16OUT || g.dxp_bf16) store_tile_f32<C>(acc, lds, g.dxp_bf16, t.m0, t.seg_end, n0, H);
     else store_tile_f32<C>(acc, lds, g.dxp, t.m0, t.seg_end, n0, H);
 }
+
+// =========================================================================
+// Kernels of the M-grouped GEMMs.  Single-shape kernels: 256-row tiles (or
+// 128-row ones) of every row (mt_off256 / mt_off128).  Mixed kernels: both
+// shapes of the mixed m-tiling in one launch (decode_mtile_mixed), each
+// block one tile of either shape; their GEMM2 and dgrad1 store bf16 only
+// (the forms the layer uses).  The two shapes' code sits side by side in
+// one kernel; the 256-row path compiles as in the single-shape kernel
+// (no spills) because the decoded tile is forced into scalar registers.
+// =========================================================================
+template <class C>
+MOE_DEV bool decode_single(const GemmArgs &g, int nN, MTile &t)
+{
+    return decode_mtile<C::BM>(blockIdx.x, C::BM == 256 ? g.sched.mt_off256 : g.sched.mt_off128,
+                               g.offsets, g.E, nN, t);
+}
+
+template <class C0, class C1>
+struct Mixed {
+    static_assert(C0::NT == C1::NT && C0::BM == 256 && C1::BM == 320 && C0::BN == C1::BN,
+                  "256- and 320-row shapes of one n-tiling");
+    static constexpr int NT = C0::NT;
+    static constexpr int LDS_BYTES = C0::LDS_BYTES > C1::LDS_BYTES ? C0::LDS_BYTES : C1::LDS_BYTES;
+};
+
+#define MOE_MIXED_KERNEL(NAME, NCOLS, ...)                                                     \
+    template <class M, class C0, class C1>                                                     \
+    __global__ __launch_bounds__(M::NT) void NAME##_mixed(GemmArgs g)                          \
+    {                                                                                          \
+        __shared__ __attribute__((aligned(16))) char lds_raw[M::LDS_BYTES];                    \
+        MTile t;                                                                               \
+        const int cls = decode_mtile_mixed(blockIdx.x, g.sched.mt_a, g.sched.mt_b, g.offsets, \
+                                           g.E, (int)(NCOLS), t);                              \
+        if (cls == 0) NAME##_tile<C0, __VA_ARGS__>(g, t, (lds_t *)lds_raw);                    \
+        else if (cls == 1) NAME##_tile<C1, __VA_ARGS__>(g, t, (lds_t *)lds_raw);               \
+    }
+
+template <class C, bool SPLIT>
+__global__ __launch_bounds__(C::NT) void k_up_swiglu(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    MTile t;
+    if (decode_single<C>(g, (int)ceil_div(g.I, C::BN / 2), t))
+        up_swiglu_tile<C, SPLIT>(g, t, (lds_t *)lds_raw);
+}
+MOE_MIXED_KERNEL(up_swiglu, ceil_div(g.I, C0::BN / 2), false)
+
+template <class C, bool SPLIT>
+__global__ __launch_bounds__(C::NT) void k_down(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    MTile t;
+    if (decode_single<C>(g, (int)ceil_div(g.H, C::BN), t)) down_tile<C, SPLIT>(g, t, (lds_t *)lds_raw);
+}
+MOE_MIXED_KERNEL(down, ceil_div(g.H, C0::BN), false, true)
+
+template <class C, bool SPLIT>
+__global__ __launch_bounds__(C::NT) void k_down_dgrad(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    MTile t;
+    if (decode_single<C>(g, (int)ceil_div(g.I, C::BN), t))
+        down_dgrad_tile<C, SPLIT>(g, t, (lds_t *)lds_raw);
+}
+MOE_MIXED_KERNEL(down_dgrad, ceil_div(g.I, C0::BN), false)
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void k_up_dgrad(GemmArgs g)
+{
+    __shared__ __attribute__((aligned(16))) char lds_raw[C::LDS_BYTES];
+    MTile t;
+    if (decode_single<C>(g, (int)ceil_div(g.H, C::BN), t)) up_dgrad_tile<C>(g, t, (lds_t *)lds_raw);
+}
+MOE_MIXED_KERNEL(up_dgrad, ceil_div(g.H, C0::BN), true)
 
 // =========================================================================
 // Weight-gradient operands: the rows of each expert, transposed into a
@@ -404,8 +464,14 @@ hipError_t launch_zero_empty(int32_t E, int64_t per_expert, const int32_t *count
 // from LDS, +3% (the other ops lose on it).  Every op takes three B stage
 // buffers (all 160 KB of LDS): the B copies of a stage get two stages to
 // land.
+// The mixed m-tiling's 257..320-row tiles run eight waves of 160 x 64 with
+// two B stage buffers (2 x 40 KB of A, 2 x 32 KB of B), A fragments refilled
+// in place.  In the mixed kernels GEMM2's 256-row tiles take eight waves (the
+// two shapes share a launch); its split and fp32-output forms keep four.
 using Tall = TileCfg<256, 256, 128, 64, 3>;
 using Quad = TileCfg<256, 256, 128, 128, 3>;
+using Tall320 = TileCfg<320, 256, 160, 64, 2>;
+using MixT = Mixed<Tall, Tall320>;
 using UpCfg = Tall;
 using DownCfg = Quad;
 using DownDgradCfg = Tall;
@@ -426,27 +492,32 @@ hipError_t launch_grouped_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
 {
     const bool sp = g.split != 0;
     switch (op) {
+    // bf16 intermediates: the mixed m-tiling (GEMM2 and dgrad1 when they store
+    // bf16); otherwise 256-row tiles
     case MOE_GEMM_UP_SWIGLU: {
         using C = UpCfg;
         const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN / 2));
         return sp ? launch_k(k_up_swiglu<C, true>, b, g, s, C::NT)
-                  : launch_k(k_up_swiglu<C, false>, b, g, s, C::NT);
+                  : launch_k(up_swiglu_mixed<MixT, Tall, Tall320>, b, g, s, MixT::NT);
     }
     case MOE_GEMM_DOWN: {
         using C = DownCfg;
         const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN));
-        return sp ? launch_k(k_down<C, true>, b, g, s, C::NT)
-                  : launch_k(k_down<C, false>, b, g, s, C::NT);
+        if (sp) return launch_k(k_down<C, true>, b, g, s, C::NT);
+        return g.o_bf16 ? launch_k(down_mixed<MixT, Tall, Tall320>, b, g, s, MixT::NT)
+                        : launch_k(k_down<C, false>, b, g, s, C::NT);
     }
     case MOE_GEMM_DOWN_DGRAD: {
         using C = DownDgradCfg;
         const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.I, C::BN));
         return sp ? launch_k(k_down_dgrad<C, true>, b, g, s, C::NT)
-                  : launch_k(k_down_dgrad<C, false>, b, g, s, C::NT);
+                  : launch_k(down_dgrad_mixed<MixT, Tall, Tall320>, b, g, s, MixT::NT);
     }
     case MOE_GEMM_UP_DGRAD: {
         using C = UpDgradCfg;
-        return launch_k(k_up_dgrad<C>, mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN)), g, s, C::NT);
+        const int64_t b = mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(g.H, C::BN));
+        return g.dxp_bf16 && !sp ? launch_k(up_dgrad_mixed<MixT, Tall, Tall320>, b, g, s, MixT::NT)
+                                 : launch_k(k_up_dgrad<C>, b, g, s, C::NT);
     }
     case MOE_GEMM_DOWN_WGRAD: {
         using C = WgradCfg;

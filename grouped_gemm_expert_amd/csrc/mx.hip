@@ -320,6 +320,7 @@ struct MxCfg {
     static constexpr int LDS_BYTES = RING_BYTES > 131072 ? RING_BYTES : 131072;
     static_assert(BM == BN && NS * (NT / 64) * 32 == BM, "scale blocks split evenly over the waves");
     static_assert(LDS_BYTES <= 163840, "LDS of one CU");
+    static constexpr int NHALF = BM / 128;  // 128-row epilogue passes
 };
 // Eight waves of 128 x 64 (two a SIMD, 256 registers each): 128 accumulator
 // registers and one in-place set of six 32-byte fragments.

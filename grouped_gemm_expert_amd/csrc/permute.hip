@@ -216,6 +216,8 @@ hipError_t launch_permute_checked(int64_t M, int32_t E, const int32_t *idx, int3
 
 // ------------------------------------------------------------- schedule ----
 // mt_off*[e] = sum_{e' < e} ceil(counts[e'] / BM) for BM = 256 and 128,
+// mt_a / mt_b the same sums of the mixed m-tiling's 256-row and 320-row
+// tile counts (mixed_head_tiles / mixed_tail_tiles),
 // order[] = the experts with rows in the order the weight-gradient GEMMs
 // visit them, and order[E] = their number (the empty experts follow).
 // Experts are ranked by count descending (ties -> lower expert index).  With
@@ -235,7 +237,7 @@ constexpr int32_t WGRAD_SHORT_ROWS = MOE_WGRAD_SHORT_ROWS;
 
 __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *counts,
                                                    int32_t *mt256, int32_t *mt128,
-                                                   int32_t *order)
+                                                   int32_t *order, int32_t *mt_a, int32_t *mt_b)
 {
     __shared__ int32_t tmp[16];
     __shared__ int32_t sc[PM_EMAX];
@@ -249,6 +251,12 @@ __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *cou
     int32_t o128 = block_excl_scan_1024((c + 127) / 128, tmp, total);
     if (e < E) mt128[e] = o128;
     if (e == E - 1) mt128[E] = total;
+    const int32_t oa = block_excl_scan_1024(mixed_head_tiles(c), tmp, total);
+    if (e < E) mt_a[e] = oa;
+    if (e == E - 1) mt_a[E] = total;
+    const int32_t ob = block_excl_scan_1024(mixed_tail_tiles(c), tmp, total);
+    if (e < E) mt_b[e] = ob;
+    if (e == E - 1) mt_b[E] = total;
     __syncthreads();
     // rank of expert er: S threads (consecutive lanes of one wave) each count
     // the experts ahead of it among every S-th one, then add up by shuffles
@@ -286,7 +294,8 @@ __global__ __launch_bounds__(1024) void k_schedule(int32_t E, const int32_t *cou
 
 hipError_t launch_schedule(int32_t E, const int32_t *counts, const Sched &sc, hipStream_t s)
 {
-    k_schedule<<<1, 1024, 0, s>>>(E, counts, sc.mt_off256, sc.mt_off128, sc.order);
+    k_schedule<<<1, 1024, 0, s>>>(E, counts, sc.mt_off256, sc.mt_off128, sc.order, sc.mt_a,
+                                  sc.mt_b);
     return hipGetLastError();
 }
 

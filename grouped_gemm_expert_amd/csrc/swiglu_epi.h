@@ -35,7 +35,7 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
     static_assert(!MX || GCOLS == MX_GROUP, "one MX scale group per tile row");
     auto soff = [](int r, int chunk) { return r * (3 * GCOLS * 2) + ((chunk ^ (r & 15)) << 4); };
 #pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
+    for (int half = 0; half < C::NHALF; ++half) {
         if (t.m0 + half * EPI_ROWS >= t.seg_end) break;
 #pragma unroll
       for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {

@@ -5,6 +5,7 @@
 // (dense.hip).
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -40,7 +41,11 @@ struct TileCfg {
     static_assert(NBB == 2 || NBB == 3, "two or three B stage buffers");
     static_assert(LDS_BYTES <= 163840, "LDS of one CU");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is a multiple of 32x32");
-    static_assert(BM == 256 || BM == 128, "m-tile prefix sums exist for 256 and 128 rows");
+    static_assert(BM == 256 || BM == 128 || BM == 320, "m-tile schedules exist for 128, 256, 320 rows");
+    // five or more row fragments a wave: A fragments refilled in place (one
+    // register set), which frees the registers the taller wave tile needs
+    static constexpr bool INPLACE = FM >= 5;
+    static constexpr int NHALF = (BM + 127) / 128;  // 128-row epilogue passes
 };
 
 // ------------------------------------------------------------- loaders ----
@@ -302,6 +307,41 @@ MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const ld
     }
 }
 
+// In-place form (INPLACE_A): the wave holds one set of A fragments and two
+// of B.  Before MFMA n < FN the wave reads B fragment n of the next k-step
+// into the other B set; right after the last MFMA that reads A fragment i
+// (n = i*FN + FN-1) it reads the next k-step's A fragment i into the same
+// registers, which the next k-step first needs NMF-FN MFMAs later.  A
+// fragments take FM*16 bytes a lane instead of twice that (used by the
+// configurations whose registers need it: it costs ~1% where the two-set
+// form fits, the refilled fragment having less time to arrive).
+template <class C, bool A_NMAJ, bool B_NMAJ, bool PARTIAL, int NC, class Copy>
+MOE_DEV void kstep_ip(bf16x8_t (&fa)[C::FM], const bf16x8_t (&bc)[C::FN], bf16x8_t (&bn)[C::FN],
+                      const lds_t *As, const lds_t *Bs, int kk_next, Copy &&copy, Acc<C> &acc,
+                      int wm, int wn, int lane, int na)
+{
+    constexpr int NMF = C::FM * C::FN;
+#pragma unroll
+    for (int n = 0; n < NMF; ++n) {
+        const int i = n / C::FN, j = n % C::FN;
+        if (n < C::FN)
+            bn[n] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + n * 32, kk_next, lane)
+                           : frag_kmaj(Bs, wn * C::WN + n * 32, kk_next, lane);
+#pragma unroll
+        for (int q = 0; q < NC; ++q)
+            if (q * NMF / NC == n) copy(q);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!PARTIAL || i < na)
+            acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[j], fa[i], acc.v[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j == C::FN - 1 && (!PARTIAL || i < na)) {
+            fa[i] = A_NMAJ ? frag_nmaj<C::BM>(As, wm * C::WM + i * 32, kk_next, lane)
+                           : frag_kmaj(As, wm * C::WM + i * 32, kk_next, lane);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 template <int S>
 struct SetTag {
     static constexpr int value = S;
@@ -369,8 +409,20 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
     wait_copies_le<NCA + NCB + (SPREAD ? SB : 0)>();
     tail(v0, As[0], Bs[0]);
     __syncthreads();
+    // two fragment sets f0 / f1 (k-step s multiplies one and reads step s+1
+    // into the other), or with INPLACE one A set (f0.a) and two B sets
     Frags<C> f0, f1;
     read_frags<C, A_NMAJ, B_NMAJ, PARTIAL>(As[0], Bs[0], 0, f0, wm, wn, lane, na);
+    // k-step: multiply `cur`, read the step kk fragments into `nxt`
+    auto kst = [&](Frags<C> &cur, Frags<C> &nxt, const lds_t *A_, const lds_t *B_, int kk,
+                   auto &&copy, auto nc) {
+        constexpr int NC_ = decltype(nc)::value;
+        if constexpr (C::INPLACE)
+            kstep_ip<C, A_NMAJ, B_NMAJ, PARTIAL, NC_>(f0.a, cur.b, nxt.b, A_, B_, kk, copy, acc, wm,
+                                                      wn, lane, na);
+        else
+            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, NC_>(cur, nxt, A_, B_, kk, copy, acc, wm, wn, lane, na);
+    };
     // one stage; the buffers it uses are compile-time constants, so LDS
     // addresses fold into instruction offsets
     auto stage = [&](auto tag, int v) {
@@ -382,14 +434,15 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
             return [&, s](int i) { copy_b(s * SB + i, vp, Bs[bp]); };
         };
         auto none = [](int) {};
+        using SBt = std::integral_constant<int, SPREAD ? SB : 0>;
         if constexpr (SPREAD) {
-            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, SB>(f0, f1, As[a], Bs[b], 1, slot(1), acc, wm, wn, lane, na);
-            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, SB>(f1, f0, As[a], Bs[b], 2, slot(2), acc, wm, wn, lane, na);
-            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, SB>(f0, f1, As[a], Bs[b], 3, slot(3), acc, wm, wn, lane, na);
+            kst(f0, f1, As[a], Bs[b], 1, slot(1), SBt());
+            kst(f1, f0, As[a], Bs[b], 2, slot(2), SBt());
+            kst(f0, f1, As[a], Bs[b], 3, slot(3), SBt());
         } else {
-            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, 0>(f0, f1, As[a], Bs[b], 1, none, acc, wm, wn, lane, na);
-            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, 0>(f1, f0, As[a], Bs[b], 2, none, acc, wm, wn, lane, na);
-            kstep<C, A_NMAJ, B_NMAJ, PARTIAL, 0>(f0, f1, As[a], Bs[b], 3, none, acc, wm, wn, lane, na);
+            kst(f0, f1, As[a], Bs[b], 1, none, SBt());
+            kst(f1, f0, As[a], Bs[b], 2, none, SBt());
+            kst(f0, f1, As[a], Bs[b], 3, none, SBt());
         }
         // every stage issues the same copies, and stage v+1's were all issued
         // before the last A copies; only the B copies of stage v+2 (three B
@@ -402,13 +455,11 @@ MOE_DEV void pipeline(lds_t *lds, int v0, int v1, CopyA &&copy_a, CopyB &&copy_b
         // branch-free: the reads fetch stale fragments that are never used,
         // and the last stage is copied again into buffers nothing reads.
         const int va = clampv(v + 2), vb = clampv(v + NB);
-        kstep<C, A_NMAJ, B_NMAJ, PARTIAL, NCA + SB>(
-            f1, f0, As[an], Bs[bn], 0,
-            [&](int q) {
-                if (q < NCA) copy_a(q, va, As[a]);
-                else copy_b(q - NCA, vb, Bs[b]);
-            },
-            acc, wm, wn, lane, na);
+        auto copy0 = [&](int q) {
+            if (q < NCA) copy_a(q, va, As[a]);
+            else copy_b(q - NCA, vb, Bs[b]);
+        };
+        kst(f1, f0, As[an], Bs[bn], 0, copy0, std::integral_constant<int, NCA + SB>());
     };
     constexpr int P = NB == 3 ? 6 : 2;  // buffer pattern period
     int v = v0;
@@ -553,46 +604,59 @@ MOE_DEV int epi16_off(int r, int chunk)
     return r * (C::BN * 2) + ((chunk ^ (r & 31)) << 4);
 }
 
+// A tile whose bf16 values do not fit the LDS at once (320 rows) goes in
+// one pass per wave row (WM rows each).
 template <class C>
 MOE_DEV void store_tile_bf16(const Acc<C> &acc, lds_t *lds, uint16_t *out, int64_t m0,
                              int64_t mlim, int64_t n0, int64_t ncols)
 {
     static_assert(C::BN == 256, "a staged row is 32 chunks: one per lane of a half wave");
-    static_assert(C::BM * C::BN * 2 <= C::LDS_BYTES, "the bf16 tile fits the LDS");
+    constexpr bool WHOLE = C::BM * C::BN * 2 <= C::LDS_BYTES;
+    constexpr int NPASS = WHOLE ? 1 : C::WAVES_M, PROWS = WHOLE ? C::BM : C::WM;
+    static_assert(PROWS * C::BN * 2 <= C::LDS_BYTES, "a pass's bf16 rows fit the LDS");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        const int r = acc_row<C>(wm, i, lane);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int c = acc_col<C>(wn, j, rg, lane);
-                *(lds_u64 *)(lds + epi16_off<C>(r, c >> 3) + (c & 4) * 2) =
-                    pack_bf4(acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1], acc.v[i][j][rg * 4 + 2],
-                             acc.v[i][j][rg * 4 + 3]);
-            }
-    }
-    __syncthreads();
     const int c = lane & 31;
     const int64_t col = n0 + 8 * c;
     constexpr int NW = C::NT / 64, RB = 8;
-    static_assert(C::BM % (2 * NW * RB) == 0, "row batches tile the tile");
-    if (col < ncols)
-        for (int r0 = 2 * wave + (lane >> 5); r0 < C::BM; r0 += 2 * NW * RB) {
-            if (m0 + r0 >= mlim) break;  // rows past the segment (no barrier in the loop)
-            u32x4_t v[RB];
+    static_assert(PROWS % (2 * NW * RB) == 0 || !WHOLE, "row batches tile the tile");
 #pragma unroll
-            for (int b = 0; b < RB; ++b) v[b] = *(const lds_u32x4 *)(lds + epi16_off<C>(r0 + b * 2 * NW, c));
+    for (int pass = 0; pass < NPASS; ++pass) {
+        const int64_t p0 = m0 + pass * PROWS;  // first row of the pass
+        if (p0 >= mlim) break;
+        if (WHOLE || wm == pass) {
 #pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                const int64_t m = m0 + r0 + b * 2 * NW;
-                if (m >= mlim) break;
-                *(u32x4_t *)(out + m * ncols + col) = v[b];
+            for (int i = 0; i < C::FM; ++i) {
+                const int r = acc_row<C>(wm, i, lane) - pass * PROWS;
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int cc = acc_col<C>(wn, j, rg, lane);
+                        *(lds_u64 *)(lds + epi16_off<C>(r, cc >> 3) + (cc & 4) * 2) =
+                            pack_bf4(acc.v[i][j][rg * 4], acc.v[i][j][rg * 4 + 1],
+                                     acc.v[i][j][rg * 4 + 2], acc.v[i][j][rg * 4 + 3]);
+                    }
             }
         }
-    __syncthreads();
+        __syncthreads();
+        if (col < ncols)
+            for (int r0 = 2 * wave + (lane >> 5); r0 < PROWS; r0 += 2 * NW * RB) {
+                if (p0 + r0 >= mlim) break;  // rows past the segment (no barrier in the loop)
+                u32x4_t v[RB];
+#pragma unroll
+                for (int b = 0; b < RB; ++b)
+                    if (WHOLE || r0 + b * 2 * NW < PROWS)
+                        v[b] = *(const lds_u32x4 *)(lds + epi16_off<C>(r0 + b * 2 * NW, c));
+#pragma unroll
+                for (int b = 0; b < RB; ++b) {
+                    const int64_t m = p0 + r0 + b * 2 * NW;
+                    if (m >= mlim || (!WHOLE && r0 + b * 2 * NW >= PROWS)) break;
+                    *(u32x4_t *)(out + m * ncols + col) = v[b];
+                }
+            }
+        __syncthreads();
+    }
 }
 
 template <class C, class OutT = float>
@@ -609,7 +673,7 @@ MOE_DEV void store_tile_f32(const Acc<C> &acc, lds_t *lds, OutT *out, int64_t m0
     constexpr int NW = C::NT / 64, RB = 8;
     static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
 #pragma unroll
-    for (int half = 0; half < C::BM / EPI_ROWS; ++half) {
+    for (int half = 0; half < C::NHALF; ++half) {
         if (m0 + half * EPI_ROWS >= mlim) break;
         epi_stage_f32<C>(acc, lds, half, wm, wn, lane);
         __syncthreads();
@@ -656,20 +720,32 @@ struct MTile {
     int e;
     int64_t m0, seg_end;
     int nt;
+    // the fields are block-uniform: keep them in scalar registers
+    MOE_DEV void uniform()
+    {
+        e = __builtin_amdgcn_readfirstlane(e);
+        nt = __builtin_amdgcn_readfirstlane(nt);
+        m0 = rfl64(m0);
+        seg_end = rfl64(seg_end);
+    }
+    static MOE_DEV int64_t rfl64(int64_t v)
+    {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    }
 };
 
 // M-grouped tile L: inside each expert, groups of GM of its m-tiles sweep
 // all n-tiles before moving on; a group never spans two experts, so the
 // tiles an XCD runs together share the expert's weight panels and their
 // token rows in its L2 (an expert with few rows is one group).
+// Tile L (0 <= L < mt_off[E] nN, after the XCD remap).
 template <int BM>
-MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offsets, int E,
-                          int nN, MTile &t)
+MOE_DEV void decode_mtile_at(int64_t L, const int32_t *mt_off, const int32_t *offsets, int E,
+                             int nN, MTile &t)
 {
     constexpr int GM = 4;
-    const int64_t total = (int64_t)mt_off[E] * nN;
-    int64_t L = xcd_remap(b, total);
-    if (L < 0) return false;
     // expert e owns tiles [mt_off[e] nN, mt_off[e + 1] nN): the largest e
     // with mt_off[e] nN <= L has m-tiles (mte >= 1)
     int lo = 0, hi = E;
@@ -687,10 +763,58 @@ MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offse
     t.e = lo;
     t.m0 = offsets[lo] + (first + in % gm) * BM;
     t.seg_end = offsets[lo + 1];
+}
+
+// The tile of block b (false: a surplus block).
+template <int BM>
+MOE_DEV bool decode_mtile(int64_t b, const int32_t *mt_off, const int32_t *offsets, int E,
+                          int nN, MTile &t)
+{
+    const int64_t L = xcd_remap(b, (int64_t)mt_off[E] * nN);
+    if (L < 0) return false;
+    decode_mtile_at<BM>(L, mt_off, offsets, E, nN, t);
     return true;
 }
 
-// Upper bound on the blocks an M-grouped launch needs (host side).
+// Mixed m-tiling of the bf16 forward and dgrad GEMMs.  Each expert's rows
+// are cut into 256-row tiles, except that an expert with more than 256 rows
+// whose count leaves 1..64 rows past a multiple of 256 ends on one tile of
+// 257..320 rows instead of a full tile and a nearly empty one: under
+// balanced routing (about 256 rows an expert) half the experts would
+// otherwise stream their weights a second time for a few rows.  mt_a counts
+// the 256-row tiles (class 0), mt_b the 320-row ones (class 1, at most one
+// an expert).  One launch holds both: the longer class-1 tiles first (so
+// that they do not end the launch on a tail of their own), then class 0,
+// each sweeping its expert's n-tiles as decode_mtile does.  Returns the
+// class, or -1 for a surplus block.
+MOE_DEV int decode_mtile_mixed(int64_t b, const int32_t *mt_a, const int32_t *mt_b,
+                               const int32_t *offsets, int E, int nN, MTile &t)
+{
+    const int64_t ta = (int64_t)mt_a[E] * nN, tb = (int64_t)mt_b[E] * nN;
+    int64_t L = xcd_remap(b, ta + tb);
+    if (L < 0) return -1;
+    if (L >= tb) {
+        decode_mtile_at<256>(L - tb, mt_a, offsets, E, nN, t);
+        // a class-0 tile ends where the expert's class-1 tile (if any) starts
+        if (t.seg_end > t.m0 + 256) t.seg_end = t.m0 + 256;
+        t.uniform();
+        return 0;
+    }
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if ((int64_t)mt_b[mid] * nN <= L) lo = mid; else hi = mid;
+    }
+    t.e = lo;
+    t.nt = (int)(L - (int64_t)mt_b[lo] * nN);
+    t.seg_end = offsets[lo + 1];
+    t.m0 = offsets[lo] + (int64_t)((t.seg_end - offsets[lo]) / 256 - 1) * 256;
+    t.uniform();
+    return 1;
+}
+
+// Upper bound on the blocks an M-grouped launch needs (host side; also
+// bounds the mixed tiling's 256-row tiles).
 int64_t mgrid_blocks(int64_t M, int E, int BM, int nN);
 
 }  // namespace moe

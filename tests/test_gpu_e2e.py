@@ -100,6 +100,12 @@ EDGE = {
     "split_single_token": _wl("mid_split", T=1),
     "split_wide_tile_tail": _wl("mid_split", H=320, I=448, T=333, E=4, k=2),
     "split_small_dims": _wl("mid_split", H=64, I=64, T=130, E=4, k=2),
+    # the mixed m-tiling of the forward and dgrad GEMMs: experts of 257..320
+    # rows are one 320-row tile, 513..576 a 256-row tile and a 320-row one
+    "even_300_rows": _wl("mid_even", T=600, E=4, k=2),
+    "even_257_rows": _wl("mid_even", T=257, E=4, k=4, n_groups=1, topk_groups=1),
+    "even_576_rows": _wl("mid_even", T=576, E=4, k=4, n_groups=1, topk_groups=1),
+    "softmax_about_300_rows": _wl("mid_softmax", T=1200, E=8, k=2),
 }
 
 

@@ -52,10 +52,16 @@ def _segments(maps, E):
 
 @pytest.mark.parametrize("shape", SHAPES)
 def test_up_swiglu_and_down(shape):
-    from grouped_gemm_expert_amd import ops
     T, H, I, E, k = shape
     hz.say(f"gemm up_swiglu/down T={T} H={H} I={I} E={E} k={k}")
     t, maps = _setup(T, H, I, E, k)
+    _check_forward(T, H, I, E, k, t, maps)
+
+
+def _check_forward(T, H, I, E, k, t, maps):
+    """GEMM1 (with the SwiGLU epilogue) and GEMM2 of the given routing against
+    an fp64 evaluation of their definitions, per expert segment."""
+    from grouped_gemm_expert_amd import ops
     d = _dev(t, maps)
     cfg = ops.config(T=T, H=H, I=I, E=E, k=k)
     M = T * k
@@ -110,6 +116,26 @@ def test_dgrad_partial_tiles_at_wave_boundaries():
     hz.say(f"gemm dgrad, segment ends at wave boundaries: T={T} E={E} k=1")
     t, maps = _setup(T, H, I, E, 1, seed=4, idx=idx[:, None])
     assert maps["counts"].tolist() == BOUNDARY_ROWS
+    _check_dgrad(T, H, I, E, 1, t, maps)
+
+
+# Rows per expert around the mixed m-tiling's shapes (forward and dgrad
+# GEMMs): 257..320 rows are one 320-row tile, 321 two 256-row tiles, 513 and
+# 576 a 256-row tile and a 320-row one, 577 three 256-row tiles, 832 two
+# 256-row tiles and a 320-row one.
+MIXED_ROWS = [257, 258, 288, 289, 300, 319, 320, 321, 512, 513, 576, 577, 832, 256, 255, 65, 0,
+              1]
+
+
+def test_mixed_m_tiles():
+    E, H, I = len(MIXED_ROWS), 384, 320
+    idx = np.repeat(np.arange(E, dtype=np.int32), MIXED_ROWS)
+    np.random.default_rng(6).shuffle(idx)
+    T = len(idx)
+    hz.say(f"gemm up_swiglu/down/dgrad, mixed m-tiles: T={T} E={E} k=1")
+    t, maps = _setup(T, H, I, E, 1, seed=6, idx=idx[:, None])
+    assert maps["counts"].tolist() == MIXED_ROWS
+    _check_forward(T, H, I, E, 1, t, maps)
     _check_dgrad(T, H, I, E, 1, t, maps)
 
 
