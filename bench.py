@@ -43,13 +43,22 @@ GEMM_STAGES = ["up_swiglu", "down", "down_dgrad", "up_dgrad", "down_wgrad", "up_
 # a forward workload (the few-large experts one): the forward's stages only
 FWD_STAGES = ["router_proj", "router", "permute", "up_swiglu", "down", "combine"]
 METRIC_FWD = "MoE layer fwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
-# kernel-name fragment of each grouped-GEMM op in a rocprofv3 trace
-GEMM_KERNELS = {"up_swiglu": "k_up_swiglu<", "down": "k_down<", "down_dgrad": "k_down_dgrad<",
-                "up_dgrad": "k_up_dgrad<", "down_wgrad": "k_wgrad<", "up_wgrad": "k_wgrad<",
-                "up_swiglu_mx": "k_up_swiglu_mx<", "down_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 128>, 1>",
-                "down_dgrad_mx": "k_down_dgrad_mx<",
-                "up_dgrad_mx": "k_rows_mx<moe::MxCfg<256, 256, 128, 128>, 3>",
-                "down_wgrad_mx": "k_wgrad_mx<", "up_wgrad_mx": "k_wgrad_mx<"}
+# kernel-name fragments of each grouped-GEMM op in a rocprofv3 trace (the
+# single-shape kernels and the mixed m-tiling ones)
+GEMM_KERNELS = {"up_swiglu": ("k_up_swiglu<", "up_swiglu_mixed<"),
+                "down": ("k_down<", "down_mixed<"),
+                "down_dgrad": ("k_down_dgrad<", "down_dgrad_mixed<"),
+                "up_dgrad": ("k_up_dgrad<", "up_dgrad_mixed<"),
+                "down_wgrad": ("k_wgrad<",), "up_wgrad": ("k_wgrad<",),
+                "up_swiglu_mx": ("k_up_swiglu_mx<",),
+                "down_mx": ("k_rows_mx<moe::MxCfg<256, 256, 128, 128>, 1>",),
+                "down_dgrad_mx": ("k_down_dgrad_mx<",),
+                "up_dgrad_mx": ("k_rows_mx<moe::MxCfg<256, 256, 128, 128>, 3>",),
+                "down_wgrad_mx": ("k_wgrad_mx<",), "up_wgrad_mx": ("k_wgrad_mx<",)}
+
+
+def is_gemm(frags, name):
+    return any(f in name for f in frags)
 # The measured HBM traffic of the grouped GEMMs lives in this file, next to a
 # hash of the kernel sources it was taken with; a changed kernel reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_deepseek_v3.md")
@@ -379,7 +388,7 @@ def pmc_busy_summary(busy_dir, out_path, cmds, workload="deepseek_v3"):
     for stage, frag in GEMM_KERNELS.items():
         want_up = stage.startswith("up_wgrad")
         wgrad = stage.startswith(("down_wgrad", "up_wgrad"))
-        sel = [(i, v) for i, n, v, _ in busy if frag in n and
+        sel = [(i, v) for i, n, v, _ in busy if is_gemm(frag, n) and
                (not wgrad or wgrad_is_up(n) == want_up)]
         if not sel:
             continue
@@ -476,7 +485,7 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_path, cmds,
         want_up = stage.startswith("up_wgrad")
         wgrad = stage.startswith(("down_wgrad", "up_wgrad"))
         def pick(rs):
-            v = [x for _, n, x in rs if frag in n and
+            v = [x for _, n, x in rs if is_gemm(frag, n) and
                  (not wgrad or wgrad_is_up(n) == want_up)]
             return sum(v) / len(v) if v else None
         f, wr = pick(fetch), pick(write)
