@@ -328,8 +328,11 @@ using MxTile = MxCfg<256, 256, 128, 64>;
 // Four waves of 128 x 128 (one a SIMD; 256 accumulators in AGPRs, eight
 // fragments): a third fewer fragment bytes read from LDS per MFMA.  Faster
 // for the kernels whose epilogue is a plain fp32 store (GEMM2, dgrad1:
-// +10% / +6%), slower where the epilogue does per-row work that eight waves
-// share (GEMM1's SwiGLU and MX quantisation, dgrad2, the weight gradients).
+// +10% / +6%) and for the weight gradients, whose read-modify-write takes 16
+// rows a wave per batch in the registers the AGPR accumulators leave free
+// (dW1 -6%, dW2 -3% against eight waves at 8 rows); slower where the
+// epilogue does per-row work that eight waves share (GEMM1's SwiGLU and MX
+// quantisation, dgrad2).
 using MxTile4 = MxCfg<256, 256, 128, 128>;
 
 // 4 bytes per lane from a per-lane global address into LDS: lane l writes
@@ -702,7 +705,7 @@ __global__ __launch_bounds__(C::NT) void k_wgrad_mx(GemmArgs g)
     }
     Acc<C> acc;
     mx_mainloop<C>(lds, (int)(Kp / MX_GROUP), la, lb, sp, wave0, acc);
-    wgrad_epilogue<C, 4>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2,
+    wgrad_epilogue<C, 4096 / C::NT>(acc, lds, r0, c0, R, Cc, (int64_t)e * R * Cc, UP ? g.dW1 : g.dW2,
                          g.dw_acc, g.dw_bf16);
 }
 
@@ -713,7 +716,7 @@ hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
         return dim3((unsigned)mgrid_blocks(g.M, g.E, C::BM, (int)ceil_div(ncols, per)));
     };
     auto wgrid = [&](int64_t R, int64_t Cc) {
-        const int64_t tiles = ceil_div(R, C::BM) * ceil_div(Cc, C::BN);
+        const int64_t tiles = ceil_div(R, MxTile4::BM) * ceil_div(Cc, MxTile4::BN);
         return dim3((unsigned)grid_for(tiles * g.E));
     };
     switch (op) {
@@ -734,11 +737,12 @@ hipError_t launch_mx_gemm(int32_t op, const GemmArgs &g, hipStream_t s)
                            dim3(MxTile4::NT), 0, s, g);
         break;
     case MOE_GEMM_DOWN_WGRAD:
-        hipLaunchKernelGGL((k_wgrad_mx<C, false>), wgrid(g.H, g.I), dim3(C::NT), 0, s, g);
+        hipLaunchKernelGGL((k_wgrad_mx<MxTile4, false>), wgrid(g.H, g.I), dim3(MxTile4::NT), 0, s,
+                           g);
         break;
     case MOE_GEMM_UP_WGRAD:
-        hipLaunchKernelGGL((k_wgrad_mx<C, true>), wgrid(2 * (int64_t)g.I, g.H), dim3(C::NT), 0, s,
-                           g);
+        hipLaunchKernelGGL((k_wgrad_mx<MxTile4, true>), wgrid(2 * (int64_t)g.I, g.H),
+                           dim3(MxTile4::NT), 0, s, g);
         break;
     default:
         return hipErrorInvalidValue;
