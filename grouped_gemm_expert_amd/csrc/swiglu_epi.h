@@ -73,41 +73,44 @@ MOE_DEV void swiglu_epilogue(const Acc<C> &acc, lds_t *lds, const MTile &t, int6
         uint16_t *hd = part ? h_lo : h, *ad = part ? a_lo : a;
         const bool live = lane < 48 && col < I && (seg == 2 || hd != nullptr);
         // RB rows a wave per pass: their LDS reads issued together, then the
-        // stores (and the MX encoding, which every lane runs: rows past the
-        // segment are only masked at the store)
+        // stores.  The MX form of a: lane l encodes a-chunk l % 16 of the
+        // batch's row l / 16, so the four rows take one pass of the encoder
+        // (every lane runs it; rows past the segment are masked at the store)
         constexpr int NW = C::NT / 64, RB = 4;
         static_assert(EPI_ROWS % (NW * RB) == 0, "row batches tile the half");
+        static_assert(!MX || RB == 4, "the MX encoding takes four rows a pass");
         for (int r0 = wave; r0 < EPI_ROWS; r0 += NW * RB) {
             if (t.m0 + half * EPI_ROWS + r0 >= t.seg_end) break;  // wave-uniform
             u32x4_t v[RB];
 #pragma unroll
             for (int b = 0; b < RB; ++b) v[b] = *(const lds_u32x4 *)(lds + soff(r0 + b * NW, lane));
+            u32x4_t va;
+            if constexpr (MX) va = *(const lds_u32x4 *)(lds + soff(r0 + (lane >> 4) * NW, 32 + (lane & 15)));
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
                 const int64_t m = t.m0 + half * EPI_ROWS + r0 + b * NW;
-                const bool row_ok = m < t.seg_end;
-                if (live && row_ok) {
+                if (live && m < t.seg_end) {
                     uint16_t *dst = seg == 2 ? ad + m * I + col : hd + m * 2 * I + (seg ? I : 0) + col;
                     *(u32x4_t *)dst = v[b];
                 }
-                if constexpr (MX) {
-                    const bool achunk = seg == 2;
-                    float f[8];
-                    const u32x4_t z = {0u, 0u, 0u, 0u};
-                    const u32x4_t va = (achunk && col < I) ? v[b] : z;
+            }
+            if constexpr (MX) {
+                const int64_t m = t.m0 + half * EPI_ROWS + r0 + (lane >> 4) * NW;
+                float f[8];
+                const u32x4_t z = {0u, 0u, 0u, 0u};
+                if (col >= I) va = z;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        f[2 * q] = bf2f((uint16_t)(va[q] & 0xffffu));
-                        f[2 * q + 1] = bf2f((uint16_t)(va[q] >> 16));
-                    }
-                    uint32_t sc;
-                    const uint64_t c = mx_quant8(f, sc);
-                    const uint32_t w = mx_group_word(sc, lane);
-                    if (achunk && row_ok) {
-                        *(uint64_t *)(aq + m * Ip + col) = c;
-                        if (lane == 32)
-                            *(uint32_t *)(as_ + mx_scale_off(m, i0 / MX_GROUP, Ip / MX_GROUP)) = w;
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    f[2 * q] = bf2f((uint16_t)(va[q] & 0xffffu));
+                    f[2 * q + 1] = bf2f((uint16_t)(va[q] >> 16));
+                }
+                uint32_t sc;
+                const uint64_t c = mx_quant8(f, sc);
+                const uint32_t w = mx_group_word(sc, lane);
+                if (m < t.seg_end) {
+                    *(uint64_t *)(aq + m * Ip + col) = c;
+                    if ((lane & 15) == 0)
+                        *(uint32_t *)(as_ + mx_scale_off(m, i0 / MX_GROUP, Ip / MX_GROUP)) = w;
                 }
             }
         }
