@@ -296,9 +296,11 @@ MOE_DEV void kstep(const Frags<C> &cur, Frags<C> &nxt, const lds_t *As, const ld
 #pragma unroll
     for (int n = 0; n < NMF; ++n) {
         if (n < NR) read_one<C, A_NMAJ, B_NMAJ, PARTIAL>(n, As, Bs, kk_next, nxt, wm, wn, lane, na);
+        if constexpr (NC > 0) {
 #pragma unroll
-        for (int i = 0; i < NC; ++i)
-            if (i * NMF / NC == n) copy(i);
+            for (int i = 0; i < NC; ++i)
+                if (i * NMF / NC == n) copy(i);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const int i = n / C::FN, j = n % C::FN;
         if (!PARTIAL || i < na)
@@ -327,9 +329,11 @@ MOE_DEV void kstep_ip(bf16x8_t (&fa)[C::FM], const bf16x8_t (&bc)[C::FN], bf16x8
         if (n < C::FN)
             bn[n] = B_NMAJ ? frag_nmaj<C::BN>(Bs, wn * C::WN + n * 32, kk_next, lane)
                            : frag_kmaj(Bs, wn * C::WN + n * 32, kk_next, lane);
+        if constexpr (NC > 0) {
 #pragma unroll
-        for (int q = 0; q < NC; ++q)
-            if (q * NMF / NC == n) copy(q);
+            for (int q = 0; q < NC; ++q)
+                if (q * NMF / NC == n) copy(q);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (!PARTIAL || i < na)
             acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bc[j], fa[i], acc.v[i][j], 0, 0, 0);
